@@ -1,0 +1,36 @@
+"""CPU fp64 oracle for one GPT pretraining step — TEST INFRASTRUCTURE ONLY.
+
+This package is the slow, plain definition that the HIP path is checked
+against.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import it; the product path never
+does.  It shares no code with the HIP path: it takes plain numpy arrays
+(weights, token ids) and returns plain numpy arrays.
+
+Sources (web pages on nanochat; cited by title and section):
+
+* [APIDOG] apidog.com, "Cara Melatih ChatGPT Sendiri dengan Budget 50 Dolar",
+  section "Bagaimana nanochat Bekerja": "1. Model GPT (nanochat/gpt.py)"
+  (feature list: RoPE, QK normalisation, untied weights, ReLU^2),
+  "2. Pengoptimal Muon (nanochat/optim.py)" (Newton-Schulz loop),
+  "3. Manajemen Presisi (nanochat/common.py)" (bias-free Linear, fp32 masters),
+  "Langkah 3: Latih Tokenizer" (32,768-token vocabulary).
+* [DEVTO] dev.to, "วิธีฝึก ChatGPT ส่วนตัว งบ 50 ดอลลาร์", section
+  "2. ตัวปรับปรุง Muon" (table: embeddings and lm_head -> AdamW, 2-D
+  matrices -> Muon) and "3. การจัดการความแม่นยำ" (dtype table).
+* [HADA] vi.news.hada.io, "NanoChat - ChatGPT tốt nhất bạn có thể mua với
+  100 USD": single GPU runs use gradient accumulation with nearly identical
+  results.
+
+Where the pages are silent, the reading taken is stated in the function that
+applies it.  Pins: every function here is checked by ``tests/test_oracle_*.py``
+against closed forms, invariants, textbook routines (SVD, polar
+decomposition) and central finite differences.  Parity unpinned: the absolute
+loss and gradient values of the d12..d26 shapes (the pages print none); they
+are covered only by the structural pins above.
+"""
+
+from .model import (  # noqa: F401
+    rmsnorm, rmsnorm_backward, rope_tables, rope, rope_inverse,
+    causal_attention, forward, loss_and_grads, logits_of,
+)
+from .optim import adamw_step, newton_schulz, muon_step, train_step  # noqa: F401

@@ -1,0 +1,241 @@
+"""Forward pass, loss and hand-written backward of the GPT, in numpy fp64.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Everything is done with
+whole-array numpy operations in float64; matrix products use ``@``.  There is
+no blocking, fusion or reordering beyond the definition.
+
+Model (decoder-only, pre-norm), per [APIDOG] "1. Model GPT (nanochat/gpt.py)":
+
+    x   = E[tok]                                   (untied token embedding)
+    for each layer:
+        a   = N(x)
+        q,k,v = a Wq^T, a Wk^T, a Wv^T              (bias-free, [APIDOG] "3.")
+        q,k = R_t(N(q_h)), R_t(N(k_h)) per head      (QK normalisation, RoPE)
+        o   = softmax(q k^T / sqrt(hd), causal) v
+        x   = x + o Wo^T
+        m   = N(x);  h = m W1^T;  g = max(h, 0)^2   (ReLU^2 MLP)
+        x   = x + g W2^T
+    z   = N(x) Wh^T                                 (untied lm_head)
+    loss = mean over all B*T positions of lse(z) - z[target]
+
+Readings where the pages are silent:
+
+* N is the parameter-free RMSNorm u * (mean(u^2) + eps)^-1/2, eps = 1e-6; no
+  norm on the embedding output; no logit soft-cap.
+* QK normalisation is the same parameter-free RMSNorm over each head vector,
+  applied before the rotation (the two commute: the rotation keeps the norm).
+* RoPE pairs dimension i with i + hd/2 (half split), angle t * base^(-2i/hd)
+  for position t = 0..T-1 of each row, y_i = x_i cos - x_{i+h} sin,
+  y_{i+h} = x_i sin + x_{i+h} cos.
+* Attention scale 1/sqrt(hd); causal mask keeps keys u <= t (diagonal kept);
+  no document masking; one KV head per query head.
+* Loss: natural log, mean over every position, no ignore index.
+"""
+
+import numpy as np
+
+F64 = np.float64
+
+
+# --------------------------------------------------------------------------
+# building blocks
+# --------------------------------------------------------------------------
+def rmsnorm(u, eps):
+    """Parameter-free RMSNorm over the last axis.  Returns (y, r) with
+    r = (mean(u^2) + eps)^-1/2 and y = u * r."""
+    u = np.asarray(u, F64)
+    r = 1.0 / np.sqrt(np.mean(u * u, axis=-1) + eps)
+    return u * r[..., None], r
+
+
+def rmsnorm_backward(dy, y, r):
+    """Gradient of y = u * r(u) with respect to u, given y and r:
+    du = r * (dy - y * mean(dy * y))   (differentiating r = (mean(u^2)+eps)^-1/2)."""
+    return r[..., None] * (dy - y * np.mean(dy * y, axis=-1, keepdims=True))
+
+
+def rope_tables(T, hd, base):
+    """cos/sin tables [T, hd/2]: angle[t, i] = t * base^(-2i/hd)."""
+    half = hd // 2
+    inv_freq = base ** (-(2.0 * np.arange(half, dtype=F64)) / hd)
+    ang = np.arange(T, dtype=F64)[:, None] * inv_freq[None, :]
+    return np.cos(ang), np.sin(ang)
+
+
+def rope(x, cos, sin):
+    """Rotate pairs (i, i+hd/2) of x [..., T, hd] by the position angle."""
+    half = x.shape[-1] // 2
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * cos - x2 * sin, x1 * sin + x2 * cos], axis=-1)
+
+
+def rope_inverse(y, cos, sin):
+    """Transpose (= inverse) of the rotation: rotate by the negative angle."""
+    half = y.shape[-1] // 2
+    y1, y2 = y[..., :half], y[..., half:]
+    return np.concatenate([y1 * cos + y2 * sin, -y1 * sin + y2 * cos], axis=-1)
+
+
+def _causal_mask(T):
+    return np.triu(np.ones((T, T), dtype=bool), k=1)   # True where key u > query t
+
+
+def causal_attention(q, k, v):
+    """o = softmax(q k^T / sqrt(hd) with keys u > t removed) v.
+
+    q, k, v: [..., T, hd].  Returns (o, P) with P the attention probabilities.
+    """
+    hd = q.shape[-1]
+    T = q.shape[-2]
+    s = (q @ np.swapaxes(k, -1, -2)) / np.sqrt(hd)
+    s = np.where(_causal_mask(T), -np.inf, s)
+    s = s - np.max(s, axis=-1, keepdims=True)
+    p = np.exp(s)
+    p = p / np.sum(p, axis=-1, keepdims=True)
+    return p @ v, p
+
+
+def _sum_outer(a, b):
+    """sum over every leading (batch, position) index of a_n^T b_n:
+    a [..., m], b [..., n] -> [m, n]."""
+    return a.reshape(-1, a.shape[-1]).T @ b.reshape(-1, b.shape[-1])
+
+
+def _layer_names(i):
+    return [f"{i}.Wq", f"{i}.Wk", f"{i}.Wv", f"{i}.Wo", f"{i}.W1", f"{i}.W2"]
+
+
+def param_shapes(cfg):
+    """Name -> shape of every parameter ([out, in] like a bias-free Linear)."""
+    d, F, V = cfg["d_model"], cfg["d_ff"], cfg["vocab"]
+    shapes = {"E": (V, d)}
+    for i in range(cfg["n_layer"]):
+        for n, s in zip(_layer_names(i), [(d, d)] * 4 + [(F, d), (d, F)]):
+            shapes[n] = s
+    shapes["Wh"] = (V, d)
+    return shapes
+
+
+# --------------------------------------------------------------------------
+# forward
+# --------------------------------------------------------------------------
+def _split_heads(u, H):
+    B, T, d = u.shape
+    return u.reshape(B, T, H, d // H).transpose(0, 2, 1, 3)      # [B,H,T,hd]
+
+
+def _merge_heads(u):
+    B, H, T, hd = u.shape
+    return u.transpose(0, 2, 1, 3).reshape(B, T, H * hd)
+
+
+def forward(params, tokens, targets, cfg, keep_cache=True):
+    """Loss of one micro-batch.  tokens, targets: int [B, T].
+
+    Returns (loss, cache); the cache holds what the backward pass needs.
+    """
+    eps = cfg["norm_eps"]
+    H = cfg["n_head"]
+    hd = cfg["head_dim"]
+    tokens = np.asarray(tokens)
+    B, T = tokens.shape
+    cos, sin = rope_tables(T, hd, cfg["rope_base"])
+    P = {k: np.asarray(v, F64) for k, v in params.items()}
+
+    x = P["E"][tokens]                                  # [B,T,d]
+    layers = []
+    for i in range(cfg["n_layer"]):
+        Wq, Wk, Wv, Wo, W1, W2 = (P[n] for n in _layer_names(i))
+        a, r1 = rmsnorm(x, eps)
+        q = _split_heads(a @ Wq.T, H)
+        k = _split_heads(a @ Wk.T, H)
+        v = _split_heads(a @ Wv.T, H)
+        qn, rq = rmsnorm(q, eps)
+        kn, rk = rmsnorm(k, eps)
+        qr = rope(qn, cos, sin)
+        kr = rope(kn, cos, sin)
+        o_h, _ = causal_attention(qr, kr, v)
+        o = _merge_heads(o_h)
+        x = x + o @ Wo.T
+        m, r2 = rmsnorm(x, eps)
+        h = m @ W1.T
+        g = np.maximum(h, 0.0) ** 2
+        x = x + g @ W2.T
+        if keep_cache:
+            layers.append(dict(a=a, r1=r1, qn=qn, rq=rq, kn=kn, rk=rk,
+                               qr=qr, kr=kr, v=v, o=o, m=m, r2=r2, h=h, g=g))
+    xf, rf = rmsnorm(x, eps)
+    z = xf @ P["Wh"].T                                  # [B,T,V]
+    zmax = np.max(z, axis=-1, keepdims=True)
+    lse = (zmax + np.log(np.sum(np.exp(z - zmax), axis=-1, keepdims=True)))[..., 0]
+    tz = np.take_along_axis(z, np.asarray(targets)[..., None], axis=-1)[..., 0]
+    loss = float(np.mean(lse - tz))
+    cache = None
+    if keep_cache:
+        cache = dict(P=P, tokens=tokens, targets=np.asarray(targets), cos=cos, sin=sin,
+                     layers=layers, xf=xf, rf=rf, z=z, lse=lse)
+    return loss, cache
+
+
+def logits_of(params, tokens, cfg):
+    """Logits z [B,T,V] of the forward pass (targets play no role)."""
+    tokens = np.asarray(tokens)
+    _, cache = forward(params, tokens, np.zeros_like(tokens), cfg)
+    return cache["z"]
+
+
+# --------------------------------------------------------------------------
+# backward
+# --------------------------------------------------------------------------
+def loss_and_grads(params, tokens, targets, cfg, grad_scale=1.0):
+    """Loss and grad_scale * d(loss)/d(param) for every parameter (fp64)."""
+    eps = cfg["norm_eps"]
+    hd = cfg["head_dim"]
+    loss, c = forward(params, tokens, targets, cfg)
+    P = c["P"]
+    B, T = c["tokens"].shape
+    n_tok = B * T
+    cos, sin = c["cos"], c["sin"]
+    grads = {}
+
+    # cross-entropy: dz = (softmax(z) - onehot(y)) / (B*T)
+    dz = np.exp(c["z"] - c["lse"][..., None])
+    np.put_along_axis(dz, c["targets"][..., None],
+                      np.take_along_axis(dz, c["targets"][..., None], axis=-1) - 1.0, axis=-1)
+    dz *= grad_scale / n_tok
+    grads["Wh"] = _sum_outer(dz, c["xf"])
+    dxf = dz @ P["Wh"]
+    dx = rmsnorm_backward(dxf, c["xf"], c["rf"])
+
+    for i in reversed(range(cfg["n_layer"])):
+        L = c["layers"][i]
+        nWq, nWk, nWv, nWo, nW1, nW2 = _layer_names(i)
+        # MLP: x += max(h,0)^2 W2^T, h = m W1^T, m = N(x)
+        grads[nW2] = _sum_outer(dx, L["g"])
+        dg = dx @ P[nW2]
+        dh = 2.0 * np.maximum(L["h"], 0.0) * dg
+        grads[nW1] = _sum_outer(dh, L["m"])
+        dm = dh @ P[nW1]
+        dx = dx + rmsnorm_backward(dm, L["m"], L["r2"])
+        # attention: x += o Wo^T
+        grads[nWo] = _sum_outer(dx, L["o"])
+        do = _split_heads(dx @ P[nWo], cfg["n_head"])
+        o_h, p = causal_attention(L["qr"], L["kr"], L["v"])     # recompute P
+        dv = np.swapaxes(p, -1, -2) @ do
+        dp = do @ np.swapaxes(L["v"], -1, -2)
+        ds = p * (dp - np.sum(dp * p, axis=-1, keepdims=True))  # softmax backward
+        dqr = (ds @ L["kr"]) / np.sqrt(hd)
+        dkr = (np.swapaxes(ds, -1, -2) @ L["qr"]) / np.sqrt(hd)
+        dq = rmsnorm_backward(rope_inverse(dqr, cos, sin), L["qn"], L["rq"])
+        dk = rmsnorm_backward(rope_inverse(dkr, cos, sin), L["kn"], L["rk"])
+        dq, dk, dv = _merge_heads(dq), _merge_heads(dk), _merge_heads(dv)
+        grads[nWq] = _sum_outer(dq, L["a"])
+        grads[nWk] = _sum_outer(dk, L["a"])
+        grads[nWv] = _sum_outer(dv, L["a"])
+        da = dq @ P[nWq] + dk @ P[nWk] + dv @ P[nWv]
+        dx = dx + rmsnorm_backward(da, L["a"], L["r1"])
+
+    dE = np.zeros_like(P["E"])
+    np.add.at(dE, c["tokens"].reshape(-1), dx.reshape(n_tok, -1))
+    grads["E"] = dE
+    return loss, grads

@@ -1,0 +1,199 @@
+"""Pins of the oracle's model, loss and backward (CPU only).
+
+Each check is tied to something other than the oracle itself: closed forms,
+invariants of the definition, textbook reductions and central finite
+differences.  None of these needs a GPU.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.model import param_shapes
+from gpt_pretraining_step_gemms_amd import synthetic
+
+
+
+def micro_cfg(L=1, d=16, H=1, V=16, T=8, F=None):
+    return dict(n_layer=L, d_model=d, n_head=H, head_dim=d // H, d_ff=F or 4 * d,
+                vocab=V, seq_len=T, rope_base=10000.0, norm_eps=1e-6)
+
+
+def make(cfg, B, seed=0, std=0.02, dist="uniform"):
+    params = synthetic.normal_params(seed, param_shapes(cfg), std)
+    tok, tgt = synthetic.token_rows(seed + 1, B, cfg["seq_len"], cfg["vocab"], dist)
+    return {k: v.astype(np.float64) for k, v in params.items()}, tok, tgt
+
+
+# ----------------------------------------------------------------- loss pins
+def test_zero_head_loss_is_ln_vocab_and_upstream_grads_vanish():
+    cfg = micro_cfg(L=2, d=32, H=2, V=64)
+    params, tok, tgt = make(cfg, B=2, std=0.3)
+    params["Wh"][:] = 0.0
+    loss, g = oracle.loss_and_grads(params, tok, tgt, cfg)
+    assert loss == pytest.approx(math.log(64), abs=1e-14)
+    for name, val in g.items():
+        if name != "Wh":
+            assert np.all(val == 0.0), name
+    # all logits are 0, softmax is uniform: dWh[v] = (1/N) sum_n (1/V - [y_n = v]) xf_n
+    _, cache = oracle.forward(params, tok, tgt, cfg)
+    xf = cache["xf"].reshape(-1, 32)
+    y = tgt.reshape(-1)
+    onehot = np.zeros((y.size, 64))
+    onehot[np.arange(y.size), y] = 1.0
+    expect = (1.0 / 64 - onehot).T @ xf / y.size
+    np.testing.assert_allclose(g["Wh"], expect, rtol=0, atol=1e-15)
+
+
+def test_zero_head_loss_golden_vocab():
+    # the pages' vocabulary size (tests/golden/zero_head_loss.txt)
+    fields = dict(line.split("=", 1) for line in open(
+        __file__.replace("test_oracle_model.py", "golden/zero_head_loss.txt")).read().split("\n")
+        if "=" in line and not line.startswith("#"))
+    V = int(fields["vocab"])
+    cfg = micro_cfg(L=1, d=16, H=1, V=V, T=4)
+    params, tok, tgt = make(cfg, B=1, std=0.5, dist="zipf")
+    params["Wh"][:] = 0.0
+    loss, _ = oracle.forward(params, tok, tgt, cfg, keep_cache=False)
+    assert loss == pytest.approx(float(fields["loss"]), abs=1e-6)
+    assert loss == pytest.approx(math.log(V), abs=1e-13)
+
+
+@pytest.mark.parametrize("d,V", [(128, 512), (256, 4096)])
+def test_random_init_loss_near_ln_vocab_plus_half_logit_variance(d, V):
+    # xf has unit RMS, Wh ~ N(0, 0.02^2): z ~ N(0, 0.02^2 d) -> E[lse] ~ ln V + var/2
+    cfg = micro_cfg(L=2, d=d, H=d // 64, V=V, T=32)
+    params, tok, tgt = make(cfg, B=2, std=0.02)
+    loss, _ = oracle.forward(params, tok, tgt, cfg, keep_cache=False)
+    expect = math.log(V) + 0.02 ** 2 * d / 2
+    assert abs(loss - expect) / expect < 0.01
+
+
+def test_softmax_rows_sum_to_one_and_head_gradient_columns_sum_to_zero():
+    cfg = micro_cfg(L=2, d=32, H=2, V=64, T=8)
+    params, tok, tgt = make(cfg, B=2, std=0.3)
+    _, cache = oracle.forward(params, tok, tgt, cfg)
+    L0 = cache["layers"][0]
+    _, p = oracle.causal_attention(L0["qr"], L0["kr"], L0["v"])
+    np.testing.assert_allclose(p.sum(-1), 1.0, atol=1e-13)
+    _, g = oracle.loss_and_grads(params, tok, tgt, cfg)
+    # sum_v dz[n, v] = 0 for every position, hence sum_v dWh[v, :] = 0
+    assert np.max(np.abs(g["Wh"].sum(0))) <= 1e-12 * max(1.0, np.max(np.abs(g["Wh"])))
+
+
+def test_causality_future_token_does_not_change_earlier_logits():
+    cfg = micro_cfg(L=2, d=32, H=2, V=64, T=12)
+    params, tok, _ = make(cfg, B=2, std=0.3)
+    z0 = oracle.logits_of(params, tok, cfg)
+    t_star = 7
+    tok2 = tok.copy()
+    tok2[1, t_star] = (tok2[1, t_star] + 5) % 64
+    z1 = oracle.logits_of(params, tok2, cfg)
+    assert np.array_equal(z0[:, :t_star], z1[:, :t_star])
+    assert np.array_equal(z0[0], z1[0])
+    assert not np.allclose(z0[1, t_star:], z1[1, t_star:])
+
+
+# ----------------------------------------------------------- building blocks
+def test_rope_identity_at_zero_norm_preserving_and_shift_invariant():
+    T, hd = 16, 32
+    cos, sin = oracle.rope_tables(T + 5, hd, 10000.0)
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((T, hd))
+    y = oracle.rope(x, cos[:T], sin[:T])
+    np.testing.assert_allclose(y[0], x[0], atol=0)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+    np.testing.assert_allclose(oracle.rope_inverse(y, cos[:T], sin[:T]), x, atol=1e-13)
+    # scores depend only on the position difference
+    q, k = rng.standard_normal(hd), rng.standard_normal(hd)
+    for t, u, c in [(5, 2, 3), (9, 9, 4), (3, 0, 5)]:
+        s1 = oracle.rope(q, cos[t], sin[t]) @ oracle.rope(k, cos[u], sin[u])
+        s2 = oracle.rope(q, cos[t + c], sin[t + c]) @ oracle.rope(k, cos[u + c], sin[u + c])
+        assert s1 == pytest.approx(s2, abs=1e-12)
+    # the half-split pairing: dim i rotates with dim i + hd/2 by t * base^(-2i/hd)
+    e = np.zeros(hd)
+    e[3] = 1.0
+    r = oracle.rope(e, cos[2], sin[2])
+    ang = 2 * 10000.0 ** (-6.0 / hd)
+    assert r[3] == pytest.approx(math.cos(ang), abs=1e-14)
+    assert r[3 + hd // 2] == pytest.approx(math.sin(ang), abs=1e-14)
+
+
+def test_rmsnorm_scale_invariant_and_unit_rms():
+    rng = np.random.default_rng(1)
+    u = rng.standard_normal((5, 64)) * 3.0
+    y, _ = oracle.rmsnorm(u, 0.0)
+    y2, _ = oracle.rmsnorm(7.5 * u, 0.0)
+    np.testing.assert_allclose(y, y2, atol=1e-13)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, -1)), 1.0, atol=1e-13)
+
+
+def test_attention_single_key_and_equal_keys():
+    rng = np.random.default_rng(2)
+    q, k, v = (rng.standard_normal((3, 1, 8)) for _ in range(3))
+    o, _ = oracle.causal_attention(q, k, v)
+    np.testing.assert_allclose(o, v, atol=1e-15)
+    T = 9
+    q = rng.standard_normal((T, 8))
+    k = np.tile(rng.standard_normal((1, 8)), (T, 1))
+    v = rng.standard_normal((T, 8))
+    o, _ = oracle.causal_attention(q, k, v)
+    expect = np.cumsum(v, 0) / np.arange(1, T + 1)[:, None]
+    np.testing.assert_allclose(o, expect, atol=1e-13)
+
+
+# --------------------------------------------------------------- gradients
+def _fd_check(cfg, B, std, names=None, max_coords=None, seed=0):
+    params, tok, tgt = make(cfg, B, seed=seed, std=std)
+    _, g = oracle.loss_and_grads(params, tok, tgt, cfg)
+    h = 1e-5
+    rng = np.random.default_rng(seed)
+    for name in names or params:
+        W = params[name]
+        idx = list(np.ndindex(W.shape))
+        if name == "E":
+            used = set(tok.reshape(-1).tolist())
+            idx = [ij for ij in idx if ij[0] in used] + [ij for ij in idx if ij[0] not in used][:3]
+        if max_coords and len(idx) > max_coords:
+            idx = [idx[i] for i in rng.choice(len(idx), max_coords, replace=False)]
+        fd = np.zeros(len(idx))
+        for j, ij in enumerate(idx):
+            old = W[ij]
+            W[ij] = old + h
+            lp, _ = oracle.forward(params, tok, tgt, cfg, keep_cache=False)
+            W[ij] = old - h
+            lm, _ = oracle.forward(params, tok, tgt, cfg, keep_cache=False)
+            W[ij] = old
+            fd[j] = (lp - lm) / (2 * h)
+        an = np.array([g[name][ij] for ij in idx])
+        scale = max(np.max(np.abs(g[name])), 1e-30)
+        err = np.max(np.abs(fd - an)) / scale
+        assert err <= 1e-6, (name, err)
+
+
+def test_fd_gradients_one_layer_every_coordinate():
+    _fd_check(micro_cfg(L=1, d=16, H=1, V=16, T=8), B=2, std=0.4)
+
+
+def test_fd_gradients_two_layers_two_heads_sampled():
+    _fd_check(micro_cfg(L=2, d=32, H=2, V=64, T=8), B=2, std=0.3, max_coords=40, seed=3)
+
+
+def test_fd_gradients_tiny_shape_sampled():
+    # the tiny configuration's shapes (d 128, one head of 128, vocab 512) at T = 16
+    cfg = micro_cfg(L=2, d=128, H=1, V=512, T=16, F=512)
+    _fd_check(cfg, B=2, std=0.05, max_coords=12, seed=5)
+
+
+def test_accumulation_of_half_batches_equals_full_batch():
+    cfg = micro_cfg(L=2, d=32, H=2, V=64, T=8)
+    params, tok, tgt = make(cfg, B=4, std=0.3)
+    l_full, g_full = oracle.loss_and_grads(params, tok, tgt, cfg)
+    l_a, g_a = oracle.loss_and_grads(params, tok[:2], tgt[:2], cfg, grad_scale=0.5)
+    l_b, g_b = oracle.loss_and_grads(params, tok[2:], tgt[2:], cfg, grad_scale=0.5)
+    assert 0.5 * (l_a + l_b) == pytest.approx(l_full, abs=1e-13)
+    for n in g_full:
+        np.testing.assert_allclose(g_a[n] + g_b[n], g_full[n], rtol=0,
+                                   atol=1e-12 * max(1e-30, np.max(np.abs(g_full[n]))))

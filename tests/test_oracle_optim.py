@@ -1,0 +1,146 @@
+"""Pins of the oracle's AdamW and Muon (CPU only)."""
+
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+import oracle
+from gpt_pretraining_step_gemms_amd.configs import NS_QUINTIC_JORDAN, NS_TEXTBOOK
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def polar_express_rows():
+    rows = []
+    for line in open(os.path.join(GOLDEN, "polar_express_rows.txt")):
+        if line.strip() and not line.startswith("#"):
+            rows.append(tuple(float(x) for x in line.split()))
+    return rows
+
+
+def ns_by_svd(M, coeffs, eps):
+    """NS applied to the singular values: M = U S V^T -> U f(S / (|M|_F + eps)) V^T
+    with f the composition of p_i(s) = a s + b s^3 + c s^5."""
+    U, s, Vt = np.linalg.svd(M, full_matrices=False)
+    s = s / (np.linalg.norm(M) + eps)
+    for a, b, c in coeffs:
+        s = a * s + b * s ** 3 + c * s ** 5
+    return (U * s) @ Vt
+
+
+# ----------------------------------------------------------------- AdamW
+def test_adamw_first_step_is_lr_times_sign():
+    rng = np.random.default_rng(0)
+    p = rng.standard_normal((7, 5))
+    g = rng.standard_normal((7, 5))
+    z = np.zeros_like(p)
+    p1, m1, v1 = oracle.adamw_step(p, g, z, z, 1, lr=0.01, eps=1e-8)
+    np.testing.assert_allclose(p1 - p, -0.01 * g / (np.abs(g) + 1e-8), atol=1e-15)
+    np.testing.assert_allclose(m1, 0.1 * g, atol=1e-15)
+    np.testing.assert_allclose(v1, 0.05 * g * g, atol=1e-15)
+
+
+def test_adamw_constant_gradient_keeps_unit_step_and_weight_decay_shrinks():
+    g = np.full((3, 3), 0.25)
+    p = np.ones((3, 3))
+    m = v = np.zeros_like(p)
+    for t in range(1, 6):
+        p_new, m, v = oracle.adamw_step(p, g, m, v, t, lr=0.1, eps=0.0)
+        # bias correction makes m_hat = g and v_hat = g^2 for a constant gradient
+        np.testing.assert_allclose(p_new - p, -0.1, atol=1e-13)
+        p = p_new
+    p2, _, _ = oracle.adamw_step(np.ones(3), np.zeros(3), np.zeros(3), np.zeros(3), 1,
+                                 lr=0.1, eps=1e-8, wd=0.5)
+    np.testing.assert_allclose(p2, 0.95, atol=1e-15)
+
+
+# -------------------------------------------------------------- Newton-Schulz
+@pytest.mark.parametrize("shape", [(16, 16), (12, 40), (40, 12)])
+@pytest.mark.parametrize("table", ["jordan", "pages", "textbook"])
+def test_newton_schulz_acts_on_singular_values(shape, table):
+    coeffs = {"jordan": NS_QUINTIC_JORDAN, "pages": polar_express_rows(),
+              "textbook": NS_TEXTBOOK * 5}[table]
+    rng = np.random.default_rng(hash(shape) % 1000)
+    M = rng.standard_normal(shape)
+    X = oracle.newton_schulz(M, coeffs, eps=1e-7)
+    np.testing.assert_allclose(X, ns_by_svd(M, coeffs, 1e-7), atol=1e-10)
+
+
+@pytest.mark.parametrize("shape", [(10, 10), (8, 24), (24, 8)])
+def test_textbook_table_converges_to_polar_factor(shape):
+    rng = np.random.default_rng(5)
+    M = rng.standard_normal(shape)
+    # well conditioned: singular values of M / |M|_F bounded away from 0
+    U, s, Vt = np.linalg.svd(M, full_matrices=False)
+    M = (U * np.linspace(1.0, 3.0, s.size)) @ Vt
+    X = oracle.newton_schulz(M, NS_TEXTBOOK * 40, eps=0.0)
+    if shape[0] >= shape[1]:
+        Q, _ = scipy.linalg.polar(M)
+    else:
+        Q, _ = scipy.linalg.polar(M.T)
+        Q = Q.T
+    np.testing.assert_allclose(X, Q, atol=1e-10)
+
+
+def test_default_table_singular_values_near_one():
+    rng = np.random.default_rng(9)
+    M = rng.standard_normal((64, 256))
+    U, _, Vt = np.linalg.svd(M, full_matrices=False)
+    # one dominant direction plus 63 small ones: sigma / |M|_F spans about [0.01, 0.98]
+    s = np.concatenate([[1.0], np.geomspace(0.0105, 0.05, 63)])
+    M = (U * s) @ Vt
+    sv = np.linalg.svd(oracle.newton_schulz(M, NS_QUINTIC_JORDAN, 1e-7), compute_uv=False)
+    # five quintic steps map [0.01, 1] into about [0.68, 1.14]: "singular values near 1"
+    assert sv.min() > 0.68 and sv.max() < 1.14
+
+
+def test_newton_schulz_orientation_does_not_matter():
+    rng = np.random.default_rng(11)
+    M = rng.standard_normal((20, 50))
+    X1 = oracle.newton_schulz(M, NS_QUINTIC_JORDAN)
+    X2 = oracle.newton_schulz(M.T, NS_QUINTIC_JORDAN).T
+    np.testing.assert_allclose(X1, X2, atol=1e-12)
+
+
+# -------------------------------------------------------------------- Muon
+def test_muon_zero_gradient_leaves_weights_and_momentum():
+    W = np.random.default_rng(1).standard_normal((6, 9))
+    Z = np.zeros_like(W)
+    W1, M1 = oracle.muon_step(W, Z, Z, lr=0.02, coeffs=NS_QUINTIC_JORDAN)
+    assert np.array_equal(W1, W) and np.array_equal(M1, Z)
+
+
+def test_muon_step_equals_momentum_then_svd_form():
+    rng = np.random.default_rng(2)
+    W, G, M = (rng.standard_normal((12, 30)) for _ in range(3))
+    W1, M1 = oracle.muon_step(W, G, M, lr=0.05, coeffs=NS_QUINTIC_JORDAN, momentum=0.95, wd=0.1)
+    np.testing.assert_allclose(M1, 0.95 * M + G, atol=1e-14)
+    np.testing.assert_allclose(W1, W * (1 - 0.05 * 0.1) - 0.05 * ns_by_svd(0.95 * M + G, NS_QUINTIC_JORDAN, 1e-7),
+                               atol=1e-10)
+
+
+def test_momentum_scale_is_normalised_away():
+    # the EMA form (1 - mu) G gives the same orthogonalised update up to eps
+    rng = np.random.default_rng(4)
+    G = rng.standard_normal((8, 8))
+    Wa, _ = oracle.muon_step(np.zeros((8, 8)), G, np.zeros((8, 8)), 0.1, NS_QUINTIC_JORDAN, eps=0.0)
+    Wb, _ = oracle.muon_step(np.zeros((8, 8)), 0.05 * G, np.zeros((8, 8)), 0.1, NS_QUINTIC_JORDAN, eps=0.0)
+    np.testing.assert_allclose(Wa, Wb, atol=1e-12)
+
+
+def test_train_step_routes_groups():
+    rng = np.random.default_rng(6)
+    params = {"E": rng.standard_normal((5, 4)), "0.Wq": rng.standard_normal((4, 4)),
+              "Wh": rng.standard_normal((5, 4))}
+    grads = {k: rng.standard_normal(v.shape) for k, v in params.items()}
+    hp = dict(adam_lr_embed=0.1, adam_lr_head=0.2, adam_beta1=0.9, adam_beta2=0.95,
+              adam_eps=1e-8, adam_wd=0.0, muon_lr=0.02, muon_momentum=0.95, muon_wd=0.0,
+              ns_eps=1e-7, ns_coeffs=NS_QUINTIC_JORDAN)
+    new, state = oracle.train_step(params, grads, {}, 1, hp)
+    np.testing.assert_allclose(new["E"] - params["E"], -0.1 * grads["E"] / (np.abs(grads["E"]) + 1e-8), atol=1e-14)
+    np.testing.assert_allclose(new["Wh"] - params["Wh"], -0.2 * grads["Wh"] / (np.abs(grads["Wh"]) + 1e-8), atol=1e-14)
+    np.testing.assert_allclose(new["0.Wq"] - params["0.Wq"], -0.02 * ns_by_svd(grads["0.Wq"], NS_QUINTIC_JORDAN, 1e-7),
+                               atol=1e-12)
+    assert set(state["E"]) == {"m", "v"} and set(state["0.Wq"]) == {"mom"}
