@@ -1,0 +1,193 @@
+"""Training-step throughput of the GPT pretraining step on one MI355X.
+
+A step is: zero the gradients, K accumulated micro-batches of forward +
+backward (nc_fwd_bwd), one optimizer step (AdamW + Muon).  Workload: the d20
+model (20 layers, width 1280, 10 heads of 128, MLP 5120, vocabulary 32768,
+sequence 2048), micro-batch 32 rows, 8 micro-batches = 524,288 tokens per
+step, Zipf(1.1) synthetic token ids, N(0, 0.02^2) weights, bf16 matrix-core
+inputs with fp32 master weights and accumulation.
+
+Prints one JSON line: tokens/s, MFU against the bf16 dense MFMA peak, the
+roofline of the dominant kernel (the bf16 GEMM at the MLP up-projection
+shape, timed with HIP events on its stream) and the CPU oracle's throughput
+on a bounded sample.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2.5e15          # MI355X dense bf16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12           # MI355X HBM3E, B/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="d20")
+    ap.add_argument("--micro-batch", type=int, default=None)
+    ap.add_argument("--accum", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--roofline-only", action="store_true",
+                    help="only the dominant-kernel timing loop (for profiling it alone)")
+    ap.add_argument("--roofline-iters", type=int, default=20)
+    return ap.parse_args()
+
+
+def roofline_gemm(cfg, iters):
+    """bf16 MFMA GEMM at the MLP up-projection shape of one micro-batch:
+    [B*T, d] x [F, d]^T with the ReLU^2 epilogue (h and relu(h)^2 in bf16)."""
+    import torch
+    from gpt_pretraining_step_gemms_amd import nc
+    M, N, K = cfg.micro_batch * cfg.seq_len, cfg.d_ff, cfg.d_model
+    A = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+    B = (0.02 * torch.randn(N, K, device="cuda")).to(torch.bfloat16)
+    H = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    G = torch.empty_like(H)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        nc.gemm(A, 0, B, 0, H, M, N, K, nc.EPI_RELU2, aux_out=G)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(iters):
+        nc.gemm(A, 0, B, 0, H, M, N, K, nc.EPI_RELU2, aux_out=G)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    sec = t0.elapsed_time(t1) / 1e3 / iters
+    flops = 2.0 * M * N * K
+    return {"kernel": "gemm_bf16_kernel<256,256,2,2,KCont,KCont> (MLP up + ReLU^2)",
+            "shape": [M, N, K], "avg_launch_us": sec * 1e6,
+            "bound": "mfma", "achieved": flops / sec / 1e12, "peak": PEAK_BF16 / 1e12,
+            "unit": "TFLOP/s", "frac": flops / sec / PEAK_BF16, "traffic": None}
+
+
+def cpu_baseline(cfg):
+    """The fp64 numpy oracle on one 2048-token row of the same model: forward
+    + backward (the optimizer, <1% of a 524,288-token step's FLOPs, is left
+    out)."""
+    import numpy as np
+    import oracle
+    from oracle.model import param_shapes
+    from gpt_pretraining_step_gemms_amd import synthetic
+    ocfg = cfg.as_oracle_cfg()
+    params = {k: v.astype(np.float64) for k, v in
+              synthetic.normal_params(0, param_shapes(ocfg), cfg.init_std).items()}
+    tok, tgt = synthetic.token_rows(1000, 1, cfg.seq_len, cfg.vocab, cfg.token_dist)
+    t0 = time.perf_counter()
+    oracle.loss_and_grads(params, tok, tgt, ocfg)
+    sec = time.perf_counter() - t0
+    cores = int(os.environ.get("OPENBLAS_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": cfg.seq_len / sec, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"fwd+bwd of 1 row x {cfg.seq_len} tokens of {cfg.name}, numpy fp64 "
+                      f"(OpenBLAS), {sec:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(gradient accumulation replaces data parallelism)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from gpt_pretraining_step_gemms_amd import nc, synthetic
+    from gpt_pretraining_step_gemms_amd.configs import CONFIGS, OptimConfig, with_batch
+
+    cfg = CONFIGS[args.config]
+    cfg = with_batch(cfg, micro_batch=args.micro_batch, accum_steps=args.accum)
+    if args.roofline_only:
+        r = roofline_gemm(cfg, args.roofline_iters)
+        print(json.dumps({"roofline": r}))
+        return
+
+    ocfg = OptimConfig()
+    model = nc.Model(cfg, ocfg, max_micro_batch=cfg.micro_batch)
+    model.init_params(seed=0, std=cfg.init_std)
+    K = cfg.accum_steps
+    toks, tgts = [], []
+    for k in range(K):
+        t, y = synthetic.token_rows(1000 + k, cfg.micro_batch, cfg.seq_len, cfg.vocab, cfg.token_dist)
+        toks.append(torch.from_numpy(t).cuda())
+        tgts.append(torch.from_numpy(y).cuda())
+    losses = torch.zeros(K, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        model.zero_grads()
+        for k in range(K):
+            model.fwd_bwd(toks[k], tgts[k], 1.0 / K, loss_out=losses[k:k + 1])
+        model.optimizer_step()
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        print(f"[bench] warmup step {i} loss {losses.mean().item():.4f}", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    sec = e0.elapsed_time(e1) / 1e3 / args.steps
+    print(f"[bench] {args.steps} steps, {sec * 1e3:.1f} ms/step (wall {wall:.1f} s), "
+          f"last loss {losses.mean().item():.4f}", file=sys.stderr, flush=True)
+    tokens = cfg.tokens_per_step
+    fb_flops, ns_flops = model.flops(cfg.micro_batch)
+    step_flops = K * fb_flops
+    tps = tokens / sec
+    mfu = step_flops / sec / PEAK_BF16
+    finite = model.check_finite()
+    model.close()
+    del model
+    torch.cuda.empty_cache()
+
+    roof = roofline_gemm(cfg, args.roofline_iters)
+    print(f"[bench] roofline {roof['achieved']:.0f} TFLOP/s ({roof['frac']:.3f} of peak)",
+          file=sys.stderr, flush=True)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(cfg)
+
+    d = cfg.d_model
+    out = {
+        "metric": "training tokens/sec and MFU (% bf16 MFMA peak) per GPT step, 1 MI355X",
+        "value": tps,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": sec * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (Zipf(1.1) token ids, N(0, 0.02^2) random-init weights)",
+        "config": {"workload": f"{cfg.name} GPT pretraining step: {cfg.n_layer} layers, d {d}, "
+                               f"{cfg.n_head}x128 heads, MLP {cfg.d_ff} ReLU^2, vocab {cfg.vocab}, "
+                               f"seq {cfg.seq_len}, micro-batch {cfg.micro_batch} x {K} accumulated "
+                               f"= {tokens} tokens/step, Muon (5 NS iters) + AdamW",
+                   "global_batch": cfg.micro_batch * K, "seq_len": cfg.seq_len,
+                   "parallelism": "1 GPU, gradient accumulation"},
+        "mfu": mfu,
+        "mfu_with_newton_schulz": (step_flops + ns_flops) / sec / PEAK_BF16,
+        "flops_per_token": fb_flops / (cfg.micro_batch * cfg.seq_len),
+        "params_finite": finite,
+        "roofline": {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
+        "roofline_kernel": {k: roof[k] for k in ("kernel", "shape", "avg_launch_us")},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

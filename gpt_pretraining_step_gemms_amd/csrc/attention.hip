@@ -1,0 +1,588 @@
+// Causal self-attention (head dim 128) on gfx950, forward and backward.
+//
+// q, k, v, o and their gradients stay token-major ([token, head*128], row
+// stride ld) as the QKV and output-projection GEMMs produce and consume them;
+// the log-sum-exp and D = rowsum(dO*O) are [B, H, T] fp32.
+//
+// bf16 path (flash attention with v_mfma_f32_32x32x16_bf16):
+//  * forward: a workgroup owns 128 queries of one (b, h) (4 waves x 32), walks
+//    the 64-key tiles up to the diagonal with K and V^T staged in LDS (double
+//    buffered).  It computes S^T = K Q^T so that every lane owns one query
+//    column: the online-softmax max/sum are lane-local plus one exchange with
+//    the lane 32 apart, and the rescale of O^T = V^T P^T is a per-lane scalar.
+//    P^T feeds the second MFMA straight from the accumulators (the reduction
+//    index is permuted identically on both operands).
+//  * backward: two deterministic kernels, no atomics.  dK/dV: a workgroup owns
+//    128 keys and walks the query tiles from the diagonal down, recomputing
+//    P = exp(S - lse) and dS = P (dP - D).  dQ: a workgroup owns 128 queries
+//    and walks the key tiles up to the diagonal.
+//  * MN-contiguous operands (V^T, Q^T, dO^T, K^T) are transposed in registers
+//    (8x8 16-bit blocks) on their way into LDS.
+// fp32 path (tiny configuration): one wave per query (or key) row, plain
+// loops over the causal range.
+#include "kernels.h"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// 8 rows x 16 bytes of a token-major operand
+struct Blk8 { u32x4 r[8]; };
+
+NC_DEV void load_blk(const bf16* __restrict__ g, int64_t ld, int row, int col, Blk8& b) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    b.r[j] = *reinterpret_cast<const u32x4*>(g + (int64_t)(row + j) * ld + col);
+}
+
+// tile [64 rows][128 cols]: 16 chunks of 16 B per row, chunk ^= row & 7
+NC_DEV int nrm_off(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 3); }
+// transposed tile [128 rows (head dim)][64 cols (tokens)]: 8 chunks per row
+NC_DEV int trs_swz(int d) { return (d ^ (d >> 3)) & 7; }
+NC_DEV int trs_off(int d, int chunk) { return d * 64 + ((chunk ^ trs_swz(d)) << 3); }
+
+// rb: 8-row block index in the 64-row tile, cb: 16-byte chunk index (0..15)
+NC_DEV void store_nrm(bf16* lds, int rb, int cb, const Blk8& b) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    *reinterpret_cast<u32x4*>(lds + nrm_off(rb * 8 + j, cb)) = b.r[j];
+}
+NC_DEV void store_trs(bf16* lds, int rb, int cb, const Blk8& b) {
+  u32x4 t[8];
+  transpose8x8_b16(b.r, t);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(lds + trs_off(cb * 8 + i, rb)) = t[i];
+}
+
+NC_DEV bf16x8 frag_nrm(const bf16* lds, int row, int chunk) {
+  return *reinterpret_cast<const bf16x8*>(lds + nrm_off(row, chunk));
+}
+// 8 values of row d of a transposed tile at columns o1..o1+3 and o1+8..o1+11
+NC_DEV bf16x8 frag_trs(const bf16* lds, int d, int o1) {
+  const int c = o1 >> 3, w = o1 & 7;
+  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(lds + trs_off(d, c) + w);
+  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(lds + trs_off(d, c + 1) + w);
+  bf16x8 r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
+// accumulator registers hf*8 .. hf*8+7 of a 32x32 tile, as an MFMA operand
+NC_DEV bf16x8 pack_half(const float* v, int hf) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (bf16)v[hf * 8 + e];
+  return r;
+}
+
+NC_DEV f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// ================================================================ forward
+__global__ __launch_bounds__(256, 1) void attn_fwd_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    int64_t ld, bf16* __restrict__ o, int64_t ldo, float* __restrict__ lse, int T, int H,
+    float scale_log2) {
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * 64 * 128 + 2 * 128 * 64];
+  // Ks[buf] = smem + buf*8192, VTs[buf] = smem + 16384 + buf*8192
+  constexpr int KT = 64 * 128;
+
+  const int nqb = T / 128;
+  const int qb = nqb - 1 - (int)(blockIdx.x % nqb);
+  const int bh = blockIdx.x / nqb, b = bh / H, h = bh % H;
+  const int64_t base = (int64_t)b * T * ld + h * 128;
+  const bf16* qg = q + base;
+  const bf16* kg = k + base;
+  const bf16* vg = v + base;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int q0w = qb * 128 + wave * 32;
+  const int myq = q0w + l32;
+
+  bf16x8 qf[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    qf[s] = *reinterpret_cast<const bf16x8*>(qg + (int64_t)myq * ld + s * 16 + half * 8);
+
+  f32x16 oacc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
+  float m = -INFINITY, l = 0.f;
+
+  const int n_kv = 2 * qb + 2;
+  // loader roles: threads 0..127 -> K block, 128..255 -> V block (transposed)
+  const int lt = tid & 127, rb = lt >> 4, cb = lt & 15;
+  const bool is_k = tid < 128;
+  Blk8 pre;
+  load_blk(is_k ? kg : vg, ld, rb * 8, cb * 8, pre);
+  if (is_k) store_nrm(smem, rb, cb, pre); else store_trs(smem + 2 * KT, rb, cb, pre);
+  __syncthreads();
+
+  for (int kv = 0; kv < n_kv; ++kv) {
+    const int cur = kv & 1;
+    const bool more = kv + 1 < n_kv;
+    if (more) load_blk(is_k ? kg : vg, ld, (kv + 1) * 64 + rb * 8, cb * 8, pre);
+
+    if (kv * 64 <= q0w + 31) {
+      const bf16* ks = smem + cur * KT;
+      const bf16* vts = smem + (2 + cur) * KT;
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          sacc[kb] = mfma(frag_nrm(ks, kb * 32 + l32, s * 2 + half), qf[s], sacc[kb]);
+      }
+      const bool need_mask = kv * 64 + 63 > q0w;
+      float sv[2][16];
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float x = sacc[kb][e] * scale_log2;
+          if (need_mask) {
+            const int key = kv * 64 + kb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+            if (key > myq) x = -INFINITY;
+          }
+          sv[kb][e] = x;
+          mt = fmaxf(mt, x);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float mn = fmaxf(m, mt);
+      const float alpha = exp2f(m - mn);
+      float ls = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = exp2f(sv[kb][e] - mn);
+          sv[kb][e] = p;
+          ls += p;
+        }
+      l = l * alpha + ls;
+      m = mn;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+      bf16x8 pf[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pf[j] = pack_half(sv[j >> 1], j & 1);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          oacc[db] = mfma(frag_trs(vts, db * 32 + l32, (j >> 1) * 32 + (j & 1) * 16 + half * 4),
+                          pf[j], oacc[db]);
+    }
+    if (more) {
+      if (is_k) store_nrm(smem + (cur ^ 1) * KT, rb, cb, pre);
+      else store_trs(smem + (2 + (cur ^ 1)) * KT, rb, cb, pre);
+    }
+    __syncthreads();
+  }
+
+  const float lt_sum = l + __shfl_xor(l, 32, 64);
+  const float inv = 1.f / lt_sum;
+  if (half == 0) lse[((int64_t)b * H + h) * T + myq] = (m + log2f(lt_sum)) * kLn2;
+
+  // stage O (this wave's 32 x 128) through LDS with padded rows, then 16-B stores
+  constexpr int OSTR = 136;
+  bf16* os = smem + wave * 32 * OSTR;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = (bf16)(oacc[db][g * 4 + i] * inv);
+      *reinterpret_cast<bf16x4*>(os + l32 * OSTR + db * 32 + g * 8 + half * 4) = w;
+    }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int idx = lane + 64 * i, r = idx >> 4, c = idx & 15;
+    const u32x2 lo = *reinterpret_cast<const u32x2*>(os + r * OSTR + c * 8);
+    const u32x2 hi = *reinterpret_cast<const u32x2*>(os + r * OSTR + c * 8 + 4);
+    u32x4 val = {lo[0], lo[1], hi[0], hi[1]};
+    *reinterpret_cast<u32x4*>(o + ((int64_t)b * T + q0w + r) * ldo + h * 128 + c * 8) = val;
+  }
+}
+
+// ============================================================ dK / dV
+__global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    int64_t ld, const bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ lse,
+    const float* __restrict__ Dv, bf16* __restrict__ dk, bf16* __restrict__ dv, int64_t ldd,
+    int T, int H, float scale_log2, float scale) {
+  constexpr int TILE = 64 * 128;
+  constexpr int BUF = 4 * TILE + 2 * 64 * 2;   // Q, Q^T, dO, dO^T + lse2, D (as bf16 slots)
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * BUF];
+
+  const int nkb = T / 128;
+  const int kblk = blockIdx.x % nkb;
+  const int bh = blockIdx.x / nkb, b = bh / H, h = bh % H;
+  const int64_t base = (int64_t)b * T * ld + h * 128;
+  const int64_t obase = (int64_t)b * T * ldo + h * 128;
+  const float* lse_bh = lse + ((int64_t)b * H + h) * T;
+  const float* D_bh = Dv + ((int64_t)b * H + h) * T;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int k0w = kblk * 128 + wave * 32;
+  const int mykey = k0w + l32;
+
+  bf16x8 kf[8], vf[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    kf[s] = *reinterpret_cast<const bf16x8*>(k + base + (int64_t)mykey * ld + s * 16 + half * 8);
+    vf[s] = *reinterpret_cast<const bf16x8*>(v + base + (int64_t)mykey * ld + s * 16 + half * 8);
+  }
+  f32x16 dkacc[4], dvacc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) { dkacc[i][e] = 0.f; dvacc[i][e] = 0.f; }
+
+  const int qt0 = kblk * 2, nqt = T / 64;
+  const int lt = tid & 127, rb = lt >> 4, cb = lt & 15;
+  const bool is_q = tid < 128;
+  const bf16* src = is_q ? q + base : dO + obase;
+  const int64_t lds_ld = is_q ? ld : ldo;
+  Blk8 pre;
+  float pre_l = 0.f, pre_d = 0.f;
+  auto bufp = [&](int i) { return smem + i * BUF; };
+  auto stage = [&](int qt, bf16* buf) {
+    bf16* nrm = buf + (is_q ? 0 : 2 * TILE);
+    bf16* trs = buf + (is_q ? TILE : 3 * TILE);
+    store_nrm(nrm, rb, cb, pre);
+    store_trs(trs, rb, cb, pre);
+    float* stats = reinterpret_cast<float*>(buf + 4 * TILE);
+    if (tid < 64) { stats[tid] = pre_l; stats[64 + tid] = pre_d; }
+    (void)qt;
+  };
+  auto fetch = [&](int qt) {
+    load_blk(src, lds_ld, qt * 64 + rb * 8, cb * 8, pre);
+    if (tid < 64) { pre_l = lse_bh[qt * 64 + tid] * kLog2e; pre_d = D_bh[qt * 64 + tid]; }
+  };
+  fetch(qt0);
+  stage(qt0, bufp(0));
+  __syncthreads();
+
+  for (int qt = qt0; qt < nqt; ++qt) {
+    const int cur = (qt - qt0) & 1;
+    const bool more = qt + 1 < nqt;
+    if (more) fetch(qt + 1);
+    if (qt * 64 + 63 >= k0w) {
+      const bf16* buf = bufp(cur);
+      const bf16* Qs = buf;
+      const bf16* QTs = buf + TILE;
+      const bf16* dOs = buf + 2 * TILE;
+      const bf16* dOTs = buf + 3 * TILE;
+      const float* lse2s = reinterpret_cast<const float*>(buf + 4 * TILE);
+      const float* Ds = lse2s + 64;
+      f32x16 sacc[2], pacc[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) { sacc[qb][e] = 0.f; pacc[qb][e] = 0.f; }
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          sacc[qb] = mfma(frag_nrm(Qs, qb * 32 + l32, s * 2 + half), kf[s], sacc[qb]);
+          pacc[qb] = mfma(frag_nrm(dOs, qb * 32 + l32, s * 2 + half), vf[s], pacc[qb]);
+        }
+      }
+      const bool need_mask = qt * 64 < k0w + 31;
+      float p[2][16], ds[2][16];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int ql = qb * 32 + g * 8 + half * 4;
+          const float4 l4 = *reinterpret_cast<const float4*>(lse2s + ql);
+          const float4 d4 = *reinterpret_cast<const float4*>(Ds + ql);
+          const float la[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float da[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = g * 4 + i;
+            float pv = exp2f(sacc[qb][e] * scale_log2 - la[i]);
+            if (need_mask && qt * 64 + ql + i < mykey) pv = 0.f;
+            p[qb][e] = pv;
+            ds[qb][e] = pv * (pacc[qb][e] - da[i]);
+          }
+        }
+      bf16x8 pa[4], dsa[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        pa[j] = pack_half(p[j >> 1], j & 1);
+        dsa[j] = pack_half(ds[j >> 1], j & 1);
+      }
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int o1 = (j >> 1) * 32 + (j & 1) * 16 + half * 4;
+          dvacc[db] = mfma(pa[j], frag_trs(dOTs, db * 32 + l32, o1), dvacc[db]);
+          dkacc[db] = mfma(dsa[j], frag_trs(QTs, db * 32 + l32, o1), dkacc[db]);
+        }
+    }
+    if (more) stage(qt + 1, bufp(cur ^ 1));
+    __syncthreads();
+  }
+
+  // C[key][d]: lane holds column d = db*32 + l32, rows key = 8*(e/4) + 4*half + e%4
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = k0w + (e >> 2) * 8 + half * 4 + (e & 3);
+      const int64_t off = ((int64_t)b * T + key) * ldd + h * 128 + db * 32 + l32;
+      dk[off] = (bf16)(dkacc[db][e] * scale);
+      dv[off] = (bf16)dvacc[db][e];
+    }
+}
+
+// ================================================================== dQ
+__global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    int64_t ld, const bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ lse,
+    const float* __restrict__ Dv, bf16* __restrict__ dq, int64_t ldd, int T, int H,
+    float scale_log2, float scale) {
+  constexpr int TILE = 64 * 128;
+  constexpr int BUF = 3 * TILE;   // K, K^T, V
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * BUF];
+
+  const int nqb = T / 128;
+  const int qb = nqb - 1 - (int)(blockIdx.x % nqb);
+  const int bh = blockIdx.x / nqb, b = bh / H, h = bh % H;
+  const int64_t base = (int64_t)b * T * ld + h * 128;
+  const int64_t obase = (int64_t)b * T * ldo + h * 128;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int q0w = qb * 128 + wave * 32;
+  const int myq = q0w + l32;
+
+  bf16x8 qf[8], df[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    qf[s] = *reinterpret_cast<const bf16x8*>(q + base + (int64_t)myq * ld + s * 16 + half * 8);
+    df[s] = *reinterpret_cast<const bf16x8*>(dO + obase + (int64_t)myq * ldo + s * 16 + half * 8);
+  }
+  const float lse2 = lse[((int64_t)b * H + h) * T + myq] * kLog2e;
+  const float Dq = Dv[((int64_t)b * H + h) * T + myq];
+  f32x16 dqacc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dqacc[i][e] = 0.f;
+
+  const int n_kv = 2 * qb + 2;
+  const int lt = tid & 127, rb = lt >> 4, cb = lt & 15;
+  const bool is_k = tid < 128;
+  const bf16* src = (is_k ? k : v) + base;
+  Blk8 pre;
+  auto stage = [&](bf16* buf) {
+    if (is_k) { store_nrm(buf, rb, cb, pre); store_trs(buf + TILE, rb, cb, pre); }
+    else store_nrm(buf + 2 * TILE, rb, cb, pre);
+  };
+  load_blk(src, ld, rb * 8, cb * 8, pre);
+  stage(smem);
+  __syncthreads();
+
+  for (int kv = 0; kv < n_kv; ++kv) {
+    const int cur = kv & 1;
+    const bool more = kv + 1 < n_kv;
+    if (more) load_blk(src, ld, (kv + 1) * 64 + rb * 8, cb * 8, pre);
+    if (kv * 64 <= q0w + 31) {
+      const bf16* Ks = smem + cur * BUF;
+      const bf16* KTs = Ks + TILE;
+      const bf16* Vs = Ks + 2 * TILE;
+      f32x16 sacc[2], pacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) { sacc[kb][e] = 0.f; pacc[kb][e] = 0.f; }
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          sacc[kb] = mfma(frag_nrm(Ks, kb * 32 + l32, s * 2 + half), qf[s], sacc[kb]);
+          pacc[kb] = mfma(frag_nrm(Vs, kb * 32 + l32, s * 2 + half), df[s], pacc[kb]);
+        }
+      }
+      const bool need_mask = kv * 64 + 63 > q0w;
+      float ds[2][16];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float pv = exp2f(sacc[kb][e] * scale_log2 - lse2);
+          if (need_mask && kv * 64 + kb * 32 + (e >> 2) * 8 + half * 4 + (e & 3) > myq) pv = 0.f;
+          ds[kb][e] = pv * (pacc[kb][e] - Dq);
+        }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8 a = pack_half(ds[j >> 1], j & 1);
+        const int o1 = (j >> 1) * 32 + (j & 1) * 16 + half * 4;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          dqacc[db] = mfma(a, frag_trs(KTs, db * 32 + l32, o1), dqacc[db]);
+      }
+    }
+    if (more) stage(smem + (cur ^ 1) * BUF);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int qq = q0w + (e >> 2) * 8 + half * 4 + (e & 3);
+      dq[((int64_t)b * T + qq) * ldd + h * 128 + db * 32 + l32] = (bf16)(dqacc[db][e] * scale);
+    }
+}
+
+// ========================================================== fp32 path
+// one wave per (b, h, t) query row; lane owns head dims lane and lane + 64
+__global__ void attn_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                                    const float* __restrict__ v, int64_t ld,
+                                    float* __restrict__ o, int64_t ldo, float* __restrict__ lse,
+                                    int B, int T, int H, float scale) {
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= B * H * T) return;
+  const int lane = threadIdx.x & 63;
+  const int t = item % T, bh = item / T, b = bh / H, h = bh % H;
+  const int64_t base = (int64_t)b * T * ld + h * 128;
+  const float q1 = q[base + (int64_t)t * ld + lane], q2 = q[base + (int64_t)t * ld + lane + 64];
+  float m = -INFINITY, l = 0.f, o1 = 0.f, o2 = 0.f;
+  for (int u = 0; u <= t; ++u) {
+    const int64_t ku = base + (int64_t)u * ld;
+    const float s = wave_sum(q1 * k[ku + lane] + q2 * k[ku + lane + 64]) * scale;
+    const float mn = fmaxf(m, s);
+    const float a = expf(m - mn), p = expf(s - mn);
+    l = l * a + p;
+    o1 = o1 * a + p * v[ku + lane];
+    o2 = o2 * a + p * v[ku + lane + 64];
+    m = mn;
+  }
+  const int64_t oo = ((int64_t)b * T + t) * ldo + h * 128;
+  o[oo + lane] = o1 / l;
+  o[oo + lane + 64] = o2 / l;
+  if (lane == 0) lse[((int64_t)b * H + h) * T + t] = m + logf(l);
+}
+
+__global__ void attn_bwd_dq_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                                       const float* __restrict__ v, int64_t ld,
+                                       const float* __restrict__ dO, int64_t ldo,
+                                       const float* __restrict__ lse,
+                                       const float* __restrict__ Dv, float* __restrict__ dq,
+                                       int64_t ldd, int B, int T, int H, float scale) {
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= B * H * T) return;
+  const int lane = threadIdx.x & 63;
+  const int t = item % T, bh = item / T, b = bh / H, h = bh % H;
+  const int64_t base = (int64_t)b * T * ld + h * 128;
+  const int64_t ob = ((int64_t)b * T + t) * ldo + h * 128;
+  const float q1 = q[base + (int64_t)t * ld + lane], q2 = q[base + (int64_t)t * ld + lane + 64];
+  const float g1 = dO[ob + lane], g2 = dO[ob + lane + 64];
+  const float L = lse[(int64_t)bh * T + t], Dt = Dv[(int64_t)bh * T + t];
+  float a1 = 0.f, a2 = 0.f;
+  for (int u = 0; u <= t; ++u) {
+    const int64_t ku = base + (int64_t)u * ld;
+    const float s = wave_sum(q1 * k[ku + lane] + q2 * k[ku + lane + 64]) * scale;
+    const float p = expf(s - L);
+    const float dp = wave_sum(g1 * v[ku + lane] + g2 * v[ku + lane + 64]);
+    const float ds = p * (dp - Dt);
+    a1 += ds * k[ku + lane];
+    a2 += ds * k[ku + lane + 64];
+  }
+  const int64_t dd = ((int64_t)b * T + t) * ldd + h * 128;
+  dq[dd + lane] = a1 * scale;
+  dq[dd + lane + 64] = a2 * scale;
+}
+
+// one wave per (b, h, u) key row
+__global__ void attn_bwd_dkv_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                                        const float* __restrict__ v, int64_t ld,
+                                        const float* __restrict__ dO, int64_t ldo,
+                                        const float* __restrict__ lse,
+                                        const float* __restrict__ Dv, float* __restrict__ dk,
+                                        float* __restrict__ dv, int64_t ldd, int B, int T, int H,
+                                        float scale) {
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= B * H * T) return;
+  const int lane = threadIdx.x & 63;
+  const int u = item % T, bh = item / T, b = bh / H, h = bh % H;
+  const int64_t base = (int64_t)b * T * ld + h * 128;
+  const int64_t ku = base + (int64_t)u * ld;
+  const float k1 = k[ku + lane], k2 = k[ku + lane + 64];
+  const float v1 = v[ku + lane], v2 = v[ku + lane + 64];
+  float ak1 = 0.f, ak2 = 0.f, av1 = 0.f, av2 = 0.f;
+  for (int t = u; t < T; ++t) {
+    const int64_t qt = base + (int64_t)t * ld;
+    const int64_t ot = ((int64_t)b * T + t) * ldo + h * 128;
+    const float q1 = q[qt + lane], q2 = q[qt + lane + 64];
+    const float g1 = dO[ot + lane], g2 = dO[ot + lane + 64];
+    const float s = wave_sum(q1 * k1 + q2 * k2) * scale;
+    const float p = expf(s - lse[(int64_t)bh * T + t]);
+    const float dp = wave_sum(g1 * v1 + g2 * v2);
+    const float ds = p * (dp - Dv[(int64_t)bh * T + t]);
+    av1 += p * g1;
+    av2 += p * g2;
+    ak1 += ds * q1;
+    ak2 += ds * q2;
+  }
+  const int64_t dd = ((int64_t)b * T + u) * ldd + h * 128;
+  dk[dd + lane] = ak1 * scale;
+  dk[dd + lane + 64] = ak2 * scale;
+  dv[dd + lane] = av1;
+  dv[dd + lane + 64] = av2;
+}
+
+}  // namespace
+
+hipError_t nc_attn_fwd(int dtype, const void* q, const void* k, const void* v, int64_t ld,
+                       void* o, int64_t ldo, float* lse, int B, int T, int H, hipStream_t st) {
+  const float scale = 1.0f / sqrtf(128.f);
+  if (dtype) {
+    if (T % 128) return hipErrorInvalidValue;
+    attn_fwd_kernel<<<B * H * (T / 128), 256, 0, st>>>((const bf16*)q, (const bf16*)k,
+                                                        (const bf16*)v, ld, (bf16*)o, ldo, lse,
+                                                        T, H, scale * kLog2e);
+  } else {
+    attn_fwd_f32_kernel<<<ceil_div(B * H * T, 4), 256, 0, st>>>(
+        (const float*)q, (const float*)k, (const float*)v, ld, (float*)o, ldo, lse, B, T, H, scale);
+  }
+  return hipGetLastError();
+}
+
+hipError_t nc_attn_bwd(int dtype, const void* q, const void* k, const void* v, int64_t ld,
+                       const void* dO, int64_t ldo, const float* lse, const float* D, void* dq,
+                       void* dk, void* dv, int64_t ldd, int B, int T, int H, hipStream_t st) {
+  const float scale = 1.0f / sqrtf(128.f);
+  if (dtype) {
+    if (T % 128) return hipErrorInvalidValue;
+    const int grid = B * H * (T / 128);
+    attn_bwd_dkv_kernel<<<grid, 256, 0, st>>>((const bf16*)q, (const bf16*)k, (const bf16*)v, ld,
+                                              (const bf16*)dO, ldo, lse, D, (bf16*)dk, (bf16*)dv,
+                                              ldd, T, H, scale * kLog2e, scale);
+    attn_bwd_dq_kernel<<<grid, 256, 0, st>>>((const bf16*)q, (const bf16*)k, (const bf16*)v, ld,
+                                             (const bf16*)dO, ldo, lse, D, (bf16*)dq, ldd, T, H,
+                                             scale * kLog2e, scale);
+  } else {
+    const int grid = ceil_div(B * H * T, 4);
+    attn_bwd_dq_f32_kernel<<<grid, 256, 0, st>>>((const float*)q, (const float*)k, (const float*)v,
+                                                 ld, (const float*)dO, ldo, lse, D, (float*)dq, ldd,
+                                                 B, T, H, scale);
+    attn_bwd_dkv_f32_kernel<<<grid, 256, 0, st>>>((const float*)q, (const float*)k, (const float*)v,
+                                                  ld, (const float*)dO, ldo, lse, D, (float*)dk,
+                                                  (float*)dv, ldd, B, T, H, scale);
+  }
+  return hipGetLastError();
+}

@@ -1,0 +1,713 @@
+// Memory-bound kernels of the GPT step: embedding (forward and deterministic
+// sort-based backward), RMSNorm, QK-norm + rotary, softmax cross-entropy,
+// attention's D = rowsum(dO*O), AdamW, the Muon elementwise parts and utilities.
+//
+// All of them stream rows with 16-byte (or wider) accesses, one wave or one
+// workgroup per row, fp32 arithmetic, and write the activation type (fp32 or
+// bf16) only where a GEMM consumes the result.
+#include "kernels.h"
+
+namespace {
+
+template <typename T> struct Vec4;
+template <> struct Vec4<float> {
+  NC_DEV static void load(const float* p, float o[4]) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+  }
+  NC_DEV static void store(float* p, const float o[4]) {
+    *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
+  }
+};
+template <> struct Vec4<bf16> {
+  NC_DEV static void load(const bf16* p, float o[4]) {
+    const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+    o[0] = (float)v[0]; o[1] = (float)v[1]; o[2] = (float)v[2]; o[3] = (float)v[3];
+  }
+  NC_DEV static void store(bf16* p, const float o[4]) {
+    bf16x4 v;
+    v[0] = (bf16)o[0]; v[1] = (bf16)o[1]; v[2] = (bf16)o[2]; v[3] = (bf16)o[3];
+    *reinterpret_cast<bf16x4*>(p) = v;
+  }
+};
+
+// ---------------------------------------------------------------- embedding
+__global__ void embed_fwd_kernel(const int32_t* __restrict__ tok, const float* __restrict__ E,
+                                 float* __restrict__ x, int n_tok, int d, int V) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= n_tok) return;
+  const int lane = threadIdx.x & 63;
+  const float* src = E + (int64_t)clamp_id(tok[row], V) * d;
+  float* dst = x + (int64_t)row * d;
+  for (int i = lane * 4; i < d; i += 256)
+    *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(src + i);
+}
+
+// (1) per group of 256 tokens: histogram of ids, written out for every id
+__global__ __launch_bounds__(256) void embed_hist_kernel(const int32_t* __restrict__ tok,
+                                                         int n_tok, int V,
+                                                         int32_t* __restrict__ counts) {
+  extern __shared__ int32_t hist[];
+  const int g = blockIdx.x;
+  for (int v = threadIdx.x; v < V; v += 256) hist[v] = 0;
+  __syncthreads();
+  const int n = g * 256 + threadIdx.x;
+  if (n < n_tok) atomicAdd(&hist[clamp_id(tok[n], V)], 1);
+  __syncthreads();
+  for (int v = threadIdx.x; v < V; v += 256) counts[(int64_t)g * V + v] = hist[v];
+}
+
+// (2) per id: exclusive prefix over groups (in place) and the id's total
+__global__ void embed_colscan_kernel(int32_t* __restrict__ counts, int G, int V,
+                                     int32_t* __restrict__ total) {
+  const int v = blockIdx.x * blockDim.x + threadIdx.x;
+  if (v >= V) return;
+  int run = 0;
+  for (int g = 0; g < G; ++g) {
+    const int c = counts[(int64_t)g * V + v];
+    counts[(int64_t)g * V + v] = run;
+    run += c;
+  }
+  total[v] = run;
+}
+
+// (3) exclusive scan of totals over ids (one workgroup of 1024 threads)
+__global__ __launch_bounds__(1024) void embed_scan_kernel(const int32_t* __restrict__ total,
+                                                          int V, int32_t* __restrict__ start) {
+  __shared__ int32_t part[1024];
+  const int per = ceil_div(V, 1024);
+  const int b = threadIdx.x * per;
+  int s = 0;
+  for (int i = 0; i < per; ++i) s += (b + i < V) ? total[b + i] : 0;
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int add = threadIdx.x >= o ? part[threadIdx.x - o] : 0;
+    __syncthreads();
+    part[threadIdx.x] += add;
+    __syncthreads();
+  }
+  int run = part[threadIdx.x] - s;
+  for (int i = 0; i < per; ++i)
+    if (b + i < V) { start[b + i] = run; run += total[b + i]; }
+}
+
+// (4) stable scatter of token positions into id order
+__global__ __launch_bounds__(256) void embed_scatter_kernel(const int32_t* __restrict__ tok,
+                                                            int n_tok, int V,
+                                                            const int32_t* __restrict__ counts,
+                                                            const int32_t* __restrict__ start,
+                                                            int32_t* __restrict__ sorted) {
+  __shared__ int32_t ids[256];
+  const int g = blockIdx.x;
+  const int n = g * 256 + threadIdx.x;
+  ids[threadIdx.x] = n < n_tok ? clamp_id(tok[n], V) : -1;
+  __syncthreads();
+  if (n >= n_tok) return;
+  const int v = ids[threadIdx.x];
+  int rank = 0;
+  for (int t = 0; t < (int)threadIdx.x; ++t) rank += (ids[t] == v);
+  sorted[start[v] + counts[(int64_t)g * V + v] + rank] = n;
+}
+
+constexpr int kEmbChunk = 64;
+
+// (5) per chunk of 64 sorted positions: sum the rows of each run of equal ids.
+// A run that is a whole segment goes straight into dE; a piece of a longer
+// segment goes to partial[chunk][slot] (slot 0: run begins the chunk, 1: not).
+__global__ __launch_bounds__(256) void embed_segsum_kernel(
+    const int32_t* __restrict__ tok, const int32_t* __restrict__ sorted,
+    const int32_t* __restrict__ start, const int32_t* __restrict__ total,
+    const float* __restrict__ dx, float* __restrict__ dE, float* __restrict__ partial,
+    int n_tok, int d, int V) {
+  __shared__ int32_t rows[kEmbChunk], ids[kEmbChunk];
+  const int c = blockIdx.x;
+  const int p0 = c * kEmbChunk;
+  const int cnt = min(kEmbChunk, n_tok - p0);
+  if (threadIdx.x < cnt) {
+    rows[threadIdx.x] = sorted[p0 + threadIdx.x];
+    ids[threadIdx.x] = clamp_id(tok[rows[threadIdx.x]], V);
+  }
+  __syncthreads();
+  constexpr int MAXC = 8;  // columns per thread: d <= 2048
+  int rs = 0;
+  while (rs < cnt) {
+    const int v = ids[rs];
+    int re = rs + 1;
+    while (re < cnt && ids[re] == v) ++re;
+    float acc[MAXC];
+#pragma unroll
+    for (int k = 0; k < MAXC; ++k) acc[k] = 0.f;
+    for (int p = rs; p < re; ++p) {
+      const float* src = dx + (int64_t)rows[p] * d;
+#pragma unroll
+      for (int k = 0; k < MAXC; ++k) {
+        const int j = threadIdx.x + k * 256;
+        if (j < d) acc[k] += src[j];
+      }
+    }
+    const int gs = p0 + rs, ge = p0 + re;
+    const bool whole = (start[v] == gs) && (start[v] + total[v] == ge);
+    float* dst = whole ? dE + (int64_t)v * d
+                       : partial + ((int64_t)c * 2 + (rs == 0 ? 0 : 1)) * d;
+#pragma unroll
+    for (int k = 0; k < MAXC; ++k) {
+      const int j = threadIdx.x + k * 256;
+      if (j < d) {
+        if (whole) dst[j] += acc[k]; else dst[j] = acc[k];
+      }
+    }
+    rs = re;
+  }
+}
+
+// (6) ids whose segment spans several chunks: add the pieces in chunk order
+__global__ __launch_bounds__(256) void embed_fixup_kernel(const int32_t* __restrict__ start,
+                                                          const int32_t* __restrict__ total,
+                                                          const float* __restrict__ partial,
+                                                          float* __restrict__ dE, int V, int d) {
+  const int v = blockIdx.x;
+  const int s = start[v], len = total[v];
+  if (len == 0) return;
+  const int c0 = s / kEmbChunk, c1 = (s + len - 1) / kEmbChunk;
+  if (c0 == c1) return;
+  for (int j = threadIdx.x; j < d; j += 256) {
+    float acc = partial[((int64_t)c0 * 2 + ((s % kEmbChunk) == 0 ? 0 : 1)) * d + j];
+    for (int c = c0 + 1; c <= c1; ++c) acc += partial[((int64_t)c * 2) * d + j];
+    dE[(int64_t)v * d + j] += acc;
+  }
+}
+
+// ------------------------------------------------------------------ RMSNorm
+constexpr int kMaxVec = 8;  // float4 per lane: d <= 2048
+
+template <typename T>
+__global__ void rmsnorm_fwd_kernel(const float* __restrict__ x, T* __restrict__ y,
+                                   float* __restrict__ r, int rows, int d, float eps) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const float* xr = x + (int64_t)row * d;
+  float v[kMaxVec][4];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMaxVec; ++k) {
+    const int i = (lane + k * 64) * 4;
+    if (i < d) {
+      Vec4<float>::load(xr + i, v[k]);
+      ss += v[k][0] * v[k][0] + v[k][1] * v[k][1] + v[k][2] * v[k][2] + v[k][3] * v[k][3];
+    }
+  }
+  ss = wave_sum(ss);
+  const float rs = 1.0f / sqrtf(ss / d + eps);
+  if (lane == 0) r[row] = rs;
+  T* yr = y + (int64_t)row * d;
+#pragma unroll
+  for (int k = 0; k < kMaxVec; ++k) {
+    const int i = (lane + k * 64) * 4;
+    if (i < d) {
+      float o[4] = {v[k][0] * rs, v[k][1] * rs, v[k][2] * rs, v[k][3] * rs};
+      Vec4<T>::store(yr + i, o);
+    }
+  }
+}
+
+template <typename T>
+__global__ void rmsnorm_bwd_kernel(const float* __restrict__ dy, const T* __restrict__ y,
+                                   const float* __restrict__ r, float* __restrict__ dx,
+                                   T* __restrict__ dxT, int rows, int d, int accumulate) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t off = (int64_t)row * d;
+  float g[kMaxVec][4], yy[kMaxVec][4];
+  float dot = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMaxVec; ++k) {
+    const int i = (lane + k * 64) * 4;
+    if (i < d) {
+      Vec4<float>::load(dy + off + i, g[k]);
+      Vec4<T>::load(y + off + i, yy[k]);
+      dot += g[k][0] * yy[k][0] + g[k][1] * yy[k][1] + g[k][2] * yy[k][2] + g[k][3] * yy[k][3];
+    }
+  }
+  const float mean = wave_sum(dot) / d;
+  const float rs = r[row];
+#pragma unroll
+  for (int k = 0; k < kMaxVec; ++k) {
+    const int i = (lane + k * 64) * 4;
+    if (i < d) {
+      float o[4];
+      if (accumulate) Vec4<float>::load(dx + off + i, o);
+      else o[0] = o[1] = o[2] = o[3] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] += rs * (g[k][e] - yy[k][e] * mean);
+      Vec4<float>::store(dx + off + i, o);
+      Vec4<T>::store(dxT + off + i, o);
+    }
+  }
+}
+
+// ------------------------------------------------------- QK-norm + rotary
+// One wave per (token, head) of the 2H q/k heads; lane l owns the rotary pair
+// (l, l+64) of the 128-dim head.
+template <typename T>
+__global__ void qk_norm_rope_fwd_kernel(T* __restrict__ qkv, float* __restrict__ rqk,
+                                        const float* __restrict__ cs, int n_tok, int Tlen,
+                                        int H, float eps) {
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= n_tok * 2 * H) return;
+  const int lane = threadIdx.x & 63;
+  const int n = item / (2 * H), j = item % (2 * H);
+  T* p = qkv + (int64_t)n * (3 * H * 128) + j * 128;
+  const float x1 = to_f(p[lane]), x2 = to_f(p[lane + 64]);
+  const float rs = 1.0f / sqrtf(wave_sum(x1 * x1 + x2 * x2) / 128.f + eps);
+  const int t = n % Tlen;
+  const float c = cs[t * 64 + lane], s = cs[Tlen * 64 + t * 64 + lane];
+  const float y1 = x1 * rs, y2 = x2 * rs;
+  p[lane] = to_t<T>(y1 * c - y2 * s);
+  p[lane + 64] = to_t<T>(y1 * s + y2 * c);
+  if (lane == 0) rqk[item] = rs;
+}
+
+template <typename T>
+__global__ void qk_norm_rope_bwd_kernel(T* __restrict__ dqkv, const T* __restrict__ qkv,
+                                        const float* __restrict__ rqk,
+                                        const float* __restrict__ cs, int n_tok, int Tlen,
+                                        int H) {
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= n_tok * 2 * H) return;
+  const int lane = threadIdx.x & 63;
+  const int n = item / (2 * H), j = item % (2 * H);
+  const int64_t off = (int64_t)n * (3 * H * 128) + j * 128;
+  const int t = n % Tlen;
+  const float c = cs[t * 64 + lane], s = cs[Tlen * 64 + t * 64 + lane];
+  // normalised pre-rotation vector, recovered by the inverse rotation
+  const float o1 = to_f(qkv[off + lane]), o2 = to_f(qkv[off + lane + 64]);
+  const float y1 = o1 * c + o2 * s, y2 = -o1 * s + o2 * c;
+  const float g1 = to_f(dqkv[off + lane]), g2 = to_f(dqkv[off + lane + 64]);
+  const float dy1 = g1 * c + g2 * s, dy2 = -g1 * s + g2 * c;
+  const float mean = wave_sum(dy1 * y1 + dy2 * y2) / 128.f;
+  const float rs = rqk[item];
+  dqkv[off + lane] = to_t<T>(rs * (dy1 - y1 * mean));
+  dqkv[off + lane + 64] = to_t<T>(rs * (dy2 - y2 * mean));
+}
+
+template <typename T>
+__global__ void attn_bwd_pre_kernel(const T* __restrict__ o, const T* __restrict__ dO,
+                                    int64_t ld, float* __restrict__ D, int B, int Tlen, int H) {
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= B * Tlen * H) return;
+  const int lane = threadIdx.x & 63;
+  const int n = item / H, h = item % H;
+  const int64_t off = (int64_t)n * ld + h * 128;
+  float s = to_f(o[off + lane]) * to_f(dO[off + lane]) +
+            to_f(o[off + lane + 64]) * to_f(dO[off + lane + 64]);
+  s = wave_sum(s);
+  const int b = n / Tlen, t = n % Tlen;
+  if (lane == 0) D[((int64_t)b * H + h) * Tlen + t] = s;
+}
+
+// ------------------------------------------------------------ cross-entropy
+template <typename T>
+__global__ __launch_bounds__(256) void cross_entropy_kernel(
+    const float* __restrict__ z, const int32_t* __restrict__ tgt, T* __restrict__ dz,
+    float* __restrict__ loss_rows, int V, float scale) {
+  __shared__ float red[4];
+  const int row = blockIdx.x;
+  const float* zr = z + (int64_t)row * V;
+  float m = -INFINITY, s = 0.f;
+  for (int i = threadIdx.x * 4; i < V; i += 1024) {
+    float v[4];
+    Vec4<float>::load(zr + i, v);
+    const float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+    const float mn = fmaxf(m, mx);
+    s = s * __expf(m - mn) + __expf(v[0] - mn) + __expf(v[1] - mn) + __expf(v[2] - mn) +
+        __expf(v[3] - mn);
+    m = mn;
+  }
+  const float M = block_max(m, red);
+  const float S = block_sum(m == -INFINITY ? 0.f : s * __expf(m - M), red);
+  const float lse = M + logf(S);
+  const int y = clamp_id(tgt[row], V);
+  if (threadIdx.x == 0) loss_rows[row] = lse - zr[y];
+  T* dr = dz + (int64_t)row * V;
+  for (int i = threadIdx.x * 4; i < V; i += 1024) {
+    float v[4];
+    Vec4<float>::load(zr + i, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = scale * (__expf(v[e] - lse) - (i + e == y ? 1.f : 0.f));
+    Vec4<T>::store(dr + i, v);
+  }
+}
+
+__global__ __launch_bounds__(1024) void sum_scaled_kernel(const float* __restrict__ vals, int n,
+                                                          float scale, float* out) {
+  __shared__ float red[16];
+  float s = 0.f;
+  for (int i = threadIdx.x; i < n; i += 1024) s += vals[i];
+  s = block_sum(s, red);
+  if (threadIdx.x == 0) out[0] = s * scale;
+}
+
+// --------------------------------------------------------------- utilities
+__global__ void fill_kernel(float* p, float v, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+template <typename T>
+__global__ void convert_kernel(const float* __restrict__ s, T* __restrict__ d, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    d[i] = to_t<T>(s[i]);
+}
+
+// Philox4x32-10 (Salmon et al., SC'11) counter-based generator + Box-Muller.
+NC_DEV void philox4x32(uint32_t ctr[4], uint32_t key[2]) {
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * ctr[0];
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * ctr[2];
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ ctr[1] ^ key[0];
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ ctr[3] ^ key[1];
+    ctr[0] = n0; ctr[1] = (uint32_t)p1; ctr[2] = n2; ctr[3] = (uint32_t)p0;
+    key[0] += 0x9E3779B9u; key[1] += 0xBB67AE85u;
+  }
+}
+
+__global__ void init_normal_kernel(float* p, size_t n, uint64_t seed, uint64_t offset,
+                                   float std) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const uint64_t c = offset + i;
+    uint32_t ctr[4] = {(uint32_t)c, (uint32_t)(c >> 32), 0u, 0u};
+    uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    philox4x32(ctr, key);
+    const float u1 = ((ctr[0] >> 8) + 1) * (1.0f / 16777217.0f);   // (0, 1]
+    const float u2 = (ctr[1] >> 8) * (1.0f / 16777216.0f);         // [0, 1)
+    p[i] = std * sqrtf(-2.f * logf(u1)) * cosf(6.283185307179586f * u2);
+  }
+}
+
+__global__ void check_finite_kernel(const float* p, size_t n, int32_t* flag) {
+  int bad = 0;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    bad |= !isfinite(p[i]);
+  if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(flag, 1);
+}
+
+// --------------------------------------------------------------- optimizers
+__global__ void adamw_kernel(float* __restrict__ p, const float* __restrict__ g,
+                             float* __restrict__ m, float* __restrict__ v, size_t n,
+                             size_t n_first, float lr0, float lr1, float b1, float b2, float eps,
+                             float wd, float bc1, float bc2, bf16* __restrict__ shadow,
+                             size_t shadow_from) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const float lr = i < n_first ? lr0 : lr1;
+    const float gi = g[i];
+    const float mi = b1 * m[i] + (1.f - b1) * gi;
+    const float vi = b2 * v[i] + (1.f - b2) * gi * gi;
+    m[i] = mi;
+    v[i] = vi;
+    const float pi = p[i] * (1.f - lr * wd) - lr * (mi / bc1) / (sqrtf(vi / bc2) + eps);
+    p[i] = pi;
+    if (shadow && i >= shadow_from) shadow[i - shadow_from] = (bf16)pi;
+  }
+}
+
+__global__ void momentum_kernel(float* __restrict__ M, const float* __restrict__ G, size_t n,
+                                float mu) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    M[i] = mu * M[i] + G[i];
+}
+
+__global__ void nesterov_kernel(const float* __restrict__ M, const float* __restrict__ G,
+                                float* __restrict__ U, size_t n, float mu) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    U[i] = G[i] + mu * M[i];
+}
+
+__global__ __launch_bounds__(256) void frob_partial_kernel(const float* __restrict__ src,
+                                                           MatBatch mb, int64_t elems,
+                                                           float* __restrict__ partial) {
+  __shared__ float red[4];
+  const int i = blockIdx.y;
+  const float* s = src + mb.off(i);
+  float acc = 0.f;
+  for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < elems; e += (int64_t)gridDim.x * 256) {
+    const float v = s[e];
+    acc += v * v;
+  }
+  acc = block_sum(acc, red);
+  if (threadIdx.x == 0) partial[(int64_t)i * 256 + blockIdx.x] = acc;
+}
+
+__global__ void frob_final_kernel(const float* __restrict__ partial, int parts, int count,
+                                  float* __restrict__ norms) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= count) return;
+  float s = 0.f;
+  for (int k = 0; k < parts; ++k) s += partial[(int64_t)i * 256 + k];
+  norms[i] = sqrtf(s);
+}
+
+// src [R, C] fp32 -> X = act(src / (norm + eps)), [R, C] or transposed [C, R]
+template <typename T>
+__global__ __launch_bounds__(256) void ns_prepare_kernel(const float* __restrict__ src,
+                                                         MatBatch mb, int R, int C,
+                                                         const float* __restrict__ norms,
+                                                         float eps, int transpose,
+                                                         T* __restrict__ X, int64_t x_stride) {
+  __shared__ float tile[32][33];
+  const int i = blockIdx.z;
+  const float sc = 1.f / (norms[i] + eps);
+  const float* s = src + mb.off(i);
+  T* x = X + (int64_t)i * x_stride;
+  const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+  for (int k = ty; k < 32; k += 8) {
+    const int r = r0 + k, c = c0 + tx;
+    tile[k][tx] = (r < R && c < C) ? s[(int64_t)r * C + c] * sc : 0.f;
+  }
+  __syncthreads();
+  for (int k = ty; k < 32; k += 8) {
+    if (!transpose) {
+      const int r = r0 + k, c = c0 + tx;
+      if (r < R && c < C) x[(int64_t)r * C + c] = to_t<T>(tile[k][tx]);
+    } else {
+      const int c = c0 + k, r = r0 + tx;   // output row c, column r
+      if (r < R && c < C) x[(int64_t)c * R + r] = to_t<T>(tile[tx][k]);
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void ns_apply_kernel(float* __restrict__ W, MatBatch mb,
+                                                       int R, int C,
+                                                       const T* __restrict__ X,
+                                                       int64_t x_stride, int transpose,
+                                                       float lr, float wd,
+                                                       bf16* __restrict__ shadow) {
+  __shared__ float tile[32][33];
+  const int i = blockIdx.z;
+  float* w = W + mb.off(i);
+  const T* x = X + (int64_t)i * x_stride;
+  const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  if (transpose) {   // X is [C, R]: stage a 32x32 block transposed
+    for (int k = ty; k < 32; k += 8) {
+      const int c = c0 + k, r = r0 + tx;
+      tile[tx][k] = (r < R && c < C) ? to_f(x[(int64_t)c * R + r]) : 0.f;
+    }
+    __syncthreads();
+  }
+  for (int k = ty; k < 32; k += 8) {
+    const int r = r0 + k, c = c0 + tx;
+    if (r < R && c < C) {
+      const int64_t off = (int64_t)r * C + c;
+      const float u = transpose ? tile[k][tx] : to_f(x[off]);
+      const float nw = w[off] * (1.f - lr * wd) - lr * u;
+      w[off] = nw;
+      if (shadow) shadow[mb.off(i) + off] = (bf16)nw;
+    }
+  }
+}
+
+inline int grid1d(size_t n, int block = 256) {
+  return (int)std::min<size_t>((n + block - 1) / block, 1 << 16);
+}
+
+}  // namespace
+
+// =============================================================== launchers
+hipError_t nc_embed_fwd(const int32_t* tok, const float* E, float* x, int n_tok, int d, int V,
+                        hipStream_t st) {
+  embed_fwd_kernel<<<ceil_div(n_tok, 4), 256, 0, st>>>(tok, E, x, n_tok, d, V);
+  return hipGetLastError();
+}
+
+size_t nc_embed_bwd_scratch_bytes(int n_tok, int vocab, int d) {
+  const size_t G = (size_t)ceil_div(n_tok, 256);
+  const size_t chunks = (size_t)ceil_div(n_tok, kEmbChunk);
+  size_t b = 0;
+  b += G * vocab * 4;          // counts / per-group offsets
+  b += (size_t)vocab * 4 * 2;  // total, start
+  b += (size_t)n_tok * 4;      // sorted
+  b = (b + 255) & ~(size_t)255;
+  b += chunks * 2 * d * 4;     // partial sums
+  return b + 256;
+}
+
+hipError_t nc_embed_bwd(const int32_t* tok, const float* dx, float* dE, int n_tok, int V, int d,
+                        void* scratch, hipStream_t st) {
+  if (n_tok <= 0) return hipSuccess;
+  const int G = ceil_div(n_tok, 256);
+  const int chunks = ceil_div(n_tok, kEmbChunk);
+  char* s = static_cast<char*>(scratch);
+  int32_t* counts = reinterpret_cast<int32_t*>(s);
+  s += (size_t)G * V * 4;
+  int32_t* total = reinterpret_cast<int32_t*>(s);
+  s += (size_t)V * 4;
+  int32_t* start = reinterpret_cast<int32_t*>(s);
+  s += (size_t)V * 4;
+  int32_t* sorted = reinterpret_cast<int32_t*>(s);
+  s += (size_t)n_tok * 4;
+  const size_t used = s - static_cast<char*>(scratch);
+  float* partial = reinterpret_cast<float*>(static_cast<char*>(scratch) + ((used + 255) & ~(size_t)255));
+  static bool lds_opt_in = false;
+  if (!lds_opt_in) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(embed_hist_kernel),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, 32768 * 4);
+    lds_opt_in = true;
+  }
+  embed_hist_kernel<<<G, 256, (size_t)V * 4, st>>>(tok, n_tok, V, counts);
+  embed_colscan_kernel<<<ceil_div(V, 256), 256, 0, st>>>(counts, G, V, total);
+  embed_scan_kernel<<<1, 1024, 0, st>>>(total, V, start);
+  embed_scatter_kernel<<<G, 256, 0, st>>>(tok, n_tok, V, counts, start, sorted);
+  embed_segsum_kernel<<<chunks, 256, 0, st>>>(tok, sorted, start, total, dx, dE, partial, n_tok, d, V);
+  embed_fixup_kernel<<<V, 256, 0, st>>>(start, total, partial, dE, V, d);
+  return hipGetLastError();
+}
+
+hipError_t nc_rmsnorm_fwd(int dtype, const float* x, void* y, float* r, int rows, int d,
+                          float eps, hipStream_t st) {
+  const int g = ceil_div(rows, 4);
+  if (dtype) rmsnorm_fwd_kernel<bf16><<<g, 256, 0, st>>>(x, (bf16*)y, r, rows, d, eps);
+  else rmsnorm_fwd_kernel<float><<<g, 256, 0, st>>>(x, (float*)y, r, rows, d, eps);
+  return hipGetLastError();
+}
+
+hipError_t nc_rmsnorm_bwd(int dtype, const float* dy, const void* y, const float* r, float* dx,
+                          void* dxT, int rows, int d, int accumulate, hipStream_t st) {
+  const int g = ceil_div(rows, 4);
+  if (dtype)
+    rmsnorm_bwd_kernel<bf16><<<g, 256, 0, st>>>(dy, (const bf16*)y, r, dx, (bf16*)dxT, rows, d, accumulate);
+  else
+    rmsnorm_bwd_kernel<float><<<g, 256, 0, st>>>(dy, (const float*)y, r, dx, (float*)dxT, rows, d, accumulate);
+  return hipGetLastError();
+}
+
+hipError_t nc_qk_norm_rope_fwd(int dtype, void* qkv, float* rqk, const float* cs, int n_tok,
+                               int T, int H, float eps, hipStream_t st) {
+  const int g = ceil_div(n_tok * 2 * H, 4);
+  if (dtype) qk_norm_rope_fwd_kernel<bf16><<<g, 256, 0, st>>>((bf16*)qkv, rqk, cs, n_tok, T, H, eps);
+  else qk_norm_rope_fwd_kernel<float><<<g, 256, 0, st>>>((float*)qkv, rqk, cs, n_tok, T, H, eps);
+  return hipGetLastError();
+}
+
+hipError_t nc_qk_norm_rope_bwd(int dtype, void* dqkv, const void* qkv, const float* rqk,
+                               const float* cs, int n_tok, int T, int H, hipStream_t st) {
+  const int g = ceil_div(n_tok * 2 * H, 4);
+  if (dtype)
+    qk_norm_rope_bwd_kernel<bf16><<<g, 256, 0, st>>>((bf16*)dqkv, (const bf16*)qkv, rqk, cs, n_tok, T, H);
+  else
+    qk_norm_rope_bwd_kernel<float><<<g, 256, 0, st>>>((float*)dqkv, (const float*)qkv, rqk, cs, n_tok, T, H);
+  return hipGetLastError();
+}
+
+hipError_t nc_attn_bwd_pre(int dtype, const void* o, const void* dO, int64_t ld, float* D,
+                           int B, int T, int H, hipStream_t st) {
+  const int g = ceil_div(B * T * H, 4);
+  if (dtype) attn_bwd_pre_kernel<bf16><<<g, 256, 0, st>>>((const bf16*)o, (const bf16*)dO, ld, D, B, T, H);
+  else attn_bwd_pre_kernel<float><<<g, 256, 0, st>>>((const float*)o, (const float*)dO, ld, D, B, T, H);
+  return hipGetLastError();
+}
+
+hipError_t nc_cross_entropy(int dtype, const float* z, const int32_t* tgt, void* dz,
+                            float* loss_rows, int rows, int V, float scale, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (dtype) cross_entropy_kernel<bf16><<<rows, 256, 0, st>>>(z, tgt, (bf16*)dz, loss_rows, V, scale);
+  else cross_entropy_kernel<float><<<rows, 256, 0, st>>>(z, tgt, (float*)dz, loss_rows, V, scale);
+  return hipGetLastError();
+}
+
+hipError_t nc_sum_scaled(const float* vals, int n, float scale, float* out, hipStream_t st) {
+  sum_scaled_kernel<<<1, 1024, 0, st>>>(vals, n, scale, out);
+  return hipGetLastError();
+}
+
+hipError_t nc_fill_f32(float* p, float v, size_t n, hipStream_t st) {
+  if (!n) return hipSuccess;
+  fill_kernel<<<grid1d(n), 256, 0, st>>>(p, v, n);
+  return hipGetLastError();
+}
+
+hipError_t nc_convert_f32(int dtype, const float* src, void* dst, size_t n, hipStream_t st) {
+  if (!n) return hipSuccess;
+  if (dtype) convert_kernel<bf16><<<grid1d(n), 256, 0, st>>>(src, (bf16*)dst, n);
+  else convert_kernel<float><<<grid1d(n), 256, 0, st>>>(src, (float*)dst, n);
+  return hipGetLastError();
+}
+
+hipError_t nc_init_normal(float* p, size_t n, uint64_t seed, uint64_t offset, float std,
+                          hipStream_t st) {
+  if (!n) return hipSuccess;
+  init_normal_kernel<<<grid1d(n), 256, 0, st>>>(p, n, seed, offset, std);
+  return hipGetLastError();
+}
+
+hipError_t nc_check_finite(const float* p, size_t n, int32_t* flag, hipStream_t st) {
+  if (!n) return hipSuccess;
+  check_finite_kernel<<<grid1d(n), 256, 0, st>>>(p, n, flag);
+  return hipGetLastError();
+}
+
+hipError_t nc_adamw(float* p, const float* g, float* m, float* v, size_t n, size_t n_first,
+                    float lr0, float lr1, float b1, float b2, float eps, float wd, float bc1,
+                    float bc2, void* shadow, size_t shadow_from, hipStream_t st) {
+  if (!n) return hipSuccess;
+  adamw_kernel<<<grid1d(n), 256, 0, st>>>(p, g, m, v, n, n_first, lr0, lr1, b1, b2, eps, wd,
+                                          bc1, bc2, (bf16*)shadow, shadow_from);
+  return hipGetLastError();
+}
+
+hipError_t nc_momentum(float* M, const float* G, size_t n, float mu, hipStream_t st) {
+  if (!n) return hipSuccess;
+  momentum_kernel<<<grid1d(n), 256, 0, st>>>(M, G, n, mu);
+  return hipGetLastError();
+}
+
+hipError_t nc_nesterov(const float* M, const float* G, float* U, size_t n, float mu,
+                       hipStream_t st) {
+  if (!n) return hipSuccess;
+  nesterov_kernel<<<grid1d(n), 256, 0, st>>>(M, G, U, n, mu);
+  return hipGetLastError();
+}
+
+hipError_t nc_frob_norms(const float* src, MatBatch mb, int64_t elems, int count,
+                         float* partial, float* norms, hipStream_t st) {
+  if (count <= 0) return hipSuccess;
+  const int parts = (int)std::min<int64_t>(256, ceil_div64(elems, 256));
+  frob_partial_kernel<<<dim3(parts, count), 256, 0, st>>>(src, mb, elems, partial);
+  frob_final_kernel<<<ceil_div(count, 256), 256, 0, st>>>(partial, parts, count, norms);
+  return hipGetLastError();
+}
+
+hipError_t nc_ns_prepare(int dtype, const float* src, MatBatch mb, int R, int C, int count,
+                         const float* norms, float eps, int transpose, void* X, int64_t x_stride,
+                         hipStream_t st) {
+  if (count <= 0) return hipSuccess;
+  dim3 grid(ceil_div(C, 32), ceil_div(R, 32), count);
+  if (dtype)
+    ns_prepare_kernel<bf16><<<grid, 256, 0, st>>>(src, mb, R, C, norms, eps, transpose, (bf16*)X, x_stride);
+  else
+    ns_prepare_kernel<float><<<grid, 256, 0, st>>>(src, mb, R, C, norms, eps, transpose, (float*)X, x_stride);
+  return hipGetLastError();
+}
+
+hipError_t nc_ns_apply(int dtype, float* W, MatBatch mb, int R, int C, int count,
+                       const void* X, int64_t x_stride, int transpose, float lr, float wd,
+                       void* shadow, hipStream_t st) {
+  if (count <= 0) return hipSuccess;
+  dim3 grid(ceil_div(C, 32), ceil_div(R, 32), count);
+  if (dtype)
+    ns_apply_kernel<bf16><<<grid, 256, 0, st>>>(W, mb, R, C, (const bf16*)X, x_stride, transpose, lr, wd, (bf16*)shadow);
+  else
+    ns_apply_kernel<float><<<grid, 256, 0, st>>>(W, mb, R, C, (const float*)X, x_stride, transpose, lr, wd, (bf16*)shadow);
+  return hipGetLastError();
+}

@@ -1,0 +1,39 @@
+// GEMM launch interface: C[M,N] (epilogue) = A[M,K] * B[N,K]^T, fp32 accumulate.
+//
+// Operand layouts (both logical views are "row = output index, col = k"):
+//   A: kKCont -> element (m,k) at A[m*lda + k];  kMNCont -> at A[k*lda + m]
+//   B: kKCont -> element (n,k) at B[n*ldb + k];  kMNCont -> at B[k*ldb + n]
+// This covers the forward products (both K-contiguous), the input gradients
+// (B = weight read as its transpose, N-contiguous) and the weight gradients
+// (both operands token-major, i.e. MN-contiguous).
+#pragma once
+#include "common.h"
+
+enum NcLayout { kKCont = 0, kMNCont = 1 };
+
+enum NcEpi {
+  kEpiStore = 0,      // C = alpha*acc (C of the activation type)
+  kEpiStoreF32 = 1,   // C(f32) = alpha*acc
+  kEpiAccF32 = 2,     // C(f32) += alpha*acc
+  kEpiRelu2 = 3,      // C = acc (pre-activation h), aux_out = max(acc,0)^2
+  kEpiRelu2Bwd = 4,   // C = 2*max(aux_in,0)*acc   (aux_in = stored h)
+  kEpiPoly = 5,       // C = p0*aux_in + p1*acc    (Newton-Schulz: b*A + c*A*A, a*X + B*X)
+};
+
+struct GemmParams {
+  const void* A; const void* B; void* C;
+  const void* aux_in; void* aux_out;
+  int64_t lda, ldb, ldc;             // leading dimensions (elements)
+  int64_t sA, sB, sC;                // batch strides (elements); aux uses sC/ldc
+  int M, N, K, batch;
+  int a_layout, b_layout, epi;
+  float alpha, p0, p1;
+  int splits;                        // split-K count (>1: C must be f32, workspace used)
+  float* workspace; size_t workspace_bytes;
+};
+
+// dtype: 0 = fp32 operands (VALU kernel), 1 = bf16 operands (MFMA kernel)
+hipError_t nc_launch_gemm(int dtype, const GemmParams& p, hipStream_t stream);
+// splits a weight-gradient GEMM would use for M x N with reduction K (bf16 path)
+int nc_gemm_pick_splits(int M, int N, int K);
+size_t nc_gemm_workspace_bytes(int M, int N, int splits);

@@ -1,0 +1,714 @@
+// Host runtime behind the C ABI (include/nc.h, include/nc_ops.h): arena
+// planning, the parameter registry, and the launch sequences of one
+// micro-batch forward/backward and of one optimizer step.
+//
+// Parameter arena (caller-owned, fp32 unless noted), element layout shared by
+// masters, gradients and Muon momenta:
+//   block region: layer l at l*S, S = 4 d^2 + 2 d F:
+//     Wq [d,d] | Wk [d,d] | Wv [d,d] | Wo [d,d] | W1 [F,d] | W2 [d,F]
+//   (Wq|Wk|Wv is one [3d, d] matrix for the QKV product), then E [V,d], Wh [V,d].
+//   regions: masters | grads | Muon momenta (block region) | AdamW m (E|Wh) |
+//   AdamW v (E|Wh) | bf16 copies (block region + Wh; bf16 models only) |
+//   rotary table cos/sin [2][T][64].
+// Activation arena: what the backward pass reads per layer (RMSNorm outputs
+// and reciprocal RMS, q/k/v after QK-norm+rotary, QK-norm reciprocal RMS,
+// attention output and log-sum-exp, MLP pre-activation h and ReLU^2 output
+// g), then scratch (residual stream x and its gradient, lm_head logits of one
+// row chunk, split-K, embedding-sort and Newton-Schulz workspaces).
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "nc.h"
+#include "nc_ops.h"
+#include "gemm.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+struct Layout {
+  size_t cur = 0;
+  size_t take(size_t bytes) {
+    const size_t o = cur;
+    cur += align_up(bytes);
+    return o;
+  }
+};
+
+struct ParamInfo {
+  std::string name;
+  int rows, cols, group;
+  size_t elem;        // element offset in the master/grad layout
+  int64_t adam_elem;  // element offset in the AdamW regions, -1 for Muon
+};
+
+struct LayerAct { size_t a1, r1, qkv, rqk, o, lse, a2, r2, h, g; };
+
+}  // namespace
+
+struct nc_ctx {
+  nc_model_config cfg;
+  nc_optim_config ocfg;
+  int dt;      // 0 fp32, 1 bf16
+  size_t es;   // activation element size
+  int L, d, H, F, V, T, maxB, Nmax, chunk;
+  int64_t S, n_block, n_total;
+  std::vector<ParamInfo> params;
+  // parameter arena byte offsets
+  size_t oP, oG, oM, oAm, oAv, oSh, oTab, param_bytes;
+  // activation arena byte offsets
+  std::vector<LayerAct> la;
+  size_t xf, rf, x, dx, dxT, da, dqkv, dO, Dbuf, dh, z, dz, loss_rows, ws, ws_bytes, emb,
+      nsXs0, nsXs1, nsAs, nsBs, nsXr0, nsXr1, nsAr, nsBr, nsU, frob, norms, act_bytes;
+  int splits_qkv, splits_o, splits_1, splits_2, splits_head;
+  char* pa = nullptr;
+  char* aa = nullptr;
+  hipStream_t st = nullptr;
+  bool bound = false;
+  int64_t step = 0;
+  std::string err;
+};
+
+namespace {
+
+nc_status fail(nc_ctx* c, nc_status s, const std::string& msg) {
+  if (c) c->err = msg;
+  return s;
+}
+
+nc_status hipcheck(nc_ctx* c, hipError_t e, const char* what) {
+  if (e == hipSuccess) return NC_OK;
+  return fail(c, NC_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define NC_TRY(expr, what)                               \
+  do {                                                   \
+    nc_status _s = hipcheck(ctx, (expr), what);          \
+    if (_s != NC_OK) return _s;                          \
+  } while (0)
+
+nc_status validate(const nc_model_config* m, const nc_optim_config* o, std::string& why) {
+  if (!m || !o) { why = "null config"; return NC_ERR_INVALID_ARG; }
+  if (m->n_layer < 0 || m->d_model <= 0 || m->n_head <= 0 || m->d_ff <= 0 || m->vocab <= 0 ||
+      m->seq_len <= 0 || m->max_micro_batch <= 0) {
+    why = "non-positive dimension";
+    return NC_ERR_INVALID_ARG;
+  }
+  if (m->dtype != NC_FP32 && m->dtype != NC_BF16) { why = "dtype"; return NC_ERR_INVALID_ARG; }
+  if (m->head_dim != 128 || m->d_model != m->n_head * 128) {
+    why = "head_dim must be 128 and d_model = n_head * 128";
+    return NC_ERR_UNSUPPORTED;
+  }
+  if (m->d_model > 2048 || m->d_ff % 64 || m->vocab % 64 || m->vocab > 32768) {
+    why = "d_model <= 2048, d_ff and vocab multiples of 64, vocab <= 32768 required";
+    return NC_ERR_UNSUPPORTED;
+  }
+  if (m->dtype == NC_BF16 && m->seq_len % 128) {
+    why = "bf16 attention needs seq_len % 128 == 0";
+    return NC_ERR_UNSUPPORTED;
+  }
+  if (!(m->norm_eps >= 0.f) || !(m->rope_base > 0.f)) { why = "eps/base"; return NC_ERR_INVALID_ARG; }
+  if (o->ns_steps < 0 || o->ns_steps > 8) { why = "ns_steps in [0, 8]"; return NC_ERR_INVALID_ARG; }
+  const int64_t n_tok = (int64_t)m->max_micro_batch * m->seq_len;
+  if (n_tok > (int64_t)1 << 30) { why = "micro-batch too large"; return NC_ERR_UNSUPPORTED; }
+  return NC_OK;
+}
+
+void plan(nc_ctx* c) {
+  const int L = c->L, d = c->d, F = c->F, V = c->V, T = c->T, H = c->H;
+  const size_t es = c->es;
+  c->S = 4LL * d * d + 2LL * d * F;
+  c->n_block = c->S * L;
+  c->n_total = c->n_block + 2LL * V * d;
+  // registry
+  c->params.clear();
+  c->params.push_back({"E", V, d, NC_GROUP_ADAMW, (size_t)c->n_block, 0});
+  const char* names[6] = {"Wq", "Wk", "Wv", "Wo", "W1", "W2"};
+  for (int l = 0; l < L; ++l) {
+    size_t base = (size_t)l * c->S;
+    const int64_t offs[6] = {0, (int64_t)d * d, 2LL * d * d, 3LL * d * d, 4LL * d * d,
+                             4LL * d * d + (int64_t)F * d};
+    const int rows[6] = {d, d, d, d, F, d}, cols[6] = {d, d, d, d, d, F};
+    for (int j = 0; j < 6; ++j)
+      c->params.push_back({std::to_string(l) + "." + names[j], rows[j], cols[j], NC_GROUP_MUON,
+                           base + (size_t)offs[j], -1});
+  }
+  c->params.push_back({"Wh", V, d, NC_GROUP_ADAMW, (size_t)(c->n_block + (int64_t)V * d),
+                       (int64_t)V * d});
+
+  Layout p;
+  c->oP = p.take(c->n_total * 4);
+  c->oG = p.take(c->n_total * 4);
+  c->oM = p.take(c->n_block * 4);
+  c->oAm = p.take(2ULL * V * d * 4);
+  c->oAv = p.take(2ULL * V * d * 4);
+  c->oSh = c->dt ? p.take((c->n_block + (size_t)V * d) * 2) : 0;
+  c->oTab = p.take(2ULL * T * 64 * 4);
+  c->param_bytes = p.cur;
+
+  const size_t N = (size_t)c->Nmax;
+  c->chunk = (int)std::min<size_t>(N, 8192);
+  Layout a;
+  c->la.resize(L);
+  for (int l = 0; l < L; ++l) {
+    LayerAct& x = c->la[l];
+    x.a1 = a.take(N * d * es);
+    x.r1 = a.take(N * 4);
+    x.qkv = a.take(N * 3 * d * es);
+    x.rqk = a.take(N * 2 * H * 4);
+    x.o = a.take(N * d * es);
+    x.lse = a.take(N * H * 4);
+    x.a2 = a.take(N * d * es);
+    x.r2 = a.take(N * 4);
+    x.h = a.take(N * F * es);
+    x.g = a.take(N * F * es);
+  }
+  c->xf = a.take(N * d * es);
+  c->rf = a.take(N * 4);
+  c->x = a.take(N * d * 4);
+  c->dx = a.take(N * d * 4);
+  c->dxT = a.take(N * d * es);
+  c->da = a.take(N * d * 4);
+  c->dqkv = a.take(N * 3 * d * es);
+  c->dO = a.take(N * d * es);
+  c->Dbuf = a.take(N * H * 4);
+  c->dh = a.take(N * F * es);
+  c->z = a.take((size_t)c->chunk * V * 4);
+  c->dz = a.take((size_t)c->chunk * V * es);
+  c->loss_rows = a.take(N * 4);
+  // split-K for the weight-gradient products (bf16 MFMA path)
+  auto sp = [&](int M, int Nn, int K) { return c->dt ? nc_gemm_pick_splits(M, Nn, K) : 1; };
+  c->splits_qkv = sp(3 * d, d, (int)N);
+  c->splits_o = sp(d, d, (int)N);
+  c->splits_1 = sp(F, d, (int)N);
+  c->splits_2 = sp(d, F, (int)N);
+  c->splits_head = sp(V, d, c->chunk);
+  size_t ws = 0;
+  ws = std::max(ws, nc_gemm_workspace_bytes(3 * d, d, c->splits_qkv));
+  ws = std::max(ws, nc_gemm_workspace_bytes(d, d, c->splits_o));
+  ws = std::max(ws, nc_gemm_workspace_bytes(F, d, c->splits_1));
+  ws = std::max(ws, nc_gemm_workspace_bytes(d, F, c->splits_2));
+  ws = std::max(ws, nc_gemm_workspace_bytes(V, d, c->splits_head));
+  c->ws_bytes = ws;
+  c->ws = a.take(std::max<size_t>(ws, 256));
+  c->emb = a.take(nc_embed_bwd_scratch_bytes((int)N, V, d));
+  // Newton-Schulz: 4L square [d,d] and 2L wide [d,F] matrices
+  c->nsXs0 = a.take((size_t)4 * L * d * d * es);
+  c->nsXs1 = a.take((size_t)4 * L * d * d * es);
+  c->nsAs = a.take((size_t)4 * L * d * d * es);
+  c->nsBs = a.take((size_t)4 * L * d * d * es);
+  c->nsXr0 = a.take((size_t)2 * L * d * F * es);
+  c->nsXr1 = a.take((size_t)2 * L * d * F * es);
+  c->nsAr = a.take((size_t)2 * L * d * d * es);
+  c->nsBr = a.take((size_t)2 * L * d * d * es);
+  c->nsU = c->ocfg.muon_nesterov ? a.take((size_t)c->n_block * 4) : 0;
+  c->frob = a.take((size_t)6 * std::max(L, 1) * 256 * 4);
+  c->norms = a.take((size_t)6 * std::max(L, 1) * 4);
+  c->act_bytes = a.cur;
+}
+
+template <typename T = void>
+T* P(nc_ctx* c, size_t off) { return reinterpret_cast<T*>(c->pa + off); }
+template <typename T = void>
+T* A(nc_ctx* c, size_t off) { return reinterpret_cast<T*>(c->aa + off); }
+
+// weight operand of a GEMM: bf16 copy (bf16 models) or the fp32 master
+const void* wptr(nc_ctx* c, size_t elem) {
+  if (c->dt) return c->pa + c->oSh + elem * 2;
+  return c->pa + c->oP + elem * 4;
+}
+
+hipError_t gemm(nc_ctx* c, const void* A_, int64_t lda, int al, const void* B_, int64_t ldb,
+                int bl, void* C_, int64_t ldc, int M, int N, int K, int epi,
+                const void* aux_in = nullptr, void* aux_out = nullptr, int splits = 1,
+                int batch = 1, int64_t sA = 0, int64_t sB = 0, int64_t sC = 0, float p0 = 0.f,
+                float p1 = 0.f) {
+  GemmParams g{};
+  g.A = A_; g.B = B_; g.C = C_; g.aux_in = aux_in; g.aux_out = aux_out;
+  g.lda = lda; g.ldb = ldb; g.ldc = ldc; g.sA = sA; g.sB = sB; g.sC = sC;
+  g.M = M; g.N = N; g.K = K; g.batch = batch;
+  g.a_layout = al; g.b_layout = bl; g.epi = epi;
+  g.alpha = 1.f; g.p0 = p0; g.p1 = p1;
+  g.splits = splits;
+  g.workspace = reinterpret_cast<float*>(c->aa + c->ws);
+  g.workspace_bytes = c->ws_bytes;
+  return nc_launch_gemm(c->dt, g, c->st);
+}
+
+}  // namespace
+
+// =================================================================== C ABI
+extern "C" {
+
+const char* nc_status_str(nc_status s) {
+  switch (s) {
+    case NC_OK: return "ok";
+    case NC_ERR_INVALID_ARG: return "invalid argument";
+    case NC_ERR_UNSUPPORTED: return "unsupported";
+    case NC_ERR_OUT_OF_MEMORY: return "arena too small";
+    case NC_ERR_HIP: return "HIP error";
+    case NC_ERR_STATE: return "bad call order";
+    case NC_ERR_NONFINITE: return "non-finite value";
+  }
+  return "unknown status";
+}
+
+const char* nc_last_error(const nc_ctx* ctx) { return ctx ? ctx->err.c_str() : ""; }
+
+static nc_ctx* make_ctx(const nc_model_config* cfg, const nc_optim_config* ocfg) {
+  nc_ctx* c = new nc_ctx();
+  c->cfg = *cfg;
+  c->ocfg = *ocfg;
+  c->dt = cfg->dtype == NC_BF16 ? 1 : 0;
+  c->es = c->dt ? 2 : 4;
+  c->L = cfg->n_layer; c->d = cfg->d_model; c->H = cfg->n_head; c->F = cfg->d_ff;
+  c->V = cfg->vocab; c->T = cfg->seq_len; c->maxB = cfg->max_micro_batch;
+  c->Nmax = c->maxB * c->T;
+  plan(c);
+  return c;
+}
+
+nc_status nc_plan(const nc_model_config* cfg, const nc_optim_config* ocfg,
+                  size_t* param_arena_bytes, size_t* act_arena_bytes) {
+  try {
+    std::string why;
+    nc_status s = validate(cfg, ocfg, why);
+    if (s != NC_OK) return s;
+    nc_ctx* c = make_ctx(cfg, ocfg);
+    if (param_arena_bytes) *param_arena_bytes = c->param_bytes;
+    if (act_arena_bytes) *act_arena_bytes = c->act_bytes;
+    delete c;
+    return NC_OK;
+  } catch (...) {
+    return NC_ERR_INVALID_ARG;
+  }
+}
+
+nc_status nc_create(const nc_model_config* cfg, const nc_optim_config* ocfg, nc_ctx** out) {
+  if (!out) return NC_ERR_INVALID_ARG;
+  *out = nullptr;
+  try {
+    std::string why;
+    nc_status s = validate(cfg, ocfg, why);
+    if (s != NC_OK) return s;
+    *out = make_ctx(cfg, ocfg);
+    return NC_OK;
+  } catch (...) {
+    return NC_ERR_INVALID_ARG;
+  }
+}
+
+void nc_destroy(nc_ctx* ctx) { delete ctx; }
+
+nc_status nc_bind(nc_ctx* ctx, void* d_param_arena, size_t param_bytes, void* d_act_arena,
+                  size_t act_bytes, void* hip_stream) {
+  if (!ctx || !d_param_arena || !d_act_arena) return fail(ctx, NC_ERR_INVALID_ARG, "null arena");
+  if ((reinterpret_cast<uintptr_t>(d_param_arena) | reinterpret_cast<uintptr_t>(d_act_arena)) %
+      kAlign)
+    return fail(ctx, NC_ERR_INVALID_ARG, "arenas must be 256-byte aligned");
+  if (param_bytes < ctx->param_bytes || act_bytes < ctx->act_bytes)
+    return fail(ctx, NC_ERR_OUT_OF_MEMORY,
+                "arena too small: need " + std::to_string(ctx->param_bytes) + " + " +
+                    std::to_string(ctx->act_bytes) + " bytes");
+  ctx->pa = static_cast<char*>(d_param_arena);
+  ctx->aa = static_cast<char*>(d_act_arena);
+  ctx->st = static_cast<hipStream_t>(hip_stream);
+  // rotary table: angle(t, i) = t * base^(-2i/128), computed in double
+  const int T = ctx->T;
+  std::vector<float> tab(2 * (size_t)T * 64);
+  for (int t = 0; t < T; ++t)
+    for (int i = 0; i < 64; ++i) {
+      const double ang = (double)t * std::pow((double)ctx->cfg.rope_base, -2.0 * i / 128.0);
+      tab[(size_t)t * 64 + i] = (float)std::cos(ang);
+      tab[(size_t)T * 64 + (size_t)t * 64 + i] = (float)std::sin(ang);
+    }
+  NC_TRY(hipMemcpyAsync(ctx->pa + ctx->oTab, tab.data(), tab.size() * 4, hipMemcpyHostToDevice,
+                        ctx->st), "upload rotary table");
+  // gradients and optimizer state start at zero, step count at 0
+  NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oG), 0.f, ctx->n_total, ctx->st), "zero grads");
+  NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oM), 0.f, ctx->n_block, ctx->st), "zero momentum");
+  NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oAm), 0.f, 2ULL * ctx->V * ctx->d, ctx->st), "zero m");
+  NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oAv), 0.f, 2ULL * ctx->V * ctx->d, ctx->st), "zero v");
+  ctx->step = 0;
+  NC_TRY(hipStreamSynchronize(ctx->st), "bind sync");
+  ctx->bound = true;
+  return NC_OK;
+}
+
+static nc_status refresh_shadows(nc_ctx* ctx) {
+  if (!ctx->dt) return NC_OK;
+  NC_TRY(nc_convert_f32(1, P<float>(ctx, ctx->oP), ctx->pa + ctx->oSh, ctx->n_block, ctx->st),
+         "shadow blocks");
+  NC_TRY(nc_convert_f32(1, P<float>(ctx, ctx->oP) + ctx->n_block + (size_t)ctx->V * ctx->d,
+                        ctx->pa + ctx->oSh + ctx->n_block * 2, (size_t)ctx->V * ctx->d, ctx->st),
+         "shadow head");
+  return NC_OK;
+}
+
+nc_status nc_init_params(nc_ctx* ctx, uint64_t seed, float std) {
+  if (!ctx) return NC_ERR_INVALID_ARG;
+  if (!ctx->bound) return fail(ctx, NC_ERR_STATE, "bind first");
+  if (!(std >= 0.f)) return fail(ctx, NC_ERR_INVALID_ARG, "std");
+  NC_TRY(nc_init_normal(P<float>(ctx, ctx->oP), ctx->n_total, seed, 0, std, ctx->st), "init");
+  NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oM), 0.f, ctx->n_block, ctx->st), "zero momentum");
+  NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oAm), 0.f, 2ULL * ctx->V * ctx->d, ctx->st), "zero m");
+  NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oAv), 0.f, 2ULL * ctx->V * ctx->d, ctx->st), "zero v");
+  ctx->step = 0;
+  return refresh_shadows(ctx);
+}
+
+nc_status nc_zero_grads(nc_ctx* ctx) {
+  if (!ctx) return NC_ERR_INVALID_ARG;
+  if (!ctx->bound) return fail(ctx, NC_ERR_STATE, "bind first");
+  NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oG), 0.f, ctx->n_total, ctx->st), "zero grads");
+  return NC_OK;
+}
+
+nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_t B,
+                     float grad_scale, float* d_loss) {
+  if (!ctx) return NC_ERR_INVALID_ARG;
+  if (!ctx->bound) return fail(ctx, NC_ERR_STATE, "bind first");
+  if (!tok || !tgt || !d_loss) return fail(ctx, NC_ERR_INVALID_ARG, "null pointer");
+  if (B < 1 || B > ctx->maxB) return fail(ctx, NC_ERR_INVALID_ARG, "B out of [1, max_micro_batch]");
+  if (!std::isfinite(grad_scale)) return fail(ctx, NC_ERR_INVALID_ARG, "grad_scale");
+  const int dt = ctx->dt, L = ctx->L, d = ctx->d, H = ctx->H, F = ctx->F, V = ctx->V,
+            T = ctx->T;
+  const int N = B * T;
+  const float eps = ctx->cfg.norm_eps;
+  hipStream_t st = ctx->st;
+  const size_t es = ctx->es;
+  float* x = A<float>(ctx, ctx->x);
+  float* dx = A<float>(ctx, ctx->dx);
+  float* da = A<float>(ctx, ctx->da);
+  void* dxT = A(ctx, ctx->dxT);
+  const float* tab = P<float>(ctx, ctx->oTab);
+  float* G = P<float>(ctx, ctx->oG);
+  char* aa = ctx->aa;
+
+  // ---------------------------------------------------------------- forward
+  NC_TRY(nc_embed_fwd(tok, P<float>(ctx, ctx->oP) + ctx->n_block, x, N, d, V, st), "embed");
+  for (int l = 0; l < L; ++l) {
+    const LayerAct& la = ctx->la[l];
+    const size_t wb = (size_t)l * ctx->S;
+    char* qkv = aa + la.qkv;
+    NC_TRY(nc_rmsnorm_fwd(dt, x, aa + la.a1, A<float>(ctx, la.r1), N, d, eps, st), "norm1");
+    NC_TRY(gemm(ctx, aa + la.a1, d, kKCont, wptr(ctx, wb), d, kKCont, qkv, 3 * d, N, 3 * d, d,
+                kEpiStore), "qkv");
+    NC_TRY(nc_qk_norm_rope_fwd(dt, qkv, A<float>(ctx, la.rqk), tab, N, T, H, eps, st), "qknorm");
+    NC_TRY(nc_attn_fwd(dt, qkv, qkv + d * es, qkv + 2 * d * es, 3 * d, aa + la.o, d,
+                       A<float>(ctx, la.lse), B, T, H, st), "attn fwd");
+    NC_TRY(gemm(ctx, aa + la.o, d, kKCont, wptr(ctx, wb + 3ULL * d * d), d, kKCont, x, d, N, d,
+                d, kEpiAccF32), "out proj");
+    NC_TRY(nc_rmsnorm_fwd(dt, x, aa + la.a2, A<float>(ctx, la.r2), N, d, eps, st), "norm2");
+    NC_TRY(gemm(ctx, aa + la.a2, d, kKCont, wptr(ctx, wb + 4ULL * d * d), d, kKCont, aa + la.h,
+                F, N, F, d, kEpiRelu2, nullptr, aa + la.g), "mlp up");
+    NC_TRY(gemm(ctx, aa + la.g, F, kKCont, wptr(ctx, wb + 4ULL * d * d + (size_t)F * d), F,
+                kKCont, x, d, N, d, F, kEpiAccF32), "mlp down");
+  }
+  NC_TRY(nc_rmsnorm_fwd(dt, x, aa + ctx->xf, A<float>(ctx, ctx->rf), N, d, eps, st), "normf");
+
+  // ------------------------------------------- lm_head + cross-entropy, chunked
+  const size_t wh = (size_t)(ctx->n_block + (int64_t)V * d);
+  const float ce_scale = grad_scale / (float)N;
+  for (int c0 = 0; c0 < N; c0 += ctx->chunk) {
+    const int nc = std::min(ctx->chunk, N - c0);
+    const char* xfc = aa + ctx->xf + (size_t)c0 * d * es;
+    NC_TRY(gemm(ctx, xfc, d, kKCont, wptr(ctx, wh), d, kKCont, aa + ctx->z, V, nc, V, d,
+                kEpiStoreF32), "logits");
+    NC_TRY(nc_cross_entropy(dt, A<float>(ctx, ctx->z), tgt + c0, aa + ctx->dz,
+                            A<float>(ctx, ctx->loss_rows) + c0, nc, V, ce_scale, st), "ce");
+    NC_TRY(gemm(ctx, aa + ctx->dz, V, kKCont, wptr(ctx, wh), d, kMNCont, da + (size_t)c0 * d, d,
+                nc, d, V, kEpiStoreF32), "dxf");
+    NC_TRY(gemm(ctx, aa + ctx->dz, V, kMNCont, xfc, d, kMNCont, G + wh, d, V, d, nc, kEpiAccF32,
+                nullptr, nullptr, ctx->splits_head), "dWh");
+  }
+  NC_TRY(nc_sum_scaled(A<float>(ctx, ctx->loss_rows), N, 1.f / (float)N, d_loss, st), "loss");
+  NC_TRY(nc_rmsnorm_bwd(dt, da, aa + ctx->xf, A<float>(ctx, ctx->rf), dx, dxT, N, d, 0, st),
+         "normf bwd");
+
+  // --------------------------------------------------------------- backward
+  for (int l = L - 1; l >= 0; --l) {
+    const LayerAct& la = ctx->la[l];
+    const size_t wb = (size_t)l * ctx->S;
+    const size_t w1 = wb + 4ULL * d * d, w2 = w1 + (size_t)F * d;
+    char* qkv = aa + la.qkv;
+    char* dqkv = aa + ctx->dqkv;
+    // MLP
+    NC_TRY(gemm(ctx, dxT, d, kKCont, wptr(ctx, w2), F, kMNCont, aa + ctx->dh, F, N, F, d,
+                kEpiRelu2Bwd, aa + la.h), "dh");
+    NC_TRY(gemm(ctx, dxT, d, kMNCont, aa + la.g, F, kMNCont, G + w2, F, d, F, N, kEpiAccF32,
+                nullptr, nullptr, ctx->splits_2), "dW2");
+    NC_TRY(gemm(ctx, aa + ctx->dh, F, kMNCont, aa + la.a2, d, kMNCont, G + w1, d, F, d, N,
+                kEpiAccF32, nullptr, nullptr, ctx->splits_1), "dW1");
+    NC_TRY(gemm(ctx, aa + ctx->dh, F, kKCont, wptr(ctx, w1), d, kMNCont, da, d, N, d, F,
+                kEpiStoreF32), "da2");
+    NC_TRY(nc_rmsnorm_bwd(dt, da, aa + la.a2, A<float>(ctx, la.r2), dx, dxT, N, d, 1, st),
+           "norm2 bwd");
+    // attention
+    NC_TRY(gemm(ctx, dxT, d, kKCont, wptr(ctx, wb + 3ULL * d * d), d, kMNCont, aa + ctx->dO, d,
+                N, d, d, kEpiStore), "dO");
+    NC_TRY(gemm(ctx, dxT, d, kMNCont, aa + la.o, d, kMNCont, G + wb + 3ULL * d * d, d, d, d, N,
+                kEpiAccF32, nullptr, nullptr, ctx->splits_o), "dWo");
+    NC_TRY(nc_attn_bwd_pre(dt, aa + la.o, aa + ctx->dO, d, A<float>(ctx, ctx->Dbuf), B, T, H, st),
+           "attn D");
+    NC_TRY(nc_attn_bwd(dt, qkv, qkv + d * es, qkv + 2 * d * es, 3 * d, aa + ctx->dO, d,
+                       A<float>(ctx, la.lse), A<float>(ctx, ctx->Dbuf), dqkv, dqkv + d * es,
+                       dqkv + 2 * d * es, 3 * d, B, T, H, st), "attn bwd");
+    NC_TRY(nc_qk_norm_rope_bwd(dt, dqkv, qkv, A<float>(ctx, la.rqk), tab, N, T, H, st),
+           "qknorm bwd");
+    NC_TRY(gemm(ctx, dqkv, 3 * d, kMNCont, aa + la.a1, d, kMNCont, G + wb, d, 3 * d, d, N,
+                kEpiAccF32, nullptr, nullptr, ctx->splits_qkv), "dWqkv");
+    NC_TRY(gemm(ctx, dqkv, 3 * d, kKCont, wptr(ctx, wb), d, kMNCont, da, d, N, d, 3 * d,
+                kEpiStoreF32), "da1");
+    NC_TRY(nc_rmsnorm_bwd(dt, da, aa + la.a1, A<float>(ctx, la.r1), dx, dxT, N, d, 1, st),
+           "norm1 bwd");
+  }
+  NC_TRY(nc_embed_bwd(tok, dx, G + ctx->n_block, N, V, d, aa + ctx->emb, st), "embed bwd");
+  return NC_OK;
+}
+
+static nc_status newton_schulz(nc_ctx* ctx, int count, int R, int C, size_t x0, size_t x1,
+                               size_t Ab, size_t Bb, size_t* result) {
+  const nc_optim_config& o = ctx->ocfg;
+  char* aa = ctx->aa;
+  size_t cur = x0, nxt = x1;
+  const int64_t sx = (int64_t)R * C, sa = (int64_t)R * R;
+  for (int it = 0; it < o.ns_steps; ++it) {
+    const float a = o.ns_coeffs[it][0], b = o.ns_coeffs[it][1], c = o.ns_coeffs[it][2];
+    // A = X X^T
+    NC_TRY(gemm(ctx, aa + cur, C, kKCont, aa + cur, C, kKCont, aa + Ab, R, R, R, C, kEpiStore,
+                nullptr, nullptr, 1, count, sx, sx, sa), "ns gram");
+    // B = b A + c A A   (A symmetric: A A = A A^T)
+    NC_TRY(gemm(ctx, aa + Ab, R, kKCont, aa + Ab, R, kKCont, aa + Bb, R, R, R, R, kEpiPoly,
+                aa + Ab, nullptr, 1, count, sa, sa, sa, b, c), "ns poly");
+    // X' = a X + B X
+    NC_TRY(gemm(ctx, aa + Bb, R, kKCont, aa + cur, C, kMNCont, aa + nxt, C, R, C, R, kEpiPoly,
+                aa + cur, nullptr, 1, count, sa, sx, sx, a, 1.f), "ns update");
+    std::swap(cur, nxt);
+  }
+  *result = cur;
+  return NC_OK;
+}
+
+nc_status nc_optimizer_step(nc_ctx* ctx, float lr_mult) {
+  if (!ctx) return NC_ERR_INVALID_ARG;
+  if (!ctx->bound) return fail(ctx, NC_ERR_STATE, "bind first");
+  if (!std::isfinite(lr_mult)) return fail(ctx, NC_ERR_INVALID_ARG, "lr_mult");
+  const nc_optim_config& o = ctx->ocfg;
+  const int dt = ctx->dt, L = ctx->L, d = ctx->d, F = ctx->F, V = ctx->V;
+  hipStream_t st = ctx->st;
+  ctx->step += 1;
+  const double t = (double)ctx->step;
+  const float bc1 = (float)(1.0 - std::pow((double)o.adam_beta1, t));
+  const float bc2 = (float)(1.0 - std::pow((double)o.adam_beta2, t));
+  float* Pm = P<float>(ctx, ctx->oP);
+  float* G = P<float>(ctx, ctx->oG);
+  const size_t Vd = (size_t)V * d;
+  // AdamW: E | Wh contiguous after the block region
+  NC_TRY(nc_adamw(Pm + ctx->n_block, G + ctx->n_block, P<float>(ctx, ctx->oAm),
+                  P<float>(ctx, ctx->oAv), 2 * Vd, Vd, o.adam_lr_embed * lr_mult,
+                  o.adam_lr_head * lr_mult, o.adam_beta1, o.adam_beta2, o.adam_eps, o.adam_wd,
+                  bc1, bc2, dt ? (void*)(ctx->pa + ctx->oSh + ctx->n_block * 2) : nullptr, Vd, st),
+         "adamw");
+  if (L == 0) return NC_OK;
+  // Muon
+  float* Mom = P<float>(ctx, ctx->oM);
+  NC_TRY(nc_momentum(Mom, G, ctx->n_block, o.muon_momentum, st), "momentum");
+  const float* U = Mom;
+  if (o.muon_nesterov) {
+    NC_TRY(nc_nesterov(Mom, G, A<float>(ctx, ctx->nsU), ctx->n_block, o.muon_momentum, st),
+           "nesterov");
+    U = A<float>(ctx, ctx->nsU);
+  }
+  float* norms = A<float>(ctx, ctx->norms);
+  float* frob = A<float>(ctx, ctx->frob);
+  const int64_t dd = (int64_t)d * d, dF = (int64_t)d * F;
+  const MatBatch sq{4, dd, ctx->S}, one{1, 0, ctx->S};
+  const size_t o1 = 4ULL * dd, o2 = o1 + (size_t)dF;
+  NC_TRY(nc_frob_norms(U, sq, dd, 4 * L, frob, norms, st), "norms sq");
+  NC_TRY(nc_frob_norms(U + o1, one, dF, L, frob + 4 * L * 256, norms + 4 * L, st), "norms W1");
+  NC_TRY(nc_frob_norms(U + o2, one, dF, L, frob + 5 * L * 256, norms + 5 * L, st), "norms W2");
+  char* aa = ctx->aa;
+  // orthogonalise on the short side: square [d,d]; W1 [F,d] -> [d,F]; W2 [d,F]
+  NC_TRY(nc_ns_prepare(dt, U, sq, d, d, 4 * L, norms, o.ns_eps, 0, aa + ctx->nsXs0, dd, st),
+         "prep sq");
+  NC_TRY(nc_ns_prepare(dt, U + o1, one, F, d, L, norms + 4 * L, o.ns_eps, 1, aa + ctx->nsXr0, dF,
+                       st), "prep W1");
+  NC_TRY(nc_ns_prepare(dt, U + o2, one, d, F, L, norms + 5 * L, o.ns_eps, 0,
+                       aa + ctx->nsXr0 + (size_t)L * dF * ctx->es, dF, st), "prep W2");
+  size_t xs, xr;
+  nc_status s = newton_schulz(ctx, 4 * L, d, d, ctx->nsXs0, ctx->nsXs1, ctx->nsAs, ctx->nsBs, &xs);
+  if (s != NC_OK) return s;
+  s = newton_schulz(ctx, 2 * L, d, F, ctx->nsXr0, ctx->nsXr1, ctx->nsAr, ctx->nsBr, &xr);
+  if (s != NC_OK) return s;
+  const float lr = o.muon_lr * lr_mult;
+  char* sh = dt ? ctx->pa + ctx->oSh : nullptr;
+  NC_TRY(nc_ns_apply(dt, Pm, sq, d, d, 4 * L, aa + xs, dd, 0, lr, o.muon_wd, sh, st), "apply sq");
+  NC_TRY(nc_ns_apply(dt, Pm + o1, one, F, d, L, aa + xr, dF, 1, lr, o.muon_wd,
+                     sh ? sh + o1 * 2 : nullptr, st), "apply W1");
+  NC_TRY(nc_ns_apply(dt, Pm + o2, one, d, F, L, aa + xr + (size_t)L * dF * ctx->es, dF, 0, lr,
+                     o.muon_wd, sh ? sh + o2 * 2 : nullptr, st), "apply W2");
+  return NC_OK;
+}
+
+nc_status nc_param_count(const nc_ctx* ctx, int32_t* n) {
+  if (!ctx || !n) return NC_ERR_INVALID_ARG;
+  *n = (int32_t)ctx->params.size();
+  return NC_OK;
+}
+
+nc_status nc_param_desc(const nc_ctx* ctx, int32_t i, nc_param_info* out) {
+  if (!ctx || !out || i < 0 || i >= (int32_t)ctx->params.size()) return NC_ERR_INVALID_ARG;
+  const ParamInfo& p = ctx->params[i];
+  std::memset(out, 0, sizeof(*out));
+  std::snprintf(out->name, sizeof(out->name), "%s", p.name.c_str());
+  out->rows = p.rows;
+  out->cols = p.cols;
+  out->group = p.group;
+  out->param_offset = (int64_t)(ctx->oP + p.elem * 4);
+  out->grad_offset = (int64_t)(ctx->oG + p.elem * 4);
+  if (p.group == NC_GROUP_MUON) {
+    out->state0_offset = (int64_t)(ctx->oM + p.elem * 4);
+    out->state1_offset = -1;
+  } else {
+    out->state0_offset = (int64_t)(ctx->oAm + p.adam_elem * 4);
+    out->state1_offset = (int64_t)(ctx->oAv + p.adam_elem * 4);
+  }
+  return NC_OK;
+}
+
+nc_status nc_set_param(nc_ctx* ctx, int32_t i, const float* src, int32_t src_on_device) {
+  if (!ctx || !src || i < 0 || i >= (int32_t)ctx->params.size()) return NC_ERR_INVALID_ARG;
+  if (!ctx->bound) return fail(ctx, NC_ERR_STATE, "bind first");
+  const ParamInfo& p = ctx->params[i];
+  const size_t n = (size_t)p.rows * p.cols;
+  float* dst = P<float>(ctx, ctx->oP) + p.elem;
+  NC_TRY(hipMemcpyAsync(dst, src, n * 4,
+                        src_on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice, ctx->st),
+         "set param");
+  if (ctx->dt && p.name != "E") {
+    // bf16 copy: block region mirrors the master layout, then Wh
+    const size_t sh_elem = p.name == "Wh" ? (size_t)ctx->n_block : p.elem;
+    NC_TRY(nc_convert_f32(1, dst, ctx->pa + ctx->oSh + sh_elem * 2, n, ctx->st), "set shadow");
+  }
+  NC_TRY(hipStreamSynchronize(ctx->st), "set param sync");
+  return NC_OK;
+}
+
+nc_status nc_get_tensor(nc_ctx* ctx, int32_t i, int32_t which, float* dst, int32_t dst_on_device) {
+  if (!ctx || !dst || i < 0 || i >= (int32_t)ctx->params.size()) return NC_ERR_INVALID_ARG;
+  if (!ctx->bound) return fail(ctx, NC_ERR_STATE, "bind first");
+  nc_param_info d;
+  nc_param_desc(ctx, i, &d);
+  int64_t off;
+  switch (which) {
+    case NC_PARAM: off = d.param_offset; break;
+    case NC_GRAD: off = d.grad_offset; break;
+    case NC_MOMENTUM: off = d.group == NC_GROUP_MUON ? d.state0_offset : -1; break;
+    case NC_ADAM_M: off = d.group == NC_GROUP_ADAMW ? d.state0_offset : -1; break;
+    case NC_ADAM_V: off = d.group == NC_GROUP_ADAMW ? d.state1_offset : -1; break;
+    default: off = -1;
+  }
+  if (off < 0) return fail(ctx, NC_ERR_INVALID_ARG, "parameter has no such tensor");
+  const size_t n = (size_t)d.rows * d.cols;
+  NC_TRY(hipMemcpyAsync(dst, ctx->pa + off, n * 4,
+                        dst_on_device ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToHost, ctx->st),
+         "get tensor");
+  NC_TRY(hipStreamSynchronize(ctx->st), "get sync");
+  return NC_OK;
+}
+
+nc_status nc_check_finite(nc_ctx* ctx, int32_t* host_flag) {
+  if (!ctx || !host_flag) return NC_ERR_INVALID_ARG;
+  if (!ctx->bound) return fail(ctx, NC_ERR_STATE, "bind first");
+  // flag lives in the first 4 bytes of the norms scratch
+  int32_t* flag = A<int32_t>(ctx, ctx->norms);
+  NC_TRY(nc_fill_f32(reinterpret_cast<float*>(flag), 0.f, 1, ctx->st), "flag clear");
+  NC_TRY(nc_check_finite(P<float>(ctx, ctx->oP), (size_t)ctx->n_total, flag, ctx->st), "finite p");
+  NC_TRY(nc_check_finite(P<float>(ctx, ctx->oG), (size_t)ctx->n_total, flag, ctx->st), "finite g");
+  int32_t h = 0;
+  NC_TRY(hipMemcpyAsync(&h, flag, 4, hipMemcpyDeviceToHost, ctx->st), "flag copy");
+  NC_TRY(hipStreamSynchronize(ctx->st), "finite sync");
+  *host_flag = h ? 1 : 0;
+  return h ? NC_ERR_NONFINITE : NC_OK;
+}
+
+nc_status nc_flops(const nc_ctx* ctx, int32_t B, double* fb, double* opt) {
+  if (!ctx || B < 0) return NC_ERR_INVALID_ARG;
+  const double L = ctx->L, d = ctx->d, F = ctx->F, V = ctx->V, T = ctx->T;
+  const double N = (double)B * T;
+  if (fb) *fb = 6.0 * N * (L * (4 * d * d + 2 * d * F) + V * d) + 6.0 * N * L * d * T;
+  if (opt) {
+    const double steps = ctx->ocfg.ns_steps;
+    const double sq = 4.0 * d * d * d + 2.0 * d * d * d;     // m = n = d
+    const double rect = 4.0 * d * d * F + 2.0 * d * d * d;   // m = d, n = F
+    *opt = steps * L * (4 * sq + 2 * rect);
+  }
+  return NC_OK;
+}
+
+// ----------------------------------------------------------- single ops
+nc_status nc_op_gemm(int32_t dtype, const void* A_, int64_t lda, int32_t al, const void* B_,
+                     int64_t ldb, int32_t bl, void* C_, int64_t ldc, int32_t M, int32_t N,
+                     int32_t K, int32_t batch, int64_t sA, int64_t sB, int64_t sC,
+                     int32_t epi, const void* aux_in, void* aux_out, float alpha, float p0,
+                     float p1, int32_t splits, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  if (!A_ || !B_ || !C_ || M < 0 || N < 0 || K < 1 || batch < 1) return NC_ERR_INVALID_ARG;
+  if ((dtype != NC_FP32 && dtype != NC_BF16) || al < 0 || al > 1 || bl < 0 || bl > 1 ||
+      epi < 0 || epi > kEpiPoly)
+    return NC_ERR_INVALID_ARG;
+  if ((epi == kEpiRelu2 && !aux_out) || ((epi == kEpiRelu2Bwd || epi == kEpiPoly) && !aux_in))
+    return NC_ERR_INVALID_ARG;
+  if (dtype == NC_BF16) {
+    if (K % 8 || (al == kMNCont && M % 8) || (bl == kMNCont && N % 8)) return NC_ERR_UNSUPPORTED;
+    if (lda % 8 || ldb % 8) return NC_ERR_UNSUPPORTED;
+  }
+  if (splits < 1) splits = 1;
+  if (splits > 1) {
+    if (dtype != NC_BF16 || (epi != kEpiStoreF32 && epi != kEpiAccF32)) return NC_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < (size_t)splits * batch * M * N * 4)
+      return NC_ERR_INVALID_ARG;
+  }
+  GemmParams g{};
+  g.A = A_; g.B = B_; g.C = C_; g.aux_in = aux_in; g.aux_out = aux_out;
+  g.lda = lda; g.ldb = ldb; g.ldc = ldc; g.sA = sA; g.sB = sB; g.sC = sC;
+  g.M = M; g.N = N; g.K = K; g.batch = batch; g.a_layout = al; g.b_layout = bl; g.epi = epi;
+  g.alpha = alpha; g.p0 = p0; g.p1 = p1; g.splits = splits;
+  g.workspace = static_cast<float*>(workspace); g.workspace_bytes = workspace_bytes;
+  return nc_launch_gemm(dtype, g, static_cast<hipStream_t>(stream)) == hipSuccess ? NC_OK
+                                                                                 : NC_ERR_HIP;
+}
+
+nc_status nc_op_attention_fwd(int32_t dtype, const void* q, const void* k, const void* v,
+                              int64_t ld_qkv, void* o, int64_t ld_o, float* lse, int32_t B,
+                              int32_t T, int32_t H, void* stream) {
+  if (!q || !k || !v || !o || !lse || B < 1 || T < 1 || H < 1) return NC_ERR_INVALID_ARG;
+  if (dtype == NC_BF16 && (T % 128 || ld_qkv % 8 || ld_o % 8)) return NC_ERR_UNSUPPORTED;
+  return nc_attn_fwd(dtype == NC_BF16, q, k, v, ld_qkv, o, ld_o, lse, B, T, H,
+                     static_cast<hipStream_t>(stream)) == hipSuccess ? NC_OK : NC_ERR_HIP;
+}
+
+nc_status nc_op_attention_bwd(int32_t dtype, const void* q, const void* k, const void* v,
+                              int64_t ld_qkv, const void* o, const void* dO, int64_t ld_o,
+                              const float* lse, float* D, void* dq, void* dk, void* dv,
+                              int64_t ld_d, int32_t B, int32_t T, int32_t H, void* stream) {
+  if (!q || !k || !v || !o || !dO || !lse || !D || !dq || !dk || !dv || B < 1 || T < 1 || H < 1)
+    return NC_ERR_INVALID_ARG;
+  if (dtype == NC_BF16 && (T % 128 || ld_qkv % 8 || ld_o % 8 || ld_d % 8)) return NC_ERR_UNSUPPORTED;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int dt = dtype == NC_BF16;
+  if (nc_attn_bwd_pre(dt, o, dO, ld_o, D, B, T, H, st) != hipSuccess) return NC_ERR_HIP;
+  return nc_attn_bwd(dt, q, k, v, ld_qkv, dO, ld_o, lse, D, dq, dk, dv, ld_d, B, T, H, st) ==
+                 hipSuccess
+             ? NC_OK
+             : NC_ERR_HIP;
+}
+
+}  // extern "C"

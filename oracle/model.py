@@ -95,6 +95,21 @@ def causal_attention(q, k, v):
     return p @ v, p
 
 
+def causal_attention_backward(q, k, v, do):
+    """(dq, dk, dv) of o = causal_attention(q, k, v) for an upstream gradient do:
+    with P the probabilities, dv = P^T do, dP = do v^T,
+    dS = P * (dP - rowsum(dP * P)) (softmax Jacobian), dq = dS k / sqrt(hd),
+    dk = dS^T q / sqrt(hd)."""
+    hd = q.shape[-1]
+    _, p = causal_attention(q, k, v)
+    dv = np.swapaxes(p, -1, -2) @ do
+    dp = do @ np.swapaxes(v, -1, -2)
+    ds = p * (dp - np.sum(dp * p, axis=-1, keepdims=True))
+    dq = (ds @ k) / np.sqrt(hd)
+    dk = (np.swapaxes(ds, -1, -2) @ q) / np.sqrt(hd)
+    return dq, dk, dv
+
+
 def _sum_outer(a, b):
     """sum over every leading (batch, position) index of a_n^T b_n:
     a [..., m], b [..., n] -> [m, n]."""
@@ -220,12 +235,7 @@ def loss_and_grads(params, tokens, targets, cfg, grad_scale=1.0):
         # attention: x += o Wo^T
         grads[nWo] = _sum_outer(dx, L["o"])
         do = _split_heads(dx @ P[nWo], cfg["n_head"])
-        o_h, p = causal_attention(L["qr"], L["kr"], L["v"])     # recompute P
-        dv = np.swapaxes(p, -1, -2) @ do
-        dp = do @ np.swapaxes(L["v"], -1, -2)
-        ds = p * (dp - np.sum(dp * p, axis=-1, keepdims=True))  # softmax backward
-        dqr = (ds @ L["kr"]) / np.sqrt(hd)
-        dkr = (np.swapaxes(ds, -1, -2) @ L["qr"]) / np.sqrt(hd)
+        dqr, dkr, dv = causal_attention_backward(L["qr"], L["kr"], L["v"], do)
         dq = rmsnorm_backward(rope_inverse(dqr, cos, sin), L["qn"], L["rq"])
         dk = rmsnorm_backward(rope_inverse(dkr, cos, sin), L["kn"], L["rk"])
         dq, dk, dv = _merge_heads(dq), _merge_heads(dk), _merge_heads(dv)

@@ -1,0 +1,122 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function declared in include/*.h, plans arenas, validates
+configurations and reports call-order errors before touching the device."""
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from gpt_pretraining_step_gemms_amd import nc
+from gpt_pretraining_step_gemms_amd.configs import CONFIGS, D26, TINY, OptimConfig, from_depth
+from oracle.model import param_shapes
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"^\s*(?:nc_status|void|const char\s*\*)\s*(nc_\w+)\s*\(", text, re.M))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = nc.load()
+    names = declared_functions()
+    assert len(names) >= 18
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_plan_sizes_fit_hbm_and_grow_with_batch():
+    for cfg in CONFIGS.values():
+        pb, ab = nc.plan(cfg)
+        assert pb > 0 and ab > 0
+        assert pb % 256 == 0 and ab % 256 == 0
+    p1, a1 = nc.plan(D26, max_micro_batch=16)
+    p2, a2 = nc.plan(D26, max_micro_batch=64)
+    assert p1 == p2 and a2 > 3 * a1
+    hbm = 288 * 10 ** 9
+    assert p2 + a2 < 0.95 * hbm           # d26 at 64 rows fits one MI355X
+    p3, a3 = nc.plan(D26, max_micro_batch=128)
+    assert p3 + a3 > hbm                  # ... and 128 rows does not
+
+
+def _status_of_plan(cfg, ocfg=OptimConfig()):
+    lib = nc.load()
+    m, o = nc.model_cfg_c(cfg), nc.optim_cfg_c(ocfg)
+    return lib.nc_plan(ctypes.byref(m), ctypes.byref(o), None, None)
+
+
+def test_invalid_configurations_are_rejected():
+    from dataclasses import replace
+    assert _status_of_plan(TINY) == nc.NC_OK
+    assert _status_of_plan(replace(TINY, head_dim=64, n_head=2)) == nc.NC_ERR_UNSUPPORTED
+    assert _status_of_plan(replace(TINY, vocab=500)) == nc.NC_ERR_UNSUPPORTED
+    assert _status_of_plan(replace(TINY, dtype="bf16")) == nc.NC_ERR_UNSUPPORTED  # T=64 not % 128
+    assert _status_of_plan(replace(TINY, d_model=0)) == nc.NC_ERR_INVALID_ARG
+    o = OptimConfig(ns_coeffs=((1.0, 0.0, 0.0),) * 8)
+    assert _status_of_plan(TINY, o) == nc.NC_OK
+    c = nc.optim_cfg_c(o)
+    c.ns_steps = 9
+    m = nc.model_cfg_c(TINY)
+    assert nc.load().nc_plan(ctypes.byref(m), ctypes.byref(c), None, None) == nc.NC_ERR_INVALID_ARG
+
+
+def test_call_order_and_arena_errors_without_device():
+    lib = nc.load()
+    m, o = nc.model_cfg_c(TINY), nc.optim_cfg_c(OptimConfig())
+    ctx = ctypes.c_void_p()
+    assert lib.nc_create(ctypes.byref(m), ctypes.byref(o), ctypes.byref(ctx)) == nc.NC_OK
+    try:
+        fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every check fails first
+        assert lib.nc_fwd_bwd(ctx, fake, fake, 1, 1.0, fake) == nc.NC_ERR_STATE
+        assert lib.nc_optimizer_step(ctx, 1.0) == nc.NC_ERR_STATE
+        assert lib.nc_zero_grads(ctx) == nc.NC_ERR_STATE
+        assert lib.nc_bind(ctx, None, 0, None, 0, None) == nc.NC_ERR_INVALID_ARG
+        assert lib.nc_bind(ctx, ctypes.c_void_p((1 << 20) + 4), 1 << 40, fake, 1 << 40, None) \
+            == nc.NC_ERR_INVALID_ARG                      # misaligned
+        assert lib.nc_bind(ctx, fake, 16, fake, 16, None) == nc.NC_ERR_OUT_OF_MEMORY
+        assert b"arena too small" in lib.nc_last_error(ctx)
+        assert lib.nc_status_str(nc.NC_ERR_STATE) == b"bad call order"
+    finally:
+        lib.nc_destroy(ctx)
+
+
+def test_parameter_registry_matches_model_shapes():
+    lib = nc.load()
+    cfg = from_depth(12, micro_batch=1, accum_steps=1)
+    m, o = nc.model_cfg_c(cfg), nc.optim_cfg_c(OptimConfig())
+    ctx = ctypes.c_void_p()
+    assert lib.nc_create(ctypes.byref(m), ctypes.byref(o), ctypes.byref(ctx)) == nc.NC_OK
+    try:
+        n = ctypes.c_int32()
+        lib.nc_param_count(ctx, ctypes.byref(n))
+        infos = []
+        for i in range(n.value):
+            info = nc.ParamInfoC()
+            assert lib.nc_param_desc(ctx, i, ctypes.byref(info)) == nc.NC_OK
+            infos.append(info)
+        shapes = {i.name.decode(): (i.rows, i.cols) for i in infos}
+        assert shapes == param_shapes(cfg.as_oracle_cfg())
+        pb, _ = nc.plan(cfg)
+        spans = sorted((i.param_offset, i.param_offset + 4 * i.rows * i.cols) for i in infos)
+        assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))   # no overlap
+        assert spans[-1][1] <= pb
+        groups = {i.name.decode(): i.group for i in infos}
+        assert groups["E"] == groups["Wh"] == 0 and groups["3.W1"] == 1
+        # Wq, Wk, Wv of a layer are adjacent rows of one [3d, d] matrix
+        q, k, v = (infos[1 + j] for j in range(3))
+        assert k.param_offset - q.param_offset == 4 * cfg.d_model ** 2
+        assert v.param_offset - k.param_offset == 4 * cfg.d_model ** 2
+        assert lib.nc_param_desc(ctx, n.value, ctypes.byref(nc.ParamInfoC())) == nc.NC_ERR_INVALID_ARG
+        fb, opt = ctypes.c_double(), ctypes.c_double()
+        lib.nc_flops(ctx, 32, ctypes.byref(fb), ctypes.byref(opt))
+        L, d, V, T = 12, 768, 32768, 2048
+        assert fb.value == pytest.approx(6 * 32 * T * (12 * L * d * d + V * d) + 6 * 32 * T * L * d * T)
+    finally:
+        lib.nc_destroy(ctx)

@@ -1,0 +1,191 @@
+"""Kernel-level parity on the GPU: the GEMM family (every operand layout and
+epilogue, batched, split-K, ragged tiles, a full-size sampled case) against
+numpy matmuls of the same (bf16-rounded) inputs, and causal attention
+forward/backward against the oracle's attention."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpt_pretraining_step_gemms_amd import nc
+from parity import cosine, max_rel
+
+pytestmark = pytest.mark.gpu
+
+BF, F32 = torch.bfloat16, torch.float32
+
+
+def dev(a, dtype):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda").to(dtype)
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def rounded(a, dtype):
+    """The values the GPU sees for a float array stored as `dtype`."""
+    return host(dev(a, dtype))
+
+
+def stored(logical, layout):
+    return logical if layout == nc.NC_K_CONTIGUOUS else np.ascontiguousarray(logical.T)
+
+
+@pytest.mark.parametrize("dtype", [BF, F32])
+@pytest.mark.parametrize("al,bl", [(0, 0), (0, 1), (1, 1), (1, 0)])
+def test_gemm_layouts_ragged(dtype, al, bl):
+    M, N, K = 264, 136, 200          # one full 256 tile + ragged edges in M, N and K
+    rng = np.random.default_rng(10 + 2 * al + bl)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    B = rng.standard_normal((N, K)).astype(np.float32)
+    As, Bs = stored(A, al), stored(B, bl)
+    dA, dB = dev(As, dtype), dev(Bs, dtype)
+    C = torch.zeros(M, N, dtype=F32, device="cuda")
+    nc.gemm(dA, al, dB, bl, C, M, N, K, nc.EPI_STORE_F32, lda=As.shape[1], ldb=Bs.shape[1])
+    torch.cuda.synchronize()
+    ref = stored(host(dA), al) @ stored(host(dB), bl).T
+    assert max_rel(host(C), ref) < 2e-6
+
+
+def test_gemm_epilogues_bf16():
+    M, N, K = 320, 264, 136
+    rng = np.random.default_rng(3)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    B = rng.standard_normal((N, K)).astype(np.float32)
+    dA, dB = dev(A, BF), dev(B, BF)
+    acc = host(dA) @ host(dB).T
+    # store (bf16 out, alpha)
+    C = torch.empty(M, N, dtype=BF, device="cuda")
+    nc.gemm(dA, 0, dB, 0, C, M, N, K, nc.EPI_STORE, alpha=0.5)
+    # accumulate into fp32
+    C0 = rng.standard_normal((M, N)).astype(np.float32)
+    Cacc = dev(C0, F32)
+    nc.gemm(dA, 0, dB, 0, Cacc, M, N, K, nc.EPI_ACC_F32)
+    # ReLU^2 forward: h and max(h,0)^2
+    H = torch.empty(M, N, dtype=BF, device="cuda")
+    G = torch.empty(M, N, dtype=BF, device="cuda")
+    nc.gemm(dA, 0, dB, 0, H, M, N, K, nc.EPI_RELU2, aux_out=G)
+    # ReLU^2 backward and the Newton-Schulz polynomial read an auxiliary input
+    aux = dev(rng.standard_normal((M, N)), BF)
+    R = torch.empty(M, N, dtype=BF, device="cuda")
+    nc.gemm(dA, 0, dB, 0, R, M, N, K, nc.EPI_RELU2_BWD, aux_in=aux)
+    Pn = torch.empty(M, N, dtype=BF, device="cuda")
+    nc.gemm(dA, 0, dB, 0, Pn, M, N, K, nc.EPI_POLY, aux_in=aux, p0=1.5, p1=-0.25)
+    torch.cuda.synchronize()
+    tol = 2 ** -8
+    assert max_rel(host(C), 0.5 * acc) < tol
+    assert max_rel(host(Cacc), C0 + acc) < 2e-6
+    assert max_rel(host(H), acc) < tol
+    assert max_rel(host(G), np.maximum(acc, 0) ** 2) < tol
+    assert max_rel(host(R), 2 * np.maximum(host(aux), 0) * acc) < tol
+    assert max_rel(host(Pn), 1.5 * host(aux) - 0.25 * acc) < tol
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_gemm_batched_and_split_k(splits):
+    batch, M, N, K = 3, 136, 200, 1024
+    rng = np.random.default_rng(4)
+    A = rng.standard_normal((batch, K, M)).astype(np.float32)   # MN-contiguous operands
+    B = rng.standard_normal((batch, K, N)).astype(np.float32)
+    C0 = rng.standard_normal((batch, M, N)).astype(np.float32)
+    dA, dB, C = dev(A, BF), dev(B, BF), dev(C0, F32)
+    ws = torch.empty(splits * batch * M * N, dtype=F32, device="cuda") if splits > 1 else None
+    nc.gemm(dA, 1, dB, 1, C, M, N, K, nc.EPI_ACC_F32, lda=M, ldb=N, ldc=N, batch=batch,
+            sA=K * M, sB=K * N, sC=M * N, splits=splits, workspace=ws)
+    torch.cuda.synchronize()
+    ref = C0 + np.einsum("bkm,bkn->bmn", host(dA), host(dB))
+    assert max_rel(host(C), ref) < 2e-6
+
+
+@pytest.mark.parametrize("shape", ["qkv_fwd", "wgrad"])
+def test_gemm_full_size_sampled(shape):
+    """d20 shapes: QKV forward (65536 x 3840 x 1280) and the QKV weight gradient
+    (3840 x 1280 over 65536 tokens, split-K); sampled rows checked exactly."""
+    rng = np.random.default_rng(5)
+    if shape == "qkv_fwd":
+        M, N, K, al, bl, splits = 65536, 3840, 1280, 0, 0, 1
+    else:
+        M, N, K, al, bl, splits = 3840, 1280, 65536, 1, 1, 8
+    A = torch.randn((M, K) if al == 0 else (K, M), device="cuda").to(BF)
+    B = torch.randn((N, K) if bl == 0 else (K, N), device="cuda").to(BF)
+    C = torch.zeros(M, N, dtype=F32, device="cuda")
+    ws = torch.empty(splits * M * N, dtype=F32, device="cuda") if splits > 1 else None
+    nc.gemm(A, al, B, bl, C, M, N, K, nc.EPI_ACC_F32, lda=A.shape[1], ldb=B.shape[1],
+            splits=splits, workspace=ws)
+    torch.cuda.synchronize()
+    rows = np.sort(rng.choice(M, 48, replace=False))
+    rows = np.concatenate([rows, [0, M - 1]])
+    Bl = host(B) if bl == 0 else host(B).T
+    if al == 0:
+        Ar = host(A[torch.from_numpy(rows).cuda()])
+    else:
+        Ar = host(A[:, torch.from_numpy(rows).cuda()]).T
+    ref = Ar @ Bl.T
+    got = host(C[torch.from_numpy(rows).cuda()])
+    assert max_rel(got, ref) < 2e-6
+
+
+# ------------------------------------------------------------------ attention
+def _attn_inputs(B, T, H, dtype, seed):
+    rng = np.random.default_rng(seed)
+    qkv = dev(rng.standard_normal((B * T, 3 * H * 128)), dtype)
+    dO = dev(rng.standard_normal((B * T, H * 128)), dtype)
+    return qkv, dO
+
+
+def _heads(x, B, T, H, col0):
+    """[B*T, ...] token-major columns col0 .. col0 + H*128 -> [B, H, T, 128]"""
+    a = host(x)[:, col0:col0 + H * 128]
+    return a.reshape(B, T, H, 128).transpose(0, 2, 1, 3)
+
+
+@pytest.mark.parametrize("dtype,B,T,H", [(BF, 2, 256, 2), (BF, 1, 2048, 2), (F32, 2, 64, 1),
+                                         (F32, 1, 100, 2)])
+def test_attention_forward_backward_vs_oracle(dtype, B, T, H):
+    d = H * 128
+    qkv, dO = _attn_inputs(B, T, H, dtype, seed=T + H)
+    o = torch.empty(B * T, d, dtype=dtype, device="cuda")
+    lse = torch.empty(B, H, T, dtype=F32, device="cuda")
+    q, k, v = qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:]
+    nc.attention_fwd(q, k, v, o, lse, B, T, H, ld_qkv=3 * d, ld_o=d)
+    dqkv = torch.zeros_like(qkv)
+    D = torch.empty(B, H, T, dtype=F32, device="cuda")
+    nc.attention_bwd(q, k, v, o, dO, lse, D, dqkv[:, :d], dqkv[:, d:2 * d], dqkv[:, 2 * d:],
+                     B, T, H, ld_qkv=3 * d, ld_o=d, ld_d=3 * d)
+    torch.cuda.synchronize()
+    Q, K, Vv = (_heads(qkv, B, T, H, c) for c in (0, d, 2 * d))
+    o_ref, p = oracle.causal_attention(Q, K, Vv)
+    s = Q @ np.swapaxes(K, -1, -2) / np.sqrt(128.0)
+    s = np.where(np.triu(np.ones((T, T), bool), 1), -np.inf, s)
+    lse_ref = np.log(np.sum(np.exp(s - s.max(-1, keepdims=True)), -1)) + s.max(-1)
+    dq_r, dk_r, dv_r = oracle.causal_attention_backward(Q, K, Vv, _heads(dO, B, T, H, 0))
+    got_o = _heads(o, B, T, H, 0)
+    bf = dtype == BF
+    assert max_rel(got_o, o_ref) < (2e-2 if bf else 1e-5)
+    assert np.max(np.abs(host(lse) - lse_ref)) < (2e-3 if bf else 1e-5)
+    for name, got, ref in [("dq", _heads(dqkv, B, T, H, 0), dq_r),
+                           ("dk", _heads(dqkv, B, T, H, d), dk_r),
+                           ("dv", _heads(dqkv, B, T, H, 2 * d), dv_r)]:
+        assert cosine(got, ref) > (0.999 if bf else 1 - 1e-9), name
+        assert max_rel(got, ref) < (3e-2 if bf else 1e-5), name
+
+
+def test_attention_causality_bitwise():
+    """Changing key/value rows at t* >= t leaves outputs of queries t < t* unchanged."""
+    B, T, H = 1, 256, 2
+    d = H * 128
+    qkv, _ = _attn_inputs(B, T, H, BF, seed=1)
+    outs = []
+    for trial in range(2):
+        x = qkv.clone()
+        if trial:
+            x[200:, d:] = torch.randn_like(x[200:, d:])
+        o = torch.empty(B * T, d, dtype=BF, device="cuda")
+        lse = torch.empty(B, H, T, dtype=F32, device="cuda")
+        nc.attention_fwd(x[:, :d], x[:, d:2 * d], x[:, 2 * d:], o, lse, B, T, H, 3 * d, d)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][:200], outs[1][:200])
+    assert not torch.equal(outs[0][200:], outs[1][200:])
