@@ -71,8 +71,10 @@ struct nc_ctx {
   char* aa = nullptr;
   hipStream_t st = nullptr;
   bool bound = false;
+  bool dry_run = false;   // host-only validation of the launch sequence
   int64_t step = 0;
   std::string err;
+  std::string range_error;
 };
 
 namespace {
@@ -87,10 +89,23 @@ nc_status hipcheck(nc_ctx* c, hipError_t e, const char* what) {
   return fail(c, NC_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
+// NC_TRY: a HIP call or non-GEMM launch (skipped in a dry run).
+// NC_GEMM: a GEMM through gemm(), whose operand ranges are checked on the host
+// (and which only checks, without launching, in a dry run).
 #define NC_TRY(expr, what)                               \
   do {                                                   \
+    if (!ctx->dry_run) {                                 \
+      nc_status _s = hipcheck(ctx, (expr), what);        \
+      if (_s != NC_OK) return _s;                        \
+    }                                                    \
+  } while (0)
+#define NC_GEMM(expr, what)                              \
+  do {                                                   \
     nc_status _s = hipcheck(ctx, (expr), what);          \
-    if (_s != NC_OK) return _s;                          \
+    if (_s != NC_OK) {                                   \
+      if (ctx->range_error.size()) ctx->err += " (" + ctx->range_error + ")"; \
+      return _s;                                         \
+    }                                                    \
   } while (0)
 
 nc_status validate(const nc_model_config* m, const nc_optim_config* o, std::string& why) {
@@ -218,10 +233,52 @@ T* P(nc_ctx* c, size_t off) { return reinterpret_cast<T*>(c->pa + off); }
 template <typename T = void>
 T* A(nc_ctx* c, size_t off) { return reinterpret_cast<T*>(c->aa + off); }
 
-// weight operand of a GEMM: bf16 copy (bf16 models) or the fp32 master
+// Weight operand of a GEMM: the bf16 copy (bf16 models) or the fp32 master.
+// `elem` is the master-layout offset of a block matrix (< n_block); the bf16
+// region mirrors the block region and then holds Wh (E has no bf16 copy).
 const void* wptr(nc_ctx* c, size_t elem) {
   if (c->dt) return c->pa + c->oSh + elem * 2;
   return c->pa + c->oP + elem * 4;
+}
+const void* wptr_head(nc_ctx* c) {
+  if (c->dt) return c->pa + c->oSh + (size_t)c->n_block * 2;
+  return c->pa + c->oP + ((size_t)c->n_block + (size_t)c->V * c->d) * 4;
+}
+
+// True if [p, p + bytes) lies inside the parameter or the activation arena.
+bool in_arena(const nc_ctx* c, const void* p, size_t bytes) {
+  const char* q = static_cast<const char*>(p);
+  auto inside = [&](const char* base, size_t size) {
+    return q >= base && q + bytes <= base + size;
+  };
+  return inside(c->pa, c->param_bytes) || inside(c->aa, c->act_bytes);
+}
+
+// Host check of every operand extent of a GEMM against the arenas.
+bool operands_in_arenas(nc_ctx* c, const GemmParams& g) {
+  const size_t es = c->es;
+  const bool c_f32 = g.epi == kEpiStoreF32 || g.epi == kEpiAccF32;
+  auto extent = [](int64_t rows, int64_t cols, int64_t ld, int64_t bstride, int batch) {
+    // elements spanned by a [rows, cols] row-major view with leading dim ld
+    return (int64_t)(batch - 1) * bstride + (rows - 1) * ld + cols;
+  };
+  const int64_t ea = g.a_layout == kKCont ? extent(g.M, g.K, g.lda, g.sA, g.batch)
+                                          : extent(g.K, g.M, g.lda, g.sA, g.batch);
+  const int64_t eb = g.b_layout == kKCont ? extent(g.N, g.K, g.ldb, g.sB, g.batch)
+                                          : extent(g.K, g.N, g.ldb, g.sB, g.batch);
+  const int64_t ec = extent(g.M, g.N, g.ldc, g.sC, g.batch);
+  std::string bad;
+  if (!in_arena(c, g.A, ea * es)) bad = "A";
+  else if (!in_arena(c, g.B, eb * es)) bad = "B";
+  else if (!in_arena(c, g.C, ec * (c_f32 ? 4 : es))) bad = "C";
+  else if (g.aux_in && !in_arena(c, g.aux_in, ec * es)) bad = "aux_in";
+  else if (g.aux_out && !in_arena(c, g.aux_out, ec * es)) bad = "aux_out";
+  else if (g.splits > 1 && (size_t)g.splits * g.batch * g.M * g.N * 4 > g.workspace_bytes)
+    bad = "split-K workspace";
+  if (bad.empty()) return true;
+  c->range_error = "GEMM operand " + bad + " outside its arena (M=" + std::to_string(g.M) +
+                   " N=" + std::to_string(g.N) + " K=" + std::to_string(g.K) + ")";
+  return false;
 }
 
 hipError_t gemm(nc_ctx* c, const void* A_, int64_t lda, int al, const void* B_, int64_t ldb,
@@ -238,6 +295,8 @@ hipError_t gemm(nc_ctx* c, const void* A_, int64_t lda, int al, const void* B_, 
   g.splits = splits;
   g.workspace = reinterpret_cast<float*>(c->aa + c->ws);
   g.workspace_bytes = c->ws_bytes;
+  if (!operands_in_arenas(c, g)) return hipErrorInvalidValue;
+  if (c->dry_run) return hipSuccess;
   return nc_launch_gemm(c->dt, g, c->st);
 }
 
@@ -398,17 +457,17 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
     const size_t wb = (size_t)l * ctx->S;
     char* qkv = aa + la.qkv;
     NC_TRY(nc_rmsnorm_fwd(dt, x, aa + la.a1, A<float>(ctx, la.r1), N, d, eps, st), "norm1");
-    NC_TRY(gemm(ctx, aa + la.a1, d, kKCont, wptr(ctx, wb), d, kKCont, qkv, 3 * d, N, 3 * d, d,
+    NC_GEMM(gemm(ctx, aa + la.a1, d, kKCont, wptr(ctx, wb), d, kKCont, qkv, 3 * d, N, 3 * d, d,
                 kEpiStore), "qkv");
     NC_TRY(nc_qk_norm_rope_fwd(dt, qkv, A<float>(ctx, la.rqk), tab, N, T, H, eps, st), "qknorm");
     NC_TRY(nc_attn_fwd(dt, qkv, qkv + d * es, qkv + 2 * d * es, 3 * d, aa + la.o, d,
                        A<float>(ctx, la.lse), B, T, H, st), "attn fwd");
-    NC_TRY(gemm(ctx, aa + la.o, d, kKCont, wptr(ctx, wb + 3ULL * d * d), d, kKCont, x, d, N, d,
+    NC_GEMM(gemm(ctx, aa + la.o, d, kKCont, wptr(ctx, wb + 3ULL * d * d), d, kKCont, x, d, N, d,
                 d, kEpiAccF32), "out proj");
     NC_TRY(nc_rmsnorm_fwd(dt, x, aa + la.a2, A<float>(ctx, la.r2), N, d, eps, st), "norm2");
-    NC_TRY(gemm(ctx, aa + la.a2, d, kKCont, wptr(ctx, wb + 4ULL * d * d), d, kKCont, aa + la.h,
+    NC_GEMM(gemm(ctx, aa + la.a2, d, kKCont, wptr(ctx, wb + 4ULL * d * d), d, kKCont, aa + la.h,
                 F, N, F, d, kEpiRelu2, nullptr, aa + la.g), "mlp up");
-    NC_TRY(gemm(ctx, aa + la.g, F, kKCont, wptr(ctx, wb + 4ULL * d * d + (size_t)F * d), F,
+    NC_GEMM(gemm(ctx, aa + la.g, F, kKCont, wptr(ctx, wb + 4ULL * d * d + (size_t)F * d), F,
                 kKCont, x, d, N, d, F, kEpiAccF32), "mlp down");
   }
   NC_TRY(nc_rmsnorm_fwd(dt, x, aa + ctx->xf, A<float>(ctx, ctx->rf), N, d, eps, st), "normf");
@@ -419,13 +478,13 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
   for (int c0 = 0; c0 < N; c0 += ctx->chunk) {
     const int nc = std::min(ctx->chunk, N - c0);
     const char* xfc = aa + ctx->xf + (size_t)c0 * d * es;
-    NC_TRY(gemm(ctx, xfc, d, kKCont, wptr(ctx, wh), d, kKCont, aa + ctx->z, V, nc, V, d,
+    NC_GEMM(gemm(ctx, xfc, d, kKCont, wptr_head(ctx), d, kKCont, aa + ctx->z, V, nc, V, d,
                 kEpiStoreF32), "logits");
     NC_TRY(nc_cross_entropy(dt, A<float>(ctx, ctx->z), tgt + c0, aa + ctx->dz,
                             A<float>(ctx, ctx->loss_rows) + c0, nc, V, ce_scale, st), "ce");
-    NC_TRY(gemm(ctx, aa + ctx->dz, V, kKCont, wptr(ctx, wh), d, kMNCont, da + (size_t)c0 * d, d,
+    NC_GEMM(gemm(ctx, aa + ctx->dz, V, kKCont, wptr_head(ctx), d, kMNCont, da + (size_t)c0 * d, d,
                 nc, d, V, kEpiStoreF32), "dxf");
-    NC_TRY(gemm(ctx, aa + ctx->dz, V, kMNCont, xfc, d, kMNCont, G + wh, d, V, d, nc, kEpiAccF32,
+    NC_GEMM(gemm(ctx, aa + ctx->dz, V, kMNCont, xfc, d, kMNCont, G + wh, d, V, d, nc, kEpiAccF32,
                 nullptr, nullptr, ctx->splits_head), "dWh");
   }
   NC_TRY(nc_sum_scaled(A<float>(ctx, ctx->loss_rows), N, 1.f / (float)N, d_loss, st), "loss");
@@ -440,20 +499,20 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
     char* qkv = aa + la.qkv;
     char* dqkv = aa + ctx->dqkv;
     // MLP
-    NC_TRY(gemm(ctx, dxT, d, kKCont, wptr(ctx, w2), F, kMNCont, aa + ctx->dh, F, N, F, d,
+    NC_GEMM(gemm(ctx, dxT, d, kKCont, wptr(ctx, w2), F, kMNCont, aa + ctx->dh, F, N, F, d,
                 kEpiRelu2Bwd, aa + la.h), "dh");
-    NC_TRY(gemm(ctx, dxT, d, kMNCont, aa + la.g, F, kMNCont, G + w2, F, d, F, N, kEpiAccF32,
+    NC_GEMM(gemm(ctx, dxT, d, kMNCont, aa + la.g, F, kMNCont, G + w2, F, d, F, N, kEpiAccF32,
                 nullptr, nullptr, ctx->splits_2), "dW2");
-    NC_TRY(gemm(ctx, aa + ctx->dh, F, kMNCont, aa + la.a2, d, kMNCont, G + w1, d, F, d, N,
+    NC_GEMM(gemm(ctx, aa + ctx->dh, F, kMNCont, aa + la.a2, d, kMNCont, G + w1, d, F, d, N,
                 kEpiAccF32, nullptr, nullptr, ctx->splits_1), "dW1");
-    NC_TRY(gemm(ctx, aa + ctx->dh, F, kKCont, wptr(ctx, w1), d, kMNCont, da, d, N, d, F,
+    NC_GEMM(gemm(ctx, aa + ctx->dh, F, kKCont, wptr(ctx, w1), d, kMNCont, da, d, N, d, F,
                 kEpiStoreF32), "da2");
     NC_TRY(nc_rmsnorm_bwd(dt, da, aa + la.a2, A<float>(ctx, la.r2), dx, dxT, N, d, 1, st),
            "norm2 bwd");
     // attention
-    NC_TRY(gemm(ctx, dxT, d, kKCont, wptr(ctx, wb + 3ULL * d * d), d, kMNCont, aa + ctx->dO, d,
+    NC_GEMM(gemm(ctx, dxT, d, kKCont, wptr(ctx, wb + 3ULL * d * d), d, kMNCont, aa + ctx->dO, d,
                 N, d, d, kEpiStore), "dO");
-    NC_TRY(gemm(ctx, dxT, d, kMNCont, aa + la.o, d, kMNCont, G + wb + 3ULL * d * d, d, d, d, N,
+    NC_GEMM(gemm(ctx, dxT, d, kMNCont, aa + la.o, d, kMNCont, G + wb + 3ULL * d * d, d, d, d, N,
                 kEpiAccF32, nullptr, nullptr, ctx->splits_o), "dWo");
     NC_TRY(nc_attn_bwd_pre(dt, aa + la.o, aa + ctx->dO, d, A<float>(ctx, ctx->Dbuf), B, T, H, st),
            "attn D");
@@ -462,9 +521,9 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
                        dqkv + 2 * d * es, 3 * d, B, T, H, st), "attn bwd");
     NC_TRY(nc_qk_norm_rope_bwd(dt, dqkv, qkv, A<float>(ctx, la.rqk), tab, N, T, H, st),
            "qknorm bwd");
-    NC_TRY(gemm(ctx, dqkv, 3 * d, kMNCont, aa + la.a1, d, kMNCont, G + wb, d, 3 * d, d, N,
+    NC_GEMM(gemm(ctx, dqkv, 3 * d, kMNCont, aa + la.a1, d, kMNCont, G + wb, d, 3 * d, d, N,
                 kEpiAccF32, nullptr, nullptr, ctx->splits_qkv), "dWqkv");
-    NC_TRY(gemm(ctx, dqkv, 3 * d, kKCont, wptr(ctx, wb), d, kMNCont, da, d, N, d, 3 * d,
+    NC_GEMM(gemm(ctx, dqkv, 3 * d, kKCont, wptr(ctx, wb), d, kMNCont, da, d, N, d, 3 * d,
                 kEpiStoreF32), "da1");
     NC_TRY(nc_rmsnorm_bwd(dt, da, aa + la.a1, A<float>(ctx, la.r1), dx, dxT, N, d, 1, st),
            "norm1 bwd");
@@ -482,13 +541,13 @@ static nc_status newton_schulz(nc_ctx* ctx, int count, int R, int C, size_t x0, 
   for (int it = 0; it < o.ns_steps; ++it) {
     const float a = o.ns_coeffs[it][0], b = o.ns_coeffs[it][1], c = o.ns_coeffs[it][2];
     // A = X X^T
-    NC_TRY(gemm(ctx, aa + cur, C, kKCont, aa + cur, C, kKCont, aa + Ab, R, R, R, C, kEpiStore,
+    NC_GEMM(gemm(ctx, aa + cur, C, kKCont, aa + cur, C, kKCont, aa + Ab, R, R, R, C, kEpiStore,
                 nullptr, nullptr, 1, count, sx, sx, sa), "ns gram");
     // B = b A + c A A   (A symmetric: A A = A A^T)
-    NC_TRY(gemm(ctx, aa + Ab, R, kKCont, aa + Ab, R, kKCont, aa + Bb, R, R, R, R, kEpiPoly,
+    NC_GEMM(gemm(ctx, aa + Ab, R, kKCont, aa + Ab, R, kKCont, aa + Bb, R, R, R, R, kEpiPoly,
                 aa + Ab, nullptr, 1, count, sa, sa, sa, b, c), "ns poly");
     // X' = a X + B X
-    NC_TRY(gemm(ctx, aa + Bb, R, kKCont, aa + cur, C, kMNCont, aa + nxt, C, R, C, R, kEpiPoly,
+    NC_GEMM(gemm(ctx, aa + Bb, R, kKCont, aa + cur, C, kMNCont, aa + nxt, C, R, C, R, kEpiPoly,
                 aa + cur, nullptr, 1, count, sa, sx, sx, a, 1.f), "ns update");
     std::swap(cur, nxt);
   }
@@ -555,6 +614,24 @@ nc_status nc_optimizer_step(nc_ctx* ctx, float lr_mult) {
   NC_TRY(nc_ns_apply(dt, Pm + o2, one, d, F, L, aa + xr + (size_t)L * dF * ctx->es, dF, 0, lr,
                      o.muon_wd, sh ? sh + o2 * 2 : nullptr, st), "apply W2");
   return NC_OK;
+}
+
+nc_status nc_validate_launches(nc_ctx* ctx, int32_t B) {
+  if (!ctx) return NC_ERR_INVALID_ARG;
+  if (B < 1 || B > ctx->maxB) return fail(ctx, NC_ERR_INVALID_ARG, "B out of [1, max_micro_batch]");
+  nc_ctx probe = *ctx;   // same plan, fake arena bases, nothing launched
+  probe.pa = reinterpret_cast<char*>(uintptr_t(1) << 40);
+  probe.aa = reinterpret_cast<char*>(uintptr_t(1) << 44);
+  probe.bound = true;
+  probe.dry_run = true;
+  probe.err.clear();
+  probe.range_error.clear();
+  const int32_t* fake_tok = reinterpret_cast<const int32_t*>(probe.aa);
+  float* fake_loss = reinterpret_cast<float*>(probe.aa);
+  nc_status s = nc_fwd_bwd(&probe, fake_tok, fake_tok, B, 1.f, fake_loss);
+  if (s == NC_OK) s = nc_optimizer_step(&probe, 1.f);
+  ctx->err = probe.err;
+  return s;
 }
 
 nc_status nc_param_count(const nc_ctx* ctx, int32_t* n) {

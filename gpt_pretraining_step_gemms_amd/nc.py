@@ -83,6 +83,7 @@ def load():
         "nc_set_param": [P, I32, P, I32],
         "nc_get_tensor": [P, I32, I32, P, I32],
         "nc_check_finite": [P, ctypes.POINTER(I32)],
+        "nc_validate_launches": [P, I32],
         "nc_flops": [P, I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)],
         "nc_op_gemm": [I32, P, I64, I32, P, I64, I32, P, I64, I32, I32, I32, I32, I64, I64, I64,
                        I32, P, P, F32, F32, F32, I32, P, SZ, P],

@@ -136,6 +136,13 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* d_tokens, const int32_t* d_targ
  * Gradients are left as they are. */
 nc_status nc_optimizer_step(nc_ctx* ctx, float lr_mult);
 
+/* Host only, no device access: walks the launch sequence of nc_fwd_bwd on B
+ * rows and of nc_optimizer_step against placeholder arena addresses and
+ * checks that every matrix-product operand lies inside its arena (the same
+ * check guards every real launch).  NC_OK, or NC_ERR_HIP with the first
+ * violation in nc_last_error().  The context's state is not changed. */
+nc_status nc_validate_launches(nc_ctx* ctx, int32_t B);
+
 /* Parameter registry: count, then descriptors i = 0 .. count-1. */
 nc_status nc_param_count(const nc_ctx* ctx, int32_t* n);
 nc_status nc_param_desc(const nc_ctx* ctx, int32_t i, nc_param_info* out);

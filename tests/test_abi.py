@@ -87,6 +87,29 @@ def test_call_order_and_arena_errors_without_device():
         lib.nc_destroy(ctx)
 
 
+SMALL_BF16 = dict(name="small", n_layer=2, d_model=384, n_head=3, head_dim=128, d_ff=1536,
+                  vocab=4160, seq_len=256, micro_batch=2, accum_steps=1, dtype="bf16",
+                  token_dist="zipf")
+
+
+@pytest.mark.parametrize("name", ["tiny", "small", "d12", "d20", "d24", "d26"])
+def test_every_launch_of_a_step_stays_inside_the_arenas(name):
+    """Dry run of nc_fwd_bwd + nc_optimizer_step: every GEMM operand extent is
+    checked against the planned arenas (no device access)."""
+    from gpt_pretraining_step_gemms_amd.configs import ModelConfig
+    cfg = ModelConfig(**SMALL_BF16) if name == "small" else CONFIGS[name]
+    lib = nc.load()
+    for maxb, b in [(cfg.micro_batch, cfg.micro_batch), (cfg.micro_batch, 1), (1, 1)]:
+        m, o = nc.model_cfg_c(cfg, maxb), nc.optim_cfg_c(OptimConfig())
+        ctx = ctypes.c_void_p()
+        assert lib.nc_create(ctypes.byref(m), ctypes.byref(o), ctypes.byref(ctx)) == nc.NC_OK
+        try:
+            s = lib.nc_validate_launches(ctx, b)
+            assert s == nc.NC_OK, lib.nc_last_error(ctx)
+        finally:
+            lib.nc_destroy(ctx)
+
+
 def test_parameter_registry_matches_model_shapes():
     lib = nc.load()
     cfg = from_depth(12, micro_batch=1, accum_steps=1)
