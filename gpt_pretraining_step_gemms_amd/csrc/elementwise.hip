@@ -456,18 +456,20 @@ __global__ void frob_final_kernel(const float* __restrict__ partial, int parts, 
   norms[i] = sqrtf(s);
 }
 
-// src [R, C] fp32 -> X = act(src / (norm + eps)), [R, C] or transposed [C, R]
+// src [R, C] fp32 -> X = src / (norm + eps) as fp32 and in type T, [R, C] or [C, R]
 template <typename T>
 __global__ __launch_bounds__(256) void ns_prepare_kernel(const float* __restrict__ src,
                                                          MatBatch mb, int R, int C,
                                                          const float* __restrict__ norms,
                                                          float eps, int transpose,
-                                                         T* __restrict__ X, int64_t x_stride) {
+                                                         float* __restrict__ X32,
+                                                         T* __restrict__ Xh, int64_t x_stride) {
   __shared__ float tile[32][33];
   const int i = blockIdx.z;
   const float sc = 1.f / (norms[i] + eps);
   const float* s = src + mb.off(i);
-  T* x = X + (int64_t)i * x_stride;
+  float* x32 = X32 + (int64_t)i * x_stride;
+  T* xh = Xh + (int64_t)i * x_stride;
   const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
   for (int k = ty; k < 32; k += 8) {
@@ -476,33 +478,43 @@ __global__ __launch_bounds__(256) void ns_prepare_kernel(const float* __restrict
   }
   __syncthreads();
   for (int k = ty; k < 32; k += 8) {
+    int64_t off;
+    float v;
+    bool ok;
     if (!transpose) {
       const int r = r0 + k, c = c0 + tx;
-      if (r < R && c < C) x[(int64_t)r * C + c] = to_t<T>(tile[k][tx]);
+      ok = r < R && c < C;
+      off = (int64_t)r * C + c;
+      v = tile[k][tx];
     } else {
       const int c = c0 + k, r = r0 + tx;   // output row c, column r
-      if (r < R && c < C) x[(int64_t)c * R + r] = to_t<T>(tile[tx][k]);
+      ok = r < R && c < C;
+      off = (int64_t)c * R + r;
+      v = tile[tx][k];
+    }
+    if (ok) {
+      x32[off] = v;
+      xh[off] = to_t<T>(v);
     }
   }
 }
 
-template <typename T>
 __global__ __launch_bounds__(256) void ns_apply_kernel(float* __restrict__ W, MatBatch mb,
                                                        int R, int C,
-                                                       const T* __restrict__ X,
+                                                       const float* __restrict__ X,
                                                        int64_t x_stride, int transpose,
                                                        float lr, float wd,
                                                        bf16* __restrict__ shadow) {
   __shared__ float tile[32][33];
   const int i = blockIdx.z;
   float* w = W + mb.off(i);
-  const T* x = X + (int64_t)i * x_stride;
+  const float* x = X + (int64_t)i * x_stride;
   const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
   if (transpose) {   // X is [C, R]: stage a 32x32 block transposed
     for (int k = ty; k < 32; k += 8) {
       const int c = c0 + k, r = r0 + tx;
-      tile[tx][k] = (r < R && c < C) ? to_f(x[(int64_t)c * R + r]) : 0.f;
+      tile[tx][k] = (r < R && c < C) ? x[(int64_t)c * R + r] : 0.f;
     }
     __syncthreads();
   }
@@ -510,7 +522,7 @@ __global__ __launch_bounds__(256) void ns_apply_kernel(float* __restrict__ W, Ma
     const int r = r0 + k, c = c0 + tx;
     if (r < R && c < C) {
       const int64_t off = (int64_t)r * C + c;
-      const float u = transpose ? tile[k][tx] : to_f(x[off]);
+      const float u = transpose ? tile[k][tx] : x[off];
       const float nw = w[off] * (1.f - lr * wd) - lr * u;
       w[off] = nw;
       if (shadow) shadow[mb.off(i) + off] = (bf16)nw;
@@ -689,25 +701,25 @@ hipError_t nc_frob_norms(const float* src, MatBatch mb, int64_t elems, int count
 }
 
 hipError_t nc_ns_prepare(int dtype, const float* src, MatBatch mb, int R, int C, int count,
-                         const float* norms, float eps, int transpose, void* X, int64_t x_stride,
-                         hipStream_t st) {
+                         const float* norms, float eps, int transpose, float* X32, void* Xh,
+                         int64_t x_stride, hipStream_t st) {
   if (count <= 0) return hipSuccess;
   dim3 grid(ceil_div(C, 32), ceil_div(R, 32), count);
   if (dtype)
-    ns_prepare_kernel<bf16><<<grid, 256, 0, st>>>(src, mb, R, C, norms, eps, transpose, (bf16*)X, x_stride);
+    ns_prepare_kernel<bf16><<<grid, 256, 0, st>>>(src, mb, R, C, norms, eps, transpose, X32,
+                                                  (bf16*)Xh, x_stride);
   else
-    ns_prepare_kernel<float><<<grid, 256, 0, st>>>(src, mb, R, C, norms, eps, transpose, (float*)X, x_stride);
+    ns_prepare_kernel<float><<<grid, 256, 0, st>>>(src, mb, R, C, norms, eps, transpose, X32,
+                                                   (float*)Xh, x_stride);
   return hipGetLastError();
 }
 
-hipError_t nc_ns_apply(int dtype, float* W, MatBatch mb, int R, int C, int count,
-                       const void* X, int64_t x_stride, int transpose, float lr, float wd,
-                       void* shadow, hipStream_t st) {
+hipError_t nc_ns_apply(float* W, MatBatch mb, int R, int C, int count, const float* X,
+                       int64_t x_stride, int transpose, float lr, float wd, void* shadow,
+                       hipStream_t st) {
   if (count <= 0) return hipSuccess;
   dim3 grid(ceil_div(C, 32), ceil_div(R, 32), count);
-  if (dtype)
-    ns_apply_kernel<bf16><<<grid, 256, 0, st>>>(W, mb, R, C, (const bf16*)X, x_stride, transpose, lr, wd, (bf16*)shadow);
-  else
-    ns_apply_kernel<float><<<grid, 256, 0, st>>>(W, mb, R, C, (const float*)X, x_stride, transpose, lr, wd, (bf16*)shadow);
+  ns_apply_kernel<<<grid, 256, 0, st>>>(W, mb, R, C, X, x_stride, transpose, lr, wd,
+                                        (bf16*)shadow);
   return hipGetLastError();
 }

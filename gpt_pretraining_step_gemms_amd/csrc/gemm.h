@@ -18,6 +18,8 @@ enum NcEpi {
   kEpiRelu2 = 3,      // C = acc (pre-activation h), aux_out = max(acc,0)^2
   kEpiRelu2Bwd = 4,   // C = 2*max(aux_in,0)*acc   (aux_in = stored h)
   kEpiPoly = 5,       // C = p0*aux_in + p1*acc    (Newton-Schulz: b*A + c*A*A, a*X + B*X)
+  kEpiDual = 6,       // C(f32) = p0*aux_in(f32, optional) + p1*acc; aux_out = C in the
+                      // activation type (fp32 iterate + its matrix-core copy)
 };
 
 struct GemmParams {

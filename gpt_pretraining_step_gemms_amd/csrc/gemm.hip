@@ -49,6 +49,13 @@ NC_DEV void epilogue_store(const GemmParams& p, int b, int m, int n, float v) {
       static_cast<T*>(p.C)[off] = to_t<T>(2.f * fmaxf(h, 0.f) * v);
       break;
     }
+    case kEpiDual: {
+      const float a = p.aux_in ? static_cast<const float*>(p.aux_in)[off] : 0.f;
+      const float r = p.p0 * a + p.p1 * v;
+      static_cast<float*>(p.C)[off] = r;
+      static_cast<T*>(p.aux_out)[off] = to_t<T>(r);
+      break;
+    }
     case kEpiPoly: {
       const float a = to_f(static_cast<const T*>(p.aux_in)[off]);
       static_cast<T*>(p.C)[off] = to_t<T>(p.p0 * a + p.p1 * v);

@@ -75,13 +75,14 @@ struct MatBatch {
 // partial must hold count * 256 floats.
 hipError_t nc_frob_norms(const float* src, MatBatch mb, int64_t elems, int count,
                          float* partial, float* norms, hipStream_t st);
-// X[i] = act(src[i] / (norms[i] + eps)) with src[i] [R, C] fp32; X is contiguous
-// (stride x_stride), [R, C] or, when transpose != 0, [C, R].
+// X[i] = src[i] / (norms[i] + eps) with src[i] [R, C] fp32, written as fp32 (X32) and
+// in the activation type (Xh); both contiguous (stride x_stride), [R, C] or, when
+// transpose != 0, [C, R].
 hipError_t nc_ns_prepare(int dtype, const float* src, MatBatch mb, int R, int C, int count,
-                         const float* norms, float eps, int transpose, void* X,
+                         const float* norms, float eps, int transpose, float* X32, void* Xh,
                          int64_t x_stride, hipStream_t st);
-// W[i] = W[i]*(1 - lr*wd) - lr*X[i] (X read transposed when transpose != 0);
+// W[i] = W[i]*(1 - lr*wd) - lr*X[i] (fp32 X read transposed when transpose != 0);
 // shadow[i] (same addressing as W) = bf16(W[i]) when shadow != null.
-hipError_t nc_ns_apply(int dtype, float* W, MatBatch mb, int R, int C, int count,
-                       const void* X, int64_t x_stride, int transpose, float lr, float wd,
-                       void* shadow, hipStream_t st);
+hipError_t nc_ns_apply(float* W, MatBatch mb, int R, int C, int count, const float* X,
+                       int64_t x_stride, int transpose, float lr, float wd, void* shadow,
+                       hipStream_t st);

@@ -65,7 +65,11 @@ struct nc_ctx {
   // activation arena byte offsets
   std::vector<LayerAct> la;
   size_t xf, rf, x, dx, dxT, da, dqkv, dO, Dbuf, dh, z, dz, loss_rows, ws, ws_bytes, emb,
-      nsXs0, nsXs1, nsAs, nsBs, nsXr0, nsXr1, nsAr, nsBr, nsU, frob, norms, act_bytes;
+      nsU, frob, norms, act_bytes;
+  // Newton-Schulz buffers per group (0: 4L square [d,d], 1: 2L wide [d,F]): the fp32
+  // iterate X (two, ping-pong), A = X X^T, B = b A + c A A, and a copy of each in the
+  // activation type for the matrix cores.
+  struct NsBufs { size_t x32[2], xh[2], a32, ah, b32, bh; } ns[2];
   int splits_qkv, splits_o, splits_1, splits_2, splits_head;
   char* pa = nullptr;
   char* aa = nullptr;
@@ -214,14 +218,18 @@ void plan(nc_ctx* c) {
   c->ws = a.take(std::max<size_t>(ws, 256));
   c->emb = a.take(nc_embed_bwd_scratch_bytes((int)N, V, d));
   // Newton-Schulz: 4L square [d,d] and 2L wide [d,F] matrices
-  c->nsXs0 = a.take((size_t)4 * L * d * d * es);
-  c->nsXs1 = a.take((size_t)4 * L * d * d * es);
-  c->nsAs = a.take((size_t)4 * L * d * d * es);
-  c->nsBs = a.take((size_t)4 * L * d * d * es);
-  c->nsXr0 = a.take((size_t)2 * L * d * F * es);
-  c->nsXr1 = a.take((size_t)2 * L * d * F * es);
-  c->nsAr = a.take((size_t)2 * L * d * d * es);
-  c->nsBr = a.take((size_t)2 * L * d * d * es);
+  for (int g = 0; g < 2; ++g) {
+    const size_t cnt = (size_t)(g ? 2 : 4) * L, xe = cnt * d * (g ? F : d), ae = cnt * d * d;
+    auto& b = c->ns[g];
+    for (int k = 0; k < 2; ++k) {
+      b.x32[k] = a.take(xe * 4);
+      b.xh[k] = a.take(xe * es);
+    }
+    b.a32 = a.take(ae * 4);
+    b.ah = a.take(ae * es);
+    b.b32 = a.take(ae * 4);
+    b.bh = a.take(ae * es);
+  }
   c->nsU = c->ocfg.muon_nesterov ? a.take((size_t)c->n_block * 4) : 0;
   c->frob = a.take((size_t)6 * std::max(L, 1) * 256 * 4);
   c->norms = a.take((size_t)6 * std::max(L, 1) * 4);
@@ -257,7 +265,7 @@ bool in_arena(const nc_ctx* c, const void* p, size_t bytes) {
 // Host check of every operand extent of a GEMM against the arenas.
 bool operands_in_arenas(nc_ctx* c, const GemmParams& g) {
   const size_t es = c->es;
-  const bool c_f32 = g.epi == kEpiStoreF32 || g.epi == kEpiAccF32;
+  const bool c_f32 = g.epi == kEpiStoreF32 || g.epi == kEpiAccF32 || g.epi == kEpiDual;
   auto extent = [](int64_t rows, int64_t cols, int64_t ld, int64_t bstride, int batch) {
     // elements spanned by a [rows, cols] row-major view with leading dim ld
     return (int64_t)(batch - 1) * bstride + (rows - 1) * ld + cols;
@@ -271,7 +279,7 @@ bool operands_in_arenas(nc_ctx* c, const GemmParams& g) {
   if (!in_arena(c, g.A, ea * es)) bad = "A";
   else if (!in_arena(c, g.B, eb * es)) bad = "B";
   else if (!in_arena(c, g.C, ec * (c_f32 ? 4 : es))) bad = "C";
-  else if (g.aux_in && !in_arena(c, g.aux_in, ec * es)) bad = "aux_in";
+  else if (g.aux_in && !in_arena(c, g.aux_in, ec * (g.epi == kEpiDual ? 4 : es))) bad = "aux_in";
   else if (g.aux_out && !in_arena(c, g.aux_out, ec * es)) bad = "aux_out";
   else if (g.splits > 1 && (size_t)g.splits * g.batch * g.M * g.N * 4 > g.workspace_bytes)
     bad = "split-K workspace";
@@ -532,26 +540,30 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
   return NC_OK;
 }
 
-static nc_status newton_schulz(nc_ctx* ctx, int count, int R, int C, size_t x0, size_t x1,
-                               size_t Ab, size_t Bb, size_t* result) {
+// Newton-Schulz on `count` matrices X [R, C] (R <= C) of group g, starting from
+// the prepared buffers x32[0]/xh[0].  Every iterate is kept in fp32; only the
+// matrix-core inputs are rounded.  *result = byte offset of the final fp32 X.
+static nc_status newton_schulz(nc_ctx* ctx, int g, int count, int R, int C, size_t* result) {
   const nc_optim_config& o = ctx->ocfg;
   char* aa = ctx->aa;
-  size_t cur = x0, nxt = x1;
+  const auto& b = ctx->ns[g];
+  int cur = 0;
   const int64_t sx = (int64_t)R * C, sa = (int64_t)R * R;
   for (int it = 0; it < o.ns_steps; ++it) {
-    const float a = o.ns_coeffs[it][0], b = o.ns_coeffs[it][1], c = o.ns_coeffs[it][2];
+    const float ca = o.ns_coeffs[it][0], cb = o.ns_coeffs[it][1], cc = o.ns_coeffs[it][2];
     // A = X X^T
-    NC_GEMM(gemm(ctx, aa + cur, C, kKCont, aa + cur, C, kKCont, aa + Ab, R, R, R, C, kEpiStore,
-                nullptr, nullptr, 1, count, sx, sx, sa), "ns gram");
+    NC_GEMM(gemm(ctx, aa + b.xh[cur], C, kKCont, aa + b.xh[cur], C, kKCont, aa + b.a32, R, R, R,
+                 C, kEpiDual, nullptr, aa + b.ah, 1, count, sx, sx, sa, 0.f, 1.f), "ns gram");
     // B = b A + c A A   (A symmetric: A A = A A^T)
-    NC_GEMM(gemm(ctx, aa + Ab, R, kKCont, aa + Ab, R, kKCont, aa + Bb, R, R, R, R, kEpiPoly,
-                aa + Ab, nullptr, 1, count, sa, sa, sa, b, c), "ns poly");
+    NC_GEMM(gemm(ctx, aa + b.ah, R, kKCont, aa + b.ah, R, kKCont, aa + b.b32, R, R, R, R,
+                 kEpiDual, aa + b.a32, aa + b.bh, 1, count, sa, sa, sa, cb, cc), "ns poly");
     // X' = a X + B X
-    NC_GEMM(gemm(ctx, aa + Bb, R, kKCont, aa + cur, C, kMNCont, aa + nxt, C, R, C, R, kEpiPoly,
-                aa + cur, nullptr, 1, count, sa, sx, sx, a, 1.f), "ns update");
-    std::swap(cur, nxt);
+    NC_GEMM(gemm(ctx, aa + b.bh, R, kKCont, aa + b.xh[cur], C, kMNCont, aa + b.x32[cur ^ 1], C,
+                 R, C, R, kEpiDual, aa + b.x32[cur], aa + b.xh[cur ^ 1], 1, count, sa, sx, sx,
+                 ca, 1.f), "ns update");
+    cur ^= 1;
   }
-  *result = cur;
+  *result = b.x32[cur];
   return NC_OK;
 }
 
@@ -595,24 +607,29 @@ nc_status nc_optimizer_step(nc_ctx* ctx, float lr_mult) {
   NC_TRY(nc_frob_norms(U + o2, one, dF, L, frob + 5 * L * 256, norms + 5 * L, st), "norms W2");
   char* aa = ctx->aa;
   // orthogonalise on the short side: square [d,d]; W1 [F,d] -> [d,F]; W2 [d,F]
-  NC_TRY(nc_ns_prepare(dt, U, sq, d, d, 4 * L, norms, o.ns_eps, 0, aa + ctx->nsXs0, dd, st),
-         "prep sq");
-  NC_TRY(nc_ns_prepare(dt, U + o1, one, F, d, L, norms + 4 * L, o.ns_eps, 1, aa + ctx->nsXr0, dF,
-                       st), "prep W1");
+  const auto& q = ctx->ns[0];
+  const auto& w = ctx->ns[1];
+  const size_t w2x = (size_t)L * dF;   // W2 matrices follow the L W1 matrices in group 1
+  NC_TRY(nc_ns_prepare(dt, U, sq, d, d, 4 * L, norms, o.ns_eps, 0, A<float>(ctx, q.x32[0]),
+                       aa + q.xh[0], dd, st), "prep sq");
+  NC_TRY(nc_ns_prepare(dt, U + o1, one, F, d, L, norms + 4 * L, o.ns_eps, 1,
+                       A<float>(ctx, w.x32[0]), aa + w.xh[0], dF, st), "prep W1");
   NC_TRY(nc_ns_prepare(dt, U + o2, one, d, F, L, norms + 5 * L, o.ns_eps, 0,
-                       aa + ctx->nsXr0 + (size_t)L * dF * ctx->es, dF, st), "prep W2");
+                       A<float>(ctx, w.x32[0]) + w2x, aa + w.xh[0] + w2x * ctx->es, dF, st),
+         "prep W2");
   size_t xs, xr;
-  nc_status s = newton_schulz(ctx, 4 * L, d, d, ctx->nsXs0, ctx->nsXs1, ctx->nsAs, ctx->nsBs, &xs);
+  nc_status s = newton_schulz(ctx, 0, 4 * L, d, d, &xs);
   if (s != NC_OK) return s;
-  s = newton_schulz(ctx, 2 * L, d, F, ctx->nsXr0, ctx->nsXr1, ctx->nsAr, ctx->nsBr, &xr);
+  s = newton_schulz(ctx, 1, 2 * L, d, F, &xr);
   if (s != NC_OK) return s;
   const float lr = o.muon_lr * lr_mult;
   char* sh = dt ? ctx->pa + ctx->oSh : nullptr;
-  NC_TRY(nc_ns_apply(dt, Pm, sq, d, d, 4 * L, aa + xs, dd, 0, lr, o.muon_wd, sh, st), "apply sq");
-  NC_TRY(nc_ns_apply(dt, Pm + o1, one, F, d, L, aa + xr, dF, 1, lr, o.muon_wd,
+  NC_TRY(nc_ns_apply(Pm, sq, d, d, 4 * L, A<float>(ctx, xs), dd, 0, lr, o.muon_wd, sh, st),
+         "apply sq");
+  NC_TRY(nc_ns_apply(Pm + o1, one, F, d, L, A<float>(ctx, xr), dF, 1, lr, o.muon_wd,
                      sh ? sh + o1 * 2 : nullptr, st), "apply W1");
-  NC_TRY(nc_ns_apply(dt, Pm + o2, one, d, F, L, aa + xr + (size_t)L * dF * ctx->es, dF, 0, lr,
-                     o.muon_wd, sh ? sh + o2 * 2 : nullptr, st), "apply W2");
+  NC_TRY(nc_ns_apply(Pm + o2, one, d, F, L, A<float>(ctx, xr) + w2x, dF, 0, lr, o.muon_wd,
+                     sh ? sh + o2 * 2 : nullptr, st), "apply W2");
   return NC_OK;
 }
 
@@ -739,9 +756,10 @@ nc_status nc_op_gemm(int32_t dtype, const void* A_, int64_t lda, int32_t al, con
                      void* stream) {
   if (!A_ || !B_ || !C_ || M < 0 || N < 0 || K < 1 || batch < 1) return NC_ERR_INVALID_ARG;
   if ((dtype != NC_FP32 && dtype != NC_BF16) || al < 0 || al > 1 || bl < 0 || bl > 1 ||
-      epi < 0 || epi > kEpiPoly)
+      epi < 0 || epi > kEpiDual)
     return NC_ERR_INVALID_ARG;
-  if ((epi == kEpiRelu2 && !aux_out) || ((epi == kEpiRelu2Bwd || epi == kEpiPoly) && !aux_in))
+  if (((epi == kEpiRelu2 || epi == kEpiDual) && !aux_out) ||
+      ((epi == kEpiRelu2Bwd || epi == kEpiPoly) && !aux_in))
     return NC_ERR_INVALID_ARG;
   if (dtype == NC_BF16) {
     if (K % 8 || (al == kMNCont && M % 8) || (bl == kMNCont && N % 8)) return NC_ERR_UNSUPPORTED;

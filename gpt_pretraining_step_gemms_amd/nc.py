@@ -22,7 +22,7 @@ NC_ERR_HIP, NC_ERR_STATE, NC_ERR_NONFINITE = 4, 5, 6
 NC_FP32, NC_BF16 = 0, 1
 NC_PARAM, NC_GRAD, NC_MOMENTUM, NC_ADAM_M, NC_ADAM_V = 0, 1, 2, 3, 4
 NC_K_CONTIGUOUS, NC_MN_CONTIGUOUS = 0, 1
-EPI_STORE, EPI_STORE_F32, EPI_ACC_F32, EPI_RELU2, EPI_RELU2_BWD, EPI_POLY = range(6)
+EPI_STORE, EPI_STORE_F32, EPI_ACC_F32, EPI_RELU2, EPI_RELU2_BWD, EPI_POLY, EPI_DUAL = range(7)
 
 
 class NcError(RuntimeError):

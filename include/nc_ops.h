@@ -23,9 +23,12 @@ enum {
   NC_EPI_RELU2 = 3,       /* C = acc; aux_out = max(acc, 0)^2 (ReLU^2 MLP, apidog.com
                              "1. Model GPT (nanochat/gpt.py)") */
   NC_EPI_RELU2_BWD = 4,   /* C = 2 max(aux_in, 0) * acc (derivative of ReLU^2) */
-  NC_EPI_POLY = 5         /* C = p0 * aux_in + p1 * acc (Newton-Schulz steps
+  NC_EPI_POLY = 5,        /* C = p0 * aux_in + p1 * acc (Newton-Schulz steps
                              B = b A + c A A and X = a X + B X, apidog.com
                              "2. Pengoptimal Muon (nanochat/optim.py)") */
+  NC_EPI_DUAL = 6         /* C (fp32) = p0 * aux_in (fp32, may be NULL) + p1 * acc and
+                             aux_out = C in the activation dtype: the same steps with
+                             an fp32 iterate and its matrix-core copy */
 };
 
 /* Batched GEMM: for each batch index z < batch,

@@ -73,6 +73,10 @@ def test_gemm_epilogues_bf16():
     nc.gemm(dA, 0, dB, 0, R, M, N, K, nc.EPI_RELU2_BWD, aux_in=aux)
     Pn = torch.empty(M, N, dtype=BF, device="cuda")
     nc.gemm(dA, 0, dB, 0, Pn, M, N, K, nc.EPI_POLY, aux_in=aux, p0=1.5, p1=-0.25)
+    aux32 = dev(rng.standard_normal((M, N)), F32)
+    D32 = torch.empty(M, N, dtype=F32, device="cuda")
+    Dh = torch.empty(M, N, dtype=BF, device="cuda")
+    nc.gemm(dA, 0, dB, 0, D32, M, N, K, nc.EPI_DUAL, aux_in=aux32, aux_out=Dh, p0=3.0, p1=0.5)
     torch.cuda.synchronize()
     tol = 2 ** -8
     assert max_rel(host(C), 0.5 * acc) < tol
@@ -81,6 +85,9 @@ def test_gemm_epilogues_bf16():
     assert max_rel(host(G), np.maximum(acc, 0) ** 2) < tol
     assert max_rel(host(R), 2 * np.maximum(host(aux), 0) * acc) < tol
     assert max_rel(host(Pn), 1.5 * host(aux) - 0.25 * acc) < tol
+    dual = 3.0 * host(aux32) + 0.5 * acc
+    assert max_rel(host(D32), dual) < 2e-6
+    assert max_rel(host(Dh), dual) < tol
 
 
 @pytest.mark.parametrize("splits", [1, 4])

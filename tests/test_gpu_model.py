@@ -96,8 +96,10 @@ def test_zero_head_loss_is_ln_vocab_and_other_grads_vanish(cfg):
     for n, g in grads.items():
         if n != "Wh":
             assert not np.any(g), n
-    # softmax rows sum to one: sum_v dWh[v, :] = 0
-    assert np.max(np.abs(grads["Wh"].sum(0))) <= 1e-3 * np.max(np.abs(grads["Wh"]))
+    # softmax rows sum to one: sum_v dWh[v, :] = 0 up to the rounding of dz to the
+    # activation type: |sum_v dz[n, v]| <= 2^-8 sum_v |dz[n, v]| = 2^-7 / N per row
+    tol = 1e-5 if cfg.dtype == "fp32" else 1e-2
+    assert np.max(np.abs(grads["Wh"].sum(0))) <= tol * np.max(np.abs(grads["Wh"]))
     m.close()
 
 
