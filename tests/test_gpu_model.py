@@ -98,8 +98,10 @@ def test_zero_head_loss_is_ln_vocab_and_other_grads_vanish(cfg):
             assert not np.any(g), n
     # softmax rows sum to one: sum_v dWh[v, :] = 0 up to the rounding of dz to the
     # activation type: |sum_v dz[n, v]| <= 2^-8 sum_v |dz[n, v]| = 2^-7 / N per row
-    tol = 1e-5 if cfg.dtype == "fp32" else 1e-2
-    assert np.max(np.abs(grads["Wh"].sum(0))) <= tol * np.max(np.abs(grads["Wh"]))
+    # (fp32: each entry carries ~2^-24 sqrt(N) relative accumulation error)
+    tol = 2e-5 if cfg.dtype == "fp32" else 1e-2
+    gwh = grads["Wh"].astype(np.float64)
+    assert np.max(np.abs(gwh.sum(0))) <= tol * np.max(np.abs(gwh))
     m.close()
 
 
