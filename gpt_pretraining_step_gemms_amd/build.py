@@ -19,7 +19,7 @@ SOURCES = ["gemm.hip", "attention.hip", "elementwise.hip", "runtime.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 CFLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC",
     # packed fp32 ops are kept off (plain fp32 VALU code only)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}",

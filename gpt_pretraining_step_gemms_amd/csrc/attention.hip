@@ -82,13 +82,91 @@ NC_DEV f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 // ================================================================ forward
-__global__ __launch_bounds__(256, 1) void attn_fwd_kernel(
+// K and V tiles reach LDS by direct loads (global_load_lds, 16 B per lane, 1 KB
+// per wave instruction), double-buffered, in their token-major layout:
+//   K tile [64 keys][128] -> S^T fragments (rows = keys) read with ds_read_b128;
+//   V tile [64 keys][128] -> O^T = V^T P^T fragments (rows = head dims, 8 keys per lane) read with
+//        ds_read_b64_tr_b16, each 16-lane group taking a 4-key x 16-dim block.
+// Two workgroups fit on a CU (64 KB of LDS each, <= 256 registers per wave),
+// so one workgroup's softmax overlaps the other's matrix products.
+NC_DEV void fa_dma16(const void* g, const bf16* lds) {
+  const unsigned a = (unsigned)(size_t)(__attribute__((address_space(3))) const void*)lds;
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(__builtin_amdgcn_readfirstlane(a))
+      : "memory");
+}
+
+template <int N>
+NC_DEV void fa_wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+NC_DEV void fa_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Swizzle of 16-byte chunks in a [rows][128] bf16 tile: chunk c of row r is
+// stored at c ^ fa_swz(r).  Eight consecutive rows read at one chunk
+// (ds_read_b128) and four consecutive rows read at two neighbouring chunks
+// (ds_read_b64_tr_b16) both hit 8 distinct bank groups.
+NC_DEV int fa_swz(int r) { return (2 * (r & 3)) | ((r >> 2) & 1); }
+
+// this wave's share (4 x 1 KB) of a 64-row x 128 token-major tile into LDS
+NC_DEV void fa_issue_rows(const bf16* src, int64_t ld, int row0, bf16* tile, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int blk = wave * 4 + i;                 // 16 blocks of 4 rows
+    const int r = blk * 4 + (lane >> 4);
+    const int c = (lane & 15) ^ fa_swz(r);
+    fa_dma16(src + (int64_t)(row0 + r) * ld + c * 8, tile + blk * 512);
+  }
+}
+
+// 64 consecutive floats (4 bytes per lane) into LDS; one wave
+NC_DEV void fa_dma4(const float* g, const float* lds) {
+  const unsigned a = (unsigned)(size_t)(__attribute__((address_space(3))) const void*)lds;
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dword %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(__builtin_amdgcn_readfirstlane(a))
+      : "memory");
+}
+
+typedef __bf16 fa_bf16x4 __attribute__((ext_vector_type(4)));
+NC_DEV bf16x8 fa_frag_k(const bf16* tile, int r, int c) {
+  return *reinterpret_cast<const bf16x8*>(tile + r * 128 + ((c ^ fa_swz(r)) << 3));
+}
+// 8 values of head dim `col_base + lane%16` (within a 16-wide column block) at
+// key rows row_base + {0..3} and row_base + 8 + {0..3}, from a [key][128] tile
+// stored with the fa_swz swizzle (rows r and r + 8 share it)
+NC_DEV bf16x8 fa_frag_vt(const bf16* tile, int row_base, int col_base, int lane) {
+  const int t = lane & 15;
+  const int r = row_base + (t >> 2);
+  const int col = col_base + 4 * (t & 3);
+  const bf16* p0 = tile + r * 128 + (((col >> 3) ^ fa_swz(r)) << 3) + (col & 7);
+  const bf16* p1 = p0 + 8 * 128;                 // row + 8: same swizzle
+  const fa_bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) fa_bf16x4*)p0);
+  const fa_bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) fa_bf16x4*)p1);
+  bf16x8 v;
+  v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+  v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+  return v;
+}
+
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, bf16* __restrict__ o, int64_t ldo, float* __restrict__ lse, int T, int H,
     float scale_log2) {
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * 64 * 128 + 2 * 128 * 64];
-  // Ks[buf] = smem + buf*8192, VTs[buf] = smem + 16384 + buf*8192
-  constexpr int KT = 64 * 128;
+  constexpr int KT = 64 * 128;                    // one 64 x 128 tile
+  __shared__ __attribute__((aligned(1024))) bf16 st0[2 * KT];   // K | V of even tiles
+  __shared__ __attribute__((aligned(1024))) bf16 st1[2 * KT];   // K | V of odd tiles
 
   const int nqb = T / 128;
   const int qb = nqb - 1 - (int)(blockIdx.x % nqb);
@@ -97,7 +175,8 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(
   const bf16* qg = q + base;
   const bf16* kg = k + base;
   const bf16* vg = v + base;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const int q0w = qb * 128 + wave * 32;
   const int myq = q0w + l32;
@@ -115,79 +194,73 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(
   float m = -INFINITY, l = 0.f;
 
   const int n_kv = 2 * qb + 2;
-  // loader roles: threads 0..127 -> K block, 128..255 -> V block (transposed)
-  const int lt = tid & 127, rb = lt >> 4, cb = lt & 15;
-  const bool is_k = tid < 128;
-  Blk8 pre;
-  load_blk(is_k ? kg : vg, ld, rb * 8, cb * 8, pre);
-  if (is_k) store_nrm(smem, rb, cb, pre); else store_trs(smem + 2 * KT, rb, cb, pre);
-  __syncthreads();
-
-  for (int kv = 0; kv < n_kv; ++kv) {
-    const int cur = kv & 1;
-    const bool more = kv + 1 < n_kv;
-    if (more) load_blk(is_k ? kg : vg, ld, (kv + 1) * 64 + rb * 8, cb * 8, pre);
-
-    if (kv * 64 <= q0w + 31) {
-      const bf16* ks = smem + cur * KT;
-      const bf16* vts = smem + (2 + cur) * KT;
-      f32x16 sacc[2];
+  auto issue = [&](int kv, bf16* st) {
+    fa_issue_rows(kg, ld, kv * 64, st, wave, lane);
+    fa_issue_rows(vg, ld, kv * 64, st + KT, wave, lane);
+  };
+  auto step = [&](int kv, const bf16* ks, bf16* next) {
+    fa_wait_vmcnt<0>();         // this wave's loads of tile kv have landed
+    fa_barrier();               // ... and every wave's; tile kv-1 is no longer read
+    if (kv + 1 < n_kv) issue(kv + 1, next);
+    if (kv * 64 > q0w + 31) return;               // keys all after this wave's queries
+    const bf16* vs = ks + KT;
+    f32x16 sacc[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
+      for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
 #pragma unroll
-        for (int s = 0; s < 8; ++s)
-          sacc[kb] = mfma(frag_nrm(ks, kb * 32 + l32, s * 2 + half), qf[s], sacc[kb]);
+      for (int s = 0; s < 8; ++s)
+        sacc[kb] = mfma(fa_frag_k(ks, kb * 32 + l32, s * 2 + half), qf[s], sacc[kb]);
+    }
+    const bool need_mask = kv * 64 + 63 > q0w;
+    float sv[2][16];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float x = sacc[kb][e] * scale_log2;
+        if (need_mask) {
+          const int key = kv * 64 + kb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+          if (key > myq) x = -INFINITY;
+        }
+        sv[kb][e] = x;
+        mt = fmaxf(mt, x);
       }
-      const bool need_mask = kv * 64 + 63 > q0w;
-      float sv[2][16];
-      float mt = -INFINITY;
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float mn = fmaxf(m, mt);
+    const float alpha = exp2f(m - mn);
+    float ls = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float x = sacc[kb][e] * scale_log2;
-          if (need_mask) {
-            const int key = kv * 64 + kb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
-            if (key > myq) x = -INFINITY;
-          }
-          sv[kb][e] = x;
-          mt = fmaxf(mt, x);
-        }
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float mn = fmaxf(m, mt);
-      const float alpha = exp2f(m - mn);
-      float ls = 0.f;
+      for (int e = 0; e < 16; ++e) {
+        const float pv = exp2f(sv[kb][e] - mn);
+        sv[kb][e] = pv;
+        ls += pv;
+      }
+    l = l * alpha + ls;
+    m = mn;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = exp2f(sv[kb][e] - mn);
-          sv[kb][e] = p;
-          ls += p;
-        }
-      l = l * alpha + ls;
-      m = mn;
+      for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 pf = pack_half(sv[j >> 1], j & 1);
+      const int row_base = (j >> 1) * 32 + (j & 1) * 16 + half * 4;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
-      bf16x8 pf[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) pf[j] = pack_half(sv[j >> 1], j & 1);
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          oacc[db] = mfma(frag_trs(vts, db * 32 + l32, (j >> 1) * 32 + (j & 1) * 16 + half * 4),
-                          pf[j], oacc[db]);
+        oacc[db] = mfma(fa_frag_vt(vs, row_base, db * 32 + 16 * ((lane >> 4) & 1), lane), pf,
+                        oacc[db]);
     }
-    if (more) {
-      if (is_k) store_nrm(smem + (cur ^ 1) * KT, rb, cb, pre);
-      else store_trs(smem + (2 + (cur ^ 1)) * KT, rb, cb, pre);
-    }
-    __syncthreads();
+  };
+
+  issue(0, st0);
+  for (int kv = 0; kv < n_kv; kv += 2) {
+    step(kv, st0, st1);
+    if (kv + 1 < n_kv) step(kv + 1, st1, st0);
   }
 
   const float lt_sum = l + __shfl_xor(l, 32, 64);
@@ -196,7 +269,8 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(
 
   // stage O (this wave's 32 x 128) through LDS with padded rows, then 16-B stores
   constexpr int OSTR = 136;
-  bf16* os = smem + wave * 32 * OSTR;
+  __syncthreads();
+  bf16* os = (wave < 2 ? st0 : st1) + (wave & 1) * 32 * OSTR;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -217,15 +291,21 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(
   }
 }
 
+
 // ============================================================ dK / dV
+// A workgroup owns 128 keys (4 waves x 32; K and V rows of each wave's keys
+// stay in registers as the B operands) and walks the 64-query tiles from the
+// diagonal down.  Q, dO and the tile's log-sum-exp and D reach LDS by direct
+// loads, double-buffered; Q^T and dO^T fragments come from transpose reads.
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, const bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ lse,
     const float* __restrict__ Dv, bf16* __restrict__ dk, bf16* __restrict__ dv, int64_t ldd,
     int T, int H, float scale_log2, float scale) {
-  constexpr int TILE = 64 * 128;
-  constexpr int BUF = 4 * TILE + 2 * 64 * 2;   // Q, Q^T, dO, dO^T + lse2, D (as bf16 slots)
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * BUF];
+  constexpr int KT = 64 * 128;
+  constexpr int STAGE = 2 * KT + 256;             // Q | dO | lse[64] D[64] (fp32)
+  __shared__ __attribute__((aligned(1024))) bf16 st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) bf16 st1[STAGE];
 
   const int nkb = T / 128;
   const int kblk = blockIdx.x % nkb;
@@ -234,7 +314,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
   const int64_t obase = (int64_t)b * T * ldo + h * 128;
   const float* lse_bh = lse + ((int64_t)b * H + h) * T;
   const float* D_bh = Dv + ((int64_t)b * H + h) * T;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const int k0w = kblk * 128 + wave * 32;
   const int mykey = k0w + l32;
@@ -252,90 +333,73 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
     for (int e = 0; e < 16; ++e) { dkacc[i][e] = 0.f; dvacc[i][e] = 0.f; }
 
   const int qt0 = kblk * 2, nqt = T / 64;
-  const int lt = tid & 127, rb = lt >> 4, cb = lt & 15;
-  const bool is_q = tid < 128;
-  const bf16* src = is_q ? q + base : dO + obase;
-  const int64_t lds_ld = is_q ? ld : ldo;
-  Blk8 pre;
-  float pre_l = 0.f, pre_d = 0.f;
-  auto bufp = [&](int i) { return smem + i * BUF; };
-  auto stage = [&](int qt, bf16* buf) {
-    bf16* nrm = buf + (is_q ? 0 : 2 * TILE);
-    bf16* trs = buf + (is_q ? TILE : 3 * TILE);
-    store_nrm(nrm, rb, cb, pre);
-    store_trs(trs, rb, cb, pre);
-    float* stats = reinterpret_cast<float*>(buf + 4 * TILE);
-    if (tid < 64) { stats[tid] = pre_l; stats[64 + tid] = pre_d; }
-    (void)qt;
-  };
-  auto fetch = [&](int qt) {
-    load_blk(src, lds_ld, qt * 64 + rb * 8, cb * 8, pre);
-    if (tid < 64) { pre_l = lse_bh[qt * 64 + tid] * kLog2e; pre_d = D_bh[qt * 64 + tid]; }
-  };
-  fetch(qt0);
-  stage(qt0, bufp(0));
-  __syncthreads();
-
-  for (int qt = qt0; qt < nqt; ++qt) {
-    const int cur = (qt - qt0) & 1;
-    const bool more = qt + 1 < nqt;
-    if (more) fetch(qt + 1);
-    if (qt * 64 + 63 >= k0w) {
-      const bf16* buf = bufp(cur);
-      const bf16* Qs = buf;
-      const bf16* QTs = buf + TILE;
-      const bf16* dOs = buf + 2 * TILE;
-      const bf16* dOTs = buf + 3 * TILE;
-      const float* lse2s = reinterpret_cast<const float*>(buf + 4 * TILE);
-      const float* Ds = lse2s + 64;
-      f32x16 sacc[2], pacc[2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) { sacc[qb][e] = 0.f; pacc[qb][e] = 0.f; }
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          sacc[qb] = mfma(frag_nrm(Qs, qb * 32 + l32, s * 2 + half), kf[s], sacc[qb]);
-          pacc[qb] = mfma(frag_nrm(dOs, qb * 32 + l32, s * 2 + half), vf[s], pacc[qb]);
-        }
-      }
-      const bool need_mask = qt * 64 < k0w + 31;
-      float p[2][16], ds[2][16];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int ql = qb * 32 + g * 8 + half * 4;
-          const float4 l4 = *reinterpret_cast<const float4*>(lse2s + ql);
-          const float4 d4 = *reinterpret_cast<const float4*>(Ds + ql);
-          const float la[4] = {l4.x, l4.y, l4.z, l4.w};
-          const float da[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int e = g * 4 + i;
-            float pv = exp2f(sacc[qb][e] * scale_log2 - la[i]);
-            if (need_mask && qt * 64 + ql + i < mykey) pv = 0.f;
-            p[qb][e] = pv;
-            ds[qb][e] = pv * (pacc[qb][e] - da[i]);
-          }
-        }
-      bf16x8 pa[4], dsa[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        pa[j] = pack_half(p[j >> 1], j & 1);
-        dsa[j] = pack_half(ds[j >> 1], j & 1);
-      }
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int o1 = (j >> 1) * 32 + (j & 1) * 16 + half * 4;
-          dvacc[db] = mfma(pa[j], frag_trs(dOTs, db * 32 + l32, o1), dvacc[db]);
-          dkacc[db] = mfma(dsa[j], frag_trs(QTs, db * 32 + l32, o1), dkacc[db]);
-        }
+  auto issue = [&](int qt, bf16* st) {
+    fa_issue_rows(q + base, ld, qt * 64, st, wave, lane);
+    fa_issue_rows(dO + obase, ldo, qt * 64, st + KT, wave, lane);
+    if (wave == 0) {
+      float* stats = reinterpret_cast<float*>(st + 2 * KT);
+      fa_dma4(lse_bh + qt * 64 + lane, stats);
+      fa_dma4(D_bh + qt * 64 + lane, stats + 64);
     }
-    if (more) stage(qt + 1, bufp(cur ^ 1));
-    __syncthreads();
+  };
+  auto step = [&](int qt, const bf16* cur, bf16* next) {
+    fa_wait_vmcnt<0>();
+    fa_barrier();
+    if (qt + 1 < nqt) issue(qt + 1, next);
+    if (qt * 64 + 63 < k0w) return;               // queries all before this wave's keys
+    const bf16* Qs = cur;
+    const bf16* dOs = cur + KT;
+    const float* lse_s = reinterpret_cast<const float*>(cur + 2 * KT);
+    const float* D_s = lse_s + 64;
+    f32x16 sacc[2], pacc[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) { sacc[qb][e] = 0.f; pacc[qb][e] = 0.f; }
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        sacc[qb] = mfma(fa_frag_k(Qs, qb * 32 + l32, s * 2 + half), kf[s], sacc[qb]);
+        pacc[qb] = mfma(fa_frag_k(dOs, qb * 32 + l32, s * 2 + half), vf[s], pacc[qb]);
+      }
+    }
+    const bool need_mask = qt * 64 < k0w + 31;
+    float p[2][16], ds[2][16];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int ql = qb * 32 + g * 8 + half * 4;
+        const float4 l4 = *reinterpret_cast<const float4*>(lse_s + ql);
+        const float4 d4 = *reinterpret_cast<const float4*>(D_s + ql);
+        const float la[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float da[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = g * 4 + i;
+          float pv = exp2f(sacc[qb][e] * scale_log2 - la[i] * kLog2e);
+          if (need_mask && qt * 64 + ql + i < mykey) pv = 0.f;
+          p[qb][e] = pv;
+          ds[qb][e] = pv * (pacc[qb][e] - da[i]);
+        }
+      }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 pa = pack_half(p[j >> 1], j & 1);
+      const bf16x8 dsa = pack_half(ds[j >> 1], j & 1);
+      const int row_base = (j >> 1) * 32 + (j & 1) * 16 + half * 4;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int cb = db * 32 + 16 * ((lane >> 4) & 1);
+        dvacc[db] = mfma(pa, fa_frag_vt(dOs, row_base, cb, lane), dvacc[db]);
+        dkacc[db] = mfma(dsa, fa_frag_vt(Qs, row_base, cb, lane), dkacc[db]);
+      }
+    }
+  };
+
+  issue(qt0, st0);
+  for (int qt = qt0; qt < nqt; qt += 2) {
+    step(qt, st0, st1);
+    if (qt + 1 < nqt) step(qt + 1, st1, st0);
   }
 
   // C[key][d]: lane holds column d = db*32 + l32, rows key = 8*(e/4) + 4*half + e%4
@@ -351,21 +415,27 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
 }
 
 // ================================================================== dQ
-__global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
+// A workgroup owns 128 queries (4 waves x 32) and walks the 64-key tiles up
+// to the diagonal, like the forward pass: S^T = K Q^T and dP^T = V dO^T with
+// one query per lane, then dQ += dS K with K^T fragments from transpose reads.
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, const bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ lse,
     const float* __restrict__ Dv, bf16* __restrict__ dq, int64_t ldd, int T, int H,
     float scale_log2, float scale) {
-  constexpr int TILE = 64 * 128;
-  constexpr int BUF = 3 * TILE;   // K, K^T, V
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * BUF];
+  constexpr int KT = 64 * 128;
+  __shared__ __attribute__((aligned(1024))) bf16 st0[2 * KT];   // K | V
+  __shared__ __attribute__((aligned(1024))) bf16 st1[2 * KT];
 
   const int nqb = T / 128;
   const int qb = nqb - 1 - (int)(blockIdx.x % nqb);
   const int bh = blockIdx.x / nqb, b = bh / H, h = bh % H;
   const int64_t base = (int64_t)b * T * ld + h * 128;
   const int64_t obase = (int64_t)b * T * ldo + h * 128;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bf16* kg = k + base;
+  const bf16* vg = v + base;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const int q0w = qb * 128 + wave * 32;
   const int myq = q0w + l32;
@@ -385,58 +455,53 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
     for (int e = 0; e < 16; ++e) dqacc[i][e] = 0.f;
 
   const int n_kv = 2 * qb + 2;
-  const int lt = tid & 127, rb = lt >> 4, cb = lt & 15;
-  const bool is_k = tid < 128;
-  const bf16* src = (is_k ? k : v) + base;
-  Blk8 pre;
-  auto stage = [&](bf16* buf) {
-    if (is_k) { store_nrm(buf, rb, cb, pre); store_trs(buf + TILE, rb, cb, pre); }
-    else store_nrm(buf + 2 * TILE, rb, cb, pre);
+  auto issue = [&](int kv, bf16* st) {
+    fa_issue_rows(kg, ld, kv * 64, st, wave, lane);
+    fa_issue_rows(vg, ld, kv * 64, st + KT, wave, lane);
   };
-  load_blk(src, ld, rb * 8, cb * 8, pre);
-  stage(smem);
-  __syncthreads();
-
-  for (int kv = 0; kv < n_kv; ++kv) {
-    const int cur = kv & 1;
-    const bool more = kv + 1 < n_kv;
-    if (more) load_blk(src, ld, (kv + 1) * 64 + rb * 8, cb * 8, pre);
-    if (kv * 64 <= q0w + 31) {
-      const bf16* Ks = smem + cur * BUF;
-      const bf16* KTs = Ks + TILE;
-      const bf16* Vs = Ks + 2 * TILE;
-      f32x16 sacc[2], pacc[2];
+  auto step = [&](int kv, const bf16* cur, bf16* next) {
+    fa_wait_vmcnt<0>();
+    fa_barrier();
+    if (kv + 1 < n_kv) issue(kv + 1, next);
+    if (kv * 64 > q0w + 31) return;
+    const bf16* Ks = cur;
+    const bf16* Vs = cur + KT;
+    f32x16 sacc[2], pacc[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) { sacc[kb][e] = 0.f; pacc[kb][e] = 0.f; }
+      for (int e = 0; e < 16; ++e) { sacc[kb][e] = 0.f; pacc[kb][e] = 0.f; }
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          sacc[kb] = mfma(frag_nrm(Ks, kb * 32 + l32, s * 2 + half), qf[s], sacc[kb]);
-          pacc[kb] = mfma(frag_nrm(Vs, kb * 32 + l32, s * 2 + half), df[s], pacc[kb]);
-        }
-      }
-      const bool need_mask = kv * 64 + 63 > q0w;
-      float ds[2][16];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float pv = exp2f(sacc[kb][e] * scale_log2 - lse2);
-          if (need_mask && kv * 64 + kb * 32 + (e >> 2) * 8 + half * 4 + (e & 3) > myq) pv = 0.f;
-          ds[kb][e] = pv * (pacc[kb][e] - Dq);
-        }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x8 a = pack_half(ds[j >> 1], j & 1);
-        const int o1 = (j >> 1) * 32 + (j & 1) * 16 + half * 4;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-          dqacc[db] = mfma(a, frag_trs(KTs, db * 32 + l32, o1), dqacc[db]);
+      for (int s = 0; s < 8; ++s) {
+        sacc[kb] = mfma(fa_frag_k(Ks, kb * 32 + l32, s * 2 + half), qf[s], sacc[kb]);
+        pacc[kb] = mfma(fa_frag_k(Vs, kb * 32 + l32, s * 2 + half), df[s], pacc[kb]);
       }
     }
-    if (more) stage(smem + (cur ^ 1) * BUF);
-    __syncthreads();
+    const bool need_mask = kv * 64 + 63 > q0w;
+    float ds[2][16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float pv = exp2f(sacc[kb][e] * scale_log2 - lse2);
+        if (need_mask && kv * 64 + kb * 32 + (e >> 2) * 8 + half * 4 + (e & 3) > myq) pv = 0.f;
+        ds[kb][e] = pv * (pacc[kb][e] - Dq);
+      }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 a = pack_half(ds[j >> 1], j & 1);
+      const int row_base = (j >> 1) * 32 + (j & 1) * 16 + half * 4;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        dqacc[db] = mfma(a, fa_frag_vt(Ks, row_base, db * 32 + 16 * ((lane >> 4) & 1), lane),
+                         dqacc[db]);
+    }
+  };
+
+  issue(0, st0);
+  for (int kv = 0; kv < n_kv; kv += 2) {
+    step(kv, st0, st1);
+    if (kv + 1 < n_kv) step(kv + 1, st1, st0);
   }
 
 #pragma unroll

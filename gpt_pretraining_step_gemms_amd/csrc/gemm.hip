@@ -24,44 +24,45 @@ constexpr int BK = 64;
 NC_DEV int swz(int row, int chunk) { return chunk ^ ((row ^ (row >> 3)) & 7); }
 
 // ------------------------------------------------------------------ epilogue
-template <typename T>
-NC_DEV void epilogue_store(const GemmParams& p, int b, int m, int n, float v) {
-  const int64_t off = (int64_t)b * p.sC + (int64_t)m * p.ldc + n;
-  switch (p.epi) {
-    case kEpiStore:
-      static_cast<T*>(p.C)[off] = to_t<T>(p.alpha * v);
-      break;
-    case kEpiStoreF32:
-      static_cast<float*>(p.C)[off] = p.alpha * v;
-      break;
-    case kEpiAccF32:
-      static_cast<float*>(p.C)[off] += p.alpha * v;
-      break;
-    case kEpiRelu2: {
-      const T h = to_t<T>(v);
-      static_cast<T*>(p.C)[off] = h;
-      const float r = fmaxf(v, 0.f);
-      static_cast<T*>(p.aux_out)[off] = to_t<T>(r * r);
-      break;
-    }
-    case kEpiRelu2Bwd: {
-      const float h = to_f(static_cast<const T*>(p.aux_in)[off]);
-      static_cast<T*>(p.C)[off] = to_t<T>(2.f * fmaxf(h, 0.f) * v);
-      break;
-    }
-    case kEpiDual: {
-      const float a = p.aux_in ? static_cast<const float*>(p.aux_in)[off] : 0.f;
-      const float r = p.p0 * a + p.p1 * v;
-      static_cast<float*>(p.C)[off] = r;
-      static_cast<T*>(p.aux_out)[off] = to_t<T>(r);
-      break;
-    }
-    case kEpiPoly: {
-      const float a = to_f(static_cast<const T*>(p.aux_in)[off]);
-      static_cast<T*>(p.C)[off] = to_t<T>(p.p0 * a + p.p1 * v);
-      break;
-    }
-    default: break;
+// One output element at offset `off` of C (and of aux_in / aux_out).
+template <typename T, int EPI>
+NC_DEV void epi_one(const GemmParams& p, int64_t off, float v) {
+  if constexpr (EPI == kEpiStore) {
+    static_cast<T*>(p.C)[off] = to_t<T>(p.alpha * v);
+  } else if constexpr (EPI == kEpiStoreF32) {
+    static_cast<float*>(p.C)[off] = p.alpha * v;
+  } else if constexpr (EPI == kEpiAccF32) {
+    static_cast<float*>(p.C)[off] += p.alpha * v;
+  } else if constexpr (EPI == kEpiRelu2) {
+    static_cast<T*>(p.C)[off] = to_t<T>(v);
+    const float r = fmaxf(v, 0.f);
+    static_cast<T*>(p.aux_out)[off] = to_t<T>(r * r);
+  } else if constexpr (EPI == kEpiRelu2Bwd) {
+    const float h = to_f(static_cast<const T*>(p.aux_in)[off]);
+    static_cast<T*>(p.C)[off] = to_t<T>(2.f * fmaxf(h, 0.f) * v);
+  } else if constexpr (EPI == kEpiPoly) {
+    const float a = to_f(static_cast<const T*>(p.aux_in)[off]);
+    static_cast<T*>(p.C)[off] = to_t<T>(p.p0 * a + p.p1 * v);
+  } else {  // kEpiDual
+    const float a = p.aux_in ? static_cast<const float*>(p.aux_in)[off] : 0.f;
+    const float r = p.p0 * a + p.p1 * v;
+    static_cast<float*>(p.C)[off] = r;
+    static_cast<T*>(p.aux_out)[off] = to_t<T>(r);
+  }
+}
+
+// Calls f.template operator()<EPI>() with the epilogue chosen at run time, so
+// that each element loop is compiled for one epilogue.
+template <typename F>
+NC_DEV void with_epilogue(int epi, F&& f) {
+  switch (epi) {
+    case kEpiStore: f.template operator()<kEpiStore>(); break;
+    case kEpiStoreF32: f.template operator()<kEpiStoreF32>(); break;
+    case kEpiAccF32: f.template operator()<kEpiAccF32>(); break;
+    case kEpiRelu2: f.template operator()<kEpiRelu2>(); break;
+    case kEpiRelu2Bwd: f.template operator()<kEpiRelu2Bwd>(); break;
+    case kEpiPoly: f.template operator()<kEpiPoly>(); break;
+    default: f.template operator()<kEpiDual>(); break;
   }
 }
 
@@ -252,16 +253,19 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmParams p
         }
     return;
   }
+  const int64_t cb = (int64_t)b * p.sC;
+  with_epilogue(p.epi, [&]<int EPI>() {
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = m0 + wm * WTM + i * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
-        const int n = n0 + wn * WTN + j * 32 + l32;
-        if (m < p.M && n < p.N) epilogue_store<bf16>(p, b, m, n, acc[i][j][e]);
-      }
+        for (int e = 0; e < 16; ++e) {
+          const int m = m0 + wm * WTM + i * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+          const int n = n0 + wn * WTN + j * 32 + l32;
+          if (m < p.M && n < p.N) epi_one<bf16, EPI>(p, cb + (int64_t)m * p.ldc + n, acc[i][j][e]);
+        }
+  });
 }
 
 // split-K reduction: C (+)= sum_s W[s] in fixed order (deterministic)
@@ -324,13 +328,16 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
     }
     __syncthreads();
   }
+  const int64_t cb = (int64_t)b * p.sC;
+  with_epilogue(p.epi, [&]<int EPI>() {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = m0 + ty * 4 + i, n = n0 + tx * 4 + j;
-      if (m < p.M && n < p.N) epilogue_store<float>(p, b, m, n, acc[i][j]);
-    }
+      for (int j = 0; j < 4; ++j) {
+        const int m = m0 + ty * 4 + i, n = n0 + tx * 4 + j;
+        if (m < p.M && n < p.N) epi_one<float, EPI>(p, cb + (int64_t)m * p.ldc + n, acc[i][j]);
+      }
+  });
 }
 
 template <int BM, int BN, int WM, int WN>
@@ -346,6 +353,266 @@ hipError_t launch_bf16_cfg(const GemmParams& p, hipStream_t st) {
     default: gemm_bf16_kernel<BM, BN, WM, WN, kMNCont, kMNCont><<<grid, block, 0, st>>>(p); break;
   }
   return hipGetLastError();
+}
+
+// ======================================== direct-to-LDS pipelined MFMA kernel
+// Operand tiles travel global -> LDS with global_load_lds (each lane moves 16
+// bytes; a wave's 64 lanes fill 1 KB of LDS contiguously), through a 4-stage
+// ring of 256x32 + 256x32 bf16 tiles, with no staging registers.  LDS keeps
+// each operand in its global layout:
+//   K-contiguous  [256 rows][32 k], 16-byte chunk c of row r stored at
+//                 c ^ ((r >> 1) & 3)            -> read with ds_read_b128;
+//   MN-contiguous [32 k][256 rows], chunk c of k-row kr stored at c ^ 2(kr & 3)
+//                 -> read with ds_read_b64_tr_b16, which hands each lane of a
+//                 16-lane group one column of a 4 x 16 block, i.e. 4 consecutive
+//                 k of one output row: the MFMA operand layout.
+// Both swizzles make the fragment reads bank-conflict free; the swizzle is
+// applied by choosing which global chunk each lane fetches.  Needs K % 32 == 0
+// (rows beyond M or N are clamped to valid memory and discarded).
+template <int WM_, int WN_>
+struct Pipe {
+  static constexpr int BM = 256, BN = 256, PK = 32, STAGES = 4, WM = WM_, WN = WN_;
+  static constexpr int NT = WM * WN * 64;
+  static constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
+  static constexpr int TILE_A = BM * PK, TILE_B = BN * PK, STAGE = TILE_A + TILE_B;
+  static constexpr int LOADS_A = TILE_A * 2 / 1024 / (NT / 64);
+  static constexpr int LOADS_B = TILE_B * 2 / 1024 / (NT / 64);
+  static constexpr int LOADS = LOADS_A + LOADS_B;   // global_load_lds per wave per stage
+};
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+#define NC_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// global_load_lds_dwordx4: lane l's 16 bytes at g land at LDS address
+// lds + 16 l (lds is wave-uniform, passed in M0).  Issued as inline assembly:
+// the instruction has no register result, and the kernel tracks its
+// completion itself (s_waitcnt vmcnt + s_barrier), which keeps the compiler
+// from draining every load in flight before each LDS read.  M0 is restored.
+NC_DEV void dma16(const void* g, const bf16* lds) {
+  const unsigned a = (unsigned)(size_t)NC_LDS(const void, lds);
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(__builtin_amdgcn_readfirstlane(a))
+      : "memory");
+}
+
+// One operand tile of ROWS x 32 into LDS; this wave issues NI 1-KB loads.
+template <int ROWS, int LAYOUT, int NI>
+NC_DEV void issue_tile(const bf16* __restrict__ base, int64_t ld, int row0, int rows_lim, int k0,
+                       bf16* tile, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int blk = wave * NI + i;               // 1-KB block of the tile
+    const bf16* g;
+    if constexpr (LAYOUT == kKCont) {            // 16 rows of 64 B per block
+      const int r = blk * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ ((r >> 1) & 3);
+      const int row = min(row0 + r, rows_lim - 1);
+      g = base + (int64_t)row * ld + k0 + c * 8;
+    } else {                                     // 1 KB = 1024 / (2 ROWS) k-rows
+      constexpr int CH = ROWS / 8;
+      const int flat = blk * 64 + lane;
+      const int kr = flat / CH;
+      const int c = (flat % CH) ^ (2 * (kr & 3));
+      const int col = min(row0 + c * 8, rows_lim - 8);
+      g = base + (int64_t)(k0 + kr) * ld + col;
+    }
+    dma16(g, tile + blk * 512);
+  }
+}
+
+// MFMA fragment (8 k of output row o0 + lane%32, k-substep s) from a tile
+template <int ROWS, int LAYOUT>
+NC_DEV bf16x8 frag(const bf16* tile, int o0, int s, int lane) {
+  if constexpr (LAYOUT == kKCont) {
+    const int r = o0 + (lane & 31);
+    const int c = s * 2 + (lane >> 5);
+    return *reinterpret_cast<const bf16x8*>(tile + r * 32 + ((c ^ ((r >> 1) & 3)) << 3));
+  } else {
+    const int g = lane >> 4, t = lane & 15;
+    const int k = s * 16 + 8 * (g >> 1) + (t >> 2);
+    const int o = o0 + 16 * (g & 1) + 4 * (t & 3);
+    const int sw = 2 * (k & 3);                  // same for k and k + 4
+    const bf16* p0 = tile + k * ROWS + (((o >> 3) ^ sw) << 3) + (o & 7);
+    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(NC_LDS(bf16x4_t, p0));
+    const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(NC_LDS(bf16x4_t, p0 + 4 * ROWS));
+    bf16x8 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+    return r;
+  }
+}
+
+template <int N>
+NC_DEV void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int AL, int BL, int WM_, int WN_>
+__global__ __launch_bounds__(WM_ * WN_ * 64, 1) void gemm_bf16_pipe_kernel(GemmParams p) {
+  using C = Pipe<WM_, WN_>;
+  constexpr int BM = C::BM, BN = C::BN, PK = C::PK, STAGES = C::STAGES, WN = C::WN;
+  constexpr int WTM = C::WTM, WTN = C::WTN, TM = C::TM, TN = C::TN;
+  constexpr int TILE_A = C::TILE_A, STAGE = C::STAGE;
+  constexpr int LOADS_A = C::LOADS_A, LOADS_B = C::LOADS_B, LOADS = C::LOADS;
+  __shared__ __attribute__((aligned(1024))) bf16 st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) bf16 st1[STAGE];
+  __shared__ __attribute__((aligned(1024))) bf16 st2[STAGE];
+  __shared__ __attribute__((aligned(1024))) bf16 st3[STAGE];
+
+  const int tiles_m = ceil_div(p.M, BM), tiles_n = ceil_div(p.N, BN);
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int z = blockIdx.z;
+  const int b = z / p.splits, split = z % p.splits;
+  const int kt_total = p.K / PK;
+  const int kt_per = ceil_div(kt_total, p.splits);
+  const int kt0 = split * kt_per;
+  const int nk = max(0, min(kt_total, kt0 + kt_per) - kt0);
+
+  const bf16* __restrict__ A = static_cast<const bf16*>(p.A) + (int64_t)b * p.sA;
+  const bf16* __restrict__ B = static_cast<const bf16*>(p.B) + (int64_t)b * p.sB;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int half = lane >> 5, l32 = lane & 31;
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // Each stage is its own LDS object and the loop is unrolled over the 4
+  // stages, so the compiler can tell that the loads in flight (other stages)
+  // do not alias the stage being read and emits no drain before its reads.
+  auto sbuf = [&]<int S>() -> bf16* {
+    if constexpr (S == 0) return st0;
+    else if constexpr (S == 1) return st1;
+    else if constexpr (S == 2) return st2;
+    else return st3;
+  };
+  auto issue = [&](int kt, bf16* st) {
+    issue_tile<BM, AL, LOADS_A>(A, p.lda, m0, p.M, kt * PK, st, wave, lane);
+    issue_tile<BN, BL, LOADS_B>(B, p.ldb, n0, p.N, kt * PK, st + TILE_A, wave, lane);
+  };
+  auto step = [&]<int S>(int i) {
+    // tile i has landed once at most the loads of the (up to two) younger tiles remain
+    const int younger = min(nk - 1 - i, STAGES - 2);
+    if (younger >= 2) wait_vmcnt<2 * LOADS>();
+    else if (younger == 1) wait_vmcnt<LOADS>();
+    else wait_vmcnt<0>();
+    // Plain barrier: every wave has waited for its own loads of tile i above,
+    // and has consumed its fragment reads of tile i-1 (whose stage the next
+    // issue overwrites).  A fenced __syncthreads would also drain the younger
+    // prefetches.
+    asm volatile("s_barrier" ::: "memory");
+    if (i + STAGES - 1 < nk) issue(kt0 + i + STAGES - 1, sbuf.template operator()<(S + 3) % 4>());
+    const bf16* as = sbuf.template operator()<S>();
+    const bf16* bs = as + TILE_A;
+#pragma unroll
+    for (int s = 0; s < PK / 16; ++s) {
+      bf16x8 fa[TM], fb[TN];
+#pragma unroll
+      for (int ii = 0; ii < TM; ++ii) fa[ii] = frag<BM, AL>(as, wm * WTM + ii * 32, s, lane);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) fb[j] = frag<BN, BL>(bs, wn * WTN + j * 32, s, lane);
+#pragma unroll
+      for (int ii = 0; ii < TM; ++ii)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[ii][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ii], fb[j], acc[ii][j], 0, 0, 0);
+    }
+  };
+  if (nk > 0) issue(kt0, st0);
+  if (nk > 1) issue(kt0 + 1, st1);
+  if (nk > 2) issue(kt0 + 2, st2);
+  for (int i = 0; i < nk; i += 4) {
+    step.template operator()<0>(i);
+    if (i + 1 < nk) step.template operator()<1>(i + 1);
+    if (i + 2 < nk) step.template operator()<2>(i + 2);
+    if (i + 3 < nk) step.template operator()<3>(i + 3);
+  }
+
+  if (p.splits > 1) {
+    float* W = p.workspace + ((int64_t)split * p.batch + b) * (int64_t)p.M * p.N;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = m0 + wm * WTM + i * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+          const int n = n0 + wn * WTN + j * 32 + l32;
+          if (m < p.M && n < p.N) W[(int64_t)m * p.N + n] = p.alpha * acc[i][j][e];
+        }
+    return;
+  }
+  const int64_t cb = (int64_t)b * p.sC;
+  // tiles wholly inside C take an unguarded path, so the loads of an epilogue
+  // that reads C or an auxiliary input are issued together
+  const bool full = m0 + BM <= p.M && n0 + BN <= p.N;
+  with_epilogue(p.epi, [&]<int EPI>() {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int mb = m0 + wm * WTM + i * 32 + half * 4;
+        const int n = n0 + wn * WTN + j * 32 + l32;
+        if (full) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            epi_one<bf16, EPI>(p, cb + (int64_t)(mb + (e >> 2) * 8 + (e & 3)) * p.ldc + n,
+                               acc[i][j][e]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int m = mb + (e >> 2) * 8 + (e & 3);
+            if (m < p.M && n < p.N) epi_one<bf16, EPI>(p, cb + (int64_t)m * p.ldc + n, acc[i][j][e]);
+          }
+        }
+      }
+  });
+}
+
+// The pipelined kernel applies when K is a multiple of 32, every operand start
+// and leading dimension is 16-byte aligned, and M (N) is a multiple of 8 where
+// A (B) is MN-contiguous.
+bool pipe_ok(const GemmParams& p) {
+  auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+  if (p.K % 32 || p.lda % 8 || p.ldb % 8 || !al16(p.A) || !al16(p.B)) return false;
+  if (p.batch > 1 && (p.sA % 8 || p.sB % 8)) return false;
+  if (p.a_layout == kMNCont && p.M % 8) return false;
+  if (p.b_layout == kMNCont && p.N % 8) return false;
+  return true;
+}
+
+template <int WM, int WN>
+hipError_t launch_pipe_cfg(const GemmParams& p, hipStream_t st) {
+  const int tiles = ceil_div(p.M, 256) * ceil_div(p.N, 256);
+  dim3 grid(tiles, 1, p.batch * p.splits);
+  constexpr int NT = WM * WN * 64;
+  switch (p.a_layout * 2 + p.b_layout) {
+    case 0: gemm_bf16_pipe_kernel<kKCont, kKCont, WM, WN><<<grid, NT, 0, st>>>(p); break;
+    case 1: gemm_bf16_pipe_kernel<kKCont, kMNCont, WM, WN><<<grid, NT, 0, st>>>(p); break;
+    case 2: gemm_bf16_pipe_kernel<kMNCont, kKCont, WM, WN><<<grid, NT, 0, st>>>(p); break;
+    default: gemm_bf16_pipe_kernel<kMNCont, kMNCont, WM, WN><<<grid, NT, 0, st>>>(p); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pipe(const GemmParams& p, hipStream_t st) {
+  static const int waves = getenv("NC_GEMM_WAVES") ? atoi(getenv("NC_GEMM_WAVES")) : 8;
+  if (waves == 4) return launch_pipe_cfg<2, 2>(p, st);
+  return launch_pipe_cfg<2, 4>(p, st);
 }
 
 }  // namespace
@@ -379,7 +646,8 @@ hipError_t nc_launch_gemm(int dtype, const GemmParams& p_in, hipStream_t st) {
     return hipGetLastError();
   }
   if (p.K <= 0) return hipErrorInvalidValue;
-  hipError_t e = launch_bf16_cfg<256, 256, 2, 2>(p, st);
+  const bool use_pipe = pipe_ok(p) && !getenv("NC_GEMM_NO_PIPE");
+  hipError_t e = use_pipe ? launch_pipe(p, st) : launch_bf16_cfg<256, 256, 2, 4>(p, st);
   if (e != hipSuccess || p.splits == 1) return e;
   const int64_t total = (int64_t)p.M * p.N * p.batch;
   const int blocks = (int)std::min<int64_t>(ceil_div64(total, 256), 65536);
