@@ -361,17 +361,23 @@ hipError_t launch_bf16_cfg(const GemmParams& p, hipStream_t st) {
 // ring of 256x32 + 256x32 bf16 tiles, with no staging registers.  LDS keeps
 // each operand in its global layout:
 //   K-contiguous  [256 rows][32 k], 16-byte chunk c of row r stored at
-//                 c ^ ((r >> 1) & 3)            -> read with ds_read_b128;
-//   MN-contiguous [32 k][256 rows], chunk c of k-row kr stored at c ^ 2(kr & 3)
+//                 c ^ ((r >> 2) & 3)            -> read with ds_read_b128;
+//   MN-contiguous [32 k][256 rows], chunk c of k-row kr stored at c ^ 4(kr & 3)
 //                 -> read with ds_read_b64_tr_b16, which hands each lane of a
 //                 16-lane group one column of a 4 x 16 block, i.e. 4 consecutive
 //                 k of one output row: the MFMA operand layout.
 // Both swizzles make the fragment reads bank-conflict free; the swizzle is
 // applied by choosing which global chunk each lane fetches.  Needs K % 32 == 0
 // (rows beyond M or N are clamped to valid memory and discarded).
-template <int WM_, int WN_>
+// Each wave owns a 128 x 64 output tile (4 x 2 MFMA tiles): WM x WN waves
+// make a (128 WM) x (64 WN) block tile.  256 x 128 blocks with 3 stages fit
+// twice per CU (72 KB of LDS each), so one block's prologue and epilogue
+// overlap the other's main loop.
+template <int WM_, int WN_, int ST_>
 struct Pipe {
-  static constexpr int BM = 256, BN = 256, PK = 32, STAGES = 4, WM = WM_, WN = WN_;
+  static constexpr int BM = 128 * WM_, BN = 64 * WN_, PK = 32, STAGES = ST_;
+  static constexpr int WM = WM_, WN = WN_;
+  static constexpr int kBlocksPerCU = (BM + BN) * PK * 2 * ST_ <= 80 * 1024 ? 2 : 1;
   static constexpr int NT = WM * WN * 64;
   static constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
   static constexpr int TILE_A = BM * PK, TILE_B = BN * PK, STAGE = TILE_A + TILE_B;
@@ -411,14 +417,14 @@ NC_DEV void issue_tile(const bf16* __restrict__ base, int64_t ld, int row0, int 
     const bf16* g;
     if constexpr (LAYOUT == kKCont) {            // 16 rows of 64 B per block
       const int r = blk * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ ((r >> 1) & 3);
+      const int c = (lane & 3) ^ ((r >> 2) & 3);
       const int row = min(row0 + r, rows_lim - 1);
       g = base + (int64_t)row * ld + k0 + c * 8;
     } else {                                     // 1 KB = 1024 / (2 ROWS) k-rows
       constexpr int CH = ROWS / 8;
       const int flat = blk * 64 + lane;
       const int kr = flat / CH;
-      const int c = (flat % CH) ^ (2 * (kr & 3));
+      const int c = (flat % CH) ^ (4 * (kr & 3));
       const int col = min(row0 + c * 8, rows_lim - 8);
       g = base + (int64_t)(k0 + kr) * ld + col;
     }
@@ -432,12 +438,12 @@ NC_DEV bf16x8 frag(const bf16* tile, int o0, int s, int lane) {
   if constexpr (LAYOUT == kKCont) {
     const int r = o0 + (lane & 31);
     const int c = s * 2 + (lane >> 5);
-    return *reinterpret_cast<const bf16x8*>(tile + r * 32 + ((c ^ ((r >> 1) & 3)) << 3));
+    return *reinterpret_cast<const bf16x8*>(tile + r * 32 + ((c ^ ((r >> 2) & 3)) << 3));
   } else {
     const int g = lane >> 4, t = lane & 15;
     const int k = s * 16 + 8 * (g >> 1) + (t >> 2);
     const int o = o0 + 16 * (g & 1) + 4 * (t & 3);
-    const int sw = 2 * (k & 3);                  // same for k and k + 4
+    const int sw = 4 * (k & 3);                  // same for k and k + 4
     const bf16* p0 = tile + k * ROWS + (((o >> 3) ^ sw) << 3) + (o & 7);
     const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(NC_LDS(bf16x4_t, p0));
     const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(NC_LDS(bf16x4_t, p0 + 4 * ROWS));
@@ -453,9 +459,10 @@ NC_DEV void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int AL, int BL, int WM_, int WN_>
-__global__ __launch_bounds__(WM_ * WN_ * 64, 1) void gemm_bf16_pipe_kernel(GemmParams p) {
-  using C = Pipe<WM_, WN_>;
+template <int AL, int BL, int WM_, int WN_, int ST_>
+__global__ __launch_bounds__(WM_ * WN_ * 64, (Pipe<WM_, WN_, ST_>::kBlocksPerCU))
+void gemm_bf16_pipe_kernel(GemmParams p) {
+  using C = Pipe<WM_, WN_, ST_>;
   constexpr int BM = C::BM, BN = C::BN, PK = C::PK, STAGES = C::STAGES, WN = C::WN;
   constexpr int WTM = C::WTM, WTN = C::WTN, TM = C::TM, TN = C::TN;
   constexpr int TILE_A = C::TILE_A, STAGE = C::STAGE;
@@ -515,7 +522,8 @@ __global__ __launch_bounds__(WM_ * WN_ * 64, 1) void gemm_bf16_pipe_kernel(GemmP
     // issue overwrites).  A fenced __syncthreads would also drain the younger
     // prefetches.
     asm volatile("s_barrier" ::: "memory");
-    if (i + STAGES - 1 < nk) issue(kt0 + i + STAGES - 1, sbuf.template operator()<(S + 3) % 4>());
+    if (i + STAGES - 1 < nk)
+      issue(kt0 + i + STAGES - 1, sbuf.template operator()<(S + STAGES - 1) % STAGES>());
     const bf16* as = sbuf.template operator()<S>();
     const bf16* bs = as + TILE_A;
 #pragma unroll
@@ -534,12 +542,14 @@ __global__ __launch_bounds__(WM_ * WN_ * 64, 1) void gemm_bf16_pipe_kernel(GemmP
   };
   if (nk > 0) issue(kt0, st0);
   if (nk > 1) issue(kt0 + 1, st1);
-  if (nk > 2) issue(kt0 + 2, st2);
-  for (int i = 0; i < nk; i += 4) {
+  if constexpr (STAGES == 4)
+    if (nk > 2) issue(kt0 + 2, st2);
+  for (int i = 0; i < nk; i += STAGES) {
     step.template operator()<0>(i);
     if (i + 1 < nk) step.template operator()<1>(i + 1);
     if (i + 2 < nk) step.template operator()<2>(i + 2);
-    if (i + 3 < nk) step.template operator()<3>(i + 3);
+    if constexpr (STAGES == 4)
+      if (i + 3 < nk) step.template operator()<3>(i + 3);
   }
 
   if (p.splits > 1) {
@@ -595,24 +605,25 @@ bool pipe_ok(const GemmParams& p) {
   return true;
 }
 
-template <int WM, int WN>
+template <int WM, int WN, int ST>
 hipError_t launch_pipe_cfg(const GemmParams& p, hipStream_t st) {
-  const int tiles = ceil_div(p.M, 256) * ceil_div(p.N, 256);
+  using C = Pipe<WM, WN, ST>;
+  const int tiles = ceil_div(p.M, C::BM) * ceil_div(p.N, C::BN);
   dim3 grid(tiles, 1, p.batch * p.splits);
   constexpr int NT = WM * WN * 64;
   switch (p.a_layout * 2 + p.b_layout) {
-    case 0: gemm_bf16_pipe_kernel<kKCont, kKCont, WM, WN><<<grid, NT, 0, st>>>(p); break;
-    case 1: gemm_bf16_pipe_kernel<kKCont, kMNCont, WM, WN><<<grid, NT, 0, st>>>(p); break;
-    case 2: gemm_bf16_pipe_kernel<kMNCont, kKCont, WM, WN><<<grid, NT, 0, st>>>(p); break;
-    default: gemm_bf16_pipe_kernel<kMNCont, kMNCont, WM, WN><<<grid, NT, 0, st>>>(p); break;
+    case 0: gemm_bf16_pipe_kernel<kKCont, kKCont, WM, WN, ST><<<grid, NT, 0, st>>>(p); break;
+    case 1: gemm_bf16_pipe_kernel<kKCont, kMNCont, WM, WN, ST><<<grid, NT, 0, st>>>(p); break;
+    case 2: gemm_bf16_pipe_kernel<kMNCont, kKCont, WM, WN, ST><<<grid, NT, 0, st>>>(p); break;
+    default: gemm_bf16_pipe_kernel<kMNCont, kMNCont, WM, WN, ST><<<grid, NT, 0, st>>>(p); break;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_pipe(const GemmParams& p, hipStream_t st) {
-  static const int waves = getenv("NC_GEMM_WAVES") ? atoi(getenv("NC_GEMM_WAVES")) : 8;
-  if (waves == 4) return launch_pipe_cfg<2, 2>(p, st);
-  return launch_pipe_cfg<2, 4>(p, st);
+  static const int cfg = getenv("NC_GEMM_CFG") ? atoi(getenv("NC_GEMM_CFG")) : 1;
+  if (cfg == 1) return launch_pipe_cfg<2, 2, 3>(p, st);   // 256 x 128, two blocks per CU
+  return launch_pipe_cfg<2, 4, 4>(p, st);                 // 256 x 256, one block per CU
 }
 
 }  // namespace
