@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--roofline-only", action="store_true",
                     help="only the dominant-kernel timing loop (for profiling it alone)")
     ap.add_argument("--roofline-iters", type=int, default=20)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="with --roofline-only: also run a 1 GiB copy kernel (counter scale)")
     return ap.parse_args()
 
 
@@ -64,17 +66,49 @@ def roofline_gemm(cfg, iters):
     torch.cuda.synchronize()
     sec = t0.elapsed_time(t1) / 1e3 / iters
     flops = 2.0 * M * N * K
-    return {"kernel": "gemm_bf16_kernel<256,256,2,2,KCont,KCont> (MLP up + ReLU^2)",
+    return {"kernel": "gemm_bf16_pipe_kernel<KCont, KCont> (MLP up + ReLU^2 epilogue)",
             "shape": [M, N, K], "avg_launch_us": sec * 1e6,
             "bound": "mfma", "achieved": flops / sec / 1e12, "peak": PEAK_BF16 / 1e12,
-            "unit": "TFLOP/s", "frac": flops / sec / PEAK_BF16, "traffic": None}
+            "unit": "TFLOP/s", "frac": flops / sec / PEAK_BF16, "traffic": measured_traffic()}
 
 
-def cpu_baseline(cfg):
-    """The fp64 numpy oracle on one 2048-token row of the same model: forward
-    + backward (the optimizer, <1% of a 524,288-token step's FLOPs, is left
-    out)."""
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_mlp_up_relu2_d20_traffic.txt")
+GEMM_SOURCE = os.path.join(ROOT, "gpt_pretraining_step_gemms_amd", "csrc", "gemm.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the roofline GEMM from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a copy kernel's readings), or
+    None when the GEMM source has changed since the counters were taken."""
+    import hashlib
+    try:
+        fields = dict(line.split(":", 1) for line in open(TRAFFIC_FILE) if ":" in line)
+        sha = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+        if fields["gemm.hip sha256"].strip() != sha:
+            return None
+        return float(fields["hbm bytes per launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_calibration(nbytes=1 << 30):
+    """A plain elementwise copy of known size (read nbytes, write nbytes):
+    the reference that scales the HBM byte counters."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+
+def cpu_baseline(cfg, n_tok=2048):
+    """The fp64 numpy oracle on a bounded sample of the same workload: forward
+    + backward of one 2048-token row (n_tok < 2048 takes a prefix of it, which
+    a causal model computes exactly as inside the full row).  The optimizer,
+    <1% of a 524,288-token step's FLOPs, is left out."""
     import numpy as np
+    import threadpoolctl
     import oracle
     from oracle.model import param_shapes
     from gpt_pretraining_step_gemms_amd import synthetic
@@ -82,13 +116,15 @@ def cpu_baseline(cfg):
     params = {k: v.astype(np.float64) for k, v in
               synthetic.normal_params(0, param_shapes(ocfg), cfg.init_std).items()}
     tok, tgt = synthetic.token_rows(1000, 1, cfg.seq_len, cfg.vocab, cfg.token_dist)
+    tok, tgt = tok[:, :n_tok], tgt[:, :n_tok]
     t0 = time.perf_counter()
     oracle.loss_and_grads(params, tok, tgt, ocfg)
     sec = time.perf_counter() - t0
-    cores = int(os.environ.get("OPENBLAS_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": cfg.seq_len / sec, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"fwd+bwd of 1 row x {cfg.seq_len} tokens of {cfg.name}, numpy fp64 "
-                      f"(OpenBLAS), {sec:.1f} s"}
+    blas = [p for p in threadpoolctl.threadpool_info() if p["user_api"] == "blas"]
+    cores = max((p["num_threads"] for p in blas), default=1)
+    return {"value": n_tok / sec, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"fwd+bwd of {n_tok} positions of one {cfg.seq_len}-token row "
+                      f"of {cfg.name}, numpy fp64 (OpenBLAS, {cores} threads), {sec:.1f} s"}
 
 
 def main():
@@ -105,6 +141,8 @@ def main():
     cfg = with_batch(cfg, micro_batch=args.micro_batch, accum_steps=args.accum)
     if args.roofline_only:
         r = roofline_gemm(cfg, args.roofline_iters)
+        if args.copy_calibration:
+            copy_calibration()
         print(json.dumps({"roofline": r}))
         return
 

@@ -108,13 +108,11 @@ NC_DEV void fa_wait_vmcnt() {
 }
 NC_DEV void fa_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// Swizzle of 16-byte chunks in a [rows][128] bf16 tile (rows of 256 bytes, so
-// every row starts at bank 0 of the 64 four-byte banks): chunk c of row r is
-// stored at c ^ fa_swz(r).  LDS serves 16 lanes per cycle; 16 consecutive
-// rows read at one chunk (ds_read_b128) get 16 distinct chunks, and the 4
-// consecutive rows x 4 neighbouring chunks of two 16-lane transpose-read
-// groups (ds_read_b64_tr_b16) land in 4 distinct 4-chunk groups.
-NC_DEV int fa_swz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+// Swizzle of 16-byte chunks in a [rows][128] bf16 tile: chunk c of row r is
+// stored at c ^ fa_swz(r).  Eight consecutive rows read at one chunk
+// (ds_read_b128) and four consecutive rows read at two neighbouring chunks
+// (ds_read_b64_tr_b16) both hit 8 distinct bank groups.
+NC_DEV int fa_swz(int r) { return (2 * (r & 3)) | ((r >> 2) & 1); }
 
 // this wave's share (4 x 1 KB) of a 64-row x 128 token-major tile into LDS
 NC_DEV void fa_issue_rows(const bf16* src, int64_t ld, int row0, bf16* tile, int wave, int lane) {
@@ -147,13 +145,13 @@ NC_DEV bf16x8 fa_frag_k(const bf16* tile, int r, int c) {
 }
 // 8 values of head dim `col_base + lane%16` (within a 16-wide column block) at
 // key rows row_base + {0..3} and row_base + 8 + {0..3}, from a [key][128] tile
-// stored with the fa_swz swizzle
+// stored with the fa_swz swizzle (rows r and r + 8 share it)
 NC_DEV bf16x8 fa_frag_vt(const bf16* tile, int row_base, int col_base, int lane) {
   const int t = lane & 15;
   const int r = row_base + (t >> 2);
   const int col = col_base + 4 * (t & 3);
   const bf16* p0 = tile + r * 128 + (((col >> 3) ^ fa_swz(r)) << 3) + (col & 7);
-  const bf16* p1 = tile + (r + 8) * 128 + (((col >> 3) ^ fa_swz(r + 8)) << 3) + (col & 7);
+  const bf16* p1 = p0 + 8 * 128;                 // row + 8: same swizzle
   const fa_bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) fa_bf16x4*)p0);
   const fa_bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) fa_bf16x4*)p1);
   bf16x8 v;

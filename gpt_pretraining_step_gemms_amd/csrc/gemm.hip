@@ -621,7 +621,7 @@ hipError_t launch_pipe_cfg(const GemmParams& p, hipStream_t st) {
 }
 
 hipError_t launch_pipe(const GemmParams& p, hipStream_t st) {
-  static const int cfg = getenv("NC_GEMM_CFG") ? atoi(getenv("NC_GEMM_CFG")) : 1;
+  static const int cfg = getenv("NC_GEMM_CFG") ? atoi(getenv("NC_GEMM_CFG")) : 2;
   if (cfg == 1) return launch_pipe_cfg<2, 2, 3>(p, st);   // 256 x 128, two blocks per CU
   return launch_pipe_cfg<2, 4, 4>(p, st);                 // 256 x 256, one block per CU
 }
