@@ -31,6 +31,7 @@ struct GemmParams {
   int a_layout, b_layout, epi;
   float alpha, p0, p1;
   int splits;                        // split-K count (>1: C must be f32, workspace used)
+  int vec_epi;                       // set by the launcher: C/aux 16-byte aligned, ldc and sC % 8 == 0
   float* workspace; size_t workspace_bytes;
 };
 

@@ -51,6 +51,82 @@ NC_DEV void epi_one(const GemmParams& p, int64_t off, float v) {
   }
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+NC_DEV void ld8(const bf16* q, float (&x)[8]) {
+  const bf16x8 h = *reinterpret_cast<const bf16x8*>(q);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = static_cast<float>(h[e]);
+}
+NC_DEV void st8(bf16* q, const float (&x)[8]) {
+  bf16x8 h;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) h[e] = static_cast<bf16>(x[e]);
+  *reinterpret_cast<bf16x8*>(q) = h;
+}
+NC_DEV void ld8(const float* q, float (&x)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(q), b = *reinterpret_cast<const f32x4*>(q + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[e + 4] = b[e]; }
+}
+NC_DEV void st8(float* q, const float (&x)[8]) {
+  f32x4 a, b;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { a[e] = x[e]; b[e] = x[e + 4]; }
+  *reinterpret_cast<f32x4*>(q) = a;
+  *reinterpret_cast<f32x4*>(q + 4) = b;
+}
+
+// Eight consecutive outputs of one row at offset `off` of C (and aux), with
+// 16-byte accesses: the same arithmetic as epi_one (bf16 activations).
+template <int EPI>
+NC_DEV void epi_vec8(const GemmParams& p, int64_t off, const float (&v)[8]) {
+  float r[8], a[8];
+  if constexpr (EPI == kEpiStore) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = p.alpha * v[e];
+    st8(static_cast<bf16*>(p.C) + off, r);
+  } else if constexpr (EPI == kEpiStoreF32) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = p.alpha * v[e];
+    st8(static_cast<float*>(p.C) + off, r);
+  } else if constexpr (EPI == kEpiAccF32) {
+    ld8(static_cast<const float*>(p.C) + off, a);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = a[e] + p.alpha * v[e];
+    st8(static_cast<float*>(p.C) + off, r);
+  } else if constexpr (EPI == kEpiRelu2) {
+    st8(static_cast<bf16*>(p.C) + off, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float t = fmaxf(v[e], 0.f);
+      r[e] = t * t;
+    }
+    st8(static_cast<bf16*>(p.aux_out) + off, r);
+  } else if constexpr (EPI == kEpiRelu2Bwd) {
+    ld8(static_cast<const bf16*>(p.aux_in) + off, a);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = 2.f * fmaxf(a[e], 0.f) * v[e];
+    st8(static_cast<bf16*>(p.C) + off, r);
+  } else if constexpr (EPI == kEpiPoly) {
+    ld8(static_cast<const bf16*>(p.aux_in) + off, a);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = p.p0 * a[e] + p.p1 * v[e];
+    st8(static_cast<bf16*>(p.C) + off, r);
+  } else {  // kEpiDual
+    if (p.aux_in) {
+      ld8(static_cast<const float*>(p.aux_in) + off, a);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[e] = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = p.p0 * a[e] + p.p1 * v[e];
+    st8(static_cast<float*>(p.C) + off, r);
+    st8(static_cast<bf16*>(p.aux_out) + off, r);
+  }
+}
+
 // Calls f.template operator()<EPI>() with the epilogue chosen at run time, so
 // that each element loop is compiled for one epilogue.
 template <typename F>
@@ -268,6 +344,23 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_bf16_kernel(GemmParams p
   });
 }
 
+// split-K reduction, one block per output row, four columns per thread:
+// C (+)= sum_s W[s] in fixed order (deterministic; same sums as below).
+// Needs N, ldc and sC multiples of 4 and a 16-byte aligned C.
+__global__ __launch_bounds__(256) void splitk_reduce_rows_kernel(GemmParams p) {
+  const int row = blockIdx.x;                      // b * M + m
+  const int b = row / p.M, m = row - b * p.M;
+  const int64_t total = (int64_t)p.M * p.N * p.batch;
+  const float* w = p.workspace + (int64_t)row * p.N;
+  float* c = static_cast<float*>(p.C) + b * p.sC + (int64_t)m * p.ldc;
+  for (int n = threadIdx.x * 4; n < p.N; n += blockDim.x * 4) {
+    f32x4 acc = *reinterpret_cast<const f32x4*>(w + n);
+    for (int k = 1; k < p.splits; ++k) acc += *reinterpret_cast<const f32x4*>(w + k * total + n);
+    f32x4* out = reinterpret_cast<f32x4*>(c + n);
+    if (p.epi == kEpiAccF32) *out = *out + acc; else *out = acc;
+  }
+}
+
 // split-K reduction: C (+)= sum_s W[s] in fixed order (deterministic)
 __global__ void splitk_reduce_kernel(GemmParams p) {
   const int64_t MN = (int64_t)p.M * p.N;
@@ -373,10 +466,11 @@ hipError_t launch_bf16_cfg(const GemmParams& p, hipStream_t st) {
 // make a (128 WM) x (64 WN) block tile.  256 x 128 blocks with 3 stages fit
 // twice per CU (72 KB of LDS each), so one block's prologue and epilogue
 // overlap the other's main loop.
-template <int WM_, int WN_, int ST_>
+template <int WM_, int WN_, int ST_, bool FP_ = false>
 struct Pipe {
   static constexpr int BM = 128 * WM_, BN = 64 * WN_, PK = 32, STAGES = ST_;
   static constexpr int WM = WM_, WN = WN_;
+  static constexpr bool FP = FP_;   // fragments of the next k-substep read during the MFMAs
   static constexpr int kBlocksPerCU = (BM + BN) * PK * 2 * ST_ <= 80 * 1024 ? 2 : 1;
   static constexpr int NT = WM * WN * 64;
   static constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
@@ -459,10 +553,10 @@ NC_DEV void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int AL, int BL, int WM_, int WN_, int ST_>
-__global__ __launch_bounds__(WM_ * WN_ * 64, (Pipe<WM_, WN_, ST_>::kBlocksPerCU))
+template <int AL, int BL, int WM_, int WN_, int ST_, bool FP_>
+__global__ __launch_bounds__(WM_ * WN_ * 64, (Pipe<WM_, WN_, ST_, FP_>::kBlocksPerCU))
 void gemm_bf16_pipe_kernel(GemmParams p) {
-  using C = Pipe<WM_, WN_, ST_>;
+  using C = Pipe<WM_, WN_, ST_, FP_>;
   constexpr int BM = C::BM, BN = C::BN, PK = C::PK, STAGES = C::STAGES, WN = C::WN;
   constexpr int WTM = C::WTM, WTN = C::WTN, TM = C::TM, TN = C::TN;
   constexpr int TILE_A = C::TILE_A, STAGE = C::STAGE;
@@ -471,6 +565,7 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(1024))) bf16 st1[STAGE];
   __shared__ __attribute__((aligned(1024))) bf16 st2[STAGE];
   __shared__ __attribute__((aligned(1024))) bf16 st3[STAGE];
+  __shared__ __attribute__((aligned(1024))) bf16 st4[STAGE];
 
   const int tiles_m = ceil_div(p.M, BM), tiles_n = ceil_div(p.N, BN);
   int tm, tn;
@@ -505,7 +600,8 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
     if constexpr (S == 0) return st0;
     else if constexpr (S == 1) return st1;
     else if constexpr (S == 2) return st2;
-    else return st3;
+    else if constexpr (S == 3) return st3;
+    else return st4;
   };
   auto issue = [&](int kt, bf16* st) {
     issue_tile<BM, AL, LOADS_A>(A, p.lda, m0, p.M, kt * PK, st, wave, lane);
@@ -540,57 +636,152 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
           acc[ii][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ii], fb[j], acc[ii][j], 0, 0, 0);
     }
   };
-  if (nk > 0) issue(kt0, st0);
-  if (nk > 1) issue(kt0 + 1, st1);
-  if constexpr (STAGES == 4)
-    if (nk > 2) issue(kt0 + 2, st2);
-  for (int i = 0; i < nk; i += STAGES) {
-    step.template operator()<0>(i);
-    if (i + 1 < nk) step.template operator()<1>(i + 1);
-    if (i + 2 < nk) step.template operator()<2>(i + 2);
+  if constexpr (!C::FP) {
+    if (nk > 0) issue(kt0, st0);
+    if (nk > 1) issue(kt0 + 1, st1);
     if constexpr (STAGES == 4)
-      if (i + 3 < nk) step.template operator()<3>(i + 3);
+      if (nk > 2) issue(kt0 + 2, st2);
+    for (int i = 0; i < nk; i += STAGES) {
+      step.template operator()<0>(i);
+      if (i + 1 < nk) step.template operator()<1>(i + 1);
+      if (i + 2 < nk) step.template operator()<2>(i + 2);
+      if constexpr (STAGES == 4)
+        if (i + 3 < nk) step.template operator()<3>(i + 3);
+    }
+  } else if (nk > 0) {
+    // Software-pipelined variant: the fragment reads of each k-substep are
+    // issued before the MFMAs of the previous one, so LDS reads and MFMAs
+    // overlap instead of alternating across the barrier.  Tile i+1 must have
+    // landed one substep before its first use, so STAGES - 1 tiles are issued
+    // ahead and STAGES - 3 of them may still be in flight at each wait.
+    bf16x8 f0a[TM], f0b[TN], f1a[TM], f1b[TN];
+    auto read = [&](const bf16* st, int s, bf16x8 (&fa)[TM], bf16x8 (&fb)[TN]) {
+#pragma unroll
+      for (int ii = 0; ii < TM; ++ii) fa[ii] = frag<BM, AL>(st, wm * WTM + ii * 32, s, lane);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) fb[j] = frag<BN, BL>(st + TILE_A, wn * WTN + j * 32, s, lane);
+    };
+    auto mma = [&](const bf16x8 (&fa)[TM], const bf16x8 (&fb)[TN]) {
+#pragma unroll
+      for (int ii = 0; ii < TM; ++ii)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[ii][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ii], fb[j], acc[ii][j], 0, 0, 0);
+    };
+    // wait until tile t has landed, given the tiles issued after it
+    auto wait_tile = [&](int t) {
+      const int younger = min(nk - 1 - t, STAGES - 3);
+      if (younger >= 2) wait_vmcnt<2 * LOADS>();
+      else if (younger == 1) wait_vmcnt<LOADS>();
+      else wait_vmcnt<0>();
+      asm volatile("s_barrier" ::: "memory");
+    };
+    if (nk > 0) issue(kt0, st0);
+    if (nk > 1) issue(kt0 + 1, st1);
+    if (nk > 2) issue(kt0 + 2, st2);
+    if constexpr (STAGES == 5)
+      if (nk > 3) issue(kt0 + 3, st3);
+    {
+      // tile 0 landed: the tiles issued after it are 1 .. STAGES-2
+      const int younger = min(nk - 1, STAGES - 2);
+      if (younger >= 3) wait_vmcnt<3 * LOADS>();
+      else if (younger == 2) wait_vmcnt<2 * LOADS>();
+      else if (younger == 1) wait_vmcnt<LOADS>();
+      else wait_vmcnt<0>();
+      asm volatile("s_barrier" ::: "memory");
+    }
+    read(st0, 0, f0a, f0b);
+    auto pstep = [&]<int S>(int i) {
+      const bf16* cur = sbuf.template operator()<S>();
+      read(cur, 1, f1a, f1b);
+      // keep the reads ahead of the MFMAs (the scheduler would otherwise sink
+      // them past the MFMAs and reuse one register set for both substeps)
+      __builtin_amdgcn_sched_barrier(0);
+      mma(f0a, f0b);
+      if (i + 1 < nk) {
+        wait_tile(i + 1);
+        // every wave is past the MFMAs of tile i-1: its stage can be refilled
+        if (i + STAGES - 1 < nk)
+          issue(kt0 + i + STAGES - 1, sbuf.template operator()<(S + STAGES - 1) % STAGES>());
+      }
+      // Unconditional (after the last tile it reads a stale stage and the
+      // values go unused): reads issued on every path let the compiler wait
+      // for just the older substep's fragments before the MFMAs below.
+      read(sbuf.template operator()<(S + 1) % STAGES>(), 0, f0a, f0b);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(f1a, f1b);
+    };
+    for (int i = 0; i < nk; i += STAGES) {
+      pstep.template operator()<0>(i);
+      if (i + 1 < nk) pstep.template operator()<1>(i + 1);
+      if (i + 2 < nk) pstep.template operator()<2>(i + 2);
+      if constexpr (STAGES >= 4)
+        if (i + 3 < nk) pstep.template operator()<3>(i + 3);
+      if constexpr (STAGES == 5)
+        if (i + 4 < nk) pstep.template operator()<4>(i + 4);
+    }
   }
 
-  if (p.splits > 1) {
-    float* W = p.workspace + ((int64_t)split * p.batch + b) * (int64_t)p.M * p.N;
+  // ---- epilogue, staged through the (now idle) stage buffers: each wave
+  // writes a 32 x 64 block of its fp32 accumulators into its own padded LDS
+  // region, then every lane takes 8 consecutive columns of one row, so that
+  // C, the auxiliary tensors and the split-K workspace are accessed with
+  // 16-byte, row-contiguous loads and stores.
+  static_assert(WTN == 64, "the epilogue maps 8 lanes to the 64 columns of a wave tile");
+  constexpr int EP_LD = 72;                          // padded row, floats
+  constexpr int EP_FLOATS = 32 * EP_LD;
+  constexpr int EP_PER = STAGE * 2 / (EP_FLOATS * 4);  // wave regions per stage buffer
+  static_assert(C::NT / 64 <= 3 * EP_PER, "staging must fit in three stage buffers");
+  asm volatile("s_barrier" ::: "memory");            // every wave is done with the ring
+  const int sidx = wave / EP_PER;
+  float* stg = reinterpret_cast<float*>(sidx == 0 ? st0 : (sidx == 1 ? st1 : st2)) +
+               (wave % EP_PER) * EP_FLOATS;
+  const bool split_out = p.splits > 1;
+  float* W = split_out ? p.workspace + ((int64_t)split * p.batch + b) * (int64_t)p.M * p.N
+                       : nullptr;
+  const int64_t cb = (int64_t)b * p.sC;
+  const int64_t ld_out = split_out ? p.N : p.ldc;
+  const bool vec = split_out ? (p.N % 8 == 0) : p.vec_epi;
+  const int rsub = lane >> 3, q = lane & 7;
+  auto run = [&]<int EPI>() {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i) {
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = m0 + wm * WTM + i * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
-          const int n = n0 + wn * WTN + j * 32 + l32;
-          if (m < p.M && n < p.N) W[(int64_t)m * p.N + n] = p.alpha * acc[i][j][e];
-        }
-    return;
-  }
-  const int64_t cb = (int64_t)b * p.sC;
-  // tiles wholly inside C take an unguarded path, so the loads of an epilogue
-  // that reads C or an auxiliary input are issued together
-  const bool full = m0 + BM <= p.M && n0 + BN <= p.N;
-  with_epilogue(p.epi, [&]<int EPI>() {
+        for (int e = 0; e < 16; ++e)
+          stg[((e >> 2) * 8 + half * 4 + (e & 3)) * EP_LD + j * 32 + l32] = acc[i][j][e];
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+      for (int t = 0; t < 4; ++t) {
+        const int row = rsub + 8 * t;
+        float v[8];
+        ld8(stg + row * EP_LD + 8 * q, v);
+        const int m = m0 + wm * WTM + i * 32 + row;
+        const int n = n0 + wn * WTN + 8 * q;
+        if (m >= p.M || n >= p.N) continue;
+        if (split_out) {
+          float* w = W + (int64_t)m * ld_out + n;
+          if (vec && n + 8 <= p.N) {
+            float r[8];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int mb = m0 + wm * WTM + i * 32 + half * 4;
-        const int n = n0 + wn * WTN + j * 32 + l32;
-        if (full) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            epi_one<bf16, EPI>(p, cb + (int64_t)(mb + (e >> 2) * 8 + (e & 3)) * p.ldc + n,
-                               acc[i][j][e]);
+            for (int e = 0; e < 8; ++e) r[e] = p.alpha * v[e];
+            st8(w, r);
+          } else {
+            for (int e = 0; e < 8 && n + e < p.N; ++e) w[e] = p.alpha * v[e];
+          }
         } else {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int m = mb + (e >> 2) * 8 + (e & 3);
-            if (m < p.M && n < p.N) epi_one<bf16, EPI>(p, cb + (int64_t)m * p.ldc + n, acc[i][j][e]);
+          const int64_t off = cb + (int64_t)m * ld_out + n;
+          if (vec && n + 8 <= p.N) {
+            epi_vec8<EPI>(p, off, v);
+          } else {
+            for (int e = 0; e < 8 && n + e < p.N; ++e) epi_one<bf16, EPI>(p, off + e, v[e]);
           }
         }
       }
-  });
+    }
+  };
+  if (split_out) run.template operator()<kEpiStoreF32>();
+  else with_epilogue(p.epi, run);
 }
 
 // The pipelined kernel applies when K is a multiple of 32, every operand start
@@ -605,17 +796,17 @@ bool pipe_ok(const GemmParams& p) {
   return true;
 }
 
-template <int WM, int WN, int ST>
+template <int WM, int WN, int ST, bool FP = false>
 hipError_t launch_pipe_cfg(const GemmParams& p, hipStream_t st) {
-  using C = Pipe<WM, WN, ST>;
+  using C = Pipe<WM, WN, ST, FP>;
   const int tiles = ceil_div(p.M, C::BM) * ceil_div(p.N, C::BN);
   dim3 grid(tiles, 1, p.batch * p.splits);
   constexpr int NT = WM * WN * 64;
   switch (p.a_layout * 2 + p.b_layout) {
-    case 0: gemm_bf16_pipe_kernel<kKCont, kKCont, WM, WN, ST><<<grid, NT, 0, st>>>(p); break;
-    case 1: gemm_bf16_pipe_kernel<kKCont, kMNCont, WM, WN, ST><<<grid, NT, 0, st>>>(p); break;
-    case 2: gemm_bf16_pipe_kernel<kMNCont, kKCont, WM, WN, ST><<<grid, NT, 0, st>>>(p); break;
-    default: gemm_bf16_pipe_kernel<kMNCont, kMNCont, WM, WN, ST><<<grid, NT, 0, st>>>(p); break;
+    case 0: gemm_bf16_pipe_kernel<kKCont, kKCont, WM, WN, ST, FP><<<grid, NT, 0, st>>>(p); break;
+    case 1: gemm_bf16_pipe_kernel<kKCont, kMNCont, WM, WN, ST, FP><<<grid, NT, 0, st>>>(p); break;
+    case 2: gemm_bf16_pipe_kernel<kMNCont, kKCont, WM, WN, ST, FP><<<grid, NT, 0, st>>>(p); break;
+    default: gemm_bf16_pipe_kernel<kMNCont, kMNCont, WM, WN, ST, FP><<<grid, NT, 0, st>>>(p); break;
   }
   return hipGetLastError();
 }
@@ -623,17 +814,34 @@ hipError_t launch_pipe_cfg(const GemmParams& p, hipStream_t st) {
 hipError_t launch_pipe(const GemmParams& p, hipStream_t st) {
   static const int cfg = getenv("NC_GEMM_CFG") ? atoi(getenv("NC_GEMM_CFG")) : 2;
   if (cfg == 1) return launch_pipe_cfg<2, 2, 3>(p, st);   // 256 x 128, two blocks per CU
+  if (cfg == 3) return launch_pipe_cfg<2, 4, 5, true>(p, st);
+  if (cfg == 4) return launch_pipe_cfg<2, 4, 4, true>(p, st);
   return launch_pipe_cfg<2, 4, 4>(p, st);                 // 256 x 256, one block per CU
 }
 
 }  // namespace
 
+// Split count for a K-heavy product (the weight gradients), from a simple cost
+// model of the 256 x 256 kernel on a 256-CU device (one block per CU): blocks
+// run in waves of 256, each 32-deep k-step takes about 1.1 us, and the split
+// partials cost (2 splits + 2) M N fp32 values of memory traffic at 5 TB/s.
+// A larger split count is taken only when it is at least 2 % faster.
 int nc_gemm_pick_splits(int M, int N, int K) {
-  const int tiles = ceil_div(M, 256) * ceil_div(N, 256);
-  int s = 1;
+  constexpr int kCUs = 256;
+  const int64_t tiles = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
   const int kt = ceil_div(K, BK);
-  while (tiles * s < 1024 && s * 2 <= kt / 8) s *= 2;
-  return s;
+  double best = 0.0;
+  int best_s = 1;
+  for (int s = 1; s <= 64 && (s == 1 || s <= kt / 8); ++s) {
+    const int64_t waves = (tiles * s + kCUs - 1) / kCUs;
+    const double t = (double)waves * ceil_div(kt, s) * 1.1e-6 +
+                     (s > 1 ? (2.0 * s + 2.0) * M * N * 4.0 / 5e12 : 0.0);
+    if (s == 1 || t < 0.98 * best) {
+      best = t;
+      best_s = s;
+    }
+  }
+  return best_s;
 }
 
 size_t nc_gemm_workspace_bytes(int M, int N, int splits) {
@@ -657,11 +865,23 @@ hipError_t nc_launch_gemm(int dtype, const GemmParams& p_in, hipStream_t st) {
     return hipGetLastError();
   }
   if (p.K <= 0) return hipErrorInvalidValue;
+  {
+    auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+    p.vec_epi = p.ldc % 8 == 0 && (p.batch == 1 || p.sC % 8 == 0) && al16(p.C) &&
+                al16(p.aux_in) && al16(p.aux_out);
+  }
   const bool use_pipe = pipe_ok(p) && !getenv("NC_GEMM_NO_PIPE");
   hipError_t e = use_pipe ? launch_pipe(p, st) : launch_bf16_cfg<256, 256, 2, 4>(p, st);
   if (e != hipSuccess || p.splits == 1) return e;
   const int64_t total = (int64_t)p.M * p.N * p.batch;
-  const int blocks = (int)std::min<int64_t>(ceil_div64(total, 256), 65536);
-  splitk_reduce_kernel<<<blocks, 256, 0, st>>>(p);
+  const bool rows_ok = p.N % 4 == 0 && p.ldc % 4 == 0 && (p.batch == 1 || p.sC % 4 == 0) &&
+                       (reinterpret_cast<uintptr_t>(p.C) & 15) == 0 &&
+                       (int64_t)p.M * p.batch <= 0x7fffffff;
+  if (rows_ok) {
+    splitk_reduce_rows_kernel<<<p.M * p.batch, 256, 0, st>>>(p);
+  } else {
+    const int blocks = (int)std::min<int64_t>(ceil_div64(total, 256), 65536);
+    splitk_reduce_kernel<<<blocks, 256, 0, st>>>(p);
+  }
   return hipGetLastError();
 }

@@ -49,6 +49,35 @@ def test_gemm_layouts_ragged(dtype, al, bl):
     assert max_rel(host(C), ref) < 2e-6
 
 
+@pytest.mark.parametrize("epi", ["store", "relu2", "acc_f32"])
+def test_gemm_unaligned_output_rows(epi):
+    """N = 131 (ldc not a multiple of 8): the epilogue's per-element path."""
+    M, N, K = 300, 131, 96
+    rng = np.random.default_rng(8)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    B = rng.standard_normal((N, K)).astype(np.float32)
+    dA, dB = dev(A, BF), dev(B, BF)
+    acc = host(dA) @ host(dB).T
+    if epi == "store":
+        C = torch.empty(M, N, dtype=BF, device="cuda")
+        nc.gemm(dA, 0, dB, 0, C, M, N, K, nc.EPI_STORE, alpha=2.0)
+        torch.cuda.synchronize()
+        assert max_rel(host(C), 2.0 * acc) < 2 ** -8
+    elif epi == "relu2":
+        H = torch.empty(M, N, dtype=BF, device="cuda")
+        G = torch.empty(M, N, dtype=BF, device="cuda")
+        nc.gemm(dA, 0, dB, 0, H, M, N, K, nc.EPI_RELU2, aux_out=G)
+        torch.cuda.synchronize()
+        assert max_rel(host(H), acc) < 2 ** -8
+        assert max_rel(host(G), np.maximum(acc, 0) ** 2) < 2 ** -8
+    else:
+        C0 = rng.standard_normal((M, N)).astype(np.float32)
+        C = dev(C0, F32)
+        nc.gemm(dA, 0, dB, 0, C, M, N, K, nc.EPI_ACC_F32)
+        torch.cuda.synchronize()
+        assert max_rel(host(C), C0 + acc) < 2e-6
+
+
 def test_gemm_epilogues_bf16():
     M, N, K = 320, 264, 136
     rng = np.random.default_rng(3)
