@@ -77,6 +77,11 @@ NC_DEV bf16x8 pack_half(const float* v, int hf) {
   return r;
 }
 
+// 2^x with the hardware instruction alone (v_exp_f32): softmax weights below
+// 2^-126 flush to zero, which the library exp2f's denormal range handling
+// (a compare, two selects and a v_ldexp per call) would otherwise preserve.
+NC_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 NC_DEV f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -213,39 +218,47 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
       for (int s = 0; s < 8; ++s)
         sacc[kb] = mfma(fa_frag_k(ks, kb * 32 + l32, s * 2 + half), qf[s], sacc[kb]);
     }
+    // Online softmax in the log2 domain.  The running max m of a query only
+    // moves when the tile's max exceeds it by more than 8: the weights
+    // 2^(x - m) then stay below 2^8, and O and l are rescaled only on the
+    // (rare, after the first tiles) moves, skipped when no lane moves.
     const bool need_mask = kv * 64 + 63 > q0w;
-    float sv[2][16];
     float mt = -INFINITY;
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kv * 64 + kb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+          if (key > myq) sacc[kb][e] = -INFINITY;
+        }
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float x = sacc[kb][e] * scale_log2;
-        if (need_mask) {
-          const int key = kv * 64 + kb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
-          if (key > myq) x = -INFINITY;
-        }
-        sv[kb][e] = x;
-        mt = fmaxf(mt, x);
-      }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float mn = fmaxf(m, mt);
-    const float alpha = exp2f(m - mn);
+      for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[kb][e]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * scale_log2;
+    const bool move = mt > m + 8.f;
+    if (__builtin_amdgcn_ballot_w64(move)) {
+      const float alpha = move ? fast_exp2(m - mt) : 1.f;
+      if (move) m = mt;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+    }
+    float sv[2][16];
     float ls = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float pv = exp2f(sv[kb][e] - mn);
+        const float pv = fast_exp2(fmaf(sacc[kb][e], scale_log2, -m));
         sv[kb][e] = pv;
         ls += pv;
       }
-    l = l * alpha + ls;
-    m = mn;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+    l += ls;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const bf16x8 pf = pack_half(sv[j >> 1], j & 1);
@@ -362,7 +375,15 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
         pacc[qb] = mfma(fa_frag_k(dOs, qb * 32 + l32, s * 2 + half), vf[s], pacc[qb]);
       }
     }
-    const bool need_mask = qt * 64 < k0w + 31;
+    // causal mask (only tiles that reach the diagonal): queries before the key
+    if (qt * 64 < k0w + 31) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (qt * 64 + qb * 32 + (e >> 2) * 8 + half * 4 + (e & 3) < mykey)
+            sacc[qb][e] = -INFINITY;
+    }
     float p[2][16], ds[2][16];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
@@ -376,8 +397,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int e = g * 4 + i;
-          float pv = exp2f(sacc[qb][e] * scale_log2 - la[i] * kLog2e);
-          if (need_mask && qt * 64 + ql + i < mykey) pv = 0.f;
+          const float pv = fast_exp2(fmaf(sacc[qb][e], scale_log2, -la[i] * kLog2e));
           p[qb][e] = pv;
           ds[qb][e] = pv * (pacc[qb][e] - da[i]);
         }
@@ -477,14 +497,20 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
         pacc[kb] = mfma(fa_frag_k(Vs, kb * 32 + l32, s * 2 + half), df[s], pacc[kb]);
       }
     }
-    const bool need_mask = kv * 64 + 63 > q0w;
+    // causal mask (only tiles that reach the diagonal): keys after the query
+    if (kv * 64 + 63 > q0w) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (kv * 64 + kb * 32 + (e >> 2) * 8 + half * 4 + (e & 3) > myq) sacc[kb][e] = -INFINITY;
+    }
     float ds[2][16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        float pv = exp2f(sacc[kb][e] * scale_log2 - lse2);
-        if (need_mask && kv * 64 + kb * 32 + (e >> 2) * 8 + half * 4 + (e & 3) > myq) pv = 0.f;
+        const float pv = fast_exp2(fmaf(sacc[kb][e], scale_log2, -lse2));
         ds[kb][e] = pv * (pacc[kb][e] - Dq);
       }
 #pragma unroll
