@@ -293,6 +293,122 @@ __global__ void qk_norm_rope_bwd_kernel(T* __restrict__ dqkv, const T* __restric
   dqkv[off + lane + 64] = to_t<T>(rs * (dy2 - y2 * mean));
 }
 
+// bf16 versions with 16-byte accesses: 8 lanes per (token, head); lane u of
+// the group owns dims 8u..8u+7 and their rotary partners 64+8u..64+8u+7.
+NC_DEV float group8_sum(float v) {
+  v += __shfl_xor(v, 1, 64);
+  v += __shfl_xor(v, 2, 64);
+  v += __shfl_xor(v, 4, 64);
+  return v;
+}
+NC_DEV void ld8f(const bf16* p, float (&x)[8]) {
+  const bf16x8 h = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = static_cast<float>(h[e]);
+}
+NC_DEV void st8f(bf16* p, const float (&x)[8]) {
+  bf16x8 h;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) h[e] = static_cast<bf16>(x[e]);
+  *reinterpret_cast<bf16x8*>(p) = h;
+}
+NC_DEV void ld8f(const float* p, float (&x)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+__global__ __launch_bounds__(256) void qk_norm_rope_fwd_bf16_kernel(
+    bf16* __restrict__ qkv, float* __restrict__ rqk, const float* __restrict__ cs, int n_tok,
+    int Tlen, int H, float eps) {
+  const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t item = tid >> 3;
+  if (item >= (int64_t)n_tok * 2 * H) return;
+  const int u = threadIdx.x & 7;
+  const int n = (int)(item / (2 * H)), j = (int)(item % (2 * H));
+  bf16* p = qkv + (int64_t)n * (3 * H * 128) + j * 128 + 8 * u;
+  float x1[8], x2[8], c[8], sn[8];
+  ld8f(p, x1);
+  ld8f(p + 64, x2);
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss += x1[e] * x1[e] + x2[e] * x2[e];
+  const float rs = 1.0f / sqrtf(group8_sum(ss) / 128.f + eps);
+  const int t = n % Tlen;
+  ld8f(cs + t * 64 + 8 * u, c);
+  ld8f(cs + Tlen * 64 + t * 64 + 8 * u, sn);
+  float o1[8], o2[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float y1 = x1[e] * rs, y2 = x2[e] * rs;
+    o1[e] = y1 * c[e] - y2 * sn[e];
+    o2[e] = y1 * sn[e] + y2 * c[e];
+  }
+  st8f(p, o1);
+  st8f(p + 64, o2);
+  if (u == 0) rqk[item] = rs;
+}
+
+__global__ __launch_bounds__(256) void qk_norm_rope_bwd_bf16_kernel(
+    bf16* __restrict__ dqkv, const bf16* __restrict__ qkv, const float* __restrict__ rqk,
+    const float* __restrict__ cs, int n_tok, int Tlen, int H) {
+  const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t item = tid >> 3;
+  if (item >= (int64_t)n_tok * 2 * H) return;
+  const int u = threadIdx.x & 7;
+  const int n = (int)(item / (2 * H)), j = (int)(item % (2 * H));
+  const int64_t off = (int64_t)n * (3 * H * 128) + j * 128 + 8 * u;
+  const int t = n % Tlen;
+  float c[8], sn[8], o1[8], o2[8], g1[8], g2[8];
+  ld8f(cs + t * 64 + 8 * u, c);
+  ld8f(cs + Tlen * 64 + t * 64 + 8 * u, sn);
+  ld8f(qkv + off, o1);
+  ld8f(qkv + off + 64, o2);
+  ld8f(dqkv + off, g1);
+  ld8f(dqkv + off + 64, g2);
+  // normalised pre-rotation vector and its gradient, by the inverse rotation
+  float y1[8], y2[8], dy1[8], dy2[8], dot = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    y1[e] = o1[e] * c[e] + o2[e] * sn[e];
+    y2[e] = -o1[e] * sn[e] + o2[e] * c[e];
+    dy1[e] = g1[e] * c[e] + g2[e] * sn[e];
+    dy2[e] = -g1[e] * sn[e] + g2[e] * c[e];
+    dot += dy1[e] * y1[e] + dy2[e] * y2[e];
+  }
+  const float mean = group8_sum(dot) / 128.f;
+  const float rs = rqk[item];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    g1[e] = rs * (dy1[e] - y1[e] * mean);
+    g2[e] = rs * (dy2[e] - y2[e] * mean);
+  }
+  st8f(dqkv + off, g1);
+  st8f(dqkv + off + 64, g2);
+}
+
+__global__ __launch_bounds__(256) void attn_bwd_pre_bf16_kernel(
+    const bf16* __restrict__ o, const bf16* __restrict__ dO, int64_t ld, float* __restrict__ D,
+    int B, int Tlen, int H) {
+  const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t item = tid >> 3;
+  if (item >= (int64_t)B * Tlen * H) return;
+  const int u = threadIdx.x & 7;
+  const int n = (int)(item / H), h = (int)(item % H);
+  const int64_t off = (int64_t)n * ld + h * 128 + 8 * u;
+  float a1[8], a2[8], b1[8], b2[8];
+  ld8f(o + off, a1);
+  ld8f(o + off + 64, a2);
+  ld8f(dO + off, b1);
+  ld8f(dO + off + 64, b2);
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s += a1[e] * b1[e] + a2[e] * b2[e];
+  s = group8_sum(s);
+  const int b = n / Tlen, t = n % Tlen;
+  if (u == 0) D[((int64_t)b * H + h) * Tlen + t] = s;
+}
+
 template <typename T>
 __global__ void attn_bwd_pre_kernel(const T* __restrict__ o, const T* __restrict__ dO,
                                     int64_t ld, float* __restrict__ D, int B, int Tlen, int H) {
@@ -309,35 +425,57 @@ __global__ void attn_bwd_pre_kernel(const T* __restrict__ o, const T* __restrict
 }
 
 // ------------------------------------------------------------ cross-entropy
+// One block per row of logits; the row (V <= 32768, V % 4 == 0) stays in
+// registers, 128 values per thread, so z is read once: max, then
+// e = exp(z - max) kept in place, S = sum e, loss = max + ln S - z[y],
+// dz = scale * (e / S - onehot(y)).
 template <typename T>
 __global__ __launch_bounds__(256) void cross_entropy_kernel(
     const float* __restrict__ z, const int32_t* __restrict__ tgt, T* __restrict__ dz,
     float* __restrict__ loss_rows, int V, float scale) {
+  constexpr int KV = 32;                           // float4 per thread
+  constexpr float kLog2e = 1.4426950408889634f;
   __shared__ float red[4];
   const int row = blockIdx.x;
   const float* zr = z + (int64_t)row * V;
-  float m = -INFINITY, s = 0.f;
-  for (int i = threadIdx.x * 4; i < V; i += 1024) {
-    float v[4];
-    Vec4<float>::load(zr + i, v);
-    const float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
-    const float mn = fmaxf(m, mx);
-    s = s * __expf(m - mn) + __expf(v[0] - mn) + __expf(v[1] - mn) + __expf(v[2] - mn) +
-        __expf(v[3] - mn);
-    m = mn;
+  float v[KV][4];
+  float m = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < KV; ++k) {
+    const int i = threadIdx.x * 4 + k * 1024;
+    if (i < V) {
+      Vec4<float>::load(zr + i, v[k]);
+      m = fmaxf(m, fmaxf(fmaxf(v[k][0], v[k][1]), fmaxf(v[k][2], v[k][3])));
+    }
   }
   const float M = block_max(m, red);
-  const float S = block_sum(m == -INFINITY ? 0.f : s * __expf(m - M), red);
-  const float lse = M + logf(S);
-  const int y = clamp_id(tgt[row], V);
-  if (threadIdx.x == 0) loss_rows[row] = lse - zr[y];
-  T* dr = dz + (int64_t)row * V;
-  for (int i = threadIdx.x * 4; i < V; i += 1024) {
-    float v[4];
-    Vec4<float>::load(zr + i, v);
+  const float ml = M * kLog2e;
+  float s = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = scale * (__expf(v[e] - lse) - (i + e == y ? 1.f : 0.f));
-    Vec4<T>::store(dr + i, v);
+  for (int k = 0; k < KV; ++k) {
+    const int i = threadIdx.x * 4 + k * 1024;
+    if (i < V) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[k][e] = __builtin_amdgcn_exp2f(fmaf(v[k][e], kLog2e, -ml));
+        s += v[k][e];
+      }
+    }
+  }
+  const float S = block_sum(s, red);
+  const int y = clamp_id(tgt[row], V);
+  if (threadIdx.x == 0) loss_rows[row] = M + logf(S) - zr[y];
+  const float inv = 1.f / S;
+  T* dr = dz + (int64_t)row * V;
+#pragma unroll
+  for (int k = 0; k < KV; ++k) {
+    const int i = threadIdx.x * 4 + k * 1024;
+    if (i < V) {
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = scale * (v[k][e] * inv - (i + e == y ? 1.f : 0.f));
+      Vec4<T>::store(dr + i, o);
+    }
   }
 }
 
@@ -607,7 +745,12 @@ hipError_t nc_rmsnorm_bwd(int dtype, const float* dy, const void* y, const float
 hipError_t nc_qk_norm_rope_fwd(int dtype, void* qkv, float* rqk, const float* cs, int n_tok,
                                int T, int H, float eps, hipStream_t st) {
   const int g = ceil_div(n_tok * 2 * H, 4);
-  if (dtype) qk_norm_rope_fwd_kernel<bf16><<<g, 256, 0, st>>>((bf16*)qkv, rqk, cs, n_tok, T, H, eps);
+  const bool vec = (reinterpret_cast<uintptr_t>(qkv) & 15) == 0;
+  if (dtype && !vec)
+    qk_norm_rope_fwd_kernel<bf16><<<g, 256, 0, st>>>((bf16*)qkv, rqk, cs, n_tok, T, H, eps);
+  else if (dtype)
+    qk_norm_rope_fwd_bf16_kernel<<<ceil_div(n_tok * 2 * H, 32), 256, 0, st>>>((bf16*)qkv, rqk, cs,
+                                                                            n_tok, T, H, eps);
   else qk_norm_rope_fwd_kernel<float><<<g, 256, 0, st>>>((float*)qkv, rqk, cs, n_tok, T, H, eps);
   return hipGetLastError();
 }
@@ -615,8 +758,12 @@ hipError_t nc_qk_norm_rope_fwd(int dtype, void* qkv, float* rqk, const float* cs
 hipError_t nc_qk_norm_rope_bwd(int dtype, void* dqkv, const void* qkv, const float* rqk,
                                const float* cs, int n_tok, int T, int H, hipStream_t st) {
   const int g = ceil_div(n_tok * 2 * H, 4);
-  if (dtype)
+  const bool vec = ((reinterpret_cast<uintptr_t>(dqkv) | reinterpret_cast<uintptr_t>(qkv)) & 15) == 0;
+  if (dtype && !vec)
     qk_norm_rope_bwd_kernel<bf16><<<g, 256, 0, st>>>((bf16*)dqkv, (const bf16*)qkv, rqk, cs, n_tok, T, H);
+  else if (dtype)
+    qk_norm_rope_bwd_bf16_kernel<<<ceil_div(n_tok * 2 * H, 32), 256, 0, st>>>(
+        (bf16*)dqkv, (const bf16*)qkv, rqk, cs, n_tok, T, H);
   else
     qk_norm_rope_bwd_kernel<float><<<g, 256, 0, st>>>((float*)dqkv, (const float*)qkv, rqk, cs, n_tok, T, H);
   return hipGetLastError();
@@ -625,7 +772,13 @@ hipError_t nc_qk_norm_rope_bwd(int dtype, void* dqkv, const void* qkv, const flo
 hipError_t nc_attn_bwd_pre(int dtype, const void* o, const void* dO, int64_t ld, float* D,
                            int B, int T, int H, hipStream_t st) {
   const int g = ceil_div(B * T * H, 4);
-  if (dtype) attn_bwd_pre_kernel<bf16><<<g, 256, 0, st>>>((const bf16*)o, (const bf16*)dO, ld, D, B, T, H);
+  const bool vec = ld % 8 == 0 &&
+                   ((reinterpret_cast<uintptr_t>(o) | reinterpret_cast<uintptr_t>(dO)) & 15) == 0;
+  if (dtype && !vec)
+    attn_bwd_pre_kernel<bf16><<<g, 256, 0, st>>>((const bf16*)o, (const bf16*)dO, ld, D, B, T, H);
+  else if (dtype)
+    attn_bwd_pre_bf16_kernel<<<ceil_div(B * T * H, 32), 256, 0, st>>>((const bf16*)o,
+                                                                     (const bf16*)dO, ld, D, B, T, H);
   else attn_bwd_pre_kernel<float><<<g, 256, 0, st>>>((const float*)o, (const float*)dO, ld, D, B, T, H);
   return hipGetLastError();
 }

@@ -463,14 +463,12 @@ hipError_t launch_bf16_cfg(const GemmParams& p, hipStream_t st) {
 // applied by choosing which global chunk each lane fetches.  Needs K % 32 == 0
 // (rows beyond M or N are clamped to valid memory and discarded).
 // Each wave owns a 128 x 64 output tile (4 x 2 MFMA tiles): WM x WN waves
-// make a (128 WM) x (64 WN) block tile.  256 x 128 blocks with 3 stages fit
-// twice per CU (72 KB of LDS each), so one block's prologue and epilogue
-// overlap the other's main loop.
-template <int WM_, int WN_, int ST_, bool FP_ = false>
+// make a (128 WM) x (64 WN) block tile; the launcher uses 2 x 4 waves and 4
+// stages (256 x 256 tiles, 128 KB of LDS, one block per CU).
+template <int WM_, int WN_, int ST_>
 struct Pipe {
   static constexpr int BM = 128 * WM_, BN = 64 * WN_, PK = 32, STAGES = ST_;
   static constexpr int WM = WM_, WN = WN_;
-  static constexpr bool FP = FP_;   // fragments of the next k-substep read during the MFMAs
   static constexpr int kBlocksPerCU = (BM + BN) * PK * 2 * ST_ <= 80 * 1024 ? 2 : 1;
   static constexpr int NT = WM * WN * 64;
   static constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
@@ -553,10 +551,10 @@ NC_DEV void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int AL, int BL, int WM_, int WN_, int ST_, bool FP_>
-__global__ __launch_bounds__(WM_ * WN_ * 64, (Pipe<WM_, WN_, ST_, FP_>::kBlocksPerCU))
+template <int AL, int BL, int WM_, int WN_, int ST_>
+__global__ __launch_bounds__(WM_ * WN_ * 64, (Pipe<WM_, WN_, ST_>::kBlocksPerCU))
 void gemm_bf16_pipe_kernel(GemmParams p) {
-  using C = Pipe<WM_, WN_, ST_, FP_>;
+  using C = Pipe<WM_, WN_, ST_>;
   constexpr int BM = C::BM, BN = C::BN, PK = C::PK, STAGES = C::STAGES, WN = C::WN;
   constexpr int WTM = C::WTM, WTN = C::WTN, TM = C::TM, TN = C::TN;
   constexpr int TILE_A = C::TILE_A, STAGE = C::STAGE;
@@ -565,7 +563,6 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(1024))) bf16 st1[STAGE];
   __shared__ __attribute__((aligned(1024))) bf16 st2[STAGE];
   __shared__ __attribute__((aligned(1024))) bf16 st3[STAGE];
-  __shared__ __attribute__((aligned(1024))) bf16 st4[STAGE];
 
   const int tiles_m = ceil_div(p.M, BM), tiles_n = ceil_div(p.N, BN);
   int tm, tn;
@@ -600,8 +597,7 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
     if constexpr (S == 0) return st0;
     else if constexpr (S == 1) return st1;
     else if constexpr (S == 2) return st2;
-    else if constexpr (S == 3) return st3;
-    else return st4;
+    else return st3;
   };
   auto issue = [&](int kt, bf16* st) {
     issue_tile<BM, AL, LOADS_A>(A, p.lda, m0, p.M, kt * PK, st, wave, lane);
@@ -636,90 +632,16 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
           acc[ii][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ii], fb[j], acc[ii][j], 0, 0, 0);
     }
   };
-  if constexpr (!C::FP) {
-    if (nk > 0) issue(kt0, st0);
-    if (nk > 1) issue(kt0 + 1, st1);
-    if constexpr (STAGES == 4)
-      if (nk > 2) issue(kt0 + 2, st2);
-    for (int i = 0; i < nk; i += STAGES) {
-      step.template operator()<0>(i);
-      if (i + 1 < nk) step.template operator()<1>(i + 1);
-      if (i + 2 < nk) step.template operator()<2>(i + 2);
-      if constexpr (STAGES == 4)
-        if (i + 3 < nk) step.template operator()<3>(i + 3);
-    }
-  } else if (nk > 0) {
-    // Software-pipelined variant: the fragment reads of each k-substep are
-    // issued before the MFMAs of the previous one, so LDS reads and MFMAs
-    // overlap instead of alternating across the barrier.  Tile i+1 must have
-    // landed one substep before its first use, so STAGES - 1 tiles are issued
-    // ahead and STAGES - 3 of them may still be in flight at each wait.
-    bf16x8 f0a[TM], f0b[TN], f1a[TM], f1b[TN];
-    auto read = [&](const bf16* st, int s, bf16x8 (&fa)[TM], bf16x8 (&fb)[TN]) {
-#pragma unroll
-      for (int ii = 0; ii < TM; ++ii) fa[ii] = frag<BM, AL>(st, wm * WTM + ii * 32, s, lane);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) fb[j] = frag<BN, BL>(st + TILE_A, wn * WTN + j * 32, s, lane);
-    };
-    auto mma = [&](const bf16x8 (&fa)[TM], const bf16x8 (&fb)[TN]) {
-#pragma unroll
-      for (int ii = 0; ii < TM; ++ii)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[ii][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ii], fb[j], acc[ii][j], 0, 0, 0);
-    };
-    // wait until tile t has landed, given the tiles issued after it
-    auto wait_tile = [&](int t) {
-      const int younger = min(nk - 1 - t, STAGES - 3);
-      if (younger >= 2) wait_vmcnt<2 * LOADS>();
-      else if (younger == 1) wait_vmcnt<LOADS>();
-      else wait_vmcnt<0>();
-      asm volatile("s_barrier" ::: "memory");
-    };
-    if (nk > 0) issue(kt0, st0);
-    if (nk > 1) issue(kt0 + 1, st1);
+  if (nk > 0) issue(kt0, st0);
+  if (nk > 1) issue(kt0 + 1, st1);
+  if constexpr (STAGES == 4)
     if (nk > 2) issue(kt0 + 2, st2);
-    if constexpr (STAGES == 5)
-      if (nk > 3) issue(kt0 + 3, st3);
-    {
-      // tile 0 landed: the tiles issued after it are 1 .. STAGES-2
-      const int younger = min(nk - 1, STAGES - 2);
-      if (younger >= 3) wait_vmcnt<3 * LOADS>();
-      else if (younger == 2) wait_vmcnt<2 * LOADS>();
-      else if (younger == 1) wait_vmcnt<LOADS>();
-      else wait_vmcnt<0>();
-      asm volatile("s_barrier" ::: "memory");
-    }
-    read(st0, 0, f0a, f0b);
-    auto pstep = [&]<int S>(int i) {
-      const bf16* cur = sbuf.template operator()<S>();
-      read(cur, 1, f1a, f1b);
-      // keep the reads ahead of the MFMAs (the scheduler would otherwise sink
-      // them past the MFMAs and reuse one register set for both substeps)
-      __builtin_amdgcn_sched_barrier(0);
-      mma(f0a, f0b);
-      if (i + 1 < nk) {
-        wait_tile(i + 1);
-        // every wave is past the MFMAs of tile i-1: its stage can be refilled
-        if (i + STAGES - 1 < nk)
-          issue(kt0 + i + STAGES - 1, sbuf.template operator()<(S + STAGES - 1) % STAGES>());
-      }
-      // Unconditional (after the last tile it reads a stale stage and the
-      // values go unused): reads issued on every path let the compiler wait
-      // for just the older substep's fragments before the MFMAs below.
-      read(sbuf.template operator()<(S + 1) % STAGES>(), 0, f0a, f0b);
-      __builtin_amdgcn_sched_barrier(0);
-      mma(f1a, f1b);
-    };
-    for (int i = 0; i < nk; i += STAGES) {
-      pstep.template operator()<0>(i);
-      if (i + 1 < nk) pstep.template operator()<1>(i + 1);
-      if (i + 2 < nk) pstep.template operator()<2>(i + 2);
-      if constexpr (STAGES >= 4)
-        if (i + 3 < nk) pstep.template operator()<3>(i + 3);
-      if constexpr (STAGES == 5)
-        if (i + 4 < nk) pstep.template operator()<4>(i + 4);
-    }
+  for (int i = 0; i < nk; i += STAGES) {
+    step.template operator()<0>(i);
+    if (i + 1 < nk) step.template operator()<1>(i + 1);
+    if (i + 2 < nk) step.template operator()<2>(i + 2);
+    if constexpr (STAGES == 4)
+      if (i + 3 < nk) step.template operator()<3>(i + 3);
   }
 
   // ---- epilogue, staged through the (now idle) stage buffers: each wave
@@ -796,27 +718,26 @@ bool pipe_ok(const GemmParams& p) {
   return true;
 }
 
-template <int WM, int WN, int ST, bool FP = false>
+template <int WM, int WN, int ST>
 hipError_t launch_pipe_cfg(const GemmParams& p, hipStream_t st) {
-  using C = Pipe<WM, WN, ST, FP>;
+  using C = Pipe<WM, WN, ST>;
   const int tiles = ceil_div(p.M, C::BM) * ceil_div(p.N, C::BN);
   dim3 grid(tiles, 1, p.batch * p.splits);
   constexpr int NT = WM * WN * 64;
   switch (p.a_layout * 2 + p.b_layout) {
-    case 0: gemm_bf16_pipe_kernel<kKCont, kKCont, WM, WN, ST, FP><<<grid, NT, 0, st>>>(p); break;
-    case 1: gemm_bf16_pipe_kernel<kKCont, kMNCont, WM, WN, ST, FP><<<grid, NT, 0, st>>>(p); break;
-    case 2: gemm_bf16_pipe_kernel<kMNCont, kKCont, WM, WN, ST, FP><<<grid, NT, 0, st>>>(p); break;
-    default: gemm_bf16_pipe_kernel<kMNCont, kMNCont, WM, WN, ST, FP><<<grid, NT, 0, st>>>(p); break;
+    case 0: gemm_bf16_pipe_kernel<kKCont, kKCont, WM, WN, ST><<<grid, NT, 0, st>>>(p); break;
+    case 1: gemm_bf16_pipe_kernel<kKCont, kMNCont, WM, WN, ST><<<grid, NT, 0, st>>>(p); break;
+    case 2: gemm_bf16_pipe_kernel<kMNCont, kKCont, WM, WN, ST><<<grid, NT, 0, st>>>(p); break;
+    default: gemm_bf16_pipe_kernel<kMNCont, kMNCont, WM, WN, ST><<<grid, NT, 0, st>>>(p); break;
   }
   return hipGetLastError();
 }
 
+// 256 x 256 block tiles (8 waves of 128 x 64), 4 stages, one block per CU.
+// Measured against 256 x 128 tiles at two blocks per CU, 5 stages, fragment
+// prefetch across k-substeps and 4 waves of 128 x 128: none was faster.
 hipError_t launch_pipe(const GemmParams& p, hipStream_t st) {
-  static const int cfg = getenv("NC_GEMM_CFG") ? atoi(getenv("NC_GEMM_CFG")) : 2;
-  if (cfg == 1) return launch_pipe_cfg<2, 2, 3>(p, st);   // 256 x 128, two blocks per CU
-  if (cfg == 3) return launch_pipe_cfg<2, 4, 5, true>(p, st);
-  if (cfg == 4) return launch_pipe_cfg<2, 4, 4, true>(p, st);
-  return launch_pipe_cfg<2, 4, 4>(p, st);                 // 256 x 256, one block per CU
+  return launch_pipe_cfg<2, 4, 4>(p, st);
 }
 
 }  // namespace
@@ -870,7 +791,7 @@ hipError_t nc_launch_gemm(int dtype, const GemmParams& p_in, hipStream_t st) {
     p.vec_epi = p.ldc % 8 == 0 && (p.batch == 1 || p.sC % 8 == 0) && al16(p.C) &&
                 al16(p.aux_in) && al16(p.aux_out);
   }
-  const bool use_pipe = pipe_ok(p) && !getenv("NC_GEMM_NO_PIPE");
+  const bool use_pipe = pipe_ok(p);
   hipError_t e = use_pipe ? launch_pipe(p, st) : launch_bf16_cfg<256, 256, 2, 4>(p, st);
   if (e != hipSuccess || p.splits == 1) return e;
   const int64_t total = (int64_t)p.M * p.N * p.batch;
