@@ -82,6 +82,13 @@ NC_DEV bf16x8 pack_half(const float* v, int hf) {
 // (a compare, two selects and a v_ldexp per call) would otherwise preserve.
 NC_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Make the compiler wait for a register loaded from global memory here, once.
+// Without it, the first use inside the main loop carries s_waitcnt vmcnt(n)
+// in every iteration (the count cannot tell the preheader's loads from the
+// loop's), and those waits also drain the next tile's prefetch in flight.
+NC_DEV void settle(bf16x8& x) { asm volatile("" : "+v"(x)); }
+NC_DEV void settle(float& x) { asm volatile("" : "+v"(x)); }
+
 NC_DEV f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -165,17 +172,13 @@ NC_DEV bf16x8 fa_frag_vt(const bf16* tile, int row_base, int col_base, int lane)
   return v;
 }
 
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
+// one 128-query block qb of head bh; st0 / st1: K | V stages of 2 x 64 x 128
+NC_DEV void attn_fwd_block(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, bf16* __restrict__ o, int64_t ldo, float* __restrict__ lse, int T, int H,
-    float scale_log2) {
+    float scale_log2, int qb, int bh, bf16* st0, bf16* st1) {
   constexpr int KT = 64 * 128;                    // one 64 x 128 tile
-  __shared__ __attribute__((aligned(1024))) bf16 st0[2 * KT];   // K | V of even tiles
-  __shared__ __attribute__((aligned(1024))) bf16 st1[2 * KT];   // K | V of odd tiles
-
-  const int nqb = T / 128;
-  const int qb = nqb - 1 - (int)(blockIdx.x % nqb);
-  const int bh = blockIdx.x / nqb, b = bh / H, h = bh % H;
+  const int b = bh / H, h = bh % H;
   const int64_t base = (int64_t)b * T * ld + h * 128;
   const bf16* qg = q + base;
   const bf16* kg = k + base;
@@ -190,6 +193,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 #pragma unroll
   for (int s = 0; s < 8; ++s)
     qf[s] = *reinterpret_cast<const bf16x8*>(qg + (int64_t)myq * ld + s * 16 + half * 8);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) settle(qf[s]);
 
   f32x16 oacc[4];
 #pragma unroll
@@ -310,19 +315,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 // stay in registers as the B operands) and walks the 64-query tiles from the
 // diagonal down.  Q, dO and the tile's log-sum-exp and D reach LDS by direct
 // loads, double-buffered; Q^T and dO^T fragments come from transpose reads.
-__global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
+constexpr int kDkvStage = 2 * 64 * 128 + 256;     // Q | dO | lse[64] D[64] (fp32)
+
+// one 128-key block kblk of head bh; st0 / st1: stages of kDkvStage elements
+NC_DEV void attn_bwd_dkv_block(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, const bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ lse,
     const float* __restrict__ Dv, bf16* __restrict__ dk, bf16* __restrict__ dv, int64_t ldd,
-    int T, int H, float scale_log2, float scale) {
+    int T, int H, float scale_log2, float scale, int kblk, int bh, bf16* st0, bf16* st1) {
   constexpr int KT = 64 * 128;
-  constexpr int STAGE = 2 * KT + 256;             // Q | dO | lse[64] D[64] (fp32)
-  __shared__ __attribute__((aligned(1024))) bf16 st0[STAGE];
-  __shared__ __attribute__((aligned(1024))) bf16 st1[STAGE];
-
-  const int nkb = T / 128;
-  const int kblk = blockIdx.x % nkb;
-  const int bh = blockIdx.x / nkb, b = bh / H, h = bh % H;
+  const int b = bh / H, h = bh % H;
   const int64_t base = (int64_t)b * T * ld + h * 128;
   const int64_t obase = (int64_t)b * T * ldo + h * 128;
   const float* lse_bh = lse + ((int64_t)b * H + h) * T;
@@ -338,6 +340,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
   for (int s = 0; s < 8; ++s) {
     kf[s] = *reinterpret_cast<const bf16x8*>(k + base + (int64_t)mykey * ld + s * 16 + half * 8);
     vf[s] = *reinterpret_cast<const bf16x8*>(v + base + (int64_t)mykey * ld + s * 16 + half * 8);
+  }
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    settle(kf[s]);
+    settle(vf[s]);
   }
   f32x16 dkacc[4], dvacc[4];
 #pragma unroll
@@ -438,18 +445,14 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
 // A workgroup owns 128 queries (4 waves x 32) and walks the 64-key tiles up
 // to the diagonal, like the forward pass: S^T = K Q^T and dP^T = V dO^T with
 // one query per lane, then dQ += dS K with K^T fragments from transpose reads.
-__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
+// one 128-query block qb of head bh; st0 / st1: K | V stages of 2 x 64 x 128
+NC_DEV void attn_bwd_dq_block(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, const bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ lse,
     const float* __restrict__ Dv, bf16* __restrict__ dq, int64_t ldd, int T, int H,
-    float scale_log2, float scale) {
+    float scale_log2, float scale, int qb, int bh, bf16* st0, bf16* st1) {
   constexpr int KT = 64 * 128;
-  __shared__ __attribute__((aligned(1024))) bf16 st0[2 * KT];   // K | V
-  __shared__ __attribute__((aligned(1024))) bf16 st1[2 * KT];
-
-  const int nqb = T / 128;
-  const int qb = nqb - 1 - (int)(blockIdx.x % nqb);
-  const int bh = blockIdx.x / nqb, b = bh / H, h = bh % H;
+  const int b = bh / H, h = bh % H;
   const int64_t base = (int64_t)b * T * ld + h * 128;
   const int64_t obase = (int64_t)b * T * ldo + h * 128;
   const bf16* kg = k + base;
@@ -466,8 +469,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     qf[s] = *reinterpret_cast<const bf16x8*>(q + base + (int64_t)myq * ld + s * 16 + half * 8);
     df[s] = *reinterpret_cast<const bf16x8*>(dO + obase + (int64_t)myq * ldo + s * 16 + half * 8);
   }
-  const float lse2 = lse[((int64_t)b * H + h) * T + myq] * kLog2e;
-  const float Dq = Dv[((int64_t)b * H + h) * T + myq];
+  float lse2 = lse[((int64_t)b * H + h) * T + myq] * kLog2e;
+  float Dq = Dv[((int64_t)b * H + h) * T + myq];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    settle(qf[s]);
+    settle(df[s]);
+  }
+  settle(lse2);
+  settle(Dq);
   f32x16 dqacc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -537,6 +547,67 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
       const int qq = q0w + (e >> 2) * 8 + half * 4 + (e & 3);
       dq[((int64_t)b * T + qq) * ldd + h * 128 + db * 32 + l32] = (bf16)(dqacc[db][e] * scale);
     }
+}
+
+// Causal work per 128-row block grows linearly with its index, so each
+// workgroup takes block i and its mirror nb-1-i of the same head (the middle
+// block alone when nb is odd): equal work per workgroup, no tail of long
+// blocks at the end of the grid.
+NC_DEV void mirror_pair(int nb, int& first, int& second, int& bh) {
+  const int npair = (nb + 1) / 2;
+  bh = blockIdx.x / npair;
+  const int i = blockIdx.x % npair;
+  first = nb - 1 - i;                              // the longer one first
+  second = i == nb - 1 - i ? -1 : i;
+}
+
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    int64_t ld, bf16* __restrict__ o, int64_t ldo, float* __restrict__ lse, int T, int H,
+    float scale_log2) {
+  __shared__ __attribute__((aligned(1024))) bf16 st0[2 * 64 * 128];   // K | V of even tiles
+  __shared__ __attribute__((aligned(1024))) bf16 st1[2 * 64 * 128];   // K | V of odd tiles
+  int first, second, bh;
+  mirror_pair(T / 128, first, second, bh);
+  attn_fwd_block(q, k, v, ld, o, ldo, lse, T, H, scale_log2, first, bh, st0, st1);
+  if (second < 0) return;
+  __syncthreads();                                 // the first block's O staging is read
+  attn_fwd_block(q, k, v, ld, o, ldo, lse, T, H, scale_log2, second, bh, st0, st1);
+}
+
+__global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    int64_t ld, const bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ lse,
+    const float* __restrict__ Dv, bf16* __restrict__ dk, bf16* __restrict__ dv, int64_t ldd,
+    int T, int H, float scale_log2, float scale) {
+  __shared__ __attribute__((aligned(1024))) bf16 st0[kDkvStage];
+  __shared__ __attribute__((aligned(1024))) bf16 st1[kDkvStage];
+  int first, second, bh;
+  mirror_pair(T / 128, first, second, bh);
+  // key block kblk walks T/64 - 2 kblk query tiles: the longer one is kblk = second
+  if (second >= 0)
+    attn_bwd_dkv_block(q, k, v, ld, dO, ldo, lse, Dv, dk, dv, ldd, T, H, scale_log2, scale,
+                       second, bh, st0, st1);
+  __syncthreads();
+  attn_bwd_dkv_block(q, k, v, ld, dO, ldo, lse, Dv, dk, dv, ldd, T, H, scale_log2, scale, first,
+                     bh, st0, st1);
+}
+
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    int64_t ld, const bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ lse,
+    const float* __restrict__ Dv, bf16* __restrict__ dq, int64_t ldd, int T, int H,
+    float scale_log2, float scale) {
+  __shared__ __attribute__((aligned(1024))) bf16 st0[2 * 64 * 128];   // K | V
+  __shared__ __attribute__((aligned(1024))) bf16 st1[2 * 64 * 128];
+  int first, second, bh;
+  mirror_pair(T / 128, first, second, bh);
+  attn_bwd_dq_block(q, k, v, ld, dO, ldo, lse, Dv, dq, ldd, T, H, scale_log2, scale, first, bh,
+                    st0, st1);
+  if (second < 0) return;
+  __syncthreads();
+  attn_bwd_dq_block(q, k, v, ld, dO, ldo, lse, Dv, dq, ldd, T, H, scale_log2, scale, second, bh,
+                    st0, st1);
 }
 
 // ========================================================== fp32 path
@@ -643,7 +714,7 @@ hipError_t nc_attn_fwd(int dtype, const void* q, const void* k, const void* v, i
   const float scale = 1.0f / sqrtf(128.f);
   if (dtype) {
     if (T % 128) return hipErrorInvalidValue;
-    attn_fwd_kernel<<<B * H * (T / 128), 256, 0, st>>>((const bf16*)q, (const bf16*)k,
+    attn_fwd_kernel<<<B * H * ((T / 128 + 1) / 2), 256, 0, st>>>((const bf16*)q, (const bf16*)k,
                                                         (const bf16*)v, ld, (bf16*)o, ldo, lse,
                                                         T, H, scale * kLog2e);
   } else {
@@ -659,7 +730,7 @@ hipError_t nc_attn_bwd(int dtype, const void* q, const void* k, const void* v, i
   const float scale = 1.0f / sqrtf(128.f);
   if (dtype) {
     if (T % 128) return hipErrorInvalidValue;
-    const int grid = B * H * (T / 128);
+    const int grid = B * H * ((T / 128 + 1) / 2);
     attn_bwd_dkv_kernel<<<grid, 256, 0, st>>>((const bf16*)q, (const bf16*)k, (const bf16*)v, ld,
                                               (const bf16*)dO, ldo, lse, D, (bf16*)dk, (bf16*)dv,
                                               ldd, T, H, scale * kLog2e, scale);

@@ -15,8 +15,8 @@ enum NcEpi {
   kEpiStore = 0,      // C = alpha*acc (C of the activation type)
   kEpiStoreF32 = 1,   // C(f32) = alpha*acc
   kEpiAccF32 = 2,     // C(f32) += alpha*acc
-  kEpiRelu2 = 3,      // C = acc (pre-activation h), aux_out = max(acc,0)^2
-  kEpiRelu2Bwd = 4,   // C = 2*max(aux_in,0)*acc   (aux_in = stored h)
+  kEpiRelu2 = 3,      // C = max(acc,0)^2           (the MLP activation g)
+  kEpiRelu2Bwd = 4,   // C = 2*sqrt(max(aux_in,0))*acc   (aux_in = stored g: sqrt(g) = max(h,0))
   kEpiPoly = 5,       // C = p0*aux_in + p1*acc    (Newton-Schulz: b*A + c*A*A, a*X + B*X)
   kEpiDual = 6,       // C(f32) = p0*aux_in(f32, optional) + p1*acc; aux_out = C in the
                       // activation type (fp32 iterate + its matrix-core copy)

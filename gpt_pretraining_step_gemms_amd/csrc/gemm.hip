@@ -34,12 +34,12 @@ NC_DEV void epi_one(const GemmParams& p, int64_t off, float v) {
   } else if constexpr (EPI == kEpiAccF32) {
     static_cast<float*>(p.C)[off] += p.alpha * v;
   } else if constexpr (EPI == kEpiRelu2) {
-    static_cast<T*>(p.C)[off] = to_t<T>(v);
     const float r = fmaxf(v, 0.f);
-    static_cast<T*>(p.aux_out)[off] = to_t<T>(r * r);
+    static_cast<T*>(p.C)[off] = to_t<T>(r * r);
   } else if constexpr (EPI == kEpiRelu2Bwd) {
-    const float h = to_f(static_cast<const T*>(p.aux_in)[off]);
-    static_cast<T*>(p.C)[off] = to_t<T>(2.f * fmaxf(h, 0.f) * v);
+    // v_sqrt_f32 (1 ulp) rather than the correctly rounded library sequence
+    const float g = to_f(static_cast<const T*>(p.aux_in)[off]);
+    static_cast<T*>(p.C)[off] = to_t<T>(2.f * __builtin_amdgcn_sqrtf(fmaxf(g, 0.f)) * v);
   } else if constexpr (EPI == kEpiPoly) {
     const float a = to_f(static_cast<const T*>(p.aux_in)[off]);
     static_cast<T*>(p.C)[off] = to_t<T>(p.p0 * a + p.p1 * v);
@@ -96,17 +96,16 @@ NC_DEV void epi_vec8(const GemmParams& p, int64_t off, const float (&v)[8]) {
     for (int e = 0; e < 8; ++e) r[e] = a[e] + p.alpha * v[e];
     st8(static_cast<float*>(p.C) + off, r);
   } else if constexpr (EPI == kEpiRelu2) {
-    st8(static_cast<bf16*>(p.C) + off, v);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float t = fmaxf(v[e], 0.f);
       r[e] = t * t;
     }
-    st8(static_cast<bf16*>(p.aux_out) + off, r);
+    st8(static_cast<bf16*>(p.C) + off, r);
   } else if constexpr (EPI == kEpiRelu2Bwd) {
     ld8(static_cast<const bf16*>(p.aux_in) + off, a);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = 2.f * fmaxf(a[e], 0.f) * v[e];
+    for (int e = 0; e < 8; ++e) r[e] = 2.f * __builtin_amdgcn_sqrtf(fmaxf(a[e], 0.f)) * v[e];
     st8(static_cast<bf16*>(p.C) + off, r);
   } else if constexpr (EPI == kEpiPoly) {
     ld8(static_cast<const bf16*>(p.aux_in) + off, a);
@@ -465,9 +464,9 @@ hipError_t launch_bf16_cfg(const GemmParams& p, hipStream_t st) {
 // Each wave owns a 128 x 64 output tile (4 x 2 MFMA tiles): WM x WN waves
 // make a (128 WM) x (64 WN) block tile; the launcher uses 2 x 4 waves and 4
 // stages (256 x 256 tiles, 128 KB of LDS, one block per CU).
-template <int WM_, int WN_, int ST_>
+template <int WM_, int WN_, int ST_, int PK_ = 32>
 struct Pipe {
-  static constexpr int BM = 128 * WM_, BN = 64 * WN_, PK = 32, STAGES = ST_;
+  static constexpr int BM = 128 * WM_, BN = 64 * WN_, PK = PK_, STAGES = ST_;
   static constexpr int WM = WM_, WN = WN_;
   static constexpr int kBlocksPerCU = (BM + BN) * PK * 2 * ST_ <= 80 * 1024 ? 2 : 1;
   static constexpr int NT = WM * WN * 64;
@@ -500,16 +499,21 @@ NC_DEV void dma16(const void* g, const bf16* lds) {
 }
 
 // One operand tile of ROWS x 32 into LDS; this wave issues NI 1-KB loads.
-template <int ROWS, int LAYOUT, int NI>
+template <int ROWS, int LAYOUT, int NI, int PK>
 NC_DEV void issue_tile(const bf16* __restrict__ base, int64_t ld, int row0, int rows_lim, int k0,
                        bf16* tile, int wave, int lane) {
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int blk = wave * NI + i;               // 1-KB block of the tile
     const bf16* g;
-    if constexpr (LAYOUT == kKCont) {            // 16 rows of 64 B per block
+    if constexpr (LAYOUT == kKCont && PK == 32) {   // 16 rows of 64 B per block
       const int r = blk * 16 + (lane >> 2);
       const int c = (lane & 3) ^ ((r >> 2) & 3);
+      const int row = min(row0 + r, rows_lim - 1);
+      g = base + (int64_t)row * ld + k0 + c * 8;
+    } else if constexpr (LAYOUT == kKCont) {        // PK 64: 8 rows of 128 B per block
+      const int r = blk * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
       const int row = min(row0 + r, rows_lim - 1);
       g = base + (int64_t)row * ld + k0 + c * 8;
     } else {                                     // 1 KB = 1024 / (2 ROWS) k-rows
@@ -525,12 +529,13 @@ NC_DEV void issue_tile(const bf16* __restrict__ base, int64_t ld, int row0, int 
 }
 
 // MFMA fragment (8 k of output row o0 + lane%32, k-substep s) from a tile
-template <int ROWS, int LAYOUT>
+template <int ROWS, int LAYOUT, int PK>
 NC_DEV bf16x8 frag(const bf16* tile, int o0, int s, int lane) {
   if constexpr (LAYOUT == kKCont) {
     const int r = o0 + (lane & 31);
     const int c = s * 2 + (lane >> 5);
-    return *reinterpret_cast<const bf16x8*>(tile + r * 32 + ((c ^ ((r >> 2) & 3)) << 3));
+    const int sw = PK == 32 ? (r >> 2) & 3 : (r >> 1) & 7;
+    return *reinterpret_cast<const bf16x8*>(tile + r * PK + ((c ^ sw) << 3));
   } else {
     const int g = lane >> 4, t = lane & 15;
     const int k = s * 16 + 8 * (g >> 1) + (t >> 2);
@@ -551,10 +556,10 @@ NC_DEV void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int AL, int BL, int WM_, int WN_, int ST_>
-__global__ __launch_bounds__(WM_ * WN_ * 64, (Pipe<WM_, WN_, ST_>::kBlocksPerCU))
+template <int AL, int BL, int WM_, int WN_, int ST_, int PK_>
+__global__ __launch_bounds__(WM_ * WN_ * 64, (Pipe<WM_, WN_, ST_, PK_>::kBlocksPerCU))
 void gemm_bf16_pipe_kernel(GemmParams p) {
-  using C = Pipe<WM_, WN_, ST_>;
+  using C = Pipe<WM_, WN_, ST_, PK_>;
   constexpr int BM = C::BM, BN = C::BN, PK = C::PK, STAGES = C::STAGES, WN = C::WN;
   constexpr int WTM = C::WTM, WTN = C::WTN, TM = C::TM, TN = C::TN;
   constexpr int TILE_A = C::TILE_A, STAGE = C::STAGE;
@@ -600,8 +605,8 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
     else return st3;
   };
   auto issue = [&](int kt, bf16* st) {
-    issue_tile<BM, AL, LOADS_A>(A, p.lda, m0, p.M, kt * PK, st, wave, lane);
-    issue_tile<BN, BL, LOADS_B>(B, p.ldb, n0, p.N, kt * PK, st + TILE_A, wave, lane);
+    issue_tile<BM, AL, LOADS_A, PK>(A, p.lda, m0, p.M, kt * PK, st, wave, lane);
+    issue_tile<BN, BL, LOADS_B, PK>(B, p.ldb, n0, p.N, kt * PK, st + TILE_A, wave, lane);
   };
   auto step = [&]<int S>(int i) {
     // tile i has landed once at most the loads of the (up to two) younger tiles remain
@@ -622,9 +627,9 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
     for (int s = 0; s < PK / 16; ++s) {
       bf16x8 fa[TM], fb[TN];
 #pragma unroll
-      for (int ii = 0; ii < TM; ++ii) fa[ii] = frag<BM, AL>(as, wm * WTM + ii * 32, s, lane);
+      for (int ii = 0; ii < TM; ++ii) fa[ii] = frag<BM, AL, PK>(as, wm * WTM + ii * 32, s, lane);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) fb[j] = frag<BN, BL>(bs, wn * WTN + j * 32, s, lane);
+      for (int j = 0; j < TN; ++j) fb[j] = frag<BN, BL, PK>(bs, wn * WTN + j * 32, s, lane);
 #pragma unroll
       for (int ii = 0; ii < TM; ++ii)
 #pragma unroll
@@ -633,13 +638,15 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
     }
   };
   if (nk > 0) issue(kt0, st0);
-  if (nk > 1) issue(kt0 + 1, st1);
+  if constexpr (STAGES >= 3)
+    if (nk > 1) issue(kt0 + 1, st1);
   if constexpr (STAGES == 4)
     if (nk > 2) issue(kt0 + 2, st2);
   for (int i = 0; i < nk; i += STAGES) {
     step.template operator()<0>(i);
     if (i + 1 < nk) step.template operator()<1>(i + 1);
-    if (i + 2 < nk) step.template operator()<2>(i + 2);
+    if constexpr (STAGES >= 3)
+      if (i + 2 < nk) step.template operator()<2>(i + 2);
     if constexpr (STAGES == 4)
       if (i + 3 < nk) step.template operator()<3>(i + 3);
   }
@@ -653,11 +660,14 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
   constexpr int EP_LD = 72;                          // padded row, floats
   constexpr int EP_FLOATS = 32 * EP_LD;
   constexpr int EP_PER = STAGE * 2 / (EP_FLOATS * 4);  // wave regions per stage buffer
-  static_assert(C::NT / 64 <= 3 * EP_PER, "staging must fit in three stage buffers");
+  constexpr int EP_BUFS = STAGES < 3 ? STAGES : 3;
+  static_assert(C::NT / 64 <= EP_BUFS * EP_PER, "staging must fit in the stage buffers");
   asm volatile("s_barrier" ::: "memory");            // every wave is done with the ring
   const int sidx = wave / EP_PER;
-  float* stg = reinterpret_cast<float*>(sidx == 0 ? st0 : (sidx == 1 ? st1 : st2)) +
-               (wave % EP_PER) * EP_FLOATS;
+  bf16* sbase;
+  if constexpr (EP_BUFS >= 3) sbase = sidx == 0 ? st0 : (sidx == 1 ? st1 : st2);
+  else sbase = sidx == 0 ? st0 : st1;
+  float* stg = reinterpret_cast<float*>(sbase) + (wave % EP_PER) * EP_FLOATS;
   const bool split_out = p.splits > 1;
   float* W = split_out ? p.workspace + ((int64_t)split * p.batch + b) * (int64_t)p.M * p.N
                        : nullptr;
@@ -718,25 +728,31 @@ bool pipe_ok(const GemmParams& p) {
   return true;
 }
 
-template <int WM, int WN, int ST>
+template <int WM, int WN, int ST, int PK = 32>
 hipError_t launch_pipe_cfg(const GemmParams& p, hipStream_t st) {
-  using C = Pipe<WM, WN, ST>;
+  using C = Pipe<WM, WN, ST, PK>;
   const int tiles = ceil_div(p.M, C::BM) * ceil_div(p.N, C::BN);
   dim3 grid(tiles, 1, p.batch * p.splits);
   constexpr int NT = WM * WN * 64;
   switch (p.a_layout * 2 + p.b_layout) {
-    case 0: gemm_bf16_pipe_kernel<kKCont, kKCont, WM, WN, ST><<<grid, NT, 0, st>>>(p); break;
-    case 1: gemm_bf16_pipe_kernel<kKCont, kMNCont, WM, WN, ST><<<grid, NT, 0, st>>>(p); break;
-    case 2: gemm_bf16_pipe_kernel<kMNCont, kKCont, WM, WN, ST><<<grid, NT, 0, st>>>(p); break;
-    default: gemm_bf16_pipe_kernel<kMNCont, kMNCont, WM, WN, ST><<<grid, NT, 0, st>>>(p); break;
+    case 0: gemm_bf16_pipe_kernel<kKCont, kKCont, WM, WN, ST, PK><<<grid, NT, 0, st>>>(p); break;
+    case 1: gemm_bf16_pipe_kernel<kKCont, kMNCont, WM, WN, ST, PK><<<grid, NT, 0, st>>>(p); break;
+    case 2: gemm_bf16_pipe_kernel<kMNCont, kKCont, WM, WN, ST, PK><<<grid, NT, 0, st>>>(p); break;
+    default: gemm_bf16_pipe_kernel<kMNCont, kMNCont, WM, WN, ST, PK><<<grid, NT, 0, st>>>(p); break;
   }
   return hipGetLastError();
 }
 
-// 256 x 256 block tiles (8 waves of 128 x 64), 4 stages, one block per CU.
-// Measured against 256 x 128 tiles at two blocks per CU, 5 stages, fragment
-// prefetch across k-substeps and 4 waves of 128 x 128: none was faster.
+// 256 x 256 block tiles (8 waves of 128 x 64), one block per CU.  With both
+// operands K-contiguous (forward products, Newton-Schulz Gram and polynomial
+// steps) a k-depth of 64 per stage and 2 stages (one barrier per 64 k)
+// measured 3-7 % faster than depth 32 with 4 stages; with an MN-contiguous
+// operand (input and weight gradients) it measured slower, and those keep
+// depth 32.  256 x 128 tiles at two blocks per CU, 5 stages, fragment
+// prefetch across k-substeps and 4 waves of 128 x 128 were all slower.
 hipError_t launch_pipe(const GemmParams& p, hipStream_t st) {
+  if (p.a_layout == kKCont && p.b_layout == kKCont && p.K % 64 == 0)
+    return launch_pipe_cfg<2, 4, 2, 64>(p, st);
   return launch_pipe_cfg<2, 4, 4>(p, st);
 }
 

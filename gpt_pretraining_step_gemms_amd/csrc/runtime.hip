@@ -12,9 +12,10 @@
 //   rotary table cos/sin [2][T][64].
 // Activation arena: what the backward pass reads per layer (RMSNorm outputs
 // and reciprocal RMS, q/k/v after QK-norm+rotary, QK-norm reciprocal RMS,
-// attention output and log-sum-exp, MLP pre-activation h and ReLU^2 output
-// g), then scratch (residual stream x and its gradient, lm_head logits of one
-// row chunk, split-K, embedding-sort and Newton-Schulz workspaces).
+// attention output and log-sum-exp, the MLP activation g = max(h,0)^2; the
+// pre-activation h is not kept, since max(h,0) = sqrt(g)), then scratch
+// (residual stream x and its gradient, lm_head logits of one row chunk,
+// split-K, embedding-sort and Newton-Schulz workspaces).
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
@@ -48,7 +49,7 @@ struct ParamInfo {
   int64_t adam_elem;  // element offset in the AdamW regions, -1 for Muon
 };
 
-struct LayerAct { size_t a1, r1, qkv, rqk, o, lse, a2, r2, h, g; };
+struct LayerAct { size_t a1, r1, qkv, rqk, o, lse, a2, r2, g; };
 
 }  // namespace
 
@@ -185,7 +186,6 @@ void plan(nc_ctx* c) {
     x.lse = a.take(N * H * 4);
     x.a2 = a.take(N * d * es);
     x.r2 = a.take(N * 4);
-    x.h = a.take(N * F * es);
     x.g = a.take(N * F * es);
   }
   c->xf = a.take(N * d * es);
@@ -473,8 +473,8 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
     NC_GEMM(gemm(ctx, aa + la.o, d, kKCont, wptr(ctx, wb + 3ULL * d * d), d, kKCont, x, d, N, d,
                 d, kEpiAccF32), "out proj");
     NC_TRY(nc_rmsnorm_fwd(dt, x, aa + la.a2, A<float>(ctx, la.r2), N, d, eps, st), "norm2");
-    NC_GEMM(gemm(ctx, aa + la.a2, d, kKCont, wptr(ctx, wb + 4ULL * d * d), d, kKCont, aa + la.h,
-                F, N, F, d, kEpiRelu2, nullptr, aa + la.g), "mlp up");
+    NC_GEMM(gemm(ctx, aa + la.a2, d, kKCont, wptr(ctx, wb + 4ULL * d * d), d, kKCont, aa + la.g,
+                F, N, F, d, kEpiRelu2), "mlp up");
     NC_GEMM(gemm(ctx, aa + la.g, F, kKCont, wptr(ctx, wb + 4ULL * d * d + (size_t)F * d), F,
                 kKCont, x, d, N, d, F, kEpiAccF32), "mlp down");
   }
@@ -508,7 +508,7 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
     char* dqkv = aa + ctx->dqkv;
     // MLP
     NC_GEMM(gemm(ctx, dxT, d, kKCont, wptr(ctx, w2), F, kMNCont, aa + ctx->dh, F, N, F, d,
-                kEpiRelu2Bwd, aa + la.h), "dh");
+                kEpiRelu2Bwd, aa + la.g), "dh");
     NC_GEMM(gemm(ctx, dxT, d, kMNCont, aa + la.g, F, kMNCont, G + w2, F, d, F, N, kEpiAccF32,
                 nullptr, nullptr, ctx->splits_2), "dW2");
     NC_GEMM(gemm(ctx, aa + ctx->dh, F, kMNCont, aa + la.a2, d, kMNCont, G + w1, d, F, d, N,
@@ -758,7 +758,7 @@ nc_status nc_op_gemm(int32_t dtype, const void* A_, int64_t lda, int32_t al, con
   if ((dtype != NC_FP32 && dtype != NC_BF16) || al < 0 || al > 1 || bl < 0 || bl > 1 ||
       epi < 0 || epi > kEpiDual)
     return NC_ERR_INVALID_ARG;
-  if (((epi == kEpiRelu2 || epi == kEpiDual) && !aux_out) ||
+  if ((epi == kEpiDual && !aux_out) ||
       ((epi == kEpiRelu2Bwd || epi == kEpiPoly) && !aux_in))
     return NC_ERR_INVALID_ARG;
   if (dtype == NC_BF16) {

@@ -20,9 +20,11 @@ enum {
   NC_EPI_STORE = 0,       /* C = acc, activation dtype */
   NC_EPI_STORE_F32 = 1,   /* C = acc, fp32 */
   NC_EPI_ACC_F32 = 2,     /* C += acc, fp32 (residual add, gradient accumulation) */
-  NC_EPI_RELU2 = 3,       /* C = acc; aux_out = max(acc, 0)^2 (ReLU^2 MLP, apidog.com
+  NC_EPI_RELU2 = 3,       /* C = max(acc, 0)^2 (ReLU^2 MLP, apidog.com
                              "1. Model GPT (nanochat/gpt.py)") */
-  NC_EPI_RELU2_BWD = 4,   /* C = 2 max(aux_in, 0) * acc (derivative of ReLU^2) */
+  NC_EPI_RELU2_BWD = 4,   /* C = 2 sqrt(max(aux_in, 0)) * acc with aux_in = g = max(h, 0)^2:
+                             the derivative of ReLU^2, 2 max(h, 0) dg, from the stored
+                             activation (sqrt(g) = max(h, 0)), so h itself is never kept */
   NC_EPI_POLY = 5,        /* C = p0 * aux_in + p1 * acc (Newton-Schulz steps
                              B = b A + c A A and X = a X + B X, apidog.com
                              "2. Pengoptimal Muon (nanochat/optim.py)") */
