@@ -71,7 +71,7 @@ struct nc_ctx {
   // iterate X (two, ping-pong), A = X X^T, B = b A + c A A, and a copy of each in the
   // activation type for the matrix cores.
   struct NsBufs { size_t x32[2], xh[2], a32, ah, b32, bh; } ns[2];
-  int splits_qkv, splits_o, splits_1, splits_2, splits_head;
+  int splits_qkv, splits_o, splits_1, splits_2, splits_head, splits_dxf;
   char* pa = nullptr;
   char* aa = nullptr;
   hipStream_t st = nullptr;
@@ -208,12 +208,14 @@ void plan(nc_ctx* c) {
   c->splits_1 = sp(F, d, (int)N);
   c->splits_2 = sp(d, F, (int)N);
   c->splits_head = sp(V, d, c->chunk);
+  c->splits_dxf = sp(c->chunk, d, V);   // few output tiles, K = vocabulary
   size_t ws = 0;
   ws = std::max(ws, nc_gemm_workspace_bytes(3 * d, d, c->splits_qkv));
   ws = std::max(ws, nc_gemm_workspace_bytes(d, d, c->splits_o));
   ws = std::max(ws, nc_gemm_workspace_bytes(F, d, c->splits_1));
   ws = std::max(ws, nc_gemm_workspace_bytes(d, F, c->splits_2));
   ws = std::max(ws, nc_gemm_workspace_bytes(V, d, c->splits_head));
+  ws = std::max(ws, nc_gemm_workspace_bytes(c->chunk, d, c->splits_dxf));
   c->ws_bytes = ws;
   c->ws = a.take(std::max<size_t>(ws, 256));
   c->emb = a.take(nc_embed_bwd_scratch_bytes((int)N, V, d));
@@ -491,7 +493,7 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
     NC_TRY(nc_cross_entropy(dt, A<float>(ctx, ctx->z), tgt + c0, aa + ctx->dz,
                             A<float>(ctx, ctx->loss_rows) + c0, nc, V, ce_scale, st), "ce");
     NC_GEMM(gemm(ctx, aa + ctx->dz, V, kKCont, wptr_head(ctx), d, kMNCont, da + (size_t)c0 * d, d,
-                nc, d, V, kEpiStoreF32), "dxf");
+                nc, d, V, kEpiStoreF32, nullptr, nullptr, ctx->splits_dxf), "dxf");
     NC_GEMM(gemm(ctx, aa + ctx->dz, V, kMNCont, xfc, d, kMNCont, G + wh, d, V, d, nc, kEpiAccF32,
                 nullptr, nullptr, ctx->splits_head), "dWh");
   }
