@@ -11,8 +11,8 @@ from dataclasses import replace
 
 import oracle
 from gpt_pretraining_step_gemms_amd import nc, synthetic
-from gpt_pretraining_step_gemms_amd.configs import (TINY, D12, D20, ModelConfig, OptimConfig,
-                                                    with_batch)
+from gpt_pretraining_step_gemms_amd.configs import (TINY, D12, D20, CONFIGS, ModelConfig,
+                                                    OptimConfig, with_batch)
 from parity import cosine, max_rel
 
 pytestmark = pytest.mark.gpu
@@ -85,6 +85,13 @@ def test_small_bf16_full_step():
 
 def test_d12_shape_one_row():
     check_step(with_batch(D12, micro_batch=1), B=1, seed=7)
+
+
+@pytest.mark.parametrize("name,seed", [("d20", 11), ("d24", 12), ("d26", 13)])
+def test_large_shape_one_row(name, seed):
+    """The d20, d24 and d26 model shapes (one 2048-token row against the fp64
+    oracle: loss, every gradient, every Muon/AdamW update)."""
+    check_step(with_batch(CONFIGS[name], micro_batch=1), B=1, seed=seed)
 
 
 @pytest.mark.parametrize("cfg", [TINY, SMALL_BF16])
