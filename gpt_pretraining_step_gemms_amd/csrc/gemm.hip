@@ -499,33 +499,41 @@ NC_DEV void dma16(const void* g, const bf16* lds) {
 }
 
 // One operand tile of ROWS x 32 into LDS; this wave issues NI 1-KB loads.
+// Load number i (0 <= i < NI) of this wave's NI 1-KB loads of a ROWS x PK
+// operand tile into LDS.
+template <int ROWS, int LAYOUT, int NI, int PK>
+NC_DEV void issue_one(const bf16* __restrict__ base, int64_t ld, int row0, int rows_lim, int k0,
+                      bf16* tile, int wave, int lane, int i) {
+  const int blk = wave * NI + i;                 // 1-KB block of the tile
+  const bf16* g;
+  if constexpr (LAYOUT == kKCont && PK == 32) {   // 16 rows of 64 B per block
+    const int r = blk * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    const int row = min(row0 + r, rows_lim - 1);
+    g = base + (int64_t)row * ld + k0 + c * 8;
+  } else if constexpr (LAYOUT == kKCont) {        // PK 64: 8 rows of 128 B per block
+    const int r = blk * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int row = min(row0 + r, rows_lim - 1);
+    g = base + (int64_t)row * ld + k0 + c * 8;
+  } else {                                       // 1 KB = 1024 / (2 ROWS) k-rows
+    constexpr int CH = ROWS / 8;
+    const int flat = blk * 64 + lane;
+    const int kr = flat / CH;
+    const int c = (flat % CH) ^ (4 * (kr & 3));
+    const int col = min(row0 + c * 8, rows_lim - 8);
+    g = base + (int64_t)(k0 + kr) * ld + col;
+  }
+  dma16(g, tile + blk * 512);
+}
+
+// This wave's NI 1-KB loads of a ROWS x PK operand tile.
 template <int ROWS, int LAYOUT, int NI, int PK>
 NC_DEV void issue_tile(const bf16* __restrict__ base, int64_t ld, int row0, int rows_lim, int k0,
                        bf16* tile, int wave, int lane) {
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int blk = wave * NI + i;               // 1-KB block of the tile
-    const bf16* g;
-    if constexpr (LAYOUT == kKCont && PK == 32) {   // 16 rows of 64 B per block
-      const int r = blk * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ ((r >> 2) & 3);
-      const int row = min(row0 + r, rows_lim - 1);
-      g = base + (int64_t)row * ld + k0 + c * 8;
-    } else if constexpr (LAYOUT == kKCont) {        // PK 64: 8 rows of 128 B per block
-      const int r = blk * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ ((r >> 1) & 7);
-      const int row = min(row0 + r, rows_lim - 1);
-      g = base + (int64_t)row * ld + k0 + c * 8;
-    } else {                                     // 1 KB = 1024 / (2 ROWS) k-rows
-      constexpr int CH = ROWS / 8;
-      const int flat = blk * 64 + lane;
-      const int kr = flat / CH;
-      const int c = (flat % CH) ^ (4 * (kr & 3));
-      const int col = min(row0 + c * 8, rows_lim - 8);
-      g = base + (int64_t)(k0 + kr) * ld + col;
-    }
-    dma16(g, tile + blk * 512);
-  }
+  for (int i = 0; i < NI; ++i)
+    issue_one<ROWS, LAYOUT, NI, PK>(base, ld, row0, rows_lim, k0, tile, wave, lane, i);
 }
 
 // MFMA fragment (8 k of output row o0 + lane%32, k-substep s) from a tile
@@ -619,22 +627,46 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
     // issue overwrites).  A fenced __syncthreads would also drain the younger
     // prefetches.
     asm volatile("s_barrier" ::: "memory");
-    if (i + STAGES - 1 < nk)
-      issue(kt0 + i + STAGES - 1, sbuf.template operator()<(S + STAGES - 1) % STAGES>());
+    // The loads of tile i + STAGES - 1 are spread between this step's MFMAs
+    // (one after every MPL of them, pinned with scheduling barriers): a wave
+    // issues in order, so loads issued back to back would hold back the
+    // fragment reads and MFMAs behind them, while an MFMA in the matrix pipe
+    // covers the issue of the load after it.
+    const bool more = i + STAGES - 1 < nk;
+    const int ktn = kt0 + i + STAGES - 1;
+    bf16* nxt = sbuf.template operator()<(S + STAGES - 1) % STAGES>();
     const bf16* as = sbuf.template operator()<S>();
     const bf16* bs = as + TILE_A;
+    // With two stages the next tile is waited for at the start of the next
+    // step, so its loads go early (one per MFMA of the first substep); with
+    // more stages they are spread over the whole step.
+    constexpr int NSUB = PK / 16, NM = TM * TN;
+    constexpr int SPAN = STAGES == 2 ? NM : NSUB * NM;   // MFMAs the loads are spread over
+    constexpr int MPL = SPAN / LOADS;                    // MFMAs per load
+    static_assert(SPAN % LOADS == 0 && MPL >= 1, "loads must divide the MFMAs evenly");
 #pragma unroll
-    for (int s = 0; s < PK / 16; ++s) {
+    for (int s = 0; s < NSUB; ++s) {
       bf16x8 fa[TM], fb[TN];
 #pragma unroll
       for (int ii = 0; ii < TM; ++ii) fa[ii] = frag<BM, AL, PK>(as, wm * WTM + ii * 32, s, lane);
 #pragma unroll
       for (int j = 0; j < TN; ++j) fb[j] = frag<BN, BL, PK>(bs, wn * WTN + j * 32, s, lane);
 #pragma unroll
-      for (int ii = 0; ii < TM; ++ii)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[ii][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ii], fb[j], acc[ii][j], 0, 0, 0);
+      for (int t = 0; t < NM; ++t) {
+        const int ii = t / TN, j = t % TN;
+        acc[ii][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ii], fb[j], acc[ii][j], 0, 0, 0);
+        const int u = s * NM + t;                      // MFMA index within the step
+        if (u < SPAN && u % MPL == 0 && more) {
+          const int l = u / MPL;                       // load index
+          __builtin_amdgcn_sched_barrier(0);
+          if (l < LOADS_A)
+            issue_one<BM, AL, LOADS_A, PK>(A, p.lda, m0, p.M, ktn * PK, nxt, wave, lane, l);
+          else
+            issue_one<BN, BL, LOADS_B, PK>(B, p.ldb, n0, p.N, ktn * PK, nxt + TILE_A, wave, lane,
+                                           l - LOADS_A);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
     }
   };
   if (nk > 0) issue(kt0, st0);
