@@ -644,17 +644,40 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
     constexpr int SPAN = STAGES == 2 ? NM : NSUB * NM;   // MFMAs the loads are spread over
     constexpr int MPL = SPAN / LOADS;                    // MFMAs per load
     static_assert(SPAN % LOADS == 0 && MPL >= 1, "loads must divide the MFMAs evenly");
+    // Fragments of substep s + 1 are read one at a time between the MFMAs of
+    // substep s (two register sets), so only the first substep after the
+    // barrier waits for LDS.  Measured faster for every layout but A
+    // K-contiguous with B MN-contiguous, which reads each substep's
+    // fragments at its start.
+    constexpr bool PREF = !(AL == kKCont && BL == kMNCont);
+    constexpr int NR = TM + TN;                        // fragment reads per substep
+    static_assert(NR <= NM, "one read per MFMA slot");
+    bf16x8 fr[2][NR];
+    auto read_one = [&](int s, int r, bf16x8& dst) {
+      if (r < TM) dst = frag<BM, AL, PK>(as, wm * WTM + r * 32, s, lane);
+      else dst = frag<BN, BL, PK>(bs, wn * WTN + (r - TM) * 32, s, lane);
+    };
+    if constexpr (PREF) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) read_one(0, r, fr[0][r]);
+    }
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
-      bf16x8 fa[TM], fb[TN];
+      bf16x8 (&cur)[NR] = fr[PREF ? s & 1 : 0];
+      bf16x8 (&nxf)[NR] = fr[(s + 1) & 1];
+      if constexpr (!PREF) {
 #pragma unroll
-      for (int ii = 0; ii < TM; ++ii) fa[ii] = frag<BM, AL, PK>(as, wm * WTM + ii * 32, s, lane);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) fb[j] = frag<BN, BL, PK>(bs, wn * WTN + j * 32, s, lane);
+        for (int r = 0; r < NR; ++r) read_one(s, r, cur[r]);
+      }
 #pragma unroll
       for (int t = 0; t < NM; ++t) {
         const int ii = t / TN, j = t % TN;
-        acc[ii][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ii], fb[j], acc[ii][j], 0, 0, 0);
+        acc[ii][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[ii], cur[TM + j], acc[ii][j], 0, 0, 0);
+        if constexpr (PREF) __builtin_amdgcn_sched_barrier(0);
+        if (PREF && s + 1 < NSUB && t < NR) {
+          read_one(s + 1, t, nxf[t]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
         const int u = s * NM + t;                      // MFMA index within the step
         if (u < SPAN && u % MPL == 0 && more) {
           const int l = u / MPL;                       // load index
