@@ -642,8 +642,8 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
     // more stages they are spread over the whole step.
     constexpr int NSUB = PK / 16, NM = TM * TN;
     constexpr int SPAN = STAGES == 2 ? NM : NSUB * NM;   // MFMAs the loads are spread over
-    constexpr int MPL = SPAN / LOADS;                    // MFMAs per load
-    static_assert(SPAN % LOADS == 0 && MPL >= 1, "loads must divide the MFMAs evenly");
+    constexpr int MPL = SPAN / LOADS;                    // MFMAs per load (rounded down)
+    static_assert(MPL >= 1, "at most one load per MFMA");
     // Fragments of substep s + 1 are read one at a time between the MFMAs of
     // substep s (two register sets), so only the first substep after the
     // barrier waits for LDS.  Measured faster for every layout but A
@@ -679,7 +679,7 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
           __builtin_amdgcn_sched_barrier(0);
         }
         const int u = s * NM + t;                      // MFMA index within the step
-        if (u < SPAN && u % MPL == 0 && more) {
+        if (u < SPAN && u % MPL == 0 && u / MPL < LOADS && more) {
           const int l = u / MPL;                       // load index
           __builtin_amdgcn_sched_barrier(0);
           if (l < LOADS_A)
