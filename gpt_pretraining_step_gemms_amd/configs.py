@@ -85,9 +85,10 @@ TINY = ModelConfig(name="tiny", n_layer=2, d_model=128, n_head=1, head_dim=128,
 D12 = from_depth(12, micro_batch=32, accum_steps=1)
 D20 = from_depth(20, micro_batch=32, accum_steps=8)
 D24 = from_depth(24, micro_batch=16, accum_steps=16)
-# d26: 1,048,576 tokens per step; micro-batch is the largest that fits HBM
-# (chosen by the planner at run time); 64 rows x 16 steps is the default.
-D26 = from_depth(26, micro_batch=64, accum_steps=8)
+# d26: 1,048,576 tokens per step with the largest micro-batch whose arenas fit
+# one MI355X: 128 rows (about 274 GB of parameter and activation arenas)
+# x 4 accumulated micro-batches.
+D26 = from_depth(26, micro_batch=128, accum_steps=4)
 
 CONFIGS = {c.name: c for c in (TINY, D12, D20, D24, D26)}
 
