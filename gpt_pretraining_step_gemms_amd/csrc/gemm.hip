@@ -821,7 +821,7 @@ hipError_t launch_pipe(const GemmParams& p, hipStream_t st) {
 int nc_gemm_pick_splits(int M, int N, int K) {
   constexpr int kCUs = 256;
   const int64_t tiles = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
-  const int kt = ceil_div(K, BK);
+  const int kt = ceil_div(K, 32);                     // 32-deep steps (the 1.1 us unit)
   double best = 0.0;
   int best_s = 1;
   for (int s = 1; s <= 64 && (s == 1 || s <= kt / 8); ++s) {
