@@ -448,25 +448,29 @@ hipError_t launch_bf16_cfg(const GemmParams& p, hipStream_t st) {
 }
 
 // ======================================== direct-to-LDS pipelined MFMA kernel
-// Operand tiles travel global -> LDS with global_load_lds (each lane moves 16
-// bytes; a wave's 64 lanes fill 1 KB of LDS contiguously), through a 4-stage
-// ring of 256x32 + 256x32 bf16 tiles, with no staging registers.  LDS keeps
-// each operand in its global layout:
-//   K-contiguous  [256 rows][32 k], 16-byte chunk c of row r stored at
-//                 c ^ ((r >> 2) & 3)            -> read with ds_read_b128;
+// Operand tiles travel global -> LDS with buffer_load ... lds (each lane moves
+// 16 bytes; a wave's 64 lanes fill 1 KB of LDS contiguously), with no staging
+// registers, through a ring of k-steps: 4 stages of 256x32 + 256x32 bf16
+// tiles, or 2 stages of 256x64 + 256x64, or (both operands K-contiguous) the
+// half-stage ring of five 256x64 operand tiles.  LDS keeps each operand in its
+// global layout:
+//   K-contiguous  [256 rows][32 or 64 k], 16-byte chunk c of row r stored at
+//                 c ^ ((r >> 2) & 3) (depth 32) or c ^ ((r >> 1) & 7) (depth
+//                 64)                             -> read with ds_read_b128;
 //   MN-contiguous [32 k][256 rows], chunk c of k-row kr stored at c ^ 4(kr & 3)
 //                 -> read with ds_read_b64_tr_b16, which hands each lane of a
 //                 16-lane group one column of a 4 x 16 block, i.e. 4 consecutive
 //                 k of one output row: the MFMA operand layout.
 // Both swizzles make the fragment reads bank-conflict free; the swizzle is
-// applied by choosing which global chunk each lane fetches.  Needs K % 32 == 0
-// (rows beyond M or N are clamped to valid memory and discarded).
+// applied by choosing which global chunk each lane fetches.  Needs K % 32 == 0;
+// rows beyond M or N lie past the operand's buffer range, read as zeros and
+// only feed outputs that are discarded.
 // Each wave owns a 128 x 64 output tile (4 x 2 MFMA tiles): WM x WN waves
-// make a (128 WM) x (64 WN) block tile; the launcher uses 2 x 4 waves and 4
-// stages (256 x 256 tiles, 128 KB of LDS, one block per CU).
-template <int WM_, int WN_, int ST_, int PK_ = 32>
+// make a (128 WM) x (64 WN) block tile; the launcher uses 2 x 4 waves
+// (256 x 256 tiles, 128 or 160 KB of LDS, one block per CU).
+template <int WM_, int WN_, int ST_, int PK_ = 32, int WNT_ = 64>
 struct Pipe {
-  static constexpr int BM = 128 * WM_, BN = 64 * WN_, PK = PK_, STAGES = ST_;
+  static constexpr int BM = 128 * WM_, BN = WNT_ * WN_, PK = PK_, STAGES = ST_;
   static constexpr int WM = WM_, WN = WN_;
   static constexpr int kBlocksPerCU = (BM + BN) * PK * 2 * ST_ <= 80 * 1024 ? 2 : 1;
   static constexpr int NT = WM * WN * 64;
@@ -475,65 +479,106 @@ struct Pipe {
   static constexpr int LOADS_A = TILE_A * 2 / 1024 / (NT / 64);
   static constexpr int LOADS_B = TILE_B * 2 / 1024 / (NT / 64);
   static constexpr int LOADS = LOADS_A + LOADS_B;   // global_load_lds per wave per stage
+  // STAGES == 5 is the half-stage ring: five buffers, each holding one
+  // operand tile (A or B) of one k-step, so one and a half tiles load ahead.
+  static constexpr bool HALF = ST_ == 5;
+  static constexpr int BUF = HALF ? TILE_A : STAGE;  // bf16 elements per LDS buffer
+  static_assert(!HALF || TILE_A == TILE_B, "the half-stage ring needs square block tiles");
 };
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 #define NC_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-// global_load_lds_dwordx4: lane l's 16 bytes at g land at LDS address
-// lds + 16 l (lds is wave-uniform, passed in M0).  Issued as inline assembly:
-// the instruction has no register result, and the kernel tracks its
-// completion itself (s_waitcnt vmcnt + s_barrier), which keeps the compiler
-// from draining every load in flight before each LDS read.  M0 is restored.
-NC_DEV void dma16(const void* g, const bf16* lds) {
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// An operand for the direct-to-LDS loads: a raw buffer resource over the
+// operand's bytes (gfx9 layout: stride 0, dword 3 = 0x00020000), so that a load
+// past the end reads zeros instead of touching memory, plus each lane's byte
+// offset inside a 1-KB block for the two block parities (the LDS swizzle
+// alternates between even and odd blocks).
+struct Opnd {
+  i32x4 rsrc;
+  unsigned lane_off[2];
+  unsigned ld2;                                  // leading dimension in bytes
+};
+
+// Byte extent of a bf16 operand slice: rows of ld elements, the last one
+// holding `last` elements.
+__host__ __device__ inline int64_t operand_extent(int64_t rows, int64_t ld, int64_t last) {
+  return rows <= 0 ? 0 : ((rows - 1) * ld + last) * 2;
+}
+
+// ROWS x PK tile layouts (see the kernel comment): K-contiguous blocks cover
+// 16 (PK 32) or 8 (PK 64) rows of one k-step; MN-contiguous blocks cover 2
+// k-rows of 256 columns.
+template <int ROWS, int LAYOUT, int PK>
+NC_DEV Opnd make_opnd(const bf16* base, int64_t ld, int64_t bytes, int lane) {
+  static_assert(LAYOUT == kKCont || ROWS == 256, "MN-contiguous tiles are 256 wide");
+  Opnd o;
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  o.rsrc[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
+  o.rsrc[1] = __builtin_amdgcn_readfirstlane((int)((unsigned)(a >> 32) & 0xffffu));
+  o.rsrc[2] = __builtin_amdgcn_readfirstlane((int)(unsigned)bytes);
+  o.rsrc[3] = 0x00020000;
+  o.ld2 = (unsigned)ld * 2u;
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    unsigned r, c;
+    if constexpr (LAYOUT == kKCont && PK == 32) {  // row r = 16 blk + lane / 4
+      r = lane >> 2;
+      c = (lane & 3) ^ ((lane >> 4) & 3);          // (r >> 2) & 3 of the tile row
+    } else if constexpr (LAYOUT == kKCont) {       // row r = 8 blk + lane / 8
+      r = lane >> 3;
+      c = (lane & 7) ^ (4 * par + (r >> 1));       // (r >> 1) & 7 of the tile row
+    } else {                                       // k-row 2 blk + lane / 32
+      r = lane >> 5;
+      c = (lane & 31) ^ (4 * ((2 * par + r) & 3));
+    }
+    o.lane_off[par] = r * o.ld2 + c * 16u;
+  }
+  return o;
+}
+
+// buffer_load_dwordx4 ... lds: lane l's 16 bytes at byte offset voff of the
+// operand land at LDS address lds + 16 l (lds is wave-uniform, passed in M0).
+// Issued as inline assembly: the instruction has no register result, and the
+// kernel tracks its completion itself (s_waitcnt vmcnt + s_barrier), which
+// keeps the compiler from draining every load in flight before each LDS read.
+// M0 is restored.
+NC_DEV void dma16(const i32x4& rsrc, unsigned voff, const bf16* lds) {
   const unsigned a = (unsigned)(size_t)NC_LDS(const void, lds);
   unsigned saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(g), "s"(__builtin_amdgcn_readfirstlane(a))
+      : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(a))
       : "memory");
 }
 
-// One operand tile of ROWS x 32 into LDS; this wave issues NI 1-KB loads.
-// Load number i (0 <= i < NI) of this wave's NI 1-KB loads of a ROWS x PK
-// operand tile into LDS.
+// Load number i (0 <= i < NI) of this wave's NI 1-KB loads of the ROWS x PK
+// operand tile at (row0, k0).  The block's wave-uniform offset is computed in
+// scalar registers; rows (or columns) past the operand read as zeros and only
+// feed outputs that are discarded.
 template <int ROWS, int LAYOUT, int NI, int PK>
-NC_DEV void issue_one(const bf16* __restrict__ base, int64_t ld, int row0, int rows_lim, int k0,
-                      bf16* tile, int wave, int lane, int i) {
+NC_DEV void issue_one(const Opnd& o, int row0, int k0, bf16* tile, int wave, int i) {
   const int blk = wave * NI + i;                 // 1-KB block of the tile
-  const bf16* g;
-  if constexpr (LAYOUT == kKCont && PK == 32) {   // 16 rows of 64 B per block
-    const int r = blk * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ ((r >> 2) & 3);
-    const int row = min(row0 + r, rows_lim - 1);
-    g = base + (int64_t)row * ld + k0 + c * 8;
-  } else if constexpr (LAYOUT == kKCont) {        // PK 64: 8 rows of 128 B per block
-    const int r = blk * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
-    const int row = min(row0 + r, rows_lim - 1);
-    g = base + (int64_t)row * ld + k0 + c * 8;
-  } else {                                       // 1 KB = 1024 / (2 ROWS) k-rows
-    constexpr int CH = ROWS / 8;
-    const int flat = blk * 64 + lane;
-    const int kr = flat / CH;
-    const int c = (flat % CH) ^ (4 * (kr & 3));
-    const int col = min(row0 + c * 8, rows_lim - 8);
-    g = base + (int64_t)(k0 + kr) * ld + col;
-  }
-  dma16(g, tile + blk * 512);
+  unsigned u;
+  if constexpr (LAYOUT == kKCont)
+    u = (unsigned)(row0 + blk * (PK == 32 ? 16 : 8)) * o.ld2 + (unsigned)k0 * 2u;
+  else
+    u = (unsigned)(k0 + blk * 2) * o.ld2 + (unsigned)row0 * 2u;
+  u = __builtin_amdgcn_readfirstlane(u);
+  dma16(o.rsrc, o.lane_off[blk & 1] + u, tile + blk * 512);
 }
 
 // This wave's NI 1-KB loads of a ROWS x PK operand tile.
 template <int ROWS, int LAYOUT, int NI, int PK>
-NC_DEV void issue_tile(const bf16* __restrict__ base, int64_t ld, int row0, int rows_lim, int k0,
-                       bf16* tile, int wave, int lane) {
+NC_DEV void issue_tile(const Opnd& o, int row0, int k0, bf16* tile, int wave) {
 #pragma unroll
-  for (int i = 0; i < NI; ++i)
-    issue_one<ROWS, LAYOUT, NI, PK>(base, ld, row0, rows_lim, k0, tile, wave, lane, i);
+  for (int i = 0; i < NI; ++i) issue_one<ROWS, LAYOUT, NI, PK>(o, row0, k0, tile, wave, i);
 }
 
 // MFMA fragment (8 k of output row o0 + lane%32, k-substep s) from a tile
@@ -564,18 +609,21 @@ NC_DEV void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int AL, int BL, int WM_, int WN_, int ST_, int PK_>
-__global__ __launch_bounds__(WM_ * WN_ * 64, (Pipe<WM_, WN_, ST_, PK_>::kBlocksPerCU))
+template <int AL, int BL, int WM_, int WN_, int ST_, int PK_, int WNT_>
+__global__ __launch_bounds__(WM_ * WN_ * 64, (Pipe<WM_, WN_, ST_, PK_, WNT_>::kBlocksPerCU))
 void gemm_bf16_pipe_kernel(GemmParams p) {
-  using C = Pipe<WM_, WN_, ST_, PK_>;
+  using C = Pipe<WM_, WN_, ST_, PK_, WNT_>;
   constexpr int BM = C::BM, BN = C::BN, PK = C::PK, STAGES = C::STAGES, WN = C::WN;
   constexpr int WTM = C::WTM, WTN = C::WTN, TM = C::TM, TN = C::TN;
   constexpr int TILE_A = C::TILE_A, STAGE = C::STAGE;
   constexpr int LOADS_A = C::LOADS_A, LOADS_B = C::LOADS_B, LOADS = C::LOADS;
-  __shared__ __attribute__((aligned(1024))) bf16 st0[STAGE];
-  __shared__ __attribute__((aligned(1024))) bf16 st1[STAGE];
-  __shared__ __attribute__((aligned(1024))) bf16 st2[STAGE];
-  __shared__ __attribute__((aligned(1024))) bf16 st3[STAGE];
+  constexpr int BUF = C::BUF;
+  constexpr bool HALF = C::HALF;
+  __shared__ __attribute__((aligned(1024))) bf16 st0[BUF];
+  __shared__ __attribute__((aligned(1024))) bf16 st1[BUF];
+  __shared__ __attribute__((aligned(1024))) bf16 st2[BUF];
+  __shared__ __attribute__((aligned(1024))) bf16 st3[BUF];
+  __shared__ __attribute__((aligned(1024))) bf16 st4[HALF ? BUF : 1];
 
   const int tiles_m = ceil_div(p.M, BM), tiles_n = ceil_div(p.N, BN);
   int tm, tn;
@@ -594,6 +642,12 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int half = lane >> 5, l32 = lane & 31;
+  const Opnd oa = make_opnd<BM, AL, PK>(
+      A, p.lda, AL == kKCont ? operand_extent(p.M, p.lda, p.K) : operand_extent(p.K, p.lda, p.M),
+      lane);
+  const Opnd ob = make_opnd<BN, BL, PK>(
+      B, p.ldb, BL == kKCont ? operand_extent(p.N, p.ldb, p.K) : operand_extent(p.K, p.ldb, p.N),
+      lane);
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -610,18 +664,26 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
     if constexpr (S == 0) return st0;
     else if constexpr (S == 1) return st1;
     else if constexpr (S == 2) return st2;
-    else return st3;
+    else if constexpr (S == 3) return st3;
+    else return st4;
   };
   auto issue = [&](int kt, bf16* st) {
-    issue_tile<BM, AL, LOADS_A, PK>(A, p.lda, m0, p.M, kt * PK, st, wave, lane);
-    issue_tile<BN, BL, LOADS_B, PK>(B, p.ldb, n0, p.N, kt * PK, st + TILE_A, wave, lane);
+    issue_tile<BM, AL, LOADS_A, PK>(oa, m0, kt * PK, st, wave);
+    issue_tile<BN, BL, LOADS_B, PK>(ob, n0, kt * PK, st + TILE_A, wave);
   };
   auto step = [&]<int S>(int i) {
-    // tile i has landed once at most the loads of the (up to two) younger tiles remain
-    const int younger = min(nk - 1 - i, STAGES - 2);
-    if (younger >= 2) wait_vmcnt<2 * LOADS>();
-    else if (younger == 1) wait_vmcnt<LOADS>();
-    else wait_vmcnt<0>();
+    if constexpr (HALF) {
+      // loads go out as B of tile i + 1, then A of tile i + 2: tile i has
+      // landed once at most the A loads of tile i + 1 remain
+      if (i + 1 < nk) wait_vmcnt<LOADS_A>();
+      else wait_vmcnt<0>();
+    } else {
+      // tile i has landed once at most the loads of the (up to two) younger tiles remain
+      const int younger = min(nk - 1 - i, STAGES - 2);
+      if (younger >= 2) wait_vmcnt<2 * LOADS>();
+      else if (younger == 1) wait_vmcnt<LOADS>();
+      else wait_vmcnt<0>();
+    }
     // Plain barrier: every wave has waited for its own loads of tile i above,
     // and has consumed its fragment reads of tile i-1 (whose stage the next
     // issue overwrites).  A fenced __syncthreads would also drain the younger
@@ -632,16 +694,22 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
     // issues in order, so loads issued back to back would hold back the
     // fragment reads and MFMAs behind them, while an MFMA in the matrix pipe
     // covers the issue of the load after it.
-    const bool more = i + STAGES - 1 < nk;
-    const int ktn = kt0 + i + STAGES - 1;
-    bf16* nxt = sbuf.template operator()<(S + STAGES - 1) % STAGES>();
-    const bf16* as = sbuf.template operator()<S>();
-    const bf16* bs = as + TILE_A;
+    // half ring: A of tile t in buffer 2t mod 5, B in 2t + 1 mod 5; this step
+    // loads B of tile i + 1 into the buffer A of tile i - 1 held and A of
+    // tile i + 2 into that of B of tile i - 1, both read before the barrier
+    const bool more = HALF ? i + 1 < nk : i + STAGES - 1 < nk;
+    const bool more_a2 = i + 2 < nk;
+    const int ktn = kt0 + i + (HALF ? 1 : STAGES - 1);
+    bf16* nxt = HALF ? nullptr : sbuf.template operator()<(S + STAGES - 1) % STAGES>();
+    bf16* nxt_b = HALF ? sbuf.template operator()<(2 * S + 3) % 5>() : nxt + TILE_A;
+    bf16* nxt_a2 = HALF ? sbuf.template operator()<(2 * S + 4) % 5>() : nullptr;
+    const bf16* as = HALF ? sbuf.template operator()<(2 * S) % 5>() : sbuf.template operator()<S>();
+    const bf16* bs = HALF ? sbuf.template operator()<(2 * S + 1) % 5>() : as + TILE_A;
     // With two stages the next tile is waited for at the start of the next
     // step, so its loads go early (one per MFMA of the first substep); with
     // more stages they are spread over the whole step.
     constexpr int NSUB = PK / 16, NM = TM * TN;
-    constexpr int SPAN = STAGES == 2 ? NM : NSUB * NM;   // MFMAs the loads are spread over
+    constexpr int SPAN = (STAGES == 2 || HALF) ? NM : NSUB * NM;   // MFMAs the loads are spread over
     constexpr int MPL = SPAN / LOADS;                    // MFMAs per load (rounded down)
     static_assert(MPL >= 1, "at most one load per MFMA");
     // Fragments of substep s + 1 are read one at a time between the MFMAs of
@@ -679,31 +747,50 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
           __builtin_amdgcn_sched_barrier(0);
         }
         const int u = s * NM + t;                      // MFMA index within the step
-        if (u < SPAN && u % MPL == 0 && u / MPL < LOADS && more) {
+        if constexpr (HALF) {
+          const int l = u / MPL;
+          if (u < SPAN && u % MPL == 0 && l < LOADS && (l < LOADS_B ? more : more_a2)) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (l < LOADS_B)
+              issue_one<BN, BL, LOADS_B, PK>(ob, n0, ktn * PK, nxt_b, wave, l);
+            else
+              issue_one<BM, AL, LOADS_A, PK>(oa, m0, (ktn + 1) * PK, nxt_a2, wave, l - LOADS_B);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else if (u < SPAN && u % MPL == 0 && u / MPL < LOADS && more) {
           const int l = u / MPL;                       // load index
           __builtin_amdgcn_sched_barrier(0);
           if (l < LOADS_A)
-            issue_one<BM, AL, LOADS_A, PK>(A, p.lda, m0, p.M, ktn * PK, nxt, wave, lane, l);
+            issue_one<BM, AL, LOADS_A, PK>(oa, m0, ktn * PK, nxt, wave, l);
           else
-            issue_one<BN, BL, LOADS_B, PK>(B, p.ldb, n0, p.N, ktn * PK, nxt + TILE_A, wave, lane,
-                                           l - LOADS_A);
+            issue_one<BN, BL, LOADS_B, PK>(ob, n0, ktn * PK, nxt_b, wave, l - LOADS_A);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
   };
-  if (nk > 0) issue(kt0, st0);
-  if constexpr (STAGES >= 3)
-    if (nk > 1) issue(kt0 + 1, st1);
-  if constexpr (STAGES == 4)
-    if (nk > 2) issue(kt0 + 2, st2);
+  if constexpr (HALF) {
+    if (nk > 0) {
+      issue_tile<BM, AL, LOADS_A, PK>(oa, m0, kt0 * PK, st0, wave);
+      issue_tile<BN, BL, LOADS_B, PK>(ob, n0, kt0 * PK, st1, wave);
+    }
+    if (nk > 1) issue_tile<BM, AL, LOADS_A, PK>(oa, m0, (kt0 + 1) * PK, st2, wave);
+  } else {
+    if (nk > 0) issue(kt0, st0);
+    if constexpr (STAGES >= 3)
+      if (nk > 1) issue(kt0 + 1, st1);
+    if constexpr (STAGES == 4)
+      if (nk > 2) issue(kt0 + 2, st2);
+  }
   for (int i = 0; i < nk; i += STAGES) {
     step.template operator()<0>(i);
     if (i + 1 < nk) step.template operator()<1>(i + 1);
     if constexpr (STAGES >= 3)
       if (i + 2 < nk) step.template operator()<2>(i + 2);
-    if constexpr (STAGES == 4)
+    if constexpr (STAGES >= 4)
       if (i + 3 < nk) step.template operator()<3>(i + 3);
+    if constexpr (STAGES == 5)
+      if (i + 4 < nk) step.template operator()<4>(i + 4);
   }
 
   // ---- epilogue, staged through the (now idle) stage buffers: each wave
@@ -711,10 +798,11 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
   // region, then every lane takes 8 consecutive columns of one row, so that
   // C, the auxiliary tensors and the split-K workspace are accessed with
   // 16-byte, row-contiguous loads and stores.
-  static_assert(WTN == 64, "the epilogue maps 8 lanes to the 64 columns of a wave tile");
+  static_assert(WTN % 64 == 0, "the epilogue maps 8 lanes to 64 columns of a wave tile");
+  constexpr int JB = WTN / 64, TJ = TN / JB;         // 64-column blocks, MFMA tiles per block
   constexpr int EP_LD = 72;                          // padded row, floats
   constexpr int EP_FLOATS = 32 * EP_LD;
-  constexpr int EP_PER = STAGE * 2 / (EP_FLOATS * 4);  // wave regions per stage buffer
+  constexpr int EP_PER = BUF * 2 / (EP_FLOATS * 4);    // wave regions per stage buffer
   constexpr int EP_BUFS = STAGES < 3 ? STAGES : 3;
   static_assert(C::NT / 64 <= EP_BUFS * EP_PER, "staging must fit in the stage buffers");
   asm volatile("s_barrier" ::: "memory");            // every wave is done with the ring
@@ -732,19 +820,20 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
   const int rsub = lane >> 3, q = lane & 7;
   auto run = [&]<int EPI>() {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+    for (int ib = 0; ib < TM * JB; ++ib) {
+      const int i = ib / JB, jb = ib % JB;
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+      for (int jj = 0; jj < TJ; ++jj)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          stg[((e >> 2) * 8 + half * 4 + (e & 3)) * EP_LD + j * 32 + l32] = acc[i][j][e];
+          stg[((e >> 2) * 8 + half * 4 + (e & 3)) * EP_LD + jj * 32 + l32] = acc[i][jb * TJ + jj][e];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int row = rsub + 8 * t;
         float v[8];
         ld8(stg + row * EP_LD + 8 * q, v);
         const int m = m0 + wm * WTM + i * 32 + row;
-        const int n = n0 + wn * WTN + 8 * q;
+        const int n = n0 + wn * WTN + jb * 64 + 8 * q;
         if (m >= p.M || n >= p.N) continue;
         if (split_out) {
           float* w = W + (int64_t)m * ld_out + n;
@@ -780,34 +869,42 @@ bool pipe_ok(const GemmParams& p) {
   if (p.batch > 1 && (p.sA % 8 || p.sB % 8)) return false;
   if (p.a_layout == kMNCont && p.M % 8) return false;
   if (p.b_layout == kMNCont && p.N % 8) return false;
+  // operand offsets are 32-bit (buffer addressing)
+  const int64_t ea = p.a_layout == kKCont ? operand_extent(p.M, p.lda, p.K)
+                                          : operand_extent(p.K, p.lda, p.M);
+  const int64_t eb = p.b_layout == kKCont ? operand_extent(p.N, p.ldb, p.K)
+                                          : operand_extent(p.K, p.ldb, p.N);
+  if (ea >= (int64_t(1) << 32) || eb >= (int64_t(1) << 32)) return false;
   return true;
 }
 
-template <int WM, int WN, int ST, int PK = 32>
+template <int WM, int WN, int ST, int PK = 32, int WNT = 64>
 hipError_t launch_pipe_cfg(const GemmParams& p, hipStream_t st) {
-  using C = Pipe<WM, WN, ST, PK>;
+  using C = Pipe<WM, WN, ST, PK, WNT>;
   const int tiles = ceil_div(p.M, C::BM) * ceil_div(p.N, C::BN);
   dim3 grid(tiles, 1, p.batch * p.splits);
   constexpr int NT = WM * WN * 64;
   switch (p.a_layout * 2 + p.b_layout) {
-    case 0: gemm_bf16_pipe_kernel<kKCont, kKCont, WM, WN, ST, PK><<<grid, NT, 0, st>>>(p); break;
-    case 1: gemm_bf16_pipe_kernel<kKCont, kMNCont, WM, WN, ST, PK><<<grid, NT, 0, st>>>(p); break;
-    case 2: gemm_bf16_pipe_kernel<kMNCont, kKCont, WM, WN, ST, PK><<<grid, NT, 0, st>>>(p); break;
-    default: gemm_bf16_pipe_kernel<kMNCont, kMNCont, WM, WN, ST, PK><<<grid, NT, 0, st>>>(p); break;
+    case 0: gemm_bf16_pipe_kernel<kKCont, kKCont, WM, WN, ST, PK, WNT><<<grid, NT, 0, st>>>(p); break;
+    case 1: gemm_bf16_pipe_kernel<kKCont, kMNCont, WM, WN, ST, PK, WNT><<<grid, NT, 0, st>>>(p); break;
+    case 2: gemm_bf16_pipe_kernel<kMNCont, kKCont, WM, WN, ST, PK, WNT><<<grid, NT, 0, st>>>(p); break;
+    default: gemm_bf16_pipe_kernel<kMNCont, kMNCont, WM, WN, ST, PK, WNT><<<grid, NT, 0, st>>>(p); break;
   }
   return hipGetLastError();
 }
 
 // 256 x 256 block tiles (8 waves of 128 x 64), one block per CU.  With both
 // operands K-contiguous (forward products, Newton-Schulz Gram and polynomial
-// steps) a k-depth of 64 per stage and 2 stages (one barrier per 64 k)
-// measured 3-7 % faster than depth 32 with 4 stages; with an MN-contiguous
-// operand (input and weight gradients) it measured slower, and those keep
-// depth 32.  256 x 128 tiles at two blocks per CU, 5 stages, fragment
-// prefetch across k-substeps and 4 waves of 128 x 128 were all slower.
+// steps) a k-depth of 64 per stage (one barrier per 64 k, whole 128-byte rows
+// per load) measured 3-7 % faster than depth 32 with 4 stages, and the
+// half-stage ring, which keeps the A loads of the tile after next in flight
+// across the barrier, another 1.5-2.5 %; with an MN-contiguous operand
+// (input and weight gradients) depth 64 measured slower, and those keep depth
+// 32 with 4 stages.  256 x 128 tiles at two blocks per CU, 5 stages of depth
+// 32 and 4 waves of 128 x 128 (which spills) were all slower.
 hipError_t launch_pipe(const GemmParams& p, hipStream_t st) {
   if (p.a_layout == kKCont && p.b_layout == kKCont && p.K % 64 == 0)
-    return launch_pipe_cfg<2, 4, 2, 64>(p, st);
+    return launch_pipe_cfg<2, 4, 5, 64>(p, st);
   return launch_pipe_cfg<2, 4, 4>(p, st);
 }
 
