@@ -17,6 +17,8 @@
 // operand layouts and epilogues.
 #include "gemm.h"
 
+#include <type_traits>
+
 namespace {
 
 constexpr int BK = 64;
@@ -465,16 +467,19 @@ hipError_t launch_bf16_cfg(const GemmParams& p, hipStream_t st) {
 // applied by choosing which global chunk each lane fetches.  Needs K % 32 == 0;
 // rows beyond M or N lie past the operand's buffer range, read as zeros and
 // only feed outputs that are discarded.
-// Each wave owns a 128 x 64 output tile (4 x 2 MFMA tiles): WM x WN waves
-// make a (128 WM) x (64 WN) block tile; the launcher uses 2 x 4 waves
-// (256 x 256 tiles, 128 or 160 KB of LDS, one block per CU).
-template <int WM_, int WN_, int ST_, int PK_ = 32, int WNT_ = 64>
+// Each wave owns a 128 x 64 output tile (4 x 2 tiles of 32 x 32 x 16 MFMAs or
+// 8 x 4 tiles of 16 x 16 x 32 MFMAs): WM x WN waves make a (128 WM) x (64 WN)
+// block tile; the launcher uses 2 x 4 waves (256 x 256 tiles, 128 or 160 KB of
+// LDS, one block per CU).
+template <int WM_, int WN_, int ST_, int PK_ = 32, int MI_ = 32>
 struct Pipe {
-  static constexpr int BM = 128 * WM_, BN = WNT_ * WN_, PK = PK_, STAGES = ST_;
+  static constexpr int BM = 128 * WM_, BN = 64 * WN_, PK = PK_, STAGES = ST_;
+  // MFMA shape: 32 (v_mfma_f32_32x32x16_bf16) or 16 (v_mfma_f32_16x16x32_bf16)
+  static constexpr int MI = MI_, KSUB = MI_ == 32 ? 16 : 32;
   static constexpr int WM = WM_, WN = WN_;
   static constexpr int kBlocksPerCU = (BM + BN) * PK * 2 * ST_ <= 80 * 1024 ? 2 : 1;
   static constexpr int NT = WM * WN * 64;
-  static constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
+  static constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / MI, TN = WTN / MI;
   static constexpr int TILE_A = BM * PK, TILE_B = BN * PK, STAGE = TILE_A + TILE_B;
   static constexpr int LOADS_A = TILE_A * 2 / 1024 / (NT / 64);
   static constexpr int LOADS_B = TILE_B * 2 / 1024 / (NT / 64);
@@ -581,18 +586,22 @@ NC_DEV void issue_tile(const Opnd& o, int row0, int k0, bf16* tile, int wave) {
   for (int i = 0; i < NI; ++i) issue_one<ROWS, LAYOUT, NI, PK>(o, row0, k0, tile, wave, i);
 }
 
-// MFMA fragment (8 k of output row o0 + lane%32, k-substep s) from a tile
-template <int ROWS, int LAYOUT, int PK>
+// MFMA operand fragment from a tile: 8 consecutive k of one output row, for
+// k-substep s.  32 x 32 x 16: row o0 + lane % 32, k 8 (lane / 32) of the
+// substep's 16; 16 x 16 x 32: row o0 + lane % 16, k 8 (lane / 16) of its 32.
+template <int ROWS, int LAYOUT, int PK, int MI>
 NC_DEV bf16x8 frag(const bf16* tile, int o0, int s, int lane) {
   if constexpr (LAYOUT == kKCont) {
-    const int r = o0 + (lane & 31);
-    const int c = s * 2 + (lane >> 5);
+    const int r = o0 + (MI == 32 ? (lane & 31) : (lane & 15));
+    const int c = MI == 32 ? s * 2 + (lane >> 5) : s * 4 + (lane >> 4);
     const int sw = PK == 32 ? (r >> 2) & 3 : (r >> 1) & 7;
     return *reinterpret_cast<const bf16x8*>(tile + r * PK + ((c ^ sw) << 3));
   } else {
+    // each 16-lane group reads a 4 (k) x 16 (rows) block twice (k and k + 4);
+    // ds_read_b64_tr_b16 hands lane t of the group row t's 4 consecutive k
     const int g = lane >> 4, t = lane & 15;
-    const int k = s * 16 + 8 * (g >> 1) + (t >> 2);
-    const int o = o0 + 16 * (g & 1) + 4 * (t & 3);
+    const int k = MI == 32 ? s * 16 + 8 * (g >> 1) + (t >> 2) : s * 32 + 8 * g + (t >> 2);
+    const int o = o0 + (MI == 32 ? 16 * (g & 1) : 0) + 4 * (t & 3);
     const int sw = 4 * (k & 3);                  // same for k and k + 4
     const bf16* p0 = tile + k * ROWS + (((o >> 3) ^ sw) << 3) + (o & 7);
     const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(NC_LDS(bf16x4_t, p0));
@@ -609,10 +618,13 @@ NC_DEV void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int AL, int BL, int WM_, int WN_, int ST_, int PK_, int WNT_>
-__global__ __launch_bounds__(WM_ * WN_ * 64, (Pipe<WM_, WN_, ST_, PK_, WNT_>::kBlocksPerCU))
+template <int AL, int BL, int WM_, int WN_, int ST_, int PK_, int MI_>
+__global__ __launch_bounds__(WM_ * WN_ * 64, (Pipe<WM_, WN_, ST_, PK_, MI_>::kBlocksPerCU))
 void gemm_bf16_pipe_kernel(GemmParams p) {
-  using C = Pipe<WM_, WN_, ST_, PK_, WNT_>;
+  using C = Pipe<WM_, WN_, ST_, PK_, MI_>;
+  constexpr int MI = C::MI;
+  using AccT = std::conditional_t<MI == 32, f32x16, f32x4>;
+  constexpr int ACC_N = MI == 32 ? 16 : 4;
   constexpr int BM = C::BM, BN = C::BN, PK = C::PK, STAGES = C::STAGES, WN = C::WN;
   constexpr int WTM = C::WTM, WTN = C::WTN, TM = C::TM, TN = C::TN;
   constexpr int TILE_A = C::TILE_A, STAGE = C::STAGE;
@@ -649,13 +661,13 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
       B, p.ldb, BL == kKCont ? operand_extent(p.N, p.ldb, p.K) : operand_extent(p.K, p.ldb, p.N),
       lane);
 
-  f32x16 acc[TM][TN];
+  AccT acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+      for (int e = 0; e < ACC_N; ++e) acc[i][j][e] = 0.f;
 
   // Each stage is its own LDS object and the loop is unrolled over the 4
   // stages, so the compiler can tell that the loads in flight (other stages)
@@ -708,7 +720,7 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
     // With two stages the next tile is waited for at the start of the next
     // step, so its loads go early (one per MFMA of the first substep); with
     // more stages they are spread over the whole step.
-    constexpr int NSUB = PK / 16, NM = TM * TN;
+    constexpr int NSUB = PK / C::KSUB, NM = TM * TN;
     constexpr int SPAN = (STAGES == 2 || HALF) ? NM : NSUB * NM;   // MFMAs the loads are spread over
     constexpr int MPL = SPAN / LOADS;                    // MFMAs per load (rounded down)
     static_assert(MPL >= 1, "at most one load per MFMA");
@@ -722,8 +734,8 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
     static_assert(NR <= NM, "one read per MFMA slot");
     bf16x8 fr[2][NR];
     auto read_one = [&](int s, int r, bf16x8& dst) {
-      if (r < TM) dst = frag<BM, AL, PK>(as, wm * WTM + r * 32, s, lane);
-      else dst = frag<BN, BL, PK>(bs, wn * WTN + (r - TM) * 32, s, lane);
+      if (r < TM) dst = frag<BM, AL, PK, MI>(as, wm * WTM + r * MI, s, lane);
+      else dst = frag<BN, BL, PK, MI>(bs, wn * WTN + (r - TM) * MI, s, lane);
     };
     if constexpr (PREF) {
 #pragma unroll
@@ -740,7 +752,10 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
 #pragma unroll
       for (int t = 0; t < NM; ++t) {
         const int ii = t / TN, j = t % TN;
-        acc[ii][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[ii], cur[TM + j], acc[ii][j], 0, 0, 0);
+        if constexpr (MI == 32)
+          acc[ii][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[ii], cur[TM + j], acc[ii][j], 0, 0, 0);
+        else
+          acc[ii][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur[ii], cur[TM + j], acc[ii][j], 0, 0, 0);
         if constexpr (PREF) __builtin_amdgcn_sched_barrier(0);
         if (PREF && s + 1 < NSUB && t < NR) {
           read_one(s + 1, t, nxf[t]);
@@ -798,9 +813,9 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
   // region, then every lane takes 8 consecutive columns of one row, so that
   // C, the auxiliary tensors and the split-K workspace are accessed with
   // 16-byte, row-contiguous loads and stores.
-  static_assert(WTN % 64 == 0, "the epilogue maps 8 lanes to 64 columns of a wave tile");
-  constexpr int JB = WTN / 64, TJ = TN / JB;         // 64-column blocks, MFMA tiles per block
-  constexpr int EP_LD = 72;                          // padded row, floats
+  static_assert(WTN == 64, "the epilogue maps 8 lanes to the 64 columns of a wave tile");
+  // padded row (floats): conflict-free staging writes for either MFMA layout
+  constexpr int EP_LD = MI == 32 ? 72 : 68;
   constexpr int EP_FLOATS = 32 * EP_LD;
   constexpr int EP_PER = BUF * 2 / (EP_FLOATS * 4);    // wave regions per stage buffer
   constexpr int EP_BUFS = STAGES < 3 ? STAGES : 3;
@@ -820,20 +835,32 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
   const int rsub = lane >> 3, q = lane & 7;
   auto run = [&]<int EPI>() {
 #pragma unroll
-    for (int ib = 0; ib < TM * JB; ++ib) {
-      const int i = ib / JB, jb = ib % JB;
+    for (int i = 0; i < WTM / 32; ++i) {              // 32-row blocks of the wave tile
+      // 32 x 32 tile: lane c + 32 h holds column c, rows 8 (e / 4) + 4 h + e % 4;
+      // 16 x 16 tile: lane c + 16 g holds column c, rows 4 g + e
+      if constexpr (MI == 32) {
 #pragma unroll
-      for (int jj = 0; jj < TJ; ++jj)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          stg[((e >> 2) * 8 + half * 4 + (e & 3)) * EP_LD + jj * 32 + l32] = acc[i][jb * TJ + jj][e];
+          for (int e = 0; e < 16; ++e)
+            stg[((e >> 2) * 8 + half * 4 + (e & 3)) * EP_LD + j * 32 + l32] = acc[i][j][e];
+      } else {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              stg[(ii * 16 + 4 * (lane >> 4) + e) * EP_LD + j * 16 + (lane & 15)] =
+                  acc[2 * i + ii][j][e];
+      }
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int row = rsub + 8 * t;
         float v[8];
         ld8(stg + row * EP_LD + 8 * q, v);
         const int m = m0 + wm * WTM + i * 32 + row;
-        const int n = n0 + wn * WTN + jb * 64 + 8 * q;
+        const int n = n0 + wn * WTN + 8 * q;
         if (m >= p.M || n >= p.N) continue;
         if (split_out) {
           float* w = W + (int64_t)m * ld_out + n;
@@ -878,34 +905,37 @@ bool pipe_ok(const GemmParams& p) {
   return true;
 }
 
-template <int WM, int WN, int ST, int PK = 32, int WNT = 64>
+template <int AL, int BL, int WM, int WN, int ST, int PK, int MI>
 hipError_t launch_pipe_cfg(const GemmParams& p, hipStream_t st) {
-  using C = Pipe<WM, WN, ST, PK, WNT>;
+  using C = Pipe<WM, WN, ST, PK, MI>;
   const int tiles = ceil_div(p.M, C::BM) * ceil_div(p.N, C::BN);
   dim3 grid(tiles, 1, p.batch * p.splits);
-  constexpr int NT = WM * WN * 64;
-  switch (p.a_layout * 2 + p.b_layout) {
-    case 0: gemm_bf16_pipe_kernel<kKCont, kKCont, WM, WN, ST, PK, WNT><<<grid, NT, 0, st>>>(p); break;
-    case 1: gemm_bf16_pipe_kernel<kKCont, kMNCont, WM, WN, ST, PK, WNT><<<grid, NT, 0, st>>>(p); break;
-    case 2: gemm_bf16_pipe_kernel<kMNCont, kKCont, WM, WN, ST, PK, WNT><<<grid, NT, 0, st>>>(p); break;
-    default: gemm_bf16_pipe_kernel<kMNCont, kMNCont, WM, WN, ST, PK, WNT><<<grid, NT, 0, st>>>(p); break;
-  }
+  gemm_bf16_pipe_kernel<AL, BL, WM, WN, ST, PK, MI><<<grid, C::NT, 0, st>>>(p);
   return hipGetLastError();
 }
 
-// 256 x 256 block tiles (8 waves of 128 x 64), one block per CU.  With both
-// operands K-contiguous (forward products, Newton-Schulz Gram and polynomial
-// steps) a k-depth of 64 per stage (one barrier per 64 k, whole 128-byte rows
-// per load) measured 3-7 % faster than depth 32 with 4 stages, and the
-// half-stage ring, which keeps the A loads of the tile after next in flight
-// across the barrier, another 1.5-2.5 %; with an MN-contiguous operand
-// (input and weight gradients) depth 64 measured slower, and those keep depth
-// 32 with 4 stages.  256 x 128 tiles at two blocks per CU, 5 stages of depth
-// 32 and 4 waves of 128 x 128 (which spills) were all slower.
+// 256 x 256 block tiles (8 waves of 128 x 64), one block per CU.
+//  * Both operands K-contiguous (forward products, Newton-Schulz Gram and
+//    polynomial steps): k-depth 64 per step (one barrier per 64 k, whole
+//    128-byte rows per load), 3-7 % faster than depth 32 with 4 stages; the
+//    half-stage ring, which keeps the A loads of the tile after next in
+//    flight across the barrier, another 1.5-2.5 %; v_mfma_f32_16x16x32_bf16,
+//    which moves fewer accumulator bytes per FLOP than the 32 x 32 x 16 form
+//    and so draws less power at the same rate, another 3 %.
+//  * An MN-contiguous operand (input and weight gradients): depth 32 with 4
+//    stages and 32 x 32 x 16 MFMAs; depth 64 and the 16 x 16 x 32 form both
+//    measured slower there.
+// 256 x 128 tiles at two blocks per CU, 5 stages of depth 32 and 4 waves of
+// 128 x 128 (which spills) were all slower.
 hipError_t launch_pipe(const GemmParams& p, hipStream_t st) {
-  if (p.a_layout == kKCont && p.b_layout == kKCont && p.K % 64 == 0)
-    return launch_pipe_cfg<2, 4, 5, 64>(p, st);
-  return launch_pipe_cfg<2, 4, 4>(p, st);
+  switch (p.a_layout * 2 + p.b_layout) {
+    case 0:
+      if (p.K % 64 == 0) return launch_pipe_cfg<kKCont, kKCont, 2, 4, 5, 64, 16>(p, st);
+      return launch_pipe_cfg<kKCont, kKCont, 2, 4, 4, 32, 32>(p, st);
+    case 1: return launch_pipe_cfg<kKCont, kMNCont, 2, 4, 4, 32, 32>(p, st);
+    case 2: return launch_pipe_cfg<kMNCont, kKCont, 2, 4, 4, 32, 32>(p, st);
+    default: return launch_pipe_cfg<kMNCont, kMNCont, 2, 4, 4, 32, 32>(p, st);
+  }
 }
 
 }  // namespace

@@ -33,11 +33,15 @@ def stored(logical, layout):
     return logical if layout == nc.NC_K_CONTIGUOUS else np.ascontiguousarray(logical.T)
 
 
+# K = 200: the generic kernel (K not a multiple of 32); K = 320: the pipelined
+# kernel (depth 64 with 16 x 16 x 32 MFMAs for K-contiguous x K-contiguous,
+# depth 32 with 32 x 32 x 16 MFMAs otherwise); K = 288: K-contiguous at depth 32.
+@pytest.mark.parametrize("K", [200, 288, 320])
 @pytest.mark.parametrize("dtype", [BF, F32])
 @pytest.mark.parametrize("al,bl", [(0, 0), (0, 1), (1, 1), (1, 0)])
-def test_gemm_layouts_ragged(dtype, al, bl):
-    M, N, K = 264, 136, 200          # one full 256 tile + ragged edges in M, N and K
-    rng = np.random.default_rng(10 + 2 * al + bl)
+def test_gemm_layouts_ragged(dtype, al, bl, K):
+    M, N = 264, 136                  # one full 256 tile + ragged edges in M and N
+    rng = np.random.default_rng(10 + 2 * al + bl + K)
     A = rng.standard_normal((M, K)).astype(np.float32)
     B = rng.standard_normal((N, K)).astype(np.float32)
     As, Bs = stored(A, al), stored(B, bl)
@@ -76,9 +80,12 @@ def test_gemm_unaligned_output_rows(epi):
         assert max_rel(host(C), C0 + acc) < 2e-6
 
 
-def test_gemm_epilogues_bf16():
-    M, N, K = 320, 264, 136
-    rng = np.random.default_rng(3)
+# K = 136: generic kernel; 192: pipelined, depth 64, 16 x 16 x 32 MFMAs; 224:
+# pipelined, depth 32, 32 x 32 x 16 MFMAs (M and N ragged against 256 tiles)
+@pytest.mark.parametrize("K", [136, 192, 224])
+def test_gemm_epilogues_bf16(K):
+    M, N = 320, 264
+    rng = np.random.default_rng(3 + K)
     A = rng.standard_normal((M, K)).astype(np.float32)
     B = rng.standard_normal((N, K)).astype(np.float32)
     dA, dB = dev(A, BF), dev(B, BF)
@@ -115,6 +122,22 @@ def test_gemm_epilogues_bf16():
     dual = 3.0 * host(aux32) + 0.5 * acc
     assert max_rel(host(D32), dual) < 2e-6
     assert max_rel(host(Dh), dual) < tol
+
+
+@pytest.mark.parametrize("K", [256, 288])
+def test_gemm_batched_k_contiguous(K):
+    # batched K-contiguous products (the Newton-Schulz shape) on both pipelined paths
+    batch, M, N = 3, 264, 520
+    rng = np.random.default_rng(5 + K)
+    A = rng.standard_normal((batch, M, K)).astype(np.float32)
+    B = rng.standard_normal((batch, N, K)).astype(np.float32)
+    dA, dB = dev(A, BF), dev(B, BF)
+    C = torch.zeros(batch, M, N, dtype=F32, device="cuda")
+    nc.gemm(dA, 0, dB, 0, C, M, N, K, nc.EPI_STORE_F32, lda=K, ldb=K, ldc=N, batch=batch,
+            sA=M * K, sB=N * K, sC=M * N)
+    torch.cuda.synchronize()
+    ref = np.einsum("bmk,bnk->bmn", host(dA), host(dB))
+    assert max_rel(host(C), ref) < 2e-6
 
 
 @pytest.mark.parametrize("splits", [1, 4])
