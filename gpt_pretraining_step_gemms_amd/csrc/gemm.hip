@@ -922,9 +922,11 @@ hipError_t launch_pipe_cfg(const GemmParams& p, hipStream_t st) {
 //    flight across the barrier, another 1.5-2.5 %; v_mfma_f32_16x16x32_bf16,
 //    which moves fewer accumulator bytes per FLOP than the 32 x 32 x 16 form
 //    and so draws less power at the same rate, another 3 %.
-//  * An MN-contiguous operand (input and weight gradients): depth 32 with 4
-//    stages and 32 x 32 x 16 MFMAs; depth 64 and the 16 x 16 x 32 form both
-//    measured slower there.
+//  * A K-contiguous, B MN-contiguous (input gradients): the same half-stage
+//    ring with 16 x 16 x 32 MFMAs, 6-9 % faster than depth 32 with 4 stages.
+//  * Both MN-contiguous (weight gradients): depth 32 with 4 stages and
+//    32 x 32 x 16 MFMAs; depth 64 (two stages or the ring) and the 16 x 16 x 32
+//    form all measured slower there.
 // 256 x 128 tiles at two blocks per CU, 5 stages of depth 32 and 4 waves of
 // 128 x 128 (which spills) were all slower.
 hipError_t launch_pipe(const GemmParams& p, hipStream_t st) {
@@ -932,7 +934,9 @@ hipError_t launch_pipe(const GemmParams& p, hipStream_t st) {
     case 0:
       if (p.K % 64 == 0) return launch_pipe_cfg<kKCont, kKCont, 2, 4, 5, 64, 16>(p, st);
       return launch_pipe_cfg<kKCont, kKCont, 2, 4, 4, 32, 32>(p, st);
-    case 1: return launch_pipe_cfg<kKCont, kMNCont, 2, 4, 4, 32, 32>(p, st);
+    case 1:
+      if (p.K % 64 == 0) return launch_pipe_cfg<kKCont, kMNCont, 2, 4, 5, 64, 16>(p, st);
+      return launch_pipe_cfg<kKCont, kMNCont, 2, 4, 4, 32, 32>(p, st);
     case 2: return launch_pipe_cfg<kMNCont, kKCont, 2, 4, 4, 32, 32>(p, st);
     default: return launch_pipe_cfg<kMNCont, kMNCont, 2, 4, 4, 32, 32>(p, st);
   }
