@@ -217,6 +217,9 @@ def main():
                    "parallelism": "1 GPU, gradient accumulation"},
         "mfu": mfu,
         "mfu_with_newton_schulz": (step_flops + ns_flops) / sec / PEAK_BF16,
+        # attention counted as 12 L d T per token (the common non-causal convention)
+        "mfu_palm_convention": (step_flops + 6.0 * cfg.n_layer * d * cfg.seq_len * tokens)
+                               / sec / PEAK_BF16,
         "flops_per_token": fb_flops / (cfg.micro_batch * cfg.seq_len),
         "params_finite": finite,
         "roofline": {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
