@@ -425,24 +425,24 @@ __global__ void attn_bwd_pre_kernel(const T* __restrict__ o, const T* __restrict
 }
 
 // ------------------------------------------------------------ cross-entropy
-// One block per row of logits; the row (V <= 32768, V % 4 == 0) stays in
-// registers, 128 values per thread, so z is read once: max, then
-// e = exp(z - max) kept in place, S = sum e, loss = max + ln S - z[y],
+// One block of NTH threads per row of logits; the row (V <= 32768, V % 4 == 0)
+// stays in registers, 32768 / NTH values per thread, so z is read once: max,
+// then e = exp(z - max) kept in place, S = sum e, loss = max + ln S - z[y],
 // dz = scale * (e / S - onehot(y)).
-template <typename T>
-__global__ __launch_bounds__(256) void cross_entropy_kernel(
+template <typename T, int NTH>
+__global__ __launch_bounds__(NTH) void cross_entropy_kernel(
     const float* __restrict__ z, const int32_t* __restrict__ tgt, T* __restrict__ dz,
     float* __restrict__ loss_rows, int V, float scale) {
-  constexpr int KV = 32;                           // float4 per thread
+  constexpr int KV = 32768 / (4 * NTH);            // float4 per thread
   constexpr float kLog2e = 1.4426950408889634f;
-  __shared__ float red[4];
+  __shared__ float red[NTH / 64];
   const int row = blockIdx.x;
   const float* zr = z + (int64_t)row * V;
   float v[KV][4];
   float m = -INFINITY;
 #pragma unroll
   for (int k = 0; k < KV; ++k) {
-    const int i = threadIdx.x * 4 + k * 1024;
+    const int i = threadIdx.x * 4 + k * 4 * NTH;
     if (i < V) {
       Vec4<float>::load(zr + i, v[k]);
       m = fmaxf(m, fmaxf(fmaxf(v[k][0], v[k][1]), fmaxf(v[k][2], v[k][3])));
@@ -453,7 +453,7 @@ __global__ __launch_bounds__(256) void cross_entropy_kernel(
   float s = 0.f;
 #pragma unroll
   for (int k = 0; k < KV; ++k) {
-    const int i = threadIdx.x * 4 + k * 1024;
+    const int i = threadIdx.x * 4 + k * 4 * NTH;
     if (i < V) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -469,7 +469,7 @@ __global__ __launch_bounds__(256) void cross_entropy_kernel(
   T* dr = dz + (int64_t)row * V;
 #pragma unroll
   for (int k = 0; k < KV; ++k) {
-    const int i = threadIdx.x * 4 + k * 1024;
+    const int i = threadIdx.x * 4 + k * 4 * NTH;
     if (i < V) {
       float o[4];
 #pragma unroll
@@ -786,8 +786,9 @@ hipError_t nc_attn_bwd_pre(int dtype, const void* o, const void* dO, int64_t ld,
 hipError_t nc_cross_entropy(int dtype, const float* z, const int32_t* tgt, void* dz,
                             float* loss_rows, int rows, int V, float scale, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  if (dtype) cross_entropy_kernel<bf16><<<rows, 256, 0, st>>>(z, tgt, (bf16*)dz, loss_rows, V, scale);
-  else cross_entropy_kernel<float><<<rows, 256, 0, st>>>(z, tgt, (float*)dz, loss_rows, V, scale);
+  // 512 threads (64 logits each) per row: twice the waves per SIMD of 256
+  if (dtype) cross_entropy_kernel<bf16, 512><<<rows, 512, 0, st>>>(z, tgt, (bf16*)dz, loss_rows, V, scale);
+  else cross_entropy_kernel<float, 512><<<rows, 512, 0, st>>>(z, tgt, (float*)dz, loss_rows, V, scale);
   return hipGetLastError();
 }
 
