@@ -128,6 +128,72 @@ NC_DEV void epi_vec8(const GemmParams& p, int64_t off, const float (&v)[8]) {
   }
 }
 
+// The epilogue in two phases, so that a wave can issue the loads of several
+// row groups before any of its stores: a load issued after a store would wait
+// for that store (the wait counter is shared), which serialised one load
+// latency per 8 outputs.  EpiIn<EPI> is what an epilogue reads back for 8
+// consecutive outputs (raw, converted only when applied): nothing, 8 bf16 of
+// aux_in, or 8 fp32 of C or aux_in.
+template <int EPI>
+constexpr int epi_reads() {
+  return EPI == kEpiAccF32 || EPI == kEpiDual ? 2 : (EPI == kEpiRelu2Bwd || EPI == kEpiPoly ? 1 : 0);
+}
+template <int EPI>
+struct EpiIn {
+  f32x4 f[epi_reads<EPI>() == 2 ? 2 : 1];
+  bf16x8 h;
+};
+template <int EPI>
+NC_DEV void epi_load8(const GemmParams& p, int64_t off, EpiIn<EPI>& in) {
+  if constexpr (EPI == kEpiAccF32) {
+    in.f[0] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.C) + off);
+    in.f[1] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.C) + off + 4);
+  } else if constexpr (EPI == kEpiDual) {
+    if (p.aux_in) {
+      in.f[0] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.aux_in) + off);
+      in.f[1] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.aux_in) + off + 4);
+    } else {
+      in.f[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      in.f[1] = in.f[0];
+    }
+  } else if constexpr (EPI == kEpiRelu2Bwd || EPI == kEpiPoly) {
+    in.h = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(p.aux_in) + off);
+  }
+}
+// Same arithmetic as epi_one / epi_vec8, on values read by epi_load8.
+template <int EPI>
+NC_DEV void epi_apply8(const GemmParams& p, int64_t off, const float (&v)[8],
+                       const EpiIn<EPI>& in) {
+  float a[8], r[8];
+  if constexpr (epi_reads<EPI>() == 2) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { a[e] = in.f[0][e]; a[e + 4] = in.f[1][e]; }
+  } else if constexpr (epi_reads<EPI>() == 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = static_cast<float>(in.h[e]);
+  }
+  if constexpr (EPI == kEpiAccF32) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = a[e] + p.alpha * v[e];
+    st8(static_cast<float*>(p.C) + off, r);
+  } else if constexpr (EPI == kEpiRelu2Bwd) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = 2.f * __builtin_amdgcn_sqrtf(fmaxf(a[e], 0.f)) * v[e];
+    st8(static_cast<bf16*>(p.C) + off, r);
+  } else if constexpr (EPI == kEpiPoly) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = p.p0 * a[e] + p.p1 * v[e];
+    st8(static_cast<bf16*>(p.C) + off, r);
+  } else if constexpr (EPI == kEpiDual) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = p.p0 * a[e] + p.p1 * v[e];
+    st8(static_cast<float*>(p.C) + off, r);
+    st8(static_cast<bf16*>(p.aux_out) + off, r);
+  } else {
+    epi_vec8<EPI>(p, off, v);                      // stores only
+  }
+}
+
 // Calls f.template operator()<EPI>() with the epilogue chosen at run time, so
 // that each element loop is compiled for one epilogue.
 template <typename F>
@@ -834,50 +900,70 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
   const bool vec = split_out ? (p.N % 8 == 0) : p.vec_epi;
   const int rsub = lane >> 3, q = lane & 7;
   auto run = [&]<int EPI>() {
+    // row blocks whose loads (previous C or aux_in, if the epilogue reads
+    // any) are issued together, ahead of their stores: 8 (bf16) or 16 (fp32)
+    // VGPRs per lane and row block
+    constexpr int NIB = WTM / 32, GI = epi_reads<EPI>() == 2 ? 2 : NIB;
 #pragma unroll
-    for (int i = 0; i < WTM / 32; ++i) {              // 32-row blocks of the wave tile
-      // 32 x 32 tile: lane c + 32 h holds column c, rows 8 (e / 4) + 4 h + e % 4;
-      // 16 x 16 tile: lane c + 16 g holds column c, rows 4 g + e
-      if constexpr (MI == 32) {
+    for (int i0 = 0; i0 < NIB; i0 += GI) {
+      EpiIn<EPI> in[GI][4];
+      if constexpr (epi_reads<EPI>() > 0) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+        for (int ii = 0; ii < GI; ++ii)
 #pragma unroll
-          for (int e = 0; e < 16; ++e)
-            stg[((e >> 2) * 8 + half * 4 + (e & 3)) * EP_LD + j * 32 + l32] = acc[i][j][e];
-      } else {
+          for (int t = 0; t < 4; ++t) {
+            const int m = m0 + wm * WTM + (i0 + ii) * 32 + rsub + 8 * t;
+            const int n = n0 + wn * WTN + 8 * q;
+            if (m < p.M && vec && n + 8 <= p.N)
+              epi_load8<EPI>(p, cb + (int64_t)m * ld_out + n, in[ii][t]);
+          }
+      }
 #pragma unroll
-        for (int ii = 0; ii < 2; ++ii)
+      for (int ii = 0; ii < GI; ++ii) {
+        const int i = i0 + ii;                           // 32-row block of the wave tile
+        // 32 x 32 tile: lane c + 32 h holds column c, rows 8 (e / 4) + 4 h + e % 4;
+        // 16 x 16 tile: lane c + 16 g holds column c, rows 4 g + e
+        if constexpr (MI == 32) {
 #pragma unroll
           for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              stg[(ii * 16 + 4 * (lane >> 4) + e) * EP_LD + j * 16 + (lane & 15)] =
-                  acc[2 * i + ii][j][e];
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int row = rsub + 8 * t;
-        float v[8];
-        ld8(stg + row * EP_LD + 8 * q, v);
-        const int m = m0 + wm * WTM + i * 32 + row;
-        const int n = n0 + wn * WTN + 8 * q;
-        if (m >= p.M || n >= p.N) continue;
-        if (split_out) {
-          float* w = W + (int64_t)m * ld_out + n;
-          if (vec && n + 8 <= p.N) {
-            float r[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) r[e] = p.alpha * v[e];
-            st8(w, r);
-          } else {
-            for (int e = 0; e < 8 && n + e < p.N; ++e) w[e] = p.alpha * v[e];
-          }
+            for (int e = 0; e < 16; ++e)
+              stg[((e >> 2) * 8 + half * 4 + (e & 3)) * EP_LD + j * 32 + l32] = acc[i][j][e];
         } else {
-          const int64_t off = cb + (int64_t)m * ld_out + n;
-          if (vec && n + 8 <= p.N) {
-            epi_vec8<EPI>(p, off, v);
+#pragma unroll
+          for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                stg[(i2 * 16 + 4 * (lane >> 4) + e) * EP_LD + j * 16 + (lane & 15)] =
+                    acc[2 * i + i2][j][e];
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int row = rsub + 8 * t;
+          float v[8];
+          ld8(stg + row * EP_LD + 8 * q, v);
+          const int m = m0 + wm * WTM + i * 32 + row;
+          const int n = n0 + wn * WTN + 8 * q;
+          if (m >= p.M || n >= p.N) continue;
+          if (split_out) {
+            float* w = W + (int64_t)m * ld_out + n;
+            if (vec && n + 8 <= p.N) {
+              float r[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) r[e] = p.alpha * v[e];
+              st8(w, r);
+            } else {
+              for (int e = 0; e < 8 && n + e < p.N; ++e) w[e] = p.alpha * v[e];
+            }
           } else {
-            for (int e = 0; e < 8 && n + e < p.N; ++e) epi_one<bf16, EPI>(p, off + e, v[e]);
+            const int64_t off = cb + (int64_t)m * ld_out + n;
+            if (vec && n + 8 <= p.N) {
+              epi_apply8<EPI>(p, off, v, in[ii][t]);
+            } else {
+              for (int e = 0; e < 8 && n + e < p.N; ++e) epi_one<bf16, EPI>(p, off + e, v[e]);
+            }
           }
         }
       }
