@@ -794,8 +794,10 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
     // substep s (two register sets), so only the first substep after the
     // barrier waits for LDS.  Measured faster for every layout but A
     // K-contiguous with B MN-contiguous, which reads each substep's
-    // fragments at its start.
-    constexpr bool PREF = !(AL == kKCont && BL == kMNCont);
+    // fragments at its start; both MN-contiguous with 16 x 16 x 32 MFMAs
+    // has no registers for the second set.
+    constexpr bool PREF = !(AL == kKCont && BL == kMNCont) &&
+                          !(AL == kMNCont && BL == kMNCont && MI == 16);
     constexpr int NR = TM + TN;                        // fragment reads per substep
     static_assert(NR <= NM, "one read per MFMA slot");
     bf16x8 fr[2][NR];
@@ -1010,9 +1012,10 @@ hipError_t launch_pipe_cfg(const GemmParams& p, hipStream_t st) {
 //    and so draws less power at the same rate, another 3 %.
 //  * A K-contiguous, B MN-contiguous (input gradients): the same half-stage
 //    ring with 16 x 16 x 32 MFMAs, 6-9 % faster than depth 32 with 4 stages.
-//  * Both MN-contiguous (weight gradients): depth 32 with 4 stages and
-//    32 x 32 x 16 MFMAs; depth 64 (two stages or the ring) and the 16 x 16 x 32
-//    form all measured slower there.
+//  * Both MN-contiguous (weight gradients): the half-stage ring with
+//    16 x 16 x 32 MFMAs and no fragment prefetch (which would spill), 1-2 %
+//    faster than depth 32 with 4 stages and 32 x 32 x 16 MFMAs; depth 32 with
+//    16 x 16 x 32 (no room for prefetch either) measured 3.5 % slower.
 // 256 x 128 tiles at two blocks per CU, 5 stages of depth 32 and 4 waves of
 // 128 x 128 (which spills) were all slower.
 hipError_t launch_pipe(const GemmParams& p, hipStream_t st) {
@@ -1024,7 +1027,9 @@ hipError_t launch_pipe(const GemmParams& p, hipStream_t st) {
       if (p.K % 64 == 0) return launch_pipe_cfg<kKCont, kMNCont, 2, 4, 5, 64, 16>(p, st);
       return launch_pipe_cfg<kKCont, kMNCont, 2, 4, 4, 32, 32>(p, st);
     case 2: return launch_pipe_cfg<kMNCont, kKCont, 2, 4, 4, 32, 32>(p, st);
-    default: return launch_pipe_cfg<kMNCont, kMNCont, 2, 4, 4, 32, 32>(p, st);
+    default:
+      if (p.K % 64 == 0) return launch_pipe_cfg<kMNCont, kMNCont, 2, 4, 5, 64, 16>(p, st);
+      return launch_pipe_cfg<kMNCont, kMNCont, 2, 4, 4, 32, 32>(p, st);
   }
 }
 
