@@ -53,11 +53,13 @@ def test_gemm_layouts_ragged(dtype, al, bl, K):
     assert max_rel(host(C), ref) < 2e-6
 
 
+# K = 96: depth 32, 32 x 32 x 16 MFMAs; K = 128: the half-stage ring, 16 x 16 x 32
+@pytest.mark.parametrize("K", [96, 128])
 @pytest.mark.parametrize("epi", ["store", "relu2", "acc_f32"])
-def test_gemm_unaligned_output_rows(epi):
+def test_gemm_unaligned_output_rows(epi, K):
     """N = 131 (ldc not a multiple of 8): the epilogue's per-element path."""
-    M, N, K = 300, 131, 96
-    rng = np.random.default_rng(8)
+    M, N = 300, 131
+    rng = np.random.default_rng(8 + K)
     A = rng.standard_normal((M, K)).astype(np.float32)
     B = rng.standard_normal((N, K)).astype(np.float32)
     dA, dB = dev(A, BF), dev(B, BF)
