@@ -55,6 +55,9 @@ NC_DEV void epi_one(const GemmParams& p, int64_t off, float v) {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// st8 writes GEMM outputs with non-temporal stores: the outputs (hundreds of
+// MB per product) are not re-read from L2, and streaming them measured 2.5-3 %
+// faster on the store-heavy products and 6.5 % on the ReLU^2 backward.
 NC_DEV void ld8(const bf16* q, float (&x)[8]) {
   const bf16x8 h = *reinterpret_cast<const bf16x8*>(q);
 #pragma unroll
@@ -64,7 +67,7 @@ NC_DEV void st8(bf16* q, const float (&x)[8]) {
   bf16x8 h;
 #pragma unroll
   for (int e = 0; e < 8; ++e) h[e] = static_cast<bf16>(x[e]);
-  *reinterpret_cast<bf16x8*>(q) = h;
+  __builtin_nontemporal_store(h, reinterpret_cast<bf16x8*>(q));
 }
 NC_DEV void ld8(const float* q, float (&x)[8]) {
   const f32x4 a = *reinterpret_cast<const f32x4*>(q), b = *reinterpret_cast<const f32x4*>(q + 4);
@@ -75,8 +78,8 @@ NC_DEV void st8(float* q, const float (&x)[8]) {
   f32x4 a, b;
 #pragma unroll
   for (int e = 0; e < 4; ++e) { a[e] = x[e]; b[e] = x[e + 4]; }
-  *reinterpret_cast<f32x4*>(q) = a;
-  *reinterpret_cast<f32x4*>(q + 4) = b;
+  __builtin_nontemporal_store(a, reinterpret_cast<f32x4*>(q));
+  __builtin_nontemporal_store(b, reinterpret_cast<f32x4*>(q + 4));
 }
 
 // Eight consecutive outputs of one row at offset `off` of C (and aux), with
