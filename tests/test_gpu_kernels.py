@@ -142,6 +142,26 @@ def test_gemm_batched_k_contiguous(K):
     assert max_rel(host(C), ref) < 2e-6
 
 
+@pytest.mark.parametrize("al,bl", [(0, 0), (0, 1), (1, 1)])
+def test_gemm_degenerate_shapes(al, bl):
+    # more splits than 64-deep k-steps (empty splits write zero partials), and
+    # a product smaller than one 256 x 256 tile, on the pipelined kernels
+    rng = np.random.default_rng(21 + 2 * al + bl)
+    for M, N, K, splits in [(264, 136, 128, 4), (8, 16, 64, 1), (24, 8, 192, 5)]:
+        A = rng.standard_normal((M, K)).astype(np.float32)
+        B = rng.standard_normal((N, K)).astype(np.float32)
+        As, Bs = stored(A, al), stored(B, bl)
+        dA, dB = dev(As, BF), dev(Bs, BF)
+        C0 = rng.standard_normal((M, N)).astype(np.float32)
+        C = dev(C0, F32)
+        ws = torch.empty(splits * M * N, dtype=F32, device="cuda") if splits > 1 else None
+        nc.gemm(dA, al, dB, bl, C, M, N, K, nc.EPI_ACC_F32, lda=As.shape[1], ldb=Bs.shape[1],
+                splits=splits, workspace=ws)
+        torch.cuda.synchronize()
+        ref = C0 + stored(host(dA), al) @ stored(host(dB), bl).T
+        assert max_rel(host(C), ref) < 2e-6, (M, N, K, splits)
+
+
 @pytest.mark.parametrize("splits", [1, 4])
 def test_gemm_batched_and_split_k(splits):
     batch, M, N, K = 3, 136, 200, 1024
