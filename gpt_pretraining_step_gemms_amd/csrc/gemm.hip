@@ -531,10 +531,13 @@ hipError_t launch_bf16_cfg(const GemmParams& p, hipStream_t st) {
 //   K-contiguous  [256 rows][32 or 64 k], 16-byte chunk c of row r stored at
 //                 c ^ ((r >> 2) & 3) (depth 32) or c ^ ((r >> 1) & 7) (depth
 //                 64)                             -> read with ds_read_b128;
-//   MN-contiguous [32 k][256 rows], chunk c of k-row kr stored at c ^ 4(kr & 3)
+//   MN-contiguous [32 or 64 k][256 rows], chunk c of k-row kr stored at
+//                 c ^ mn_swz(kr), mn_swz(kr) = 4 (kr & 3) ^ 2 ((kr >> 3) & 1)
 //                 -> read with ds_read_b64_tr_b16, which hands each lane of a
 //                 16-lane group one column of a 4 x 16 block, i.e. 4 consecutive
-//                 k of one output row: the MFMA operand layout.
+//                 k of one output row: the MFMA operand layout.  (The k-row bit
+//                 3 term keeps the 16 x 16 x 32 reads, whose lanes 16-31 read
+//                 the k-rows 8 below lanes 0-15, off the same 64 banks.)
 // Both swizzles make the fragment reads bank-conflict free; the swizzle is
 // applied by choosing which global chunk each lane fetches.  Needs K % 32 == 0;
 // rows beyond M or N lie past the operand's buffer range, read as zeros and
@@ -575,7 +578,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 // alternates between even and odd blocks).
 struct Opnd {
   i32x4 rsrc;
-  unsigned lane_off[2];
+  unsigned lane_off[4];                          // by block bit 0 (and bit 2, MN-contiguous)
   unsigned ld2;                                  // leading dimension in bytes
 };
 
@@ -599,7 +602,8 @@ NC_DEV Opnd make_opnd(const bf16* base, int64_t ld, int64_t bytes, int lane) {
   o.rsrc[3] = 0x00020000;
   o.ld2 = (unsigned)ld * 2u;
 #pragma unroll
-  for (int par = 0; par < 2; ++par) {
+  for (int v = 0; v < 4; ++v) {
+    const int par = v & 1, b2 = v >> 1;            // bits 0 and 2 of the block index
     unsigned r, c;
     if constexpr (LAYOUT == kKCont && PK == 32) {  // row r = 16 blk + lane / 4
       r = lane >> 2;
@@ -607,11 +611,11 @@ NC_DEV Opnd make_opnd(const bf16* base, int64_t ld, int64_t bytes, int lane) {
     } else if constexpr (LAYOUT == kKCont) {       // row r = 8 blk + lane / 8
       r = lane >> 3;
       c = (lane & 7) ^ (4 * par + (r >> 1));       // (r >> 1) & 7 of the tile row
-    } else {                                       // k-row 2 blk + lane / 32
+    } else {                                       // k-row kr = 2 blk + lane / 32
       r = lane >> 5;
-      c = (lane & 31) ^ (4 * ((2 * par + r) & 3));
+      c = (lane & 31) ^ (4 * ((2 * par + r) & 3)) ^ (2 * b2);   // mn_swz(kr)
     }
-    o.lane_off[par] = r * o.ld2 + c * 16u;
+    o.lane_off[v] = r * o.ld2 + c * 16u;
   }
   return o;
 }
@@ -648,7 +652,13 @@ NC_DEV void issue_one(const Opnd& o, int row0, int k0, bf16* tile, int wave, int
   else
     u = (unsigned)(k0 + blk * 2) * o.ld2 + (unsigned)row0 * 2u;
   u = __builtin_amdgcn_readfirstlane(u);
-  dma16(o.rsrc, o.lane_off[blk & 1] + u, tile + blk * 512);
+  // explicit selects (a runtime array index would move lane_off to scratch)
+  unsigned lo = (blk & 1) ? o.lane_off[1] : o.lane_off[0];
+  if constexpr (LAYOUT != kKCont) {
+    const unsigned hi = (blk & 1) ? o.lane_off[3] : o.lane_off[2];
+    lo = ((blk >> 2) & 1) ? hi : lo;
+  }
+  dma16(o.rsrc, lo + u, tile + blk * 512);
 }
 
 // This wave's NI 1-KB loads of a ROWS x PK operand tile.
@@ -674,7 +684,7 @@ NC_DEV bf16x8 frag(const bf16* tile, int o0, int s, int lane) {
     const int g = lane >> 4, t = lane & 15;
     const int k = MI == 32 ? s * 16 + 8 * (g >> 1) + (t >> 2) : s * 32 + 8 * g + (t >> 2);
     const int o = o0 + (MI == 32 ? 16 * (g & 1) : 0) + 4 * (t & 3);
-    const int sw = 4 * (k & 3);                  // same for k and k + 4
+    const int sw = (4 * (k & 3)) ^ (2 * ((k >> 3) & 1));   // mn_swz(k), same for k + 4
     const bf16* p0 = tile + k * ROWS + (((o >> 3) ^ sw) << 3) + (o & 7);
     const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(NC_LDS(bf16x4_t, p0));
     const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(NC_LDS(bf16x4_t, p0 + 4 * ROWS));
