@@ -786,9 +786,10 @@ hipError_t nc_attn_bwd_pre(int dtype, const void* o, const void* dO, int64_t ld,
 hipError_t nc_cross_entropy(int dtype, const float* z, const int32_t* tgt, void* dz,
                             float* loss_rows, int rows, int V, float scale, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  // 512 threads (64 logits each) per row: twice the waves per SIMD of 256
-  if (dtype) cross_entropy_kernel<bf16, 512><<<rows, 512, 0, st>>>(z, tgt, (bf16*)dz, loss_rows, V, scale);
-  else cross_entropy_kernel<float, 512><<<rows, 512, 0, st>>>(z, tgt, (float*)dz, loss_rows, V, scale);
+  // 1024 threads (32 logits each) per row: 455 us per 8192-row chunk at 256
+  // threads, 305 at 512, 285 at 1024
+  if (dtype) cross_entropy_kernel<bf16, 1024><<<rows, 1024, 0, st>>>(z, tgt, (bf16*)dz, loss_rows, V, scale);
+  else cross_entropy_kernel<float, 1024><<<rows, 1024, 0, st>>>(z, tgt, (float*)dz, loss_rows, V, scale);
   return hipGetLastError();
 }
 
