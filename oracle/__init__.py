@@ -31,6 +31,7 @@ are covered only by the structural pins above.
 
 from .model import (  # noqa: F401
     rmsnorm, rmsnorm_backward, rope_tables, rope, rope_inverse,
-    causal_attention, causal_attention_backward, forward, loss_and_grads, logits_of,
+    causal_attention, causal_attention_backward, layer_windows, forward, loss_and_grads,
+    logits_of,
 )
 from .optim import adamw_step, newton_schulz, muon_step, train_step  # noqa: F401

@@ -29,6 +29,14 @@ Readings where the pages are silent:
   y_{i+h} = x_i sin + x_{i+h} cos.
 * Attention scale 1/sqrt(hd); causal mask keeps keys u <= t (diagonal kept);
   no document masking; one KV head per query head.
+* Sliding-window layers ([APIDOG] "1. Model GPT (nanochat/gpt.py)" lists a
+  configurable short/long window pattern such as "SSSL", and section
+  "5. Penyatuan Flash Attention" passes a window size to the attention call
+  next to causal=True): a layer with window w keeps keys t - w <= u <= t, the
+  w earlier positions plus the query's own (the left extent of a
+  flash-attention window with nothing on the right).  cfg["windows"] holds
+  one entry per layer, None for the plain causal mask; without the key every
+  layer is plain causal.  The pages print no window size.
 * Loss: natural log, mean over every position, no ignore index.
 """
 
@@ -76,32 +84,39 @@ def rope_inverse(y, cos, sin):
     return np.concatenate([y1 * cos + y2 * sin, -y1 * sin + y2 * cos], axis=-1)
 
 
-def _causal_mask(T):
-    return np.triu(np.ones((T, T), dtype=bool), k=1)   # True where key u > query t
+def _causal_mask(T, window=None):
+    """True where key u is hidden from query t: u > t, or u < t - window."""
+    t = np.arange(T)[:, None]
+    u = np.arange(T)[None, :]
+    hidden = u > t
+    if window is not None:
+        hidden |= u < t - window
+    return hidden
 
 
-def causal_attention(q, k, v):
-    """o = softmax(q k^T / sqrt(hd) with keys u > t removed) v.
+def causal_attention(q, k, v, window=None):
+    """o = softmax(q k^T / sqrt(hd) with keys u > t, and u < t - window when a
+    window is given, removed) v.
 
     q, k, v: [..., T, hd].  Returns (o, P) with P the attention probabilities.
     """
     hd = q.shape[-1]
     T = q.shape[-2]
     s = (q @ np.swapaxes(k, -1, -2)) / np.sqrt(hd)
-    s = np.where(_causal_mask(T), -np.inf, s)
+    s = np.where(_causal_mask(T, window), -np.inf, s)
     s = s - np.max(s, axis=-1, keepdims=True)
     p = np.exp(s)
     p = p / np.sum(p, axis=-1, keepdims=True)
     return p @ v, p
 
 
-def causal_attention_backward(q, k, v, do):
-    """(dq, dk, dv) of o = causal_attention(q, k, v) for an upstream gradient do:
+def causal_attention_backward(q, k, v, do, window=None):
+    """(dq, dk, dv) of o = causal_attention(q, k, v, window) for an upstream gradient do:
     with P the probabilities, dv = P^T do, dP = do v^T,
     dS = P * (dP - rowsum(dP * P)) (softmax Jacobian), dq = dS k / sqrt(hd),
     dk = dS^T q / sqrt(hd)."""
     hd = q.shape[-1]
-    _, p = causal_attention(q, k, v)
+    _, p = causal_attention(q, k, v, window)
     dv = np.swapaxes(p, -1, -2) @ do
     dp = do @ np.swapaxes(v, -1, -2)
     ds = p * (dp - np.sum(dp * p, axis=-1, keepdims=True))
@@ -144,6 +159,15 @@ def _merge_heads(u):
     return u.transpose(0, 2, 1, 3).reshape(B, T, H * hd)
 
 
+def layer_windows(cfg):
+    """Attention window of every layer (None = plain causal)."""
+    w = cfg.get("windows")
+    if w is None:
+        return [None] * cfg["n_layer"]
+    assert len(w) == cfg["n_layer"]
+    return list(w)
+
+
 def forward(params, tokens, targets, cfg, keep_cache=True):
     """Loss of one micro-batch.  tokens, targets: int [B, T].
 
@@ -158,6 +182,7 @@ def forward(params, tokens, targets, cfg, keep_cache=True):
     P = {k: np.asarray(v, F64) for k, v in params.items()}
 
     x = P["E"][tokens]                                  # [B,T,d]
+    windows = layer_windows(cfg)
     layers = []
     for i in range(cfg["n_layer"]):
         Wq, Wk, Wv, Wo, W1, W2 = (P[n] for n in _layer_names(i))
@@ -169,7 +194,7 @@ def forward(params, tokens, targets, cfg, keep_cache=True):
         kn, rk = rmsnorm(k, eps)
         qr = rope(qn, cos, sin)
         kr = rope(kn, cos, sin)
-        o_h, _ = causal_attention(qr, kr, v)
+        o_h, _ = causal_attention(qr, kr, v, windows[i])
         o = _merge_heads(o_h)
         x = x + o @ Wo.T
         m, r2 = rmsnorm(x, eps)
@@ -211,6 +236,7 @@ def loss_and_grads(params, tokens, targets, cfg, grad_scale=1.0):
     B, T = c["tokens"].shape
     n_tok = B * T
     cos, sin = c["cos"], c["sin"]
+    windows = layer_windows(cfg)
     grads = {}
 
     # cross-entropy: dz = (softmax(z) - onehot(y)) / (B*T)
@@ -235,7 +261,7 @@ def loss_and_grads(params, tokens, targets, cfg, grad_scale=1.0):
         # attention: x += o Wo^T
         grads[nWo] = _sum_outer(dx, L["o"])
         do = _split_heads(dx @ P[nWo], cfg["n_head"])
-        dqr, dkr, dv = causal_attention_backward(L["qr"], L["kr"], L["v"], do)
+        dqr, dkr, dv = causal_attention_backward(L["qr"], L["kr"], L["v"], do, windows[i])
         dq = rmsnorm_backward(rope_inverse(dqr, cos, sin), L["qn"], L["rq"])
         dk = rmsnorm_backward(rope_inverse(dkr, cos, sin), L["kn"], L["rk"])
         dq, dk, dv = _merge_heads(dq), _merge_heads(dk), _merge_heads(dv)

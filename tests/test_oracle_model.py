@@ -144,6 +144,74 @@ def test_attention_single_key_and_equal_keys():
     np.testing.assert_allclose(o, expect, atol=1e-13)
 
 
+# ---------------------------------------------------- sliding-window pins
+def test_window_zero_attends_to_self_only():
+    # one visible key: softmax weight 1, so o = v and the scores get no gradient
+    rng = np.random.default_rng(11)
+    q, k, v, do = (rng.standard_normal((2, 12, 8)) for _ in range(4))
+    o, p = oracle.causal_attention(q, k, v, window=0)
+    np.testing.assert_array_equal(o, v)
+    np.testing.assert_array_equal(p, np.broadcast_to(np.eye(12), p.shape))
+    dq, dk, dv = oracle.causal_attention_backward(q, k, v, do, window=0)
+    np.testing.assert_array_equal(dq, 0.0)
+    np.testing.assert_array_equal(dk, 0.0)
+    np.testing.assert_array_equal(dv, do)
+
+
+def test_window_covering_the_row_is_plain_causal():
+    rng = np.random.default_rng(12)
+    T = 10
+    q, k, v, do = (rng.standard_normal((T, 8)) for _ in range(4))
+    for w in (T - 1, T, 5 * T):
+        np.testing.assert_array_equal(oracle.causal_attention(q, k, v, w)[0],
+                                      oracle.causal_attention(q, k, v)[0])
+        for a, b in zip(oracle.causal_attention_backward(q, k, v, do, w),
+                        oracle.causal_attention_backward(q, k, v, do)):
+            np.testing.assert_array_equal(a, b)
+
+
+def test_window_equal_keys_give_moving_average():
+    # identical keys: uniform weights over the visible keys t-w..t
+    rng = np.random.default_rng(13)
+    T, w = 11, 3
+    q = rng.standard_normal((T, 8))
+    k = np.tile(rng.standard_normal((1, 8)), (T, 1))
+    v = rng.standard_normal((T, 8))
+    o, _ = oracle.causal_attention(q, k, v, window=w)
+    expect = np.stack([v[max(0, t - w):t + 1].mean(0) for t in range(T)])
+    np.testing.assert_allclose(o, expect, atol=1e-14)
+
+
+@pytest.mark.parametrize("w", [1, 2, 5])
+def test_window_matches_per_query_softmax_over_the_sliced_keys(w):
+    # brute force: each query's softmax written out over its own key slice
+    rng = np.random.default_rng(20 + w)
+    T, hd = 9, 8
+    q, k, v = (rng.standard_normal((T, hd)) for _ in range(3))
+    o, _ = oracle.causal_attention(q, k, v, window=w)
+    for t in range(T):
+        lo = max(0, t - w)
+        s = [float(q[t] @ k[u]) / math.sqrt(hd) for u in range(lo, t + 1)]
+        e = [math.exp(x - max(s)) for x in s]
+        ref = sum(ei * v[lo + j] for j, ei in enumerate(e)) / sum(e)
+        np.testing.assert_allclose(o[t], ref, rtol=1e-13, atol=1e-14)
+
+
+def test_window_receptive_field_of_stacked_layers():
+    # with windows w1, w2 a token reaches the logits of positions j .. j + w1 + w2 only
+    cfg = micro_cfg(L=2, d=16, H=1, V=16, T=12)
+    cfg["windows"] = [2, 3]
+    params, tok, _ = make(cfg, B=1, std=0.5)
+    z0 = oracle.logits_of(params, tok, cfg)
+    j = 3
+    tok2 = tok.copy()
+    tok2[0, j] = (tok[0, j] + 1) % cfg["vocab"]
+    z1 = oracle.logits_of(params, tok2, cfg)
+    changed = np.any(z0 != z1, axis=-1)[0]
+    assert not changed[:j].any() and not changed[j + 6:].any()
+    assert changed[j:j + 6].all()
+
+
 # --------------------------------------------------------------- gradients
 def _fd_check(cfg, B, std, names=None, max_coords=None, seed=0):
     params, tok, tgt = make(cfg, B, seed=seed, std=std)
@@ -179,6 +247,12 @@ def test_fd_gradients_one_layer_every_coordinate():
 
 def test_fd_gradients_two_layers_two_heads_sampled():
     _fd_check(micro_cfg(L=2, d=32, H=2, V=64, T=8), B=2, std=0.3, max_coords=40, seed=3)
+
+
+def test_fd_gradients_sliding_window_layers():
+    cfg = micro_cfg(L=2, d=32, H=2, V=32, T=10)
+    cfg["windows"] = [3, None]
+    _fd_check(cfg, B=2, std=0.3, max_coords=40, seed=7)
 
 
 def test_fd_gradients_tiny_shape_sampled():
