@@ -35,6 +35,11 @@ def parse():
     ap.add_argument("--micro-batch", type=int, default=None)
     ap.add_argument("--accum", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--window-pattern", default=None,
+                    help='sliding-window attention pattern over the layers, e.g. "SSSL" '
+                         '(S: short window, L: whole causal context); default: none')
+    ap.add_argument("--short-window", type=int, default=None,
+                    help="keys before the query in an S layer (default seq_len / 2)")
     ap.add_argument("--roofline-only", action="store_true",
                     help="only the dominant-kernel timing loop (for profiling it alone)")
     ap.add_argument("--roofline-iters", type=int, default=20)
@@ -101,7 +106,7 @@ def copy_calibration(nbytes=1 << 30):
     torch.cuda.synchronize()
 
 
-def cpu_baseline(cfg, n_tok=2048):
+def cpu_baseline(cfg, n_tok=2048, windows=None):
     """The fp64 numpy oracle on a bounded sample of the same workload: forward
     + backward of one 2048-token row (n_tok < 2048 takes a prefix of it, which
     a causal model computes exactly as inside the full row).  The optimizer,
@@ -112,6 +117,8 @@ def cpu_baseline(cfg, n_tok=2048):
     from oracle.model import param_shapes
     from gpt_pretraining_step_gemms_amd import synthetic
     ocfg = cfg.as_oracle_cfg()
+    if windows is not None:
+        ocfg["windows"] = [None if w < 0 else w for w in windows]
     params = {k: v.astype(np.float64) for k, v in
               synthetic.normal_params(0, param_shapes(ocfg), cfg.init_std).items()}
     tok, tgt = synthetic.token_rows(1000, 1, cfg.seq_len, cfg.vocab, cfg.token_dist)
@@ -134,7 +141,8 @@ def main():
         sys.exit(2)
     import torch
     from gpt_pretraining_step_gemms_amd import nc, synthetic
-    from gpt_pretraining_step_gemms_amd.configs import CONFIGS, OptimConfig, with_batch
+    from gpt_pretraining_step_gemms_amd.configs import (CONFIGS, OptimConfig, with_batch,
+                                                        sliding_windows)
 
     cfg = CONFIGS[args.config]
     cfg = with_batch(cfg, micro_batch=args.micro_batch, accum_steps=args.accum)
@@ -148,6 +156,10 @@ def main():
     ocfg = OptimConfig()
     model = nc.Model(cfg, ocfg, max_micro_batch=cfg.micro_batch)
     model.init_params(seed=0, std=cfg.init_std)
+    windows = None
+    if args.window_pattern:
+        windows = sliding_windows(cfg.n_layer, cfg.seq_len, args.window_pattern, args.short_window)
+        model.set_attention_windows(windows)
     K = cfg.accum_steps
     toks, tgts = [], []
     for k in range(K):
@@ -193,7 +205,11 @@ def main():
     roof = roofline_gemm(cfg, args.roofline_iters)
     print(f"[bench] roofline {roof['achieved']:.0f} TFLOP/s ({roof['frac']:.3f} of peak)",
           file=sys.stderr, flush=True)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(cfg)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(cfg, windows=windows)
+    attention = "causal attention"
+    if windows is not None:
+        attention = (f"sliding-window attention, pattern {args.window_pattern.upper()} "
+                     f"(S layers see {max(windows)} earlier keys)")
 
     d = cfg.d_model
     out = {
@@ -210,7 +226,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (Zipf(1.1) token ids, N(0, 0.02^2) random-init weights)",
         "config": {"workload": f"{cfg.name} GPT pretraining step: {cfg.n_layer} layers, d {d}, "
-                               f"{cfg.n_head}x128 heads, MLP {cfg.d_ff} ReLU^2, vocab {cfg.vocab}, "
+                               f"{cfg.n_head}x128 heads, {attention}, MLP {cfg.d_ff} ReLU^2, "
+                               f"vocab {cfg.vocab}, "
                                f"seq {cfg.seq_len}, micro-batch {cfg.micro_batch} x {K} accumulated "
                                f"= {tokens} tokens/step, Muon (5 NS iters) + AdamW",
                    "global_batch": cfg.micro_batch * K, "seq_len": cfg.seq_len,
@@ -218,8 +235,8 @@ def main():
         "mfu": mfu,
         "mfu_with_newton_schulz": (step_flops + ns_flops) / sec / PEAK_BF16,
         # attention counted as 12 L d T per token (the common non-causal convention)
-        "mfu_palm_convention": (step_flops + 6.0 * cfg.n_layer * d * cfg.seq_len * tokens)
-                               / sec / PEAK_BF16,
+        "mfu_palm_convention": None if windows is not None else
+        (step_flops + 6.0 * cfg.n_layer * d * cfg.seq_len * tokens) / sec / PEAK_BF16,
         "flops_per_token": fb_flops / (cfg.micro_batch * cfg.seq_len),
         "params_finite": finite,
         "roofline": {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},

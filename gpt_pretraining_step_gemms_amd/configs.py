@@ -93,6 +93,22 @@ D26 = from_depth(26, micro_batch=128, accum_steps=4)
 CONFIGS = {c.name: c for c in (TINY, D12, D20, D24, D26)}
 
 
+def sliding_windows(n_layer, seq_len, pattern, short=None):
+    """Per-layer attention windows from a pattern of "S" (short window) and
+    "L" (the whole causal context) letters, repeated over the layers from the
+    first one.  apidog.com, "1. Model GPT (nanochat/gpt.py)", names such a
+    configurable pattern ("SSSL") without a window size; the short window
+    here defaults to half the sequence (keys t - seq_len/2 .. t).  Returns a
+    list with -1 for "L" layers."""
+    pattern = pattern.upper()
+    if not pattern or set(pattern) - {"S", "L"}:
+        raise ValueError(f"window pattern {pattern!r}: letters S and L only")
+    short = seq_len // 2 if short is None else int(short)
+    if short < 0:
+        raise ValueError("short window must be >= 0")
+    return [short if pattern[i % len(pattern)] == "S" else -1 for i in range(n_layer)]
+
+
 def with_batch(cfg, micro_batch=None, accum_steps=None, seq_len=None):
     kw = {}
     if micro_batch is not None:

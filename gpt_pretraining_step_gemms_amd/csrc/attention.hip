@@ -20,6 +20,11 @@
 //    (8x8 16-bit blocks) on their way into LDS.
 // fp32 path (tiny configuration): one wave per query (or key) row, plain
 // loops over the causal range.
+//
+// Sliding window: with a window w, query t sees keys t - w .. t (the causal
+// mask plus a left edge).  Every kernel takes it as `win`, with win = T for
+// the plain causal mask; tiles wholly outside the band are never loaded and
+// only the tiles the band's edges cross are masked element by element.
 #include "kernels.h"
 
 namespace {
@@ -176,7 +181,7 @@ NC_DEV bf16x8 fa_frag_vt(const bf16* tile, int row_base, int col_base, int lane)
 NC_DEV void attn_fwd_block(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, bf16* __restrict__ o, int64_t ldo, float* __restrict__ lse, int T, int H,
-    float scale_log2, int qb, int bh, bf16* st0, bf16* st1) {
+    int win, float scale_log2, int qb, int bh, bf16* st0, bf16* st1) {
   constexpr int KT = 64 * 128;                    // one 64 x 128 tile
   const int b = bh / H, h = bh % H;
   const int64_t base = (int64_t)b * T * ld + h * 128;
@@ -203,7 +208,9 @@ NC_DEV void attn_fwd_block(
     for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
   float m = -INFINITY, l = 0.f;
 
+  // key tiles from the block's first window start to the diagonal
   const int n_kv = 2 * qb + 2;
+  const int kv_lo = max(0, qb * 128 - win) / 64;
   auto issue = [&](int kv, bf16* st) {
     fa_issue_rows(kg, ld, kv * 64, st, wave, lane);
     fa_issue_rows(vg, ld, kv * 64, st + KT, wave, lane);
@@ -213,6 +220,7 @@ NC_DEV void attn_fwd_block(
     fa_barrier();               // ... and every wave's; tile kv-1 is no longer read
     if (kv + 1 < n_kv) issue(kv + 1, next);
     if (kv * 64 > q0w + 31) return;               // keys all after this wave's queries
+    if (kv * 64 + 63 < q0w - win) return;         // keys all before this wave's windows
     const bf16* vs = ks + KT;
     f32x16 sacc[2];
 #pragma unroll
@@ -227,7 +235,11 @@ NC_DEV void attn_fwd_block(
     // moves when the tile's max exceeds it by more than 8: the weights
     // 2^(x - m) then stay below 2^8, and O and l are rescaled only on the
     // (rare, after the first tiles) moves, skipped when no lane moves.
-    const bool need_mask = kv * 64 + 63 > q0w;
+    // Masks: keys after the query (tiles reaching the diagonal) and keys
+    // before its window (tiles crossing the window's left edge).  A lane can
+    // then see no key at all in a tile; its running max stays -inf and the
+    // weights below use a finite stand-in so that they come out 0, not NaN.
+    const bool need_mask = kv * 64 + 63 > q0w || kv * 64 < q0w + 31 - win;
     float mt = -INFINITY;
     if (need_mask) {
 #pragma unroll
@@ -235,7 +247,7 @@ NC_DEV void attn_fwd_block(
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = kv * 64 + kb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
-          if (key > myq) sacc[kb][e] = -INFINITY;
+          if (key > myq || key < myq - win) sacc[kb][e] = -INFINITY;
         }
     }
 #pragma unroll
@@ -255,11 +267,12 @@ NC_DEV void attn_fwd_block(
     }
     float sv[2][16];
     float ls = 0.f;
+    const float mf = fmaxf(m, -3.0e38f);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float pv = fast_exp2(fmaf(sacc[kb][e], scale_log2, -m));
+        const float pv = fast_exp2(fmaf(sacc[kb][e], scale_log2, -mf));
         sv[kb][e] = pv;
         ls += pv;
       }
@@ -275,8 +288,8 @@ NC_DEV void attn_fwd_block(
     }
   };
 
-  issue(0, st0);
-  for (int kv = 0; kv < n_kv; kv += 2) {
+  issue(kv_lo, st0);
+  for (int kv = kv_lo; kv < n_kv; kv += 2) {
     step(kv, st0, st1);
     if (kv + 1 < n_kv) step(kv + 1, st1, st0);
   }
@@ -322,7 +335,8 @@ NC_DEV void attn_bwd_dkv_block(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, const bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ lse,
     const float* __restrict__ Dv, bf16* __restrict__ dk, bf16* __restrict__ dv, int64_t ldd,
-    int T, int H, float scale_log2, float scale, int kblk, int bh, bf16* st0, bf16* st1) {
+    int T, int H, int win, float scale_log2, float scale, int kblk, int bh, bf16* st0,
+    bf16* st1) {
   constexpr int KT = 64 * 128;
   const int b = bh / H, h = bh % H;
   const int64_t base = (int64_t)b * T * ld + h * 128;
@@ -352,7 +366,8 @@ NC_DEV void attn_bwd_dkv_block(
 #pragma unroll
     for (int e = 0; e < 16; ++e) { dkacc[i][e] = 0.f; dvacc[i][e] = 0.f; }
 
-  const int qt0 = kblk * 2, nqt = T / 64;
+  // query tiles from the diagonal to the last query whose window holds a key of the block
+  const int qt0 = kblk * 2, nqt = min(T / 64, (kblk * 128 + 127 + win) / 64 + 1);
   auto issue = [&](int qt, bf16* st) {
     fa_issue_rows(q + base, ld, qt * 64, st, wave, lane);
     fa_issue_rows(dO + obase, ldo, qt * 64, st + KT, wave, lane);
@@ -367,6 +382,7 @@ NC_DEV void attn_bwd_dkv_block(
     fa_barrier();
     if (qt + 1 < nqt) issue(qt + 1, next);
     if (qt * 64 + 63 < k0w) return;               // queries all before this wave's keys
+    if (qt * 64 > k0w + 31 + win) return;         // queries all past these keys' windows
     const bf16* Qs = cur;
     const bf16* dOs = cur + KT;
     const float* lse_s = reinterpret_cast<const float*>(cur + 2 * KT);
@@ -382,14 +398,16 @@ NC_DEV void attn_bwd_dkv_block(
         pacc[qb] = mfma(fa_frag_k(dOs, qb * 32 + l32, s * 2 + half), vf[s], pacc[qb]);
       }
     }
-    // causal mask (only tiles that reach the diagonal): queries before the key
-    if (qt * 64 < k0w + 31) {
+    // masks (only tiles crossing an edge of the band): queries before the
+    // key, and queries whose window ends before it
+    if (qt * 64 < k0w + 31 || qt * 64 + 63 > k0w + win) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (qt * 64 + qb * 32 + (e >> 2) * 8 + half * 4 + (e & 3) < mykey)
-            sacc[qb][e] = -INFINITY;
+        for (int e = 0; e < 16; ++e) {
+          const int qq = qt * 64 + qb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+          if (qq < mykey || qq > mykey + win) sacc[qb][e] = -INFINITY;
+        }
     }
     float p[2][16], ds[2][16];
 #pragma unroll
@@ -449,7 +467,7 @@ NC_DEV void attn_bwd_dkv_block(
 NC_DEV void attn_bwd_dq_block(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, const bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ lse,
-    const float* __restrict__ Dv, bf16* __restrict__ dq, int64_t ldd, int T, int H,
+    const float* __restrict__ Dv, bf16* __restrict__ dq, int64_t ldd, int T, int H, int win,
     float scale_log2, float scale, int qb, int bh, bf16* st0, bf16* st1) {
   constexpr int KT = 64 * 128;
   const int b = bh / H, h = bh % H;
@@ -485,6 +503,7 @@ NC_DEV void attn_bwd_dq_block(
     for (int e = 0; e < 16; ++e) dqacc[i][e] = 0.f;
 
   const int n_kv = 2 * qb + 2;
+  const int kv_lo = max(0, qb * 128 - win) / 64;
   auto issue = [&](int kv, bf16* st) {
     fa_issue_rows(kg, ld, kv * 64, st, wave, lane);
     fa_issue_rows(vg, ld, kv * 64, st + KT, wave, lane);
@@ -494,6 +513,7 @@ NC_DEV void attn_bwd_dq_block(
     fa_barrier();
     if (kv + 1 < n_kv) issue(kv + 1, next);
     if (kv * 64 > q0w + 31) return;
+    if (kv * 64 + 63 < q0w - win) return;
     const bf16* Ks = cur;
     const bf16* Vs = cur + KT;
     f32x16 sacc[2], pacc[2];
@@ -507,13 +527,16 @@ NC_DEV void attn_bwd_dq_block(
         pacc[kb] = mfma(fa_frag_k(Vs, kb * 32 + l32, s * 2 + half), df[s], pacc[kb]);
       }
     }
-    // causal mask (only tiles that reach the diagonal): keys after the query
-    if (kv * 64 + 63 > q0w) {
+    // masks (only tiles crossing an edge of the band): keys after the query
+    // and keys before its window
+    if (kv * 64 + 63 > q0w || kv * 64 < q0w + 31 - win) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (kv * 64 + kb * 32 + (e >> 2) * 8 + half * 4 + (e & 3) > myq) sacc[kb][e] = -INFINITY;
+        for (int e = 0; e < 16; ++e) {
+          const int key = kv * 64 + kb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+          if (key > myq || key < myq - win) sacc[kb][e] = -INFINITY;
+        }
     }
     float ds[2][16];
 #pragma unroll
@@ -534,8 +557,8 @@ NC_DEV void attn_bwd_dq_block(
     }
   };
 
-  issue(0, st0);
-  for (int kv = 0; kv < n_kv; kv += 2) {
+  issue(kv_lo, st0);
+  for (int kv = kv_lo; kv < n_kv; kv += 2) {
     step(kv, st0, st1);
     if (kv + 1 < n_kv) step(kv + 1, st1, st0);
   }
@@ -549,65 +572,89 @@ NC_DEV void attn_bwd_dq_block(
     }
 }
 
-// Causal work per 128-row block grows linearly with its index, so each
-// workgroup takes block i and its mirror nb-1-i of the same head (the middle
-// block alone when nb is odd): equal work per workgroup, no tail of long
-// blocks at the end of the grid.
-NC_DEV void mirror_pair(int nb, int& first, int& second, int& bh) {
-  const int npair = (nb + 1) / 2;
-  bh = blockIdx.x / npair;
-  const int i = blockIdx.x % npair;
-  first = nb - 1 - i;                              // the longer one first
-  second = i == nb - 1 - i ? -1 : i;
+// Workgroup -> (b*H + h, 128-row blocks).
+//  * Workgroups are dealt to the 8 XCDs round robin.  When the (b, h) count is
+//    a multiple of 8, all workgroups of one (b, h) go to the same XCD, one
+//    after the other, so that the K/V (or Q/dO) tiles they all walk are shared
+//    in that XCD's L2 and every XCD gets the same mix of long and short jobs.
+//  * Plain causal mask (paired): the work of a 128-row block grows linearly
+//    with its index, so a workgroup takes block i and its mirror nb-1-i (the
+//    middle block alone when nb is odd): equal work per workgroup.
+//  * Sliding window: the work levels off once the window is full, so a
+//    workgroup takes one block, the longest ones first (high_first: the
+//    block index at which work is largest is the highest one).
+struct BlockJob { int bh, first, second; };
+NC_DEV BlockJob block_job(int nb, bool paired, bool high_first) {
+  const int per = paired ? (nb + 1) / 2 : nb;     // workgroups per (b, h)
+  const int nbh = gridDim.x / per, b = blockIdx.x;
+  int j;
+  BlockJob jb;
+  if (nbh % 8 == 0) {
+    const int x = b % 8, r = b / 8;
+    jb.bh = x + 8 * (r / per);
+    j = r % per;
+  } else {
+    jb.bh = b / per;
+    j = b % per;
+  }
+  if (paired) {
+    jb.first = nb - 1 - j;
+    jb.second = j == nb - 1 - j ? -1 : j;
+  } else {
+    jb.first = high_first ? nb - 1 - j : j;
+    jb.second = -1;
+  }
+  return jb;
 }
+
+// workgroups per (b, h) for the bf16 kernels
+inline int attn_jobs_per_head(int T, int win) { return win >= T ? (T / 128 + 1) / 2 : T / 128; }
 
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, bf16* __restrict__ o, int64_t ldo, float* __restrict__ lse, int T, int H,
-    float scale_log2) {
+    int win, float scale_log2) {
   __shared__ __attribute__((aligned(1024))) bf16 st0[2 * 64 * 128];   // K | V of even tiles
   __shared__ __attribute__((aligned(1024))) bf16 st1[2 * 64 * 128];   // K | V of odd tiles
-  int first, second, bh;
-  mirror_pair(T / 128, first, second, bh);
-  attn_fwd_block(q, k, v, ld, o, ldo, lse, T, H, scale_log2, first, bh, st0, st1);
-  if (second < 0) return;
+  const BlockJob jb = block_job(T / 128, win >= T, true);
+  attn_fwd_block(q, k, v, ld, o, ldo, lse, T, H, win, scale_log2, jb.first, jb.bh, st0, st1);
+  if (jb.second < 0) return;
   __syncthreads();                                 // the first block's O staging is read
-  attn_fwd_block(q, k, v, ld, o, ldo, lse, T, H, scale_log2, second, bh, st0, st1);
+  attn_fwd_block(q, k, v, ld, o, ldo, lse, T, H, win, scale_log2, jb.second, jb.bh, st0, st1);
 }
 
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, const bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ lse,
     const float* __restrict__ Dv, bf16* __restrict__ dk, bf16* __restrict__ dv, int64_t ldd,
-    int T, int H, float scale_log2, float scale) {
+    int T, int H, int win, float scale_log2, float scale) {
   __shared__ __attribute__((aligned(1024))) bf16 st0[kDkvStage];
   __shared__ __attribute__((aligned(1024))) bf16 st1[kDkvStage];
-  int first, second, bh;
-  mirror_pair(T / 128, first, second, bh);
-  // key block kblk walks T/64 - 2 kblk query tiles: the longer one is kblk = second
-  if (second >= 0)
-    attn_bwd_dkv_block(q, k, v, ld, dO, ldo, lse, Dv, dk, dv, ldd, T, H, scale_log2, scale,
-                       second, bh, st0, st1);
-  __syncthreads();
-  attn_bwd_dkv_block(q, k, v, ld, dO, ldo, lse, Dv, dk, dv, ldd, T, H, scale_log2, scale, first,
-                     bh, st0, st1);
+  // key block kblk walks up to T/64 - 2 kblk query tiles: the low blocks are the long ones
+  const BlockJob jb = block_job(T / 128, win >= T, false);
+  if (jb.second >= 0) {
+    attn_bwd_dkv_block(q, k, v, ld, dO, ldo, lse, Dv, dk, dv, ldd, T, H, win, scale_log2, scale,
+                       jb.second, jb.bh, st0, st1);
+    __syncthreads();
+  }
+  attn_bwd_dkv_block(q, k, v, ld, dO, ldo, lse, Dv, dk, dv, ldd, T, H, win, scale_log2, scale,
+                     jb.first, jb.bh, st0, st1);
 }
 
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, const bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ lse,
-    const float* __restrict__ Dv, bf16* __restrict__ dq, int64_t ldd, int T, int H,
+    const float* __restrict__ Dv, bf16* __restrict__ dq, int64_t ldd, int T, int H, int win,
     float scale_log2, float scale) {
   __shared__ __attribute__((aligned(1024))) bf16 st0[2 * 64 * 128];   // K | V
   __shared__ __attribute__((aligned(1024))) bf16 st1[2 * 64 * 128];
-  int first, second, bh;
-  mirror_pair(T / 128, first, second, bh);
-  attn_bwd_dq_block(q, k, v, ld, dO, ldo, lse, Dv, dq, ldd, T, H, scale_log2, scale, first, bh,
-                    st0, st1);
-  if (second < 0) return;
+  const BlockJob jb = block_job(T / 128, win >= T, true);
+  attn_bwd_dq_block(q, k, v, ld, dO, ldo, lse, Dv, dq, ldd, T, H, win, scale_log2, scale,
+                    jb.first, jb.bh, st0, st1);
+  if (jb.second < 0) return;
   __syncthreads();
-  attn_bwd_dq_block(q, k, v, ld, dO, ldo, lse, Dv, dq, ldd, T, H, scale_log2, scale, second, bh,
-                    st0, st1);
+  attn_bwd_dq_block(q, k, v, ld, dO, ldo, lse, Dv, dq, ldd, T, H, win, scale_log2, scale,
+                    jb.second, jb.bh, st0, st1);
 }
 
 // ========================================================== fp32 path
@@ -615,7 +662,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
 __global__ void attn_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                     const float* __restrict__ v, int64_t ld,
                                     float* __restrict__ o, int64_t ldo, float* __restrict__ lse,
-                                    int B, int T, int H, float scale) {
+                                    int B, int T, int H, int win, float scale) {
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= B * H * T) return;
   const int lane = threadIdx.x & 63;
@@ -623,7 +670,7 @@ __global__ void attn_fwd_f32_kernel(const float* __restrict__ q, const float* __
   const int64_t base = (int64_t)b * T * ld + h * 128;
   const float q1 = q[base + (int64_t)t * ld + lane], q2 = q[base + (int64_t)t * ld + lane + 64];
   float m = -INFINITY, l = 0.f, o1 = 0.f, o2 = 0.f;
-  for (int u = 0; u <= t; ++u) {
+  for (int u = max(0, t - win); u <= t; ++u) {
     const int64_t ku = base + (int64_t)u * ld;
     const float s = wave_sum(q1 * k[ku + lane] + q2 * k[ku + lane + 64]) * scale;
     const float mn = fmaxf(m, s);
@@ -644,7 +691,7 @@ __global__ void attn_bwd_dq_f32_kernel(const float* __restrict__ q, const float*
                                        const float* __restrict__ dO, int64_t ldo,
                                        const float* __restrict__ lse,
                                        const float* __restrict__ Dv, float* __restrict__ dq,
-                                       int64_t ldd, int B, int T, int H, float scale) {
+                                       int64_t ldd, int B, int T, int H, int win, float scale) {
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= B * H * T) return;
   const int lane = threadIdx.x & 63;
@@ -655,7 +702,7 @@ __global__ void attn_bwd_dq_f32_kernel(const float* __restrict__ q, const float*
   const float g1 = dO[ob + lane], g2 = dO[ob + lane + 64];
   const float L = lse[(int64_t)bh * T + t], Dt = Dv[(int64_t)bh * T + t];
   float a1 = 0.f, a2 = 0.f;
-  for (int u = 0; u <= t; ++u) {
+  for (int u = max(0, t - win); u <= t; ++u) {
     const int64_t ku = base + (int64_t)u * ld;
     const float s = wave_sum(q1 * k[ku + lane] + q2 * k[ku + lane + 64]) * scale;
     const float p = expf(s - L);
@@ -676,7 +723,7 @@ __global__ void attn_bwd_dkv_f32_kernel(const float* __restrict__ q, const float
                                         const float* __restrict__ lse,
                                         const float* __restrict__ Dv, float* __restrict__ dk,
                                         float* __restrict__ dv, int64_t ldd, int B, int T, int H,
-                                        float scale) {
+                                        int win, float scale) {
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= B * H * T) return;
   const int lane = threadIdx.x & 63;
@@ -686,7 +733,8 @@ __global__ void attn_bwd_dkv_f32_kernel(const float* __restrict__ q, const float
   const float k1 = k[ku + lane], k2 = k[ku + lane + 64];
   const float v1 = v[ku + lane], v2 = v[ku + lane + 64];
   float ak1 = 0.f, ak2 = 0.f, av1 = 0.f, av2 = 0.f;
-  for (int t = u; t < T; ++t) {
+  const int t_end = min(T - 1, u + win);
+  for (int t = u; t <= t_end; ++t) {
     const int64_t qt = base + (int64_t)t * ld;
     const int64_t ot = ((int64_t)b * T + t) * ldo + h * 128;
     const float q1 = q[qt + lane], q2 = q[qt + lane + 64];
@@ -710,41 +758,46 @@ __global__ void attn_bwd_dkv_f32_kernel(const float* __restrict__ q, const float
 }  // namespace
 
 hipError_t nc_attn_fwd(int dtype, const void* q, const void* k, const void* v, int64_t ld,
-                       void* o, int64_t ldo, float* lse, int B, int T, int H, hipStream_t st) {
+                       void* o, int64_t ldo, float* lse, int B, int T, int H, int window,
+                       hipStream_t st) {
   const float scale = 1.0f / sqrtf(128.f);
+  const int win = window < 0 || window > T ? T : window;
   if (dtype) {
     if (T % 128) return hipErrorInvalidValue;
-    attn_fwd_kernel<<<B * H * ((T / 128 + 1) / 2), 256, 0, st>>>((const bf16*)q, (const bf16*)k,
-                                                        (const bf16*)v, ld, (bf16*)o, ldo, lse,
-                                                        T, H, scale * kLog2e);
+    attn_fwd_kernel<<<B * H * attn_jobs_per_head(T, win), 256, 0, st>>>(
+        (const bf16*)q, (const bf16*)k, (const bf16*)v, ld, (bf16*)o, ldo, lse, T, H, win,
+        scale * kLog2e);
   } else {
     attn_fwd_f32_kernel<<<ceil_div(B * H * T, 4), 256, 0, st>>>(
-        (const float*)q, (const float*)k, (const float*)v, ld, (float*)o, ldo, lse, B, T, H, scale);
+        (const float*)q, (const float*)k, (const float*)v, ld, (float*)o, ldo, lse, B, T, H, win,
+        scale);
   }
   return hipGetLastError();
 }
 
 hipError_t nc_attn_bwd(int dtype, const void* q, const void* k, const void* v, int64_t ld,
                        const void* dO, int64_t ldo, const float* lse, const float* D, void* dq,
-                       void* dk, void* dv, int64_t ldd, int B, int T, int H, hipStream_t st) {
+                       void* dk, void* dv, int64_t ldd, int B, int T, int H, int window,
+                       hipStream_t st) {
   const float scale = 1.0f / sqrtf(128.f);
+  const int win = window < 0 || window > T ? T : window;
   if (dtype) {
     if (T % 128) return hipErrorInvalidValue;
-    const int grid = B * H * ((T / 128 + 1) / 2);
+    const int grid = B * H * attn_jobs_per_head(T, win);
     attn_bwd_dkv_kernel<<<grid, 256, 0, st>>>((const bf16*)q, (const bf16*)k, (const bf16*)v, ld,
                                               (const bf16*)dO, ldo, lse, D, (bf16*)dk, (bf16*)dv,
-                                              ldd, T, H, scale * kLog2e, scale);
+                                              ldd, T, H, win, scale * kLog2e, scale);
     attn_bwd_dq_kernel<<<grid, 256, 0, st>>>((const bf16*)q, (const bf16*)k, (const bf16*)v, ld,
                                              (const bf16*)dO, ldo, lse, D, (bf16*)dq, ldd, T, H,
-                                             scale * kLog2e, scale);
+                                             win, scale * kLog2e, scale);
   } else {
     const int grid = ceil_div(B * H * T, 4);
     attn_bwd_dq_f32_kernel<<<grid, 256, 0, st>>>((const float*)q, (const float*)k, (const float*)v,
                                                  ld, (const float*)dO, ldo, lse, D, (float*)dq, ldd,
-                                                 B, T, H, scale);
+                                                 B, T, H, win, scale);
     attn_bwd_dkv_f32_kernel<<<grid, 256, 0, st>>>((const float*)q, (const float*)k, (const float*)v,
                                                   ld, (const float*)dO, ldo, lse, D, (float*)dk,
-                                                  (float*)dv, ldd, B, T, H, scale);
+                                                  (float*)dv, ldd, B, T, H, win, scale);
   }
   return hipGetLastError();
 }

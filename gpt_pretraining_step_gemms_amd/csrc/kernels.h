@@ -26,16 +26,18 @@ hipError_t nc_qk_norm_rope_fwd(int dtype, void* qkv, float* rqk, const float* co
 hipError_t nc_qk_norm_rope_bwd(int dtype, void* dqkv, const void* qkv, const float* rqk,
                                const float* cos_sin, int n_tok, int T, int H, hipStream_t st);
 
-// ---- attention on token-major q/k/v (row stride ld_qkv), head dim 128
+// ---- attention on token-major q/k/v (row stride ld_qkv), head dim 128; query t
+// sees keys max(0, t - window) .. t (window < 0: keys 0 .. t)
 hipError_t nc_attn_fwd(int dtype, const void* q, const void* k, const void* v, int64_t ld_qkv,
-                       void* o, int64_t ld_o, float* lse, int B, int T, int H, hipStream_t st);
+                       void* o, int64_t ld_o, float* lse, int B, int T, int H, int window,
+                       hipStream_t st);
 // D[b,h,t] = sum_d dO*O
 hipError_t nc_attn_bwd_pre(int dtype, const void* o, const void* dO, int64_t ld_o, float* D,
                            int B, int T, int H, hipStream_t st);
 hipError_t nc_attn_bwd(int dtype, const void* q, const void* k, const void* v, int64_t ld_qkv,
                        const void* dO, int64_t ld_o, const float* lse, const float* D,
                        void* dq, void* dk, void* dv, int64_t ld_dqkv, int B, int T, int H,
-                       hipStream_t st);
+                       int window, hipStream_t st);
 
 // ---- softmax cross-entropy over rows of fp32 logits
 // dz = scale*(softmax(z) - onehot(y)) in the activation type; loss_rows[i] = lse - z[y]

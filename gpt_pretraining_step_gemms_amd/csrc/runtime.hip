@@ -72,6 +72,7 @@ struct nc_ctx {
   // activation type for the matrix cores.
   struct NsBufs { size_t x32[2], xh[2], a32, ah, b32, bh; } ns[2];
   int splits_qkv, splits_o, splits_1, splits_2, splits_head, splits_dxf;
+  std::vector<int> windows;   // attention window per layer, -1 = plain causal
   char* pa = nullptr;
   char* aa = nullptr;
   hipStream_t st = nullptr;
@@ -339,6 +340,7 @@ static nc_ctx* make_ctx(const nc_model_config* cfg, const nc_optim_config* ocfg)
   c->L = cfg->n_layer; c->d = cfg->d_model; c->H = cfg->n_head; c->F = cfg->d_ff;
   c->V = cfg->vocab; c->T = cfg->seq_len; c->maxB = cfg->max_micro_batch;
   c->Nmax = c->maxB * c->T;
+  c->windows.assign(c->L, -1);
   plan(c);
   return c;
 }
@@ -432,6 +434,19 @@ nc_status nc_init_params(nc_ctx* ctx, uint64_t seed, float std) {
   return refresh_shadows(ctx);
 }
 
+nc_status nc_set_attention_windows(nc_ctx* ctx, const int32_t* windows) {
+  if (!ctx) return NC_ERR_INVALID_ARG;
+  if (!windows) {
+    ctx->windows.assign(ctx->L, -1);
+    return NC_OK;
+  }
+  for (int l = 0; l < ctx->L; ++l)
+    if (windows[l] < -1)
+      return fail(ctx, NC_ERR_INVALID_ARG, "window of layer " + std::to_string(l) + " below -1");
+  for (int l = 0; l < ctx->L; ++l) ctx->windows[l] = windows[l] >= ctx->T ? -1 : windows[l];
+  return NC_OK;
+}
+
 nc_status nc_zero_grads(nc_ctx* ctx) {
   if (!ctx) return NC_ERR_INVALID_ARG;
   if (!ctx->bound) return fail(ctx, NC_ERR_STATE, "bind first");
@@ -471,7 +486,7 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
                 kEpiStore), "qkv");
     NC_TRY(nc_qk_norm_rope_fwd(dt, qkv, A<float>(ctx, la.rqk), tab, N, T, H, eps, st), "qknorm");
     NC_TRY(nc_attn_fwd(dt, qkv, qkv + d * es, qkv + 2 * d * es, 3 * d, aa + la.o, d,
-                       A<float>(ctx, la.lse), B, T, H, st), "attn fwd");
+                       A<float>(ctx, la.lse), B, T, H, ctx->windows[l], st), "attn fwd");
     NC_GEMM(gemm(ctx, aa + la.o, d, kKCont, wptr(ctx, wb + 3ULL * d * d), d, kKCont, x, d, N, d,
                 d, kEpiAccF32), "out proj");
     NC_TRY(nc_rmsnorm_fwd(dt, x, aa + la.a2, A<float>(ctx, la.r2), N, d, eps, st), "norm2");
@@ -528,7 +543,7 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
            "attn D");
     NC_TRY(nc_attn_bwd(dt, qkv, qkv + d * es, qkv + 2 * d * es, 3 * d, aa + ctx->dO, d,
                        A<float>(ctx, la.lse), A<float>(ctx, ctx->Dbuf), dqkv, dqkv + d * es,
-                       dqkv + 2 * d * es, 3 * d, B, T, H, st), "attn bwd");
+                       dqkv + 2 * d * es, 3 * d, B, T, H, ctx->windows[l], st), "attn bwd");
     NC_TRY(nc_qk_norm_rope_bwd(dt, dqkv, qkv, A<float>(ctx, la.rqk), tab, N, T, H, st),
            "qknorm bwd");
     NC_GEMM(gemm(ctx, dqkv, 3 * d, kMNCont, aa + la.a1, d, kMNCont, G + wb, d, 3 * d, d, N,
@@ -739,7 +754,21 @@ nc_status nc_flops(const nc_ctx* ctx, int32_t B, double* fb, double* opt) {
   if (!ctx || B < 0) return NC_ERR_INVALID_ARG;
   const double L = ctx->L, d = ctx->d, F = ctx->F, V = ctx->V, T = ctx->T;
   const double N = (double)B * T;
-  if (fb) *fb = 6.0 * N * (L * (4 * d * d + 2 * d * F) + V * d) + 6.0 * N * L * d * T;
+  // attention: 12 d FLOP per (query, visible key) pair over forward and
+  // backward; a plain causal layer is counted at T/2 keys per query, a
+  // windowed one at its exact mean number of visible keys
+  double keys = 0;
+  for (int l = 0; l < ctx->L; ++l) {
+    const int w = ctx->windows[l];
+    if (w < 0) {
+      keys += T / 2;
+    } else {
+      double sum = 0;
+      for (int t = 0; t < ctx->T; ++t) sum += std::min(t, w) + 1;
+      keys += sum / T;
+    }
+  }
+  if (fb) *fb = 6.0 * N * (L * (4 * d * d + 2 * d * F) + V * d) + 12.0 * N * d * keys;
   if (opt) {
     const double steps = ctx->ocfg.ns_steps;
     const double sq = 4.0 * d * d * d + 2.0 * d * d * d;     // m = n = d
@@ -785,24 +814,28 @@ nc_status nc_op_gemm(int32_t dtype, const void* A_, int64_t lda, int32_t al, con
 
 nc_status nc_op_attention_fwd(int32_t dtype, const void* q, const void* k, const void* v,
                               int64_t ld_qkv, void* o, int64_t ld_o, float* lse, int32_t B,
-                              int32_t T, int32_t H, void* stream) {
-  if (!q || !k || !v || !o || !lse || B < 1 || T < 1 || H < 1) return NC_ERR_INVALID_ARG;
+                              int32_t T, int32_t H, int32_t window, void* stream) {
+  if (!q || !k || !v || !o || !lse || B < 1 || T < 1 || H < 1 || window < -1)
+    return NC_ERR_INVALID_ARG;
   if (dtype == NC_BF16 && (T % 128 || ld_qkv % 8 || ld_o % 8)) return NC_ERR_UNSUPPORTED;
-  return nc_attn_fwd(dtype == NC_BF16, q, k, v, ld_qkv, o, ld_o, lse, B, T, H,
+  return nc_attn_fwd(dtype == NC_BF16, q, k, v, ld_qkv, o, ld_o, lse, B, T, H, window,
                      static_cast<hipStream_t>(stream)) == hipSuccess ? NC_OK : NC_ERR_HIP;
 }
 
 nc_status nc_op_attention_bwd(int32_t dtype, const void* q, const void* k, const void* v,
                               int64_t ld_qkv, const void* o, const void* dO, int64_t ld_o,
                               const float* lse, float* D, void* dq, void* dk, void* dv,
-                              int64_t ld_d, int32_t B, int32_t T, int32_t H, void* stream) {
-  if (!q || !k || !v || !o || !dO || !lse || !D || !dq || !dk || !dv || B < 1 || T < 1 || H < 1)
+                              int64_t ld_d, int32_t B, int32_t T, int32_t H, int32_t window,
+                              void* stream) {
+  if (!q || !k || !v || !o || !dO || !lse || !D || !dq || !dk || !dv || B < 1 || T < 1 || H < 1 ||
+      window < -1)
     return NC_ERR_INVALID_ARG;
   if (dtype == NC_BF16 && (T % 128 || ld_qkv % 8 || ld_o % 8 || ld_d % 8)) return NC_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int dt = dtype == NC_BF16;
   if (nc_attn_bwd_pre(dt, o, dO, ld_o, D, B, T, H, st) != hipSuccess) return NC_ERR_HIP;
-  return nc_attn_bwd(dt, q, k, v, ld_qkv, dO, ld_o, lse, D, dq, dk, dv, ld_d, B, T, H, st) ==
+  return nc_attn_bwd(dt, q, k, v, ld_qkv, dO, ld_o, lse, D, dq, dk, dv, ld_d, B, T, H, window,
+                     st) ==
                  hipSuccess
              ? NC_OK
              : NC_ERR_HIP;

@@ -76,6 +76,7 @@ def load():
         "nc_bind": [P, P, SZ, P, SZ, P],
         "nc_init_params": [P, ctypes.c_uint64, F32],
         "nc_zero_grads": [P],
+        "nc_set_attention_windows": [P, P],
         "nc_fwd_bwd": [P, P, P, I32, F32, P],
         "nc_optimizer_step": [P, F32],
         "nc_param_count": [P, ctypes.POINTER(I32)],
@@ -87,8 +88,9 @@ def load():
         "nc_flops": [P, I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)],
         "nc_op_gemm": [I32, P, I64, I32, P, I64, I32, P, I64, I32, I32, I32, I32, I64, I64, I64,
                        I32, P, P, F32, F32, F32, I32, P, SZ, P],
-        "nc_op_attention_fwd": [I32, P, P, P, I64, P, I64, P, I32, I32, I32, P],
-        "nc_op_attention_bwd": [I32, P, P, P, I64, P, P, I64, P, P, P, P, P, I64, I32, I32, I32, P],
+        "nc_op_attention_fwd": [I32, P, P, P, I64, P, I64, P, I32, I32, I32, I32, P],
+        "nc_op_attention_bwd": [I32, P, P, P, I64, P, P, I64, P, P, P, P, P, I64, I32, I32, I32,
+                                I32, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -214,6 +216,16 @@ class Model:
     def init_params(self, seed, std=0.02):
         _check(self.lib.nc_init_params(self.ctx, seed, std), self.ctx, "init")
 
+    def set_attention_windows(self, windows):
+        """Per-layer attention window (None or -1: plain causal); None for all
+        layers plain causal."""
+        if windows is None:
+            _check(self.lib.nc_set_attention_windows(self.ctx, None), self.ctx, "windows")
+            return
+        assert len(windows) == self.cfg.n_layer
+        arr = (ctypes.c_int32 * len(windows))(*[-1 if w is None else int(w) for w in windows])
+        _check(self.lib.nc_set_attention_windows(self.ctx, arr), self.ctx, "windows")
+
     def zero_grads(self):
         _check(self.lib.nc_zero_grads(self.ctx), self.ctx, "zero_grads")
 
@@ -284,18 +296,18 @@ def gemm(A, a_layout, B, b_layout, C, M, N, K, epilogue=EPI_STORE, aux_in=None, 
     _check(s, what="nc_op_gemm")
 
 
-def attention_fwd(q, k, v, o, lse, B, T, H, ld_qkv, ld_o):
+def attention_fwd(q, k, v, o, lse, B, T, H, ld_qkv, ld_o, window=-1):
     lib = load()
     s = lib.nc_op_attention_fwd(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), ld_qkv, _ptr(o), ld_o,
-                                _ptr(lse), B, T, H,
+                                _ptr(lse), B, T, H, window,
                                 ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     _check(s, what="nc_op_attention_fwd")
 
 
-def attention_bwd(q, k, v, o, dO, lse, D, dq, dk, dv, B, T, H, ld_qkv, ld_o, ld_d):
+def attention_bwd(q, k, v, o, dO, lse, D, dq, dk, dv, B, T, H, ld_qkv, ld_o, ld_d, window=-1):
     lib = load()
     s = lib.nc_op_attention_bwd(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), ld_qkv, _ptr(o),
                                 _ptr(dO), ld_o, _ptr(lse), _ptr(D), _ptr(dq), _ptr(dk), _ptr(dv),
-                                ld_d, B, T, H,
+                                ld_d, B, T, H, window,
                                 ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     _check(s, what="nc_op_attention_bwd")

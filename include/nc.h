@@ -117,6 +117,18 @@ nc_status nc_bind(nc_ctx* ctx, void* d_param_arena, size_t param_bytes, void* d_
  * reset to zero. */
 nc_status nc_init_params(nc_ctx* ctx, uint64_t seed, float std);
 
+/* Host only.  Sliding-window attention per layer: windows[l] = w >= 0 lets
+ * query t of layer l see keys max(0, t - w) .. t (w earlier positions and its
+ * own), -1 keeps the plain causal mask; values >= seq_len equal -1.  The
+ * pages name a configurable pattern of short and long windows ("SSSL") and
+ * pass a window size to the attention call (apidog.com, "1. Model GPT
+ * (nanochat/gpt.py)" and "5. Penyatuan Flash Attention"); they print no
+ * size, so the sizes are the caller's.  windows: host array of n_layer
+ * entries, or NULL to make every layer plain causal again (the state after
+ * nc_create).  NC_ERR_INVALID_ARG (nothing changed) if an entry is below -1.
+ * Applies to later nc_fwd_bwd calls and to nc_flops. */
+nc_status nc_set_attention_windows(nc_ctx* ctx, const int32_t* windows);
+
 /* Sets every gradient to zero (start of a step). */
 nc_status nc_zero_grads(nc_ctx* ctx);
 
@@ -160,8 +172,10 @@ nc_status nc_get_tensor(nc_ctx* ctx, int32_t i, int32_t which, float* dst, int32
  * *host_flag = 1 and NC_ERR_NONFINITE if one is found, else 0 and NC_OK. */
 nc_status nc_check_finite(nc_ctx* ctx, int32_t* host_flag);
 
-/* Model FLOPs of one nc_fwd_bwd on B rows (matrix products only, causal
- * attention counted on its lower triangle) and of one Newton-Schulz pass. */
+/* Model FLOPs of one nc_fwd_bwd on B rows (matrix products only; a plain
+ * causal layer's attention counted at seq_len/2 keys per query, a windowed
+ * layer's at its exact mean number of visible keys) and of one Newton-Schulz
+ * pass. */
 nc_status nc_flops(const nc_ctx* ctx, int32_t B, double* fwd_bwd_flops, double* optimizer_flops);
 
 const char* nc_status_str(nc_status s);

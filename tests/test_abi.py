@@ -145,3 +145,40 @@ def test_parameter_registry_matches_model_shapes():
         assert fb.value == pytest.approx(6 * 32 * T * (12 * L * d * d + V * d) + 6 * 32 * T * L * d * T)
     finally:
         lib.nc_destroy(ctx)
+
+
+def test_attention_windows_set_and_counted_in_flops():
+    """nc_set_attention_windows (host only): rejects entries below -1, and
+    nc_flops counts a windowed layer at its mean number of visible keys."""
+    import ctypes
+    from gpt_pretraining_step_gemms_amd.configs import sliding_windows
+    cfg = TINY
+    lib = nc.load()
+    m, o = nc.model_cfg_c(cfg), nc.optim_cfg_c(OptimConfig())
+    ctx = ctypes.c_void_p()
+    assert lib.nc_create(ctypes.byref(m), ctypes.byref(o), ctypes.byref(ctx)) == nc.NC_OK
+    fb, opt = ctypes.c_double(), ctypes.c_double()
+
+    def flops():
+        assert lib.nc_flops(ctx, 2, ctypes.byref(fb), ctypes.byref(opt)) == nc.NC_OK
+        return fb.value
+
+    T, d, L = cfg.seq_len, cfg.d_model, cfg.n_layer
+    causal = flops()
+    Wn = (ctypes.c_int32 * L)
+    assert lib.nc_set_attention_windows(ctx, Wn(-2, 3)) == nc.NC_ERR_INVALID_ARG
+    assert flops() == causal
+    w = 8
+    assert lib.nc_set_attention_windows(ctx, Wn(w, -1)) == nc.NC_OK
+    visible = sum(min(t, w) + 1 for t in range(T))          # pairs (t, u) with t-w <= u <= t
+    expect = causal - 12.0 * 2 * T * d * (T / 2 - visible / T)
+    assert flops() == pytest.approx(expect, rel=1e-12)
+    assert lib.nc_set_attention_windows(ctx, Wn(T, 10 * T)) == nc.NC_OK
+    assert flops() == causal                                 # windows past the row = causal
+    assert lib.nc_set_attention_windows(ctx, Wn(w, -1)) == nc.NC_OK
+    assert lib.nc_set_attention_windows(ctx, None) == nc.NC_OK
+    assert flops() == causal
+    assert sliding_windows(5, 64, "SSL") == [32, 32, -1, 32, 32]
+    with pytest.raises(ValueError):
+        sliding_windows(4, 64, "SXL")
+    lib.nc_destroy(ctx)

@@ -221,7 +221,7 @@ def _heads(x, B, T, H, col0):
 
 
 @pytest.mark.parametrize("dtype,B,T,H", [(BF, 2, 256, 2), (BF, 1, 2048, 2), (BF, 2, 384, 1),
-                                         (F32, 2, 64, 1), (F32, 1, 100, 2)])
+                                         (BF, 4, 640, 2), (F32, 2, 64, 1), (F32, 1, 100, 2)])
 def test_attention_forward_backward_vs_oracle(dtype, B, T, H):
     d = H * 128
     qkv, dO = _attn_inputs(B, T, H, dtype, seed=T + H)
@@ -249,6 +249,107 @@ def test_attention_forward_backward_vs_oracle(dtype, B, T, H):
                            ("dv", _heads(dqkv, B, T, H, 2 * d), dv_r)]:
         assert cosine(got, ref) > (0.999 if bf else 1 - 1e-9), name
         assert max_rel(got, ref) < (3e-2 if bf else 1e-5), name
+
+
+def _band_lse(Q, K, w):
+    T = Q.shape[-2]
+    s = Q @ np.swapaxes(K, -1, -2) / np.sqrt(128.0)
+    t, u = np.arange(T)[:, None], np.arange(T)[None, :]
+    s = np.where((u > t) | (u < t - w), -np.inf, s)
+    return np.log(np.sum(np.exp(s - s.max(-1, keepdims=True)), -1)) + s.max(-1)
+
+
+@pytest.mark.parametrize("dtype,B,T,H,w", [
+    (BF, 1, 512, 2, 0), (BF, 1, 512, 2, 1), (BF, 1, 512, 2, 31), (BF, 1, 512, 2, 63),
+    (BF, 1, 512, 2, 64), (BF, 1, 512, 2, 100), (BF, 1, 512, 2, 128), (BF, 1, 512, 2, 200),
+    (BF, 1, 512, 2, 383), (BF, 1, 512, 2, 511), (BF, 2, 384, 1, 127), (BF, 1, 2048, 1, 1024),
+    (BF, 4, 640, 2, 100), (BF, 8, 256, 2, 64),
+    (F32, 2, 64, 1, 0), (F32, 2, 64, 1, 5), (F32, 1, 100, 2, 17), (F32, 1, 100, 2, 99)])
+def test_attention_sliding_window_vs_oracle(dtype, B, T, H, w):
+    """Query t sees keys t-w .. t: forward, log-sum-exp and all three
+    gradients against the oracle's banded attention."""
+    d = H * 128
+    qkv, dO = _attn_inputs(B, T, H, dtype, seed=1000 + T + w)
+    o = torch.empty(B * T, d, dtype=dtype, device="cuda")
+    lse = torch.empty(B, H, T, dtype=F32, device="cuda")
+    q, k, v = qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:]
+    print(f"[attn window] {dtype} B={B} T={T} H={H} w={w}", flush=True)
+    nc.attention_fwd(q, k, v, o, lse, B, T, H, ld_qkv=3 * d, ld_o=d, window=w)
+    dqkv = torch.zeros_like(qkv)
+    D = torch.empty(B, H, T, dtype=F32, device="cuda")
+    nc.attention_bwd(q, k, v, o, dO, lse, D, dqkv[:, :d], dqkv[:, d:2 * d], dqkv[:, 2 * d:],
+                     B, T, H, ld_qkv=3 * d, ld_o=d, ld_d=3 * d, window=w)
+    torch.cuda.synchronize()
+    Q, K, Vv = (_heads(qkv, B, T, H, c) for c in (0, d, 2 * d))
+    o_ref, _ = oracle.causal_attention(Q, K, Vv, window=w)
+    dq_r, dk_r, dv_r = oracle.causal_attention_backward(Q, K, Vv, _heads(dO, B, T, H, 0), window=w)
+    bf = dtype == BF
+    assert max_rel(_heads(o, B, T, H, 0), o_ref) < (2e-2 if bf else 1e-5)
+    assert np.max(np.abs(host(lse) - _band_lse(Q, K, w))) < (2e-3 if bf else 1e-5)
+    for name, got, ref in [("dq", _heads(dqkv, B, T, H, 0), dq_r),
+                           ("dk", _heads(dqkv, B, T, H, d), dk_r),
+                           ("dv", _heads(dqkv, B, T, H, 2 * d), dv_r)]:
+        if not np.any(ref):
+            # w = 0: one visible key, no gradient reaches the scores; what is
+            # left is the rounding of dP - D (both sums of the same products)
+            assert np.max(np.abs(got)) < (2e-2 if bf else 1e-5), name
+            continue
+        assert cosine(got, ref) > (0.999 if bf else 1 - 1e-9), name
+        assert max_rel(got, ref) < (3e-2 if bf else 1e-5), name
+
+
+@pytest.mark.parametrize("w", [-1, 1024])
+def test_attention_many_heads_sampled(w):
+    """16 (row, head) pairs of 2048 tokens (each XCD's share of the grid
+    holds whole heads, the layout of the full-size launches): sampled heads
+    against the oracle."""
+    B, T, H = 8, 2048, 2
+    d = H * 128
+    qkv, dO = _attn_inputs(B, T, H, BF, seed=77 + w)
+    q, k, v = qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:]
+    o = torch.empty(B * T, d, dtype=BF, device="cuda")
+    lse = torch.empty(B, H, T, dtype=F32, device="cuda")
+    print(f"[attn heads] B={B} T={T} H={H} w={w}", flush=True)
+    nc.attention_fwd(q, k, v, o, lse, B, T, H, 3 * d, d, window=w)
+    dqkv = torch.zeros_like(qkv)
+    D = torch.empty(B, H, T, dtype=F32, device="cuda")
+    nc.attention_bwd(q, k, v, o, dO, lse, D, dqkv[:, :d], dqkv[:, d:2 * d], dqkv[:, 2 * d:],
+                     B, T, H, 3 * d, d, 3 * d, window=w)
+    torch.cuda.synchronize()
+    win = None if w < 0 else w
+    heads = {c: _heads(x, B, T, H, c0) for c, (x, c0) in
+             {"q": (qkv, 0), "k": (qkv, d), "v": (qkv, 2 * d), "o": (o, 0), "dO": (dO, 0),
+              "dq": (dqkv, 0), "dk": (dqkv, d), "dv": (dqkv, 2 * d)}.items()}
+    for b, h in [(0, 0), (2, 1), (5, 0), (7, 1)]:
+        Q, K, Vv = heads["q"][b, h], heads["k"][b, h], heads["v"][b, h]
+        o_ref, _ = oracle.causal_attention(Q, K, Vv, window=win)
+        assert max_rel(heads["o"][b, h], o_ref) < 2e-2, (b, h)
+        assert np.max(np.abs(host(lse)[b, h] - _band_lse(Q, K, T if win is None else win))) < 2e-3
+        refs = oracle.causal_attention_backward(Q, K, Vv, heads["dO"][b, h], window=win)
+        for name, ref in zip(("dq", "dk", "dv"), refs):
+            got = heads[name][b, h]
+            assert cosine(got, ref) > 0.999 and max_rel(got, ref) < 3e-2, (b, h, name)
+
+
+def test_attention_window_covering_the_row_is_bitwise_causal():
+    B, T, H = 1, 384, 2
+    d = H * 128
+    qkv, dO = _attn_inputs(B, T, H, BF, seed=5)
+    q, k, v = qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:]
+    res = []
+    for w in (-1, T - 1, T, 10 * T):
+        o = torch.empty(B * T, d, dtype=BF, device="cuda")
+        lse = torch.empty(B, H, T, dtype=F32, device="cuda")
+        nc.attention_fwd(q, k, v, o, lse, B, T, H, 3 * d, d, window=w)
+        dqkv = torch.zeros_like(qkv)
+        D = torch.empty(B, H, T, dtype=F32, device="cuda")
+        nc.attention_bwd(q, k, v, o, dO, lse, D, dqkv[:, :d], dqkv[:, d:2 * d], dqkv[:, 2 * d:],
+                         B, T, H, 3 * d, d, 3 * d, window=w)
+        res.append((o, lse, dqkv))
+    torch.cuda.synchronize()
+    for r in res[1:]:
+        for a, b in zip(res[0], r):
+            assert torch.equal(a, b)
 
 
 def test_attention_causality_bitwise():

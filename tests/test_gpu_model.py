@@ -12,7 +12,7 @@ from dataclasses import replace
 import oracle
 from gpt_pretraining_step_gemms_amd import nc, synthetic
 from gpt_pretraining_step_gemms_amd.configs import (TINY, D12, D20, CONFIGS, ModelConfig,
-                                                    OptimConfig, with_batch)
+                                                    OptimConfig, with_batch, sliding_windows)
 from parity import cosine, max_rel
 
 pytestmark = pytest.mark.gpu
@@ -47,13 +47,17 @@ def run_gpu(m, tok, tgt, grad_scale=1.0):
     return float(loss.item()), {n: m.get(n, nc.NC_GRAD) for n in m.names()}
 
 
-def check_step(cfg, B, seed=0):
+def check_step(cfg, B, seed=0, windows=None):
     tol_l, tol_c, tol_r = TOL[cfg.dtype]
     ocfg = OptimConfig()
     m, params, tok, tgt = setup(cfg, B, seed, ocfg)
-    print(f"[parity] {cfg.name} B={B} seed={seed}", flush=True)
+    print(f"[parity] {cfg.name} B={B} seed={seed} windows={windows}", flush=True)
+    ocfg_model = cfg.as_oracle_cfg()
+    if windows is not None:
+        m.set_attention_windows(windows)
+        ocfg_model["windows"] = [None if w < 0 else w for w in windows]
     loss, grads = run_gpu(m, tok, tgt)
-    loss_o, grads_o = oracle.loss_and_grads(params, tok, tgt, cfg.as_oracle_cfg())
+    loss_o, grads_o = oracle.loss_and_grads(params, tok, tgt, ocfg_model)
     assert abs(loss - loss_o) / abs(loss_o) <= tol_l, (loss, loss_o)
     worst = []
     for n in grads_o:
@@ -81,6 +85,21 @@ def test_tiny_fp32_full_step():
 
 def test_small_bf16_full_step():
     check_step(SMALL_BF16, B=2, seed=3)
+
+
+def test_tiny_fp32_sliding_windows():
+    check_step(TINY, B=4, seed=4, windows=[8, -1])
+
+
+def test_small_bf16_sliding_windows():
+    check_step(SMALL_BF16, B=2, seed=5, windows=[127, 40])
+
+
+def test_d12_shape_sssl_pattern_one_row():
+    """The d12 shape with the short/short/short/long window pattern (short
+    window of 1024 keys) on one 2048-token row."""
+    cfg = with_batch(D12, micro_batch=1)
+    check_step(cfg, B=1, seed=9, windows=sliding_windows(cfg.n_layer, cfg.seq_len, "SSSL"))
 
 
 def test_d12_shape_one_row():
