@@ -142,7 +142,7 @@ def main():
     import torch
     from gpt_pretraining_step_gemms_amd import nc, synthetic
     from gpt_pretraining_step_gemms_amd.configs import (CONFIGS, OptimConfig, with_batch,
-                                                        sliding_windows)
+                                                        sliding_windows, NS_POLAR_EXPRESS)
 
     cfg = CONFIGS[args.config]
     cfg = with_batch(cfg, micro_batch=args.micro_batch, accum_steps=args.accum)
@@ -212,6 +212,8 @@ def main():
                      f"(S layers see {max(windows)} earlier keys)")
 
     d = cfg.d_model
+    ns_name = ("Polar Express schedule" if tuple(ocfg.ns_coeffs) == tuple(NS_POLAR_EXPRESS)
+               else "custom table")
     out = {
         "metric": "training tokens/sec and MFU (% bf16 MFMA peak) per GPT step, 1 MI355X",
         "value": tps,
@@ -229,7 +231,8 @@ def main():
                                f"{cfg.n_head}x128 heads, {attention}, MLP {cfg.d_ff} ReLU^2, "
                                f"vocab {cfg.vocab}, "
                                f"seq {cfg.seq_len}, micro-batch {cfg.micro_batch} x {K} accumulated "
-                               f"= {tokens} tokens/step, Muon (5 NS iters) + AdamW",
+                               f"= {tokens} tokens/step, Muon ({len(ocfg.ns_coeffs)} Newton-Schulz "
+                               f"steps, {ns_name}) + AdamW",
                    "global_batch": cfg.micro_batch * K, "seq_len": cfg.seq_len,
                    "parallelism": "1 GPU, gradient accumulation"},
         "mfu": mfu,

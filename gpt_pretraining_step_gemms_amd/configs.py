@@ -9,6 +9,8 @@ correctness case computed in fp32 end to end.
 
 from dataclasses import dataclass, field, asdict, replace
 
+from .polar_express import polar_express_table
+
 # Newton-Schulz coefficient tables (a, b, c) per iteration: data, not code.
 # Constant quintic from K. Jordan's public Muon write-up (the optimizer the
 # nanochat pages name), five iterations.
@@ -16,6 +18,9 @@ NS_QUINTIC_JORDAN = [(3.4445, -4.7750, 2.0315)] * 5
 # Textbook order-5 Newton-Schulz polar iteration (Higham, Functions of
 # Matrices, ch. 8): p(s) = (15 s - 10 s^3 + 3 s^5) / 8.
 NS_TEXTBOOK = [(15.0 / 8.0, -10.0 / 8.0, 3.0 / 8.0)]
+# The Polar Express schedule the pages name (five rows; the pages print the
+# first two), rebuilt by its published construction in polar_express.py.
+NS_POLAR_EXPRESS = polar_express_table()
 
 
 @dataclass(frozen=True)
@@ -57,7 +62,7 @@ class OptimConfig:
     muon_wd: float = 0.0
     ns_eps: float = 1e-7
     muon_nesterov: bool = False
-    ns_coeffs: tuple = tuple(NS_QUINTIC_JORDAN)
+    ns_coeffs: tuple = tuple(NS_POLAR_EXPRESS)
     adam_lr_embed: float = 3e-3
     adam_lr_head: float = 3e-3
     adam_beta1: float = 0.9

@@ -12,7 +12,8 @@ from dataclasses import replace
 import oracle
 from gpt_pretraining_step_gemms_amd import nc, synthetic
 from gpt_pretraining_step_gemms_amd.configs import (TINY, D12, D20, CONFIGS, ModelConfig,
-                                                    OptimConfig, with_batch, sliding_windows)
+                                                    OptimConfig, with_batch, sliding_windows,
+                                                    NS_QUINTIC_JORDAN)
 from parity import cosine, max_rel
 
 pytestmark = pytest.mark.gpu
@@ -47,9 +48,9 @@ def run_gpu(m, tok, tgt, grad_scale=1.0):
     return float(loss.item()), {n: m.get(n, nc.NC_GRAD) for n in m.names()}
 
 
-def check_step(cfg, B, seed=0, windows=None):
+def check_step(cfg, B, seed=0, windows=None, ocfg=None):
     tol_l, tol_c, tol_r = TOL[cfg.dtype]
-    ocfg = OptimConfig()
+    ocfg = ocfg or OptimConfig()
     m, params, tok, tgt = setup(cfg, B, seed, ocfg)
     print(f"[parity] {cfg.name} B={B} seed={seed} windows={windows}", flush=True)
     ocfg_model = cfg.as_oracle_cfg()
@@ -69,13 +70,16 @@ def check_step(cfg, B, seed=0, windows=None):
     torch.cuda.synchronize()
     new_o, _ = oracle.train_step(params, {n: g.astype(np.float64) for n, g in grads.items()}, {},
                                  1, ocfg.as_dict())
+    upd = []
     for n in params:
         dW = m.get(n).astype(np.float64) - params[n]
         dW_o = new_o[n] - params[n]
         c, r = cosine(dW, dW_o), max_rel(dW, dW_o)
+        upd.append((c, r, n))
         assert c >= tol_c and r <= tol_r, ("update", n, c, r)
     print(f"[parity] loss gpu {loss:.6f} oracle {loss_o:.6f}; worst grad cos "
-          f"{min(worst)[0]:.6f} max-rel {max(w[1] for w in worst):.3e}", flush=True)
+          f"{min(worst)[0]:.6f} max-rel {max(w[1] for w in worst):.3e}; worst update cos "
+          f"{min(upd)[0]:.6f} max-rel {max(u[1] for u in upd):.3e}", flush=True)
     m.close()
 
 
@@ -100,6 +104,16 @@ def test_d12_shape_sssl_pattern_one_row():
     window of 1024 keys) on one 2048-token row."""
     cfg = with_batch(D12, micro_batch=1)
     check_step(cfg, B=1, seed=9, windows=sliding_windows(cfg.n_layer, cfg.seq_len, "SSSL"))
+
+
+@pytest.mark.parametrize("name", ["tiny", "small", "d12", "d20"])
+def test_constant_quintic_schedule_full_step(name):
+    """The full step with the constant-quintic Newton-Schulz table (the
+    default table is the Polar Express schedule)."""
+    cfg = {"tiny": TINY, "small": SMALL_BF16, "d12": with_batch(D12, micro_batch=1),
+           "d20": with_batch(D20, micro_batch=1)}[name]
+    B = {"tiny": 4, "small": 2}.get(name, 1)
+    check_step(cfg, B, seed=21, ocfg=OptimConfig(ns_coeffs=tuple(NS_QUINTIC_JORDAN)))
 
 
 def test_d12_shape_one_row():

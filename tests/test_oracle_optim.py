@@ -84,7 +84,7 @@ def test_textbook_table_converges_to_polar_factor(shape):
     np.testing.assert_allclose(X, Q, atol=1e-10)
 
 
-def test_default_table_singular_values_near_one():
+def test_constant_quintic_singular_values_near_one():
     rng = np.random.default_rng(9)
     M = rng.standard_normal((64, 256))
     U, _, Vt = np.linalg.svd(M, full_matrices=False)
