@@ -34,4 +34,6 @@ from .model import (  # noqa: F401
     causal_attention, causal_attention_backward, layer_windows, forward, loss_and_grads,
     logits_of,
 )
-from .optim import adamw_step, newton_schulz, muon_step, train_step  # noqa: F401
+from .optim import (  # noqa: F401
+    adamw_step, newton_schulz, muon_step, normuon_update, muon_normuon_step, train_step,
+)

@@ -16,6 +16,16 @@ Readings where the pages are silent:
   pre-normalised by its Frobenius norm before Newton-Schulz (the iteration
   needs a spectral norm <= 1; the pages do not show this step), update
   W <- W (1 - lr wd) - lr * X.
+* NorMuon ([APIDOG] "2. Pengoptimal Muon (nanochat/optim.py)", the variance
+  reduction paragraph and its fragment): the fragment computes per-neuron
+  mean squares of the orthogonalised update, the norm they add up to, and a
+  final rescale by that norm over a "new" norm, but the lines between them
+  are missing.  Reading: a per-neuron second moment v2 (one value per output
+  row of W [out, in], zero at the start, no bias correction) follows
+  v2 <- beta2 v2 + (1 - beta2) mean_in(X^2); the update is X / sqrt(max(v2,
+  1e-10)) row by row, rescaled so that sqrt(sum over rows of mean_in(.^2))
+  equals the same quantity of X, times the Muon learning rate (the fragment's
+  step size); the new norm is clamped at 1e-10 as printed.
 * The Newton-Schulz coefficient table is data passed in; the pages print a
   partial Polar Express table.  Each iteration follows the loop printed in
   [APIDOG] "2. Pengoptimal Muon (nanochat/optim.py)": with X oriented tall,
@@ -73,6 +83,31 @@ def muon_step(W, G, M, lr, coeffs, momentum=0.95, eps=1e-7, wd=0.0,
     return W, M
 
 
+def normuon_update(X, v2, beta2, lr):
+    """NorMuon's per-neuron normalisation of an orthogonalised update X
+    [out, in] (the reading in the module docstring).  Returns (update, new v2);
+    the update is subtracted from W."""
+    X = np.asarray(X, F64)
+    vm = np.mean(X * X, axis=1)                       # per output neuron
+    v2 = beta2 * np.asarray(v2, F64) + (1.0 - beta2) * vm
+    Y = X / np.sqrt(np.maximum(v2, 1e-10))[:, None]
+    v_norm = np.sqrt(np.sum(vm))
+    v_norm_new = np.sqrt(np.sum(np.mean(Y * Y, axis=1)))
+    return Y * (lr * v_norm / max(v_norm_new, 1e-10)), v2
+
+
+def muon_normuon_step(W, G, M, v2, lr, coeffs, beta2, momentum=0.95, eps=1e-7, wd=0.0,
+                      nesterov=False):
+    """One Muon step followed by NorMuon's normalisation.  Returns new
+    (W, M, v2)."""
+    W, G, M = (np.asarray(a, F64) for a in (W, G, M))
+    M = momentum * M + G
+    U = G + momentum * M if nesterov else M
+    X = newton_schulz(U, coeffs, eps)
+    upd, v2 = normuon_update(X, v2, beta2, lr)
+    return W * (1.0 - lr * wd) - upd, M, v2
+
+
 def train_step(params, grads, state, step, hp):
     """Apply one optimizer step to every parameter.
 
@@ -80,7 +115,9 @@ def train_step(params, grads, state, step, hp):
     for AdamW; "mom" for Muon), created on first use; step: 1-based step
     number; hp: dict with adam_lr_embed, adam_lr_head, adam_beta1,
     adam_beta2, adam_eps, adam_wd, muon_lr, muon_momentum, muon_wd, ns_eps,
-    muon_nesterov, ns_coeffs.  Returns (new params, new state).
+    muon_nesterov, ns_coeffs, and optionally normuon (bool) and
+    normuon_beta2 (Muon state then also holds "v2").  Returns (new params,
+    new state).
     """
     new_p, new_s = {}, {}
     for name, W in params.items():
@@ -91,6 +128,14 @@ def train_step(params, grads, state, step, hp):
             p, m, v = adamw_step(W, G, st["m"], st["v"], step, lr, hp["adam_beta1"],
                                  hp["adam_beta2"], hp["adam_eps"], hp["adam_wd"])
             new_p[name], new_s[name] = p, {"m": m, "v": v}
+        elif hp.get("normuon"):
+            st = state.get(name) or {"mom": np.zeros_like(W, F64),
+                                     "v2": np.zeros(W.shape[0], F64)}
+            p, mom, v2 = muon_normuon_step(W, G, st["mom"], st["v2"], hp["muon_lr"],
+                                           hp["ns_coeffs"], hp["normuon_beta2"],
+                                           hp["muon_momentum"], hp["ns_eps"], hp["muon_wd"],
+                                           bool(hp.get("muon_nesterov", False)))
+            new_p[name], new_s[name] = p, {"mom": mom, "v2": v2}
         else:
             st = state.get(name) or {"mom": np.zeros_like(W, F64)}
             p, mom = muon_step(W, G, st["mom"], hp["muon_lr"], hp["ns_coeffs"],

@@ -144,3 +144,67 @@ def test_train_step_routes_groups():
     np.testing.assert_allclose(new["0.Wq"] - params["0.Wq"], -0.02 * ns_by_svd(grads["0.Wq"], NS_QUINTIC_JORDAN, 1e-7),
                                atol=1e-12)
     assert set(state["E"]) == {"m", "v"} and set(state["0.Wq"]) == {"mom"}
+
+
+# ------------------------------------------------------------------- NorMuon
+def test_normuon_first_step_equalises_rows_and_keeps_the_norm():
+    # v2 = (1 - beta2) mean(X^2) on the first step, so every output row ends up
+    # with the same RMS, each row keeps its direction, and the whole update
+    # has Frobenius norm lr ||X||_F
+    rng = np.random.default_rng(21)
+    X = rng.standard_normal((12, 30)) * rng.uniform(0.1, 3.0, (12, 1))
+    lr = 0.02
+    U, v2 = oracle.normuon_update(X, np.zeros(12), 0.95, lr)
+    rms = np.sqrt(np.mean(U * U, axis=1))
+    np.testing.assert_allclose(rms, lr * np.linalg.norm(X) / np.sqrt(X.size), rtol=1e-12)
+    np.testing.assert_allclose(np.linalg.norm(U), lr * np.linalg.norm(X), rtol=1e-12)
+    ratio = U / X
+    np.testing.assert_allclose(ratio, np.broadcast_to(ratio[:, :1], ratio.shape), rtol=1e-12)
+    assert np.all(ratio[:, 0] > 0)
+    np.testing.assert_allclose(v2, 0.05 * np.mean(X * X, axis=1), rtol=1e-14)
+
+
+def test_normuon_leaves_an_update_with_equal_rows_unchanged():
+    # rows of equal RMS (an orthogonal matrix): the normalisation is uniform
+    # and the rescale undoes it, whatever the state, so the update is lr X
+    rng = np.random.default_rng(22)
+    Q, _ = np.linalg.qr(rng.standard_normal((16, 16)))
+    v2 = rng.uniform(0.01, 1.0, 16)
+    v2[:] = v2[0]
+    U, _ = oracle.normuon_update(Q, v2, 0.9, 0.05)
+    np.testing.assert_allclose(U, 0.05 * Q, rtol=1e-12, atol=1e-15)
+
+
+def test_normuon_state_is_an_exponential_average_of_row_mean_squares():
+    rng = np.random.default_rng(23)
+    Xs = [rng.standard_normal((5, 9)) for _ in range(3)]
+    v2 = np.zeros(5)
+    for X in Xs:
+        _, v2 = oracle.normuon_update(X, v2, 0.9, 1.0)
+    ms = [np.mean(X * X, axis=1) for X in Xs]
+    np.testing.assert_allclose(v2, 0.1 * (0.81 * ms[0] + 0.9 * ms[1] + ms[2]), rtol=1e-13)
+    # the same X every step: v2 = (1 - beta2^t) mean(X^2) scales every row alike,
+    # so the update does not change from step to step
+    X = Xs[0]
+    v2 = np.zeros(5)
+    ups = []
+    for _ in range(3):
+        U, v2 = oracle.normuon_update(X, v2, 0.9, 0.3)
+        ups.append(U)
+    np.testing.assert_allclose(ups[1], ups[0], rtol=1e-12)
+    np.testing.assert_allclose(ups[2], ups[0], rtol=1e-12)
+
+
+def test_train_step_with_normuon_keeps_per_row_state():
+    rng = np.random.default_rng(24)
+    params = {"E": rng.standard_normal((6, 4)), "0.Wq": rng.standard_normal((4, 4)),
+              "0.W1": rng.standard_normal((8, 4)), "Wh": rng.standard_normal((6, 4))}
+    grads = {k: rng.standard_normal(v.shape) for k, v in params.items()}
+    hp = dict(adam_lr_embed=0.01, adam_lr_head=0.01, adam_beta1=0.9, adam_beta2=0.95,
+              adam_eps=1e-8, adam_wd=0.0, muon_lr=0.02, muon_momentum=0.95, muon_wd=0.0,
+              ns_eps=1e-7, ns_coeffs=NS_QUINTIC_JORDAN, normuon=True, normuon_beta2=0.95)
+    new_p, st = oracle.train_step(params, grads, {}, 1, hp)
+    assert st["0.W1"]["v2"].shape == (8,) and st["0.Wq"]["v2"].shape == (4,)
+    X = oracle.newton_schulz(grads["0.W1"], NS_QUINTIC_JORDAN, 1e-7)
+    U, _ = oracle.normuon_update(X, np.zeros(8), 0.95, 0.02)
+    np.testing.assert_allclose(params["0.W1"] - new_p["0.W1"], U, rtol=1e-12, atol=1e-15)
