@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--window-pattern", default=None,
                     help='sliding-window attention pattern over the layers, e.g. "SSSL" '
                          '(S: short window, L: whole causal context); default: none')
+    ap.add_argument("--normuon", action="store_true",
+                    help="NorMuon per-neuron normalisation after Newton-Schulz")
     ap.add_argument("--short-window", type=int, default=None,
                     help="keys before the query in an S layer (default seq_len / 2)")
     ap.add_argument("--roofline-only", action="store_true",
@@ -153,7 +155,7 @@ def main():
         print(json.dumps({"roofline": r}))
         return
 
-    ocfg = OptimConfig()
+    ocfg = OptimConfig(normuon=args.normuon)
     model = nc.Model(cfg, ocfg, max_micro_batch=cfg.micro_batch)
     model.init_params(seed=0, std=cfg.init_std)
     windows = None
@@ -213,7 +215,7 @@ def main():
 
     d = cfg.d_model
     ns_name = ("Polar Express schedule" if tuple(ocfg.ns_coeffs) == tuple(NS_POLAR_EXPRESS)
-               else "custom table")
+               else "custom table") + (", NorMuon" if ocfg.normuon else "")
     out = {
         "metric": "training tokens/sec and MFU (% bf16 MFMA peak) per GPT step, 1 MI355X",
         "value": tps,

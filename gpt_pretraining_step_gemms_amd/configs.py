@@ -69,6 +69,8 @@ class OptimConfig:
     adam_beta2: float = 0.95
     adam_eps: float = 1e-8
     adam_wd: float = 0.0
+    normuon: bool = False       # NorMuon per-neuron normalisation after Newton-Schulz
+    normuon_beta2: float = 0.95
 
     def as_dict(self):
         d = asdict(self)

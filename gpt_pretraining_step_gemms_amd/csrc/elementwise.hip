@@ -637,11 +637,71 @@ __global__ __launch_bounds__(256) void ns_prepare_kernel(const float* __restrict
   }
 }
 
+// NorMuon statistics, one value per row r of W_i [R, C] (row r of X_i [R, C],
+// or column r of X_i [C, R] when transpose != 0): vm = mean of the row's X^2;
+// the second moment v2 <- beta2 v2 + (1 - beta2) vm; then vm, q = vm / v2c and
+// inv = v2c^-1/2 with v2c = max(v2, 1e-10).  Per matrix, sum q is the squared
+// norm of the row-normalised update and sum vm that of X.
+__global__ __launch_bounds__(256) void normuon_rows_kernel(const float* __restrict__ X,
+                                                           int64_t x_stride, int R, int C,
+                                                           int transpose,
+                                                           float* __restrict__ v2, float beta2,
+                                                           float* __restrict__ vm_out,
+                                                           float* __restrict__ q_out,
+                                                           float* __restrict__ inv_out) {
+  const int i = blockIdx.y;
+  const float* x = X + (int64_t)i * x_stride;
+  int r;
+  float ss = 0.f;
+  if (transpose) {          // one thread per row: consecutive threads read consecutive r
+    r = blockIdx.x * 256 + threadIdx.x;
+    if (r >= R) return;
+    for (int c = 0; c < C; ++c) {
+      const float v = x[(int64_t)c * R + r];
+      ss = fmaf(v, v, ss);
+    }
+  } else {                  // one wave per row
+    r = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= R) return;
+    const float* row = x + (int64_t)r * C;
+    for (int c = threadIdx.x & 63; c < C; c += 64) ss = fmaf(row[c], row[c], ss);
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) != 0) return;
+  }
+  const int64_t k = (int64_t)i * R + r;
+  const float vm = ss / (float)C;
+  const float m2 = beta2 * v2[k] + (1.f - beta2) * vm;
+  v2[k] = m2;
+  const float m2c = fmaxf(m2, 1e-10f);
+  vm_out[k] = vm;
+  q_out[k] = vm / m2c;
+  inv_out[k] = rsqrtf(m2c);
+}
+
+// scale[i] = sqrt(sum_r vm) / max(sqrt(sum_r q), 1e-10): one block per matrix,
+// fixed summation order
+__global__ __launch_bounds__(256) void normuon_scale_kernel(const float* __restrict__ vm,
+                                                            const float* __restrict__ q, int R,
+                                                            float* __restrict__ scale) {
+  __shared__ float red[4];
+  const int i = blockIdx.x;
+  float a = 0.f, b = 0.f;
+  for (int r = threadIdx.x; r < R; r += 256) {
+    a += vm[(int64_t)i * R + r];
+    b += q[(int64_t)i * R + r];
+  }
+  a = block_sum(a, red);
+  b = block_sum(b, red);
+  if (threadIdx.x == 0) scale[i] = sqrtf(a) / fmaxf(sqrtf(b), 1e-10f);
+}
+
 __global__ __launch_bounds__(256) void ns_apply_kernel(float* __restrict__ W, MatBatch mb,
                                                        int R, int C,
                                                        const float* __restrict__ X,
                                                        int64_t x_stride, int transpose,
                                                        float lr, float wd,
+                                                       const float* __restrict__ row_mul,
+                                                       const float* __restrict__ mat_scale,
                                                        bf16* __restrict__ shadow) {
   __shared__ float tile[32][33];
   const int i = blockIdx.z;
@@ -660,7 +720,8 @@ __global__ __launch_bounds__(256) void ns_apply_kernel(float* __restrict__ W, Ma
     const int r = r0 + k, c = c0 + tx;
     if (r < R && c < C) {
       const int64_t off = (int64_t)r * C + c;
-      const float u = transpose ? tile[k][tx] : x[off];
+      float u = transpose ? tile[k][tx] : x[off];
+      if (row_mul) u *= mat_scale[i] * row_mul[(int64_t)i * R + r];
       const float nw = w[off] * (1.f - lr * wd) - lr * u;
       w[off] = nw;
       if (shadow) shadow[mb.off(i) + off] = (bf16)nw;
@@ -870,11 +931,21 @@ hipError_t nc_ns_prepare(int dtype, const float* src, MatBatch mb, int R, int C,
 }
 
 hipError_t nc_ns_apply(float* W, MatBatch mb, int R, int C, int count, const float* X,
-                       int64_t x_stride, int transpose, float lr, float wd, void* shadow,
-                       hipStream_t st) {
+                       int64_t x_stride, int transpose, float lr, float wd, const float* row_mul,
+                       const float* mat_scale, void* shadow, hipStream_t st) {
   if (count <= 0) return hipSuccess;
   dim3 grid(ceil_div(C, 32), ceil_div(R, 32), count);
-  ns_apply_kernel<<<grid, 256, 0, st>>>(W, mb, R, C, X, x_stride, transpose, lr, wd,
-                                        (bf16*)shadow);
+  ns_apply_kernel<<<grid, 256, 0, st>>>(W, mb, R, C, X, x_stride, transpose, lr, wd, row_mul,
+                                        mat_scale, (bf16*)shadow);
+  return hipGetLastError();
+}
+
+hipError_t nc_normuon_stats(const float* X, int64_t x_stride, int R, int C, int transpose,
+                            int count, float* v2, float beta2, float* vm, float* q, float* inv,
+                            float* scale, hipStream_t st) {
+  if (count <= 0) return hipSuccess;
+  dim3 grid(transpose ? ceil_div(R, 256) : ceil_div(R, 4), count);
+  normuon_rows_kernel<<<grid, 256, 0, st>>>(X, x_stride, R, C, transpose, v2, beta2, vm, q, inv);
+  normuon_scale_kernel<<<count, 256, 0, st>>>(vm, q, R, scale);
   return hipGetLastError();
 }

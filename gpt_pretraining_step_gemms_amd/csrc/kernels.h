@@ -83,8 +83,17 @@ hipError_t nc_frob_norms(const float* src, MatBatch mb, int64_t elems, int count
 hipError_t nc_ns_prepare(int dtype, const float* src, MatBatch mb, int R, int C, int count,
                          const float* norms, float eps, int transpose, float* X32, void* Xh,
                          int64_t x_stride, hipStream_t st);
-// W[i] = W[i]*(1 - lr*wd) - lr*X[i] (fp32 X read transposed when transpose != 0);
+// W[i] = W[i]*(1 - lr*wd) - lr*X[i] (fp32 X read transposed when transpose != 0),
+// with row r of X[i] multiplied by mat_scale[i] * row_mul[i*R + r] when row_mul != null;
 // shadow[i] (same addressing as W) = bf16(W[i]) when shadow != null.
 hipError_t nc_ns_apply(float* W, MatBatch mb, int R, int C, int count, const float* X,
-                       int64_t x_stride, int transpose, float lr, float wd, void* shadow,
-                       hipStream_t st);
+                       int64_t x_stride, int transpose, float lr, float wd, const float* row_mul,
+                       const float* mat_scale, void* shadow, hipStream_t st);
+// NorMuon: per row r of W_i [R, C] (X_i as for nc_ns_apply) updates the second
+// moment v2[i*R + r] with the row's mean X^2 and writes inv[i*R + r] = v2c^-1/2
+// (v2c = max(v2, 1e-10)) and scale[i] = sqrt(sum vm) / max(sqrt(sum vm / v2c), 1e-10);
+// vm and q are [count*R] scratch.  nc_ns_apply(row_mul = inv, mat_scale = scale)
+// then applies the normalised update.
+hipError_t nc_normuon_stats(const float* X, int64_t x_stride, int R, int C, int transpose,
+                            int count, float* v2, float beta2, float* vm, float* q, float* inv,
+                            float* scale, hipStream_t st);

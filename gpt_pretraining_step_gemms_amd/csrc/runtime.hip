@@ -62,11 +62,12 @@ struct nc_ctx {
   int64_t S, n_block, n_total;
   std::vector<ParamInfo> params;
   // parameter arena byte offsets
-  size_t oP, oG, oM, oAm, oAv, oSh, oTab, param_bytes;
+  size_t oP, oG, oM, oAm, oAv, oSh, oTab, oV2, param_bytes;
   // activation arena byte offsets
   std::vector<LayerAct> la;
   size_t xf, rf, x, dx, dxT, da, dqkv, dO, Dbuf, dh, z, dz, loss_rows, ws, ws_bytes, emb,
-      nsU, frob, norms, act_bytes;
+      nsU, frob, norms, nm_vm, nm_q, nm_inv, nm_scale, act_bytes;
+  int64_t nm_rows = 0;   // NorMuon: rows of all block matrices (4L d + L F + L d)
   // Newton-Schulz buffers per group (0: 4L square [d,d], 1: 2L wide [d,F]): the fp32
   // iterate X (two, ping-pong), A = X X^T, B = b A + c A A, and a copy of each in the
   // activation type for the matrix cores.
@@ -136,6 +137,11 @@ nc_status validate(const nc_model_config* m, const nc_optim_config* o, std::stri
   }
   if (!(m->norm_eps >= 0.f) || !(m->rope_base > 0.f)) { why = "eps/base"; return NC_ERR_INVALID_ARG; }
   if (o->ns_steps < 0 || o->ns_steps > 8) { why = "ns_steps in [0, 8]"; return NC_ERR_INVALID_ARG; }
+  if (o->normuon != 0 && o->normuon != 1) { why = "normuon is 0 or 1"; return NC_ERR_INVALID_ARG; }
+  if (o->normuon && !(o->normuon_beta2 >= 0.f && o->normuon_beta2 < 1.f)) {
+    why = "normuon_beta2 in [0, 1)";
+    return NC_ERR_INVALID_ARG;
+  }
   const int64_t n_tok = (int64_t)m->max_micro_batch * m->seq_len;
   if (n_tok > (int64_t)1 << 30) { why = "micro-batch too large"; return NC_ERR_UNSUPPORTED; }
   return NC_OK;
@@ -171,6 +177,8 @@ void plan(nc_ctx* c) {
   c->oAv = p.take(2ULL * V * d * 4);
   c->oSh = c->dt ? p.take((c->n_block + (size_t)V * d) * 2) : 0;
   c->oTab = p.take(2ULL * T * 64 * 4);
+  c->nm_rows = c->ocfg.normuon ? (int64_t)L * (5LL * d + F) : 0;
+  c->oV2 = c->nm_rows ? p.take((size_t)c->nm_rows * 4) : 0;
   c->param_bytes = p.cur;
 
   const size_t N = (size_t)c->Nmax;
@@ -236,6 +244,12 @@ void plan(nc_ctx* c) {
   c->nsU = c->ocfg.muon_nesterov ? a.take((size_t)c->n_block * 4) : 0;
   c->frob = a.take((size_t)6 * std::max(L, 1) * 256 * 4);
   c->norms = a.take((size_t)6 * std::max(L, 1) * 4);
+  if (c->nm_rows) {
+    c->nm_vm = a.take((size_t)c->nm_rows * 4);
+    c->nm_q = a.take((size_t)c->nm_rows * 4);
+    c->nm_inv = a.take((size_t)c->nm_rows * 4);
+    c->nm_scale = a.take((size_t)6 * L * 4);
+  }
   c->act_bytes = a.cur;
 }
 
@@ -406,6 +420,8 @@ nc_status nc_bind(nc_ctx* ctx, void* d_param_arena, size_t param_bytes, void* d_
   NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oM), 0.f, ctx->n_block, ctx->st), "zero momentum");
   NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oAm), 0.f, 2ULL * ctx->V * ctx->d, ctx->st), "zero m");
   NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oAv), 0.f, 2ULL * ctx->V * ctx->d, ctx->st), "zero v");
+  if (ctx->nm_rows)
+    NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oV2), 0.f, ctx->nm_rows, ctx->st), "zero normuon v2");
   ctx->step = 0;
   NC_TRY(hipStreamSynchronize(ctx->st), "bind sync");
   ctx->bound = true;
@@ -430,6 +446,8 @@ nc_status nc_init_params(nc_ctx* ctx, uint64_t seed, float std) {
   NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oM), 0.f, ctx->n_block, ctx->st), "zero momentum");
   NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oAm), 0.f, 2ULL * ctx->V * ctx->d, ctx->st), "zero m");
   NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oAv), 0.f, 2ULL * ctx->V * ctx->d, ctx->st), "zero v");
+  if (ctx->nm_rows)
+    NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oV2), 0.f, ctx->nm_rows, ctx->st), "zero normuon v2");
   ctx->step = 0;
   return refresh_shadows(ctx);
 }
@@ -641,12 +659,34 @@ nc_status nc_optimizer_step(nc_ctx* ctx, float lr_mult) {
   if (s != NC_OK) return s;
   const float lr = o.muon_lr * lr_mult;
   char* sh = dt ? ctx->pa + ctx->oSh : nullptr;
-  NC_TRY(nc_ns_apply(Pm, sq, d, d, 4 * L, A<float>(ctx, xs), dd, 0, lr, o.muon_wd, sh, st),
-         "apply sq");
-  NC_TRY(nc_ns_apply(Pm + o1, one, F, d, L, A<float>(ctx, xr), dF, 1, lr, o.muon_wd,
+  // NorMuon (optional): per-row statistics of each orthogonalised update, in the
+  // orientation of W (W1's update is held transposed); rows of the three groups
+  // follow each other in v2 and the scratch arrays
+  const float* rm[3] = {nullptr, nullptr, nullptr};
+  const float* ms[3] = {nullptr, nullptr, nullptr};
+  if (ctx->nm_rows) {
+    float* v2 = P<float>(ctx, ctx->oV2);
+    float* vm = A<float>(ctx, ctx->nm_vm);
+    float* qv = A<float>(ctx, ctx->nm_q);
+    float* inv = A<float>(ctx, ctx->nm_inv);
+    float* scl = A<float>(ctx, ctx->nm_scale);
+    const float b2 = o.normuon_beta2;
+    const int64_t r1 = 4LL * L * d, r2 = r1 + (int64_t)L * F;   // row offsets of W1, W2
+    NC_TRY(nc_normuon_stats(A<float>(ctx, xs), dd, d, d, 0, 4 * L, v2, b2, vm, qv, inv, scl, st),
+           "normuon sq");
+    NC_TRY(nc_normuon_stats(A<float>(ctx, xr), dF, F, d, 1, L, v2 + r1, b2, vm + r1, qv + r1,
+                            inv + r1, scl + 4 * L, st), "normuon W1");
+    NC_TRY(nc_normuon_stats(A<float>(ctx, xr) + w2x, dF, d, F, 0, L, v2 + r2, b2, vm + r2,
+                            qv + r2, inv + r2, scl + 5 * L, st), "normuon W2");
+    rm[0] = inv; rm[1] = inv + r1; rm[2] = inv + r2;
+    ms[0] = scl; ms[1] = scl + 4 * L; ms[2] = scl + 5 * L;
+  }
+  NC_TRY(nc_ns_apply(Pm, sq, d, d, 4 * L, A<float>(ctx, xs), dd, 0, lr, o.muon_wd, rm[0], ms[0],
+                     sh, st), "apply sq");
+  NC_TRY(nc_ns_apply(Pm + o1, one, F, d, L, A<float>(ctx, xr), dF, 1, lr, o.muon_wd, rm[1], ms[1],
                      sh ? sh + o1 * 2 : nullptr, st), "apply W1");
-  NC_TRY(nc_ns_apply(Pm + o2, one, d, F, L, A<float>(ctx, xr) + w2x, dF, 0, lr, o.muon_wd,
-                     sh ? sh + o2 * 2 : nullptr, st), "apply W2");
+  NC_TRY(nc_ns_apply(Pm + o2, one, d, F, L, A<float>(ctx, xr) + w2x, dF, 0, lr, o.muon_wd, rm[2],
+                     ms[2], sh ? sh + o2 * 2 : nullptr, st), "apply W2");
   return NC_OK;
 }
 

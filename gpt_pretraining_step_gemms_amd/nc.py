@@ -45,7 +45,8 @@ class OptimCfgC(ctypes.Structure):
                 ("ns_coeffs", (ctypes.c_float * 3) * 8),
                 ("adam_lr_embed", ctypes.c_float), ("adam_lr_head", ctypes.c_float),
                 ("adam_beta1", ctypes.c_float), ("adam_beta2", ctypes.c_float),
-                ("adam_eps", ctypes.c_float), ("adam_wd", ctypes.c_float)]
+                ("adam_eps", ctypes.c_float), ("adam_wd", ctypes.c_float),
+                ("normuon", ctypes.c_int32), ("normuon_beta2", ctypes.c_float)]
 
 
 class ParamInfoC(ctypes.Structure):
@@ -124,6 +125,7 @@ def optim_cfg_c(o: OptimConfig):
         c.ns_coeffs[i][0], c.ns_coeffs[i][1], c.ns_coeffs[i][2] = a, b, cc
     c.adam_lr_embed, c.adam_lr_head = o.adam_lr_embed, o.adam_lr_head
     c.adam_beta1, c.adam_beta2, c.adam_eps, c.adam_wd = o.adam_beta1, o.adam_beta2, o.adam_eps, o.adam_wd
+    c.normuon, c.normuon_beta2 = int(bool(o.normuon)), o.normuon_beta2
     return c
 
 

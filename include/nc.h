@@ -70,12 +70,23 @@ typedef struct {
  * for i < ns_steps: A = X X^T, B = b_i A + c_i A A, X = a_i X + B X (on the
  * short side); W <- W (1 - lr wd) - lr X.  AdamW (E, Wh): decoupled, bias
  * corrected, with the given betas, eps, weight decay and per-group LR.  The
- * coefficient table is data: any (a_i, b_i, c_i) rows may be given. */
+ * coefficient table is data: any (a_i, b_i, c_i) rows may be given.
+ * normuon = 1 adds NorMuon's per-neuron normalisation after Newton-Schulz
+ * (apidog.com, "2. Pengoptimal Muon (nanochat/optim.py)", variance
+ * reduction; the page's fragment is incomplete and is read as follows): per
+ * output row r of W [out, in], vm_r = mean over the row of X^2 and a second
+ * moment v2_r <- normuon_beta2 v2_r + (1 - normuon_beta2) vm_r (zero after
+ * nc_bind / nc_init_params); row r of X is divided by sqrt(max(v2_r, 1e-10))
+ * and the whole update rescaled by sqrt(sum vm) / max(sqrt(sum of the new
+ * rows' mean squares), 1e-10), so W <- W (1 - lr wd) - lr X'.  normuon_beta2
+ * in [0, 1); both fields are ignored when normuon = 0. */
 typedef struct {
   float muon_lr, muon_momentum, muon_wd, ns_eps;
   int32_t ns_steps, muon_nesterov;
   float ns_coeffs[8][3];
   float adam_lr_embed, adam_lr_head, adam_beta1, adam_beta2, adam_eps, adam_wd;
+  int32_t normuon;
+  float normuon_beta2;
 } nc_optim_config;
 
 typedef struct nc_ctx nc_ctx;

@@ -182,3 +182,16 @@ def test_attention_windows_set_and_counted_in_flops():
     with pytest.raises(ValueError):
         sliding_windows(4, 64, "SXL")
     lib.nc_destroy(ctx)
+
+
+def test_normuon_options_validated_and_planned():
+    from dataclasses import replace as dc_replace
+    base = OptimConfig()
+    pb0, _ = nc.plan(TINY, base)
+    pb1, _ = nc.plan(TINY, dc_replace(base, normuon=True))
+    L, d, F = TINY.n_layer, TINY.d_model, TINY.d_ff
+    assert pb1 >= pb0 + L * (5 * d + F) * 4          # one second-moment value per block row
+    for beta2 in (-0.1, 1.0, float("nan")):
+        with pytest.raises(nc.NcError):
+            nc.plan(TINY, dc_replace(base, normuon=True, normuon_beta2=beta2))
+    nc.plan(TINY, dc_replace(base, normuon=False, normuon_beta2=5.0))   # ignored when off

@@ -116,6 +116,38 @@ def test_constant_quintic_schedule_full_step(name):
     check_step(cfg, B, seed=21, ocfg=OptimConfig(ns_coeffs=tuple(NS_QUINTIC_JORDAN)))
 
 
+@pytest.mark.parametrize("name", ["tiny", "small", "d12"])
+def test_normuon_two_steps(name):
+    """Two full steps with NorMuon's per-neuron normalisation: the second one
+    exercises the second-moment state the first one left."""
+    cfg = {"tiny": TINY, "small": SMALL_BF16, "d12": with_batch(D12, micro_batch=1)}[name]
+    B = {"tiny": 4, "small": 2}.get(name, 1)
+    tol_l, tol_c, tol_r = TOL[cfg.dtype]
+    ocfg = OptimConfig(normuon=True)
+    m, params, tok, tgt = setup(cfg, B, 31, ocfg)
+    hp = ocfg.as_dict()
+    cur = {n: p.astype(np.float64) for n, p in params.items()}
+    state = {}
+    for step in (1, 2):
+        print(f"[normuon] {cfg.name} step {step}", flush=True)
+        _, grads = run_gpu(m, tok, tgt)
+        m.optimizer_step()
+        torch.cuda.synchronize()
+        new_o, state = oracle.train_step(cur, {n: g.astype(np.float64) for n, g in grads.items()},
+                                         state, step, hp)
+        after = {n: m.get(n).astype(np.float64) for n in params}
+        worst = []
+        for n in params:
+            dW, dW_o = after[n] - cur[n], new_o[n] - cur[n]
+            c, r = cosine(dW, dW_o), max_rel(dW, dW_o)
+            worst.append((c, r, n))
+            assert c >= tol_c and r <= tol_r, ("update", step, n, c, r)
+        print(f"[normuon] step {step}: worst update cos {min(worst)[0]:.6f} "
+              f"max-rel {max(w[1] for w in worst):.3e}", flush=True)
+        cur = after
+    m.close()
+
+
 def test_d12_shape_one_row():
     check_step(with_batch(D12, micro_batch=1), B=1, seed=7)
 
