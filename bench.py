@@ -75,22 +75,26 @@ def roofline_gemm(cfg, iters):
     return {"kernel": "gemm_bf16_pipe_kernel<KCont, KCont> (MLP up + ReLU^2 epilogue)",
             "shape": [M, N, K], "avg_launch_us": sec * 1e6,
             "bound": "mfma", "achieved": flops / sec / 1e12, "peak": PEAK_BF16 / 1e12,
-            "unit": "TFLOP/s", "frac": flops / sec / PEAK_BF16, "traffic": measured_traffic()}
+            "unit": "TFLOP/s", "frac": flops / sec / PEAK_BF16,
+            "traffic": measured_traffic(2 * (M * K + N * K + M * N))}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_mlp_up_relu2_d20_traffic.txt")
 GEMM_SOURCE = os.path.join(ROOT, "gpt_pretraining_step_gemms_amd", "csrc", "gemm.hip")
 
 
-def measured_traffic():
+def measured_traffic(algorithmic_bytes):
     """HBM bytes per launch of the roofline GEMM from the committed counter
     summary (FETCH_SIZE + WRITE_SIZE, scaled by a copy kernel's readings), or
-    None when the GEMM source has changed since the counters were taken."""
+    None when the GEMM source has changed since the counters were taken or
+    the counters belong to another shape (their algorithmic bytes differ)."""
     import hashlib
     try:
         fields = dict(line.split(":", 1) for line in open(TRAFFIC_FILE) if ":" in line)
         sha = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
         if fields["gemm.hip sha256"].strip() != sha:
+            return None
+        if int(fields["algorithmic bytes per launch"]) != algorithmic_bytes:
             return None
         return float(fields["hbm bytes per launch"])
     except (OSError, KeyError, ValueError):
