@@ -37,6 +37,11 @@ Readings where the pages are silent:
   flash-attention window with nothing on the right).  cfg["windows"] holds
   one entry per layer, None for the plain causal mask; without the key every
   layer is plain causal.  The pages print no window size.
+* Grouped-query attention ([APIDOG] "1. Model GPT (nanochat/gpt.py)" lists
+  fewer key/value heads than query heads, without a ratio): cfg["n_kv_head"]
+  key/value heads (default n_head), Wk and Wv [n_kv_head * hd, d]; query
+  head h reads key/value head h // (n_head / n_kv_head), so consecutive query
+  heads share one, and a key/value head's gradient sums over its query heads.
 * Loss: natural log, mean over every position, no ignore index.
 """
 
@@ -135,12 +140,17 @@ def _layer_names(i):
     return [f"{i}.Wq", f"{i}.Wk", f"{i}.Wv", f"{i}.Wo", f"{i}.W1", f"{i}.W2"]
 
 
+def n_kv_heads(cfg):
+    return cfg.get("n_kv_head") or cfg["n_head"]
+
+
 def param_shapes(cfg):
     """Name -> shape of every parameter ([out, in] like a bias-free Linear)."""
     d, F, V = cfg["d_model"], cfg["d_ff"], cfg["vocab"]
+    dk = n_kv_heads(cfg) * cfg["head_dim"]
     shapes = {"E": (V, d)}
     for i in range(cfg["n_layer"]):
-        for n, s in zip(_layer_names(i), [(d, d)] * 4 + [(F, d), (d, F)]):
+        for n, s in zip(_layer_names(i), [(d, d), (dk, d), (dk, d), (d, d), (F, d), (d, F)]):
             shapes[n] = s
     shapes["Wh"] = (V, d)
     return shapes
@@ -168,6 +178,19 @@ def layer_windows(cfg):
     return list(w)
 
 
+def _repeat_kv(u, group):
+    """[B, Hkv, T, hd] -> [B, Hkv * group, T, hd]: query head h gets key/value
+    head h // group."""
+    return np.repeat(u, group, axis=1)
+
+
+def _sum_groups(u, group):
+    """[B, Hkv * group, T, hd] -> [B, Hkv, T, hd]: sum over each key/value
+    head's query heads (the transpose of _repeat_kv)."""
+    B, H, T, hd = u.shape
+    return u.reshape(B, H // group, group, T, hd).sum(axis=2)
+
+
 def forward(params, tokens, targets, cfg, keep_cache=True):
     """Loss of one micro-batch.  tokens, targets: int [B, T].
 
@@ -175,6 +198,8 @@ def forward(params, tokens, targets, cfg, keep_cache=True):
     """
     eps = cfg["norm_eps"]
     H = cfg["n_head"]
+    Hkv = n_kv_heads(cfg)
+    group = H // Hkv
     hd = cfg["head_dim"]
     tokens = np.asarray(tokens)
     B, T = tokens.shape
@@ -188,13 +213,13 @@ def forward(params, tokens, targets, cfg, keep_cache=True):
         Wq, Wk, Wv, Wo, W1, W2 = (P[n] for n in _layer_names(i))
         a, r1 = rmsnorm(x, eps)
         q = _split_heads(a @ Wq.T, H)
-        k = _split_heads(a @ Wk.T, H)
-        v = _split_heads(a @ Wv.T, H)
+        k = _split_heads(a @ Wk.T, Hkv)
+        v = _split_heads(a @ Wv.T, Hkv)
         qn, rq = rmsnorm(q, eps)
         kn, rk = rmsnorm(k, eps)
         qr = rope(qn, cos, sin)
         kr = rope(kn, cos, sin)
-        o_h, _ = causal_attention(qr, kr, v, windows[i])
+        o_h, _ = causal_attention(qr, _repeat_kv(kr, group), _repeat_kv(v, group), windows[i])
         o = _merge_heads(o_h)
         x = x + o @ Wo.T
         m, r2 = rmsnorm(x, eps)
@@ -237,6 +262,7 @@ def loss_and_grads(params, tokens, targets, cfg, grad_scale=1.0):
     n_tok = B * T
     cos, sin = c["cos"], c["sin"]
     windows = layer_windows(cfg)
+    group = cfg["n_head"] // n_kv_heads(cfg)
     grads = {}
 
     # cross-entropy: dz = (softmax(z) - onehot(y)) / (B*T)
@@ -261,7 +287,9 @@ def loss_and_grads(params, tokens, targets, cfg, grad_scale=1.0):
         # attention: x += o Wo^T
         grads[nWo] = _sum_outer(dx, L["o"])
         do = _split_heads(dx @ P[nWo], cfg["n_head"])
-        dqr, dkr, dv = causal_attention_backward(L["qr"], L["kr"], L["v"], do, windows[i])
+        dqr, dkr, dv = causal_attention_backward(L["qr"], _repeat_kv(L["kr"], group),
+                                                 _repeat_kv(L["v"], group), do, windows[i])
+        dkr, dv = _sum_groups(dkr, group), _sum_groups(dv, group)
         dq = rmsnorm_backward(rope_inverse(dqr, cos, sin), L["qn"], L["rq"])
         dk = rmsnorm_backward(rope_inverse(dkr, cos, sin), L["kn"], L["rk"])
         dq, dk, dv = _merge_heads(dq), _merge_heads(dk), _merge_heads(dv)

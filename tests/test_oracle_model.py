@@ -255,6 +255,35 @@ def test_fd_gradients_sliding_window_layers():
     _fd_check(cfg, B=2, std=0.3, max_coords=40, seed=7)
 
 
+def test_fd_gradients_grouped_query_attention():
+    cfg = micro_cfg(L=2, d=32, H=4, V=32, T=8)      # head dim 8, 4 query heads
+    cfg["n_kv_head"] = 2
+    _fd_check(cfg, B=2, std=0.3, max_coords=40, seed=8)
+
+
+def test_grouped_query_attention_equals_heads_with_copied_key_value_weights():
+    # GQA with Wk, Wv = the MHA model whose key/value weight rows are repeated
+    # per group: same loss; the GQA gradient of Wk (Wv) is the MHA gradient
+    # summed over the copies
+    H, Hkv, hd = 4, 2, 8
+    g = H // Hkv
+    cfg = micro_cfg(L=1, d=H * hd, H=H, V=24, T=7)
+    gcfg = dict(cfg, n_kv_head=Hkv)
+    pg, tok, tgt = make(gcfg, B=2, seed=4, std=0.3)
+    pm = dict(pg)
+    for n in ("0.Wk", "0.Wv"):
+        W = pg[n].reshape(Hkv, hd, -1)
+        pm[n] = np.repeat(W, g, axis=0).reshape(H * hd, -1)
+    lg, gg = oracle.loss_and_grads(pg, tok, tgt, gcfg)
+    lm, gm = oracle.loss_and_grads(pm, tok, tgt, cfg)
+    assert lg == pytest.approx(lm, rel=1e-13)
+    for n in ("0.Wk", "0.Wv"):
+        summed = gm[n].reshape(Hkv, g, hd, -1).sum(axis=1).reshape(Hkv * hd, -1)
+        np.testing.assert_allclose(gg[n], summed, rtol=1e-11, atol=1e-14)
+    for n in ("0.Wq", "0.Wo", "0.W1", "0.W2", "E", "Wh"):
+        np.testing.assert_allclose(gg[n], gm[n], rtol=1e-11, atol=1e-14)
+
+
 def test_fd_gradients_tiny_shape_sampled():
     # the tiny configuration's shapes (d 128, one head of 128, vocab 512) at T = 16
     cfg = micro_cfg(L=2, d=128, H=1, V=512, T=16, F=512)
