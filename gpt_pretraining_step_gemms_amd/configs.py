@@ -40,11 +40,17 @@ class ModelConfig:
     rope_base: float = 10000.0
     norm_eps: float = 1e-6
     init_std: float = 0.02
+    n_kv_head: int = 0    # key/value heads for grouped-query attention (0: n_head)
+
+    @property
+    def kv_heads(self):
+        return self.n_kv_head or self.n_head
 
     def as_oracle_cfg(self):
         return dict(n_layer=self.n_layer, d_model=self.d_model, n_head=self.n_head,
                     head_dim=self.head_dim, d_ff=self.d_ff, vocab=self.vocab,
-                    seq_len=self.seq_len, rope_base=self.rope_base, norm_eps=self.norm_eps)
+                    seq_len=self.seq_len, rope_base=self.rope_base, norm_eps=self.norm_eps,
+                    n_kv_head=self.kv_heads)
 
     @property
     def tokens_per_step(self):
@@ -52,7 +58,8 @@ class ModelConfig:
 
     def n_params(self):
         d, F, V, L = self.d_model, self.d_ff, self.vocab, self.n_layer
-        return L * (4 * d * d + 2 * d * F) + 2 * V * d
+        dk = self.kv_heads * self.head_dim
+        return L * (2 * d * d + 2 * dk * d + 2 * d * F) + 2 * V * d
 
 
 @dataclass(frozen=True)

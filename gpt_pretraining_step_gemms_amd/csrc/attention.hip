@@ -21,6 +21,11 @@
 // fp32 path (tiny configuration): one wave per query (or key) row, plain
 // loops over the causal range.
 //
+// Grouped-query attention: H query heads share Hkv key/value heads in groups
+// of G = H / Hkv consecutive heads (query head h reads key/value head h / G).
+// The forward and dQ kernels run per query head; a dK/dV workgroup owns keys of
+// one key/value head and walks the query tiles of its G query heads in turn.
+//
 // Sliding window: with a window w, query t sees keys t - w .. t (the causal
 // mask plus a left edge).  Every kernel takes it as `win`, with win = T for
 // the plain causal mask; tiles wholly outside the band are never loaded and
@@ -181,13 +186,14 @@ NC_DEV bf16x8 fa_frag_vt(const bf16* tile, int row_base, int col_base, int lane)
 NC_DEV void attn_fwd_block(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, bf16* __restrict__ o, int64_t ldo, float* __restrict__ lse, int T, int H,
-    int win, float scale_log2, int qb, int bh, bf16* st0, bf16* st1) {
+    int G, int win, float scale_log2, int qb, int bh, bf16* st0, bf16* st1) {
   constexpr int KT = 64 * 128;                    // one 64 x 128 tile
   const int b = bh / H, h = bh % H;
   const int64_t base = (int64_t)b * T * ld + h * 128;
+  const int64_t kvbase = (int64_t)b * T * ld + (h / G) * 128;
   const bf16* qg = q + base;
-  const bf16* kg = k + base;
-  const bf16* vg = v + base;
+  const bf16* kg = k + kvbase;
+  const bf16* vg = v + kvbase;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, l32 = lane & 31;
@@ -330,19 +336,26 @@ NC_DEV void attn_fwd_block(
 // loads, double-buffered; Q^T and dO^T fragments come from transpose reads.
 constexpr int kDkvStage = 2 * 64 * 128 + 256;     // Q | dO | lse[64] D[64] (fp32)
 
-// one 128-key block kblk of head bh; st0 / st1: stages of kDkvStage elements
+// one 128-key block kblk of key/value head bhk; st0 / st1: stages of kDkvStage
+// elements.  kGrouped: G > 1 query heads per key/value head, walked in turn (a
+// separate instantiation keeps the plain path's registers as they were).
+template <bool kGrouped>
 NC_DEV void attn_bwd_dkv_block(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, const bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ lse,
     const float* __restrict__ Dv, bf16* __restrict__ dk, bf16* __restrict__ dv, int64_t ldd,
-    int T, int H, int win, float scale_log2, float scale, int kblk, int bh, bf16* st0,
+    int T, int H, int G, int win, float scale_log2, float scale, int kblk, int bhk, bf16* st0,
     bf16* st1) {
   constexpr int KT = 64 * 128;
-  const int b = bh / H, h = bh % H;
-  const int64_t base = (int64_t)b * T * ld + h * 128;
-  const int64_t obase = (int64_t)b * T * ldo + h * 128;
-  const float* lse_bh = lse + ((int64_t)b * H + h) * T;
-  const float* D_bh = Dv + ((int64_t)b * H + h) * T;
+  const int Hkv = kGrouped ? H / G : H;
+  const int b = bhk / Hkv, hk = bhk % Hkv;
+  const int64_t kvbase = (int64_t)b * T * ld + hk * 128;
+  // the query head being walked: hk itself, or each head of the group in turn
+  const int h0 = kGrouped ? hk * G : hk;
+  int64_t base = (int64_t)b * T * ld + h0 * 128;
+  int64_t obase = (int64_t)b * T * ldo + h0 * 128;
+  const float* lse_bh = lse + ((int64_t)b * H + h0) * T;
+  const float* D_bh = Dv + ((int64_t)b * H + h0) * T;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, l32 = lane & 31;
@@ -352,8 +365,8 @@ NC_DEV void attn_bwd_dkv_block(
   bf16x8 kf[8], vf[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
-    kf[s] = *reinterpret_cast<const bf16x8*>(k + base + (int64_t)mykey * ld + s * 16 + half * 8);
-    vf[s] = *reinterpret_cast<const bf16x8*>(v + base + (int64_t)mykey * ld + s * 16 + half * 8);
+    kf[s] = *reinterpret_cast<const bf16x8*>(k + kvbase + (int64_t)mykey * ld + s * 16 + half * 8);
+    vf[s] = *reinterpret_cast<const bf16x8*>(v + kvbase + (int64_t)mykey * ld + s * 16 + half * 8);
   }
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
@@ -441,10 +454,27 @@ NC_DEV void attn_bwd_dkv_block(
     }
   };
 
-  issue(qt0, st0);
-  for (int qt = qt0; qt < nqt; qt += 2) {
-    step(qt, st0, st1);
-    if (qt + 1 < nqt) step(qt + 1, st1, st0);
+  auto walk = [&]() {
+    issue(qt0, st0);
+    for (int qt = qt0; qt < nqt; qt += 2) {
+      step(qt, st0, st1);
+      if (qt + 1 < nqt) step(qt + 1, st1, st0);
+    }
+  };
+  if constexpr (kGrouped) {
+    for (int g = 0; g < G; ++g) {
+      if (g) {
+        const int h = h0 + g;
+        base = (int64_t)b * T * ld + h * 128;
+        obase = (int64_t)b * T * ldo + h * 128;
+        lse_bh = lse + ((int64_t)b * H + h) * T;
+        D_bh = Dv + ((int64_t)b * H + h) * T;
+        __syncthreads();                           // the previous head's last tile is read
+      }
+      walk();
+    }
+  } else {
+    walk();
   }
 
   // C[key][d]: lane holds column d = db*32 + l32, rows key = 8*(e/4) + 4*half + e%4
@@ -453,7 +483,7 @@ NC_DEV void attn_bwd_dkv_block(
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int key = k0w + (e >> 2) * 8 + half * 4 + (e & 3);
-      const int64_t off = ((int64_t)b * T + key) * ldd + h * 128 + db * 32 + l32;
+      const int64_t off = ((int64_t)b * T + key) * ldd + hk * 128 + db * 32 + l32;
       dk[off] = (bf16)(dkacc[db][e] * scale);
       dv[off] = (bf16)dvacc[db][e];
     }
@@ -467,14 +497,15 @@ NC_DEV void attn_bwd_dkv_block(
 NC_DEV void attn_bwd_dq_block(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, const bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ lse,
-    const float* __restrict__ Dv, bf16* __restrict__ dq, int64_t ldd, int T, int H, int win,
-    float scale_log2, float scale, int qb, int bh, bf16* st0, bf16* st1) {
+    const float* __restrict__ Dv, bf16* __restrict__ dq, int64_t ldd, int T, int H, int G,
+    int win, float scale_log2, float scale, int qb, int bh, bf16* st0, bf16* st1) {
   constexpr int KT = 64 * 128;
   const int b = bh / H, h = bh % H;
   const int64_t base = (int64_t)b * T * ld + h * 128;
   const int64_t obase = (int64_t)b * T * ldo + h * 128;
-  const bf16* kg = k + base;
-  const bf16* vg = v + base;
+  const int64_t kvbase = (int64_t)b * T * ld + (h / G) * 128;
+  const bf16* kg = k + kvbase;
+  const bf16* vg = v + kvbase;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, l32 = lane & 31;
@@ -613,47 +644,49 @@ inline int attn_jobs_per_head(int T, int win) { return win >= T ? (T / 128 + 1) 
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, bf16* __restrict__ o, int64_t ldo, float* __restrict__ lse, int T, int H,
-    int win, float scale_log2) {
+    int G, int win, float scale_log2) {
   __shared__ __attribute__((aligned(1024))) bf16 st0[2 * 64 * 128];   // K | V of even tiles
   __shared__ __attribute__((aligned(1024))) bf16 st1[2 * 64 * 128];   // K | V of odd tiles
   const BlockJob jb = block_job(T / 128, win >= T, true);
-  attn_fwd_block(q, k, v, ld, o, ldo, lse, T, H, win, scale_log2, jb.first, jb.bh, st0, st1);
+  attn_fwd_block(q, k, v, ld, o, ldo, lse, T, H, G, win, scale_log2, jb.first, jb.bh, st0, st1);
   if (jb.second < 0) return;
   __syncthreads();                                 // the first block's O staging is read
-  attn_fwd_block(q, k, v, ld, o, ldo, lse, T, H, win, scale_log2, jb.second, jb.bh, st0, st1);
+  attn_fwd_block(q, k, v, ld, o, ldo, lse, T, H, G, win, scale_log2, jb.second, jb.bh, st0,
+                 st1);
 }
 
+template <bool kGrouped>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, const bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ lse,
     const float* __restrict__ Dv, bf16* __restrict__ dk, bf16* __restrict__ dv, int64_t ldd,
-    int T, int H, int win, float scale_log2, float scale) {
+    int T, int H, int G, int win, float scale_log2, float scale) {
   __shared__ __attribute__((aligned(1024))) bf16 st0[kDkvStage];
   __shared__ __attribute__((aligned(1024))) bf16 st1[kDkvStage];
   // key block kblk walks up to T/64 - 2 kblk query tiles: the low blocks are the long ones
   const BlockJob jb = block_job(T / 128, win >= T, false);
   if (jb.second >= 0) {
-    attn_bwd_dkv_block(q, k, v, ld, dO, ldo, lse, Dv, dk, dv, ldd, T, H, win, scale_log2, scale,
-                       jb.second, jb.bh, st0, st1);
+    attn_bwd_dkv_block<kGrouped>(q, k, v, ld, dO, ldo, lse, Dv, dk, dv, ldd, T, H, G, win,
+                                 scale_log2, scale, jb.second, jb.bh, st0, st1);
     __syncthreads();
   }
-  attn_bwd_dkv_block(q, k, v, ld, dO, ldo, lse, Dv, dk, dv, ldd, T, H, win, scale_log2, scale,
-                     jb.first, jb.bh, st0, st1);
+  attn_bwd_dkv_block<kGrouped>(q, k, v, ld, dO, ldo, lse, Dv, dk, dv, ldd, T, H, G, win,
+                               scale_log2, scale, jb.first, jb.bh, st0, st1);
 }
 
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, const bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ lse,
-    const float* __restrict__ Dv, bf16* __restrict__ dq, int64_t ldd, int T, int H, int win,
-    float scale_log2, float scale) {
+    const float* __restrict__ Dv, bf16* __restrict__ dq, int64_t ldd, int T, int H, int G,
+    int win, float scale_log2, float scale) {
   __shared__ __attribute__((aligned(1024))) bf16 st0[2 * 64 * 128];   // K | V
   __shared__ __attribute__((aligned(1024))) bf16 st1[2 * 64 * 128];
   const BlockJob jb = block_job(T / 128, win >= T, true);
-  attn_bwd_dq_block(q, k, v, ld, dO, ldo, lse, Dv, dq, ldd, T, H, win, scale_log2, scale,
+  attn_bwd_dq_block(q, k, v, ld, dO, ldo, lse, Dv, dq, ldd, T, H, G, win, scale_log2, scale,
                     jb.first, jb.bh, st0, st1);
   if (jb.second < 0) return;
   __syncthreads();
-  attn_bwd_dq_block(q, k, v, ld, dO, ldo, lse, Dv, dq, ldd, T, H, win, scale_log2, scale,
+  attn_bwd_dq_block(q, k, v, ld, dO, ldo, lse, Dv, dq, ldd, T, H, G, win, scale_log2, scale,
                     jb.second, jb.bh, st0, st1);
 }
 
@@ -662,16 +695,17 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
 __global__ void attn_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                     const float* __restrict__ v, int64_t ld,
                                     float* __restrict__ o, int64_t ldo, float* __restrict__ lse,
-                                    int B, int T, int H, int win, float scale) {
+                                    int B, int T, int H, int G, int win, float scale) {
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= B * H * T) return;
   const int lane = threadIdx.x & 63;
   const int t = item % T, bh = item / T, b = bh / H, h = bh % H;
   const int64_t base = (int64_t)b * T * ld + h * 128;
+  const int64_t kvb = (int64_t)b * T * ld + (h / G) * 128;
   const float q1 = q[base + (int64_t)t * ld + lane], q2 = q[base + (int64_t)t * ld + lane + 64];
   float m = -INFINITY, l = 0.f, o1 = 0.f, o2 = 0.f;
   for (int u = max(0, t - win); u <= t; ++u) {
-    const int64_t ku = base + (int64_t)u * ld;
+    const int64_t ku = kvb + (int64_t)u * ld;
     const float s = wave_sum(q1 * k[ku + lane] + q2 * k[ku + lane + 64]) * scale;
     const float mn = fmaxf(m, s);
     const float a = expf(m - mn), p = expf(s - mn);
@@ -691,19 +725,21 @@ __global__ void attn_bwd_dq_f32_kernel(const float* __restrict__ q, const float*
                                        const float* __restrict__ dO, int64_t ldo,
                                        const float* __restrict__ lse,
                                        const float* __restrict__ Dv, float* __restrict__ dq,
-                                       int64_t ldd, int B, int T, int H, int win, float scale) {
+                                       int64_t ldd, int B, int T, int H, int G, int win,
+                                       float scale) {
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= B * H * T) return;
   const int lane = threadIdx.x & 63;
   const int t = item % T, bh = item / T, b = bh / H, h = bh % H;
   const int64_t base = (int64_t)b * T * ld + h * 128;
+  const int64_t kvb = (int64_t)b * T * ld + (h / G) * 128;
   const int64_t ob = ((int64_t)b * T + t) * ldo + h * 128;
   const float q1 = q[base + (int64_t)t * ld + lane], q2 = q[base + (int64_t)t * ld + lane + 64];
   const float g1 = dO[ob + lane], g2 = dO[ob + lane + 64];
   const float L = lse[(int64_t)bh * T + t], Dt = Dv[(int64_t)bh * T + t];
   float a1 = 0.f, a2 = 0.f;
   for (int u = max(0, t - win); u <= t; ++u) {
-    const int64_t ku = base + (int64_t)u * ld;
+    const int64_t ku = kvb + (int64_t)u * ld;
     const float s = wave_sum(q1 * k[ku + lane] + q2 * k[ku + lane + 64]) * scale;
     const float p = expf(s - L);
     const float dp = wave_sum(g1 * v[ku + lane] + g2 * v[ku + lane + 64]);
@@ -716,39 +752,43 @@ __global__ void attn_bwd_dq_f32_kernel(const float* __restrict__ q, const float*
   dq[dd + lane + 64] = a2 * scale;
 }
 
-// one wave per (b, h, u) key row
+// one wave per (b, key/value head, u) key row, summing over the head's G query heads
 __global__ void attn_bwd_dkv_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                         const float* __restrict__ v, int64_t ld,
                                         const float* __restrict__ dO, int64_t ldo,
                                         const float* __restrict__ lse,
                                         const float* __restrict__ Dv, float* __restrict__ dk,
                                         float* __restrict__ dv, int64_t ldd, int B, int T, int H,
-                                        int win, float scale) {
+                                        int G, int win, float scale) {
+  const int Hkv = H / G;
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (item >= B * H * T) return;
+  if (item >= B * Hkv * T) return;
   const int lane = threadIdx.x & 63;
-  const int u = item % T, bh = item / T, b = bh / H, h = bh % H;
-  const int64_t base = (int64_t)b * T * ld + h * 128;
-  const int64_t ku = base + (int64_t)u * ld;
+  const int u = item % T, bhk = item / T, b = bhk / Hkv, hk = bhk % Hkv;
+  const int64_t ku = (int64_t)b * T * ld + hk * 128 + (int64_t)u * ld;
   const float k1 = k[ku + lane], k2 = k[ku + lane + 64];
   const float v1 = v[ku + lane], v2 = v[ku + lane + 64];
   float ak1 = 0.f, ak2 = 0.f, av1 = 0.f, av2 = 0.f;
   const int t_end = min(T - 1, u + win);
-  for (int t = u; t <= t_end; ++t) {
-    const int64_t qt = base + (int64_t)t * ld;
-    const int64_t ot = ((int64_t)b * T + t) * ldo + h * 128;
-    const float q1 = q[qt + lane], q2 = q[qt + lane + 64];
-    const float g1 = dO[ot + lane], g2 = dO[ot + lane + 64];
-    const float s = wave_sum(q1 * k1 + q2 * k2) * scale;
-    const float p = expf(s - lse[(int64_t)bh * T + t]);
-    const float dp = wave_sum(g1 * v1 + g2 * v2);
-    const float ds = p * (dp - Dv[(int64_t)bh * T + t]);
-    av1 += p * g1;
-    av2 += p * g2;
-    ak1 += ds * q1;
-    ak2 += ds * q2;
+  for (int g = 0; g < G; ++g) {
+    const int h = hk * G + g;
+    const int64_t bh = (int64_t)b * H + h;
+    for (int t = u; t <= t_end; ++t) {
+      const int64_t qt = (int64_t)b * T * ld + h * 128 + (int64_t)t * ld;
+      const int64_t ot = ((int64_t)b * T + t) * ldo + h * 128;
+      const float q1 = q[qt + lane], q2 = q[qt + lane + 64];
+      const float g1 = dO[ot + lane], g2 = dO[ot + lane + 64];
+      const float s = wave_sum(q1 * k1 + q2 * k2) * scale;
+      const float p = expf(s - lse[bh * T + t]);
+      const float dp = wave_sum(g1 * v1 + g2 * v2);
+      const float ds = p * (dp - Dv[bh * T + t]);
+      av1 += p * g1;
+      av2 += p * g2;
+      ak1 += ds * q1;
+      ak2 += ds * q2;
+    }
   }
-  const int64_t dd = ((int64_t)b * T + u) * ldd + h * 128;
+  const int64_t dd = ((int64_t)b * T + u) * ldd + hk * 128;
   dk[dd + lane] = ak1 * scale;
   dk[dd + lane + 64] = ak2 * scale;
   dv[dd + lane] = av1;
@@ -758,46 +798,50 @@ __global__ void attn_bwd_dkv_f32_kernel(const float* __restrict__ q, const float
 }  // namespace
 
 hipError_t nc_attn_fwd(int dtype, const void* q, const void* k, const void* v, int64_t ld,
-                       void* o, int64_t ldo, float* lse, int B, int T, int H, int window,
+                       void* o, int64_t ldo, float* lse, int B, int T, int H, int Hkv, int window,
                        hipStream_t st) {
   const float scale = 1.0f / sqrtf(128.f);
   const int win = window < 0 || window > T ? T : window;
+  if (Hkv < 1 || H % Hkv) return hipErrorInvalidValue;
+  const int G = H / Hkv;
   if (dtype) {
     if (T % 128) return hipErrorInvalidValue;
     attn_fwd_kernel<<<B * H * attn_jobs_per_head(T, win), 256, 0, st>>>(
-        (const bf16*)q, (const bf16*)k, (const bf16*)v, ld, (bf16*)o, ldo, lse, T, H, win,
+        (const bf16*)q, (const bf16*)k, (const bf16*)v, ld, (bf16*)o, ldo, lse, T, H, G, win,
         scale * kLog2e);
   } else {
     attn_fwd_f32_kernel<<<ceil_div(B * H * T, 4), 256, 0, st>>>(
-        (const float*)q, (const float*)k, (const float*)v, ld, (float*)o, ldo, lse, B, T, H, win,
-        scale);
+        (const float*)q, (const float*)k, (const float*)v, ld, (float*)o, ldo, lse, B, T, H, G,
+        win, scale);
   }
   return hipGetLastError();
 }
 
 hipError_t nc_attn_bwd(int dtype, const void* q, const void* k, const void* v, int64_t ld,
                        const void* dO, int64_t ldo, const float* lse, const float* D, void* dq,
-                       void* dk, void* dv, int64_t ldd, int B, int T, int H, int window,
+                       void* dk, void* dv, int64_t ldd, int B, int T, int H, int Hkv, int window,
                        hipStream_t st) {
   const float scale = 1.0f / sqrtf(128.f);
   const int win = window < 0 || window > T ? T : window;
+  if (Hkv < 1 || H % Hkv) return hipErrorInvalidValue;
+  const int G = H / Hkv;
   if (dtype) {
     if (T % 128) return hipErrorInvalidValue;
-    const int grid = B * H * attn_jobs_per_head(T, win);
-    attn_bwd_dkv_kernel<<<grid, 256, 0, st>>>((const bf16*)q, (const bf16*)k, (const bf16*)v, ld,
-                                              (const bf16*)dO, ldo, lse, D, (bf16*)dk, (bf16*)dv,
-                                              ldd, T, H, win, scale * kLog2e, scale);
-    attn_bwd_dq_kernel<<<grid, 256, 0, st>>>((const bf16*)q, (const bf16*)k, (const bf16*)v, ld,
-                                             (const bf16*)dO, ldo, lse, D, (bf16*)dq, ldd, T, H,
-                                             win, scale * kLog2e, scale);
+    const int jobs = attn_jobs_per_head(T, win);
+    auto dkv_kernel = G > 1 ? attn_bwd_dkv_kernel<true> : attn_bwd_dkv_kernel<false>;
+    dkv_kernel<<<B * Hkv * jobs, 256, 0, st>>>(
+        (const bf16*)q, (const bf16*)k, (const bf16*)v, ld, (const bf16*)dO, ldo, lse, D,
+        (bf16*)dk, (bf16*)dv, ldd, T, H, G, win, scale * kLog2e, scale);
+    attn_bwd_dq_kernel<<<B * H * jobs, 256, 0, st>>>(
+        (const bf16*)q, (const bf16*)k, (const bf16*)v, ld, (const bf16*)dO, ldo, lse, D,
+        (bf16*)dq, ldd, T, H, G, win, scale * kLog2e, scale);
   } else {
-    const int grid = ceil_div(B * H * T, 4);
-    attn_bwd_dq_f32_kernel<<<grid, 256, 0, st>>>((const float*)q, (const float*)k, (const float*)v,
-                                                 ld, (const float*)dO, ldo, lse, D, (float*)dq, ldd,
-                                                 B, T, H, win, scale);
-    attn_bwd_dkv_f32_kernel<<<grid, 256, 0, st>>>((const float*)q, (const float*)k, (const float*)v,
-                                                  ld, (const float*)dO, ldo, lse, D, (float*)dk,
-                                                  (float*)dv, ldd, B, T, H, win, scale);
+    attn_bwd_dq_f32_kernel<<<ceil_div(B * H * T, 4), 256, 0, st>>>(
+        (const float*)q, (const float*)k, (const float*)v, ld, (const float*)dO, ldo, lse, D,
+        (float*)dq, ldd, B, T, H, G, win, scale);
+    attn_bwd_dkv_f32_kernel<<<ceil_div(B * Hkv * T, 4), 256, 0, st>>>(
+        (const float*)q, (const float*)k, (const float*)v, ld, (const float*)dO, ldo, lse, D,
+        (float*)dk, (float*)dv, ldd, B, T, H, G, win, scale);
   }
   return hipGetLastError();
 }

@@ -249,17 +249,18 @@ __global__ void rmsnorm_bwd_kernel(const float* __restrict__ dy, const T* __rest
 }
 
 // ------------------------------------------------------- QK-norm + rotary
-// One wave per (token, head) of the 2H q/k heads; lane l owns the rotary pair
-// (l, l+64) of the 128-dim head.
+// One wave per (token, head) of the nh = H + Hkv q/k heads (q heads, then k
+// heads, at the start of each qkv row of ld elements); lane l owns the rotary
+// pair (l, l+64) of the 128-dim head.
 template <typename T>
 __global__ void qk_norm_rope_fwd_kernel(T* __restrict__ qkv, float* __restrict__ rqk,
                                         const float* __restrict__ cs, int n_tok, int Tlen,
-                                        int H, float eps) {
+                                        int nh, int64_t ld, float eps) {
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (item >= n_tok * 2 * H) return;
+  if (item >= n_tok * nh) return;
   const int lane = threadIdx.x & 63;
-  const int n = item / (2 * H), j = item % (2 * H);
-  T* p = qkv + (int64_t)n * (3 * H * 128) + j * 128;
+  const int n = item / nh, j = item % nh;
+  T* p = qkv + (int64_t)n * ld + j * 128;
   const float x1 = to_f(p[lane]), x2 = to_f(p[lane + 64]);
   const float rs = 1.0f / sqrtf(wave_sum(x1 * x1 + x2 * x2) / 128.f + eps);
   const int t = n % Tlen;
@@ -274,12 +275,12 @@ template <typename T>
 __global__ void qk_norm_rope_bwd_kernel(T* __restrict__ dqkv, const T* __restrict__ qkv,
                                         const float* __restrict__ rqk,
                                         const float* __restrict__ cs, int n_tok, int Tlen,
-                                        int H) {
+                                        int nh, int64_t ld) {
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (item >= n_tok * 2 * H) return;
+  if (item >= n_tok * nh) return;
   const int lane = threadIdx.x & 63;
-  const int n = item / (2 * H), j = item % (2 * H);
-  const int64_t off = (int64_t)n * (3 * H * 128) + j * 128;
+  const int n = item / nh, j = item % nh;
+  const int64_t off = (int64_t)n * ld + j * 128;
   const int t = n % Tlen;
   const float c = cs[t * 64 + lane], s = cs[Tlen * 64 + t * 64 + lane];
   // normalised pre-rotation vector, recovered by the inverse rotation
@@ -320,13 +321,13 @@ NC_DEV void ld8f(const float* p, float (&x)[8]) {
 
 __global__ __launch_bounds__(256) void qk_norm_rope_fwd_bf16_kernel(
     bf16* __restrict__ qkv, float* __restrict__ rqk, const float* __restrict__ cs, int n_tok,
-    int Tlen, int H, float eps) {
+    int Tlen, int nh, int64_t ld, float eps) {
   const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t item = tid >> 3;
-  if (item >= (int64_t)n_tok * 2 * H) return;
+  if (item >= (int64_t)n_tok * nh) return;
   const int u = threadIdx.x & 7;
-  const int n = (int)(item / (2 * H)), j = (int)(item % (2 * H));
-  bf16* p = qkv + (int64_t)n * (3 * H * 128) + j * 128 + 8 * u;
+  const int n = (int)(item / nh), j = (int)(item % nh);
+  bf16* p = qkv + (int64_t)n * ld + j * 128 + 8 * u;
   float x1[8], x2[8], c[8], sn[8];
   ld8f(p, x1);
   ld8f(p + 64, x2);
@@ -351,13 +352,13 @@ __global__ __launch_bounds__(256) void qk_norm_rope_fwd_bf16_kernel(
 
 __global__ __launch_bounds__(256) void qk_norm_rope_bwd_bf16_kernel(
     bf16* __restrict__ dqkv, const bf16* __restrict__ qkv, const float* __restrict__ rqk,
-    const float* __restrict__ cs, int n_tok, int Tlen, int H) {
+    const float* __restrict__ cs, int n_tok, int Tlen, int nh, int64_t ld) {
   const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t item = tid >> 3;
-  if (item >= (int64_t)n_tok * 2 * H) return;
+  if (item >= (int64_t)n_tok * nh) return;
   const int u = threadIdx.x & 7;
-  const int n = (int)(item / (2 * H)), j = (int)(item % (2 * H));
-  const int64_t off = (int64_t)n * (3 * H * 128) + j * 128 + 8 * u;
+  const int n = (int)(item / nh), j = (int)(item % nh);
+  const int64_t off = (int64_t)n * ld + j * 128 + 8 * u;
   const int t = n % Tlen;
   float c[8], sn[8], o1[8], o2[8], g1[8], g2[8];
   ld8f(cs + t * 64 + 8 * u, c);
@@ -804,29 +805,36 @@ hipError_t nc_rmsnorm_bwd(int dtype, const float* dy, const void* y, const float
 }
 
 hipError_t nc_qk_norm_rope_fwd(int dtype, void* qkv, float* rqk, const float* cs, int n_tok,
-                               int T, int H, float eps, hipStream_t st) {
-  const int g = ceil_div(n_tok * 2 * H, 4);
+                               int T, int H, int Hkv, float eps, hipStream_t st) {
+  const int nh = H + Hkv;
+  const int64_t ld = (int64_t)(H + 2 * Hkv) * 128;
+  const int g = ceil_div(n_tok * nh, 4);
   const bool vec = (reinterpret_cast<uintptr_t>(qkv) & 15) == 0;
   if (dtype && !vec)
-    qk_norm_rope_fwd_kernel<bf16><<<g, 256, 0, st>>>((bf16*)qkv, rqk, cs, n_tok, T, H, eps);
+    qk_norm_rope_fwd_kernel<bf16><<<g, 256, 0, st>>>((bf16*)qkv, rqk, cs, n_tok, T, nh, ld, eps);
   else if (dtype)
-    qk_norm_rope_fwd_bf16_kernel<<<ceil_div(n_tok * 2 * H, 32), 256, 0, st>>>((bf16*)qkv, rqk, cs,
-                                                                            n_tok, T, H, eps);
-  else qk_norm_rope_fwd_kernel<float><<<g, 256, 0, st>>>((float*)qkv, rqk, cs, n_tok, T, H, eps);
+    qk_norm_rope_fwd_bf16_kernel<<<ceil_div(n_tok * nh, 32), 256, 0, st>>>((bf16*)qkv, rqk, cs,
+                                                                         n_tok, T, nh, ld, eps);
+  else
+    qk_norm_rope_fwd_kernel<float><<<g, 256, 0, st>>>((float*)qkv, rqk, cs, n_tok, T, nh, ld, eps);
   return hipGetLastError();
 }
 
 hipError_t nc_qk_norm_rope_bwd(int dtype, void* dqkv, const void* qkv, const float* rqk,
-                               const float* cs, int n_tok, int T, int H, hipStream_t st) {
-  const int g = ceil_div(n_tok * 2 * H, 4);
+                               const float* cs, int n_tok, int T, int H, int Hkv, hipStream_t st) {
+  const int nh = H + Hkv;
+  const int64_t ld = (int64_t)(H + 2 * Hkv) * 128;
+  const int g = ceil_div(n_tok * nh, 4);
   const bool vec = ((reinterpret_cast<uintptr_t>(dqkv) | reinterpret_cast<uintptr_t>(qkv)) & 15) == 0;
   if (dtype && !vec)
-    qk_norm_rope_bwd_kernel<bf16><<<g, 256, 0, st>>>((bf16*)dqkv, (const bf16*)qkv, rqk, cs, n_tok, T, H);
+    qk_norm_rope_bwd_kernel<bf16><<<g, 256, 0, st>>>((bf16*)dqkv, (const bf16*)qkv, rqk, cs, n_tok,
+                                                     T, nh, ld);
   else if (dtype)
-    qk_norm_rope_bwd_bf16_kernel<<<ceil_div(n_tok * 2 * H, 32), 256, 0, st>>>(
-        (bf16*)dqkv, (const bf16*)qkv, rqk, cs, n_tok, T, H);
+    qk_norm_rope_bwd_bf16_kernel<<<ceil_div(n_tok * nh, 32), 256, 0, st>>>(
+        (bf16*)dqkv, (const bf16*)qkv, rqk, cs, n_tok, T, nh, ld);
   else
-    qk_norm_rope_bwd_kernel<float><<<g, 256, 0, st>>>((float*)dqkv, (const float*)qkv, rqk, cs, n_tok, T, H);
+    qk_norm_rope_bwd_kernel<float><<<g, 256, 0, st>>>((float*)dqkv, (const float*)qkv, rqk, cs,
+                                                      n_tok, T, nh, ld);
   return hipGetLastError();
 }
 

@@ -20,24 +20,27 @@ hipError_t nc_rmsnorm_fwd(int dtype, const float* x, void* y, float* r, int rows
 hipError_t nc_rmsnorm_bwd(int dtype, const float* dy, const void* y, const float* r, float* dx,
                           void* dxT, int rows, int d, int accumulate, hipStream_t st);
 
-// ---- QK RMSNorm + rotary (qkv token-major [n_tok, 3*H*128], in place)
+// ---- QK RMSNorm + rotary (qkv token-major [n_tok, (H + 2 Hkv)*128]: H q heads, Hkv k
+// heads, Hkv v heads; in place on the q and k heads; rqk [n_tok, H + Hkv])
 hipError_t nc_qk_norm_rope_fwd(int dtype, void* qkv, float* rqk, const float* cos_sin,
-                               int n_tok, int T, int H, float eps, hipStream_t st);
+                               int n_tok, int T, int H, int Hkv, float eps, hipStream_t st);
 hipError_t nc_qk_norm_rope_bwd(int dtype, void* dqkv, const void* qkv, const float* rqk,
-                               const float* cos_sin, int n_tok, int T, int H, hipStream_t st);
+                               const float* cos_sin, int n_tok, int T, int H, int Hkv,
+                               hipStream_t st);
 
 // ---- attention on token-major q/k/v (row stride ld_qkv), head dim 128; query t
-// sees keys max(0, t - window) .. t (window < 0: keys 0 .. t)
+// sees keys max(0, t - window) .. t (window < 0: keys 0 .. t); H query heads,
+// Hkv key/value heads (H % Hkv == 0), query head h reads key/value head h / (H / Hkv)
 hipError_t nc_attn_fwd(int dtype, const void* q, const void* k, const void* v, int64_t ld_qkv,
-                       void* o, int64_t ld_o, float* lse, int B, int T, int H, int window,
-                       hipStream_t st);
+                       void* o, int64_t ld_o, float* lse, int B, int T, int H, int Hkv,
+                       int window, hipStream_t st);
 // D[b,h,t] = sum_d dO*O
 hipError_t nc_attn_bwd_pre(int dtype, const void* o, const void* dO, int64_t ld_o, float* D,
                            int B, int T, int H, hipStream_t st);
 hipError_t nc_attn_bwd(int dtype, const void* q, const void* k, const void* v, int64_t ld_qkv,
                        const void* dO, int64_t ld_o, const float* lse, const float* D,
                        void* dq, void* dk, void* dv, int64_t ld_dqkv, int B, int T, int H,
-                       int window, hipStream_t st);
+                       int Hkv, int window, hipStream_t st);
 
 // ---- softmax cross-entropy over rows of fp32 logits
 // dz = scale*(softmax(z) - onehot(y)) in the activation type; loss_rows[i] = lse - z[y]

@@ -59,6 +59,7 @@ struct nc_ctx {
   int dt;      // 0 fp32, 1 bf16
   size_t es;   // activation element size
   int L, d, H, F, V, T, maxB, Nmax, chunk;
+  int Hkv, dk, W;   // key/value heads, their width Hkv*128, qkv row width d + 2 dk
   int64_t S, n_block, n_total;
   std::vector<ParamInfo> params;
   // parameter arena byte offsets
@@ -68,10 +69,11 @@ struct nc_ctx {
   size_t xf, rf, x, dx, dxT, da, dqkv, dO, Dbuf, dh, z, dz, loss_rows, ws, ws_bytes, emb,
       nsU, frob, norms, nm_vm, nm_q, nm_inv, nm_scale, act_bytes;
   int64_t nm_rows = 0;   // NorMuon: rows of all block matrices (4L d + L F + L d)
-  // Newton-Schulz buffers per group (0: 4L square [d,d], 1: 2L wide [d,F]): the fp32
-  // iterate X (two, ping-pong), A = X X^T, B = b A + c A A, and a copy of each in the
-  // activation type for the matrix cores.
-  struct NsBufs { size_t x32[2], xh[2], a32, ah, b32, bh; } ns[2];
+  // Newton-Schulz buffers per group (0: square [d,d] (4L, or 2L with grouped
+  // key/value heads), 1: 2L wide [d,F], 2: 2L [dk,d] with grouped key/value heads):
+  // the fp32 iterate X (two, ping-pong), A = X X^T, B = b A + c A A, and a copy of
+  // each in the activation type for the matrix cores.
+  struct NsBufs { size_t x32[2], xh[2], a32, ah, b32, bh; } ns[3];
   int splits_qkv, splits_o, splits_1, splits_2, splits_head, splits_dxf;
   std::vector<int> windows;   // attention window per layer, -1 = plain causal
   char* pa = nullptr;
@@ -123,6 +125,10 @@ nc_status validate(const nc_model_config* m, const nc_optim_config* o, std::stri
     return NC_ERR_INVALID_ARG;
   }
   if (m->dtype != NC_FP32 && m->dtype != NC_BF16) { why = "dtype"; return NC_ERR_INVALID_ARG; }
+  if (m->n_kv_head < 0 || (m->n_kv_head > 0 && m->n_head % m->n_kv_head)) {
+    why = "n_kv_head must divide n_head (0: n_head)";
+    return NC_ERR_INVALID_ARG;
+  }
   if (m->head_dim != 128 || m->d_model != m->n_head * 128) {
     why = "head_dim must be 128 and d_model = n_head * 128";
     return NC_ERR_UNSUPPORTED;
@@ -149,8 +155,10 @@ nc_status validate(const nc_model_config* m, const nc_optim_config* o, std::stri
 
 void plan(nc_ctx* c) {
   const int L = c->L, d = c->d, F = c->F, V = c->V, T = c->T, H = c->H;
+  const int dk = c->dk, Hkv = c->Hkv, W = c->W;
   const size_t es = c->es;
-  c->S = 4LL * d * d + 2LL * d * F;
+  // per layer: Wq [d,d] | Wk [dk,d] | Wv [dk,d] | Wo [d,d] | W1 [F,d] | W2 [d,F]
+  c->S = 2LL * d * d + 2LL * dk * d + 2LL * d * F;
   c->n_block = c->S * L;
   c->n_total = c->n_block + 2LL * V * d;
   // registry
@@ -159,9 +167,10 @@ void plan(nc_ctx* c) {
   const char* names[6] = {"Wq", "Wk", "Wv", "Wo", "W1", "W2"};
   for (int l = 0; l < L; ++l) {
     size_t base = (size_t)l * c->S;
-    const int64_t offs[6] = {0, (int64_t)d * d, 2LL * d * d, 3LL * d * d, 4LL * d * d,
-                             4LL * d * d + (int64_t)F * d};
-    const int rows[6] = {d, d, d, d, F, d}, cols[6] = {d, d, d, d, d, F};
+    const int64_t dd = (int64_t)d * d, kd = (int64_t)dk * d;
+    const int64_t offs[6] = {0, dd, dd + kd, dd + 2 * kd, 2 * dd + 2 * kd,
+                             2 * dd + 2 * kd + (int64_t)F * d};
+    const int rows[6] = {d, dk, dk, d, F, d}, cols[6] = {d, d, d, d, d, F};
     for (int j = 0; j < 6; ++j)
       c->params.push_back({std::to_string(l) + "." + names[j], rows[j], cols[j], NC_GROUP_MUON,
                            base + (size_t)offs[j], -1});
@@ -177,7 +186,7 @@ void plan(nc_ctx* c) {
   c->oAv = p.take(2ULL * V * d * 4);
   c->oSh = c->dt ? p.take((c->n_block + (size_t)V * d) * 2) : 0;
   c->oTab = p.take(2ULL * T * 64 * 4);
-  c->nm_rows = c->ocfg.normuon ? (int64_t)L * (5LL * d + F) : 0;
+  c->nm_rows = c->ocfg.normuon ? (int64_t)L * (3LL * d + 2LL * dk + F) : 0;
   c->oV2 = c->nm_rows ? p.take((size_t)c->nm_rows * 4) : 0;
   c->param_bytes = p.cur;
 
@@ -189,8 +198,8 @@ void plan(nc_ctx* c) {
     LayerAct& x = c->la[l];
     x.a1 = a.take(N * d * es);
     x.r1 = a.take(N * 4);
-    x.qkv = a.take(N * 3 * d * es);
-    x.rqk = a.take(N * 2 * H * 4);
+    x.qkv = a.take(N * W * es);
+    x.rqk = a.take(N * (H + Hkv) * 4);
     x.o = a.take(N * d * es);
     x.lse = a.take(N * H * 4);
     x.a2 = a.take(N * d * es);
@@ -203,7 +212,7 @@ void plan(nc_ctx* c) {
   c->dx = a.take(N * d * 4);
   c->dxT = a.take(N * d * es);
   c->da = a.take(N * d * 4);
-  c->dqkv = a.take(N * 3 * d * es);
+  c->dqkv = a.take(N * W * es);
   c->dO = a.take(N * d * es);
   c->Dbuf = a.take(N * H * 4);
   c->dh = a.take(N * F * es);
@@ -212,14 +221,14 @@ void plan(nc_ctx* c) {
   c->loss_rows = a.take(N * 4);
   // split-K for the weight-gradient products (bf16 MFMA path)
   auto sp = [&](int M, int Nn, int K) { return c->dt ? nc_gemm_pick_splits(M, Nn, K) : 1; };
-  c->splits_qkv = sp(3 * d, d, (int)N);
+  c->splits_qkv = sp(W, d, (int)N);
   c->splits_o = sp(d, d, (int)N);
   c->splits_1 = sp(F, d, (int)N);
   c->splits_2 = sp(d, F, (int)N);
   c->splits_head = sp(V, d, c->chunk);
   c->splits_dxf = sp(c->chunk, d, V);   // few output tiles, K = vocabulary
   size_t ws = 0;
-  ws = std::max(ws, nc_gemm_workspace_bytes(3 * d, d, c->splits_qkv));
+  ws = std::max(ws, nc_gemm_workspace_bytes(W, d, c->splits_qkv));
   ws = std::max(ws, nc_gemm_workspace_bytes(d, d, c->splits_o));
   ws = std::max(ws, nc_gemm_workspace_bytes(F, d, c->splits_1));
   ws = std::max(ws, nc_gemm_workspace_bytes(d, F, c->splits_2));
@@ -228,10 +237,15 @@ void plan(nc_ctx* c) {
   c->ws_bytes = ws;
   c->ws = a.take(std::max<size_t>(ws, 256));
   c->emb = a.take(nc_embed_bwd_scratch_bytes((int)N, V, d));
-  // Newton-Schulz: 4L square [d,d] and 2L wide [d,F] matrices
-  for (int g = 0; g < 2; ++g) {
-    const size_t cnt = (size_t)(g ? 2 : 4) * L, xe = cnt * d * (g ? F : d), ae = cnt * d * d;
+  // Newton-Schulz groups (see NsBufs)
+  const bool gqa = dk != d;
+  const int ns_cnt[3] = {(gqa ? 2 : 4) * L, 2 * L, gqa ? 2 * L : 0};
+  const int ns_r[3] = {d, d, dk}, ns_c[3] = {d, F, d};
+  for (int g = 0; g < 3; ++g) {
     auto& b = c->ns[g];
+    b = {};
+    if (!ns_cnt[g]) continue;
+    const size_t cnt = ns_cnt[g], xe = cnt * ns_r[g] * ns_c[g], ae = cnt * ns_r[g] * ns_r[g];
     for (int k = 0; k < 2; ++k) {
       b.x32[k] = a.take(xe * 4);
       b.xh[k] = a.take(xe * es);
@@ -352,6 +366,9 @@ static nc_ctx* make_ctx(const nc_model_config* cfg, const nc_optim_config* ocfg)
   c->dt = cfg->dtype == NC_BF16 ? 1 : 0;
   c->es = c->dt ? 2 : 4;
   c->L = cfg->n_layer; c->d = cfg->d_model; c->H = cfg->n_head; c->F = cfg->d_ff;
+  c->Hkv = cfg->n_kv_head > 0 ? cfg->n_kv_head : cfg->n_head;
+  c->dk = c->Hkv * 128;
+  c->W = c->d + 2 * c->dk;
   c->V = cfg->vocab; c->T = cfg->seq_len; c->maxB = cfg->max_micro_batch;
   c->Nmax = c->maxB * c->T;
   c->windows.assign(c->L, -1);
@@ -482,6 +499,9 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
   const int dt = ctx->dt, L = ctx->L, d = ctx->d, H = ctx->H, F = ctx->F, V = ctx->V,
             T = ctx->T;
   const int N = B * T;
+  const int Hkv = ctx->Hkv, dk = ctx->dk, Wd = ctx->W;
+  // offsets of Wo and W1 inside a layer's block (Wq | Wk | Wv | Wo | W1 | W2)
+  const size_t oWo = (size_t)d * d + 2ULL * dk * d, oW1 = oWo + (size_t)d * d;
   const float eps = ctx->cfg.norm_eps;
   hipStream_t st = ctx->st;
   const size_t es = ctx->es;
@@ -500,17 +520,18 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
     const size_t wb = (size_t)l * ctx->S;
     char* qkv = aa + la.qkv;
     NC_TRY(nc_rmsnorm_fwd(dt, x, aa + la.a1, A<float>(ctx, la.r1), N, d, eps, st), "norm1");
-    NC_GEMM(gemm(ctx, aa + la.a1, d, kKCont, wptr(ctx, wb), d, kKCont, qkv, 3 * d, N, 3 * d, d,
+    NC_GEMM(gemm(ctx, aa + la.a1, d, kKCont, wptr(ctx, wb), d, kKCont, qkv, Wd, N, Wd, d,
                 kEpiStore), "qkv");
-    NC_TRY(nc_qk_norm_rope_fwd(dt, qkv, A<float>(ctx, la.rqk), tab, N, T, H, eps, st), "qknorm");
-    NC_TRY(nc_attn_fwd(dt, qkv, qkv + d * es, qkv + 2 * d * es, 3 * d, aa + la.o, d,
-                       A<float>(ctx, la.lse), B, T, H, ctx->windows[l], st), "attn fwd");
-    NC_GEMM(gemm(ctx, aa + la.o, d, kKCont, wptr(ctx, wb + 3ULL * d * d), d, kKCont, x, d, N, d,
+    NC_TRY(nc_qk_norm_rope_fwd(dt, qkv, A<float>(ctx, la.rqk), tab, N, T, H, Hkv, eps, st),
+           "qknorm");
+    NC_TRY(nc_attn_fwd(dt, qkv, qkv + d * es, qkv + (d + dk) * es, Wd, aa + la.o, d,
+                       A<float>(ctx, la.lse), B, T, H, Hkv, ctx->windows[l], st), "attn fwd");
+    NC_GEMM(gemm(ctx, aa + la.o, d, kKCont, wptr(ctx, wb + oWo), d, kKCont, x, d, N, d,
                 d, kEpiAccF32), "out proj");
     NC_TRY(nc_rmsnorm_fwd(dt, x, aa + la.a2, A<float>(ctx, la.r2), N, d, eps, st), "norm2");
-    NC_GEMM(gemm(ctx, aa + la.a2, d, kKCont, wptr(ctx, wb + 4ULL * d * d), d, kKCont, aa + la.g,
+    NC_GEMM(gemm(ctx, aa + la.a2, d, kKCont, wptr(ctx, wb + oW1), d, kKCont, aa + la.g,
                 F, N, F, d, kEpiRelu2), "mlp up");
-    NC_GEMM(gemm(ctx, aa + la.g, F, kKCont, wptr(ctx, wb + 4ULL * d * d + (size_t)F * d), F,
+    NC_GEMM(gemm(ctx, aa + la.g, F, kKCont, wptr(ctx, wb + oW1 + (size_t)F * d), F,
                 kKCont, x, d, N, d, F, kEpiAccF32), "mlp down");
   }
   NC_TRY(nc_rmsnorm_fwd(dt, x, aa + ctx->xf, A<float>(ctx, ctx->rf), N, d, eps, st), "normf");
@@ -538,7 +559,7 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
   for (int l = L - 1; l >= 0; --l) {
     const LayerAct& la = ctx->la[l];
     const size_t wb = (size_t)l * ctx->S;
-    const size_t w1 = wb + 4ULL * d * d, w2 = w1 + (size_t)F * d;
+    const size_t w1 = wb + oW1, w2 = w1 + (size_t)F * d;
     char* qkv = aa + la.qkv;
     char* dqkv = aa + ctx->dqkv;
     // MLP
@@ -553,20 +574,20 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
     NC_TRY(nc_rmsnorm_bwd(dt, da, aa + la.a2, A<float>(ctx, la.r2), dx, dxT, N, d, 1, st),
            "norm2 bwd");
     // attention
-    NC_GEMM(gemm(ctx, dxT, d, kKCont, wptr(ctx, wb + 3ULL * d * d), d, kMNCont, aa + ctx->dO, d,
+    NC_GEMM(gemm(ctx, dxT, d, kKCont, wptr(ctx, wb + oWo), d, kMNCont, aa + ctx->dO, d,
                 N, d, d, kEpiStore), "dO");
-    NC_GEMM(gemm(ctx, dxT, d, kMNCont, aa + la.o, d, kMNCont, G + wb + 3ULL * d * d, d, d, d, N,
+    NC_GEMM(gemm(ctx, dxT, d, kMNCont, aa + la.o, d, kMNCont, G + wb + oWo, d, d, d, N,
                 kEpiAccF32, nullptr, nullptr, ctx->splits_o), "dWo");
     NC_TRY(nc_attn_bwd_pre(dt, aa + la.o, aa + ctx->dO, d, A<float>(ctx, ctx->Dbuf), B, T, H, st),
            "attn D");
-    NC_TRY(nc_attn_bwd(dt, qkv, qkv + d * es, qkv + 2 * d * es, 3 * d, aa + ctx->dO, d,
+    NC_TRY(nc_attn_bwd(dt, qkv, qkv + d * es, qkv + (d + dk) * es, Wd, aa + ctx->dO, d,
                        A<float>(ctx, la.lse), A<float>(ctx, ctx->Dbuf), dqkv, dqkv + d * es,
-                       dqkv + 2 * d * es, 3 * d, B, T, H, ctx->windows[l], st), "attn bwd");
-    NC_TRY(nc_qk_norm_rope_bwd(dt, dqkv, qkv, A<float>(ctx, la.rqk), tab, N, T, H, st),
+                       dqkv + (d + dk) * es, Wd, B, T, H, Hkv, ctx->windows[l], st), "attn bwd");
+    NC_TRY(nc_qk_norm_rope_bwd(dt, dqkv, qkv, A<float>(ctx, la.rqk), tab, N, T, H, Hkv, st),
            "qknorm bwd");
-    NC_GEMM(gemm(ctx, dqkv, 3 * d, kMNCont, aa + la.a1, d, kMNCont, G + wb, d, 3 * d, d, N,
+    NC_GEMM(gemm(ctx, dqkv, Wd, kMNCont, aa + la.a1, d, kMNCont, G + wb, d, Wd, d, N,
                 kEpiAccF32, nullptr, nullptr, ctx->splits_qkv), "dWqkv");
-    NC_GEMM(gemm(ctx, dqkv, 3 * d, kKCont, wptr(ctx, wb), d, kMNCont, da, d, N, d, 3 * d,
+    NC_GEMM(gemm(ctx, dqkv, Wd, kKCont, wptr(ctx, wb), d, kMNCont, da, d, N, d, Wd,
                 kEpiStoreF32), "da1");
     NC_TRY(nc_rmsnorm_bwd(dt, da, aa + la.a1, A<float>(ctx, la.r1), dx, dxT, N, d, 1, st),
            "norm1 bwd");
@@ -634,59 +655,80 @@ nc_status nc_optimizer_step(nc_ctx* ctx, float lr_mult) {
   }
   float* norms = A<float>(ctx, ctx->norms);
   float* frob = A<float>(ctx, ctx->frob);
-  const int64_t dd = (int64_t)d * d, dF = (int64_t)d * F;
-  const MatBatch sq{4, dd, ctx->S}, one{1, 0, ctx->S};
-  const size_t o1 = 4ULL * dd, o2 = o1 + (size_t)dF;
-  NC_TRY(nc_frob_norms(U, sq, dd, 4 * L, frob, norms, st), "norms sq");
-  NC_TRY(nc_frob_norms(U + o1, one, dF, L, frob + 4 * L * 256, norms + 4 * L, st), "norms W1");
-  NC_TRY(nc_frob_norms(U + o2, one, dF, L, frob + 5 * L * 256, norms + 5 * L, st), "norms W2");
   char* aa = ctx->aa;
-  // orthogonalise on the short side: square [d,d]; W1 [F,d] -> [d,F]; W2 [d,F]
-  const auto& q = ctx->ns[0];
-  const auto& w = ctx->ns[1];
-  const size_t w2x = (size_t)L * dF;   // W2 matrices follow the L W1 matrices in group 1
-  NC_TRY(nc_ns_prepare(dt, U, sq, d, d, 4 * L, norms, o.ns_eps, 0, A<float>(ctx, q.x32[0]),
-                       aa + q.xh[0], dd, st), "prep sq");
-  NC_TRY(nc_ns_prepare(dt, U + o1, one, F, d, L, norms + 4 * L, o.ns_eps, 1,
-                       A<float>(ctx, w.x32[0]), aa + w.xh[0], dF, st), "prep W1");
-  NC_TRY(nc_ns_prepare(dt, U + o2, one, d, F, L, norms + 5 * L, o.ns_eps, 0,
-                       A<float>(ctx, w.x32[0]) + w2x, aa + w.xh[0] + w2x * ctx->es, dF, st),
-         "prep W2");
-  size_t xs, xr;
-  nc_status s = newton_schulz(ctx, 0, 4 * L, d, d, &xs);
+  const int dk = ctx->dk;
+  const int64_t dd = (int64_t)d * d, dF = (int64_t)d * F, kd = (int64_t)dk * d;
+  const size_t oWo = (size_t)(dd + 2 * kd), o1 = oWo + (size_t)dd, o2 = o1 + (size_t)dF;
+  // Matrix groups, each orthogonalised as one batch on its short side.  Their
+  // Frobenius norms, NorMuon rows and scales follow each other in this order.
+  struct Grp {
+    size_t woff;   // block-region offset of the group's first matrix
+    MatBatch mb;   // offsets of its matrices from there
+    int R, C;      // W shape [R, C]
+    int count;
+    int tr;        // 1: orthogonalised as [C, R] (W1)
+    int ns;        // Newton-Schulz buffer group
+    size_t xoff;   // offset of the group's iterates in that buffer group
+  };
+  const MatBatch one{1, 0, ctx->S};
+  Grp grps[4];
+  int ng = 0;
+  if (dk == d) {
+    grps[ng++] = {0, MatBatch{4, dd, ctx->S}, d, d, 4 * L, 0, 0, 0};            // Wq Wk Wv Wo
+  } else {
+    grps[ng++] = {0, MatBatch{2, (int64_t)oWo, ctx->S}, d, d, 2 * L, 0, 0, 0};  // Wq Wo
+    grps[ng++] = {(size_t)dd, MatBatch{2, kd, ctx->S}, dk, d, 2 * L, 0, 2, 0};  // Wk Wv
+  }
+  grps[ng++] = {o1, one, F, d, L, 1, 1, 0};                                     // W1
+  grps[ng++] = {o2, one, d, F, L, 0, 1, (size_t)L * dF};                        // W2
+  int nidx = 0;
+  for (int i = 0; i < ng; ++i) {
+    const Grp& g = grps[i];
+    const int64_t el = (int64_t)g.R * g.C;
+    const auto& b = ctx->ns[g.ns];
+    NC_TRY(nc_frob_norms(U + g.woff, g.mb, el, g.count, frob + (size_t)nidx * 256, norms + nidx,
+                         st), "norms");
+    NC_TRY(nc_ns_prepare(dt, U + g.woff, g.mb, g.R, g.C, g.count, norms + nidx, o.ns_eps, g.tr,
+                         A<float>(ctx, b.x32[0]) + g.xoff, aa + b.xh[0] + g.xoff * ctx->es, el,
+                         st), "ns prepare");
+    nidx += g.count;
+  }
+  // Newton-Schulz per buffer group: 0 square, 1 W1^T | W2 [d, F], 2 Wk | Wv [dk, d]
+  size_t xres[3] = {0, 0, 0};
+  nc_status s = newton_schulz(ctx, 0, grps[0].count, d, d, &xres[0]);
   if (s != NC_OK) return s;
-  s = newton_schulz(ctx, 1, 2 * L, d, F, &xr);
+  s = newton_schulz(ctx, 1, 2 * L, d, F, &xres[1]);
   if (s != NC_OK) return s;
+  if (dk != d) {
+    s = newton_schulz(ctx, 2, 2 * L, dk, d, &xres[2]);
+    if (s != NC_OK) return s;
+  }
   const float lr = o.muon_lr * lr_mult;
   char* sh = dt ? ctx->pa + ctx->oSh : nullptr;
   // NorMuon (optional): per-row statistics of each orthogonalised update, in the
-  // orientation of W (W1's update is held transposed); rows of the three groups
-  // follow each other in v2 and the scratch arrays
-  const float* rm[3] = {nullptr, nullptr, nullptr};
-  const float* ms[3] = {nullptr, nullptr, nullptr};
-  if (ctx->nm_rows) {
-    float* v2 = P<float>(ctx, ctx->oV2);
-    float* vm = A<float>(ctx, ctx->nm_vm);
-    float* qv = A<float>(ctx, ctx->nm_q);
-    float* inv = A<float>(ctx, ctx->nm_inv);
-    float* scl = A<float>(ctx, ctx->nm_scale);
-    const float b2 = o.normuon_beta2;
-    const int64_t r1 = 4LL * L * d, r2 = r1 + (int64_t)L * F;   // row offsets of W1, W2
-    NC_TRY(nc_normuon_stats(A<float>(ctx, xs), dd, d, d, 0, 4 * L, v2, b2, vm, qv, inv, scl, st),
-           "normuon sq");
-    NC_TRY(nc_normuon_stats(A<float>(ctx, xr), dF, F, d, 1, L, v2 + r1, b2, vm + r1, qv + r1,
-                            inv + r1, scl + 4 * L, st), "normuon W1");
-    NC_TRY(nc_normuon_stats(A<float>(ctx, xr) + w2x, dF, d, F, 0, L, v2 + r2, b2, vm + r2,
-                            qv + r2, inv + r2, scl + 5 * L, st), "normuon W2");
-    rm[0] = inv; rm[1] = inv + r1; rm[2] = inv + r2;
-    ms[0] = scl; ms[1] = scl + 4 * L; ms[2] = scl + 5 * L;
+  // orientation of W (W1's update is held transposed)
+  int64_t roff = 0;
+  nidx = 0;
+  for (int i = 0; i < ng; ++i) {
+    const Grp& g = grps[i];
+    const int64_t el = (int64_t)g.R * g.C;
+    const float* X = A<float>(ctx, xres[g.ns]) + g.xoff;
+    const float* rm = nullptr;
+    const float* ms = nullptr;
+    if (ctx->nm_rows) {
+      float* inv = A<float>(ctx, ctx->nm_inv) + roff;
+      float* scl = A<float>(ctx, ctx->nm_scale) + nidx;
+      NC_TRY(nc_normuon_stats(X, el, g.R, g.C, g.tr, g.count, P<float>(ctx, ctx->oV2) + roff,
+                              o.normuon_beta2, A<float>(ctx, ctx->nm_vm) + roff,
+                              A<float>(ctx, ctx->nm_q) + roff, inv, scl, st), "normuon");
+      rm = inv;
+      ms = scl;
+    }
+    NC_TRY(nc_ns_apply(Pm + g.woff, g.mb, g.R, g.C, g.count, X, el, g.tr, lr, o.muon_wd, rm, ms,
+                       sh ? sh + g.woff * 2 : nullptr, st), "ns apply");
+    roff += (int64_t)g.count * g.R;
+    nidx += g.count;
   }
-  NC_TRY(nc_ns_apply(Pm, sq, d, d, 4 * L, A<float>(ctx, xs), dd, 0, lr, o.muon_wd, rm[0], ms[0],
-                     sh, st), "apply sq");
-  NC_TRY(nc_ns_apply(Pm + o1, one, F, d, L, A<float>(ctx, xr), dF, 1, lr, o.muon_wd, rm[1], ms[1],
-                     sh ? sh + o1 * 2 : nullptr, st), "apply W1");
-  NC_TRY(nc_ns_apply(Pm + o2, one, d, F, L, A<float>(ctx, xr) + w2x, dF, 0, lr, o.muon_wd, rm[2],
-                     ms[2], sh ? sh + o2 * 2 : nullptr, st), "apply W2");
   return NC_OK;
 }
 
@@ -808,12 +850,16 @@ nc_status nc_flops(const nc_ctx* ctx, int32_t B, double* fb, double* opt) {
       keys += sum / T;
     }
   }
-  if (fb) *fb = 6.0 * N * (L * (4 * d * d + 2 * d * F) + V * d) + 12.0 * N * d * keys;
+  const double dk = ctx->dk;
+  if (fb) *fb = 6.0 * N * (L * (2 * d * d + 2 * dk * d + 2 * d * F) + V * d) + 12.0 * N * d * keys;
   if (opt) {
     const double steps = ctx->ocfg.ns_steps;
+    // 4 m^2 n + 2 m^3 per iteration for an m x n matrix, m <= n
+    const double dk = ctx->dk;
     const double sq = 4.0 * d * d * d + 2.0 * d * d * d;     // m = n = d
+    const double kv = 4.0 * dk * dk * d + 2.0 * dk * dk * dk; // m = dk, n = d
     const double rect = 4.0 * d * d * F + 2.0 * d * d * d;   // m = d, n = F
-    *opt = steps * L * (4 * sq + 2 * rect);
+    *opt = steps * L * (2 * sq + 2 * kv + 2 * rect);
   }
   return NC_OK;
 }
@@ -854,28 +900,30 @@ nc_status nc_op_gemm(int32_t dtype, const void* A_, int64_t lda, int32_t al, con
 
 nc_status nc_op_attention_fwd(int32_t dtype, const void* q, const void* k, const void* v,
                               int64_t ld_qkv, void* o, int64_t ld_o, float* lse, int32_t B,
-                              int32_t T, int32_t H, int32_t window, void* stream) {
-  if (!q || !k || !v || !o || !lse || B < 1 || T < 1 || H < 1 || window < -1)
+                              int32_t T, int32_t H, int32_t n_kv_head, int32_t window,
+                              void* stream) {
+  if (!q || !k || !v || !o || !lse || B < 1 || T < 1 || H < 1 || window < -1 ||
+      n_kv_head < 1 || H % n_kv_head)
     return NC_ERR_INVALID_ARG;
   if (dtype == NC_BF16 && (T % 128 || ld_qkv % 8 || ld_o % 8)) return NC_ERR_UNSUPPORTED;
-  return nc_attn_fwd(dtype == NC_BF16, q, k, v, ld_qkv, o, ld_o, lse, B, T, H, window,
+  return nc_attn_fwd(dtype == NC_BF16, q, k, v, ld_qkv, o, ld_o, lse, B, T, H, n_kv_head, window,
                      static_cast<hipStream_t>(stream)) == hipSuccess ? NC_OK : NC_ERR_HIP;
 }
 
 nc_status nc_op_attention_bwd(int32_t dtype, const void* q, const void* k, const void* v,
                               int64_t ld_qkv, const void* o, const void* dO, int64_t ld_o,
                               const float* lse, float* D, void* dq, void* dk, void* dv,
-                              int64_t ld_d, int32_t B, int32_t T, int32_t H, int32_t window,
-                              void* stream) {
+                              int64_t ld_d, int32_t B, int32_t T, int32_t H, int32_t n_kv_head,
+                              int32_t window, void* stream) {
   if (!q || !k || !v || !o || !dO || !lse || !D || !dq || !dk || !dv || B < 1 || T < 1 || H < 1 ||
-      window < -1)
+      window < -1 || n_kv_head < 1 || H % n_kv_head)
     return NC_ERR_INVALID_ARG;
   if (dtype == NC_BF16 && (T % 128 || ld_qkv % 8 || ld_o % 8 || ld_d % 8)) return NC_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int dt = dtype == NC_BF16;
   if (nc_attn_bwd_pre(dt, o, dO, ld_o, D, B, T, H, st) != hipSuccess) return NC_ERR_HIP;
-  return nc_attn_bwd(dt, q, k, v, ld_qkv, dO, ld_o, lse, D, dq, dk, dv, ld_d, B, T, H, window,
-                     st) ==
+  return nc_attn_bwd(dt, q, k, v, ld_qkv, dO, ld_o, lse, D, dq, dk, dv, ld_d, B, T, H, n_kv_head,
+                     window, st) ==
                  hipSuccess
              ? NC_OK
              : NC_ERR_HIP;

@@ -35,7 +35,8 @@ class ModelCfgC(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("n_layer", "d_model", "n_head", "head_dim", "d_ff", "vocab", "seq_len",
                  "max_micro_batch", "dtype")] + [("rope_base", ctypes.c_float),
-                                                 ("norm_eps", ctypes.c_float)]
+                                                 ("norm_eps", ctypes.c_float),
+                                                 ("n_kv_head", ctypes.c_int32)]
 
 
 class OptimCfgC(ctypes.Structure):
@@ -89,9 +90,9 @@ def load():
         "nc_flops": [P, I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)],
         "nc_op_gemm": [I32, P, I64, I32, P, I64, I32, P, I64, I32, I32, I32, I32, I64, I64, I64,
                        I32, P, P, F32, F32, F32, I32, P, SZ, P],
-        "nc_op_attention_fwd": [I32, P, P, P, I64, P, I64, P, I32, I32, I32, I32, P],
+        "nc_op_attention_fwd": [I32, P, P, P, I64, P, I64, P, I32, I32, I32, I32, I32, P],
         "nc_op_attention_bwd": [I32, P, P, P, I64, P, P, I64, P, P, P, P, P, I64, I32, I32, I32,
-                                I32, P],
+                                I32, I32, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -110,7 +111,8 @@ def load():
 def model_cfg_c(cfg: ModelConfig, max_micro_batch=None):
     return ModelCfgC(cfg.n_layer, cfg.d_model, cfg.n_head, cfg.head_dim, cfg.d_ff, cfg.vocab,
                      cfg.seq_len, max_micro_batch or cfg.micro_batch,
-                     NC_BF16 if cfg.dtype == "bf16" else NC_FP32, cfg.rope_base, cfg.norm_eps)
+                     NC_BF16 if cfg.dtype == "bf16" else NC_FP32, cfg.rope_base, cfg.norm_eps,
+                     cfg.n_kv_head)
 
 
 def optim_cfg_c(o: OptimConfig):
@@ -298,18 +300,19 @@ def gemm(A, a_layout, B, b_layout, C, M, N, K, epilogue=EPI_STORE, aux_in=None, 
     _check(s, what="nc_op_gemm")
 
 
-def attention_fwd(q, k, v, o, lse, B, T, H, ld_qkv, ld_o, window=-1):
+def attention_fwd(q, k, v, o, lse, B, T, H, ld_qkv, ld_o, window=-1, n_kv_head=None):
     lib = load()
     s = lib.nc_op_attention_fwd(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), ld_qkv, _ptr(o), ld_o,
-                                _ptr(lse), B, T, H, window,
+                                _ptr(lse), B, T, H, n_kv_head or H, window,
                                 ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     _check(s, what="nc_op_attention_fwd")
 
 
-def attention_bwd(q, k, v, o, dO, lse, D, dq, dk, dv, B, T, H, ld_qkv, ld_o, ld_d, window=-1):
+def attention_bwd(q, k, v, o, dO, lse, D, dq, dk, dv, B, T, H, ld_qkv, ld_o, ld_d, window=-1,
+                  n_kv_head=None):
     lib = load()
     s = lib.nc_op_attention_bwd(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), ld_qkv, _ptr(o),
                                 _ptr(dO), ld_o, _ptr(lse), _ptr(D), _ptr(dq), _ptr(dk), _ptr(dv),
-                                ld_d, B, T, H, window,
+                                ld_d, B, T, H, n_kv_head or H, window,
                                 ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     _check(s, what="nc_op_attention_bwd")

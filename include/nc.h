@@ -52,7 +52,11 @@ typedef enum {
 
 enum { NC_FP32 = 0, NC_BF16 = 1 };
 
-/* Model shape.  head_dim must be 128 and d_model = n_head * 128.  dtype
+/* Model shape.  head_dim must be 128 and d_model = n_head * 128.  n_kv_head
+ * key/value heads (0 = n_head; it must divide n_head): grouped-query
+ * attention as listed on apidog.com, "1. Model GPT (nanochat/gpt.py)" (no
+ * ratio is printed there) -- Wk and Wv are [n_kv_head * 128, d_model] and
+ * query head h reads key/value head h / (n_head / n_kv_head).  dtype
  * NC_FP32 computes everything in fp32; NC_BF16 feeds bf16 (round to nearest
  * even) to the matrix cores with fp32 accumulation and keeps fp32 master
  * weights, residual stream, softmax statistics and gradients.  The norm is a
@@ -63,6 +67,7 @@ typedef struct {
   int32_t max_micro_batch; /* rows per nc_fwd_bwd call the arenas are planned for */
   int32_t dtype;           /* NC_FP32 | NC_BF16 */
   float rope_base, norm_eps;
+  int32_t n_kv_head;
 } nc_model_config;
 
 /* Optimizer settings.  Muon (per block matrix): M <- mu M + G;
@@ -97,7 +102,8 @@ enum { NC_GROUP_ADAMW = 0, NC_GROUP_MUON = 1 };
 enum { NC_PARAM = 0, NC_GRAD = 1, NC_MOMENTUM = 2, NC_ADAM_M = 3, NC_ADAM_V = 4 };
 
 typedef struct {
-  char name[32];           /* "E", "<layer>.Wq|Wk|Wv|Wo|W1|W2", "Wh" */
+  char name[32];           /* "E", "<layer>.Wq|Wk|Wv|Wo|W1|W2", "Wh" (a layer's six
+                              matrices are contiguous in this order) */
   int32_t rows, cols, group;
   int64_t param_offset;    /* byte offsets into the parameter arena (fp32) */
   int64_t grad_offset;

@@ -53,25 +53,29 @@ nc_status nc_op_gemm(int32_t dtype, const void* A, int64_t lda, int32_t a_layout
 
 /* Causal attention forward, head dim 128, scale 1/sqrt(128).  q, k, v:
  * token-major rows (row b*T + t, head h at columns h*128 .. h*128+127, row
- * stride ld_qkv elements); o: same layout with stride ld_o; lse: fp32
- * [B, H, T] natural-log log-sum-exp of each query's scores.  window: -1 for
+ * stride ld_qkv elements); q has H heads, k and v n_kv_head heads (n_kv_head
+ * divides H; query head h reads key/value head h / (H / n_kv_head)); o: the
+ * layout of q with stride ld_o; lse: fp32 [B, H, T] natural-log log-sum-exp
+ * of each query's scores.  window: -1 for
  * the plain causal mask (query t sees keys 0 .. t), w >= 0 for a sliding
  * window (keys max(0, t - w) .. t; apidog.com, "5. Penyatuan Flash
  * Attention"); below -1 is NC_ERR_INVALID_ARG.  bf16 path needs
  * T % 128 == 0. */
 nc_status nc_op_attention_fwd(int32_t dtype, const void* q, const void* k, const void* v,
                               int64_t ld_qkv, void* o, int64_t ld_o, float* lse, int32_t B,
-                              int32_t T, int32_t H, int32_t window, void* stream);
+                              int32_t T, int32_t H, int32_t n_kv_head, int32_t window,
+                              void* stream);
 
 /* Causal attention backward from o, lse of the forward and dO (layout of o).
  * D (fp32 [B, H, T]) is caller-provided scratch receiving rowsum(dO * o).
- * Writes dq, dk, dv (layout of q/k/v with row stride ld_d).  window as for
- * the forward pass (the same value the forward pass used). */
+ * Writes dq, dk, dv (layout of q/k/v with row stride ld_d; dk and dv of a
+ * key/value head sum over its query heads).  n_kv_head and window as for the
+ * forward pass (the same values the forward pass used). */
 nc_status nc_op_attention_bwd(int32_t dtype, const void* q, const void* k, const void* v,
                               int64_t ld_qkv, const void* o, const void* dO, int64_t ld_o,
                               const float* lse, float* D, void* dq, void* dk, void* dv,
-                              int64_t ld_d, int32_t B, int32_t T, int32_t H, int32_t window,
-                              void* stream);
+                              int64_t ld_d, int32_t B, int32_t T, int32_t H, int32_t n_kv_head,
+                              int32_t window, void* stream);
 
 #ifdef __cplusplus
 }

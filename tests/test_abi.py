@@ -94,15 +94,20 @@ SMALL_BF16 = dict(name="small", n_layer=2, d_model=384, n_head=3, head_dim=128, 
                   token_dist="zipf")
 
 
-@pytest.mark.parametrize("name", ["tiny", "small", "d12", "d20", "d24", "d26"])
+@pytest.mark.parametrize("name", ["tiny", "small", "d12", "d20", "d24", "d26", "small_gqa",
+                                  "d20_gqa", "d26_gqa"])
 def test_every_launch_of_a_step_stays_inside_the_arenas(name):
     """Dry run of nc_fwd_bwd + nc_optimizer_step: every GEMM operand extent is
     checked against the planned arenas (no device access)."""
+    from dataclasses import replace as dc_replace
     from gpt_pretraining_step_gemms_amd.configs import ModelConfig
-    cfg = ModelConfig(**SMALL_BF16) if name == "small" else CONFIGS[name]
+    base = name.replace("_gqa", "")
+    cfg = ModelConfig(**SMALL_BF16) if base == "small" else CONFIGS[base]
+    if name.endswith("_gqa"):
+        cfg = dc_replace(cfg, n_kv_head=1)
     lib = nc.load()
     for maxb, b in [(cfg.micro_batch, cfg.micro_batch), (cfg.micro_batch, 1), (1, 1)]:
-        m, o = nc.model_cfg_c(cfg, maxb), nc.optim_cfg_c(OptimConfig())
+        m, o = nc.model_cfg_c(cfg, maxb), nc.optim_cfg_c(OptimConfig(normuon=True))
         ctx = ctypes.c_void_p()
         assert lib.nc_create(ctypes.byref(m), ctypes.byref(o), ctypes.byref(ctx)) == nc.NC_OK
         try:
@@ -145,6 +150,46 @@ def test_parameter_registry_matches_model_shapes():
         assert fb.value == pytest.approx(6 * 32 * T * (12 * L * d * d + V * d) + 6 * 32 * T * L * d * T)
     finally:
         lib.nc_destroy(ctx)
+
+
+def test_grouped_query_registry_and_flops():
+    """n_kv_head < n_head: Wk, Wv narrower, the six matrices of a layer still
+    contiguous (Wq | Wk | Wv form the fused QKV weight), FLOPs counted with
+    the narrower products; n_kv_head must divide n_head."""
+    from dataclasses import replace as dc_replace
+    lib = nc.load()
+    cfg = dc_replace(from_depth(12, micro_batch=1, accum_steps=1), n_kv_head=2)
+    d, dk, F, L, V, T = 768, 256, 3072, 12, 32768, 2048
+    m, o = nc.model_cfg_c(cfg), nc.optim_cfg_c(OptimConfig())
+    ctx = ctypes.c_void_p()
+    assert lib.nc_create(ctypes.byref(m), ctypes.byref(o), ctypes.byref(ctx)) == nc.NC_OK
+    try:
+        n = ctypes.c_int32()
+        lib.nc_param_count(ctx, ctypes.byref(n))
+        infos = []
+        for i in range(n.value):
+            info = nc.ParamInfoC()
+            assert lib.nc_param_desc(ctx, i, ctypes.byref(info)) == nc.NC_OK
+            infos.append(info)
+        shapes = {i.name.decode(): (i.rows, i.cols) for i in infos}
+        assert shapes == param_shapes(cfg.as_oracle_cfg())
+        assert shapes["0.Wk"] == (dk, d) and shapes["0.Wv"] == (dk, d)
+        layer = infos[1:7]
+        for a, b in zip(layer, layer[1:]):
+            assert b.param_offset == a.param_offset + 4 * a.rows * a.cols
+        fb, opt = ctypes.c_double(), ctypes.c_double()
+        lib.nc_flops(ctx, 1, ctypes.byref(fb), ctypes.byref(opt))
+        per_tok = 6 * (L * (2 * d * d + 2 * dk * d + 2 * d * F) + V * d) + 6 * L * d * T
+        assert fb.value == pytest.approx(T * per_tok)
+        ns = 5 * L * (2 * (6 * d ** 3) + 2 * (4 * dk * dk * d + 2 * dk ** 3) +
+                      2 * (4 * d * d * F + 2 * d ** 3))
+        assert opt.value == pytest.approx(ns)
+    finally:
+        lib.nc_destroy(ctx)
+    for bad in (4, 5, -1):           # 6 heads: 4 and 5 do not divide it
+        mb = nc.model_cfg_c(dc_replace(cfg, n_kv_head=bad))
+        ctx = ctypes.c_void_p()
+        assert lib.nc_create(ctypes.byref(mb), ctypes.byref(o), ctypes.byref(ctx)) == nc.NC_ERR_INVALID_ARG
 
 
 def test_attention_windows_set_and_counted_in_flops():

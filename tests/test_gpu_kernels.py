@@ -331,6 +331,50 @@ def test_attention_many_heads_sampled(w):
             assert cosine(got, ref) > 0.999 and max_rel(got, ref) < 3e-2, (b, h, name)
 
 
+@pytest.mark.parametrize("dtype,B,T,H,Hkv,w", [
+    (BF, 2, 256, 4, 2, -1), (BF, 1, 512, 6, 1, -1), (BF, 8, 256, 4, 1, -1),
+    (BF, 2, 384, 4, 2, 100), (BF, 8, 256, 2, 1, 64), (F32, 2, 64, 2, 1, -1),
+    (F32, 1, 100, 4, 2, 17)])
+def test_attention_grouped_query_vs_oracle(dtype, B, T, H, Hkv, w):
+    """H query heads over Hkv key/value heads (query head h reads head
+    h // (H / Hkv)): forward, log-sum-exp and gradients against the oracle,
+    dk and dv summed over each key/value head's query heads."""
+    g = H // Hkv
+    d, dk = H * 128, Hkv * 128
+    rng = np.random.default_rng(500 + H * 10 + Hkv + max(w, 0))
+    qkv = dev(rng.standard_normal((B * T, d + 2 * dk)), dtype)
+    dO = dev(rng.standard_normal((B * T, d)), dtype)
+    q, k, v = qkv[:, :d], qkv[:, d:d + dk], qkv[:, d + dk:]
+    o = torch.empty(B * T, d, dtype=dtype, device="cuda")
+    lse = torch.empty(B, H, T, dtype=F32, device="cuda")
+    print(f"[attn gqa] {dtype} B={B} T={T} H={H} Hkv={Hkv} w={w}", flush=True)
+    ld = d + 2 * dk
+    nc.attention_fwd(q, k, v, o, lse, B, T, H, ld, d, window=w, n_kv_head=Hkv)
+    dqkv = torch.zeros_like(qkv)
+    D = torch.empty(B, H, T, dtype=F32, device="cuda")
+    nc.attention_bwd(q, k, v, o, dO, lse, D, dqkv[:, :d], dqkv[:, d:d + dk], dqkv[:, d + dk:],
+                     B, T, H, ld, d, ld, window=w, n_kv_head=Hkv)
+    torch.cuda.synchronize()
+    win = None if w < 0 else w
+    Q = _heads(qkv, B, T, H, 0)
+    K, Vv = (_heads(qkv, B, T, Hkv, c) for c in (d, d + dk))
+    Kr, Vr = np.repeat(K, g, axis=1), np.repeat(Vv, g, axis=1)
+    o_ref, _ = oracle.causal_attention(Q, Kr, Vr, window=win)
+    dq_r, dk_r, dv_r = oracle.causal_attention_backward(Q, Kr, Vr, _heads(dO, B, T, H, 0),
+                                                        window=win)
+    dk_r = dk_r.reshape(B, Hkv, g, T, 128).sum(2)
+    dv_r = dv_r.reshape(B, Hkv, g, T, 128).sum(2)
+    bf = dtype == BF
+    assert max_rel(_heads(o, B, T, H, 0), o_ref) < (2e-2 if bf else 1e-5)
+    assert np.max(np.abs(host(lse) - _band_lse(Q, Kr, T if win is None else win))) < (
+        2e-3 if bf else 1e-5)
+    for name, got, ref in [("dq", _heads(dqkv, B, T, H, 0), dq_r),
+                           ("dk", _heads(dqkv, B, T, Hkv, d), dk_r),
+                           ("dv", _heads(dqkv, B, T, Hkv, d + dk), dv_r)]:
+        assert cosine(got, ref) > (0.999 if bf else 1 - 1e-9), name
+        assert max_rel(got, ref) < (3e-2 if bf else 1e-5), name
+
+
 def test_attention_window_covering_the_row_is_bitwise_causal():
     B, T, H = 1, 384, 2
     d = H * 128

@@ -148,6 +148,20 @@ def test_normuon_two_steps(name):
     m.close()
 
 
+TINY_GQA = ModelConfig(name="tiny_gqa", n_layer=2, d_model=256, n_head=2, head_dim=128,
+                       d_ff=512, vocab=512, seq_len=64, micro_batch=2, accum_steps=1,
+                       dtype="fp32", token_dist="uniform", n_kv_head=1)
+
+
+@pytest.mark.parametrize("name", ["tiny_gqa", "small_gqa", "d12_gqa"])
+def test_grouped_query_attention_full_step(name):
+    """Loss, every gradient and every update with fewer key/value heads than
+    query heads (fp32: 2 heads over 1; small bf16: 3 over 1; d12: 6 over 2)."""
+    cfg = {"tiny_gqa": TINY_GQA, "small_gqa": replace(SMALL_BF16, n_kv_head=1),
+           "d12_gqa": replace(with_batch(D12, micro_batch=1), n_kv_head=2)}[name]
+    check_step(cfg, B=cfg.micro_batch, seed=41, ocfg=OptimConfig(normuon=(name == "small_gqa")))
+
+
 def test_d12_shape_one_row():
     check_step(with_batch(D12, micro_batch=1), B=1, seed=7)
 
