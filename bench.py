@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--window-pattern", default=None,
                     help='sliding-window attention pattern over the layers, e.g. "SSSL" '
                          '(S: short window, L: whole causal context); default: none')
+    ap.add_argument("--kv-heads", type=int, default=0,
+                    help="key/value heads for grouped-query attention (default: one per head)")
     ap.add_argument("--normuon", action="store_true",
                     help="NorMuon per-neuron normalisation after Newton-Schulz")
     ap.add_argument("--short-window", type=int, default=None,
@@ -152,6 +154,9 @@ def main():
 
     cfg = CONFIGS[args.config]
     cfg = with_batch(cfg, micro_batch=args.micro_batch, accum_steps=args.accum)
+    if args.kv_heads:
+        from dataclasses import replace as dc_replace
+        cfg = dc_replace(cfg, n_kv_head=args.kv_heads)
     if args.roofline_only:
         r = roofline_gemm(cfg, args.roofline_iters)
         if args.copy_calibration:
@@ -234,7 +239,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (Zipf(1.1) token ids, N(0, 0.02^2) random-init weights)",
         "config": {"workload": f"{cfg.name} GPT pretraining step: {cfg.n_layer} layers, d {d}, "
-                               f"{cfg.n_head}x128 heads, {attention}, MLP {cfg.d_ff} ReLU^2, "
+                               f"{cfg.n_head}x128 heads"
+                               f"{f' over {cfg.kv_heads} key/value heads' if cfg.kv_heads != cfg.n_head else ''}"
+                               f", {attention}, MLP {cfg.d_ff} ReLU^2, "
                                f"vocab {cfg.vocab}, "
                                f"seq {cfg.seq_len}, micro-batch {cfg.micro_batch} x {K} accumulated "
                                f"= {tokens} tokens/step, Muon ({len(ocfg.ns_coeffs)} Newton-Schulz "
