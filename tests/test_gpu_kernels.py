@@ -375,6 +375,41 @@ def test_attention_grouped_query_vs_oracle(dtype, B, T, H, Hkv, w):
         assert max_rel(got, ref) < (3e-2 if bf else 1e-5), name
 
 
+@pytest.mark.parametrize("w", [-1, 1024])
+def test_attention_d20_launch_sampled(w):
+    """The attention launches of a d20 micro-batch as the step runs them (32
+    rows x 10 heads x 2048 tokens, q/k/v inside one [N, 3d] row): sampled
+    (row, head) pairs against the oracle."""
+    B, T, H = 32, 2048, 10
+    d = H * 128
+    rng = np.random.default_rng(90 + max(w, 0))
+    qkv = dev(rng.standard_normal((B * T, 3 * d), dtype=np.float32), BF)
+    dO = dev(rng.standard_normal((B * T, d), dtype=np.float32), BF)
+    q, k, v = qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:]
+    o = torch.empty(B * T, d, dtype=BF, device="cuda")
+    lse = torch.empty(B, H, T, dtype=F32, device="cuda")
+    print(f"[attn d20] w={w}", flush=True)
+    nc.attention_fwd(q, k, v, o, lse, B, T, H, 3 * d, d, window=w)
+    dqkv = torch.empty_like(qkv)
+    D = torch.empty(B, H, T, dtype=F32, device="cuda")
+    nc.attention_bwd(q, k, v, o, dO, lse, D, dqkv[:, :d], dqkv[:, d:2 * d], dqkv[:, 2 * d:],
+                     B, T, H, 3 * d, d, 3 * d, window=w)
+    torch.cuda.synchronize()
+    win = None if w < 0 else w
+    for b, h in [(0, 0), (13, 7), (31, 9)]:
+        rows = slice(b * T, (b + 1) * T)
+        cols = lambda c0: slice(c0 + h * 128, c0 + (h + 1) * 128)
+        Q, K, Vv = (host(qkv[rows, cols(c)]).astype(np.float64) for c in (0, d, 2 * d))
+        o_ref, _ = oracle.causal_attention(Q, K, Vv, window=win)
+        assert max_rel(host(o[rows, cols(0)]), o_ref) < 2e-2, (b, h)
+        assert np.max(np.abs(host(lse)[b, h] - _band_lse(Q, K, T if win is None else win))) < 2e-3
+        refs = oracle.causal_attention_backward(Q, K, Vv, host(dO[rows, cols(0)]).astype(np.float64),
+                                                window=win)
+        for name, c0, ref in zip(("dq", "dk", "dv"), (0, d, 2 * d), refs):
+            got = host(dqkv[rows, cols(c0)])
+            assert cosine(got, ref) > 0.999 and max_rel(got, ref) < 3e-2, (b, h, name)
+
+
 def test_attention_window_covering_the_row_is_bitwise_causal():
     B, T, H = 1, 384, 2
     d = H * 128
