@@ -144,7 +144,7 @@ def cpu_baseline(cfg, n_tok=2048, windows=None):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
               "(gradient accumulation replaces data parallelism)", file=sys.stderr)
         sys.exit(2)
     import torch

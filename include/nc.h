@@ -43,7 +43,7 @@ extern "C" {
 typedef enum {
   NC_OK = 0,
   NC_ERR_INVALID_ARG = 1,   /* null pointer, bad size, value out of range */
-  NC_ERR_UNSUPPORTED = 2,   /* shape or option this build does not implement */
+  NC_ERR_UNSUPPORTED = 2,   /* shape or option the library does not implement */
   NC_ERR_OUT_OF_MEMORY = 3, /* an arena is smaller than nc_plan requires */
   NC_ERR_HIP = 4,           /* a HIP call or kernel launch failed */
   NC_ERR_STATE = 5,         /* call order: e.g. fwd_bwd before bind */
