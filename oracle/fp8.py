@@ -1,0 +1,68 @@
+"""OCP fp8 e4m3 encoding and tensorwise scaling, in numpy — TEST INFRASTRUCTURE
+ONLY (see the package docstring).
+
+[APIDOG] "3. Manajemen Presisi (nanochat/common.py)": later runs train most
+linear layers in FP8 with tensorwise scaling.  Readings where the page is
+silent: the format is e4m3 of the OCP 8-bit floating point specification
+(sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent 15 with mantissa
+7 is NaN, so the largest finite value is 448; no infinities); the tensorwise
+scale is s = 448 / max|x| (1 when x is all zero), computed in fp32, and a
+value x is stored as e4m3(x * s), the product taken in fp32, rounded to the
+nearest representable value with ties to the even code, saturating at 448.
+
+The encoder here works from the table of all representable values: a plain
+nearest-value search, not the bit manipulation of the HIP kernel.
+"""
+
+import numpy as np
+
+
+def e4m3_decode_table():
+    """float64 value of every code 0..255 (NaN for the two NaN codes)."""
+    vals = np.empty(256, np.float64)
+    for c in range(256):
+        sign = -1.0 if c & 0x80 else 1.0
+        e, m = (c >> 3) & 0xF, c & 7
+        if e == 0xF and m == 7:
+            vals[c] = np.nan
+        elif e == 0:
+            vals[c] = sign * (m / 8.0) * 2.0 ** -6
+        else:
+            vals[c] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return vals
+
+
+_TABLE = e4m3_decode_table()
+_POS = _TABLE[:0x7F]                 # codes 0x00 .. 0x7E: 0 .. 448, increasing
+
+
+def e4m3_encode(x):
+    """Codes (uint8) of float values x: nearest of the 127 non-negative finite
+    values to |x| (|x| above 448 saturates), ties to the even code, sign bit
+    from x."""
+    x = np.asarray(x, np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    hi = np.clip(np.searchsorted(_POS, a, side="left"), 0, 0x7E)
+    lo = np.clip(hi - 1, 0, 0x7E)
+    d_lo, d_hi = a - _POS[lo], _POS[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
+
+
+def e4m3_decode(codes):
+    return _TABLE[np.asarray(codes, np.uint8)]
+
+
+def quantize_tensorwise(x):
+    """(codes, amax, scale) of a tensor: scale = 448 / amax in fp32, codes of
+    x * scale evaluated in fp32."""
+    x32 = np.asarray(x, np.float32)
+    amax = np.float32(np.max(np.abs(x32))) if x32.size else np.float32(0)
+    scale = np.float32(448.0) / amax if amax > 0 else np.float32(1.0)
+    return e4m3_encode((x32 * scale).astype(np.float32)), float(amax), float(scale)
+
+
+def fp8_matmul(a_codes, b_codes, alpha):
+    """alpha * A B^T of two code matrices [M, K], [N, K], in fp64."""
+    return alpha * (e4m3_decode(a_codes) @ e4m3_decode(b_codes).T)
