@@ -734,6 +734,60 @@ inline int grid1d(size_t n, int block = 256) {
   return (int)std::min<size_t>((n + block - 1) / block, 1 << 16);
 }
 
+
+// ------------------------------------------------ fp8 e4m3, tensorwise scale
+// amax: per-block partial maxima of |x| (fixed order), then one block folds them
+template <typename T>
+__global__ __launch_bounds__(256) void amax_partial_kernel(const T* __restrict__ x, int64_t n,
+                                                           float* __restrict__ partial) {
+  __shared__ float red[4];
+  float m = 0.f;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    m = fmaxf(m, fabsf(to_f(x[i])));
+  m = block_max(m, red);
+  if (threadIdx.x == 0) partial[blockIdx.x] = m;
+}
+
+// amax_scale[0] = amax, amax_scale[1] = 448 / amax (1 when amax is 0)
+__global__ __launch_bounds__(256) void amax_final_kernel(const float* __restrict__ partial,
+                                                         int parts,
+                                                         float* __restrict__ amax_scale) {
+  __shared__ float red[4];
+  float m = 0.f;
+  for (int i = threadIdx.x; i < parts; i += 256) m = fmaxf(m, partial[i]);
+  m = block_max(m, red);
+  if (threadIdx.x == 0) {
+    amax_scale[0] = m;
+    amax_scale[1] = m > 0.f ? 448.f / m : 1.f;
+  }
+}
+
+// OCP fp8 e4m3 (bias 7, 3 mantissa bits, largest finite 448, no infinities),
+// round to nearest even, saturating at 448
+NC_DEV unsigned e4m3_rne(float x) {
+  const unsigned sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fminf(fabsf(x), 448.f);
+  if (!(a >= 0x1p-6f)) return sign | (unsigned)rintf(a * 512.f);   // multiples of 2^-9
+  int e;
+  const float f = frexpf(a, &e);                 // a = f 2^e, f in [0.5, 1)
+  float m = rintf((2.f * f - 1.f) * 8.f);        // a = (1 + m/8) 2^(e-1)
+  int E = e - 1 + 7;
+  if (m >= 8.f) {
+    m = 0.f;
+    E += 1;
+  }
+  const unsigned code = min(((unsigned)E << 3) | (unsigned)m, 0x7Eu);
+  return sign | code;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void fp8_quantize_kernel(const T* __restrict__ x, int64_t n,
+                                                           const float* __restrict__ amax_scale,
+                                                           uint8_t* __restrict__ q) {
+  const float sc = amax_scale[1];
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    q[i] = (uint8_t)e4m3_rne(to_f(x[i]) * sc);
+}
 }  // namespace
 
 // =============================================================== launchers
@@ -955,5 +1009,21 @@ hipError_t nc_normuon_stats(const float* X, int64_t x_stride, int R, int C, int 
   dim3 grid(transpose ? ceil_div(R, 256) : ceil_div(R, 4), count);
   normuon_rows_kernel<<<grid, 256, 0, st>>>(X, x_stride, R, C, transpose, v2, beta2, vm, q, inv);
   normuon_scale_kernel<<<count, 256, 0, st>>>(vm, q, R, scale);
+  return hipGetLastError();
+}
+
+hipError_t nc_fp8_quantize(int dtype, const void* x, int64_t n, float* partial,
+                           float* amax_scale, uint8_t* q, hipStream_t st) {
+  const int parts = (int)std::min<int64_t>(std::max<int64_t>(ceil_div64(n, 256), 1), 1024);
+  if (dtype)
+    amax_partial_kernel<bf16><<<parts, 256, 0, st>>>((const bf16*)x, n, partial);
+  else
+    amax_partial_kernel<float><<<parts, 256, 0, st>>>((const float*)x, n, partial);
+  amax_final_kernel<<<1, 256, 0, st>>>(partial, parts, amax_scale);
+  const int blocks = (int)std::min<int64_t>(std::max<int64_t>(ceil_div64(n, 256), 1), 8192);
+  if (dtype)
+    fp8_quantize_kernel<bf16><<<blocks, 256, 0, st>>>((const bf16*)x, n, amax_scale, q);
+  else
+    fp8_quantize_kernel<float><<<blocks, 256, 0, st>>>((const float*)x, n, amax_scale, q);
   return hipGetLastError();
 }

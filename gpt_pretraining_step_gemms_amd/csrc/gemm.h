@@ -37,6 +37,9 @@ struct GemmParams {
 
 // dtype: 0 = fp32 operands (VALU kernel), 1 = bf16 operands (MFMA kernel)
 hipError_t nc_launch_gemm(int dtype, const GemmParams& p, hipStream_t stream);
+// fp8 e4m3 operands (bytes), both K-contiguous: K % 128 == 0, lda, ldb (and batch
+// strides) % 16 == 0, 16-byte aligned; epilogues as for bf16, no split-K
+hipError_t nc_launch_gemm_f8(const GemmParams& p, hipStream_t stream);
 // splits a weight-gradient GEMM would use for M x N with reduction K (bf16 path)
 int nc_gemm_pick_splits(int M, int N, int K);
 size_t nc_gemm_workspace_bytes(int M, int N, int splits);

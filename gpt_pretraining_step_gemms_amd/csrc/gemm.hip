@@ -700,11 +700,29 @@ NC_DEV void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int AL, int BL, int WM_, int WN_, int ST_, int PK_, int MI_>
+// One v_mfma_f32_16x16x128_f8f6f4 (fp8 e4m3 on both operands): a lane's 32
+// operand bytes are the two 16-byte fragments the bf16 path reads for the two
+// 32-deep substeps of a 64-element (128-byte) k-step.  Both operands take the
+// same byte positions, so each of the step's 128 k is summed exactly once.
+NC_DEV f32x4 mfma_f8(bf16x8 a0, bf16x8 a1, bf16x8 b0, bf16x8 b1, f32x4 c) {
+  typedef int i32x8 __attribute__((ext_vector_type(8)));
+  const i32x4 x0 = __builtin_bit_cast(i32x4, a0), x1 = __builtin_bit_cast(i32x4, a1);
+  const i32x4 y0 = __builtin_bit_cast(i32x4, b0), y1 = __builtin_bit_cast(i32x4, b1);
+  const i32x8 a = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+  const i32x8 b = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// F8: operands are fp8 e4m3 bytes, handled by the loads as pairs (the
+// launcher halves K and the leading dimensions), K-contiguous, half-stage ring
+// with 16 x 16 MFMAs only.
+template <int AL, int BL, int WM_, int WN_, int ST_, int PK_, int MI_, bool F8 = false>
 __global__ __launch_bounds__(WM_ * WN_ * 64, (Pipe<WM_, WN_, ST_, PK_, MI_>::kBlocksPerCU))
 void gemm_bf16_pipe_kernel(GemmParams p) {
   using C = Pipe<WM_, WN_, ST_, PK_, MI_>;
   constexpr int MI = C::MI;
+  static_assert(!F8 || (MI == 16 && PK_ == 64 && ST_ == 5 && AL == kKCont && BL == kKCont),
+                "fp8: K-contiguous operands in the 64-deep half-stage ring");
   using AccT = std::conditional_t<MI == 32, f32x16, f32x4>;
   constexpr int ACC_N = MI == 32 ? 16 : 4;
   constexpr int BM = C::BM, BN = C::BN, PK = C::PK, STAGES = C::STAGES, WN = C::WN;
@@ -821,6 +839,42 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
       if (r < TM) dst = frag<BM, AL, PK, MI>(as, wm * WTM + r * MI, s, lane);
       else dst = frag<BN, BL, PK, MI>(bs, wn * WTN + (r - TM) * MI, s, lane);
     };
+    // next tiles' loads, one at MFMA index u of the step
+    auto load_at = [&](int u) {
+      if constexpr (HALF) {
+        const int l = u / MPL;
+        if (u < SPAN && u % MPL == 0 && l < LOADS && (l < LOADS_B ? more : more_a2)) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (l < LOADS_B)
+            issue_one<BN, BL, LOADS_B, PK>(ob, n0, ktn * PK, nxt_b, wave, l);
+          else
+            issue_one<BM, AL, LOADS_A, PK>(oa, m0, (ktn + 1) * PK, nxt_a2, wave, l - LOADS_B);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else if (u < SPAN && u % MPL == 0 && u / MPL < LOADS && more) {
+        const int l = u / MPL;                       // load index
+        __builtin_amdgcn_sched_barrier(0);
+        if (l < LOADS_A)
+          issue_one<BM, AL, LOADS_A, PK>(oa, m0, ktn * PK, nxt, wave, l);
+        else
+          issue_one<BN, BL, LOADS_B, PK>(ob, n0, ktn * PK, nxt_b, wave, l - LOADS_A);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    if constexpr (F8) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        read_one(0, r, fr[0][r]);
+        read_one(1, r, fr[1][r]);
+      }
+#pragma unroll
+      for (int t = 0; t < NM; ++t) {
+        const int ii = t / TN, j = t % TN;
+        acc[ii][j] = mfma_f8(fr[0][ii], fr[1][ii], fr[0][TM + j], fr[1][TM + j], acc[ii][j]);
+        load_at(t);
+      }
+      return;
+    }
     if constexpr (PREF) {
 #pragma unroll
       for (int r = 0; r < NR; ++r) read_one(0, r, fr[0][r]);
@@ -845,26 +899,7 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
           read_one(s + 1, t, nxf[t]);
           __builtin_amdgcn_sched_barrier(0);
         }
-        const int u = s * NM + t;                      // MFMA index within the step
-        if constexpr (HALF) {
-          const int l = u / MPL;
-          if (u < SPAN && u % MPL == 0 && l < LOADS && (l < LOADS_B ? more : more_a2)) {
-            __builtin_amdgcn_sched_barrier(0);
-            if (l < LOADS_B)
-              issue_one<BN, BL, LOADS_B, PK>(ob, n0, ktn * PK, nxt_b, wave, l);
-            else
-              issue_one<BM, AL, LOADS_A, PK>(oa, m0, (ktn + 1) * PK, nxt_a2, wave, l - LOADS_B);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        } else if (u < SPAN && u % MPL == 0 && u / MPL < LOADS && more) {
-          const int l = u / MPL;                       // load index
-          __builtin_amdgcn_sched_barrier(0);
-          if (l < LOADS_A)
-            issue_one<BM, AL, LOADS_A, PK>(oa, m0, ktn * PK, nxt, wave, l);
-          else
-            issue_one<BN, BL, LOADS_B, PK>(ob, n0, ktn * PK, nxt_b, wave, l - LOADS_A);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        load_at(s * NM + t);                           // MFMA index within the step
       }
     }
   };
@@ -1009,12 +1044,12 @@ bool pipe_ok(const GemmParams& p) {
   return true;
 }
 
-template <int AL, int BL, int WM, int WN, int ST, int PK, int MI>
+template <int AL, int BL, int WM, int WN, int ST, int PK, int MI, bool F8 = false>
 hipError_t launch_pipe_cfg(const GemmParams& p, hipStream_t st) {
   using C = Pipe<WM, WN, ST, PK, MI>;
   const int tiles = ceil_div(p.M, C::BM) * ceil_div(p.N, C::BN);
   dim3 grid(tiles, 1, p.batch * p.splits);
-  gemm_bf16_pipe_kernel<AL, BL, WM, WN, ST, PK, MI><<<grid, C::NT, 0, st>>>(p);
+  gemm_bf16_pipe_kernel<AL, BL, WM, WN, ST, PK, MI, F8><<<grid, C::NT, 0, st>>>(p);
   return hipGetLastError();
 }
 
@@ -1076,6 +1111,26 @@ int nc_gemm_pick_splits(int M, int N, int K) {
 
 size_t nc_gemm_workspace_bytes(int M, int N, int splits) {
   return splits > 1 ? (size_t)splits * M * N * sizeof(float) : 0;
+}
+
+hipError_t nc_launch_gemm_f8(const GemmParams& p_in, hipStream_t st) {
+  GemmParams p = p_in;
+  if (p.M <= 0 || p.N <= 0 || p.batch <= 0) return hipSuccess;
+  auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+  if (p.a_layout != kKCont || p.b_layout != kKCont || p.K <= 0 || p.K % 128 || p.lda % 16 ||
+      p.ldb % 16 || (p.batch > 1 && (p.sA % 16 || p.sB % 16)) || !al16(p.A) || !al16(p.B))
+    return hipErrorInvalidValue;
+  p.splits = 1;
+  p.vec_epi = p.ldc % 8 == 0 && (p.batch == 1 || p.sC % 8 == 0) && al16(p.C) &&
+              al16(p.aux_in) && al16(p.aux_out);
+  // the loads move byte pairs: K, leading dimensions and batch strides in pairs
+  p.K /= 2;
+  p.lda /= 2;
+  p.ldb /= 2;
+  p.sA /= 2;
+  p.sB /= 2;
+  if (!pipe_ok(p)) return hipErrorInvalidValue;
+  return launch_pipe_cfg<kKCont, kKCont, 2, 4, 5, 64, 16, true>(p, st);
 }
 
 hipError_t nc_launch_gemm(int dtype, const GemmParams& p_in, hipStream_t st) {

@@ -42,6 +42,12 @@ hipError_t nc_attn_bwd(int dtype, const void* q, const void* k, const void* v, i
                        void* dq, void* dk, void* dv, int64_t ld_dqkv, int B, int T, int H,
                        int Hkv, int window, hipStream_t st);
 
+// ---- fp8 e4m3 with one scale per tensor: amax_scale[0] = max |x|, amax_scale[1] =
+// 448 / amax (1 if amax = 0), q[i] = e4m3(x[i] * scale) (round to nearest even,
+// saturating); partial: 1024 floats of scratch
+hipError_t nc_fp8_quantize(int dtype, const void* x, int64_t n, float* partial,
+                           float* amax_scale, uint8_t* q, hipStream_t st);
+
 // ---- softmax cross-entropy over rows of fp32 logits
 // dz = scale*(softmax(z) - onehot(y)) in the activation type; loss_rows[i] = lse - z[y]
 hipError_t nc_cross_entropy(int dtype, const float* z, const int32_t* tgt, void* dz,

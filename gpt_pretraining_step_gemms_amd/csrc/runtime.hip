@@ -898,6 +898,35 @@ nc_status nc_op_gemm(int32_t dtype, const void* A_, int64_t lda, int32_t al, con
                                                                                  : NC_ERR_HIP;
 }
 
+nc_status nc_op_gemm_fp8(const void* A_, int64_t lda, const void* B_, int64_t ldb, void* C_,
+                         int64_t ldc, int32_t M, int32_t N, int32_t K, int32_t epi, float alpha,
+                         void* stream) {
+  if (!A_ || !B_ || !C_ || M < 0 || N < 0 || K < 1) return NC_ERR_INVALID_ARG;
+  if (epi != kEpiStore && epi != kEpiStoreF32) return NC_ERR_INVALID_ARG;
+  if (lda < K || ldb < K || ldc < N) return NC_ERR_INVALID_ARG;
+  if (K % 128 || lda % 16 || ldb % 16) return NC_ERR_UNSUPPORTED;
+  GemmParams g{};
+  g.A = A_; g.B = B_; g.C = C_;
+  g.lda = lda; g.ldb = ldb; g.ldc = ldc;
+  g.M = M; g.N = N; g.K = K; g.batch = 1; g.splits = 1;
+  g.a_layout = kKCont; g.b_layout = kKCont; g.epi = epi;
+  g.alpha = alpha;
+  const hipError_t e = nc_launch_gemm_f8(g, static_cast<hipStream_t>(stream));
+  if (e == hipErrorInvalidValue) return NC_ERR_UNSUPPORTED;
+  return e == hipSuccess ? NC_OK : NC_ERR_HIP;
+}
+
+nc_status nc_op_fp8_quantize(int32_t dtype, const void* x, int64_t n, float* amax_scale,
+                             void* q, float* workspace, void* stream) {
+  if (!x || !amax_scale || !q || !workspace || n < 1) return NC_ERR_INVALID_ARG;
+  if (dtype != NC_FP32 && dtype != NC_BF16) return NC_ERR_INVALID_ARG;
+  return nc_fp8_quantize(dtype == NC_BF16, x, n, workspace, amax_scale,
+                         static_cast<uint8_t*>(q), static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? NC_OK
+             : NC_ERR_HIP;
+}
+
 nc_status nc_op_attention_fwd(int32_t dtype, const void* q, const void* k, const void* v,
                               int64_t ld_qkv, void* o, int64_t ld_o, float* lse, int32_t B,
                               int32_t T, int32_t H, int32_t n_kv_head, int32_t window,

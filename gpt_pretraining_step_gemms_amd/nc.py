@@ -90,6 +90,8 @@ def load():
         "nc_flops": [P, I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)],
         "nc_op_gemm": [I32, P, I64, I32, P, I64, I32, P, I64, I32, I32, I32, I32, I64, I64, I64,
                        I32, P, P, F32, F32, F32, I32, P, SZ, P],
+        "nc_op_gemm_fp8": [P, I64, P, I64, P, I64, I32, I32, I32, I32, F32, P],
+        "nc_op_fp8_quantize": [I32, P, I64, P, P, P, P],
         "nc_op_attention_fwd": [I32, P, P, P, I64, P, I64, P, I32, I32, I32, I32, I32, P],
         "nc_op_attention_bwd": [I32, P, P, P, I64, P, P, I64, P, P, P, P, P, I64, I32, I32, I32,
                                 I32, I32, P],
@@ -316,3 +318,21 @@ def attention_bwd(q, k, v, o, dO, lse, D, dq, dk, dv, B, T, H, ld_qkv, ld_o, ld_
                                 ld_d, B, T, H, n_kv_head or H, window,
                                 ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     _check(s, what="nc_op_attention_bwd")
+
+
+def gemm_fp8(A8, B8, C, M, N, K, alpha, epilogue=EPI_STORE, lda=None, ldb=None, ldc=None):
+    """C = alpha * A8 B8^T for K-contiguous uint8 (fp8 e4m3) operands."""
+    lib = load()
+    s = lib.nc_op_gemm_fp8(_ptr(A8), lda or A8.shape[-1], _ptr(B8), ldb or B8.shape[-1], _ptr(C),
+                           ldc or C.shape[-1], M, N, K, epilogue, alpha,
+                           ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    _check(s, what="nc_op_gemm_fp8")
+
+
+def fp8_quantize(x, q, amax_scale, workspace):
+    """q (uint8, x.numel()) = e4m3(x * 448 / amax); amax_scale (2 floats) = amax, scale."""
+    lib = load()
+    s = lib.nc_op_fp8_quantize(_dtype_code(x), _ptr(x), x.numel(), _ptr(amax_scale), _ptr(q),
+                               _ptr(workspace),
+                               ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    _check(s, what="nc_op_fp8_quantize")

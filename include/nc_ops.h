@@ -51,6 +51,25 @@ nc_status nc_op_gemm(int32_t dtype, const void* A, int64_t lda, int32_t a_layout
                      float p1, int32_t splits, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/* fp8 GEMM: C[m, n] = alpha * sum_k A(m, k) B(n, k) with A [M, K] and B [N, K]
+ * K-contiguous OCP fp8 e4m3 bytes (row strides lda, ldb in bytes), fp32
+ * accumulation; C bf16 (NC_EPI_STORE) or fp32 (NC_EPI_STORE_F32) with row
+ * stride ldc elements.  The pages' later runs train most linear layers in FP8
+ * with one scale per tensor (apidog.com, "3. Manajemen Presisi
+ * (nanochat/common.py)"); alpha carries the product of the two inverse scales.
+ * Requirements: K % 128 == 0, lda and ldb multiples of 16, 16-byte aligned
+ * operands (NC_ERR_UNSUPPORTED otherwise). */
+nc_status nc_op_gemm_fp8(const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                         int64_t ldc, int32_t M, int32_t N, int32_t K, int32_t epilogue,
+                         float alpha, void* stream);
+
+/* Tensorwise fp8 quantisation of n values x (dtype NC_FP32 or NC_BF16):
+ * amax_scale[0] = max |x|, amax_scale[1] = s = 448 / amax (1 if amax = 0), and
+ * q[i] = e4m3(x[i] * s) rounded to nearest even and saturated at 448, so that
+ * x ~ q / s.  amax_scale: 2 device floats; workspace: 1024 device floats. */
+nc_status nc_op_fp8_quantize(int32_t dtype, const void* x, int64_t n, float* amax_scale,
+                             void* q, float* workspace, void* stream);
+
 /* Causal attention forward, head dim 128, scale 1/sqrt(128).  q, k, v:
  * token-major rows (row b*T + t, head h at columns h*128 .. h*128+127, row
  * stride ld_qkv elements); q has H heads, k and v n_kv_head heads (n_kv_head

@@ -448,3 +448,79 @@ def test_attention_causality_bitwise():
     torch.cuda.synchronize()
     assert torch.equal(outs[0][:200], outs[1][:200])
     assert not torch.equal(outs[0][200:], outs[1][200:])
+
+
+# ------------------------------------------------------------------------ fp8
+from oracle import fp8 as ofp8  # noqa: E402
+
+
+@pytest.mark.parametrize("dtype,n", [(F32, 1000), (F32, 300001), (BF, 65536 + 7)])
+def test_fp8_quantize_bit_exact(dtype, n):
+    """Tensorwise e4m3 quantisation: amax and scale exact, every byte equal to
+    the oracle's (same fp32 products; rounding decided on the same values)."""
+    rng = np.random.default_rng(n)
+    x = rng.standard_normal(n).astype(np.float32) * rng.uniform(0.01, 5.0)
+    x[:7] = [0.0, -0.0, 1e-12, -3e-9, 1e-4, 2.5, -2.5]
+    xd = dev(x, dtype)
+    xs = host(xd).astype(np.float32)                 # the values the GPU sees
+    q = torch.empty(n, dtype=torch.uint8, device="cuda")
+    amax_scale = torch.empty(2, dtype=F32, device="cuda")
+    ws = torch.empty(1024, dtype=F32, device="cuda")
+    nc.fp8_quantize(xd, q, amax_scale, ws)
+    torch.cuda.synchronize()
+    codes, amax, scale = ofp8.quantize_tensorwise(xs)
+    got_amax, got_scale = host(amax_scale)
+    assert got_amax == amax and got_scale == scale
+    got = q.cpu().numpy()
+    assert np.array_equal(got, codes), np.flatnonzero(got != codes)[:10]
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 128), (300, 520, 256), (1024, 768, 1280),
+                                   (70, 40, 384), (513, 1000, 2048)])
+def test_fp8_gemm_vs_oracle(M, N, K):
+    """C = alpha A B^T on e4m3 codes against the fp64 product of the decoded
+    values.  The products are exact, but the fp8 MFMA's internal sums round
+    more coarsely than fp32 (about 4e-5 of the largest output at K = 128 on
+    gfx950, against 1e-7 for fp32 sums): the bound is 2e-4, while a wrong
+    pairing of k positions gives errors of order one."""
+    rng = np.random.default_rng(M + N + K)
+    a, _, sa = ofp8.quantize_tensorwise(rng.standard_normal((M, K)))
+    b, _, sb = ofp8.quantize_tensorwise(0.02 * rng.standard_normal((N, K)))
+    alpha = 1.0 / (sa * sb)
+    ref = ofp8.fp8_matmul(a, b, alpha)
+    A8 = torch.from_numpy(a).cuda()
+    B8 = torch.from_numpy(b).cuda()
+    print(f"[fp8 gemm] M={M} N={N} K={K}", flush=True)
+    Cf = torch.empty(M, N, dtype=F32, device="cuda")
+    nc.gemm_fp8(A8, B8, Cf, M, N, K, alpha, epilogue=nc.EPI_STORE_F32)
+    Cb = torch.empty(M, N, dtype=BF, device="cuda")
+    nc.gemm_fp8(A8, B8, Cb, M, N, K, alpha, epilogue=nc.EPI_STORE)
+    torch.cuda.synchronize()
+    err = max_rel(host(Cf), ref)
+    print(f"[fp8 gemm] max-rel {err:.2e}", flush=True)
+    assert err < 2e-4
+    assert max_rel(host(Cb), ref) < 2 ** -8
+
+
+def test_fp8_gemm_rejects_unsupported_shapes():
+    A8 = torch.zeros(64, 192, dtype=torch.uint8, device="cuda")
+    C = torch.empty(64, 64, dtype=F32, device="cuda")
+    with pytest.raises(nc.NcError):                  # K not a multiple of 128
+        nc.gemm_fp8(A8, A8, C, 64, 64, 192, 1.0, epilogue=nc.EPI_STORE_F32)
+
+
+def test_fp8_gemm_mlp_up_shape_sampled():
+    """The MLP up-projection shape of a d20 micro-batch in fp8: sampled rows."""
+    M, N, K = 65536, 5120, 1280
+    g = torch.Generator(device="cuda").manual_seed(5)
+    A8 = torch.randint(0, 256, (M, K), dtype=torch.uint8, device="cuda", generator=g)
+    B8 = torch.randint(0, 256, (N, K), dtype=torch.uint8, device="cuda", generator=g)
+    for t in (A8, B8):                               # no NaN codes; keep magnitudes modest
+        t &= 0xB7
+    C = torch.empty(M, N, dtype=F32, device="cuda")
+    nc.gemm_fp8(A8, B8, C, M, N, K, 0.25, epilogue=nc.EPI_STORE_F32)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 255, 256, 40000, M - 1])
+    a = A8[torch.from_numpy(rows).cuda()].cpu().numpy()
+    ref = ofp8.fp8_matmul(a, B8.cpu().numpy(), 0.25)
+    assert max_rel(host(C[torch.from_numpy(rows).cuda()]), ref) < 2e-4
