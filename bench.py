@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--roofline-only", action="store_true",
                     help="only the dominant-kernel timing loop (for profiling it alone)")
     ap.add_argument("--roofline-iters", type=int, default=20)
+    ap.add_argument("--roofline-fp8", action="store_true",
+                    help="only the fp8 GEMM at the MLP up-projection shape (tensorwise e4m3)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="with --roofline-only: also run a 1 GiB copy kernel (counter scale)")
     return ap.parse_args()
@@ -79,6 +81,45 @@ def roofline_gemm(cfg, iters):
             "bound": "mfma", "achieved": flops / sec / 1e12, "peak": PEAK_BF16 / 1e12,
             "unit": "TFLOP/s", "frac": flops / sec / PEAK_BF16,
             "traffic": measured_traffic(2 * (M * K + N * K + M * N))}
+
+
+PEAK_FP8 = 5.0e15           # MI355X dense fp8 MFMA, FLOP/s
+
+
+def roofline_gemm_fp8(cfg, iters):
+    """fp8 e4m3 GEMM at the MLP up-projection shape of one micro-batch, both
+    operands quantised with one scale per tensor, bf16 output."""
+    import torch
+    from gpt_pretraining_step_gemms_amd import nc
+    M, N, K = cfg.micro_batch * cfg.seq_len, cfg.d_ff, cfg.d_model
+    A = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+    B = (0.02 * torch.randn(N, K, device="cuda")).to(torch.bfloat16)
+    A8 = torch.empty(M, K, dtype=torch.uint8, device="cuda")
+    B8 = torch.empty(N, K, dtype=torch.uint8, device="cuda")
+    sa = torch.empty(2, device="cuda")
+    sb = torch.empty(2, device="cuda")
+    ws = torch.empty(1024, device="cuda")
+    nc.fp8_quantize(A, A8, sa, ws)
+    nc.fp8_quantize(B, B8, sb, ws)
+    alpha = 1.0 / (sa[1].item() * sb[1].item())
+    C = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        nc.gemm_fp8(A8, B8, C, M, N, K, alpha)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(iters):
+        nc.gemm_fp8(A8, B8, C, M, N, K, alpha)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    sec = t0.elapsed_time(t1) / 1e3 / iters
+    flops = 2.0 * M * N * K
+    return {"kernel": "gemm_bf16_pipe_kernel<KCont, KCont, ..., fp8> (e4m3, bf16 output)",
+            "shape": [M, N, K], "avg_launch_us": sec * 1e6, "bound": "mfma",
+            "achieved": flops / sec / 1e12, "peak": PEAK_FP8 / 1e12, "unit": "TFLOP/s",
+            "frac": flops / sec / PEAK_FP8}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_mlp_up_relu2_d20_traffic.txt")
@@ -157,6 +198,9 @@ def main():
     if args.kv_heads:
         from dataclasses import replace as dc_replace
         cfg = dc_replace(cfg, n_kv_head=args.kv_heads)
+    if args.roofline_fp8:
+        print(json.dumps({"roofline_fp8": roofline_gemm_fp8(cfg, args.roofline_iters)}))
+        return
     if args.roofline_only:
         r = roofline_gemm(cfg, args.roofline_iters)
         if args.copy_calibration:
