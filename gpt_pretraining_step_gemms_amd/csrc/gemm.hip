@@ -26,7 +26,8 @@ constexpr int BK = 64;
 NC_DEV int swz(int row, int chunk) { return chunk ^ ((row ^ (row >> 3)) & 7); }
 
 // ------------------------------------------------------------------ epilogue
-// One output element at offset `off` of C (and of aux_in / aux_out).
+// One output element at offset `off` of C (and of aux_in / aux_out); every
+// epilogue takes acc = alpha * v.
 template <typename T, int EPI>
 NC_DEV void epi_one(const GemmParams& p, int64_t off, float v) {
   if constexpr (EPI == kEpiStore) {
@@ -36,18 +37,18 @@ NC_DEV void epi_one(const GemmParams& p, int64_t off, float v) {
   } else if constexpr (EPI == kEpiAccF32) {
     static_cast<float*>(p.C)[off] += p.alpha * v;
   } else if constexpr (EPI == kEpiRelu2) {
-    const float r = fmaxf(v, 0.f);
+    const float r = fmaxf(p.alpha * v, 0.f);
     static_cast<T*>(p.C)[off] = to_t<T>(r * r);
   } else if constexpr (EPI == kEpiRelu2Bwd) {
     // v_sqrt_f32 (1 ulp) rather than the correctly rounded library sequence
     const float g = to_f(static_cast<const T*>(p.aux_in)[off]);
-    static_cast<T*>(p.C)[off] = to_t<T>(2.f * __builtin_amdgcn_sqrtf(fmaxf(g, 0.f)) * v);
+    static_cast<T*>(p.C)[off] = to_t<T>(2.f * __builtin_amdgcn_sqrtf(fmaxf(g, 0.f)) * (p.alpha * v));
   } else if constexpr (EPI == kEpiPoly) {
     const float a = to_f(static_cast<const T*>(p.aux_in)[off]);
-    static_cast<T*>(p.C)[off] = to_t<T>(p.p0 * a + p.p1 * v);
+    static_cast<T*>(p.C)[off] = to_t<T>(p.p0 * a + p.p1 * (p.alpha * v));
   } else {  // kEpiDual
     const float a = p.aux_in ? static_cast<const float*>(p.aux_in)[off] : 0.f;
-    const float r = p.p0 * a + p.p1 * v;
+    const float r = p.p0 * a + p.p1 * (p.alpha * v);
     static_cast<float*>(p.C)[off] = r;
     static_cast<T*>(p.aux_out)[off] = to_t<T>(r);
   }
@@ -103,19 +104,19 @@ NC_DEV void epi_vec8(const GemmParams& p, int64_t off, const float (&v)[8]) {
   } else if constexpr (EPI == kEpiRelu2) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float t = fmaxf(v[e], 0.f);
+      const float t = fmaxf(p.alpha * v[e], 0.f);
       r[e] = t * t;
     }
     st8(static_cast<bf16*>(p.C) + off, r);
   } else if constexpr (EPI == kEpiRelu2Bwd) {
     ld8(static_cast<const bf16*>(p.aux_in) + off, a);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = 2.f * __builtin_amdgcn_sqrtf(fmaxf(a[e], 0.f)) * v[e];
+    for (int e = 0; e < 8; ++e) r[e] = 2.f * __builtin_amdgcn_sqrtf(fmaxf(a[e], 0.f)) * (p.alpha * v[e]);
     st8(static_cast<bf16*>(p.C) + off, r);
   } else if constexpr (EPI == kEpiPoly) {
     ld8(static_cast<const bf16*>(p.aux_in) + off, a);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = p.p0 * a[e] + p.p1 * v[e];
+    for (int e = 0; e < 8; ++e) r[e] = p.p0 * a[e] + p.p1 * (p.alpha * v[e]);
     st8(static_cast<bf16*>(p.C) + off, r);
   } else {  // kEpiDual
     if (p.aux_in) {
@@ -125,7 +126,7 @@ NC_DEV void epi_vec8(const GemmParams& p, int64_t off, const float (&v)[8]) {
       for (int e = 0; e < 8; ++e) a[e] = 0.f;
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = p.p0 * a[e] + p.p1 * v[e];
+    for (int e = 0; e < 8; ++e) r[e] = p.p0 * a[e] + p.p1 * (p.alpha * v[e]);
     st8(static_cast<float*>(p.C) + off, r);
     st8(static_cast<bf16*>(p.aux_out) + off, r);
   }
@@ -184,15 +185,15 @@ NC_DEV void epi_apply8(const GemmParams& p, int64_t off, const float (&v)[8],
     st8(static_cast<float*>(p.C) + off, r);
   } else if constexpr (EPI == kEpiRelu2Bwd) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = 2.f * __builtin_amdgcn_sqrtf(fmaxf(a[e], 0.f)) * v[e];
+    for (int e = 0; e < 8; ++e) r[e] = 2.f * __builtin_amdgcn_sqrtf(fmaxf(a[e], 0.f)) * (p.alpha * v[e]);
     st8(static_cast<bf16*>(p.C) + off, r);
   } else if constexpr (EPI == kEpiPoly) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = p.p0 * a[e] + p.p1 * v[e];
+    for (int e = 0; e < 8; ++e) r[e] = p.p0 * a[e] + p.p1 * (p.alpha * v[e]);
     st8(static_cast<bf16*>(p.C) + off, r);
   } else if constexpr (EPI == kEpiDual) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = p.p0 * a[e] + p.p1 * v[e];
+    for (int e = 0; e < 8; ++e) r[e] = p.p0 * a[e] + p.p1 * (p.alpha * v[e]);
     st8(static_cast<float*>(p.C) + off, r);
     st8(static_cast<bf16*>(p.aux_out) + off, r);
   } else {

@@ -902,7 +902,8 @@ nc_status nc_op_gemm_fp8(const void* A_, int64_t lda, const void* B_, int64_t ld
                          int64_t ldc, int32_t M, int32_t N, int32_t K, int32_t epi, float alpha,
                          void* stream) {
   if (!A_ || !B_ || !C_ || M < 0 || N < 0 || K < 1) return NC_ERR_INVALID_ARG;
-  if (epi != kEpiStore && epi != kEpiStoreF32) return NC_ERR_INVALID_ARG;
+  if (epi != kEpiStore && epi != kEpiStoreF32 && epi != kEpiAccF32 && epi != kEpiRelu2)
+    return NC_ERR_INVALID_ARG;
   if (lda < K || ldb < K || ldc < N) return NC_ERR_INVALID_ARG;
   if (K % 128 || lda % 16 || ldb % 16) return NC_ERR_UNSUPPORTED;
   GemmParams g{};

@@ -51,10 +51,11 @@ nc_status nc_op_gemm(int32_t dtype, const void* A, int64_t lda, int32_t a_layout
                      float p1, int32_t splits, void* workspace, size_t workspace_bytes,
                      void* stream);
 
-/* fp8 GEMM: C[m, n] = alpha * sum_k A(m, k) B(n, k) with A [M, K] and B [N, K]
+/* fp8 GEMM: acc[m, n] = alpha * sum_k A(m, k) B(n, k) with A [M, K] and B [N, K]
  * K-contiguous OCP fp8 e4m3 bytes (row strides lda, ldb in bytes), fp32
- * accumulation; C bf16 (NC_EPI_STORE) or fp32 (NC_EPI_STORE_F32) with row
- * stride ldc elements.  The pages' later runs train most linear layers in FP8
+ * accumulation; the epilogue writes C (row stride ldc elements): NC_EPI_STORE
+ * (bf16), NC_EPI_STORE_F32, NC_EPI_ACC_F32 (C += acc) or NC_EPI_RELU2 (bf16
+ * max(acc, 0)^2), as for nc_op_gemm.  The pages' later runs train most linear layers in FP8
  * with one scale per tensor (apidog.com, "3. Manajemen Presisi
  * (nanochat/common.py)"); alpha carries the product of the two inverse scales.
  * Requirements: K % 128 == 0, lda and ldb multiples of 16, 16-byte aligned

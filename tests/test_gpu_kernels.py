@@ -102,26 +102,30 @@ def test_gemm_epilogues_bf16(K):
     # ReLU^2 forward: g = max(h,0)^2
     G = torch.empty(M, N, dtype=BF, device="cuda")
     nc.gemm(dA, 0, dB, 0, G, M, N, K, nc.EPI_RELU2)
+    G2 = torch.empty(M, N, dtype=BF, device="cuda")     # acc = alpha A B^T in every epilogue
+    nc.gemm(dA, 0, dB, 0, G2, M, N, K, nc.EPI_RELU2, alpha=-0.5)
     # ReLU^2 backward (from the stored activation g >= 0, some entries 0) and the
     # Newton-Schulz polynomial read an auxiliary input
     aux = dev(rng.standard_normal((M, N)), BF)
     gst = dev(np.maximum(rng.standard_normal((M, N)), 0) ** 2, BF)
     R = torch.empty(M, N, dtype=BF, device="cuda")
-    nc.gemm(dA, 0, dB, 0, R, M, N, K, nc.EPI_RELU2_BWD, aux_in=gst)
+    nc.gemm(dA, 0, dB, 0, R, M, N, K, nc.EPI_RELU2_BWD, aux_in=gst, alpha=0.75)
     Pn = torch.empty(M, N, dtype=BF, device="cuda")
-    nc.gemm(dA, 0, dB, 0, Pn, M, N, K, nc.EPI_POLY, aux_in=aux, p0=1.5, p1=-0.25)
+    nc.gemm(dA, 0, dB, 0, Pn, M, N, K, nc.EPI_POLY, aux_in=aux, p0=1.5, p1=-0.25, alpha=2.0)
     aux32 = dev(rng.standard_normal((M, N)), F32)
     D32 = torch.empty(M, N, dtype=F32, device="cuda")
     Dh = torch.empty(M, N, dtype=BF, device="cuda")
-    nc.gemm(dA, 0, dB, 0, D32, M, N, K, nc.EPI_DUAL, aux_in=aux32, aux_out=Dh, p0=3.0, p1=0.5)
+    nc.gemm(dA, 0, dB, 0, D32, M, N, K, nc.EPI_DUAL, aux_in=aux32, aux_out=Dh, p0=3.0, p1=0.5,
+            alpha=0.25)
     torch.cuda.synchronize()
     tol = 2 ** -8
     assert max_rel(host(C), 0.5 * acc) < tol
     assert max_rel(host(Cacc), C0 + acc) < 2e-6
     assert max_rel(host(G), np.maximum(acc, 0) ** 2) < tol
-    assert max_rel(host(R), 2 * np.sqrt(host(gst)) * acc) < tol
-    assert max_rel(host(Pn), 1.5 * host(aux) - 0.25 * acc) < tol
-    dual = 3.0 * host(aux32) + 0.5 * acc
+    assert max_rel(host(G2), np.maximum(-0.5 * acc, 0) ** 2) < tol
+    assert max_rel(host(R), 2 * np.sqrt(host(gst)) * 0.75 * acc) < tol
+    assert max_rel(host(Pn), 1.5 * host(aux) - 0.25 * 2.0 * acc) < tol
+    dual = 3.0 * host(aux32) + 0.5 * 0.25 * acc
     assert max_rel(host(D32), dual) < 2e-6
     assert max_rel(host(Dh), dual) < tol
 
@@ -500,6 +504,27 @@ def test_fp8_gemm_vs_oracle(M, N, K):
     print(f"[fp8 gemm] max-rel {err:.2e}", flush=True)
     assert err < 2e-4
     assert max_rel(host(Cb), ref) < 2 ** -8
+
+
+def test_fp8_gemm_accumulate_and_relu2_epilogues():
+    """The residual-add (C += acc, fp32) and ReLU^2 (bf16 max(acc, 0)^2)
+    epilogues on fp8 operands."""
+    M, N, K = 300, 520, 384
+    rng = np.random.default_rng(12)
+    a, _, sa = ofp8.quantize_tensorwise(rng.standard_normal((M, K)))
+    b, _, sb = ofp8.quantize_tensorwise(0.02 * rng.standard_normal((N, K)))
+    alpha = 1.0 / (sa * sb)
+    acc = ofp8.fp8_matmul(a, b, alpha)
+    A8, B8 = torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()
+    c0 = rng.standard_normal((M, N)).astype(np.float32)
+    C = torch.from_numpy(c0).cuda()
+    nc.gemm_fp8(A8, B8, C, M, N, K, alpha, epilogue=nc.EPI_ACC_F32)
+    G = torch.empty(M, N, dtype=BF, device="cuda")
+    nc.gemm_fp8(A8, B8, G, M, N, K, alpha, epilogue=nc.EPI_RELU2)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(host(C) - (c0 + acc))) < 2e-4 * np.max(np.abs(acc)) + 1e-6
+    g_ref = np.maximum(acc, 0.0) ** 2
+    assert max_rel(host(G), g_ref) < 2 ** -7
 
 
 def test_fp8_gemm_rejects_unsupported_shapes():
