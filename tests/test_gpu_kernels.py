@@ -458,6 +458,17 @@ def test_attention_causality_bitwise():
 from oracle import fp8 as ofp8  # noqa: E402
 
 
+def test_fp8_quantize_all_zero_input():
+    x = torch.zeros(4096, dtype=F32, device="cuda")
+    q = torch.full((4096,), 0x55, dtype=torch.uint8, device="cuda")
+    amax_scale = torch.empty(2, dtype=F32, device="cuda")
+    ws = torch.empty(1024, dtype=F32, device="cuda")
+    nc.fp8_quantize(x, q, amax_scale, ws)
+    torch.cuda.synchronize()
+    assert host(amax_scale).tolist() == [0.0, 1.0]
+    assert not q.any()
+
+
 @pytest.mark.parametrize("dtype,n", [(F32, 1000), (F32, 300001), (BF, 65536 + 7)])
 def test_fp8_quantize_bit_exact(dtype, n):
     """Tensorwise e4m3 quantisation: amax and scale exact, every byte equal to

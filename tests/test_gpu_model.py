@@ -162,6 +162,12 @@ def test_grouped_query_attention_full_step(name):
     check_step(cfg, B=cfg.micro_batch, seed=41, ocfg=OptimConfig(normuon=(name == "small_gqa")))
 
 
+def test_grouped_heads_with_sliding_windows_full_step():
+    """Grouped key/value heads and per-layer windows together (fp32, 2 query
+    heads over 1, windows 8 and 40 keys)."""
+    check_step(TINY_GQA, B=2, seed=43, windows=[8, 40])
+
+
 def test_d12_shape_one_row():
     check_step(with_batch(D12, micro_batch=1), B=1, seed=7)
 
