@@ -16,8 +16,9 @@
 //    128 keys and walks the query tiles from the diagonal down, recomputing
 //    P = exp(S - lse) and dS = P (dP - D).  dQ: a workgroup owns 128 queries
 //    and walks the key tiles up to the diagonal.
-//  * MN-contiguous operands (V^T, Q^T, dO^T, K^T) are transposed in registers
-//    (8x8 16-bit blocks) on their way into LDS.
+//  * Tiles reach LDS in their token-major layout by direct loads; the operands
+//    needed transposed (V^T, Q^T, dO^T, K^T) are read with ds_read_b64_tr_b16,
+//    which transposes 16-bit values in the LDS read.
 // fp32 path (tiny configuration): one wave per query (or key) row, plain
 // loops over the causal range.
 //
@@ -36,48 +37,6 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-
-// 8 rows x 16 bytes of a token-major operand
-struct Blk8 { u32x4 r[8]; };
-
-NC_DEV void load_blk(const bf16* __restrict__ g, int64_t ld, int row, int col, Blk8& b) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    b.r[j] = *reinterpret_cast<const u32x4*>(g + (int64_t)(row + j) * ld + col);
-}
-
-// tile [64 rows][128 cols]: 16 chunks of 16 B per row, chunk ^= row & 7
-NC_DEV int nrm_off(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 3); }
-// transposed tile [128 rows (head dim)][64 cols (tokens)]: 8 chunks per row
-NC_DEV int trs_swz(int d) { return (d ^ (d >> 3)) & 7; }
-NC_DEV int trs_off(int d, int chunk) { return d * 64 + ((chunk ^ trs_swz(d)) << 3); }
-
-// rb: 8-row block index in the 64-row tile, cb: 16-byte chunk index (0..15)
-NC_DEV void store_nrm(bf16* lds, int rb, int cb, const Blk8& b) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    *reinterpret_cast<u32x4*>(lds + nrm_off(rb * 8 + j, cb)) = b.r[j];
-}
-NC_DEV void store_trs(bf16* lds, int rb, int cb, const Blk8& b) {
-  u32x4 t[8];
-  transpose8x8_b16(b.r, t);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(lds + trs_off(cb * 8 + i, rb)) = t[i];
-}
-
-NC_DEV bf16x8 frag_nrm(const bf16* lds, int row, int chunk) {
-  return *reinterpret_cast<const bf16x8*>(lds + nrm_off(row, chunk));
-}
-// 8 values of row d of a transposed tile at columns o1..o1+3 and o1+8..o1+11
-NC_DEV bf16x8 frag_trs(const bf16* lds, int d, int o1) {
-  const int c = o1 >> 3, w = o1 & 7;
-  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(lds + trs_off(d, c) + w);
-  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(lds + trs_off(d, c + 1) + w);
-  bf16x8 r;
-  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
-  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
-  return r;
-}
 
 // accumulator registers hf*8 .. hf*8+7 of a 32x32 tile, as an MFMA operand
 NC_DEV bf16x8 pack_half(const float* v, int hf) {
