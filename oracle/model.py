@@ -28,7 +28,8 @@ Readings where the pages are silent:
   for position t = 0..T-1 of each row, y_i = x_i cos - x_{i+h} sin,
   y_{i+h} = x_i sin + x_{i+h} cos.
 * Attention scale 1/sqrt(hd); causal mask keeps keys u <= t (diagonal kept);
-  no document masking; one KV head per query head.
+  no document masking; one key/value head per query head unless
+  cfg["n_kv_head"] says otherwise (below).
 * Sliding-window layers ([APIDOG] "1. Model GPT (nanochat/gpt.py)" lists a
   configurable short/long window pattern such as "SSSL", and section
   "5. Penyatuan Flash Attention" passes a window size to the attention call
