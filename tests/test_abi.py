@@ -240,3 +240,33 @@ def test_normuon_options_validated_and_planned():
         with pytest.raises(nc.NcError):
             nc.plan(TINY, dc_replace(base, normuon=True, normuon_beta2=beta2))
     nc.plan(TINY, dc_replace(base, normuon=False, normuon_beta2=5.0))   # ignored when off
+
+
+def test_op_argument_errors_return_before_any_launch():
+    """The single-kernel entry points reject bad arguments synchronously,
+    before touching the device (placeholder pointers are never dereferenced)."""
+    lib = nc.load()
+    fake = ctypes.c_void_p(0x100000)
+    fp = ctypes.c_void_p(0x200000)
+    # fp8 GEMM: epilogue, leading dimensions, K
+    args = lambda K, lda, ldb, ldc, epi: (fake, lda, fake, ldb, fake, ldc, 64, 64, K, epi, 1.0, None)
+    assert lib.nc_op_gemm_fp8(*args(256, 256, 256, 64, nc.EPI_RELU2_BWD)) == nc.NC_ERR_INVALID_ARG
+    assert lib.nc_op_gemm_fp8(*args(256, 128, 256, 64, nc.EPI_STORE)) == nc.NC_ERR_INVALID_ARG
+    assert lib.nc_op_gemm_fp8(*args(192, 192, 192, 64, nc.EPI_STORE)) == nc.NC_ERR_UNSUPPORTED
+    assert lib.nc_op_gemm_fp8(*args(256, 264, 256, 64, nc.EPI_STORE)) == nc.NC_ERR_UNSUPPORTED
+    assert lib.nc_op_gemm_fp8(None, 256, fake, 256, fake, 64, 64, 64, 256, 0, 1.0, None) == \
+        nc.NC_ERR_INVALID_ARG
+    # fp8 quantiser
+    assert lib.nc_op_fp8_quantize(nc.NC_FP32, fake, 0, fp, fake, fp, None) == nc.NC_ERR_INVALID_ARG
+    assert lib.nc_op_fp8_quantize(7, fake, 16, fp, fake, fp, None) == nc.NC_ERR_INVALID_ARG
+    assert lib.nc_op_fp8_quantize(nc.NC_FP32, fake, 16, fp, fake, None, None) == nc.NC_ERR_INVALID_ARG
+    # attention: key/value heads must divide the query heads; window >= -1; bf16 T % 128
+    def fwd(H, hkv, win, T=256, dt=nc.NC_BF16):
+        return lib.nc_op_attention_fwd(dt, fake, fake, fake, 3 * 128 * H, fake, 128 * H, fp, 1, T,
+                                       H, hkv, win, None)
+    assert fwd(4, 3, -1) == nc.NC_ERR_INVALID_ARG
+    assert fwd(4, 0, -1) == nc.NC_ERR_INVALID_ARG
+    assert fwd(4, 2, -2) == nc.NC_ERR_INVALID_ARG
+    assert fwd(4, 2, 10, T=200) == nc.NC_ERR_UNSUPPORTED
+    assert lib.nc_op_attention_bwd(nc.NC_BF16, fake, fake, fake, 384, fake, fake, 128, fp, fp, fake,
+                                   fake, fake, 384, 1, 256, 1, 1, -3, None) == nc.NC_ERR_INVALID_ARG
