@@ -235,16 +235,18 @@ def main():
         torch.cuda.synchronize()
         print(f"[bench] warmup step {i} loss {losses.mean().item():.4f}", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    # one event per step boundary on the bound stream (the first and last bracket
+    # the timed region; the ones between give each step's own time)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     w0 = time.perf_counter()
-    e0.record(stream)
+    ev[0].record(stream)
     for i in range(args.steps):
         step()
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    sec = e0.elapsed_time(e1) / 1e3 / args.steps
+    sec = ev[0].elapsed_time(ev[-1]) / 1e3 / args.steps
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     print(f"[bench] {args.steps} steps, {sec * 1e3:.1f} ms/step (wall {wall:.1f} s), "
           f"last loss {losses.mean().item():.4f}", file=sys.stderr, flush=True)
     tokens = cfg.tokens_per_step
@@ -277,6 +279,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": sec * 1e3,
+        "step_ms": {"min": per_step[0], "median": per_step[len(per_step) // 2],
+                    "max": per_step[-1]},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
