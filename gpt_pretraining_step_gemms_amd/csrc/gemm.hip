@@ -868,12 +868,14 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
         read_one(0, r, fr[0][r]);
         read_one(1, r, fr[1][r]);
       }
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int t = 0; t < NM; ++t) {
         const int ii = t / TN, j = t % TN;
         acc[ii][j] = mfma_f8(fr[0][ii], fr[1][ii], fr[0][TM + j], fr[1][TM + j], acc[ii][j]);
         load_at(t);
       }
+      __builtin_amdgcn_s_setprio(0);
       return;
     }
     if constexpr (PREF) {
@@ -888,6 +890,10 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
 #pragma unroll
         for (int r = 0; r < NR; ++r) read_one(s, r, cur[r]);
       }
+      // Raised wave priority over the substep's MFMAs: 1.5-2 % faster with A
+      // K-contiguous (forward and input-gradient products), 1.7 % slower for the
+      // weight gradients, where it stays off.
+      if constexpr (AL == kKCont) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int t = 0; t < NM; ++t) {
         const int ii = t / TN, j = t % TN;
@@ -902,6 +908,7 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
         }
         load_at(s * NM + t);                           // MFMA index within the step
       }
+      if constexpr (AL == kKCont) __builtin_amdgcn_s_setprio(0);
     }
   };
   if constexpr (HALF) {
