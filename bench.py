@@ -40,6 +40,8 @@ def parse():
                          '(S: short window, L: whole causal context); default: none')
     ap.add_argument("--kv-heads", type=int, default=0,
                     help="key/value heads for grouped-query attention (default: one per head)")
+    ap.add_argument("--fp8-forward", action="store_true",
+                    help="forward block products in fp8 e4m3 (tensorwise scales; backward bf16)")
     ap.add_argument("--normuon", action="store_true",
                     help="NorMuon per-neuron normalisation after Newton-Schulz")
     ap.add_argument("--short-window", type=int, default=None,
@@ -195,9 +197,11 @@ def main():
 
     cfg = CONFIGS[args.config]
     cfg = with_batch(cfg, micro_batch=args.micro_batch, accum_steps=args.accum)
+    from dataclasses import replace as dc_replace
     if args.kv_heads:
-        from dataclasses import replace as dc_replace
         cfg = dc_replace(cfg, n_kv_head=args.kv_heads)
+    if args.fp8_forward:
+        cfg = dc_replace(cfg, fp8_forward=True)
     if args.roofline_fp8:
         print(json.dumps({"roofline_fp8": roofline_gemm_fp8(cfg, args.roofline_iters)}))
         return
@@ -289,6 +293,7 @@ def main():
         "config": {"workload": f"{cfg.name} GPT pretraining step: {cfg.n_layer} layers, d {d}, "
                                f"{cfg.n_head}x128 heads"
                                f"{f' over {cfg.kv_heads} key/value heads' if cfg.kv_heads != cfg.n_head else ''}"
+                               f"{', forward block products in fp8 e4m3' if cfg.fp8_forward else ''}"
                                f", {attention}, MLP {cfg.d_ff} ReLU^2, "
                                f"vocab {cfg.vocab}, "
                                f"seq {cfg.seq_len}, micro-batch {cfg.micro_batch} x {K} accumulated "

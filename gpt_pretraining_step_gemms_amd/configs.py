@@ -41,6 +41,7 @@ class ModelConfig:
     norm_eps: float = 1e-6
     init_std: float = 0.02
     n_kv_head: int = 0    # key/value heads for grouped-query attention (0: n_head)
+    fp8_forward: bool = False   # forward block products in fp8 e4m3, tensorwise scales
 
     @property
     def kv_heads(self):
@@ -50,7 +51,7 @@ class ModelConfig:
         return dict(n_layer=self.n_layer, d_model=self.d_model, n_head=self.n_head,
                     head_dim=self.head_dim, d_ff=self.d_ff, vocab=self.vocab,
                     seq_len=self.seq_len, rope_base=self.rope_base, norm_eps=self.norm_eps,
-                    n_kv_head=self.kv_heads)
+                    n_kv_head=self.kv_heads, fp8_forward=self.fp8_forward)
 
     @property
     def tokens_per_step(self):

@@ -780,6 +780,44 @@ NC_DEV unsigned e4m3_rne(float x) {
   return sign | code;
 }
 
+// bf16 input, 16-byte aligned: 8 values per load, 8 codes per store, then the
+// scalar tail (n % 8 values)
+__global__ __launch_bounds__(256) void amax_partial_bf16x8_kernel(const bf16* __restrict__ x,
+                                                                  int64_t n,
+                                                                  float* __restrict__ partial) {
+  __shared__ float red[4];
+  float m = 0.f;
+  const int64_t n8 = n / 8, stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += stride) {
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(x + 8 * i);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(static_cast<float>(v[e])));
+  }
+  for (int64_t i = 8 * n8 + (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
+    m = fmaxf(m, fabsf(static_cast<float>(x[i])));
+  m = block_max(m, red);
+  if (threadIdx.x == 0) partial[blockIdx.x] = m;
+}
+
+__global__ __launch_bounds__(256) void fp8_quantize_bf16x8_kernel(
+    const bf16* __restrict__ x, int64_t n, const float* __restrict__ amax_scale,
+    uint8_t* __restrict__ q) {
+  const float sc = amax_scale[1];
+  const int64_t n8 = n / 8, stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += stride) {
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(x + 8 * i);
+    unsigned lo = 0, hi = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      lo |= e4m3_rne(static_cast<float>(v[e]) * sc) << (8 * e);
+      hi |= e4m3_rne(static_cast<float>(v[e + 4]) * sc) << (8 * e);
+    }
+    *reinterpret_cast<uint2*>(q + 8 * i) = make_uint2(lo, hi);
+  }
+  for (int64_t i = 8 * n8 + (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
+    q[i] = (uint8_t)e4m3_rne(static_cast<float>(x[i]) * sc);
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void fp8_quantize_kernel(const T* __restrict__ x, int64_t n,
                                                            const float* __restrict__ amax_scale,
@@ -1014,14 +1052,21 @@ hipError_t nc_normuon_stats(const float* X, int64_t x_stride, int R, int C, int 
 
 hipError_t nc_fp8_quantize(int dtype, const void* x, int64_t n, float* partial,
                            float* amax_scale, uint8_t* q, hipStream_t st) {
-  const int parts = (int)std::min<int64_t>(std::max<int64_t>(ceil_div64(n, 256), 1), 1024);
-  if (dtype)
+  const bool vec = dtype && (reinterpret_cast<uintptr_t>(x) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(q) & 7) == 0;
+  const int64_t per = vec ? 8 * 256 : 256;          // values per block and pass
+  const int parts = (int)std::min<int64_t>(std::max<int64_t>(ceil_div64(n, per), 1), 1024);
+  if (vec)
+    amax_partial_bf16x8_kernel<<<parts, 256, 0, st>>>((const bf16*)x, n, partial);
+  else if (dtype)
     amax_partial_kernel<bf16><<<parts, 256, 0, st>>>((const bf16*)x, n, partial);
   else
     amax_partial_kernel<float><<<parts, 256, 0, st>>>((const float*)x, n, partial);
   amax_final_kernel<<<1, 256, 0, st>>>(partial, parts, amax_scale);
-  const int blocks = (int)std::min<int64_t>(std::max<int64_t>(ceil_div64(n, 256), 1), 8192);
-  if (dtype)
+  const int blocks = (int)std::min<int64_t>(std::max<int64_t>(ceil_div64(n, per), 1), 8192);
+  if (vec)
+    fp8_quantize_bf16x8_kernel<<<blocks, 256, 0, st>>>((const bf16*)x, n, amax_scale, q);
+  else if (dtype)
     fp8_quantize_kernel<bf16><<<blocks, 256, 0, st>>>((const bf16*)x, n, amax_scale, q);
   else
     fp8_quantize_kernel<float><<<blocks, 256, 0, st>>>((const float*)x, n, amax_scale, q);

@@ -33,6 +33,9 @@ struct GemmParams {
   int splits;                        // split-K count (>1: C must be f32, workspace used)
   int vec_epi;                       // set by the launcher: C/aux 16-byte aligned, ldc and sC % 8 == 0
   float* workspace; size_t workspace_bytes;
+  // fp8 only: per-tensor scales {amax, s} of A and B (device); acc is divided by
+  // s_A * s_B before the epilogue.  Null: no device scales.
+  const float* scale_a; const float* scale_b;
 };
 
 // dtype: 0 = fp32 operands (VALU kernel), 1 = bf16 operands (MFMA kernel)

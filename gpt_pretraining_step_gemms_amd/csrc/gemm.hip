@@ -941,6 +941,17 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
   // C, the auxiliary tensors and the split-K workspace are accessed with
   // 16-byte, row-contiguous loads and stores.
   static_assert(WTN == 64, "the epilogue maps 8 lanes to the 64 columns of a wave tile");
+  if constexpr (F8) {
+    if (p.scale_a) {                                   // tensorwise scales kept on the device
+      const float inv = 1.f / (p.scale_a[1] * p.scale_b[1]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int e = 0; e < ACC_N; ++e) acc[i][j][e] *= inv;
+    }
+  }
   // padded row (floats): conflict-free staging writes for either MFMA layout
   constexpr int EP_LD = MI == 32 ? 72 : 68;
   constexpr int EP_FLOATS = 32 * EP_LD;

@@ -60,6 +60,8 @@ struct nc_ctx {
   size_t es;   // activation element size
   int L, d, H, F, V, T, maxB, Nmax, chunk;
   int Hkv, dk, W;   // key/value heads, their width Hkv*128, qkv row width d + 2 dk
+  bool fp8 = false;  // forward block products in fp8 e4m3 (tensorwise scales)
+  size_t q8a = 0, q8w = 0, q8s = 0, q8ws = 0;   // their codes, scales and amax scratch
   int64_t S, n_block, n_total;
   std::vector<ParamInfo> params;
   // parameter arena byte offsets
@@ -125,6 +127,11 @@ nc_status validate(const nc_model_config* m, const nc_optim_config* o, std::stri
     return NC_ERR_INVALID_ARG;
   }
   if (m->dtype != NC_FP32 && m->dtype != NC_BF16) { why = "dtype"; return NC_ERR_INVALID_ARG; }
+  if (m->fp8_forward != 0 && m->fp8_forward != 1) { why = "fp8_forward is 0 or 1"; return NC_ERR_INVALID_ARG; }
+  if (m->fp8_forward && m->dtype != NC_BF16) {
+    why = "fp8_forward needs the bf16 configuration";
+    return NC_ERR_UNSUPPORTED;
+  }
   if (m->n_kv_head < 0 || (m->n_kv_head > 0 && m->n_head % m->n_kv_head)) {
     why = "n_kv_head must divide n_head (0: n_head)";
     return NC_ERR_INVALID_ARG;
@@ -264,6 +271,13 @@ void plan(nc_ctx* c) {
     c->nm_inv = a.take((size_t)c->nm_rows * 4);
     c->nm_scale = a.take((size_t)6 * L * 4);
   }
+  if (c->fp8) {
+    // codes of the largest activation operand [N, max(d, F)] and weight operand
+    c->q8a = a.take(N * (size_t)std::max(d, F));
+    c->q8w = a.take((size_t)std::max(W, F) * std::max(d, F));
+    c->q8s = a.take(4 * sizeof(float));
+    c->q8ws = a.take(1024 * sizeof(float));
+  }
   c->act_bytes = a.cur;
 }
 
@@ -339,6 +353,39 @@ hipError_t gemm(nc_ctx* c, const void* A_, int64_t lda, int al, const void* B_, 
   return nc_launch_gemm(c->dt, g, c->st);
 }
 
+// Forward block product in fp8: C (epilogue epi) = X W^T with X bf16 [N, K]
+// and W the bf16 weight copy [Nout, K], both quantised to e4m3 with one scale
+// per tensor (codes in q8a / q8w, scales {amax, s} in q8s[0..1] / q8s[2..3]);
+// the kernel divides the sums by s_X s_W.
+hipError_t gemm_fp8_fwd(nc_ctx* c, const void* X, int K, const void* Wt, int Nout, void* C,
+                        int64_t ldc, int N, int epi) {
+  float* sc = reinterpret_cast<float*>(c->aa + c->q8s);
+  float* ws = reinterpret_cast<float*>(c->aa + c->q8ws);
+  uint8_t* xa = reinterpret_cast<uint8_t*>(c->aa + c->q8a);
+  uint8_t* wq = reinterpret_cast<uint8_t*>(c->aa + c->q8w);
+  const bool c_f32 = epi == kEpiStoreF32 || epi == kEpiAccF32;
+  const size_t nx = (size_t)N * K, nw = (size_t)Nout * K;
+  // every extent inside its arena, also in a dry run
+  if (!in_arena(c, X, nx * 2) || !in_arena(c, Wt, nw * 2) || !in_arena(c, xa, nx) ||
+      !in_arena(c, wq, nw) || !in_arena(c, C, ((size_t)(N - 1) * ldc + Nout) * (c_f32 ? 4 : 2))) {
+    c->range_error = "fp8 GEMM operand outside its arena (N=" + std::to_string(N) +
+                     " Nout=" + std::to_string(Nout) + " K=" + std::to_string(K) + ")";
+    return hipErrorInvalidValue;
+  }
+  if (c->dry_run) return hipSuccess;
+  hipError_t e = nc_fp8_quantize(1, X, (int64_t)nx, ws, sc, xa, c->st);
+  if (e != hipSuccess) return e;
+  e = nc_fp8_quantize(1, Wt, (int64_t)nw, ws, sc + 2, wq, c->st);
+  if (e != hipSuccess) return e;
+  GemmParams g{};
+  g.A = xa; g.B = wq; g.C = C;
+  g.lda = K; g.ldb = K; g.ldc = ldc;
+  g.M = N; g.N = Nout; g.K = K; g.batch = 1; g.splits = 1;
+  g.a_layout = kKCont; g.b_layout = kKCont; g.epi = epi; g.alpha = 1.f;
+  g.scale_a = sc; g.scale_b = sc + 2;
+  return nc_launch_gemm_f8(g, c->st);
+}
+
 }  // namespace
 
 // =================================================================== C ABI
@@ -367,6 +414,7 @@ static nc_ctx* make_ctx(const nc_model_config* cfg, const nc_optim_config* ocfg)
   c->es = c->dt ? 2 : 4;
   c->L = cfg->n_layer; c->d = cfg->d_model; c->H = cfg->n_head; c->F = cfg->d_ff;
   c->Hkv = cfg->n_kv_head > 0 ? cfg->n_kv_head : cfg->n_head;
+  c->fp8 = cfg->fp8_forward != 0;
   c->dk = c->Hkv * 128;
   c->W = c->d + 2 * c->dk;
   c->V = cfg->vocab; c->T = cfg->seq_len; c->maxB = cfg->max_micro_batch;
@@ -520,19 +568,25 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
     const size_t wb = (size_t)l * ctx->S;
     char* qkv = aa + la.qkv;
     NC_TRY(nc_rmsnorm_fwd(dt, x, aa + la.a1, A<float>(ctx, la.r1), N, d, eps, st), "norm1");
-    NC_GEMM(gemm(ctx, aa + la.a1, d, kKCont, wptr(ctx, wb), d, kKCont, qkv, Wd, N, Wd, d,
-                kEpiStore), "qkv");
+    NC_GEMM(ctx->fp8 ? gemm_fp8_fwd(ctx, aa + la.a1, d, wptr(ctx, wb), Wd, qkv, Wd, N, kEpiStore)
+                     : gemm(ctx, aa + la.a1, d, kKCont, wptr(ctx, wb), d, kKCont, qkv, Wd, N, Wd,
+                            d, kEpiStore), "qkv");
     NC_TRY(nc_qk_norm_rope_fwd(dt, qkv, A<float>(ctx, la.rqk), tab, N, T, H, Hkv, eps, st),
            "qknorm");
     NC_TRY(nc_attn_fwd(dt, qkv, qkv + d * es, qkv + (d + dk) * es, Wd, aa + la.o, d,
                        A<float>(ctx, la.lse), B, T, H, Hkv, ctx->windows[l], st), "attn fwd");
-    NC_GEMM(gemm(ctx, aa + la.o, d, kKCont, wptr(ctx, wb + oWo), d, kKCont, x, d, N, d,
-                d, kEpiAccF32), "out proj");
+    NC_GEMM(ctx->fp8 ? gemm_fp8_fwd(ctx, aa + la.o, d, wptr(ctx, wb + oWo), d, x, d, N, kEpiAccF32)
+                     : gemm(ctx, aa + la.o, d, kKCont, wptr(ctx, wb + oWo), d, kKCont, x, d, N, d,
+                            d, kEpiAccF32), "out proj");
     NC_TRY(nc_rmsnorm_fwd(dt, x, aa + la.a2, A<float>(ctx, la.r2), N, d, eps, st), "norm2");
-    NC_GEMM(gemm(ctx, aa + la.a2, d, kKCont, wptr(ctx, wb + oW1), d, kKCont, aa + la.g,
-                F, N, F, d, kEpiRelu2), "mlp up");
-    NC_GEMM(gemm(ctx, aa + la.g, F, kKCont, wptr(ctx, wb + oW1 + (size_t)F * d), F,
-                kKCont, x, d, N, d, F, kEpiAccF32), "mlp down");
+    NC_GEMM(ctx->fp8 ? gemm_fp8_fwd(ctx, aa + la.a2, d, wptr(ctx, wb + oW1), F, aa + la.g, F, N,
+                                    kEpiRelu2)
+                     : gemm(ctx, aa + la.a2, d, kKCont, wptr(ctx, wb + oW1), d, kKCont, aa + la.g,
+                            F, N, F, d, kEpiRelu2), "mlp up");
+    NC_GEMM(ctx->fp8 ? gemm_fp8_fwd(ctx, aa + la.g, F, wptr(ctx, wb + oW1 + (size_t)F * d), d, x,
+                                    d, N, kEpiAccF32)
+                     : gemm(ctx, aa + la.g, F, kKCont, wptr(ctx, wb + oW1 + (size_t)F * d), F,
+                            kKCont, x, d, N, d, F, kEpiAccF32), "mlp down");
   }
   NC_TRY(nc_rmsnorm_fwd(dt, x, aa + ctx->xf, A<float>(ctx, ctx->rf), N, d, eps, st), "normf");
 

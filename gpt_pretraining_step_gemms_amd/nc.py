@@ -36,7 +36,8 @@ class ModelCfgC(ctypes.Structure):
                 ("n_layer", "d_model", "n_head", "head_dim", "d_ff", "vocab", "seq_len",
                  "max_micro_batch", "dtype")] + [("rope_base", ctypes.c_float),
                                                  ("norm_eps", ctypes.c_float),
-                                                 ("n_kv_head", ctypes.c_int32)]
+                                                 ("n_kv_head", ctypes.c_int32),
+                                                 ("fp8_forward", ctypes.c_int32)]
 
 
 class OptimCfgC(ctypes.Structure):
@@ -114,7 +115,7 @@ def model_cfg_c(cfg: ModelConfig, max_micro_batch=None):
     return ModelCfgC(cfg.n_layer, cfg.d_model, cfg.n_head, cfg.head_dim, cfg.d_ff, cfg.vocab,
                      cfg.seq_len, max_micro_batch or cfg.micro_batch,
                      NC_BF16 if cfg.dtype == "bf16" else NC_FP32, cfg.rope_base, cfg.norm_eps,
-                     cfg.n_kv_head)
+                     cfg.n_kv_head, int(bool(cfg.fp8_forward)))
 
 
 def optim_cfg_c(o: OptimConfig):

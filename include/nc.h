@@ -68,6 +68,14 @@ typedef struct {
   int32_t dtype;           /* NC_FP32 | NC_BF16 */
   float rope_base, norm_eps;
   int32_t n_kv_head;
+  int32_t fp8_forward;     /* 1: the four forward block products of every layer (QKV,
+                              output projection, MLP up and down) run in fp8 e4m3 with
+                              one scale per tensor -- the activation and the weight
+                              copy are quantised on the device before each product
+                              (apidog.com, "3. Manajemen Presisi (nanochat/common.py)":
+                              later runs train most linear layers in FP8 with tensorwise
+                              scaling); the backward products stay bf16 and take the
+                              unquantised operands.  NC_BF16 only. */
 } nc_model_config;
 
 /* Optimizer settings.  Muon (per block matrix): M <- mu M + G;

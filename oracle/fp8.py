@@ -54,6 +54,15 @@ def e4m3_decode(codes):
     return _TABLE[np.asarray(codes, np.uint8)]
 
 
+def bf16_round(x):
+    """Round to bfloat16 (nearest, ties to even), returned as float64: the
+    fp8 operands of the forward products are quantised from their bf16 copies
+    (the stored activations and weight copies of the bf16 configuration)."""
+    u = np.ascontiguousarray(np.asarray(x, np.float32)).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 def quantize_tensorwise(x):
     """(codes, amax, scale) of a tensor: scale = 448 / amax in fp32, codes of
     x * scale evaluated in fp32."""

@@ -43,6 +43,15 @@ Readings where the pages are silent:
   key/value heads (default n_head), Wk and Wv [n_kv_head * hd, d]; query
   head h reads key/value head h // (n_head / n_kv_head), so consecutive query
   heads share one, and a key/value head's gradient sums over its query heads.
+* FP8 forward products ([APIDOG] "3. Manajemen Presisi (nanochat/common.py)":
+  most linear layers in FP8 with tensorwise scaling): with cfg["fp8_forward"]
+  the four block products of every layer (QKV -- its fused weight Wq|Wk|Wv
+  taken as one tensor -- output projection, MLP up and down) use the e4m3
+  values of the bf16 copies of their two operands (the fp8 path exists in
+  the bf16 configuration, whose activations and weight copies are bf16), one
+  scale per tensor (oracle.fp8), and the
+  backward treats the rounding as the identity (gradients with the
+  unrounded operands).  The lm_head and every backward product are exact.
 * Loss: natural log, mean over every position, no ignore index.
 """
 
@@ -160,6 +169,21 @@ def param_shapes(cfg):
 # --------------------------------------------------------------------------
 # forward
 # --------------------------------------------------------------------------
+def _fp8_linear(x, W):
+    """x W^T with both operands replaced by the tensorwise e4m3 values of
+    their bf16 copies (the codes are decided on the same bf16 values the
+    kernels quantise)."""
+    from . import fp8
+    qx, _, sx = fp8.quantize_tensorwise(fp8.bf16_round(x.reshape(-1, x.shape[-1])))
+    qw, _, sw = fp8.quantize_tensorwise(fp8.bf16_round(W))
+    y = (fp8.e4m3_decode(qx) / sx) @ (fp8.e4m3_decode(qw) / sw).T
+    return y.reshape(*x.shape[:-1], W.shape[0])
+
+
+def _linear(x, W, cfg):
+    return _fp8_linear(x, W) if cfg.get("fp8_forward") else x @ W.T
+
+
 def _split_heads(u, H):
     B, T, d = u.shape
     return u.reshape(B, T, H, d // H).transpose(0, 2, 1, 3)      # [B,H,T,hd]
@@ -213,20 +237,26 @@ def forward(params, tokens, targets, cfg, keep_cache=True):
     for i in range(cfg["n_layer"]):
         Wq, Wk, Wv, Wo, W1, W2 = (P[n] for n in _layer_names(i))
         a, r1 = rmsnorm(x, eps)
-        q = _split_heads(a @ Wq.T, H)
-        k = _split_heads(a @ Wk.T, Hkv)
-        v = _split_heads(a @ Wv.T, Hkv)
+        if cfg.get("fp8_forward"):             # the fused QKV weight is one tensor
+            qkv = _fp8_linear(a, np.concatenate([Wq, Wk, Wv], axis=0))
+            dq_, dk_ = Wq.shape[0], Wk.shape[0]
+            q_, k_, v_ = qkv[..., :dq_], qkv[..., dq_:dq_ + dk_], qkv[..., dq_ + dk_:]
+        else:
+            q_, k_, v_ = a @ Wq.T, a @ Wk.T, a @ Wv.T
+        q = _split_heads(q_, H)
+        k = _split_heads(k_, Hkv)
+        v = _split_heads(v_, Hkv)
         qn, rq = rmsnorm(q, eps)
         kn, rk = rmsnorm(k, eps)
         qr = rope(qn, cos, sin)
         kr = rope(kn, cos, sin)
         o_h, _ = causal_attention(qr, _repeat_kv(kr, group), _repeat_kv(v, group), windows[i])
         o = _merge_heads(o_h)
-        x = x + o @ Wo.T
+        x = x + _linear(o, Wo, cfg)
         m, r2 = rmsnorm(x, eps)
-        h = m @ W1.T
+        h = _linear(m, W1, cfg)
         g = np.maximum(h, 0.0) ** 2
-        x = x + g @ W2.T
+        x = x + _linear(g, W2, cfg)
         if keep_cache:
             layers.append(dict(a=a, r1=r1, qn=qn, rq=rq, kn=kn, rk=rk,
                                qr=qr, kr=kr, v=v, o=o, m=m, r2=r2, h=h, g=g))

@@ -95,16 +95,18 @@ SMALL_BF16 = dict(name="small", n_layer=2, d_model=384, n_head=3, head_dim=128, 
 
 
 @pytest.mark.parametrize("name", ["tiny", "small", "d12", "d20", "d24", "d26", "small_gqa",
-                                  "d20_gqa", "d26_gqa"])
+                                  "d20_gqa", "d26_gqa", "small_fp8", "d20_fp8", "d26_gqa_fp8"])
 def test_every_launch_of_a_step_stays_inside_the_arenas(name):
     """Dry run of nc_fwd_bwd + nc_optimizer_step: every GEMM operand extent is
     checked against the planned arenas (no device access)."""
     from dataclasses import replace as dc_replace
     from gpt_pretraining_step_gemms_amd.configs import ModelConfig
-    base = name.replace("_gqa", "")
+    base = name.replace("_gqa", "").replace("_fp8", "")
     cfg = ModelConfig(**SMALL_BF16) if base == "small" else CONFIGS[base]
-    if name.endswith("_gqa"):
+    if "_gqa" in name:
         cfg = dc_replace(cfg, n_kv_head=1)
+    if "_fp8" in name:
+        cfg = dc_replace(cfg, fp8_forward=True)
     lib = nc.load()
     for maxb, b in [(cfg.micro_batch, cfg.micro_batch), (cfg.micro_batch, 1), (1, 1)]:
         m, o = nc.model_cfg_c(cfg, maxb), nc.optim_cfg_c(OptimConfig(normuon=True))

@@ -62,3 +62,44 @@ def test_fp8_matmul_is_the_product_of_decoded_values():
     ref = np.array([[sum(fp8.e4m3_decode(a[i, k]) * fp8.e4m3_decode(b[j, k]) for k in range(16))
                      for j in range(4)] for i in range(3)]) * 0.5
     np.testing.assert_allclose(fp8.fp8_matmul(a, b, 0.5), ref, rtol=1e-15)
+
+
+def test_fp8_linear_is_exact_for_representable_operands():
+    # entries in {0, +-1, +-2}: amax 2, scale 224, scaled values 0, +-224, +-448 are
+    # e4m3 values, so the fp8 product is the exact product
+    from oracle.model import _fp8_linear
+    rng = np.random.default_rng(3)
+    x = rng.choice([-2.0, -1.0, 0.0, 1.0, 2.0], size=(2, 5, 16))
+    W = rng.choice([-2.0, -1.0, 1.0, 2.0], size=(7, 16))
+    np.testing.assert_array_equal(_fp8_linear(x, W), x @ W.T)
+
+
+def test_fp8_forward_model_stays_close_to_the_exact_one():
+    # e4m3 keeps 3 mantissa bits: the loss moves by well under its own size, and
+    # the straight-through gradients keep their direction
+    import oracle
+    from oracle.model import param_shapes
+    from gpt_pretraining_step_gemms_amd import synthetic
+    cfg = dict(n_layer=2, d_model=32, n_head=2, head_dim=16, d_ff=128, vocab=64, seq_len=8,
+               rope_base=10000.0, norm_eps=1e-6)
+    params = {k: v.astype(np.float64) for k, v in
+              synthetic.normal_params(0, param_shapes(cfg), 0.3).items()}
+    tok, tgt = synthetic.token_rows(1, 2, 8, 64, "uniform")
+    l0, g0 = oracle.loss_and_grads(params, tok, tgt, cfg)
+    l8, g8 = oracle.loss_and_grads(params, tok, tgt, dict(cfg, fp8_forward=True))
+    assert l8 != l0 and abs(l8 - l0) / l0 < 0.05
+    for n in g0:
+        a, b = g0[n].ravel(), g8[n].ravel()
+        assert a @ b / (np.linalg.norm(a) * np.linalg.norm(b)) > 0.95, n
+
+
+def test_bf16_round_known_values_and_ties():
+    r = fp8.bf16_round
+    assert r(1.0) == 1.0 and r(-2.5) == -2.5
+    assert r(1.0 + 2.0 ** -8) == 1.0               # halfway to 1 + 2^-7: ties to even (1.0)
+    assert r(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6   # halfway 1+2^-7 / 1+2^-6: even is 1+2^-6
+    assert r(1.0 + 2.0 ** -8 + 2.0 ** -12) == 1.0 + 2.0 ** -7
+    x = np.random.default_rng(0).standard_normal(1000)
+    y = r(x)
+    assert np.all(np.abs(y - x) <= 2.0 ** -8 * np.abs(x) * (1 + 1e-6))   # unit roundoff 2^-8
+    assert np.all(np.ascontiguousarray(y.astype(np.float32)).view(np.uint32) & 0xFFFF == 0)
