@@ -157,31 +157,75 @@ def copy_calibration(nbytes=1 << 30):
     torch.cuda.synchronize()
 
 
-def cpu_baseline(cfg, n_tok=2048, windows=None):
-    """The fp64 numpy oracle on a bounded sample of the same workload: forward
-    + backward of one 2048-token row (n_tok < 2048 takes a prefix of it, which
-    a causal model computes exactly as inside the full row).  The optimizer,
-    <1% of a 524,288-token step's FLOPs, is left out."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, windows=None, ocfg=None):
+    """The fp64 numpy oracle on a bounded sample of the same workload:
+      * forward + backward of one 2048-token row of the model;
+      * the optimizer on layer 0's six block matrices (Muon with Newton-Schulz)
+        and on E and Wh (AdamW);
+      * the whole tiny-config step (fwd + bwd + optimizer), timed on its own.
+    The step time is extrapolated linearly from the sample: (micro-batch rows
+    x accumulation steps) row passes + n_layer times the per-layer optimizer +
+    the AdamW part; value = tokens per step / that time (labelled as
+    extrapolated)."""
     import numpy as np
     import threadpoolctl
     import oracle
     from oracle.model import param_shapes
     from gpt_pretraining_step_gemms_amd import synthetic
-    ocfg = cfg.as_oracle_cfg()
+    from gpt_pretraining_step_gemms_amd.configs import TINY, OptimConfig
+    hp = (ocfg or OptimConfig()).as_dict()
+    mcfg = cfg.as_oracle_cfg()
     if windows is not None:
-        ocfg["windows"] = [None if w < 0 else w for w in windows]
+        mcfg["windows"] = [None if w < 0 else w for w in windows]
     params = {k: v.astype(np.float64) for k, v in
-              synthetic.normal_params(0, param_shapes(ocfg), cfg.init_std).items()}
+              synthetic.normal_params(0, param_shapes(mcfg), cfg.init_std).items()}
     tok, tgt = synthetic.token_rows(1000, 1, cfg.seq_len, cfg.vocab, cfg.token_dist)
-    tok, tgt = tok[:, :n_tok], tgt[:, :n_tok]
     t0 = time.perf_counter()
-    oracle.loss_and_grads(params, tok, tgt, ocfg)
-    sec = time.perf_counter() - t0
+    _, grads = oracle.loss_and_grads(params, tok, tgt, mcfg)
+    t_row = time.perf_counter() - t0
+    layer0 = [n for n in params if n.startswith("0.")]
+    t0 = time.perf_counter()
+    oracle.train_step({n: params[n] for n in layer0}, grads, {}, 1, hp)
+    t_layer = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.train_step({n: params[n] for n in ("E", "Wh")}, grads, {}, 1, hp)
+    t_adamw = time.perf_counter() - t0
+    del grads
+    # the tiny configuration's whole step
+    tcfg = TINY.as_oracle_cfg()
+    tparams = {k: v.astype(np.float64) for k, v in
+               synthetic.normal_params(0, param_shapes(tcfg), TINY.init_std).items()}
+    ttok, ttgt = synthetic.token_rows(1, TINY.micro_batch, TINY.seq_len, TINY.vocab,
+                                      TINY.token_dist)
+    t0 = time.perf_counter()
+    _, tgrads = oracle.loss_and_grads(tparams, ttok, ttgt, tcfg)
+    oracle.train_step(tparams, tgrads, {}, 1, hp)
+    t_tiny = time.perf_counter() - t0
+    rows = cfg.micro_batch * cfg.accum_steps
+    t_step = rows * t_row + cfg.n_layer * t_layer + t_adamw
     blas = [p for p in threadpoolctl.threadpool_info() if p["user_api"] == "blas"]
-    cores = max((p["num_threads"] for p in blas), default=1)
-    return {"value": n_tok / sec, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"fwd+bwd of {n_tok} positions of one {cfg.seq_len}-token row "
-                      f"of {cfg.name}, numpy fp64 (OpenBLAS, {cores} threads), {sec:.1f} s"}
+    threads = max((p["num_threads"] for p in blas), default=1)
+    return {"value": cfg.tokens_per_step / t_step, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{cfg.name}: fwd+bwd of one {cfg.seq_len}-token row {t_row:.1f} s, "
+                      f"optimizer of layer 0's 6 matrices {t_layer:.1f} s, AdamW of E and Wh "
+                      f"{t_adamw:.1f} s; step time extrapolated to {rows} rows + "
+                      f"{cfg.n_layer} layers = {t_step:.0f} s; numpy fp64 (OpenBLAS, "
+                      f"{threads} threads)",
+            "extrapolated": True,
+            "host": {"logical_cpus": os.cpu_count(), "cpu_model": _cpu_model()},
+            "tiny_full_step": {"seconds": t_tiny, "tokens_per_s": TINY.tokens_per_step / t_tiny,
+                               "what": "tiny config fwd+bwd+optimizer, whole step"}}
 
 
 def main():
@@ -266,7 +310,7 @@ def main():
     roof = roofline_gemm(cfg, args.roofline_iters)
     print(f"[bench] roofline {roof['achieved']:.0f} TFLOP/s ({roof['frac']:.3f} of peak)",
           file=sys.stderr, flush=True)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(cfg, windows=windows)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(cfg, windows=windows, ocfg=ocfg)
     attention = "causal attention"
     if windows is not None:
         attention = (f"sliding-window attention, pattern {args.window_pattern.upper()} "

@@ -32,13 +32,24 @@ template <> struct Vec4<bf16> {
 };
 
 // ---------------------------------------------------------------- embedding
+// A token id outside [0, V) is not looked up: its row of x becomes NaN (so
+// the loss and every gradient of the step turn non-finite) and bit 0 of
+// *flag is set.
 __global__ void embed_fwd_kernel(const int32_t* __restrict__ tok, const float* __restrict__ E,
-                                 float* __restrict__ x, int n_tok, int d, int V) {
+                                 float* __restrict__ x, int n_tok, int d, int V,
+                                 int32_t* __restrict__ flag) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= n_tok) return;
   const int lane = threadIdx.x & 63;
-  const float* src = E + (int64_t)clamp_id(tok[row], V) * d;
+  const int id = tok[row];
   float* dst = x + (int64_t)row * d;
+  if (id < 0 || id >= V) {
+    if (lane == 0) atomicOr(flag, 1);
+    const float4 nan4 = make_float4(NAN, NAN, NAN, NAN);
+    for (int i = lane * 4; i < d; i += 256) *reinterpret_cast<float4*>(dst + i) = nan4;
+    return;
+  }
+  const float* src = E + (int64_t)id * d;
   for (int i = lane * 4; i < d; i += 256)
     *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(src + i);
 }
@@ -433,7 +444,7 @@ __global__ void attn_bwd_pre_kernel(const T* __restrict__ o, const T* __restrict
 template <typename T, int NTH>
 __global__ __launch_bounds__(NTH) void cross_entropy_kernel(
     const float* __restrict__ z, const int32_t* __restrict__ tgt, T* __restrict__ dz,
-    float* __restrict__ loss_rows, int V, float scale) {
+    float* __restrict__ loss_rows, int V, float scale, int32_t* __restrict__ flag) {
   constexpr int KV = 32768 / (4 * NTH);            // float4 per thread
   constexpr float kLog2e = 1.4426950408889634f;
   __shared__ float red[NTH / 64];
@@ -464,9 +475,15 @@ __global__ __launch_bounds__(NTH) void cross_entropy_kernel(
     }
   }
   const float S = block_sum(s, red);
-  const int y = clamp_id(tgt[row], V);
-  if (threadIdx.x == 0) loss_rows[row] = M + logf(S) - zr[y];
-  const float inv = 1.f / S;
+  // a target outside [0, V): NaN loss and dz for the row, bit 1 of *flag
+  const int yraw = tgt[row];
+  const bool ok = yraw >= 0 && yraw < V;
+  const int y = ok ? yraw : -1;
+  if (threadIdx.x == 0) {
+    loss_rows[row] = ok ? M + logf(S) - zr[y] : NAN;
+    if (!ok) atomicOr(flag, 2);
+  }
+  const float inv = ok ? 1.f / S : NAN;
   T* dr = dz + (int64_t)row * V;
 #pragma unroll
   for (int k = 0; k < KV; ++k) {
@@ -736,6 +753,21 @@ inline int grid1d(size_t n, int block = 256) {
 
 
 // ------------------------------------------------ fp8 e4m3, tensorwise scale
+// The maximum that keeps a NaN (fmaxf drops it): a NaN anywhere in a tensor
+// makes its amax and scale NaN, and with them every code (0x7F).
+NC_DEV float max_nan(float a, float b) { return (a > b || a != a) ? a : b; }
+NC_DEV float block_max_nan(float v, float* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max_nan(v, __shfl_xor(v, o, kWave));
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.f;
+  for (int i = 0; i < nw; ++i) s = max_nan(s, red[i]);
+  return s;
+}
+
 // amax: per-block partial maxima of |x| (fixed order), then one block folds them
 template <typename T>
 __global__ __launch_bounds__(256) void amax_partial_kernel(const T* __restrict__ x, int64_t n,
@@ -743,8 +775,8 @@ __global__ __launch_bounds__(256) void amax_partial_kernel(const T* __restrict__
   __shared__ float red[4];
   float m = 0.f;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-    m = fmaxf(m, fabsf(to_f(x[i])));
-  m = block_max(m, red);
+    m = max_nan(m, fabsf(to_f(x[i])));
+  m = block_max_nan(m, red);
   if (threadIdx.x == 0) partial[blockIdx.x] = m;
 }
 
@@ -754,17 +786,18 @@ __global__ __launch_bounds__(256) void amax_final_kernel(const float* __restrict
                                                          float* __restrict__ amax_scale) {
   __shared__ float red[4];
   float m = 0.f;
-  for (int i = threadIdx.x; i < parts; i += 256) m = fmaxf(m, partial[i]);
-  m = block_max(m, red);
+  for (int i = threadIdx.x; i < parts; i += 256) m = max_nan(m, partial[i]);
+  m = block_max_nan(m, red);
   if (threadIdx.x == 0) {
     amax_scale[0] = m;
-    amax_scale[1] = m > 0.f ? 448.f / m : 1.f;
+    amax_scale[1] = m != m ? m : (m > 0.f ? 448.f / m : 1.f);
   }
 }
 
 // OCP fp8 e4m3 (bias 7, 3 mantissa bits, largest finite 448, no infinities),
-// round to nearest even, saturating at 448
+// round to nearest even, saturating at 448; NaN is code 0x7F
 NC_DEV unsigned e4m3_rne(float x) {
+  if (x != x) return 0x7Fu;
   const unsigned sign = (__float_as_uint(x) >> 24) & 0x80u;
   const float a = fminf(fabsf(x), 448.f);
   if (!(a >= 0x1p-6f)) return sign | (unsigned)rintf(a * 512.f);   // multiples of 2^-9
@@ -791,11 +824,11 @@ __global__ __launch_bounds__(256) void amax_partial_bf16x8_kernel(const bf16* __
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += stride) {
     const bf16x8 v = *reinterpret_cast<const bf16x8*>(x + 8 * i);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(static_cast<float>(v[e])));
+    for (int e = 0; e < 8; ++e) m = max_nan(m, fabsf(static_cast<float>(v[e])));
   }
   for (int64_t i = 8 * n8 + (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
-    m = fmaxf(m, fabsf(static_cast<float>(x[i])));
-  m = block_max(m, red);
+    m = max_nan(m, fabsf(static_cast<float>(x[i])));
+  m = block_max_nan(m, red);
   if (threadIdx.x == 0) partial[blockIdx.x] = m;
 }
 
@@ -830,8 +863,8 @@ __global__ __launch_bounds__(256) void fp8_quantize_kernel(const T* __restrict__
 
 // =============================================================== launchers
 hipError_t nc_embed_fwd(const int32_t* tok, const float* E, float* x, int n_tok, int d, int V,
-                        hipStream_t st) {
-  embed_fwd_kernel<<<ceil_div(n_tok, 4), 256, 0, st>>>(tok, E, x, n_tok, d, V);
+                        int32_t* flag, hipStream_t st) {
+  embed_fwd_kernel<<<ceil_div(n_tok, 4), 256, 0, st>>>(tok, E, x, n_tok, d, V, flag);
   return hipGetLastError();
 }
 
@@ -863,12 +896,12 @@ hipError_t nc_embed_bwd(const int32_t* tok, const float* dx, float* dE, int n_to
   s += (size_t)n_tok * 4;
   const size_t used = s - static_cast<char*>(scratch);
   float* partial = reinterpret_cast<float*>(static_cast<char*>(scratch) + ((used + 255) & ~(size_t)255));
-  static bool lds_opt_in = false;
-  if (!lds_opt_in) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(embed_hist_kernel),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, 32768 * 4);
-    lds_opt_in = true;
-  }
+  // the histogram keeps V counters in LDS (up to 128 KB); the attribute is
+  // set on every call (a host-side call) so that it holds on whichever
+  // device is current
+  const hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(embed_hist_kernel),
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, V * 4);
+  if (ea != hipSuccess) return ea;
   embed_hist_kernel<<<G, 256, (size_t)V * 4, st>>>(tok, n_tok, V, counts);
   embed_colscan_kernel<<<ceil_div(V, 256), 256, 0, st>>>(counts, G, V, total);
   embed_scan_kernel<<<1, 1024, 0, st>>>(total, V, start);
@@ -945,12 +978,17 @@ hipError_t nc_attn_bwd_pre(int dtype, const void* o, const void* dO, int64_t ld,
 }
 
 hipError_t nc_cross_entropy(int dtype, const float* z, const int32_t* tgt, void* dz,
-                            float* loss_rows, int rows, int V, float scale, hipStream_t st) {
+                            float* loss_rows, int rows, int V, float scale, int32_t* flag,
+                            hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   // 1024 threads (32 logits each) per row: 455 us per 8192-row chunk at 256
   // threads, 305 at 512, 285 at 1024
-  if (dtype) cross_entropy_kernel<bf16, 1024><<<rows, 1024, 0, st>>>(z, tgt, (bf16*)dz, loss_rows, V, scale);
-  else cross_entropy_kernel<float, 1024><<<rows, 1024, 0, st>>>(z, tgt, (float*)dz, loss_rows, V, scale);
+  if (dtype)
+    cross_entropy_kernel<bf16, 1024><<<rows, 1024, 0, st>>>(z, tgt, (bf16*)dz, loss_rows, V,
+                                                           scale, flag);
+  else
+    cross_entropy_kernel<float, 1024><<<rows, 1024, 0, st>>>(z, tgt, (float*)dz, loss_rows, V,
+                                                            scale, flag);
   return hipGetLastError();
 }
 

@@ -5,9 +5,11 @@
 #include "common.h"
 
 // ---- embedding
-// token ids outside [0, vocab) are clamped (no out-of-bounds access)
+// A token id outside [0, vocab) makes its row of x NaN and sets bit 0 of *flag
+// (a device int); the backward sorts such ids as clamped (no out-of-bounds
+// access), on rows that are NaN already.
 hipError_t nc_embed_fwd(const int32_t* tok, const float* E, float* x, int n_tok, int d, int V,
-                        hipStream_t st);
+                        int32_t* flag, hipStream_t st);
 // scratch: see nc_embed_bwd_scratch_bytes
 size_t nc_embed_bwd_scratch_bytes(int n_tok, int vocab, int d);
 hipError_t nc_embed_bwd(const int32_t* tok, const float* dx, float* dE, int n_tok, int vocab,
@@ -49,9 +51,11 @@ hipError_t nc_fp8_quantize(int dtype, const void* x, int64_t n, float* partial,
                            float* amax_scale, uint8_t* q, hipStream_t st);
 
 // ---- softmax cross-entropy over rows of fp32 logits
-// dz = scale*(softmax(z) - onehot(y)) in the activation type; loss_rows[i] = lse - z[y]
+// dz = scale*(softmax(z) - onehot(y)) in the activation type; loss_rows[i] = lse - z[y].
+// A target outside [0, V) gives a NaN loss row and dz row and sets bit 1 of *flag.
 hipError_t nc_cross_entropy(int dtype, const float* z, const int32_t* tgt, void* dz,
-                            float* loss_rows, int rows, int V, float scale, hipStream_t st);
+                            float* loss_rows, int rows, int V, float scale, int32_t* flag,
+                            hipStream_t st);
 // out[0] = scale * sum(vals[0..n))   (fixed-order, single workgroup)
 hipError_t nc_sum_scaled(const float* vals, int n, float scale, float* out, hipStream_t st);
 

@@ -69,7 +69,7 @@ struct nc_ctx {
   // activation arena byte offsets
   std::vector<LayerAct> la;
   size_t xf, rf, x, dx, dxT, da, dqkv, dO, Dbuf, dh, z, dz, loss_rows, ws, ws_bytes, emb,
-      nsU, frob, norms, nm_vm, nm_q, nm_inv, nm_scale, act_bytes;
+      nsU, frob, norms, nm_vm, nm_q, nm_inv, nm_scale, flags, act_bytes;
   int64_t nm_rows = 0;   // NorMuon: rows of all block matrices (4L d + L F + L d)
   // Newton-Schulz buffers per group (0: square [d,d] (4L, or 2L with grouped
   // key/value heads), 1: 2L wide [d,F], 2: 2L [dk,d] with grouped key/value heads):
@@ -130,6 +130,10 @@ nc_status validate(const nc_model_config* m, const nc_optim_config* o, std::stri
   if (m->fp8_forward != 0 && m->fp8_forward != 1) { why = "fp8_forward is 0 or 1"; return NC_ERR_INVALID_ARG; }
   if (m->fp8_forward && m->dtype != NC_BF16) {
     why = "fp8_forward needs the bf16 configuration";
+    return NC_ERR_UNSUPPORTED;
+  }
+  if (m->fp8_forward && m->d_ff % 128) {
+    why = "fp8_forward needs d_ff % 128 == 0 (the fp8 products take K in steps of 128)";
     return NC_ERR_UNSUPPORTED;
   }
   if (m->n_kv_head < 0 || (m->n_kv_head > 0 && m->n_head % m->n_kv_head)) {
@@ -226,6 +230,7 @@ void plan(nc_ctx* c) {
   c->z = a.take((size_t)c->chunk * V * 4);
   c->dz = a.take((size_t)c->chunk * V * es);
   c->loss_rows = a.take(N * 4);
+  c->flags = a.take(256);   // [0]: bits of out-of-range ids seen (1 token, 2 target)
   // split-K for the weight-gradient products (bf16 MFMA path)
   auto sp = [&](int M, int Nn, int K) { return c->dt ? nc_gemm_pick_splits(M, Nn, K) : 1; };
   c->splits_qkv = sp(W, d, (int)N);
@@ -365,6 +370,10 @@ hipError_t gemm_fp8_fwd(nc_ctx* c, const void* X, int K, const void* Wt, int Nou
   uint8_t* wq = reinterpret_cast<uint8_t*>(c->aa + c->q8w);
   const bool c_f32 = epi == kEpiStoreF32 || epi == kEpiAccF32;
   const size_t nx = (size_t)N * K, nw = (size_t)Nout * K;
+  if (K % 128) {
+    c->range_error = "fp8 GEMM needs K % 128 == 0 (K=" + std::to_string(K) + ")";
+    return hipErrorInvalidValue;
+  }
   // every extent inside its arena, also in a dry run
   if (!in_arena(c, X, nx * 2) || !in_arena(c, Wt, nw * 2) || !in_arena(c, xa, nx) ||
       !in_arena(c, wq, nw) || !in_arena(c, C, ((size_t)(N - 1) * ldc + Nout) * (c_f32 ? 4 : 2))) {
@@ -487,6 +496,7 @@ nc_status nc_bind(nc_ctx* ctx, void* d_param_arena, size_t param_bytes, void* d_
   NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oAv), 0.f, 2ULL * ctx->V * ctx->d, ctx->st), "zero v");
   if (ctx->nm_rows)
     NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oV2), 0.f, ctx->nm_rows, ctx->st), "zero normuon v2");
+  NC_TRY(nc_fill_f32(A<float>(ctx, ctx->flags), 0.f, 1, ctx->st), "clear input flags");
   ctx->step = 0;
   NC_TRY(hipStreamSynchronize(ctx->st), "bind sync");
   ctx->bound = true;
@@ -562,7 +572,8 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
   char* aa = ctx->aa;
 
   // ---------------------------------------------------------------- forward
-  NC_TRY(nc_embed_fwd(tok, P<float>(ctx, ctx->oP) + ctx->n_block, x, N, d, V, st), "embed");
+  int32_t* flags = A<int32_t>(ctx, ctx->flags);
+  NC_TRY(nc_embed_fwd(tok, P<float>(ctx, ctx->oP) + ctx->n_block, x, N, d, V, flags, st), "embed");
   for (int l = 0; l < L; ++l) {
     const LayerAct& la = ctx->la[l];
     const size_t wb = (size_t)l * ctx->S;
@@ -599,7 +610,8 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
     NC_GEMM(gemm(ctx, xfc, d, kKCont, wptr_head(ctx), d, kKCont, aa + ctx->z, V, nc, V, d,
                 kEpiStoreF32), "logits");
     NC_TRY(nc_cross_entropy(dt, A<float>(ctx, ctx->z), tgt + c0, aa + ctx->dz,
-                            A<float>(ctx, ctx->loss_rows) + c0, nc, V, ce_scale, st), "ce");
+                            A<float>(ctx, ctx->loss_rows) + c0, nc, V, ce_scale, flags, st),
+           "ce");
     NC_GEMM(gemm(ctx, aa + ctx->dz, V, kKCont, wptr_head(ctx), d, kMNCont, da + (size_t)c0 * d, d,
                 nc, d, V, kEpiStoreF32, nullptr, nullptr, ctx->splits_dxf), "dxf");
     NC_GEMM(gemm(ctx, aa + ctx->dz, V, kMNCont, xfc, d, kMNCont, G + wh, d, V, d, nc, kEpiAccF32,
@@ -886,6 +898,21 @@ nc_status nc_check_finite(nc_ctx* ctx, int32_t* host_flag) {
   return h ? NC_ERR_NONFINITE : NC_OK;
 }
 
+nc_status nc_check_inputs(nc_ctx* ctx, int32_t* host_flags) {
+  if (!ctx || !host_flags) return NC_ERR_INVALID_ARG;
+  if (!ctx->bound) return fail(ctx, NC_ERR_STATE, "bind first");
+  int32_t* flag = A<int32_t>(ctx, ctx->flags);
+  int32_t h = 0;
+  NC_TRY(hipMemcpyAsync(&h, flag, 4, hipMemcpyDeviceToHost, ctx->st), "flag copy");
+  NC_TRY(nc_fill_f32(reinterpret_cast<float*>(flag), 0.f, 1, ctx->st), "flag clear");
+  NC_TRY(hipStreamSynchronize(ctx->st), "inputs sync");
+  *host_flags = h & 3;
+  if (!h) return NC_OK;
+  return fail(ctx, NC_ERR_INVALID_ARG,
+              std::string("out-of-range ") + ((h & 1) ? "token" : "") + ((h & 3) == 3 ? " and " : "") +
+                  ((h & 2) ? "target" : "") + " id(s) since the last check");
+}
+
 nc_status nc_flops(const nc_ctx* ctx, int32_t B, double* fb, double* opt) {
   if (!ctx || B < 0) return NC_ERR_INVALID_ARG;
   const double L = ctx->L, d = ctx->d, F = ctx->F, V = ctx->V, T = ctx->T;
@@ -919,11 +946,24 @@ nc_status nc_flops(const nc_ctx* ctx, int32_t B, double* fb, double* opt) {
 }
 
 // ----------------------------------------------------------- single ops
-nc_status nc_op_gemm(int32_t dtype, const void* A_, int64_t lda, int32_t al, const void* B_,
-                     int64_t ldb, int32_t bl, void* C_, int64_t ldc, int32_t M, int32_t N,
-                     int32_t K, int32_t batch, int64_t sA, int64_t sB, int64_t sC,
-                     int32_t epi, const void* aux_in, void* aux_out, float alpha, float p0,
-                     float p1, int32_t splits, void* workspace, size_t workspace_bytes,
+// True if `batch` row-major [rows, cols] slices with leading dimension ld and
+// batch stride bs, of es-byte elements, fit in `have` bytes from their base,
+// and ld is at least cols.  Empty operands always fit.
+static bool span_ok(size_t have, int64_t rows, int64_t cols, int64_t ld, int64_t bs, int64_t batch,
+                    size_t es) {
+  if (rows <= 0 || cols <= 0 || batch <= 0) return true;
+  if (ld < cols || bs < 0) return false;
+  const unsigned __int128 elems = (unsigned __int128)(batch - 1) * (uint64_t)bs +
+                                  (unsigned __int128)(rows - 1) * (uint64_t)ld + (uint64_t)cols;
+  return elems * es <= (unsigned __int128)have;
+}
+
+nc_status nc_op_gemm(int32_t dtype, const void* A_, size_t A_bytes, int64_t lda, int32_t al,
+                     const void* B_, size_t B_bytes, int64_t ldb, int32_t bl, void* C_,
+                     size_t C_bytes, int64_t ldc, int32_t M, int32_t N, int32_t K, int32_t batch,
+                     int64_t sA, int64_t sB, int64_t sC, int32_t epi, const void* aux_in,
+                     size_t aux_in_bytes, void* aux_out, size_t aux_out_bytes, float alpha,
+                     float p0, float p1, int32_t splits, void* workspace, size_t workspace_bytes,
                      void* stream) {
   if (!A_ || !B_ || !C_ || M < 0 || N < 0 || K < 1 || batch < 1) return NC_ERR_INVALID_ARG;
   if ((dtype != NC_FP32 && dtype != NC_BF16) || al < 0 || al > 1 || bl < 0 || bl > 1 ||
@@ -932,11 +972,24 @@ nc_status nc_op_gemm(int32_t dtype, const void* A_, int64_t lda, int32_t al, con
   if ((epi == kEpiDual && !aux_out) ||
       ((epi == kEpiRelu2Bwd || epi == kEpiPoly) && !aux_in))
     return NC_ERR_INVALID_ARG;
+  if (splits < 1) splits = 1;
+  // operand extents
+  const size_t es = dtype == NC_BF16 ? 2 : 4;
+  const bool c_f32 = splits > 1 || epi == kEpiStoreF32 || epi == kEpiAccF32 || epi == kEpiDual;
+  const bool a_ok = al == kKCont ? span_ok(A_bytes, M, K, lda, sA, batch, es)
+                                 : span_ok(A_bytes, K, M, lda, sA, batch, es);
+  const bool b_ok = bl == kKCont ? span_ok(B_bytes, N, K, ldb, sB, batch, es)
+                                 : span_ok(B_bytes, K, N, ldb, sB, batch, es);
+  const bool c_ok = span_ok(C_bytes, M, N, ldc, sC, batch, c_f32 ? 4 : es);
+  const bool aux_reads = epi == kEpiRelu2Bwd || epi == kEpiPoly || (epi == kEpiDual && aux_in);
+  const bool ai_ok = !aux_reads || span_ok(aux_in_bytes, M, N, ldc, sC, batch,
+                                           epi == kEpiDual ? 4 : es);
+  const bool ao_ok = epi != kEpiDual || span_ok(aux_out_bytes, M, N, ldc, sC, batch, es);
+  if (!a_ok || !b_ok || !c_ok || !ai_ok || !ao_ok) return NC_ERR_INVALID_ARG;
   if (dtype == NC_BF16) {
     if (K % 8 || (al == kMNCont && M % 8) || (bl == kMNCont && N % 8)) return NC_ERR_UNSUPPORTED;
     if (lda % 8 || ldb % 8) return NC_ERR_UNSUPPORTED;
   }
-  if (splits < 1) splits = 1;
   if (splits > 1) {
     if (dtype != NC_BF16 || (epi != kEpiStoreF32 && epi != kEpiAccF32)) return NC_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < (size_t)splits * batch * M * N * 4)
@@ -952,13 +1005,17 @@ nc_status nc_op_gemm(int32_t dtype, const void* A_, int64_t lda, int32_t al, con
                                                                                  : NC_ERR_HIP;
 }
 
-nc_status nc_op_gemm_fp8(const void* A_, int64_t lda, const void* B_, int64_t ldb, void* C_,
-                         int64_t ldc, int32_t M, int32_t N, int32_t K, int32_t epi, float alpha,
-                         void* stream) {
+nc_status nc_op_gemm_fp8(const void* A_, size_t A_bytes, int64_t lda, const void* B_,
+                         size_t B_bytes, int64_t ldb, void* C_, size_t C_bytes, int64_t ldc,
+                         int32_t M, int32_t N, int32_t K, int32_t epi, float alpha, void* stream) {
   if (!A_ || !B_ || !C_ || M < 0 || N < 0 || K < 1) return NC_ERR_INVALID_ARG;
   if (epi != kEpiStore && epi != kEpiStoreF32 && epi != kEpiAccF32 && epi != kEpiRelu2)
     return NC_ERR_INVALID_ARG;
   if (lda < K || ldb < K || ldc < N) return NC_ERR_INVALID_ARG;
+  const size_t ce = epi == kEpiStoreF32 || epi == kEpiAccF32 ? 4 : 2;
+  if (!span_ok(A_bytes, M, K, lda, 0, 1, 1) || !span_ok(B_bytes, N, K, ldb, 0, 1, 1) ||
+      !span_ok(C_bytes, M, N, ldc, 0, 1, ce))
+    return NC_ERR_INVALID_ARG;
   if (K % 128 || lda % 16 || ldb % 16) return NC_ERR_UNSUPPORTED;
   GemmParams g{};
   g.A = A_; g.B = B_; g.C = C_;
@@ -971,10 +1028,15 @@ nc_status nc_op_gemm_fp8(const void* A_, int64_t lda, const void* B_, int64_t ld
   return e == hipSuccess ? NC_OK : NC_ERR_HIP;
 }
 
-nc_status nc_op_fp8_quantize(int32_t dtype, const void* x, int64_t n, float* amax_scale,
-                             void* q, float* workspace, void* stream) {
+nc_status nc_op_fp8_quantize(int32_t dtype, const void* x, size_t x_bytes, int64_t n,
+                             float* amax_scale, size_t amax_scale_bytes, void* q, size_t q_bytes,
+                             float* workspace, size_t workspace_bytes, void* stream) {
   if (!x || !amax_scale || !q || !workspace || n < 1) return NC_ERR_INVALID_ARG;
   if (dtype != NC_FP32 && dtype != NC_BF16) return NC_ERR_INVALID_ARG;
+  const size_t es = dtype == NC_BF16 ? 2 : 4;
+  if ((uint64_t)n > x_bytes / es || (uint64_t)n > q_bytes || amax_scale_bytes < 2 * sizeof(float) ||
+      workspace_bytes < 1024 * sizeof(float))
+    return NC_ERR_INVALID_ARG;
   return nc_fp8_quantize(dtype == NC_BF16, x, n, workspace, amax_scale,
                          static_cast<uint8_t*>(q), static_cast<hipStream_t>(stream)) ==
                  hipSuccess
@@ -982,25 +1044,51 @@ nc_status nc_op_fp8_quantize(int32_t dtype, const void* x, int64_t n, float* ama
              : NC_ERR_HIP;
 }
 
-nc_status nc_op_attention_fwd(int32_t dtype, const void* q, const void* k, const void* v,
-                              int64_t ld_qkv, void* o, int64_t ld_o, float* lse, int32_t B,
-                              int32_t T, int32_t H, int32_t n_kv_head, int32_t window,
+// Extents of the attention operands: q, o, dq have H heads, k, v, dk, dv
+// n_kv_head heads, of 128 columns each, on B*T token rows; lse and D are
+// [B, H, T] fp32.
+static bool attn_rows_ok(size_t have, int64_t rows, int64_t heads, int64_t ld, size_t es) {
+  return span_ok(have, rows, heads * 128, ld, 0, 1, es);
+}
+
+nc_status nc_op_attention_fwd(int32_t dtype, const void* q, size_t q_bytes, const void* k,
+                              size_t k_bytes, const void* v, size_t v_bytes, int64_t ld_qkv,
+                              void* o, size_t o_bytes, int64_t ld_o, float* lse, size_t lse_bytes,
+                              int32_t B, int32_t T, int32_t H, int32_t n_kv_head, int32_t window,
                               void* stream) {
   if (!q || !k || !v || !o || !lse || B < 1 || T < 1 || H < 1 || window < -1 ||
-      n_kv_head < 1 || H % n_kv_head)
+      n_kv_head < 1 || H % n_kv_head || (dtype != NC_FP32 && dtype != NC_BF16))
+    return NC_ERR_INVALID_ARG;
+  const size_t es = dtype == NC_BF16 ? 2 : 4;
+  const int64_t rows = (int64_t)B * T;
+  if (!attn_rows_ok(q_bytes, rows, H, ld_qkv, es) || !attn_rows_ok(k_bytes, rows, n_kv_head, ld_qkv, es) ||
+      !attn_rows_ok(v_bytes, rows, n_kv_head, ld_qkv, es) || !attn_rows_ok(o_bytes, rows, H, ld_o, es) ||
+      !span_ok(lse_bytes, (int64_t)B * H, T, T, 0, 1, 4))
     return NC_ERR_INVALID_ARG;
   if (dtype == NC_BF16 && (T % 128 || ld_qkv % 8 || ld_o % 8)) return NC_ERR_UNSUPPORTED;
   return nc_attn_fwd(dtype == NC_BF16, q, k, v, ld_qkv, o, ld_o, lse, B, T, H, n_kv_head, window,
                      static_cast<hipStream_t>(stream)) == hipSuccess ? NC_OK : NC_ERR_HIP;
 }
 
-nc_status nc_op_attention_bwd(int32_t dtype, const void* q, const void* k, const void* v,
-                              int64_t ld_qkv, const void* o, const void* dO, int64_t ld_o,
-                              const float* lse, float* D, void* dq, void* dk, void* dv,
-                              int64_t ld_d, int32_t B, int32_t T, int32_t H, int32_t n_kv_head,
-                              int32_t window, void* stream) {
+nc_status nc_op_attention_bwd(int32_t dtype, const void* q, size_t q_bytes, const void* k,
+                              size_t k_bytes, const void* v, size_t v_bytes, int64_t ld_qkv,
+                              const void* o, size_t o_bytes, const void* dO, size_t dO_bytes,
+                              int64_t ld_o, const float* lse, size_t lse_bytes, float* D,
+                              size_t D_bytes, void* dq, size_t dq_bytes, void* dk,
+                              size_t dk_bytes, void* dv, size_t dv_bytes, int64_t ld_d, int32_t B,
+                              int32_t T, int32_t H, int32_t n_kv_head, int32_t window,
+                              void* stream) {
   if (!q || !k || !v || !o || !dO || !lse || !D || !dq || !dk || !dv || B < 1 || T < 1 || H < 1 ||
-      window < -1 || n_kv_head < 1 || H % n_kv_head)
+      window < -1 || n_kv_head < 1 || H % n_kv_head || (dtype != NC_FP32 && dtype != NC_BF16))
+    return NC_ERR_INVALID_ARG;
+  const size_t es = dtype == NC_BF16 ? 2 : 4;
+  const int64_t rows = (int64_t)B * T, hk = n_kv_head;
+  if (!attn_rows_ok(q_bytes, rows, H, ld_qkv, es) || !attn_rows_ok(k_bytes, rows, hk, ld_qkv, es) ||
+      !attn_rows_ok(v_bytes, rows, hk, ld_qkv, es) || !attn_rows_ok(o_bytes, rows, H, ld_o, es) ||
+      !attn_rows_ok(dO_bytes, rows, H, ld_o, es) || !attn_rows_ok(dq_bytes, rows, H, ld_d, es) ||
+      !attn_rows_ok(dk_bytes, rows, hk, ld_d, es) || !attn_rows_ok(dv_bytes, rows, hk, ld_d, es) ||
+      !span_ok(lse_bytes, (int64_t)B * H, T, T, 0, 1, 4) ||
+      !span_ok(D_bytes, (int64_t)B * H, T, T, 0, 1, 4))
     return NC_ERR_INVALID_ARG;
   if (dtype == NC_BF16 && (T % 128 || ld_qkv % 8 || ld_o % 8 || ld_d % 8)) return NC_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);

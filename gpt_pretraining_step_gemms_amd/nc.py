@@ -87,15 +87,17 @@ def load():
         "nc_set_param": [P, I32, P, I32],
         "nc_get_tensor": [P, I32, I32, P, I32],
         "nc_check_finite": [P, ctypes.POINTER(I32)],
+        "nc_check_inputs": [P, ctypes.POINTER(I32)],
         "nc_validate_launches": [P, I32],
         "nc_flops": [P, I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)],
-        "nc_op_gemm": [I32, P, I64, I32, P, I64, I32, P, I64, I32, I32, I32, I32, I64, I64, I64,
-                       I32, P, P, F32, F32, F32, I32, P, SZ, P],
-        "nc_op_gemm_fp8": [P, I64, P, I64, P, I64, I32, I32, I32, I32, F32, P],
-        "nc_op_fp8_quantize": [I32, P, I64, P, P, P, P],
-        "nc_op_attention_fwd": [I32, P, P, P, I64, P, I64, P, I32, I32, I32, I32, I32, P],
-        "nc_op_attention_bwd": [I32, P, P, P, I64, P, P, I64, P, P, P, P, P, I64, I32, I32, I32,
+        "nc_op_gemm": [I32, P, SZ, I64, I32, P, SZ, I64, I32, P, SZ, I64, I32, I32, I32, I32,
+                       I64, I64, I64, I32, P, SZ, P, SZ, F32, F32, F32, I32, P, SZ, P],
+        "nc_op_gemm_fp8": [P, SZ, I64, P, SZ, I64, P, SZ, I64, I32, I32, I32, I32, F32, P],
+        "nc_op_fp8_quantize": [I32, P, SZ, I64, P, SZ, P, SZ, P, SZ, P],
+        "nc_op_attention_fwd": [I32, P, SZ, P, SZ, P, SZ, I64, P, SZ, I64, P, SZ, I32, I32, I32,
                                 I32, I32, P],
+        "nc_op_attention_bwd": [I32, P, SZ, P, SZ, P, SZ, I64, P, SZ, P, SZ, I64, P, SZ, P, SZ,
+                                P, SZ, P, SZ, P, SZ, I64, I32, I32, I32, I32, I32, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -257,6 +259,15 @@ class Model:
             _check(s, self.ctx, "check_finite")
         return flag.value == 0
 
+    def check_inputs(self):
+        """(ok, flags): whether every token and target id since the last call
+        was in [0, vocab); flags bit 0 = a bad token id, bit 1 = a bad target."""
+        flag = ctypes.c_int32()
+        s = self.lib.nc_check_inputs(self.ctx, ctypes.byref(flag))
+        if s not in (NC_OK, NC_ERR_INVALID_ARG):
+            _check(s, self.ctx, "check_inputs")
+        return flag.value == 0, flag.value
+
     def flops(self, B=None):
         fb, opt = ctypes.c_double(), ctypes.c_double()
         _check(self.lib.nc_flops(self.ctx, B or self.max_b, ctypes.byref(fb), ctypes.byref(opt)),
@@ -284,6 +295,23 @@ def _dtype_code(t):
     raise TypeError(t.dtype)
 
 
+def extent(t):
+    """Bytes of device memory the caller owns from t's first element to the
+    end of its storage (what the op entry points check layouts against)."""
+    if t is None:
+        return 0
+    st = t.untyped_storage()
+    return st.nbytes() - (t.data_ptr() - st.data_ptr())
+
+
+def _opt(t):
+    return (_ptr(t), extent(t)) if t is not None else (None, 0)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
 def gemm(A, a_layout, B, b_layout, C, M, N, K, epilogue=EPI_STORE, aux_in=None, aux_out=None,
          alpha=1.0, p0=0.0, p1=0.0, lda=None, ldb=None, ldc=None, batch=1, sA=0, sB=0, sC=0,
          splits=1, workspace=None, dtype=None):
@@ -292,48 +320,45 @@ def gemm(A, a_layout, B, b_layout, C, M, N, K, epilogue=EPI_STORE, aux_in=None, 
     lda = lda if lda is not None else A.shape[-1]
     ldb = ldb if ldb is not None else B.shape[-1]
     ldc = ldc if ldc is not None else C.shape[-1]
-    ws = workspace if workspace is not None else None
-    s = lib.nc_op_gemm(dt, _ptr(A), lda, a_layout, _ptr(B), ldb, b_layout, _ptr(C), ldc, M, N, K,
-                       batch, sA, sB, sC, epilogue,
-                       _ptr(aux_in) if aux_in is not None else None,
-                       _ptr(aux_out) if aux_out is not None else None,
-                       alpha, p0, p1, splits, _ptr(ws) if ws is not None else None,
-                       ws.numel() * ws.element_size() if ws is not None else 0,
-                       ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    ai, ao, ws = _opt(aux_in), _opt(aux_out), _opt(workspace)
+    s = lib.nc_op_gemm(dt, _ptr(A), extent(A), lda, a_layout, _ptr(B), extent(B), ldb, b_layout,
+                       _ptr(C), extent(C), ldc, M, N, K, batch, sA, sB, sC, epilogue, ai[0], ai[1],
+                       ao[0], ao[1], alpha, p0, p1, splits, ws[0], ws[1], _stream())
     _check(s, what="nc_op_gemm")
 
 
 def attention_fwd(q, k, v, o, lse, B, T, H, ld_qkv, ld_o, window=-1, n_kv_head=None):
     lib = load()
-    s = lib.nc_op_attention_fwd(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), ld_qkv, _ptr(o), ld_o,
-                                _ptr(lse), B, T, H, n_kv_head or H, window,
-                                ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    s = lib.nc_op_attention_fwd(_dtype_code(q), _ptr(q), extent(q), _ptr(k), extent(k), _ptr(v),
+                                extent(v), ld_qkv, _ptr(o), extent(o), ld_o, _ptr(lse),
+                                extent(lse), B, T, H, n_kv_head or H, window, _stream())
     _check(s, what="nc_op_attention_fwd")
 
 
 def attention_bwd(q, k, v, o, dO, lse, D, dq, dk, dv, B, T, H, ld_qkv, ld_o, ld_d, window=-1,
                   n_kv_head=None):
     lib = load()
-    s = lib.nc_op_attention_bwd(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), ld_qkv, _ptr(o),
-                                _ptr(dO), ld_o, _ptr(lse), _ptr(D), _ptr(dq), _ptr(dk), _ptr(dv),
-                                ld_d, B, T, H, n_kv_head or H, window,
-                                ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    s = lib.nc_op_attention_bwd(_dtype_code(q), _ptr(q), extent(q), _ptr(k), extent(k), _ptr(v),
+                                extent(v), ld_qkv, _ptr(o), extent(o), _ptr(dO), extent(dO), ld_o,
+                                _ptr(lse), extent(lse), _ptr(D), extent(D), _ptr(dq), extent(dq),
+                                _ptr(dk), extent(dk), _ptr(dv), extent(dv), ld_d, B, T, H,
+                                n_kv_head or H, window, _stream())
     _check(s, what="nc_op_attention_bwd")
 
 
 def gemm_fp8(A8, B8, C, M, N, K, alpha, epilogue=EPI_STORE, lda=None, ldb=None, ldc=None):
     """C = alpha * A8 B8^T for K-contiguous uint8 (fp8 e4m3) operands."""
     lib = load()
-    s = lib.nc_op_gemm_fp8(_ptr(A8), lda or A8.shape[-1], _ptr(B8), ldb or B8.shape[-1], _ptr(C),
-                           ldc or C.shape[-1], M, N, K, epilogue, alpha,
-                           ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    s = lib.nc_op_gemm_fp8(_ptr(A8), extent(A8), lda or A8.shape[-1], _ptr(B8), extent(B8),
+                           ldb or B8.shape[-1], _ptr(C), extent(C), ldc or C.shape[-1], M, N, K,
+                           epilogue, alpha, _stream())
     _check(s, what="nc_op_gemm_fp8")
 
 
 def fp8_quantize(x, q, amax_scale, workspace):
     """q (uint8, x.numel()) = e4m3(x * 448 / amax); amax_scale (2 floats) = amax, scale."""
     lib = load()
-    s = lib.nc_op_fp8_quantize(_dtype_code(x), _ptr(x), x.numel(), _ptr(amax_scale), _ptr(q),
-                               _ptr(workspace),
-                               ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    s = lib.nc_op_fp8_quantize(_dtype_code(x), _ptr(x), extent(x), x.numel(), _ptr(amax_scale),
+                               extent(amax_scale), _ptr(q), extent(q), _ptr(workspace),
+                               extent(workspace), _stream())
     _check(s, what="nc_op_fp8_quantize")

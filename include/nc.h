@@ -159,7 +159,11 @@ nc_status nc_zero_grads(nc_ctx* ctx);
 
 /* One micro-batch: forward and backward on B rows of seq_len tokens.
  * d_tokens, d_targets: device int32 [B, seq_len], ids in [0, vocab) (the
- * targets are the inputs shifted by one position; no ignore index).
+ * targets are the inputs shifted by one position; no ignore index).  The ids
+ * are read on the device only: an id outside [0, vocab) is never used as an
+ * index -- its embedding row, or its loss and logit-gradient row, becomes NaN
+ * (so the loss and the gradients of the step are non-finite) and a device
+ * flag records it for nc_check_inputs.
  * Adds grad_scale * d(mean cross-entropy over the B*seq_len positions)/dtheta
  * to every gradient (grad_scale = 1/K for K accumulated micro-batches) and
  * writes that mean cross-entropy (natural log, before grad_scale) to the
@@ -196,6 +200,11 @@ nc_status nc_get_tensor(nc_ctx* ctx, int32_t i, int32_t which, float* dst, int32
 /* Checks every parameter and gradient for NaN/Inf; synchronous.
  * *host_flag = 1 and NC_ERR_NONFINITE if one is found, else 0 and NC_OK. */
 nc_status nc_check_finite(nc_ctx* ctx, int32_t* host_flag);
+
+/* Synchronous.  *host_flags = the kinds of out-of-range ids nc_fwd_bwd has
+ * seen since nc_bind or the previous call (bit 0: a token id, bit 1: a target
+ * id), then clears the record; NC_ERR_INVALID_ARG if any, else NC_OK. */
+nc_status nc_check_inputs(nc_ctx* ctx, int32_t* host_flags);
 
 /* Model FLOPs of one nc_fwd_bwd on B rows (matrix products only; a plain
  * causal layer's attention counted at seq_len/2 keys per query, a windowed

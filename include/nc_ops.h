@@ -3,6 +3,13 @@
  * measuring the kernels the step is built from in isolation.  Same error
  * conventions as nc.h; all pointers are device pointers owned by the caller;
  * work is enqueued on `stream` (a hipStream_t, NULL = default stream).
+ *
+ * Every operand pointer comes with the number of bytes the caller owns from
+ * that address on (`<name>_bytes`).  Before anything is launched the library
+ * computes the bytes the requested layout touches (rows, leading dimension,
+ * batch stride, element size) and returns NC_ERR_INVALID_ARG if any operand
+ * would reach past its extent, or if a leading dimension is narrower than
+ * the rows it describes.
  */
 #ifndef NC_OPS_H_
 #define NC_OPS_H_
@@ -44,12 +51,13 @@ enum {
  * `workspace` (at least splits*batch*M*N*4 bytes).  Requirements: K, and M
  * or N where that operand is MN-contiguous, multiples of 8; 16-byte aligned
  * operands and leading dimensions (bf16 path). */
-nc_status nc_op_gemm(int32_t dtype, const void* A, int64_t lda, int32_t a_layout, const void* B,
-                     int64_t ldb, int32_t b_layout, void* C, int64_t ldc, int32_t M, int32_t N,
-                     int32_t K, int32_t batch, int64_t sA, int64_t sB, int64_t sC,
-                     int32_t epilogue, const void* aux_in, void* aux_out, float alpha, float p0,
-                     float p1, int32_t splits, void* workspace, size_t workspace_bytes,
-                     void* stream);
+nc_status nc_op_gemm(int32_t dtype, const void* A, size_t A_bytes, int64_t lda,
+                     int32_t a_layout, const void* B, size_t B_bytes, int64_t ldb,
+                     int32_t b_layout, void* C, size_t C_bytes, int64_t ldc, int32_t M,
+                     int32_t N, int32_t K, int32_t batch, int64_t sA, int64_t sB, int64_t sC,
+                     int32_t epilogue, const void* aux_in, size_t aux_in_bytes, void* aux_out,
+                     size_t aux_out_bytes, float alpha, float p0, float p1, int32_t splits,
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* fp8 GEMM: acc[m, n] = alpha * sum_k A(m, k) B(n, k) with A [M, K] and B [N, K]
  * K-contiguous OCP fp8 e4m3 bytes (row strides lda, ldb in bytes), fp32
@@ -60,16 +68,19 @@ nc_status nc_op_gemm(int32_t dtype, const void* A, int64_t lda, int32_t a_layout
  * (nanochat/common.py)"); alpha carries the product of the two inverse scales.
  * Requirements: K % 128 == 0, lda and ldb multiples of 16, 16-byte aligned
  * operands (NC_ERR_UNSUPPORTED otherwise). */
-nc_status nc_op_gemm_fp8(const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
-                         int64_t ldc, int32_t M, int32_t N, int32_t K, int32_t epilogue,
-                         float alpha, void* stream);
+nc_status nc_op_gemm_fp8(const void* A, size_t A_bytes, int64_t lda, const void* B,
+                         size_t B_bytes, int64_t ldb, void* C, size_t C_bytes, int64_t ldc,
+                         int32_t M, int32_t N, int32_t K, int32_t epilogue, float alpha,
+                         void* stream);
 
 /* Tensorwise fp8 quantisation of n values x (dtype NC_FP32 or NC_BF16):
  * amax_scale[0] = max |x|, amax_scale[1] = s = 448 / amax (1 if amax = 0), and
  * q[i] = e4m3(x[i] * s) rounded to nearest even and saturated at 448, so that
- * x ~ q / s.  amax_scale: 2 device floats; workspace: 1024 device floats. */
-nc_status nc_op_fp8_quantize(int32_t dtype, const void* x, int64_t n, float* amax_scale,
-                             void* q, float* workspace, void* stream);
+ * x ~ q / s.  A NaN in x makes amax and s NaN and every code 0x7F (e4m3 NaN).
+ * amax_scale: 2 device floats; workspace: 1024 device floats of scratch. */
+nc_status nc_op_fp8_quantize(int32_t dtype, const void* x, size_t x_bytes, int64_t n,
+                             float* amax_scale, size_t amax_scale_bytes, void* q, size_t q_bytes,
+                             float* workspace, size_t workspace_bytes, void* stream);
 
 /* Causal attention forward, head dim 128, scale 1/sqrt(128).  q, k, v:
  * token-major rows (row b*T + t, head h at columns h*128 .. h*128+127, row
@@ -81,20 +92,24 @@ nc_status nc_op_fp8_quantize(int32_t dtype, const void* x, int64_t n, float* ama
  * window (keys max(0, t - w) .. t; apidog.com, "5. Penyatuan Flash
  * Attention"); below -1 is NC_ERR_INVALID_ARG.  bf16 path needs
  * T % 128 == 0. */
-nc_status nc_op_attention_fwd(int32_t dtype, const void* q, const void* k, const void* v,
-                              int64_t ld_qkv, void* o, int64_t ld_o, float* lse, int32_t B,
-                              int32_t T, int32_t H, int32_t n_kv_head, int32_t window,
-                              void* stream);
+nc_status nc_op_attention_fwd(int32_t dtype, const void* q, size_t q_bytes, const void* k,
+                              size_t k_bytes, const void* v, size_t v_bytes, int64_t ld_qkv,
+                              void* o, size_t o_bytes, int64_t ld_o, float* lse,
+                              size_t lse_bytes, int32_t B, int32_t T, int32_t H,
+                              int32_t n_kv_head, int32_t window, void* stream);
 
 /* Causal attention backward from o, lse of the forward and dO (layout of o).
  * D (fp32 [B, H, T]) is caller-provided scratch receiving rowsum(dO * o).
  * Writes dq, dk, dv (layout of q/k/v with row stride ld_d; dk and dv of a
  * key/value head sum over its query heads).  n_kv_head and window as for the
  * forward pass (the same values the forward pass used). */
-nc_status nc_op_attention_bwd(int32_t dtype, const void* q, const void* k, const void* v,
-                              int64_t ld_qkv, const void* o, const void* dO, int64_t ld_o,
-                              const float* lse, float* D, void* dq, void* dk, void* dv,
-                              int64_t ld_d, int32_t B, int32_t T, int32_t H, int32_t n_kv_head,
+nc_status nc_op_attention_bwd(int32_t dtype, const void* q, size_t q_bytes, const void* k,
+                              size_t k_bytes, const void* v, size_t v_bytes, int64_t ld_qkv,
+                              const void* o, size_t o_bytes, const void* dO, size_t dO_bytes,
+                              int64_t ld_o, const float* lse, size_t lse_bytes, float* D,
+                              size_t D_bytes, void* dq, size_t dq_bytes, void* dk,
+                              size_t dk_bytes, void* dv, size_t dv_bytes, int64_t ld_d,
+                              int32_t B, int32_t T, int32_t H, int32_t n_kv_head,
                               int32_t window, void* stream);
 
 #ifdef __cplusplus

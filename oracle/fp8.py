@@ -9,6 +9,10 @@ silent: the format is e4m3 of the OCP 8-bit floating point specification
 scale is s = 448 / max|x| (1 when x is all zero), computed in fp32, and a
 value x is stored as e4m3(x * s), the product taken in fp32, rounded to the
 nearest representable value with ties to the even code, saturating at 448.
+A NaN is stored as the code 0x7F (the format's NaN, sign bit clear), and a
+NaN anywhere in a tensor makes its amax and scale NaN, so every code of that
+tensor is 0x7F: the error reaches the product instead of becoming a finite
+value.
 
 The encoder here works from the table of all representable values: a plain
 nearest-value search, not the bit manipulation of the HIP kernel.
@@ -39,15 +43,17 @@ _POS = _TABLE[:0x7F]                 # codes 0x00 .. 0x7E: 0 .. 448, increasing
 def e4m3_encode(x):
     """Codes (uint8) of float values x: nearest of the 127 non-negative finite
     values to |x| (|x| above 448 saturates), ties to the even code, sign bit
-    from x."""
+    from x; NaN -> 0x7F."""
     x = np.asarray(x, np.float64)
-    a = np.minimum(np.abs(x), 448.0)
+    nan = np.isnan(x)
+    a = np.minimum(np.abs(np.where(nan, 0.0, x)), 448.0)
     hi = np.clip(np.searchsorted(_POS, a, side="left"), 0, 0x7E)
     lo = np.clip(hi - 1, 0, 0x7E)
     d_lo, d_hi = a - _POS[lo], _POS[hi] - a
     pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
     code = np.where(pick_hi, hi, lo).astype(np.uint8)
-    return np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
+    code = np.where(np.signbit(x), code | 0x80, code)
+    return np.where(nan, 0x7F, code).astype(np.uint8)
 
 
 def e4m3_decode(codes):
@@ -68,7 +74,10 @@ def quantize_tensorwise(x):
     x * scale evaluated in fp32."""
     x32 = np.asarray(x, np.float32)
     amax = np.float32(np.max(np.abs(x32))) if x32.size else np.float32(0)
-    scale = np.float32(448.0) / amax if amax > 0 else np.float32(1.0)
+    if np.isnan(amax):
+        scale = np.float32(np.nan)
+    else:
+        scale = np.float32(448.0) / amax if amax > 0 else np.float32(1.0)
     return e4m3_encode((x32 * scale).astype(np.float32)), float(amax), float(scale)
 
 

@@ -61,6 +61,11 @@ def test_invalid_configurations_are_rejected():
     assert _status_of_plan(replace(TINY, vocab=500)) == nc.NC_ERR_UNSUPPORTED
     assert _status_of_plan(replace(TINY, dtype="bf16")) == nc.NC_ERR_UNSUPPORTED  # T=64 not % 128
     assert _status_of_plan(replace(TINY, d_model=0)) == nc.NC_ERR_INVALID_ARG
+    # the fp8 products take K in steps of 128: d_ff = 1536 + 64 is refused at plan time
+    small = replace(TINY, dtype="bf16", seq_len=128, d_ff=1536)
+    assert _status_of_plan(replace(small, fp8_forward=True)) == nc.NC_OK
+    assert _status_of_plan(replace(small, d_ff=1600, fp8_forward=True)) == nc.NC_ERR_UNSUPPORTED
+    assert _status_of_plan(replace(small, d_ff=1600)) == nc.NC_OK
     o = OptimConfig(ns_coeffs=((1.0, 0.0, 0.0),) * 8)
     assert _status_of_plan(TINY, o) == nc.NC_OK
     c = nc.optim_cfg_c(o)
@@ -250,25 +255,93 @@ def test_op_argument_errors_return_before_any_launch():
     lib = nc.load()
     fake = ctypes.c_void_p(0x100000)
     fp = ctypes.c_void_p(0x200000)
+    BIG = 1 << 40
     # fp8 GEMM: epilogue, leading dimensions, K
-    args = lambda K, lda, ldb, ldc, epi: (fake, lda, fake, ldb, fake, ldc, 64, 64, K, epi, 1.0, None)
+    args = lambda K, lda, ldb, ldc, epi: (fake, BIG, lda, fake, BIG, ldb, fake, BIG, ldc, 64, 64,
+                                          K, epi, 1.0, None)
     assert lib.nc_op_gemm_fp8(*args(256, 256, 256, 64, nc.EPI_RELU2_BWD)) == nc.NC_ERR_INVALID_ARG
     assert lib.nc_op_gemm_fp8(*args(256, 128, 256, 64, nc.EPI_STORE)) == nc.NC_ERR_INVALID_ARG
     assert lib.nc_op_gemm_fp8(*args(192, 192, 192, 64, nc.EPI_STORE)) == nc.NC_ERR_UNSUPPORTED
     assert lib.nc_op_gemm_fp8(*args(256, 264, 256, 64, nc.EPI_STORE)) == nc.NC_ERR_UNSUPPORTED
-    assert lib.nc_op_gemm_fp8(None, 256, fake, 256, fake, 64, 64, 64, 256, 0, 1.0, None) == \
-        nc.NC_ERR_INVALID_ARG
+    assert lib.nc_op_gemm_fp8(None, BIG, 256, fake, BIG, 256, fake, BIG, 64, 64, 64, 256, 0, 1.0,
+                              None) == nc.NC_ERR_INVALID_ARG
     # fp8 quantiser
-    assert lib.nc_op_fp8_quantize(nc.NC_FP32, fake, 0, fp, fake, fp, None) == nc.NC_ERR_INVALID_ARG
-    assert lib.nc_op_fp8_quantize(7, fake, 16, fp, fake, fp, None) == nc.NC_ERR_INVALID_ARG
-    assert lib.nc_op_fp8_quantize(nc.NC_FP32, fake, 16, fp, fake, None, None) == nc.NC_ERR_INVALID_ARG
+    q = lambda dt, n, ws: lib.nc_op_fp8_quantize(dt, fake, BIG, n, fp, 8, fake, BIG, ws, 4096, None)
+    assert q(nc.NC_FP32, 0, fp) == nc.NC_ERR_INVALID_ARG
+    assert q(7, 16, fp) == nc.NC_ERR_INVALID_ARG
+    assert q(nc.NC_FP32, 16, None) == nc.NC_ERR_INVALID_ARG
     # attention: key/value heads must divide the query heads; window >= -1; bf16 T % 128
     def fwd(H, hkv, win, T=256, dt=nc.NC_BF16):
-        return lib.nc_op_attention_fwd(dt, fake, fake, fake, 3 * 128 * H, fake, 128 * H, fp, 1, T,
-                                       H, hkv, win, None)
+        return lib.nc_op_attention_fwd(dt, fake, BIG, fake, BIG, fake, BIG, 3 * 128 * H, fake, BIG,
+                                       128 * H, fp, BIG, 1, T, H, hkv, win, None)
     assert fwd(4, 3, -1) == nc.NC_ERR_INVALID_ARG
     assert fwd(4, 0, -1) == nc.NC_ERR_INVALID_ARG
     assert fwd(4, 2, -2) == nc.NC_ERR_INVALID_ARG
     assert fwd(4, 2, 10, T=200) == nc.NC_ERR_UNSUPPORTED
-    assert lib.nc_op_attention_bwd(nc.NC_BF16, fake, fake, fake, 384, fake, fake, 128, fp, fp, fake,
-                                   fake, fake, 384, 1, 256, 1, 1, -3, None) == nc.NC_ERR_INVALID_ARG
+    assert lib.nc_op_attention_bwd(nc.NC_BF16, fake, BIG, fake, BIG, fake, BIG, 384, fake, BIG,
+                                   fake, BIG, 128, fp, BIG, fp, BIG, fake, BIG, fake, BIG, fake,
+                                   BIG, 384, 1, 256, 1, 1, -3, None) == nc.NC_ERR_INVALID_ARG
+
+
+def test_op_operand_extents_are_checked_before_any_launch():
+    """Every op entry point takes the bytes owned behind each operand and
+    refuses a layout that reaches past them, before any launch.  One case is
+    the layout mistake of a grouped-query buffer read with the full-width
+    strides (v at column 2 d, row stride 3 d): it must be refused."""
+    lib = nc.load()
+    fake = ctypes.c_void_p(0x100000)
+    BIG = 1 << 40
+    B, T, H, hkv = 32, 2048, 10, 2
+    d, dk = H * 128, hkv * 128
+    rows = B * T
+    qkv_bytes = rows * (d + 2 * dk) * 2            # the grouped-query buffer
+    # right layout: q at 0, k at d, v at d + dk, stride d + 2 dk
+    def fwd(v_bytes, ld, o_bytes=BIG, lse_bytes=B * H * T * 4):
+        return lib.nc_op_attention_fwd(nc.NC_BF16, fake, qkv_bytes, fake, qkv_bytes - d * 2, fake,
+                                       v_bytes, ld, fake, o_bytes, d, fake, lse_bytes, B, T, H,
+                                       hkv, -1, None)
+    good_ld = d + 2 * dk
+    assert fwd(qkv_bytes - (d + dk) * 2, 3 * d) == nc.NC_ERR_INVALID_ARG   # full-width stride
+    assert fwd(qkv_bytes - 2 * d * 2, 3 * d) == nc.NC_ERR_INVALID_ARG      # and v at 2 d
+    assert fwd(qkv_bytes - (d + dk) * 2, good_ld, o_bytes=rows * d * 2 - 2) == nc.NC_ERR_INVALID_ARG
+    assert fwd(qkv_bytes - (d + dk) * 2, good_ld, lse_bytes=B * H * T * 4 - 4) == nc.NC_ERR_INVALID_ARG
+    assert fwd(qkv_bytes - (d + dk) * 2, d - 8) == nc.NC_ERR_INVALID_ARG   # rows overlap
+    # backward: every one of the ten operands is checked
+    # exactly the bytes each one needs: ((rows - 1) ld + heads 128) elements
+    need_q, need_kv = ((rows - 1) * good_ld + d) * 2, ((rows - 1) * good_ld + dk) * 2
+    ext = dict(q=need_q, k=need_kv, v=need_kv, o=rows * d * 2, dO=rows * d * 2,
+               lse=B * H * T * 4, D=B * H * T * 4, dq=need_q, dk=need_kv, dv=need_kv)
+    def bwd(**short):
+        e = {k: v - short.get(k, 0) for k, v in ext.items()}
+        return lib.nc_op_attention_bwd(nc.NC_BF16, fake, e["q"], fake, e["k"], fake, e["v"], good_ld,
+                                       fake, e["o"], fake, e["dO"], d, fake, e["lse"], fake, e["D"],
+                                       fake, e["dq"], fake, e["dk"], fake, e["dv"], good_ld, B, T, H,
+                                       hkv, -1, None)
+    for name in ext:
+        assert bwd(**{name: 2}) == nc.NC_ERR_INVALID_ARG, name
+    # GEMM: A K-contiguous [M, K] needs ((M - 1) lda + K) elements; batch strides count
+    M, N, K = 300, 200, 256
+    def gemm(a_bytes=BIG, c_bytes=BIG, lda=K, batch=1, sA=0, epi=nc.EPI_STORE_F32, aux=0,
+             ws_bytes=0, splits=1):
+        return lib.nc_op_gemm(nc.NC_BF16, fake, a_bytes, lda, 0, fake, BIG, K, 0, fake, c_bytes, N,
+                              M, N, K, batch, sA, 0, 0, epi, fake if aux else None, aux,
+                              fake if aux else None, aux, 1.0, 0.0, 0.0, splits,
+                              fake if ws_bytes else None, ws_bytes, None)
+    need_a = ((M - 1) * K + K) * 2
+    assert gemm(a_bytes=need_a - 2) == nc.NC_ERR_INVALID_ARG
+    assert gemm(a_bytes=need_a, batch=2, sA=M * K) == nc.NC_ERR_INVALID_ARG
+    assert gemm(c_bytes=M * N * 4 - 4) == nc.NC_ERR_INVALID_ARG         # fp32 output
+    assert gemm(lda=K - 8) == nc.NC_ERR_INVALID_ARG
+    assert gemm(epi=nc.EPI_RELU2_BWD, aux=M * N * 2 - 2) == nc.NC_ERR_INVALID_ARG
+    assert gemm(splits=4, ws_bytes=4 * M * N * 4 - 4) == nc.NC_ERR_INVALID_ARG
+    # fp8 GEMM and quantiser
+    assert lib.nc_op_gemm_fp8(fake, 64 * 256 - 1, 256, fake, BIG, 256, fake, BIG, 64, 64, 64, 256,
+                              nc.EPI_STORE, 1.0, None) == nc.NC_ERR_INVALID_ARG
+    assert lib.nc_op_gemm_fp8(fake, BIG, 256, fake, BIG, 256, fake, 64 * 64 * 4 - 4, 64, 64, 64,
+                              256, nc.EPI_STORE_F32, 1.0, None) == nc.NC_ERR_INVALID_ARG
+    qz = lambda xb, qb, ab=8, wb=4096: lib.nc_op_fp8_quantize(nc.NC_BF16, fake, xb, 1000, fake, ab,
+                                                              fake, qb, fake, wb, None)
+    assert qz(1999, BIG) == nc.NC_ERR_INVALID_ARG
+    assert qz(BIG, 999) == nc.NC_ERR_INVALID_ARG
+    assert qz(BIG, BIG, ab=4) == nc.NC_ERR_INVALID_ARG
+    assert qz(BIG, BIG, wb=4092) == nc.NC_ERR_INVALID_ARG

@@ -469,6 +469,26 @@ def test_fp8_quantize_all_zero_input():
     assert not q.any()
 
 
+@pytest.mark.parametrize("dtype", [F32, BF])
+def test_fp8_quantize_nan_reaches_every_code(dtype):
+    """One NaN in the tensor: amax and scale NaN and every code 0x7F, as in
+    the oracle's codec (a NaN must not become a finite e4m3 value)."""
+    n = 20000 + 3
+    x = np.random.default_rng(3).standard_normal(n).astype(np.float32)
+    x[12345] = np.nan
+    xd = dev(x, dtype)
+    q = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    amax_scale = torch.empty(2, dtype=F32, device="cuda")
+    ws = torch.empty(1024, dtype=F32, device="cuda")
+    nc.fp8_quantize(xd, q, amax_scale, ws)
+    torch.cuda.synchronize()
+    codes, amax, scale = ofp8.quantize_tensorwise(host(xd).astype(np.float32))
+    assert np.isnan(amax) and np.isnan(scale)
+    got_amax, got_scale = host(amax_scale)
+    assert np.isnan(got_amax) and np.isnan(got_scale)
+    assert np.array_equal(q.cpu().numpy(), codes)
+
+
 @pytest.mark.parametrize("dtype,n", [(F32, 1000), (F32, 300001), (BF, 65536 + 7)])
 def test_fp8_quantize_bit_exact(dtype, n):
     """Tensorwise e4m3 quantisation: amax and scale exact, every byte equal to

@@ -176,19 +176,105 @@ def test_grouped_heads_with_sliding_windows_full_step():
     check_step(TINY_GQA, B=2, seed=43, windows=[8, 40])
 
 
-@pytest.mark.parametrize("name", ["small", "d12"])
+@pytest.mark.parametrize("name", ["small", "d12", "d20"])
 def test_fp8_forward_full_step(name):
     """Forward block products in fp8 e4m3 (tensorwise scales, quantised on the
     device) against the oracle's e4m3 emulation of the same products; the
     backward stays bf16 with the unquantised operands on both sides (bounds:
-    TOL["fp8"])."""
+    TOL["fp8"]).  d12 and d20 on one 2048-token row."""
     cfg = {"small": replace(SMALL_BF16, fp8_forward=True),
-           "d12": replace(with_batch(D12, micro_batch=1), fp8_forward=True)}[name]
+           "d12": replace(with_batch(D12, micro_batch=1), fp8_forward=True),
+           "d20": replace(with_batch(D20, micro_batch=1), fp8_forward=True)}[name]
     check_step(cfg, B=cfg.micro_batch, seed=51)
 
 
 def test_d12_shape_one_row():
     check_step(with_batch(D12, micro_batch=1), B=1, seed=7)
+
+
+def test_small_bf16_two_logit_chunks_with_ragged_tail():
+    """40 rows of 256 tokens = 10,240 positions: the lm_head / cross-entropy
+    loop runs a full 8,192-row chunk and a ragged 2,048-row one (offsets into
+    xf, targets, loss rows and the logit gradient), dWh accumulates over both
+    chunks with split-K, and every weight gradient takes K = 10,240 tokens in
+    more than one split.  Loss, every gradient and every update against the
+    oracle."""
+    cfg = with_batch(SMALL_BF16, micro_batch=40)
+    check_step(cfg, B=40, seed=61)
+
+
+def test_d20_two_rows():
+    """The d20 model shape on two 2048-token rows (4,096 positions), the
+    oracle's d20 micro-batch in the parity protocol."""
+    check_step(with_batch(D20, micro_batch=2), B=2, seed=17)
+
+
+def test_d20_full_micro_batch_equals_its_rows():
+    """The bench's launch configuration (d20, 32 rows = 65,536 positions: 8
+    logit chunks, the split-K counts planned for K = 65,536) against the same
+    32 rows run one at a time with grad_scale 1/32 and accumulated, a property
+    of the mean loss that holds at any size; single rows are tied to the
+    oracle by the one-row and two-row tests.  The forward and every
+    per-position gradient are the same arithmetic on both sides (products
+    over K are summed in the same order whatever M is, and
+    dz = (softmax - onehot) / 65,536 in both), so only the sums over
+    positions -- the weight gradients and the embedding's segment sums -- are
+    added in another order: fp32 rounding, far inside the bf16 bounds."""
+    cfg = D20
+    B = cfg.micro_batch
+    m = nc.Model(cfg, OptimConfig(), max_micro_batch=B)
+    m.init_params(seed=5, std=cfg.init_std)
+    tok, tgt = synthetic.token_rows(1000, B, cfg.seq_len, cfg.vocab, cfg.token_dist)
+    tok_d, tgt_d = gpu_tokens(tok), gpu_tokens(tgt)
+    print("[linearity] d20 B=32 full micro-batch", flush=True)
+    m.zero_grads()
+    loss_full = float(m.fwd_bwd(tok_d, tgt_d, 1.0).item())
+    full = {n: m.grad(n).clone() for n in m.names()}
+    m.zero_grads()
+    losses = []
+    out = torch.zeros(B, dtype=torch.float32, device="cuda")
+    for r in range(B):
+        m.fwd_bwd(tok_d[r:r + 1].contiguous(), tgt_d[r:r + 1].contiguous(), 1.0 / B,
+                  loss_out=out[r:r + 1])
+    torch.cuda.synchronize()
+    print(f"[linearity] loss full {loss_full:.6f} rows {out.mean().item():.6f}", flush=True)
+    assert out.mean().item() == pytest.approx(loss_full, rel=1e-6)
+    worst_c, worst_r = 1.0, 0.0
+    for n, g in full.items():
+        a = m.grad(n).double()
+        b = g.double()
+        c = float((a * b).sum() / (a.norm() * b.norm()))
+        r = float((a - b).abs().max() / b.abs().max())
+        worst_c, worst_r = min(worst_c, c), max(worst_r, r)
+        assert c >= 1 - 1e-6 and r <= 1e-3, (n, c, r)
+    print(f"[linearity] worst cos {worst_c:.9f} max-rel {worst_r:.2e}", flush=True)
+    assert m.check_inputs() == (True, 0)
+    m.close()
+
+
+def test_out_of_range_ids_are_reported_not_clamped():
+    """A token or target id outside [0, vocab) never indexes memory: the loss
+    and the gradients turn non-finite and nc_check_inputs reports which kind
+    of id it was (then clears)."""
+    cfg = TINY
+    m, params, tok, tgt = setup(cfg, B=2, seed=8)
+    run_gpu(m, tok, tgt)
+    assert m.check_inputs() == (True, 0)
+    bad = tok.copy()
+    bad[1, 5] = cfg.vocab
+    loss, grads = run_gpu(m, bad, tgt)
+    assert math.isnan(loss)
+    assert m.check_inputs() == (False, 1)
+    assert m.check_inputs() == (True, 0)            # cleared
+    assert not m.check_finite()
+    bad_t = tgt.copy()
+    bad_t[0, 0] = -1
+    loss, grads = run_gpu(m, tok, bad_t)
+    assert math.isnan(loss) and not np.isfinite(grads["Wh"]).all()
+    assert m.check_inputs() == (False, 2)
+    loss, _ = run_gpu(m, tok, tgt)
+    assert np.isfinite(loss) and m.check_inputs() == (True, 0)
+    m.close()
 
 
 @pytest.mark.parametrize("name,seed", [("d20", 11), ("d24", 12), ("d26", 13)])

@@ -53,6 +53,21 @@ def test_tensorwise_scale_maps_amax_to_448():
     assert a0 == 0.0 and s0 == 1.0 and not zero_codes.any()
 
 
+def test_nan_is_code_0x7f_and_poisons_the_tensor_scale():
+    """OCP e4m3 has one NaN pattern per sign (exponent 15, mantissa 7) and
+    no infinities: a NaN value is stored as 0x7F, and one NaN in a tensor
+    makes its amax and scale NaN, so every code of that tensor is 0x7F."""
+    assert fp8.e4m3_encode(np.nan) == 0x7F and fp8.e4m3_encode(-np.nan) == 0x7F
+    assert np.isnan(fp8.e4m3_decode(0x7F))
+    x = np.linspace(-3, 3, 11).astype(np.float32)
+    x[4] = np.nan
+    codes, amax, scale = fp8.quantize_tensorwise(x)
+    assert np.isnan(amax) and np.isnan(scale)
+    assert np.all(codes == 0x7F)
+    # finite values beside a NaN are not what decides the codes
+    assert fp8.e4m3_encode(np.array([1.0, np.nan, -2.0])).tolist() == [0x38, 0x7F, 0xC0]
+
+
 def test_fp8_matmul_is_the_product_of_decoded_values():
     rng = np.random.default_rng(1)
     a = rng.integers(0, 256, (3, 16)).astype(np.uint8)
