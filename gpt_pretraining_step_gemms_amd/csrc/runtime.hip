@@ -20,6 +20,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1003,6 +1004,64 @@ nc_status nc_op_gemm(int32_t dtype, const void* A_, size_t A_bytes, int64_t lda,
   g.workspace = static_cast<float*>(workspace); g.workspace_bytes = workspace_bytes;
   return nc_launch_gemm(dtype, g, static_cast<hipStream_t>(stream)) == hipSuccess ? NC_OK
                                                                                  : NC_ERR_HIP;
+}
+
+// ------------------------------------------- GEMM without a caller workspace
+// The split-K partial slabs of nc_op_gemm_noalloc live in this file-scope
+// device array (one copy per GPU, held until the process ends).  Host code
+// never passes the array's name to a kernel: it looks up each device's
+// address once with hipGetSymbolAddress and passes that.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+// Address of `scratch` on `dev`, looked up on the first call for that device
+// (with that device current, then the caller's device restored).
+static hipError_t scratch_on_device(int dev, float** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float* ptr[kMaxDevices] = {};
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return e;
+    if (back != hipSuccess) return back;
+    ptr[dev] = static_cast<float*>(p);
+  }
+  *out = ptr[dev];
+  return hipSuccess;
+}
+
+nc_status nc_op_gemm_noalloc(int32_t dtype, const void* A_, size_t A_bytes, int64_t lda,
+                             int32_t al, const void* B_, size_t B_bytes, int64_t ldb, int32_t bl,
+                             void* C_, size_t C_bytes, int64_t ldc, int32_t M, int32_t N, int32_t K,
+                             int32_t batch, int64_t sA, int64_t sB, int64_t sC, int32_t epi,
+                             const void* aux_in, size_t aux_in_bytes, void* aux_out,
+                             size_t aux_out_bytes, float alpha, float p0, float p1,
+                             int32_t splits, void* stream) {
+  if (splits < 1) splits = 1;
+  float* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (splits > 1) {
+    if (M < 0 || N < 0 || batch < 1) return NC_ERR_INVALID_ARG;
+    const unsigned __int128 need = (unsigned __int128)splits * (uint64_t)batch * (uint64_t)M *
+                                   (uint64_t)N * sizeof(float);
+    if (need > kNoAllocScratchBytes) return NC_ERR_INVALID_ARG;   // splits*batch*M*N*4 > 16 MiB
+    int dev = 0;
+    const hipError_t e = stream ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev)
+                                : hipGetDevice(&dev);
+    if (e != hipSuccess || scratch_on_device(dev, &ws) != hipSuccess) return NC_ERR_HIP;
+    ws_bytes = kNoAllocScratchBytes;
+  }
+  return nc_op_gemm(dtype, A_, A_bytes, lda, al, B_, B_bytes, ldb, bl, C_, C_bytes, ldc, M, N, K,
+                    batch, sA, sB, sC, epi, aux_in, aux_in_bytes, aux_out, aux_out_bytes, alpha,
+                    p0, p1, splits, ws, ws_bytes, stream);
 }
 
 nc_status nc_op_gemm_fp8(const void* A_, size_t A_bytes, int64_t lda, const void* B_,

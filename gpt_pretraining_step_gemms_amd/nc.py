@@ -92,6 +92,8 @@ def load():
         "nc_flops": [P, I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)],
         "nc_op_gemm": [I32, P, SZ, I64, I32, P, SZ, I64, I32, P, SZ, I64, I32, I32, I32, I32,
                        I64, I64, I64, I32, P, SZ, P, SZ, F32, F32, F32, I32, P, SZ, P],
+        "nc_op_gemm_noalloc": [I32, P, SZ, I64, I32, P, SZ, I64, I32, P, SZ, I64, I32, I32, I32,
+                               I32, I64, I64, I64, I32, P, SZ, P, SZ, F32, F32, F32, I32, P],
         "nc_op_gemm_fp8": [P, SZ, I64, P, SZ, I64, P, SZ, I64, I32, I32, I32, I32, F32, P],
         "nc_op_fp8_quantize": [I32, P, SZ, I64, P, SZ, P, SZ, P, SZ, P],
         "nc_op_attention_fwd": [I32, P, SZ, P, SZ, P, SZ, I64, P, SZ, I64, P, SZ, I32, I32, I32,
@@ -325,6 +327,24 @@ def gemm(A, a_layout, B, b_layout, C, M, N, K, epilogue=EPI_STORE, aux_in=None, 
                        _ptr(C), extent(C), ldc, M, N, K, batch, sA, sB, sC, epilogue, ai[0], ai[1],
                        ao[0], ao[1], alpha, p0, p1, splits, ws[0], ws[1], _stream())
     _check(s, what="nc_op_gemm")
+
+
+def gemm_noalloc(A, a_layout, B, b_layout, C, M, N, K, epilogue=EPI_STORE, aux_in=None,
+                 aux_out=None, alpha=1.0, p0=0.0, p1=0.0, lda=None, ldb=None, ldc=None, batch=1,
+                 sA=0, sB=0, sC=0, splits=1, dtype=None):
+    """gemm() through nc_op_gemm_noalloc: split-K partials in the library's
+    fixed device scratch instead of a caller workspace."""
+    lib = load()
+    dt = dtype if dtype is not None else _dtype_code(A)
+    lda = lda if lda is not None else A.shape[-1]
+    ldb = ldb if ldb is not None else B.shape[-1]
+    ldc = ldc if ldc is not None else C.shape[-1]
+    ai, ao = _opt(aux_in), _opt(aux_out)
+    s = lib.nc_op_gemm_noalloc(dt, _ptr(A), extent(A), lda, a_layout, _ptr(B), extent(B), ldb,
+                               b_layout, _ptr(C), extent(C), ldc, M, N, K, batch, sA, sB, sC,
+                               epilogue, ai[0], ai[1], ao[0], ao[1], alpha, p0, p1, splits,
+                               _stream())
+    _check(s, what="nc_op_gemm_noalloc")
 
 
 def attention_fwd(q, k, v, o, lse, B, T, H, ld_qkv, ld_o, window=-1, n_kv_head=None):

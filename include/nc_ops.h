@@ -59,6 +59,25 @@ nc_status nc_op_gemm(int32_t dtype, const void* A, size_t A_bytes, int64_t lda,
                      size_t aux_out_bytes, float alpha, float p0, float p1, int32_t splits,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* nc_op_gemm for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same product, epilogues and arguments, but no workspace argument.  With
+ * splits > 1 the split-K partial slabs go to a 16 MiB array the library
+ * keeps in each GPU's memory for the life of the process, so
+ * splits * batch * M * N * 4 must be at most 16 MiB (NC_ERR_INVALID_ARG
+ * otherwise, before any launch); splits = 1 uses no scratch.  Every slab is
+ * written before it is read, so no call depends on what an earlier one left.
+ * Calls on one GPU share that array: calls that can overlap (on different
+ * streams, or from different threads) race and must be serialised by the
+ * caller.  No hipMalloc, hipFree or allocating library routine is called. */
+nc_status nc_op_gemm_noalloc(int32_t dtype, const void* A, size_t A_bytes, int64_t lda,
+                             int32_t a_layout, const void* B, size_t B_bytes, int64_t ldb,
+                             int32_t b_layout, void* C, size_t C_bytes, int64_t ldc, int32_t M,
+                             int32_t N, int32_t K, int32_t batch, int64_t sA, int64_t sB,
+                             int64_t sC, int32_t epilogue, const void* aux_in,
+                             size_t aux_in_bytes, void* aux_out, size_t aux_out_bytes,
+                             float alpha, float p0, float p1, int32_t splits, void* stream);
+
 /* fp8 GEMM: acc[m, n] = alpha * sum_k A(m, k) B(n, k) with A [M, K] and B [N, K]
  * K-contiguous OCP fp8 e4m3 bytes (row strides lda, ldb in bytes), fp32
  * accumulation; the epilogue writes C (row stride ldc elements): NC_EPI_STORE
