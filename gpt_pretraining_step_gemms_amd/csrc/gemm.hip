@@ -547,9 +547,9 @@ hipError_t launch_bf16_cfg(const GemmParams& p, hipStream_t st) {
 // 8 x 4 tiles of 16 x 16 x 32 MFMAs): WM x WN waves make a (128 WM) x (64 WN)
 // block tile; the launcher uses 2 x 4 waves (256 x 256 tiles, 128 or 160 KB of
 // LDS, one block per CU).
-template <int WM_, int WN_, int ST_, int PK_ = 32, int MI_ = 32>
+template <int WM_, int WN_, int ST_, int PK_ = 32, int MI_ = 32, int WTN_ = 64>
 struct Pipe {
-  static constexpr int BM = 128 * WM_, BN = 64 * WN_, PK = PK_, STAGES = ST_;
+  static constexpr int BM = 128 * WM_, BN = WTN_ * WN_, PK = PK_, STAGES = ST_;
   // MFMA shape: 32 (v_mfma_f32_32x32x16_bf16) or 16 (v_mfma_f32_16x16x32_bf16)
   static constexpr int MI = MI_, KSUB = MI_ == 32 ? 16 : 32;
   static constexpr int WM = WM_, WN = WN_;
@@ -717,10 +717,11 @@ NC_DEV f32x4 mfma_f8(bf16x8 a0, bf16x8 a1, bf16x8 b0, bf16x8 b1, f32x4 c) {
 // F8: operands are fp8 e4m3 bytes, handled by the loads as pairs (the
 // launcher halves K and the leading dimensions), K-contiguous, half-stage ring
 // with 16 x 16 MFMAs only.
-template <int AL, int BL, int WM_, int WN_, int ST_, int PK_, int MI_, bool F8 = false>
-__global__ __launch_bounds__(WM_ * WN_ * 64, (Pipe<WM_, WN_, ST_, PK_, MI_>::kBlocksPerCU))
+template <int AL, int BL, int WM_, int WN_, int ST_, int PK_, int MI_, bool F8 = false,
+          int WTN_ = 64>
+__global__ __launch_bounds__(WM_ * WN_ * 64, (Pipe<WM_, WN_, ST_, PK_, MI_, WTN_>::kBlocksPerCU))
 void gemm_bf16_pipe_kernel(GemmParams p) {
-  using C = Pipe<WM_, WN_, ST_, PK_, MI_>;
+  using C = Pipe<WM_, WN_, ST_, PK_, MI_, WTN_>;
   constexpr int MI = C::MI;
   static_assert(!F8 || (MI == 16 && PK_ == 64 && ST_ == 5 && AL == kKCont && BL == kKCont),
                 "fp8: K-contiguous operands in the 64-deep half-stage ring");
@@ -784,6 +785,7 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
     issue_tile<BM, AL, LOADS_A, PK>(oa, m0, kt * PK, st, wave);
     issue_tile<BN, BL, LOADS_B, PK>(ob, n0, kt * PK, st + TILE_A, wave);
   };
+  bf16x8 frA[C::TM], frB[2][C::TN];                  // fragments of the mid-step schedule
   auto step = [&]<int S>(int i) {
     if constexpr (HALF) {
       // loads go out as B of tile i + 1, then A of tile i + 2: tile i has
@@ -911,7 +913,113 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
       if constexpr (AL == kKCont) __builtin_amdgcn_s_setprio(0);
     }
   };
-  if constexpr (HALF) {
+  // Mid-step barrier (half-stage ring, 16 x 16 x 32 MFMAs): the wait and
+  // barrier for tile i + 1 sit between the two substeps of tile i, once this
+  // wave's fragment reads of tile i are complete.  The fragments of tile
+  // i + 1's first substep are then read, and the loads that reuse tile i's
+  // buffers issued, under the MFMAs of tile i's second substep, so no
+  // substep starts with a burst of LDS reads in front of an idle matrix pipe
+  // (with the barrier at the start of a step, all eight waves read their
+  // first fragments at once and wait for them).
+  // Registers: an A fragment is used by the TN MFMAs of one row of the wave
+  // tile, so the next substep's A fragment is read into the same registers
+  // right after that row's last MFMA; only the B fragments, used by every
+  // row, have two sets.
+  // Ring: A(t) in buffer 2t mod 5, B(t) in 2t + 1 mod 5; after the barrier of
+  // step i, B(i + 2) goes into A(i)'s buffer and A(i + 3) into B(i)'s.
+  // Same-box A/B against the barrier at the start of each step: forward
+  // products 2-5 % faster, input gradients 1-3 %; the weight gradients (both
+  // operands read transposed) need more registers for the second B set and
+  // spill (13-18 % slower), so they keep the start-of-step barrier.
+  constexpr bool MIDBAR = HALF && !F8 && MI == 16 &&
+                          (C::NT == 256 || !(AL == kMNCont && BL == kMNCont));
+  if constexpr (MIDBAR) {
+    auto step_mb = [&]<int S>(int i) {
+      constexpr int NSUB = PK / C::KSUB, NM = TM * TN;
+      static_assert(NSUB == 2, "two substeps per k-step");
+      static_assert(TN <= TN * TM && LOADS <= NM / 4, "reads and loads fit between MFMAs");
+      const bf16* as = sbuf.template operator()<(2 * S) % 5>();
+      const bf16* bs = sbuf.template operator()<(2 * S + 1) % 5>();
+      const bf16* as1 = sbuf.template operator()<(2 * S + 2) % 5>();
+      const bf16* bs1 = sbuf.template operator()<(2 * S + 3) % 5>();
+      bf16* nxt_b = sbuf.template operator()<(2 * S) % 5>();
+      bf16* nxt_a = sbuf.template operator()<(2 * S + 1) % 5>();
+      // one substep: MFMAs on (frA, frB[cur]); reads of the next substep's
+      // fragments (tile ta/tb, substep sub) into frA and frB[cur ^ 1]
+      auto substep = [&](int cur, const bf16* ta, const bf16* tb, int sub, auto&& after_mfma) {
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int t = 0; t < NM; ++t) {
+          const int ii = t / TN, j = t % TN;
+          acc[ii][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(frA[ii], frB[cur][j], acc[ii][j],
+                                                                0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          if (t < TN) {
+            frB[cur ^ 1][t] = frag<BN, BL, PK, MI>(tb, wn * WTN + t * MI, sub, lane);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if (j == TN - 1) {                         // row ii's last MFMA of this substep
+            frA[ii] = frag<BM, AL, PK, MI>(ta, wm * WTM + ii * MI, sub, lane);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          after_mfma(t);
+        }
+        __builtin_amdgcn_s_setprio(0);
+      };
+      substep(0, as, bs, 1, [](int) {});
+      // substep 1's fragments complete on every path (the compiler then
+      // places no wait for them among the reads issued after the barrier)
+#pragma unroll
+      for (int r = 0; r < TM; ++r) asm volatile("" : "+v"(frA[r]));
+#pragma unroll
+      for (int r = 0; r < TN; ++r) asm volatile("" : "+v"(frB[1][r]));
+      if (i + 1 < nk) {
+        // tile i + 1 has landed once at most the A loads of tile i + 2 remain
+        if (i + 2 < nk) wait_vmcnt<LOADS_A>();
+        else wait_vmcnt<0>();
+        asm volatile("s_barrier" ::: "memory");
+      }
+      const bool more_b = i + 2 < nk, more_a = i + 3 < nk;
+      const int kb = (kt0 + i + 2) * PK, ka = (kt0 + i + 3) * PK;
+      // (after the last step the reads below fetch an idle buffer, unused)
+      substep(1, as1, bs1, 0, [&](int t) {
+        if (t % 4 == 1 && t / 4 < LOADS) {
+          const int l = t / 4;
+          if (l < LOADS_B ? more_b : more_a) {
+            if (l < LOADS_B)
+              issue_one<BN, BL, LOADS_B, PK>(ob, n0, kb, nxt_b, wave, l);
+            else
+              issue_one<BM, AL, LOADS_A, PK>(oa, m0, ka, nxt_a, wave, l - LOADS_B);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      });
+    };
+    if (nk > 0) {
+      issue_tile<BM, AL, LOADS_A, PK>(oa, m0, kt0 * PK, st0, wave);
+      issue_tile<BN, BL, LOADS_B, PK>(ob, n0, kt0 * PK, st1, wave);
+      if (nk > 1) {
+        issue_tile<BM, AL, LOADS_A, PK>(oa, m0, (kt0 + 1) * PK, st2, wave);
+        wait_vmcnt<LOADS_A>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      asm volatile("s_barrier" ::: "memory");
+      if (nk > 1) issue_tile<BN, BL, LOADS_B, PK>(ob, n0, (kt0 + 1) * PK, st3, wave);
+      if (nk > 2) issue_tile<BM, AL, LOADS_A, PK>(oa, m0, (kt0 + 2) * PK, st4, wave);
+#pragma unroll
+      for (int r = 0; r < TM; ++r) frA[r] = frag<BM, AL, PK, MI>(st0, wm * WTM + r * MI, 0, lane);
+#pragma unroll
+      for (int r = 0; r < TN; ++r) frB[0][r] = frag<BN, BL, PK, MI>(st1, wn * WTN + r * MI, 0, lane);
+    }
+    for (int i = 0; i < nk; i += 5) {
+      step_mb.template operator()<0>(i);
+      if (i + 1 < nk) step_mb.template operator()<1>(i + 1);
+      if (i + 2 < nk) step_mb.template operator()<2>(i + 2);
+      if (i + 3 < nk) step_mb.template operator()<3>(i + 3);
+      if (i + 4 < nk) step_mb.template operator()<4>(i + 4);
+    }
+  } else if constexpr (HALF) {
     if (nk > 0) {
       issue_tile<BM, AL, LOADS_A, PK>(oa, m0, kt0 * PK, st0, wave);
       issue_tile<BN, BL, LOADS_B, PK>(ob, n0, kt0 * PK, st1, wave);
@@ -924,6 +1032,7 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
     if constexpr (STAGES == 4)
       if (nk > 2) issue(kt0 + 2, st2);
   }
+  if constexpr (!MIDBAR)
   for (int i = 0; i < nk; i += STAGES) {
     step.template operator()<0>(i);
     if (i + 1 < nk) step.template operator()<1>(i + 1);
@@ -940,7 +1049,8 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
   // region, then every lane takes 8 consecutive columns of one row, so that
   // C, the auxiliary tensors and the split-K workspace are accessed with
   // 16-byte, row-contiguous loads and stores.
-  static_assert(WTN == 64, "the epilogue maps 8 lanes to the 64 columns of a wave tile");
+  static_assert(WTN % 64 == 0, "the epilogue maps 8 lanes to 64 columns of a wave tile");
+  constexpr int NH = WTN / 64, TNH = TN / NH;          // 64-column halves of the wave tile
   if constexpr (F8) {
     if (p.scale_a) {                                   // tensorwise scales kept on the device
       const float inv = 1.f / (p.scale_a[1] * p.scale_b[1]);
@@ -977,6 +1087,8 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
     // VGPRs per lane and row block
     constexpr int NIB = WTM / 32, GI = epi_reads<EPI>() == 2 ? 2 : NIB;
 #pragma unroll
+    for (int hc = 0; hc < NH; ++hc)
+#pragma unroll
     for (int i0 = 0; i0 < NIB; i0 += GI) {
       EpiIn<EPI> in[GI][4];
       if constexpr (epi_reads<EPI>() > 0) {
@@ -985,7 +1097,7 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const int m = m0 + wm * WTM + (i0 + ii) * 32 + rsub + 8 * t;
-            const int n = n0 + wn * WTN + 8 * q;
+            const int n = n0 + wn * WTN + hc * 64 + 8 * q;
             if (m < p.M && vec && n + 8 <= p.N)
               epi_load8<EPI>(p, cb + (int64_t)m * ld_out + n, in[ii][t]);
           }
@@ -997,19 +1109,20 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
         // 16 x 16 tile: lane c + 16 g holds column c, rows 4 g + e
         if constexpr (MI == 32) {
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
+          for (int j = 0; j < TNH; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e)
-              stg[((e >> 2) * 8 + half * 4 + (e & 3)) * EP_LD + j * 32 + l32] = acc[i][j][e];
+              stg[((e >> 2) * 8 + half * 4 + (e & 3)) * EP_LD + j * 32 + l32] =
+                  acc[i][hc * TNH + j][e];
         } else {
 #pragma unroll
           for (int i2 = 0; i2 < 2; ++i2)
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
+            for (int j = 0; j < TNH; ++j)
 #pragma unroll
               for (int e = 0; e < 4; ++e)
                 stg[(i2 * 16 + 4 * (lane >> 4) + e) * EP_LD + j * 16 + (lane & 15)] =
-                    acc[2 * i + i2][j][e];
+                    acc[2 * i + i2][hc * TNH + j][e];
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -1017,7 +1130,7 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
           float v[8];
           ld8(stg + row * EP_LD + 8 * q, v);
           const int m = m0 + wm * WTM + i * 32 + row;
-          const int n = n0 + wn * WTN + 8 * q;
+          const int n = n0 + wn * WTN + hc * 64 + 8 * q;
           if (m >= p.M || n >= p.N) continue;
           if (split_out) {
             float* w = W + (int64_t)m * ld_out + n;
@@ -1063,12 +1176,12 @@ bool pipe_ok(const GemmParams& p) {
   return true;
 }
 
-template <int AL, int BL, int WM, int WN, int ST, int PK, int MI, bool F8 = false>
+template <int AL, int BL, int WM, int WN, int ST, int PK, int MI, bool F8 = false, int WTN = 64>
 hipError_t launch_pipe_cfg(const GemmParams& p, hipStream_t st) {
-  using C = Pipe<WM, WN, ST, PK, MI>;
+  using C = Pipe<WM, WN, ST, PK, MI, WTN>;
   const int tiles = ceil_div(p.M, C::BM) * ceil_div(p.N, C::BN);
   dim3 grid(tiles, 1, p.batch * p.splits);
-  gemm_bf16_pipe_kernel<AL, BL, WM, WN, ST, PK, MI, F8><<<grid, C::NT, 0, st>>>(p);
+  gemm_bf16_pipe_kernel<AL, BL, WM, WN, ST, PK, MI, F8, WTN><<<grid, C::NT, 0, st>>>(p);
   return hipGetLastError();
 }
 
