@@ -288,6 +288,120 @@ NC_DEV void attn_fwd_block(
 }
 
 
+// ====================================================== gradient stores
+// The QK-norm + rotary backward, folded into the stores of dQ and dK.  The
+// forward normalised each q/k head vector x to y = x r (r = (mean(x^2) +
+// eps)^-1/2) and rotated it, xr = R_t y, which is what attention read.  For
+// the gradient g at xr: dy = R_t^T g, y = R_t^T xr, and the gradient at x is
+// r (dy - y mean(dy y)) over the head's 128 dims.  rqk: [token, nh] values
+// of r for the nh = H + Hkv normalised heads; cs: cos | sin [T][64].
+struct QkNorm {
+  const float* rqk;   // null: store the gradient at xr as it is
+  const float* cs;
+  int nh;
+};
+
+// One wave's 32 rows x 128 dims of dQ, dK or dV from 32 x 32 MFMA
+// accumulators acc[db] (lane holds dim db*32 + l32 of rows 8(e/4) + 4 half +
+// e%4), times `scale`.  Row r is position row0 + r of its sequence and token
+// n0 + r; out_row / xr_row: element offsets of row 0 (head column 0) in out
+// and in the stored rotated vectors xr; hn: the head's index among the nh.
+// Sixteen rows at a time go through this wave's LDS region `stg` (16 x 132
+// floats) and come back as 8 consecutive dims (and their rotary partners 64
+// further) per lane, 8 lanes per row, so that xr, the rotary table and the
+// output move in 16-byte accesses, all issued before any of them is used.
+// The caller has made the region free (no wave still reads it).
+NC_DEV void attn_store_grad(const f32x16 (&acc)[4], float scale, bf16* __restrict__ out,
+                            int64_t ldd, int64_t out_row, const bf16* __restrict__ xr,
+                            int64_t ld, int64_t xr_row, int row0, int64_t n0, int T, int hn,
+                            const QkNorm& nq, float* stg, int lane) {
+  constexpr int SL = 132;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int u = lane & 7, rl = lane >> 3;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int e8 = 0; e8 < 8; ++e8) {
+        const int e = 8 * p + e8;
+        const int r = (e >> 2) * 8 + half * 4 + (e & 3) - 16 * p;
+        stg[r * SL + db * 32 + l32] = acc[db][e] * scale;
+      }
+    // (read back by the same wave: a wave's LDS operations complete in order)
+    float g1[2][8], g2[2][8];
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const float* sr = stg + (it * 8 + rl) * SL + 8 * u;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        g1[it][j] = sr[j];
+        g2[it][j] = sr[64 + j];
+      }
+    }
+    if (!nq.rqk) {
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const int row = 16 * p + it * 8 + rl;
+        bf16x8 h1, h2;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          h1[j] = (bf16)g1[it][j];
+          h2[j] = (bf16)g2[it][j];
+        }
+        bf16* o = out + out_row + row * ldd + 8 * u;
+        *reinterpret_cast<bf16x8*>(o) = h1;
+        *reinterpret_cast<bf16x8*>(o + 64) = h2;
+      }
+      continue;
+    }
+    bf16x8 x1[2], x2[2];
+    f32x4 c[2][2], sn[2][2];
+    float rs[2];
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int row = 16 * p + it * 8 + rl, t = row0 + row;
+      const bf16* xp = xr + xr_row + row * ld + 8 * u;
+      x1[it] = *reinterpret_cast<const bf16x8*>(xp);
+      x2[it] = *reinterpret_cast<const bf16x8*>(xp + 64);
+      const float* cp = nq.cs + t * 64 + 8 * u;
+      c[it][0] = *reinterpret_cast<const f32x4*>(cp);
+      c[it][1] = *reinterpret_cast<const f32x4*>(cp + 4);
+      sn[it][0] = *reinterpret_cast<const f32x4*>(cp + T * 64);
+      sn[it][1] = *reinterpret_cast<const f32x4*>(cp + T * 64 + 4);
+      rs[it] = nq.rqk[(n0 + row) * nq.nh + hn];
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      float y1[8], y2[8], dy1[8], dy2[8], dot = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float cj = c[it][j >> 2][j & 3], sj = sn[it][j >> 2][j & 3];
+        const float o1 = (float)x1[it][j], o2 = (float)x2[it][j];
+        y1[j] = o1 * cj + o2 * sj;
+        y2[j] = -o1 * sj + o2 * cj;
+        dy1[j] = g1[it][j] * cj + g2[it][j] * sj;
+        dy2[j] = -g1[it][j] * sj + g2[it][j] * cj;
+        dot += dy1[j] * y1[j] + dy2[j] * y2[j];
+      }
+      dot += __shfl_xor(dot, 1, 64);
+      dot += __shfl_xor(dot, 2, 64);
+      dot += __shfl_xor(dot, 4, 64);
+      const float mean = dot * (1.f / 128.f);
+      bf16x8 h1, h2;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        h1[j] = (bf16)(rs[it] * (dy1[j] - y1[j] * mean));
+        h2[j] = (bf16)(rs[it] * (dy2[j] - y2[j] * mean));
+      }
+      const int row = 16 * p + it * 8 + rl;
+      bf16* o = out + out_row + row * ldd + 8 * u;
+      *reinterpret_cast<bf16x8*>(o) = h1;
+      *reinterpret_cast<bf16x8*>(o + 64) = h2;
+    }
+  }
+}
+
 // ============================================================ dK / dV
 // A workgroup owns 128 keys (4 waves x 32; K and V rows of each wave's keys
 // stay in registers as the B operands) and walks the 64-query tiles from the
@@ -304,7 +418,7 @@ NC_DEV void attn_bwd_dkv_block(
     int64_t ld, const bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ lse,
     const float* __restrict__ Dv, bf16* __restrict__ dk, bf16* __restrict__ dv, int64_t ldd,
     int T, int H, int G, int win, float scale_log2, float scale, int kblk, int bhk, bf16* st0,
-    bf16* st1) {
+    bf16* st1, const QkNorm& nq) {
   constexpr int KT = 64 * 128;
   const int Hkv = kGrouped ? H / G : H;
   const int b = bhk / Hkv, hk = bhk % Hkv;
@@ -437,15 +551,13 @@ NC_DEV void attn_bwd_dkv_block(
   }
 
   // C[key][d]: lane holds column d = db*32 + l32, rows key = 8*(e/4) + 4*half + e%4
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int key = k0w + (e >> 2) * 8 + half * 4 + (e & 3);
-      const int64_t off = ((int64_t)b * T + key) * ldd + hk * 128 + db * 32 + l32;
-      dk[off] = (bf16)(dkacc[db][e] * scale);
-      dv[off] = (bf16)dvacc[db][e];
-    }
+  const int64_t row_out = ((int64_t)b * T + k0w) * ldd + hk * 128;
+  __syncthreads();                                 // every wave is done with the stages
+  float* stg = reinterpret_cast<float*>(wave < 2 ? st0 : st1) + (wave & 1) * 16 * 132;
+  attn_store_grad(dvacc, 1.f, dv, ldd, row_out, nullptr, 0, 0, k0w, 0, T, 0,
+                  QkNorm{nullptr, nullptr, 0}, stg, lane);
+  attn_store_grad(dkacc, scale, dk, ldd, row_out, k, ld, kvbase + (int64_t)k0w * ld, k0w,
+                  (int64_t)b * T + k0w, T, H + hk, nq, stg, lane);
 }
 
 // ================================================================== dQ
@@ -455,9 +567,10 @@ NC_DEV void attn_bwd_dkv_block(
 // one 128-query block qb of head bh; st0 / st1: K | V stages of 2 x 64 x 128
 NC_DEV void attn_bwd_dq_block(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    int64_t ld, const bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ lse,
-    const float* __restrict__ Dv, bf16* __restrict__ dq, int64_t ldd, int T, int H, int G,
-    int win, float scale_log2, float scale, int qb, int bh, bf16* st0, bf16* st1) {
+    int64_t ld, const bf16* __restrict__ o, const bf16* __restrict__ dO, int64_t ldo,
+    const float* __restrict__ lse, float* __restrict__ Dv, bf16* __restrict__ dq, int64_t ldd,
+    int T, int H, int G, int win, float scale_log2, float scale, int qb, int bh, bf16* st0,
+    bf16* st1, const QkNorm& nq) {
   constexpr int KT = 64 * 128;
   const int b = bh / H, h = bh % H;
   const int64_t base = (int64_t)b * T * ld + h * 128;
@@ -478,7 +591,20 @@ NC_DEV void attn_bwd_dq_block(
     df[s] = *reinterpret_cast<const bf16x8*>(dO + obase + (int64_t)myq * ldo + s * 16 + half * 8);
   }
   float lse2 = lse[((int64_t)b * H + h) * T + myq] * kLog2e;
-  float Dq = Dv[((int64_t)b * H + h) * T + myq];
+  // D = rowsum(dO * O) of this lane's query, from its half of the row (the
+  // dO layout) and the other half's (lane ^ 32); written for the dK/dV kernel
+  float Dq;
+  {
+    float part = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const bf16x8 of = *reinterpret_cast<const bf16x8*>(o + obase + (int64_t)myq * ldo + s * 16 + half * 8);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) part += (float)df[s][j] * (float)of[j];
+    }
+    Dq = part + __shfl_xor(part, 32, 64);
+    if (half == 0) Dv[((int64_t)b * H + h) * T + myq] = Dq;
+  }
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     settle(qf[s]);
@@ -553,13 +679,10 @@ NC_DEV void attn_bwd_dq_block(
     if (kv + 1 < n_kv) step(kv + 1, st1, st0);
   }
 
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int qq = q0w + (e >> 2) * 8 + half * 4 + (e & 3);
-      dq[((int64_t)b * T + qq) * ldd + h * 128 + db * 32 + l32] = (bf16)(dqacc[db][e] * scale);
-    }
+  __syncthreads();                                 // every wave is done with the stages
+  float* stg = reinterpret_cast<float*>(wave < 2 ? st0 : st1) + (wave & 1) * 16 * 132;
+  attn_store_grad(dqacc, scale, dq, ldd, ((int64_t)b * T + q0w) * ldd + h * 128, q, ld,
+                  base + (int64_t)q0w * ld, q0w, (int64_t)b * T + q0w, T, h, nq, stg, lane);
 }
 
 // Workgroup -> (b*H + h, 128-row blocks).
@@ -619,34 +742,34 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, const bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ lse,
     const float* __restrict__ Dv, bf16* __restrict__ dk, bf16* __restrict__ dv, int64_t ldd,
-    int T, int H, int G, int win, float scale_log2, float scale) {
+    int T, int H, int G, int win, float scale_log2, float scale, QkNorm nq) {
   __shared__ __attribute__((aligned(1024))) bf16 st0[kDkvStage];
   __shared__ __attribute__((aligned(1024))) bf16 st1[kDkvStage];
   // key block kblk walks up to T/64 - 2 kblk query tiles: the low blocks are the long ones
   const BlockJob jb = block_job(T / 128, win >= T, false);
   if (jb.second >= 0) {
     attn_bwd_dkv_block<kGrouped>(q, k, v, ld, dO, ldo, lse, Dv, dk, dv, ldd, T, H, G, win,
-                                 scale_log2, scale, jb.second, jb.bh, st0, st1);
+                                 scale_log2, scale, jb.second, jb.bh, st0, st1, nq);
     __syncthreads();
   }
   attn_bwd_dkv_block<kGrouped>(q, k, v, ld, dO, ldo, lse, Dv, dk, dv, ldd, T, H, G, win,
-                               scale_log2, scale, jb.first, jb.bh, st0, st1);
+                               scale_log2, scale, jb.first, jb.bh, st0, st1, nq);
 }
 
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    int64_t ld, const bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ lse,
-    const float* __restrict__ Dv, bf16* __restrict__ dq, int64_t ldd, int T, int H, int G,
-    int win, float scale_log2, float scale) {
+    int64_t ld, const bf16* __restrict__ o, const bf16* __restrict__ dO, int64_t ldo,
+    const float* __restrict__ lse, float* __restrict__ Dv, bf16* __restrict__ dq, int64_t ldd,
+    int T, int H, int G, int win, float scale_log2, float scale, QkNorm nq) {
   __shared__ __attribute__((aligned(1024))) bf16 st0[2 * 64 * 128];   // K | V
   __shared__ __attribute__((aligned(1024))) bf16 st1[2 * 64 * 128];
   const BlockJob jb = block_job(T / 128, win >= T, true);
-  attn_bwd_dq_block(q, k, v, ld, dO, ldo, lse, Dv, dq, ldd, T, H, G, win, scale_log2, scale,
-                    jb.first, jb.bh, st0, st1);
+  attn_bwd_dq_block(q, k, v, ld, o, dO, ldo, lse, Dv, dq, ldd, T, H, G, win, scale_log2, scale,
+                    jb.first, jb.bh, st0, st1, nq);
   if (jb.second < 0) return;
   __syncthreads();
-  attn_bwd_dq_block(q, k, v, ld, dO, ldo, lse, Dv, dq, ldd, T, H, G, win, scale_log2, scale,
-                    jb.second, jb.bh, st0, st1);
+  attn_bwd_dq_block(q, k, v, ld, o, dO, ldo, lse, Dv, dq, ldd, T, H, G, win, scale_log2, scale,
+                    jb.second, jb.bh, st0, st1, nq);
 }
 
 // ========================================================== fp32 path
@@ -777,9 +900,9 @@ hipError_t nc_attn_fwd(int dtype, const void* q, const void* k, const void* v, i
 }
 
 hipError_t nc_attn_bwd(int dtype, const void* q, const void* k, const void* v, int64_t ld,
-                       const void* dO, int64_t ldo, const float* lse, const float* D, void* dq,
-                       void* dk, void* dv, int64_t ldd, int B, int T, int H, int Hkv, int window,
-                       hipStream_t st) {
+                       const void* o, const void* dO, int64_t ldo, const float* lse, float* D,
+                       void* dq, void* dk, void* dv, int64_t ldd, int B, int T, int H, int Hkv,
+                       int window, const float* rqk, const float* cos_sin, hipStream_t st) {
   const float scale = 1.0f / sqrtf(128.f);
   const int win = window < 0 || window > T ? T : window;
   if (Hkv < 1 || H % Hkv) return hipErrorInvalidValue;
@@ -787,14 +910,19 @@ hipError_t nc_attn_bwd(int dtype, const void* q, const void* k, const void* v, i
   if (dtype) {
     if (T % 128) return hipErrorInvalidValue;
     const int jobs = attn_jobs_per_head(T, win);
+    const QkNorm nq{rqk, cos_sin, H + Hkv};
+    // dQ first: it also forms D = rowsum(dO * O), which the dK/dV kernel reads
+    attn_bwd_dq_kernel<<<B * H * jobs, 256, 0, st>>>(
+        (const bf16*)q, (const bf16*)k, (const bf16*)v, ld, (const bf16*)o, (const bf16*)dO,
+        ldo, lse, D, (bf16*)dq, ldd, T, H, G, win, scale * kLog2e, scale, nq);
     auto dkv_kernel = G > 1 ? attn_bwd_dkv_kernel<true> : attn_bwd_dkv_kernel<false>;
     dkv_kernel<<<B * Hkv * jobs, 256, 0, st>>>(
         (const bf16*)q, (const bf16*)k, (const bf16*)v, ld, (const bf16*)dO, ldo, lse, D,
-        (bf16*)dk, (bf16*)dv, ldd, T, H, G, win, scale * kLog2e, scale);
-    attn_bwd_dq_kernel<<<B * H * jobs, 256, 0, st>>>(
-        (const bf16*)q, (const bf16*)k, (const bf16*)v, ld, (const bf16*)dO, ldo, lse, D,
-        (bf16*)dq, ldd, T, H, G, win, scale * kLog2e, scale);
+        (bf16*)dk, (bf16*)dv, ldd, T, H, G, win, scale * kLog2e, scale, nq);
   } else {
+    if (rqk) return hipErrorInvalidValue;     // fp32: separate D and QK-norm kernels
+    hipError_t e = nc_attn_bwd_pre(0, o, dO, ldo, D, B, T, H, st);
+    if (e != hipSuccess) return e;
     attn_bwd_dq_f32_kernel<<<ceil_div(B * H * T, 4), 256, 0, st>>>(
         (const float*)q, (const float*)k, (const float*)v, ld, (const float*)dO, ldo, lse, D,
         (float*)dq, ldd, B, T, H, G, win, scale);

@@ -39,10 +39,16 @@ hipError_t nc_attn_fwd(int dtype, const void* q, const void* k, const void* v, i
 // D[b,h,t] = sum_d dO*O
 hipError_t nc_attn_bwd_pre(int dtype, const void* o, const void* dO, int64_t ld_o, float* D,
                            int B, int T, int H, hipStream_t st);
+// Writes D = rowsum(dO*O) ([B, H, T]) and dq, dk, dv.  With rqk and cos_sin
+// (bf16 only) the QK-norm + rotary backward is applied to dq and dk on their
+// way out (rqk [B*T, H + Hkv] reciprocal RMS of the forward's q/k heads,
+// cos_sin the rotary table [2][T][64]): the gradients are then those at the
+// un-normalised q and k.
 hipError_t nc_attn_bwd(int dtype, const void* q, const void* k, const void* v, int64_t ld_qkv,
-                       const void* dO, int64_t ld_o, const float* lse, const float* D,
+                       const void* o, const void* dO, int64_t ld_o, const float* lse, float* D,
                        void* dq, void* dk, void* dv, int64_t ld_dqkv, int B, int T, int H,
-                       int Hkv, int window, hipStream_t st);
+                       int Hkv, int window, const float* rqk, const float* cos_sin,
+                       hipStream_t st);
 
 // ---- fp8 e4m3 with one scale per tensor: amax_scale[0] = max |x|, amax_scale[1] =
 // 448 / amax (1 if amax = 0), q[i] = e4m3(x[i] * scale) (round to nearest even,

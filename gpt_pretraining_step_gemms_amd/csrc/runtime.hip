@@ -645,13 +645,15 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
                 N, d, d, kEpiStore), "dO");
     NC_GEMM(gemm(ctx, dxT, d, kMNCont, aa + la.o, d, kMNCont, G + wb + oWo, d, d, d, N,
                 kEpiAccF32, nullptr, nullptr, ctx->splits_o), "dWo");
-    NC_TRY(nc_attn_bwd_pre(dt, aa + la.o, aa + ctx->dO, d, A<float>(ctx, ctx->Dbuf), B, T, H, st),
-           "attn D");
-    NC_TRY(nc_attn_bwd(dt, qkv, qkv + d * es, qkv + (d + dk) * es, Wd, aa + ctx->dO, d,
+    // bf16: D and the QK-norm + rotary backward are formed inside the attention
+    // backward kernels; fp32: separate kernels
+    NC_TRY(nc_attn_bwd(dt, qkv, qkv + d * es, qkv + (d + dk) * es, Wd, aa + la.o, aa + ctx->dO, d,
                        A<float>(ctx, la.lse), A<float>(ctx, ctx->Dbuf), dqkv, dqkv + d * es,
-                       dqkv + (d + dk) * es, Wd, B, T, H, Hkv, ctx->windows[l], st), "attn bwd");
-    NC_TRY(nc_qk_norm_rope_bwd(dt, dqkv, qkv, A<float>(ctx, la.rqk), tab, N, T, H, Hkv, st),
-           "qknorm bwd");
+                       dqkv + (d + dk) * es, Wd, B, T, H, Hkv, ctx->windows[l],
+                       dt ? A<float>(ctx, la.rqk) : nullptr, dt ? tab : nullptr, st), "attn bwd");
+    if (!dt)
+      NC_TRY(nc_qk_norm_rope_bwd(dt, dqkv, qkv, A<float>(ctx, la.rqk), tab, N, T, H, Hkv, st),
+             "qknorm bwd");
     NC_GEMM(gemm(ctx, dqkv, Wd, kMNCont, aa + la.a1, d, kMNCont, G + wb, d, Wd, d, N,
                 kEpiAccF32, nullptr, nullptr, ctx->splits_qkv), "dWqkv");
     NC_GEMM(gemm(ctx, dqkv, Wd, kKCont, wptr(ctx, wb), d, kMNCont, da, d, N, d, Wd,
@@ -1152,10 +1154,8 @@ nc_status nc_op_attention_bwd(int32_t dtype, const void* q, size_t q_bytes, cons
   if (dtype == NC_BF16 && (T % 128 || ld_qkv % 8 || ld_o % 8 || ld_d % 8)) return NC_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int dt = dtype == NC_BF16;
-  if (nc_attn_bwd_pre(dt, o, dO, ld_o, D, B, T, H, st) != hipSuccess) return NC_ERR_HIP;
-  return nc_attn_bwd(dt, q, k, v, ld_qkv, dO, ld_o, lse, D, dq, dk, dv, ld_d, B, T, H, n_kv_head,
-                     window, st) ==
-                 hipSuccess
+  return nc_attn_bwd(dt, q, k, v, ld_qkv, o, dO, ld_o, lse, D, dq, dk, dv, ld_d, B, T, H,
+                     n_kv_head, window, nullptr, nullptr, st) == hipSuccess
              ? NC_OK
              : NC_ERR_HIP;
 }
