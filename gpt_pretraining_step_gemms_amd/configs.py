@@ -42,6 +42,11 @@ class ModelConfig:
     init_std: float = 0.02
     n_kv_head: int = 0    # key/value heads for grouped-query attention (0: n_head)
     fp8_forward: bool = False   # forward block products in fp8 e4m3, tensorwise scales
+    # the pages' further model mechanisms (off in the benchmark configurations)
+    value_embeds: bool = False  # gated value embeddings on every other layer
+    resid_lambdas: bool = False # per-layer scaling of the stream and of the embedding output
+    smear: bool = False         # gated mix-in of the previous token's embedding
+    backout: bool = False       # subtract the mid-depth stream after the last layer
 
     @property
     def kv_heads(self):
@@ -51,7 +56,9 @@ class ModelConfig:
         return dict(n_layer=self.n_layer, d_model=self.d_model, n_head=self.n_head,
                     head_dim=self.head_dim, d_ff=self.d_ff, vocab=self.vocab,
                     seq_len=self.seq_len, rope_base=self.rope_base, norm_eps=self.norm_eps,
-                    n_kv_head=self.kv_heads, fp8_forward=self.fp8_forward)
+                    n_kv_head=self.kv_heads, fp8_forward=self.fp8_forward,
+                    value_embeds=self.value_embeds, resid_lambdas=self.resid_lambdas,
+                    smear=self.smear, backout=self.backout)
 
     @property
     def tokens_per_step(self):
@@ -73,6 +80,7 @@ class OptimConfig:
     ns_coeffs: tuple = tuple(NS_POLAR_EXPRESS)
     adam_lr_embed: float = 3e-3
     adam_lr_head: float = 3e-3
+    adam_lr_scalar: float = 3e-3        # scalar parameters (residual, smear, backout lambdas)
     adam_beta1: float = 0.9
     adam_beta2: float = 0.95
     adam_eps: float = 1e-8

@@ -53,6 +53,28 @@ Readings where the pages are silent:
   backward treats the rounding as the identity (gradients with the
   unrounded operands).  The lm_head and every backward product are exact.
 * Loss: natural log, mean over every position, no ignore index.
+
+The rest of the pages' model ([APIDOG] "1. Model GPT (nanochat/gpt.py)",
+the "Value Embeddings (ResFormer)" and efficiency-trick listings), each
+switched on by a cfg flag; readings where the listings leave a step open:
+
+* value embeddings (cfg["value_embeds"]): "alternating layers" carry a
+  learnable table VE_l [V, n_kv_head * hd] looked up by the input token ids,
+  added to v through a per-(token, key/value head) gate
+  g = 3 sigmoid(a[:, :C] Wg_l^T), Wg_l [n_kv_head, C] bias-free, where a is
+  the attention block's (normalised) input.  Readings: the layers are every
+  other one counted down from the last (l = L-1, L-3, ...); C = 32
+  (cfg["ve_gate_channels"]); the mix happens before attention, v has no
+  QK-norm or rotation.
+* residual scaling (cfg["resid_lambdas"]): at the start of layer i the
+  stream becomes resid_lambdas[i] x + x0_lambdas[i] x0, x0 being the
+  embedding output (after smear).  Parameters [1, L] each.
+* smear (cfg["smear"]): after the embedding, x_t = e_t + lam_s
+  sigmoid(e_t[:24] Ws^T) e_{t-1}, e_t = E[tok_t] and e_{-1} = 0 (the
+  previous token of the same row; Ws [1, 24] bias-free, lam_s [1, 1]).
+* backout (cfg["backout"]): after the last layer x <- x - lam_b xb, where
+  xb is the stream entering layer L // 2 (before its residual scaling);
+  lam_b [1, 1] (the final stream itself when L // 2 == L).
 """
 
 import numpy as np
@@ -154,16 +176,67 @@ def n_kv_heads(cfg):
     return cfg.get("n_kv_head") or cfg["n_head"]
 
 
+SMEAR_CHANNELS = 24
+
+
+def ve_layers(cfg):
+    """Layers carrying a value embedding: every other one down from the last."""
+    if not cfg.get("value_embeds"):
+        return []
+    L = cfg["n_layer"]
+    return [l for l in range(L) if (L - 1 - l) % 2 == 0]
+
+
+def ve_gate_channels(cfg):
+    return cfg.get("ve_gate_channels", 32)
+
+
+def backout_layer(cfg):
+    return cfg["n_layer"] // 2
+
+
 def param_shapes(cfg):
     """Name -> shape of every parameter ([out, in] like a bias-free Linear)."""
     d, F, V = cfg["d_model"], cfg["d_ff"], cfg["vocab"]
     dk = n_kv_heads(cfg) * cfg["head_dim"]
+    L = cfg["n_layer"]
     shapes = {"E": (V, d)}
-    for i in range(cfg["n_layer"]):
+    for i in range(L):
         for n, s in zip(_layer_names(i), [(d, d), (dk, d), (dk, d), (d, d), (F, d), (d, F)]):
             shapes[n] = s
     shapes["Wh"] = (V, d)
+    for l in ve_layers(cfg):
+        shapes[f"ve.{l}"] = (V, dk)
+        shapes[f"{l}.Wg"] = (n_kv_heads(cfg), ve_gate_channels(cfg))
+    if cfg.get("resid_lambdas"):
+        shapes["resid_lambdas"] = (1, L)
+        shapes["x0_lambdas"] = (1, L)
+    if cfg.get("smear"):
+        shapes["smear_gate"] = (1, SMEAR_CHANNELS)
+        shapes["smear_lambda"] = (1, 1)
+    if cfg.get("backout"):
+        shapes["backout_lambda"] = (1, 1)
     return shapes
+
+
+def identity_values(cfg):
+    """Values of the scalar parameters at which residual scaling, smear and
+    backout leave the plain model unchanged (resid 1, x0 0, smear 0,
+    backout 0)."""
+    out = {}
+    L = cfg["n_layer"]
+    if cfg.get("resid_lambdas"):
+        out["resid_lambdas"] = np.ones((1, L))
+        out["x0_lambdas"] = np.zeros((1, L))
+    if cfg.get("smear"):
+        out["smear_lambda"] = np.zeros((1, 1))
+    if cfg.get("backout"):
+        out["backout_lambda"] = np.zeros((1, 1))
+    return out
+
+
+def _sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-z))
 
 
 # --------------------------------------------------------------------------
@@ -231,11 +304,32 @@ def forward(params, tokens, targets, cfg, keep_cache=True):
     cos, sin = rope_tables(T, hd, cfg["rope_base"])
     P = {k: np.asarray(v, F64) for k, v in params.items()}
 
-    x = P["E"][tokens]                                  # [B,T,d]
+    L = cfg["n_layer"]
+    xe = P["E"][tokens]                                 # [B,T,d]
+    x = xe
+    smear = None
+    if cfg.get("smear"):
+        prev = np.zeros_like(xe)
+        prev[:, 1:] = xe[:, :-1]
+        ss = _sigmoid(xe[..., :SMEAR_CHANNELS] @ P["smear_gate"].T)      # [B,T,1]
+        gs = P["smear_lambda"][0, 0] * ss
+        x = xe + gs * prev
+        smear = dict(prev=prev, ss=ss, gs=gs)
+    x0 = x
+    resid = cfg.get("resid_lambdas")
+    Lb = backout_layer(cfg) if cfg.get("backout") else None
+    xb = None
+    vls = set(ve_layers(cfg))
+    Cg = ve_gate_channels(cfg)
     windows = layer_windows(cfg)
     layers = []
-    for i in range(cfg["n_layer"]):
+    for i in range(L):
         Wq, Wk, Wv, Wo, W1, W2 = (P[n] for n in _layer_names(i))
+        x_prev = x
+        if i == Lb:
+            xb = x
+        if resid:
+            x = P["resid_lambdas"][0, i] * x + P["x0_lambdas"][0, i] * x0
         a, r1 = rmsnorm(x, eps)
         if cfg.get("fp8_forward"):             # the fused QKV weight is one tensor
             qkv = _fp8_linear(a, np.concatenate([Wq, Wk, Wv], axis=0))
@@ -243,6 +337,13 @@ def forward(params, tokens, targets, cfg, keep_cache=True):
             q_, k_, v_ = qkv[..., :dq_], qkv[..., dq_:dq_ + dk_], qkv[..., dq_ + dk_:]
         else:
             q_, k_, v_ = a @ Wq.T, a @ Wk.T, a @ Wv.T
+        ve_cache = None
+        if i in vls:                                     # value embedding, gated per head
+            ve = _split_heads(P[f"ve.{i}"][tokens], Hkv)                   # [B,Hkv,T,hd]
+            sg = _sigmoid(a[..., :Cg] @ P[f"{i}.Wg"].T)                     # [B,T,Hkv]
+            gg = 3.0 * sg.transpose(0, 2, 1)[..., None]                     # [B,Hkv,T,1]
+            v_ = v_ + _merge_heads(gg * ve)
+            ve_cache = dict(ve=ve, sg=sg)
         q = _split_heads(q_, H)
         k = _split_heads(k_, Hkv)
         v = _split_heads(v_, Hkv)
@@ -259,7 +360,12 @@ def forward(params, tokens, targets, cfg, keep_cache=True):
         x = x + _linear(g, W2, cfg)
         if keep_cache:
             layers.append(dict(a=a, r1=r1, qn=qn, rq=rq, kn=kn, rk=rk,
-                               qr=qr, kr=kr, v=v, o=o, m=m, r2=r2, h=h, g=g))
+                               qr=qr, kr=kr, v=v, o=o, m=m, r2=r2, h=h, g=g,
+                               x_prev=x_prev, ve=ve_cache))
+    if Lb is not None:
+        if xb is None:                                   # L // 2 == L: the final stream
+            xb = x
+        x = x - P["backout_lambda"][0, 0] * xb
     xf, rf = rmsnorm(x, eps)
     z = xf @ P["Wh"].T                                  # [B,T,V]
     zmax = np.max(z, axis=-1, keepdims=True)
@@ -269,7 +375,8 @@ def forward(params, tokens, targets, cfg, keep_cache=True):
     cache = None
     if keep_cache:
         cache = dict(P=P, tokens=tokens, targets=np.asarray(targets), cos=cos, sin=sin,
-                     layers=layers, xf=xf, rf=rf, z=z, lse=lse)
+                     layers=layers, xf=xf, rf=rf, z=z, lse=lse, xe=xe, x0=x0, xb=xb,
+                     smear=smear)
     return loss, cache
 
 
@@ -304,8 +411,22 @@ def loss_and_grads(params, tokens, targets, cfg, grad_scale=1.0):
     grads["Wh"] = _sum_outer(dz, c["xf"])
     dxf = dz @ P["Wh"]
     dx = rmsnorm_backward(dxf, c["xf"], c["rf"])
+    nL = cfg["n_layer"]
+    Lb = backout_layer(cfg) if cfg.get("backout") else None
+    dxb = None
+    if Lb is not None:                      # x_final = x - lam_b xb
+        grads["backout_lambda"] = np.array([[-np.sum(dx * c["xb"])]])
+        dxb = -P["backout_lambda"][0, 0] * dx
+        if Lb >= nL:
+            dx = dx + dxb
+    resid = cfg.get("resid_lambdas")
+    if resid:
+        grads["resid_lambdas"] = np.zeros((1, nL))
+        grads["x0_lambdas"] = np.zeros((1, nL))
+    dx0 = np.zeros_like(dx)
+    Cg = ve_gate_channels(cfg)
 
-    for i in reversed(range(cfg["n_layer"])):
+    for i in reversed(range(nL)):
         L = c["layers"][i]
         nWq, nWk, nWv, nWo, nW1, nW2 = _layer_names(i)
         # MLP: x += max(h,0)^2 W2^T, h = m W1^T, m = N(x)
@@ -321,6 +442,18 @@ def loss_and_grads(params, tokens, targets, cfg, grad_scale=1.0):
         dqr, dkr, dv = causal_attention_backward(L["qr"], _repeat_kv(L["kr"], group),
                                                  _repeat_kv(L["v"], group), do, windows[i])
         dkr, dv = _sum_groups(dkr, group), _sum_groups(dv, group)
+        da_gate = None
+        if L["ve"] is not None:             # v += 3 sigmoid(a[:, :Cg] Wg^T) ve, per head
+            ve, sg = L["ve"]["ve"], L["ve"]["sg"]
+            gg = 3.0 * sg.transpose(0, 2, 1)[..., None]                     # [B,Hkv,T,1]
+            dve = _merge_heads(gg * dv)                                     # [B,T,dk]
+            dVE = np.zeros_like(P[f"ve.{i}"])
+            np.add.at(dVE, c["tokens"].reshape(-1), dve.reshape(n_tok, -1))
+            grads[f"ve.{i}"] = dVE
+            dgg = np.sum(dv * ve, axis=-1).transpose(0, 2, 1)               # [B,T,Hkv]
+            dzg = dgg * 3.0 * sg * (1.0 - sg)
+            grads[f"{i}.Wg"] = _sum_outer(dzg, L["a"][..., :Cg])
+            da_gate = dzg @ P[f"{i}.Wg"]                                    # [B,T,Cg]
         dq = rmsnorm_backward(rope_inverse(dqr, cos, sin), L["qn"], L["rq"])
         dk = rmsnorm_backward(rope_inverse(dkr, cos, sin), L["kn"], L["rk"])
         dq, dk, dv = _merge_heads(dq), _merge_heads(dk), _merge_heads(dv)
@@ -328,8 +461,28 @@ def loss_and_grads(params, tokens, targets, cfg, grad_scale=1.0):
         grads[nWk] = _sum_outer(dk, L["a"])
         grads[nWv] = _sum_outer(dv, L["a"])
         da = dq @ P[nWq] + dk @ P[nWk] + dv @ P[nWv]
+        if da_gate is not None:
+            da[..., :Cg] += da_gate
         dx = dx + rmsnorm_backward(da, L["a"], L["r1"])
+        if resid:                           # x_in = resid_i x_prev + x0_i x0
+            grads["resid_lambdas"][0, i] = np.sum(dx * L["x_prev"])
+            grads["x0_lambdas"][0, i] = np.sum(dx * c["x0"])
+            dx0 += P["x0_lambdas"][0, i] * dx
+            dx = P["resid_lambdas"][0, i] * dx
+        if i == Lb:                         # xb is the stream entering this layer
+            dx = dx + dxb
 
+    dx = dx + dx0                           # gradient at x0 (the smeared embedding)
+    if cfg.get("smear"):                    # x0_t = e_t + lam_s sigmoid(e_t[:24] Ws^T) e_{t-1}
+        sm = c["smear"]
+        gamma = np.sum(dx * sm["prev"], axis=-1, keepdims=True)            # [B,T,1]
+        grads["smear_lambda"] = np.array([[np.sum(gamma * sm["ss"])]])
+        dzs = gamma * P["smear_lambda"][0, 0] * sm["ss"] * (1.0 - sm["ss"])
+        grads["smear_gate"] = _sum_outer(dzs, c["xe"][..., :SMEAR_CHANNELS])
+        dxe = dx.copy()
+        dxe[:, :-1] += sm["gs"][:, 1:] * dx[:, 1:]
+        dxe[..., :SMEAR_CHANNELS] += dzs * P["smear_gate"]
+        dx = dxe
     dE = np.zeros_like(P["E"])
     np.add.at(dE, c["tokens"].reshape(-1), dx.reshape(n_tok, -1))
     grads["E"] = dE

@@ -3,9 +3,11 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 Parameter groups follow [DEVTO] "2. ตัวปรับปรุง Muon" (table of optimizer per
-parameter type): the token embedding E and the lm_head Wh take AdamW; every
-2-D block matrix (Wq, Wk, Wv, Wo, W1, W2 of every layer, each one on its own)
-takes Muon.  The model has no scalar parameters.
+parameter type): embeddings (the token embedding E and the value-embedding
+tables ve.<l>) and the lm_head Wh take AdamW, and so do the scalar
+parameters (resid_lambdas, x0_lambdas, smear_lambda, backout_lambda, at
+adam_lr_scalar); every 2-D matrix -- Wq, Wk, Wv, Wo, W1, W2 of every layer
+and the gates <l>.Wg and smear_gate, each one on its own -- takes Muon.
 
 Readings where the pages are silent:
 
@@ -108,6 +110,9 @@ def muon_normuon_step(W, G, M, v2, lr, coeffs, beta2, momentum=0.95, eps=1e-7, w
     return W * (1.0 - lr * wd) - upd, M, v2
 
 
+ADAMW_SCALARS = ("resid_lambdas", "x0_lambdas", "smear_lambda", "backout_lambda")
+
+
 def train_step(params, grads, state, step, hp):
     """Apply one optimizer step to every parameter.
 
@@ -122,9 +127,12 @@ def train_step(params, grads, state, step, hp):
     new_p, new_s = {}, {}
     for name, W in params.items():
         G = grads[name]
-        if name in ("E", "Wh"):
+        if name in ADAMW_SCALARS or name in ("E", "Wh") or name.startswith("ve."):
             st = state.get(name) or {"m": np.zeros_like(W, F64), "v": np.zeros_like(W, F64)}
-            lr = hp["adam_lr_embed"] if name == "E" else hp["adam_lr_head"]
+            if name in ADAMW_SCALARS:
+                lr = hp["adam_lr_scalar"]
+            else:
+                lr = hp["adam_lr_head"] if name == "Wh" else hp["adam_lr_embed"]
             p, m, v = adamw_step(W, G, st["m"], st["v"], step, lr, hp["adam_beta1"],
                                  hp["adam_beta2"], hp["adam_eps"], hp["adam_wd"])
             new_p[name], new_s[name] = p, {"m": m, "v": v}
