@@ -42,6 +42,9 @@ def parse():
                     help="key/value heads for grouped-query attention (default: one per head)")
     ap.add_argument("--fp8-forward", action="store_true",
                     help="forward block products in fp8 e4m3 (tensorwise scales; backward bf16)")
+    ap.add_argument("--model-features", default="",
+                    help='comma list of the further model mechanisms: ve (value embeddings), '
+                         'resid (residual/x0 lambdas), smear, backout; or "all"')
     ap.add_argument("--normuon", action="store_true",
                     help="NorMuon per-neuron normalisation after Newton-Schulz")
     ap.add_argument("--short-window", type=int, default=None,
@@ -167,6 +170,13 @@ def _cpu_model():
     return "unknown"
 
 
+def feature_text(cfg):
+    names = [n for on, n in ((cfg.value_embeds, "value embeddings on every second layer"),
+                             (cfg.resid_lambdas, "residual/x0 lambdas"),
+                             (cfg.smear, "smear"), (cfg.backout, "backout")) if on]
+    return (", " + ", ".join(names)) if names else ""
+
+
 def cpu_baseline(cfg, windows=None, ocfg=None):
     """The fp64 numpy oracle on a bounded sample of the same workload:
       * forward + backward of one 2048-token row of the model;
@@ -246,6 +256,15 @@ def main():
         cfg = dc_replace(cfg, n_kv_head=args.kv_heads)
     if args.fp8_forward:
         cfg = dc_replace(cfg, fp8_forward=True)
+    feats = {f.strip() for f in args.model_features.split(",") if f.strip()}
+    if "all" in feats:
+        feats = {"ve", "resid", "smear", "backout"}
+    unknown = feats - {"ve", "resid", "smear", "backout"}
+    if unknown:
+        print(f"bench.py: unknown --model-features {sorted(unknown)}", file=sys.stderr)
+        sys.exit(2)
+    cfg = dc_replace(cfg, value_embeds="ve" in feats, resid_lambdas="resid" in feats,
+                     smear="smear" in feats, backout="backout" in feats)
     if args.roofline_fp8:
         print(json.dumps({"roofline_fp8": roofline_gemm_fp8(cfg, args.roofline_iters)}))
         return
@@ -338,6 +357,7 @@ def main():
                                f"{cfg.n_head}x128 heads"
                                f"{f' over {cfg.kv_heads} key/value heads' if cfg.kv_heads != cfg.n_head else ''}"
                                f"{', forward block products in fp8 e4m3' if cfg.fp8_forward else ''}"
+                               f"{feature_text(cfg)}"
                                f", {attention}, MLP {cfg.d_ff} ReLU^2, "
                                f"vocab {cfg.vocab}, "
                                f"seq {cfg.seq_len}, micro-batch {cfg.micro_batch} x {K} accumulated "

@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libncgpt.so")
-SOURCES = ["gemm.hip", "attention.hip", "elementwise.hip", "runtime.hip"]
+SOURCES = ["gemm.hip", "attention.hip", "elementwise.hip", "extras.hip", "runtime.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -47,6 +47,7 @@ class ModelConfig:
     resid_lambdas: bool = False # per-layer scaling of the stream and of the embedding output
     smear: bool = False         # gated mix-in of the previous token's embedding
     backout: bool = False       # subtract the mid-depth stream after the last layer
+    ve_gate_channels: int = 32  # leading channels of the block input that drive a value gate
 
     @property
     def kv_heads(self):
@@ -58,7 +59,8 @@ class ModelConfig:
                     seq_len=self.seq_len, rope_base=self.rope_base, norm_eps=self.norm_eps,
                     n_kv_head=self.kv_heads, fp8_forward=self.fp8_forward,
                     value_embeds=self.value_embeds, resid_lambdas=self.resid_lambdas,
-                    smear=self.smear, backout=self.backout)
+                    smear=self.smear, backout=self.backout,
+                    ve_gate_channels=self.ve_gate_channels)
 
     @property
     def tokens_per_step(self):

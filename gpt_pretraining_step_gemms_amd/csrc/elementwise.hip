@@ -880,35 +880,57 @@ size_t nc_embed_bwd_scratch_bytes(int n_tok, int vocab, int d) {
   return b + 256;
 }
 
-hipError_t nc_embed_bwd(const int32_t* tok, const float* dx, float* dE, int n_tok, int V, int d,
-                        void* scratch, hipStream_t st) {
-  if (n_tok <= 0) return hipSuccess;
+namespace {
+struct EmbSort { int32_t *counts, *total, *start, *sorted; float* partial; };
+EmbSort emb_sort_layout(void* scratch, int n_tok, int V) {
   const int G = ceil_div(n_tok, 256);
-  const int chunks = ceil_div(n_tok, kEmbChunk);
   char* s = static_cast<char*>(scratch);
-  int32_t* counts = reinterpret_cast<int32_t*>(s);
+  EmbSort e;
+  e.counts = reinterpret_cast<int32_t*>(s);
   s += (size_t)G * V * 4;
-  int32_t* total = reinterpret_cast<int32_t*>(s);
+  e.total = reinterpret_cast<int32_t*>(s);
   s += (size_t)V * 4;
-  int32_t* start = reinterpret_cast<int32_t*>(s);
+  e.start = reinterpret_cast<int32_t*>(s);
   s += (size_t)V * 4;
-  int32_t* sorted = reinterpret_cast<int32_t*>(s);
+  e.sorted = reinterpret_cast<int32_t*>(s);
   s += (size_t)n_tok * 4;
   const size_t used = s - static_cast<char*>(scratch);
-  float* partial = reinterpret_cast<float*>(static_cast<char*>(scratch) + ((used + 255) & ~(size_t)255));
-  // the histogram keeps V counters in LDS (up to 128 KB); the attribute is
-  // set on every call (a host-side call) so that it holds on whichever
-  // device is current
+  e.partial = reinterpret_cast<float*>(static_cast<char*>(scratch) + ((used + 255) & ~(size_t)255));
+  return e;
+}
+}  // namespace
+
+hipError_t nc_embed_sort(const int32_t* tok, int n_tok, int V, void* scratch, hipStream_t st) {
+  if (n_tok <= 0) return hipSuccess;
+  const int G = ceil_div(n_tok, 256);
+  const EmbSort e = emb_sort_layout(scratch, n_tok, V);
   const hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(embed_hist_kernel),
                                             hipFuncAttributeMaxDynamicSharedMemorySize, V * 4);
   if (ea != hipSuccess) return ea;
-  embed_hist_kernel<<<G, 256, (size_t)V * 4, st>>>(tok, n_tok, V, counts);
-  embed_colscan_kernel<<<ceil_div(V, 256), 256, 0, st>>>(counts, G, V, total);
-  embed_scan_kernel<<<1, 1024, 0, st>>>(total, V, start);
-  embed_scatter_kernel<<<G, 256, 0, st>>>(tok, n_tok, V, counts, start, sorted);
-  embed_segsum_kernel<<<chunks, 256, 0, st>>>(tok, sorted, start, total, dx, dE, partial, n_tok, d, V);
-  embed_fixup_kernel<<<V, 256, 0, st>>>(start, total, partial, dE, V, d);
+  embed_hist_kernel<<<G, 256, (size_t)V * 4, st>>>(tok, n_tok, V, e.counts);
+  embed_colscan_kernel<<<ceil_div(V, 256), 256, 0, st>>>(e.counts, G, V, e.total);
+  embed_scan_kernel<<<1, 1024, 0, st>>>(e.total, V, e.start);
+  embed_scatter_kernel<<<G, 256, 0, st>>>(tok, n_tok, V, e.counts, e.start, e.sorted);
   return hipGetLastError();
+}
+
+hipError_t nc_embed_segsum(const int32_t* tok, const float* rows, float* dE, int n_tok, int V,
+                           int width, void* scratch, hipStream_t st) {
+  if (n_tok <= 0) return hipSuccess;
+  const int chunks = ceil_div(n_tok, kEmbChunk);
+  const EmbSort e = emb_sort_layout(scratch, n_tok, V);
+  embed_segsum_kernel<<<chunks, 256, 0, st>>>(tok, e.sorted, e.start, e.total, rows, dE,
+                                              e.partial, n_tok, width, V);
+  embed_fixup_kernel<<<V, 256, 0, st>>>(e.start, e.total, e.partial, dE, V, width);
+  return hipGetLastError();
+}
+
+hipError_t nc_embed_bwd(const int32_t* tok, const float* dx, float* dE, int n_tok, int V, int d,
+                        void* scratch, hipStream_t st) {
+  if (n_tok <= 0) return hipSuccess;
+  const hipError_t e = nc_embed_sort(tok, n_tok, V, scratch, st);
+  if (e != hipSuccess) return e;
+  return nc_embed_segsum(tok, dx, dE, n_tok, V, d, scratch, st);
 }
 
 hipError_t nc_rmsnorm_fwd(int dtype, const float* x, void* y, float* r, int rows, int d,

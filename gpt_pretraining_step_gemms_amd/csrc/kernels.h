@@ -14,6 +14,64 @@ hipError_t nc_embed_fwd(const int32_t* tok, const float* E, float* x, int n_tok,
 size_t nc_embed_bwd_scratch_bytes(int n_tok, int vocab, int d);
 hipError_t nc_embed_bwd(const int32_t* tok, const float* dx, float* dE, int n_tok, int vocab,
                         int d, void* scratch, hipStream_t st);
+// The same in two parts: the stable sort of token positions by id (kept in
+// scratch), then dE[v, :width] += sum of rows[n, :width] over the positions
+// of id v (rows of `width` <= d floats), as often as needed for one sort.
+hipError_t nc_embed_sort(const int32_t* tok, int n_tok, int vocab, void* scratch,
+                         hipStream_t st);
+hipError_t nc_embed_segsum(const int32_t* tok, const float* rows, float* dE, int n_tok,
+                           int vocab, int width, void* scratch, hipStream_t st);
+
+// ---- the further model mechanisms (extras.hip); scalars are device pointers
+// x = E[tok] + lam_s sigmoid(E[tok][:24] . Ws) E[previous tok] (0 at a row
+// start); x0 (optional) = x; sig[n] = the sigmoid.  Out-of-range ids as nc_embed_fwd.
+hipError_t nc_embed_smear_fwd(const int32_t* tok, const float* E, const float* Ws,
+                              const float* lam_s, float* x, float* x0, float* sig, int n_tok,
+                              int T, int d, int V, int32_t* flag, hipStream_t st);
+// Per row: u = a x + sign_b b xo (a = *lam_a or 1, b = *lam_b or 0); xsave (optional)
+// = x before the mix; write_back: x = u; y = u r, r = (mean(u^2) + eps)^-1/2.
+hipError_t nc_rmsnorm_mix_fwd(int dtype, float* x, const float* xo, float* xsave,
+                              const float* lam_a, const float* lam_b, float sign_b,
+                              int write_back, void* y, float* r, int rows, int d, float eps,
+                              hipStream_t st);
+// RMSNorm backward at the mixed stream u = lam_r x_prev + lam_0 x0 (din), then
+// per-row din . xprev and din . x0 (part_r, part_0, optional), dx0 += lam_0 din
+// (optional), dx = dxT = lam_r din + gb (lam_r null: 1; gb optional).
+hipError_t nc_rmsnorm_mix_bwd(int dtype, const float* dy, const void* y, const float* r,
+                              float* dx, void* dxT, const float* xprev, const float* x0,
+                              float* dx0, const float* lam_r, const float* lam_0, const float* gb,
+                              float* part_r, float* part_0, int rows, int d, int accumulate,
+                              hipStream_t st);
+// Backward of x - lam_b xb: part[row] = -dx . xb, gb = -lam_b dx.
+hipError_t nc_backout_bwd(const float* dx, const float* xb, const float* lam_b, float* gb,
+                          float* part, int rows, int d, hipStream_t st);
+// Smear backward with dX = dx + dx0 (dx0 optional): gs[n] = gamma sig, dz[n] =
+// gamma lam_s sig (1 - sig) with gamma = dX[n] . E[previous tok]; dxe = the
+// gradient at the looked-up embedding rows.
+hipError_t nc_smear_bwd(const int32_t* tok, const float* E, const float* dx, const float* dx0,
+                        const float* sig, const float* lam_s, const float* Ws, float* gs,
+                        float* dz, float* dxe, int n_tok, int T, int d, int V, hipStream_t st);
+// v[n, h] += 3 sigmoid(a[n, :C] . Wg[h]) VE[tok[n], h] per key/value head h (C % 8 == 0,
+// C <= 64); sig [n_tok, Hkv] = the sigmoids.
+hipError_t nc_ve_mix_fwd(int dtype, const int32_t* tok, const float* VE, const float* Wg,
+                         const void* a, int64_t lda, void* v, int64_t ldv, float* sig, int n_tok,
+                         int Hkv, int C, int V, hipStream_t st);
+// rows[n, h] = 3 sig dv[n, h] (fp32 [n_tok, Hkv*128]); dz[n, h] = (dv . VE[tok, h]) 3 sig (1 - sig).
+hipError_t nc_ve_bwd(int dtype, const int32_t* tok, const float* VE, const void* dv,
+                     int64_t lddv, const float* sig, float* rows, float* dz, int n_tok, int Hkv,
+                     int V, hipStream_t st);
+// da[n, j] += sum_h dz[n, h] Wg[h, j], j < C.
+hipError_t nc_ve_gate_da(const float* dz, const float* Wg, float* da, int64_t ldda, int n_tok,
+                         int Hkv, int C, hipStream_t st);
+// out[h, j] += sum_n A[n, h] B(n, j), h < H, j < C; B(n, j) = B[n ldb + j] or, with tok,
+// B[tok[n] ldb + j] (an embedding row).  part: nc_outer_scratch_floats(H, C) floats.
+constexpr int kOuterParts = 256;
+size_t nc_outer_scratch_floats(int H, int C);
+hipError_t nc_outer_accumulate(int dtype, const float* A, int H, const void* B, int64_t ldb,
+                               const int32_t* tok, int V, int C, int n_tok, float* part,
+                               float* out, hipStream_t st);
+// out[0] += sum of vals[0..n), fixed order.
+hipError_t nc_sum_into(const float* vals, int n, float* out, hipStream_t st);
 
 // ---- RMSNorm (rows of length d; eps)
 hipError_t nc_rmsnorm_fwd(int dtype, const float* x, void* y, float* r, int rows, int d,

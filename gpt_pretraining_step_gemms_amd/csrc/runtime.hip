@@ -62,6 +62,18 @@ struct nc_ctx {
   int L, d, H, F, V, T, maxB, Nmax, chunk;
   int Hkv, dk, W;   // key/value heads, their width Hkv*128, qkv row width d + 2 dk
   bool fp8 = false;  // forward block products in fp8 e4m3 (tensorwise scales)
+  // further mechanisms (nc_model_config.features)
+  bool ve_on = false, resid_on = false, smear_on = false, backout_on = false;
+  int Cg = 32;                 // value-embedding gate channels
+  std::vector<int> ve_layers;  // layers with a value embedding, ascending
+  std::vector<int> ve_slot;    // layer -> index in ve_layers, or -1
+  int Lb = 0;                  // backout layer: xb is the stream entering it
+  // element offsets (master / gradient layout) of the feature parameters
+  size_t e_wg = 0, e_ws = 0, e_ve = 0, e_rl = 0, e_x0l = 0, e_sl = 0, e_bl = 0;
+  int64_t n_vet = 0, n_sc = 0, n_adam = 0;   // VE table and scalar elements, AdamW region
+  // activation arena: feature buffers
+  size_t x0b = 0, xprev = 0, dx0b = 0, gbb = 0, xbb = 0, part_a = 0, part_b = 0, sig_s = 0,
+         gs_s = 0, dz_s = 0, sig_ve = 0, dz_ve = 0, ve_rows = 0, outer_part = 0;
   size_t q8a = 0, q8w = 0, q8s = 0, q8ws = 0;   // their codes, scales and amax scratch
   int64_t S, n_block, n_total;
   std::vector<ParamInfo> params;
@@ -76,7 +88,9 @@ struct nc_ctx {
   // key/value heads), 1: 2L wide [d,F], 2: 2L [dk,d] with grouped key/value heads):
   // the fp32 iterate X (two, ping-pong), A = X X^T, B = b A + c A A, and a copy of
   // each in the activation type for the matrix cores.
-  struct NsBufs { size_t x32[2], xh[2], a32, ah, b32, bh; } ns[3];
+  // Groups 3 and 4 (value-embedding gates, smear gate) are tiny and iterate in
+  // fp32 with the VALU product (their xh buffers are their x32 buffers).
+  struct NsBufs { size_t x32[2], xh[2], a32, ah, b32, bh; } ns[5];
   int splits_qkv, splits_o, splits_1, splits_2, splits_head, splits_dxf;
   std::vector<int> windows;   // attention window per layer, -1 = plain causal
   char* pa = nullptr;
@@ -137,6 +151,27 @@ nc_status validate(const nc_model_config* m, const nc_optim_config* o, std::stri
     why = "fp8_forward needs d_ff % 128 == 0 (the fp8 products take K in steps of 128)";
     return NC_ERR_UNSUPPORTED;
   }
+  if (m->features < 0 || m->features > 15) { why = "unknown feature bits"; return NC_ERR_INVALID_ARG; }
+  if (m->ve_gate_channels < 0) { why = "ve_gate_channels"; return NC_ERR_INVALID_ARG; }
+  {
+    const int cg = m->ve_gate_channels ? m->ve_gate_channels : 32;
+    if ((m->features & NC_FEAT_VALUE_EMBEDS) && (cg % 8 || cg > 64 || cg > m->d_model)) {
+      why = "ve_gate_channels must be a multiple of 8, at most 64 and at most d_model";
+      return NC_ERR_UNSUPPORTED;
+    }
+    if ((m->features & NC_FEAT_SMEAR) && m->d_model < 24) {
+      why = "smear reads 24 embedding channels";
+      return NC_ERR_UNSUPPORTED;
+    }
+    if ((m->features & NC_FEAT_BACKOUT) && m->n_layer < 1) {
+      why = "backout needs at least one layer";
+      return NC_ERR_UNSUPPORTED;
+    }
+    if ((m->features & (NC_FEAT_VALUE_EMBEDS | NC_FEAT_SMEAR)) && o && o->normuon) {
+      why = "NorMuon is not combined with the gate parameters";
+      return NC_ERR_UNSUPPORTED;
+    }
+  }
   if (m->n_kv_head < 0 || (m->n_kv_head > 0 && m->n_head % m->n_kv_head)) {
     why = "n_kv_head must divide n_head (0: n_head)";
     return NC_ERR_INVALID_ARG;
@@ -171,8 +206,24 @@ void plan(nc_ctx* c) {
   const size_t es = c->es;
   // per layer: Wq [d,d] | Wk [dk,d] | Wv [dk,d] | Wo [d,d] | W1 [F,d] | W2 [d,F]
   c->S = 2LL * d * d + 2LL * dk * d + 2LL * d * F;
-  c->n_block = c->S * L;
-  c->n_total = c->n_block + 2LL * V * d;
+  // Muon region: the layers' blocks, then the value-embedding gates
+  // [n_ve][Hkv, Cg] and the smear gate [1, 24]; then E, Wh and the AdamW
+  // extras: the value-embedding tables [n_ve][V, dk] and the scalars
+  // (resid_lambdas [L], x0_lambdas [L], smear_lambda, backout_lambda), padded to 8.
+  const int n_ve = (int)c->ve_layers.size();
+  c->e_wg = (size_t)c->S * L;
+  c->e_ws = c->e_wg + (size_t)n_ve * Hkv * c->Cg;
+  c->n_block = (int64_t)c->e_ws + (c->smear_on ? 24 : 0);
+  c->e_ve = (size_t)c->n_block + 2ULL * V * d;
+  c->n_vet = (int64_t)n_ve * V * dk;
+  c->e_rl = c->e_ve + (size_t)c->n_vet;
+  c->e_x0l = c->e_rl + (c->resid_on ? L : 0);
+  c->e_sl = c->e_x0l + (c->resid_on ? L : 0);
+  c->e_bl = c->e_sl + (c->smear_on ? 1 : 0);
+  c->n_sc = (int64_t)(c->e_bl + (c->backout_on ? 1 : 0) - c->e_rl);
+  c->n_sc = (c->n_sc + 7) / 8 * 8;
+  c->n_total = (int64_t)c->e_rl + c->n_sc;
+  c->n_adam = 2LL * V * d + c->n_vet + c->n_sc;
   // registry
   c->params.clear();
   c->params.push_back({"E", V, d, NC_GROUP_ADAMW, (size_t)c->n_block, 0});
@@ -189,13 +240,32 @@ void plan(nc_ctx* c) {
   }
   c->params.push_back({"Wh", V, d, NC_GROUP_ADAMW, (size_t)(c->n_block + (int64_t)V * d),
                        (int64_t)V * d});
+  const int64_t ad0 = c->n_block;   // AdamW state offsets count from E
+  for (int i = 0; i < n_ve; ++i) {
+    const int l = c->ve_layers[i];
+    c->params.push_back({"ve." + std::to_string(l), V, dk, NC_GROUP_ADAMW,
+                         c->e_ve + (size_t)i * V * dk,
+                         (int64_t)(c->e_ve + (size_t)i * V * dk) - ad0});
+    c->params.push_back({std::to_string(l) + ".Wg", Hkv, c->Cg, NC_GROUP_MUON,
+                         c->e_wg + (size_t)i * Hkv * c->Cg, -1});
+  }
+  if (c->resid_on) {
+    c->params.push_back({"resid_lambdas", 1, L, NC_GROUP_ADAMW, c->e_rl, (int64_t)c->e_rl - ad0});
+    c->params.push_back({"x0_lambdas", 1, L, NC_GROUP_ADAMW, c->e_x0l, (int64_t)c->e_x0l - ad0});
+  }
+  if (c->smear_on) {
+    c->params.push_back({"smear_gate", 1, 24, NC_GROUP_MUON, c->e_ws, -1});
+    c->params.push_back({"smear_lambda", 1, 1, NC_GROUP_ADAMW, c->e_sl, (int64_t)c->e_sl - ad0});
+  }
+  if (c->backout_on)
+    c->params.push_back({"backout_lambda", 1, 1, NC_GROUP_ADAMW, c->e_bl, (int64_t)c->e_bl - ad0});
 
   Layout p;
   c->oP = p.take(c->n_total * 4);
   c->oG = p.take(c->n_total * 4);
   c->oM = p.take(c->n_block * 4);
-  c->oAm = p.take(2ULL * V * d * 4);
-  c->oAv = p.take(2ULL * V * d * 4);
+  c->oAm = p.take((size_t)c->n_adam * 4);
+  c->oAv = p.take((size_t)c->n_adam * 4);
   c->oSh = c->dt ? p.take((c->n_block + (size_t)V * d) * 2) : 0;
   c->oTab = p.take(2ULL * T * 64 * 4);
   c->nm_rows = c->ocfg.normuon ? (int64_t)L * (3LL * d + 2LL * dk + F) : 0;
@@ -269,8 +339,52 @@ void plan(nc_ctx* c) {
     b.bh = a.take(ae * es);
   }
   c->nsU = c->ocfg.muon_nesterov ? a.take((size_t)c->n_block * 4) : 0;
-  c->frob = a.take((size_t)6 * std::max(L, 1) * 256 * 4);
-  c->norms = a.take((size_t)6 * std::max(L, 1) * 4);
+  const size_t n_mats = (size_t)6 * std::max(L, 1) + n_ve + 1;   // Muon matrices
+  c->frob = a.take(n_mats * 256 * 4);
+  c->norms = a.take(n_mats * 4);
+  // Newton-Schulz buffers of the gate groups (fp32 only)
+  {
+    const int cnt[2] = {n_ve, c->smear_on ? 1 : 0};
+    const int R[2] = {std::min(Hkv, c->Cg), 1}, Cc[2] = {std::max(Hkv, c->Cg), 24};
+    for (int g = 0; g < 2; ++g) {
+      auto& b = c->ns[3 + g];
+      b = {};
+      if (!cnt[g]) continue;
+      const size_t xe = (size_t)cnt[g] * R[g] * Cc[g], ae = (size_t)cnt[g] * R[g] * R[g];
+      for (int k = 0; k < 2; ++k) {
+        b.x32[k] = a.take(xe * 4);
+        b.xh[k] = b.x32[k];
+      }
+      b.a32 = b.ah = a.take(ae * 4);
+      b.b32 = b.bh = a.take(ae * 4);
+    }
+  }
+  // feature buffers
+  if (c->resid_on) {
+    c->x0b = a.take(N * d * 4);
+    c->xprev = a.take((size_t)L * N * d * 4);      // each layer's stream before its mix
+    c->dx0b = a.take(N * d * 4);
+  }
+  if (c->backout_on) {
+    c->gbb = a.take(N * d * 4);
+    if (!c->resid_on) c->xbb = a.take(N * d * 4);
+  }
+  if (c->resid_on || c->backout_on) {
+    c->part_a = a.take(N * 4);
+    c->part_b = a.take(N * 4);
+  }
+  if (c->smear_on) {
+    c->sig_s = a.take(N * 4);
+    c->gs_s = a.take(N * 4);
+    c->dz_s = a.take(N * 4);
+  }
+  if (n_ve) {
+    c->sig_ve = a.take((size_t)n_ve * N * Hkv * 4);
+    c->dz_ve = a.take(N * Hkv * 4);
+    c->ve_rows = a.take(N * (size_t)dk * 4);
+  }
+  if (n_ve || c->smear_on)
+    c->outer_part = a.take(nc_outer_scratch_floats(std::max(Hkv, 1), std::max(c->Cg, 24)) * 4);
   if (c->nm_rows) {
     c->nm_vm = a.take((size_t)c->nm_rows * 4);
     c->nm_q = a.take((size_t)c->nm_rows * 4);
@@ -314,8 +428,7 @@ bool in_arena(const nc_ctx* c, const void* p, size_t bytes) {
 }
 
 // Host check of every operand extent of a GEMM against the arenas.
-bool operands_in_arenas(nc_ctx* c, const GemmParams& g) {
-  const size_t es = c->es;
+bool operands_in_arenas(nc_ctx* c, const GemmParams& g, size_t es) {
   const bool c_f32 = g.epi == kEpiStoreF32 || g.epi == kEpiAccF32 || g.epi == kEpiDual;
   auto extent = [](int64_t rows, int64_t cols, int64_t ld, int64_t bstride, int batch) {
     // elements spanned by a [rows, cols] row-major view with leading dim ld
@@ -344,7 +457,8 @@ hipError_t gemm(nc_ctx* c, const void* A_, int64_t lda, int al, const void* B_, 
                 int bl, void* C_, int64_t ldc, int M, int N, int K, int epi,
                 const void* aux_in = nullptr, void* aux_out = nullptr, int splits = 1,
                 int batch = 1, int64_t sA = 0, int64_t sB = 0, int64_t sC = 0, float p0 = 0.f,
-                float p1 = 0.f) {
+                float p1 = 0.f, int dtype = -1) {
+  const int dt = dtype < 0 ? c->dt : dtype;   // fp32 products of a bf16 model: dtype 0
   GemmParams g{};
   g.A = A_; g.B = B_; g.C = C_; g.aux_in = aux_in; g.aux_out = aux_out;
   g.lda = lda; g.ldb = ldb; g.ldc = ldc; g.sA = sA; g.sB = sB; g.sC = sC;
@@ -354,9 +468,9 @@ hipError_t gemm(nc_ctx* c, const void* A_, int64_t lda, int al, const void* B_, 
   g.splits = splits;
   g.workspace = reinterpret_cast<float*>(c->aa + c->ws);
   g.workspace_bytes = c->ws_bytes;
-  if (!operands_in_arenas(c, g)) return hipErrorInvalidValue;
+  if (!operands_in_arenas(c, g, dt ? 2 : 4)) return hipErrorInvalidValue;
   if (c->dry_run) return hipSuccess;
-  return nc_launch_gemm(c->dt, g, c->st);
+  return nc_launch_gemm(dt, g, c->st);
 }
 
 // Forward block product in fp8: C (epilogue epi) = X W^T with X bf16 [N, K]
@@ -430,6 +544,19 @@ static nc_ctx* make_ctx(const nc_model_config* cfg, const nc_optim_config* ocfg)
   c->V = cfg->vocab; c->T = cfg->seq_len; c->maxB = cfg->max_micro_batch;
   c->Nmax = c->maxB * c->T;
   c->windows.assign(c->L, -1);
+  c->ve_on = cfg->features & NC_FEAT_VALUE_EMBEDS;
+  c->resid_on = cfg->features & NC_FEAT_RESID_LAMBDAS;
+  c->smear_on = cfg->features & NC_FEAT_SMEAR;
+  c->backout_on = cfg->features & NC_FEAT_BACKOUT;
+  c->Cg = cfg->ve_gate_channels ? cfg->ve_gate_channels : 32;
+  c->ve_slot.assign(c->L, -1);
+  if (c->ve_on)
+    for (int l = 0; l < c->L; ++l)
+      if ((c->L - 1 - l) % 2 == 0) {
+        c->ve_slot[l] = (int)c->ve_layers.size();
+        c->ve_layers.push_back(l);
+      }
+  c->Lb = c->L / 2;
   plan(c);
   return c;
 }
@@ -493,8 +620,8 @@ nc_status nc_bind(nc_ctx* ctx, void* d_param_arena, size_t param_bytes, void* d_
   // gradients and optimizer state start at zero, step count at 0
   NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oG), 0.f, ctx->n_total, ctx->st), "zero grads");
   NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oM), 0.f, ctx->n_block, ctx->st), "zero momentum");
-  NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oAm), 0.f, 2ULL * ctx->V * ctx->d, ctx->st), "zero m");
-  NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oAv), 0.f, 2ULL * ctx->V * ctx->d, ctx->st), "zero v");
+  NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oAm), 0.f, ctx->n_adam, ctx->st), "zero m");
+  NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oAv), 0.f, ctx->n_adam, ctx->st), "zero v");
   if (ctx->nm_rows)
     NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oV2), 0.f, ctx->nm_rows, ctx->st), "zero normuon v2");
   NC_TRY(nc_fill_f32(A<float>(ctx, ctx->flags), 0.f, 1, ctx->st), "clear input flags");
@@ -520,10 +647,17 @@ nc_status nc_init_params(nc_ctx* ctx, uint64_t seed, float std) {
   if (!(std >= 0.f)) return fail(ctx, NC_ERR_INVALID_ARG, "std");
   NC_TRY(nc_init_normal(P<float>(ctx, ctx->oP), ctx->n_total, seed, 0, std, ctx->st), "init");
   NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oM), 0.f, ctx->n_block, ctx->st), "zero momentum");
-  NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oAm), 0.f, 2ULL * ctx->V * ctx->d, ctx->st), "zero m");
-  NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oAv), 0.f, 2ULL * ctx->V * ctx->d, ctx->st), "zero v");
+  NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oAm), 0.f, ctx->n_adam, ctx->st), "zero m");
+  NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oAv), 0.f, ctx->n_adam, ctx->st), "zero v");
   if (ctx->nm_rows)
     NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oV2), 0.f, ctx->nm_rows, ctx->st), "zero normuon v2");
+  // scalars at the values that leave the plain model unchanged: resid 1, x0,
+  // smear and backout 0 (and the padding after them 0)
+  if (ctx->n_sc) {
+    NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oP) + ctx->e_rl, 0.f, ctx->n_sc, ctx->st), "scalars");
+    if (ctx->resid_on)
+      NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oP) + ctx->e_rl, 1.f, ctx->L, ctx->st), "resid");
+  }
   ctx->step = 0;
   return refresh_shadows(ctx);
 }
@@ -574,15 +708,46 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
 
   // ---------------------------------------------------------------- forward
   int32_t* flags = A<int32_t>(ctx, ctx->flags);
-  NC_TRY(nc_embed_fwd(tok, P<float>(ctx, ctx->oP) + ctx->n_block, x, N, d, V, flags, st), "embed");
+  const float* Pm = P<float>(ctx, ctx->oP);
+  const float* E = Pm + ctx->n_block;
+  float* x0b = ctx->resid_on ? A<float>(ctx, ctx->x0b) : nullptr;
+  const size_t Nd = (size_t)N * d;
+  auto xprev_of = [&](int l) { return A<float>(ctx, ctx->xprev) + (size_t)l * Nd; };
+  // the stream entering layer Lb (backout's xb)
+  float* xb = !ctx->backout_on ? nullptr
+              : ctx->resid_on  ? xprev_of(ctx->Lb)
+                               : A<float>(ctx, ctx->xbb);
+  if (ctx->smear_on) {
+    NC_TRY(nc_embed_smear_fwd(tok, E, Pm + ctx->e_ws, Pm + ctx->e_sl, x, x0b,
+                              A<float>(ctx, ctx->sig_s), N, T, d, V, flags, st), "embed smear");
+  } else {
+    NC_TRY(nc_embed_fwd(tok, E, x, N, d, V, flags, st), "embed");
+    if (x0b) NC_TRY(hipMemcpyAsync(x0b, x, Nd * 4, hipMemcpyDeviceToDevice, st), "x0");
+  }
   for (int l = 0; l < L; ++l) {
     const LayerAct& la = ctx->la[l];
     const size_t wb = (size_t)l * ctx->S;
     char* qkv = aa + la.qkv;
-    NC_TRY(nc_rmsnorm_fwd(dt, x, aa + la.a1, A<float>(ctx, la.r1), N, d, eps, st), "norm1");
+    if (ctx->resid_on || (ctx->backout_on && l == ctx->Lb)) {
+      // x <- resid_l x + x0_l x0 (saving the stream before the mix), then norm1
+      NC_TRY(nc_rmsnorm_mix_fwd(dt, x, x0b, ctx->resid_on ? xprev_of(l) : xb,
+                                ctx->resid_on ? Pm + ctx->e_rl + l : nullptr,
+                                ctx->resid_on ? Pm + ctx->e_x0l + l : nullptr, 1.f,
+                                ctx->resid_on, aa + la.a1, A<float>(ctx, la.r1), N, d, eps, st),
+             "mix norm1");
+    } else {
+      NC_TRY(nc_rmsnorm_fwd(dt, x, aa + la.a1, A<float>(ctx, la.r1), N, d, eps, st), "norm1");
+    }
     NC_GEMM(ctx->fp8 ? gemm_fp8_fwd(ctx, aa + la.a1, d, wptr(ctx, wb), Wd, qkv, Wd, N, kEpiStore)
                      : gemm(ctx, aa + la.a1, d, kKCont, wptr(ctx, wb), d, kKCont, qkv, Wd, N, Wd,
                             d, kEpiStore), "qkv");
+    if (ctx->ve_slot[l] >= 0) {
+      const int i = ctx->ve_slot[l];
+      NC_TRY(nc_ve_mix_fwd(dt, tok, Pm + ctx->e_ve + (size_t)i * V * dk,
+                           Pm + ctx->e_wg + (size_t)i * Hkv * ctx->Cg, aa + la.a1, d,
+                           qkv + (d + dk) * es, Wd, A<float>(ctx, ctx->sig_ve) + (size_t)i * N * Hkv,
+                           N, Hkv, ctx->Cg, V, st), "value embedding");
+    }
     NC_TRY(nc_qk_norm_rope_fwd(dt, qkv, A<float>(ctx, la.rqk), tab, N, T, H, Hkv, eps, st),
            "qknorm");
     NC_TRY(nc_attn_fwd(dt, qkv, qkv + d * es, qkv + (d + dk) * es, Wd, aa + la.o, d,
@@ -600,7 +765,11 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
                      : gemm(ctx, aa + la.g, F, kKCont, wptr(ctx, wb + oW1 + (size_t)F * d), F,
                             kKCont, x, d, N, d, F, kEpiAccF32), "mlp down");
   }
-  NC_TRY(nc_rmsnorm_fwd(dt, x, aa + ctx->xf, A<float>(ctx, ctx->rf), N, d, eps, st), "normf");
+  if (ctx->backout_on)        // xf = N(x - backout xb)
+    NC_TRY(nc_rmsnorm_mix_fwd(dt, x, xb, nullptr, nullptr, Pm + ctx->e_bl, -1.f, 0, aa + ctx->xf,
+                              A<float>(ctx, ctx->rf), N, d, eps, st), "backout normf");
+  else
+    NC_TRY(nc_rmsnorm_fwd(dt, x, aa + ctx->xf, A<float>(ctx, ctx->rf), N, d, eps, st), "normf");
 
   // ------------------------------------------- lm_head + cross-entropy, chunked
   const size_t wh = (size_t)(ctx->n_block + (int64_t)V * d);
@@ -621,6 +790,17 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
   NC_TRY(nc_sum_scaled(A<float>(ctx, ctx->loss_rows), N, 1.f / (float)N, d_loss, st), "loss");
   NC_TRY(nc_rmsnorm_bwd(dt, da, aa + ctx->xf, A<float>(ctx, ctx->rf), dx, dxT, N, d, 0, st),
          "normf bwd");
+  float* part_a = (ctx->resid_on || ctx->backout_on) ? A<float>(ctx, ctx->part_a) : nullptr;
+  float* part_b = (ctx->resid_on || ctx->backout_on) ? A<float>(ctx, ctx->part_b) : nullptr;
+  float* gb = ctx->backout_on ? A<float>(ctx, ctx->gbb) : nullptr;
+  float* dx0b = ctx->resid_on ? A<float>(ctx, ctx->dx0b) : nullptr;
+  void* emb_scratch = aa + ctx->emb;
+  if (ctx->backout_on) {      // d backout = -dx . xb; gb = -backout dx joins at layer Lb
+    NC_TRY(nc_backout_bwd(dx, xb, Pm + ctx->e_bl, gb, part_a, N, d, st), "backout bwd");
+    NC_TRY(nc_sum_into(part_a, N, G + ctx->e_bl, st), "backout grad");
+  }
+  if (dx0b) NC_TRY(nc_fill_f32(dx0b, 0.f, Nd, st), "zero dx0");
+  if (ctx->ve_on) NC_TRY(nc_embed_sort(tok, N, V, emb_scratch, st), "token sort");
 
   // --------------------------------------------------------------- backward
   for (int l = L - 1; l >= 0; --l) {
@@ -654,21 +834,68 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
     if (!dt)
       NC_TRY(nc_qk_norm_rope_bwd(dt, dqkv, qkv, A<float>(ctx, la.rqk), tab, N, T, H, Hkv, st),
              "qknorm bwd");
+    const int vs = ctx->ve_slot[l];
+    if (vs >= 0) {   // value embedding: table rows, gate matrix, gate input
+      const float* VEl = Pm + ctx->e_ve + (size_t)vs * V * dk;
+      float* dz = A<float>(ctx, ctx->dz_ve);
+      float* rows = A<float>(ctx, ctx->ve_rows);
+      NC_TRY(nc_ve_bwd(dt, tok, VEl, dqkv + (d + dk) * es, Wd,
+                       A<float>(ctx, ctx->sig_ve) + (size_t)vs * N * Hkv, rows, dz, N, Hkv, V, st),
+             "value embedding bwd");
+      NC_TRY(nc_embed_segsum(tok, rows, G + ctx->e_ve + (size_t)vs * V * dk, N, V, dk,
+                             emb_scratch, st), "value embedding rows");
+      NC_TRY(nc_outer_accumulate(dt, dz, Hkv, aa + la.a1, d, nullptr, V, ctx->Cg, N,
+                                 A<float>(ctx, ctx->outer_part),
+                                 G + ctx->e_wg + (size_t)vs * Hkv * ctx->Cg, st), "gate grad");
+    }
     NC_GEMM(gemm(ctx, dqkv, Wd, kMNCont, aa + la.a1, d, kMNCont, G + wb, d, Wd, d, N,
                 kEpiAccF32, nullptr, nullptr, ctx->splits_qkv), "dWqkv");
     NC_GEMM(gemm(ctx, dqkv, Wd, kKCont, wptr(ctx, wb), d, kMNCont, da, d, N, d, Wd,
                 kEpiStoreF32), "da1");
-    NC_TRY(nc_rmsnorm_bwd(dt, da, aa + la.a1, A<float>(ctx, la.r1), dx, dxT, N, d, 1, st),
-           "norm1 bwd");
+    if (vs >= 0)
+      NC_TRY(nc_ve_gate_da(A<float>(ctx, ctx->dz_ve), Pm + ctx->e_wg + (size_t)vs * Hkv * ctx->Cg,
+                           da, d, N, Hkv, ctx->Cg, st), "gate input grad");
+    if (ctx->resid_on || (ctx->backout_on && l == ctx->Lb)) {
+      NC_TRY(nc_rmsnorm_mix_bwd(dt, da, aa + la.a1, A<float>(ctx, la.r1), dx, dxT,
+                                ctx->resid_on ? xprev_of(l) : nullptr, x0b, dx0b,
+                                ctx->resid_on ? Pm + ctx->e_rl + l : nullptr,
+                                ctx->resid_on ? Pm + ctx->e_x0l + l : nullptr,
+                                ctx->backout_on && l == ctx->Lb ? gb : nullptr,
+                                ctx->resid_on ? part_a : nullptr, ctx->resid_on ? part_b : nullptr,
+                                N, d, 1, st), "mix norm1 bwd");
+      if (ctx->resid_on) {
+        NC_TRY(nc_sum_into(part_a, N, G + ctx->e_rl + l, st), "resid grad");
+        NC_TRY(nc_sum_into(part_b, N, G + ctx->e_x0l + l, st), "x0 grad");
+      }
+    } else {
+      NC_TRY(nc_rmsnorm_bwd(dt, da, aa + la.a1, A<float>(ctx, la.r1), dx, dxT, N, d, 1, st),
+             "norm1 bwd");
+    }
   }
-  NC_TRY(nc_embed_bwd(tok, dx, G + ctx->n_block, N, V, d, aa + ctx->emb, st), "embed bwd");
+  // the gradient at the embedding output: dx (+ dx0b, the x0 paths)
+  float* dEm = G + ctx->n_block;
+  const float* rows = dx;
+  if (ctx->smear_on) {        // through the smear mix to the looked-up rows (into da)
+    NC_TRY(nc_smear_bwd(tok, E, dx, dx0b, A<float>(ctx, ctx->sig_s), Pm + ctx->e_sl,
+                        Pm + ctx->e_ws, A<float>(ctx, ctx->gs_s), A<float>(ctx, ctx->dz_s), da,
+                        N, T, d, V, st), "smear bwd");
+    NC_TRY(nc_sum_into(A<float>(ctx, ctx->gs_s), N, G + ctx->e_sl, st), "smear lambda grad");
+    NC_TRY(nc_outer_accumulate(0, A<float>(ctx, ctx->dz_s), 1, E, d, tok, V, 24, N,
+                               A<float>(ctx, ctx->outer_part), G + ctx->e_ws, st), "smear gate grad");
+    rows = da;
+  }
+  if (!ctx->ve_on) NC_TRY(nc_embed_sort(tok, N, V, emb_scratch, st), "token sort");
+  NC_TRY(nc_embed_segsum(tok, rows, dEm, N, V, d, emb_scratch, st), "embed bwd");
+  if (dx0b && !ctx->smear_on)
+    NC_TRY(nc_embed_segsum(tok, dx0b, dEm, N, V, d, emb_scratch, st), "embed bwd (x0)");
   return NC_OK;
 }
 
 // Newton-Schulz on `count` matrices X [R, C] (R <= C) of group g, starting from
 // the prepared buffers x32[0]/xh[0].  Every iterate is kept in fp32; only the
 // matrix-core inputs are rounded.  *result = byte offset of the final fp32 X.
-static nc_status newton_schulz(nc_ctx* ctx, int g, int count, int R, int C, size_t* result) {
+static nc_status newton_schulz(nc_ctx* ctx, int g, int count, int R, int C, size_t* result,
+                               int dtype = -1) {
   const nc_optim_config& o = ctx->ocfg;
   char* aa = ctx->aa;
   const auto& b = ctx->ns[g];
@@ -678,14 +905,16 @@ static nc_status newton_schulz(nc_ctx* ctx, int g, int count, int R, int C, size
     const float ca = o.ns_coeffs[it][0], cb = o.ns_coeffs[it][1], cc = o.ns_coeffs[it][2];
     // A = X X^T
     NC_GEMM(gemm(ctx, aa + b.xh[cur], C, kKCont, aa + b.xh[cur], C, kKCont, aa + b.a32, R, R, R,
-                 C, kEpiDual, nullptr, aa + b.ah, 1, count, sx, sx, sa, 0.f, 1.f), "ns gram");
+                 C, kEpiDual, nullptr, aa + b.ah, 1, count, sx, sx, sa, 0.f, 1.f, dtype),
+            "ns gram");
     // B = b A + c A A   (A symmetric: A A = A A^T)
     NC_GEMM(gemm(ctx, aa + b.ah, R, kKCont, aa + b.ah, R, kKCont, aa + b.b32, R, R, R, R,
-                 kEpiDual, aa + b.a32, aa + b.bh, 1, count, sa, sa, sa, cb, cc), "ns poly");
+                 kEpiDual, aa + b.a32, aa + b.bh, 1, count, sa, sa, sa, cb, cc, dtype),
+            "ns poly");
     // X' = a X + B X
     NC_GEMM(gemm(ctx, aa + b.bh, R, kKCont, aa + b.xh[cur], C, kMNCont, aa + b.x32[cur ^ 1], C,
                  R, C, R, kEpiDual, aa + b.x32[cur], aa + b.xh[cur ^ 1], 1, count, sa, sx, sx,
-                 ca, 1.f), "ns update");
+                 ca, 1.f, dtype), "ns update");
     cur ^= 1;
   }
   *result = b.x32[cur];
@@ -712,7 +941,19 @@ nc_status nc_optimizer_step(nc_ctx* ctx, float lr_mult) {
                   o.adam_lr_head * lr_mult, o.adam_beta1, o.adam_beta2, o.adam_eps, o.adam_wd,
                   bc1, bc2, dt ? (void*)(ctx->pa + ctx->oSh + ctx->n_block * 2) : nullptr, Vd, st),
          "adamw");
-  if (L == 0) return NC_OK;
+  // value-embedding tables and scalars: AdamW state continues after E | Wh
+  if (ctx->n_vet)
+    NC_TRY(nc_adamw(Pm + ctx->e_ve, G + ctx->e_ve, P<float>(ctx, ctx->oAm) + 2 * Vd,
+                    P<float>(ctx, ctx->oAv) + 2 * Vd, ctx->n_vet, ctx->n_vet,
+                    o.adam_lr_embed * lr_mult, o.adam_lr_embed * lr_mult, o.adam_beta1,
+                    o.adam_beta2, o.adam_eps, o.adam_wd, bc1, bc2, nullptr, 0, st), "adamw ve");
+  if (ctx->n_sc)
+    NC_TRY(nc_adamw(Pm + ctx->e_rl, G + ctx->e_rl, P<float>(ctx, ctx->oAm) + 2 * Vd + ctx->n_vet,
+                    P<float>(ctx, ctx->oAv) + 2 * Vd + ctx->n_vet, ctx->n_sc, ctx->n_sc,
+                    o.adam_lr_scalar * lr_mult, o.adam_lr_scalar * lr_mult, o.adam_beta1,
+                    o.adam_beta2, o.adam_eps, o.adam_wd, bc1, bc2, nullptr, 0, st),
+           "adamw scalars");
+  if (ctx->n_block == 0) return NC_OK;
   // Muon
   float* Mom = P<float>(ctx, ctx->oM);
   NC_TRY(nc_momentum(Mom, G, ctx->n_block, o.muon_momentum, st), "momentum");
@@ -740,7 +981,7 @@ nc_status nc_optimizer_step(nc_ctx* ctx, float lr_mult) {
     size_t xoff;   // offset of the group's iterates in that buffer group
   };
   const MatBatch one{1, 0, ctx->S};
-  Grp grps[4];
+  Grp grps[6];
   int ng = 0;
   if (dk == d) {
     grps[ng++] = {0, MatBatch{4, dd, ctx->S}, d, d, 4 * L, 0, 0, 0};            // Wq Wk Wv Wo
@@ -748,8 +989,19 @@ nc_status nc_optimizer_step(nc_ctx* ctx, float lr_mult) {
     grps[ng++] = {0, MatBatch{2, (int64_t)oWo, ctx->S}, d, d, 2 * L, 0, 0, 0};  // Wq Wo
     grps[ng++] = {(size_t)dd, MatBatch{2, kd, ctx->S}, dk, d, 2 * L, 0, 2, 0};  // Wk Wv
   }
-  grps[ng++] = {o1, one, F, d, L, 1, 1, 0};                                     // W1
-  grps[ng++] = {o2, one, d, F, L, 0, 1, (size_t)L * dF};                        // W2
+  if (L) {
+    grps[ng++] = {o1, one, F, d, L, 1, 1, 0};                                   // W1
+    grps[ng++] = {o2, one, d, F, L, 0, 1, (size_t)L * dF};                      // W2
+  } else {
+    ng = 0;
+  }
+  const int ng_block = ng;
+  // gates (fp32 Newton-Schulz groups 3 and 4), oriented on their short side
+  const int n_ve = (int)ctx->ve_layers.size(), Hkv = ctx->Hkv, Cg = ctx->Cg;
+  if (n_ve)
+    grps[ng++] = {ctx->e_wg, MatBatch{1, 0, (int64_t)Hkv * Cg}, Hkv, Cg, n_ve, Hkv > Cg ? 1 : 0,
+                  3, 0};
+  if (ctx->smear_on) grps[ng++] = {ctx->e_ws, one, 1, 24, 1, 0, 4, 0};
   int nidx = 0;
   for (int i = 0; i < ng; ++i) {
     const Grp& g = grps[i];
@@ -757,19 +1009,32 @@ nc_status nc_optimizer_step(nc_ctx* ctx, float lr_mult) {
     const auto& b = ctx->ns[g.ns];
     NC_TRY(nc_frob_norms(U + g.woff, g.mb, el, g.count, frob + (size_t)nidx * 256, norms + nidx,
                          st), "norms");
-    NC_TRY(nc_ns_prepare(dt, U + g.woff, g.mb, g.R, g.C, g.count, norms + nidx, o.ns_eps, g.tr,
-                         A<float>(ctx, b.x32[0]) + g.xoff, aa + b.xh[0] + g.xoff * ctx->es, el,
-                         st), "ns prepare");
+    const int gdt = g.ns >= 3 ? 0 : dt;           // gate groups iterate in fp32
+    NC_TRY(nc_ns_prepare(gdt, U + g.woff, g.mb, g.R, g.C, g.count, norms + nidx, o.ns_eps, g.tr,
+                         A<float>(ctx, b.x32[0]) + g.xoff,
+                         aa + b.xh[0] + g.xoff * (gdt ? ctx->es : 4), el, st), "ns prepare");
     nidx += g.count;
   }
-  // Newton-Schulz per buffer group: 0 square, 1 W1^T | W2 [d, F], 2 Wk | Wv [dk, d]
-  size_t xres[3] = {0, 0, 0};
-  nc_status s = newton_schulz(ctx, 0, grps[0].count, d, d, &xres[0]);
-  if (s != NC_OK) return s;
-  s = newton_schulz(ctx, 1, 2 * L, d, F, &xres[1]);
-  if (s != NC_OK) return s;
-  if (dk != d) {
-    s = newton_schulz(ctx, 2, 2 * L, dk, d, &xres[2]);
+  // Newton-Schulz per buffer group: 0 square, 1 W1^T | W2 [d, F], 2 Wk | Wv [dk, d],
+  // 3 value-embedding gates, 4 smear gate
+  size_t xres[5] = {0, 0, 0, 0, 0};
+  nc_status s = NC_OK;
+  if (L) {
+    s = newton_schulz(ctx, 0, grps[0].count, d, d, &xres[0]);
+    if (s != NC_OK) return s;
+    s = newton_schulz(ctx, 1, 2 * L, d, F, &xres[1]);
+    if (s != NC_OK) return s;
+    if (dk != d) {
+      s = newton_schulz(ctx, 2, 2 * L, dk, d, &xres[2]);
+      if (s != NC_OK) return s;
+    }
+  }
+  if (n_ve) {
+    s = newton_schulz(ctx, 3, n_ve, std::min(Hkv, Cg), std::max(Hkv, Cg), &xres[3], 0);
+    if (s != NC_OK) return s;
+  }
+  if (ctx->smear_on) {
+    s = newton_schulz(ctx, 4, 1, 1, 24, &xres[4], 0);
     if (s != NC_OK) return s;
   }
   const float lr = o.muon_lr * lr_mult;
@@ -794,7 +1059,7 @@ nc_status nc_optimizer_step(nc_ctx* ctx, float lr_mult) {
       ms = scl;
     }
     NC_TRY(nc_ns_apply(Pm + g.woff, g.mb, g.R, g.C, g.count, X, el, g.tr, lr, o.muon_wd, rm, ms,
-                       sh ? sh + g.woff * 2 : nullptr, st), "ns apply");
+                       sh && i < ng_block ? sh + g.woff * 2 : nullptr, st), "ns apply");
     roff += (int64_t)g.count * g.R;
     nidx += g.count;
   }
@@ -854,7 +1119,7 @@ nc_status nc_set_param(nc_ctx* ctx, int32_t i, const float* src, int32_t src_on_
   NC_TRY(hipMemcpyAsync(dst, src, n * 4,
                         src_on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice, ctx->st),
          "set param");
-  if (ctx->dt && p.name != "E") {
+  if (ctx->dt && ((int64_t)p.elem < ctx->n_block || p.name == "Wh")) {
     // bf16 copy: block region mirrors the master layout, then Wh
     const size_t sh_elem = p.name == "Wh" ? (size_t)ctx->n_block : p.elem;
     NC_TRY(nc_convert_f32(1, dst, ctx->pa + ctx->oSh + sh_elem * 2, n, ctx->st), "set shadow");

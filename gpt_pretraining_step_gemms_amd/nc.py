@@ -22,6 +22,7 @@ NC_ERR_HIP, NC_ERR_STATE, NC_ERR_NONFINITE = 4, 5, 6
 NC_FP32, NC_BF16 = 0, 1
 NC_PARAM, NC_GRAD, NC_MOMENTUM, NC_ADAM_M, NC_ADAM_V = 0, 1, 2, 3, 4
 NC_K_CONTIGUOUS, NC_MN_CONTIGUOUS = 0, 1
+NC_FEAT_VALUE_EMBEDS, NC_FEAT_RESID_LAMBDAS, NC_FEAT_SMEAR, NC_FEAT_BACKOUT = 1, 2, 4, 8
 EPI_STORE, EPI_STORE_F32, EPI_ACC_F32, EPI_RELU2, EPI_RELU2_BWD, EPI_POLY, EPI_DUAL = range(7)
 
 
@@ -37,7 +38,9 @@ class ModelCfgC(ctypes.Structure):
                  "max_micro_batch", "dtype")] + [("rope_base", ctypes.c_float),
                                                  ("norm_eps", ctypes.c_float),
                                                  ("n_kv_head", ctypes.c_int32),
-                                                 ("fp8_forward", ctypes.c_int32)]
+                                                 ("fp8_forward", ctypes.c_int32),
+                                                 ("features", ctypes.c_int32),
+                                                 ("ve_gate_channels", ctypes.c_int32)]
 
 
 class OptimCfgC(ctypes.Structure):
@@ -48,7 +51,8 @@ class OptimCfgC(ctypes.Structure):
                 ("adam_lr_embed", ctypes.c_float), ("adam_lr_head", ctypes.c_float),
                 ("adam_beta1", ctypes.c_float), ("adam_beta2", ctypes.c_float),
                 ("adam_eps", ctypes.c_float), ("adam_wd", ctypes.c_float),
-                ("normuon", ctypes.c_int32), ("normuon_beta2", ctypes.c_float)]
+                ("normuon", ctypes.c_int32), ("normuon_beta2", ctypes.c_float),
+                ("adam_lr_scalar", ctypes.c_float)]
 
 
 class ParamInfoC(ctypes.Structure):
@@ -119,7 +123,14 @@ def model_cfg_c(cfg: ModelConfig, max_micro_batch=None):
     return ModelCfgC(cfg.n_layer, cfg.d_model, cfg.n_head, cfg.head_dim, cfg.d_ff, cfg.vocab,
                      cfg.seq_len, max_micro_batch or cfg.micro_batch,
                      NC_BF16 if cfg.dtype == "bf16" else NC_FP32, cfg.rope_base, cfg.norm_eps,
-                     cfg.n_kv_head, int(bool(cfg.fp8_forward)))
+                     cfg.n_kv_head, int(bool(cfg.fp8_forward)), features_of(cfg),
+                     cfg.ve_gate_channels)
+
+
+def features_of(cfg: ModelConfig):
+    return ((NC_FEAT_VALUE_EMBEDS if cfg.value_embeds else 0) |
+            (NC_FEAT_RESID_LAMBDAS if cfg.resid_lambdas else 0) |
+            (NC_FEAT_SMEAR if cfg.smear else 0) | (NC_FEAT_BACKOUT if cfg.backout else 0))
 
 
 def optim_cfg_c(o: OptimConfig):
@@ -135,6 +146,7 @@ def optim_cfg_c(o: OptimConfig):
     c.adam_lr_embed, c.adam_lr_head = o.adam_lr_embed, o.adam_lr_head
     c.adam_beta1, c.adam_beta2, c.adam_eps, c.adam_wd = o.adam_beta1, o.adam_beta2, o.adam_eps, o.adam_wd
     c.normuon, c.normuon_beta2 = int(bool(o.normuon)), o.normuon_beta2
+    c.adam_lr_scalar = o.adam_lr_scalar
     return c
 
 

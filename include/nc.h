@@ -76,7 +76,30 @@ typedef struct {
                               later runs train most linear layers in FP8 with tensorwise
                               scaling); the backward products stay bf16 and take the
                               unquantised operands.  NC_BF16 only. */
+  int32_t features;        /* bits of NC_FEAT_*: the further mechanisms of apidog.com,
+                              "1. Model GPT (nanochat/gpt.py)" (value-embedding listing and
+                              the three efficiency tricks); 0 = the plain model */
+  int32_t ve_gate_channels;/* channels of the value-embedding gate input (0 = 32;
+                              a multiple of 8, at most 64 and at most d_model) */
 } nc_model_config;
+
+/* Feature bits of nc_model_config.features.
+ * NC_FEAT_VALUE_EMBEDS: every other layer counted down from the last
+ *   (l = L-1, L-3, ...) has a table "ve.<l>" [vocab, n_kv_head*128] and a gate
+ *   "<l>.Wg" [n_kv_head, C]; v += 3 sigmoid(a[:, :C] Wg^T) ve.<l>[token] per
+ *   key/value head, a being the layer's first RMSNorm output.
+ * NC_FEAT_RESID_LAMBDAS: "resid_lambdas", "x0_lambdas" [1, n_layer]; layer i
+ *   starts from resid_lambdas[i] x + x0_lambdas[i] x0 (x0: the embedding output).
+ * NC_FEAT_SMEAR: "smear_gate" [1, 24], "smear_lambda" [1, 1]; the embedding
+ *   output is e_t + smear_lambda sigmoid(e_t[:24] . smear_gate) e_{t-1}.
+ * NC_FEAT_BACKOUT: "backout_lambda" [1, 1]; after the last layer
+ *   x <- x - backout_lambda xb, xb being the stream entering layer n_layer/2.
+ * Tables and scalars take AdamW (tables at adam_lr_embed, scalars at
+ * adam_lr_scalar), the gates take Muon.  nc_init_params sets resid_lambdas to
+ * 1 and the other scalars to 0 (the plain model plus value embeddings).
+ * Not combined with normuon (NC_ERR_UNSUPPORTED). */
+enum { NC_FEAT_VALUE_EMBEDS = 1, NC_FEAT_RESID_LAMBDAS = 2, NC_FEAT_SMEAR = 4,
+       NC_FEAT_BACKOUT = 8 };
 
 /* Optimizer settings.  Muon (per block matrix): M <- mu M + G;
  * X0 = U / (||U||_F + ns_eps) with U = M (or G + mu M if muon_nesterov);
@@ -100,6 +123,7 @@ typedef struct {
   float adam_lr_embed, adam_lr_head, adam_beta1, adam_beta2, adam_eps, adam_wd;
   int32_t normuon;
   float normuon_beta2;
+  float adam_lr_scalar;    /* AdamW learning rate of the scalar parameters (features) */
 } nc_optim_config;
 
 typedef struct nc_ctx nc_ctx;
@@ -111,7 +135,8 @@ enum { NC_PARAM = 0, NC_GRAD = 1, NC_MOMENTUM = 2, NC_ADAM_M = 3, NC_ADAM_V = 4 
 
 typedef struct {
   char name[32];           /* "E", "<layer>.Wq|Wk|Wv|Wo|W1|W2", "Wh" (a layer's six
-                              matrices are contiguous in this order) */
+                              matrices are contiguous in this order), then the
+                              feature parameters (see NC_FEAT_*) */
   int32_t rows, cols, group;
   int64_t param_offset;    /* byte offsets into the parameter arena (fp32) */
   int64_t grad_offset;

@@ -58,7 +58,7 @@ The rest of the pages' model ([APIDOG] "1. Model GPT (nanochat/gpt.py)",
 the "Value Embeddings (ResFormer)" and efficiency-trick listings), each
 switched on by a cfg flag; readings where the listings leave a step open:
 
-* value embeddings (cfg["value_embeds"]): "alternating layers" carry a
+* value embeddings (cfg["value_embeds"]): every second layer carries a
   learnable table VE_l [V, n_kv_head * hd] looked up by the input token ids,
   added to v through a per-(token, key/value head) gate
   g = 3 sigmoid(a[:, :C] Wg_l^T), Wg_l [n_kv_head, C] bias-free, where a is

@@ -100,21 +100,26 @@ SMALL_BF16 = dict(name="small", n_layer=2, d_model=384, n_head=3, head_dim=128, 
 
 
 @pytest.mark.parametrize("name", ["tiny", "small", "d12", "d20", "d24", "d26", "small_gqa",
-                                  "d20_gqa", "d26_gqa", "small_fp8", "d20_fp8", "d26_gqa_fp8"])
+                                  "d20_gqa", "d26_gqa", "small_fp8", "d20_fp8", "d26_gqa_fp8",
+                                  "tiny_feat", "small_feat", "d20_feat", "d20_gqa_feat",
+                                  "small_fp8_feat"])
 def test_every_launch_of_a_step_stays_inside_the_arenas(name):
     """Dry run of nc_fwd_bwd + nc_optimizer_step: every GEMM operand extent is
     checked against the planned arenas (no device access)."""
     from dataclasses import replace as dc_replace
     from gpt_pretraining_step_gemms_amd.configs import ModelConfig
-    base = name.replace("_gqa", "").replace("_fp8", "")
+    base = name.replace("_gqa", "").replace("_fp8", "").replace("_feat", "")
     cfg = ModelConfig(**SMALL_BF16) if base == "small" else CONFIGS[base]
     if "_gqa" in name:
         cfg = dc_replace(cfg, n_kv_head=1)
     if "_fp8" in name:
         cfg = dc_replace(cfg, fp8_forward=True)
+    if "_feat" in name:
+        cfg = dc_replace(cfg, value_embeds=True, resid_lambdas=True, smear=True, backout=True)
     lib = nc.load()
     for maxb, b in [(cfg.micro_batch, cfg.micro_batch), (cfg.micro_batch, 1), (1, 1)]:
-        m, o = nc.model_cfg_c(cfg, maxb), nc.optim_cfg_c(OptimConfig(normuon=True))
+        o = nc.optim_cfg_c(OptimConfig(normuon="_feat" not in name))
+        m = nc.model_cfg_c(cfg, maxb)
         ctx = ctypes.c_void_p()
         assert lib.nc_create(ctypes.byref(m), ctypes.byref(o), ctypes.byref(ctx)) == nc.NC_OK
         try:
@@ -157,6 +162,66 @@ def test_parameter_registry_matches_model_shapes():
         assert fb.value == pytest.approx(6 * 32 * T * (12 * L * d * d + V * d) + 6 * 32 * T * L * d * T)
     finally:
         lib.nc_destroy(ctx)
+
+
+@pytest.mark.parametrize("n_kv,cg", [(0, 32), (2, 8), (1, 64)])
+def test_feature_parameter_registry_matches_model_shapes(n_kv, cg):
+    """Value embeddings, residual/x0 lambdas, smear and backout: the registry
+    lists the oracle's parameters with its shapes, every span inside the
+    parameter arena without overlap, the gates in the Muon group next to the
+    block matrices and the tables and scalars in the AdamW group; the FLOP
+    count of the products is that of the plain model."""
+    from dataclasses import replace as dc_replace
+    lib = nc.load()
+    plain = dc_replace(from_depth(12, micro_batch=1, accum_steps=1), n_kv_head=n_kv)
+    cfg = dc_replace(plain, value_embeds=True, resid_lambdas=True, smear=True, backout=True,
+                     ve_gate_channels=cg)
+    m, o = nc.model_cfg_c(cfg), nc.optim_cfg_c(OptimConfig())
+    ctx = ctypes.c_void_p()
+    assert lib.nc_create(ctypes.byref(m), ctypes.byref(o), ctypes.byref(ctx)) == nc.NC_OK
+    try:
+        n = ctypes.c_int32()
+        lib.nc_param_count(ctx, ctypes.byref(n))
+        infos = []
+        for i in range(n.value):
+            info = nc.ParamInfoC()
+            assert lib.nc_param_desc(ctx, i, ctypes.byref(info)) == nc.NC_OK
+            infos.append(info)
+        shapes = {i.name.decode(): (i.rows, i.cols) for i in infos}
+        assert shapes == param_shapes(cfg.as_oracle_cfg())
+        assert shapes["11.Wg"] == (cfg.kv_heads, cg) and "10.Wg" not in shapes
+        assert shapes["smear_gate"] == (1, 24) and shapes["resid_lambdas"] == (1, 12)
+        pb, _ = nc.plan(cfg)
+        spans = sorted((i.param_offset, i.param_offset + 4 * i.rows * i.cols) for i in infos)
+        assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
+        assert spans[-1][1] <= pb
+        groups = {i.name.decode(): i.group for i in infos}
+        for k, g in groups.items():
+            adam = k in ("E", "Wh", "resid_lambdas", "x0_lambdas", "smear_lambda",
+                         "backout_lambda") or k.startswith("ve.")
+            assert g == (0 if adam else 1), (k, g)
+        fb, opt = ctypes.c_double(), ctypes.c_double()
+        lib.nc_flops(ctx, 1, ctypes.byref(fb), ctypes.byref(opt))
+        mp = nc.model_cfg_c(plain)
+        ctx2 = ctypes.c_void_p()
+        assert lib.nc_create(ctypes.byref(mp), ctypes.byref(o), ctypes.byref(ctx2)) == nc.NC_OK
+        fb2 = ctypes.c_double()
+        lib.nc_flops(ctx2, 1, ctypes.byref(fb2), ctypes.byref(opt))
+        lib.nc_destroy(ctx2)
+        assert fb.value == fb2.value
+    finally:
+        lib.nc_destroy(ctx)
+    bad = [(dict(ve_gate_channels=12), nc.NC_ERR_UNSUPPORTED),
+           (dict(ve_gate_channels=72), nc.NC_ERR_UNSUPPORTED),
+           (dict(ve_gate_channels=-8), nc.NC_ERR_INVALID_ARG)]
+    for b, err in bad:
+        mb = nc.model_cfg_c(dc_replace(cfg, **b))
+        ctx = ctypes.c_void_p()
+        assert lib.nc_create(ctypes.byref(mb), ctypes.byref(o), ctypes.byref(ctx)) == err
+    # the NorMuon option does not cover the gate groups
+    on = nc.optim_cfg_c(OptimConfig(normuon=True))
+    ctx = ctypes.c_void_p()
+    assert lib.nc_create(ctypes.byref(m), ctypes.byref(on), ctypes.byref(ctx)) != nc.NC_OK
 
 
 def test_grouped_query_registry_and_flops():

@@ -56,10 +56,13 @@ def run_gpu(m, tok, tgt, grad_scale=1.0):
     return float(loss.item()), {n: m.get(n, nc.NC_GRAD) for n in m.names()}
 
 
-def check_step(cfg, B, seed=0, windows=None, ocfg=None):
-    tol_l, tol_c, tol_r = TOL["fp8" if cfg.fp8_forward else cfg.dtype]
+def check_step(cfg, B, seed=0, windows=None, ocfg=None, prep=None, tol=None):
+    tol_l, tol_c, tol_r = tol or TOL["fp8" if cfg.fp8_forward else cfg.dtype]
     ocfg = ocfg or OptimConfig()
     m, params, tok, tgt = setup(cfg, B, seed, ocfg)
+    if prep is not None:
+        params = prep(params, seed)
+        m.set_params(params)
     print(f"[parity] {cfg.name} B={B} seed={seed} windows={windows}", flush=True)
     ocfg_model = cfg.as_oracle_cfg()
     if windows is not None:
@@ -314,6 +317,119 @@ def test_accumulation_matches_large_batch_and_is_deterministic(cfg):
     losses = []
     for r in range(2):
         losses.append(float(m.fwd_bwd(gpu_tokens(tok[r:r + 1]), gpu_tokens(tgt[r:r + 1]), 0.5).item()))
+    torch.cuda.synchronize()
+    assert 0.5 * sum(losses) == pytest.approx(loss_full, rel=1e-5)
+    tol_c = 1 - 1e-10 if cfg.dtype == "fp32" else 0.9999
+    for n in g_full:
+        g_acc = m.get(n, nc.NC_GRAD)
+        assert cosine(g_acc, g_full[n]) >= tol_c, n
+        assert max_rel(g_acc, g_full[n]) <= (1e-5 if cfg.dtype == "fp32" else 2e-2), n
+    m.close()
+
+
+# ---------------------------------------------------------------------------
+# value embeddings, residual/x0 lambdas, smear and backout
+
+ALL_FEATURES = dict(value_embeds=True, resid_lambdas=True, smear=True, backout=True)
+
+
+def feature_params(params, seed):
+    """Scalars away from their identity values and gate weights large enough
+    that the sigmoids leave their midpoint, so that every term of the
+    mechanisms carries weight in the loss and in the gradients."""
+    rng = np.random.default_rng(seed + 100)
+    out = dict(params)
+    if "resid_lambdas" in out:
+        out["resid_lambdas"] = (1.0 + 0.3 * rng.standard_normal(out["resid_lambdas"].shape)).astype(np.float32)
+        out["x0_lambdas"] = (0.5 * rng.standard_normal(out["x0_lambdas"].shape)).astype(np.float32)
+    if "smear_lambda" in out:
+        out["smear_lambda"] = np.full((1, 1), 0.8, np.float32)
+        out["smear_gate"] = (0.3 * rng.standard_normal((1, 24))).astype(np.float32)
+    if "backout_lambda" in out:
+        out["backout_lambda"] = np.full((1, 1), 0.4, np.float32)
+    for n in out:
+        if n.endswith(".Wg"):
+            out[n] = (0.3 * rng.standard_normal(out[n].shape)).astype(np.float32)
+        if n.startswith("ve."):
+            out[n] = (0.5 * rng.standard_normal(out[n].shape)).astype(np.float32)
+    return out
+
+
+TINY_FEAT = replace(TINY, name="tiny_feat", n_layer=4, **ALL_FEATURES)
+FEATURE_CASES = {
+    "tiny_all": TINY_FEAT,
+    "tiny_ve": replace(TINY, n_layer=3, value_embeds=True),
+    "tiny_resid": replace(TINY, n_layer=3, resid_lambdas=True),
+    "tiny_smear": replace(TINY, n_layer=3, smear=True),
+    "tiny_backout": replace(TINY, n_layer=3, backout=True),
+    # 9 key/value heads over 8 gate channels: the gate matrices are wider than
+    # tall, so Muon orthogonalises their transposes
+    "tiny_heads9_cg8": ModelConfig(name="tiny_heads9", n_layer=2, d_model=1152, n_head=9,
+                                   head_dim=128, d_ff=512, vocab=512, seq_len=64,
+                                   micro_batch=1, accum_steps=1, dtype="fp32",
+                                   token_dist="uniform", ve_gate_channels=8, **ALL_FEATURES),
+    "tiny_gqa_all": replace(TINY_GQA, n_layer=3, **ALL_FEATURES),
+    "small_all": replace(SMALL_BF16, n_layer=3, **ALL_FEATURES),
+    "small_fp8_all": replace(SMALL_BF16, n_layer=3, fp8_forward=True, **ALL_FEATURES),
+    "d12_all": replace(with_batch(D12, micro_batch=1), **ALL_FEATURES),
+}
+
+
+@pytest.mark.parametrize("name", list(FEATURE_CASES))
+def test_model_features_full_step(name):
+    """Loss, every gradient (block matrices, embedding and value-embedding
+    tables, gates, lambdas) and every update against the fp64 oracle with the
+    mechanisms switched on, alone and together."""
+    cfg = FEATURE_CASES[name]
+    # fp32 at d = 1152: the Newton-Schulz products sum over K = 1152, and the
+    # polynomial's slope near zero (8.2 for the first row) amplifies their
+    # rounding on the small singular values, so the fp32 update bound is
+    # raised from 1e-4 to 5e-4 (measured 1.4e-4 on 0.Wk; gradients stay
+    # within the plain fp32 bounds)
+    tol = (1e-4, 1 - 1e-8, 5e-4) if name == "tiny_heads9_cg8" else None
+    check_step(cfg, B=min(cfg.micro_batch, 2), seed=61, prep=feature_params, tol=tol)
+
+
+@pytest.mark.parametrize("cfg", [TINY, SMALL_BF16])
+def test_features_at_identity_values_reproduce_the_plain_model(cfg):
+    """Residual lambdas 1, x0 lambdas 0, smear and backout lambdas 0 and
+    zero value-embedding tables leave the plain model: same loss, same
+    gradients of every shared parameter."""
+    mp, params, tok, tgt = setup(cfg, B=2, seed=5)
+    loss_p, g_p = run_gpu(mp, tok, tgt)
+    mp.close()
+    fcfg = replace(cfg, **ALL_FEATURES)
+    mf = nc.Model(fcfg, OptimConfig(), max_micro_batch=2)
+    full = dict(params)
+    for n, (r, c) in mf.shapes().items():
+        if n not in full:
+            full[n] = np.zeros((r, c), np.float32)
+    full["resid_lambdas"] = np.ones_like(full["resid_lambdas"])
+    mf.set_params(full)
+    loss_f, g_f = run_gpu(mf, tok, tgt)
+    tol = 1e-6 if cfg.dtype == "fp32" else 2e-3
+    assert loss_f == pytest.approx(loss_p, rel=tol)
+    for n in g_p:
+        assert cosine(g_f[n], g_p[n]) >= 1 - tol, n
+        assert max_rel(g_f[n], g_p[n]) <= 50 * tol, n
+    mf.close()
+
+
+@pytest.mark.parametrize("cfg", [TINY_FEAT, replace(SMALL_BF16, **ALL_FEATURES)])
+def test_features_accumulate_over_micro_batches(cfg):
+    """Gradients of the feature parameters accumulate across micro-batches
+    like the rest: two rows one at a time at scale 1/2 equal both at once,
+    and a repeated step is bitwise identical."""
+    m, params, tok, tgt = setup(cfg, B=2, seed=7)
+    m.set_params(feature_params(params, 7))
+    loss_full, g_full = run_gpu(m, tok, tgt)
+    loss_again, g_again = run_gpu(m, tok, tgt)
+    assert loss_full == loss_again
+    for n in g_full:
+        assert np.array_equal(g_full[n], g_again[n]), n
+    m.zero_grads()
+    losses = [float(m.fwd_bwd(gpu_tokens(tok[r:r + 1]), gpu_tokens(tgt[r:r + 1]), 0.5).item())
+              for r in range(2)]
     torch.cuda.synchronize()
     assert 0.5 * sum(losses) == pytest.approx(loss_full, rel=1e-5)
     tol_c = 1 - 1e-10 if cfg.dtype == "fp32" else 0.9999
