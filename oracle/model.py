@@ -51,7 +51,15 @@ Readings where the pages are silent:
   the bf16 configuration, whose activations and weight copies are bf16), one
   scale per tensor (oracle.fp8), and the
   backward treats the rounding as the identity (gradients with the
-  unrounded operands).  The lm_head and every backward product are exact.
+  unrounded operands).  The lm_head is exact.
+* FP8 backward products (cfg["fp8_backward"], the same passage: the
+  reading takes "most linear layers" to cover their backward products
+  too): the input gradient dX = dY W and the weight gradient dW = dY^T X of
+  each of the four block products use the e5m2 values of the bf16 gradient
+  dY (one scale per tensor; the fused QKV gradient [dq | dk | dv] is one
+  tensor) and the e4m3 values of the bf16 copies of X and W, the operands
+  the forward products quantise.  Everything else in the backward (norms,
+  attention, the ReLU^2 derivative, the lm_head) stays exact.
 * Loss: natural log, mean over every position, no ignore index.
 
 The rest of the pages' model ([APIDOG] "1. Model GPT (nanochat/gpt.py)",
@@ -253,6 +261,24 @@ def _fp8_linear(x, W):
     return y.reshape(*x.shape[:-1], W.shape[0])
 
 
+def _fp8_backward_pair(dY, X, W):
+    """(dX, dW) of y = x W^T with dY in e5m2 and X, W in e4m3 (tensorwise
+    scales, codes decided on the bf16 values): dX = dY W, dW = dY^T X."""
+    from . import fp8
+    out, inp = W.shape
+    d = fp8.dequantized(fp8.bf16_round(dY.reshape(-1, out)), fp8.E5M2)
+    x = fp8.dequantized(fp8.bf16_round(X.reshape(-1, inp)), fp8.E4M3)
+    w = fp8.dequantized(fp8.bf16_round(W), fp8.E4M3)
+    return (d @ w).reshape(*dY.shape[:-1], inp), d.T @ x
+
+
+def _grad_pair(dY, X, W, cfg):
+    """Input and weight gradients of y = x W^T."""
+    if cfg.get("fp8_backward"):
+        return _fp8_backward_pair(dY, X, W)
+    return dY @ W, _sum_outer(dY, X)
+
+
 def _linear(x, W, cfg):
     return _fp8_linear(x, W) if cfg.get("fp8_forward") else x @ W.T
 
@@ -430,15 +456,13 @@ def loss_and_grads(params, tokens, targets, cfg, grad_scale=1.0):
         L = c["layers"][i]
         nWq, nWk, nWv, nWo, nW1, nW2 = _layer_names(i)
         # MLP: x += max(h,0)^2 W2^T, h = m W1^T, m = N(x)
-        grads[nW2] = _sum_outer(dx, L["g"])
-        dg = dx @ P[nW2]
+        dg, grads[nW2] = _grad_pair(dx, L["g"], P[nW2], cfg)
         dh = 2.0 * np.maximum(L["h"], 0.0) * dg
-        grads[nW1] = _sum_outer(dh, L["m"])
-        dm = dh @ P[nW1]
+        dm, grads[nW1] = _grad_pair(dh, L["m"], P[nW1], cfg)
         dx = dx + rmsnorm_backward(dm, L["m"], L["r2"])
         # attention: x += o Wo^T
-        grads[nWo] = _sum_outer(dx, L["o"])
-        do = _split_heads(dx @ P[nWo], cfg["n_head"])
+        do, grads[nWo] = _grad_pair(dx, L["o"], P[nWo], cfg)
+        do = _split_heads(do, cfg["n_head"])
         dqr, dkr, dv = causal_attention_backward(L["qr"], _repeat_kv(L["kr"], group),
                                                  _repeat_kv(L["v"], group), do, windows[i])
         dkr, dv = _sum_groups(dkr, group), _sum_groups(dv, group)
@@ -457,10 +481,18 @@ def loss_and_grads(params, tokens, targets, cfg, grad_scale=1.0):
         dq = rmsnorm_backward(rope_inverse(dqr, cos, sin), L["qn"], L["rq"])
         dk = rmsnorm_backward(rope_inverse(dkr, cos, sin), L["kn"], L["rk"])
         dq, dk, dv = _merge_heads(dq), _merge_heads(dk), _merge_heads(dv)
-        grads[nWq] = _sum_outer(dq, L["a"])
-        grads[nWk] = _sum_outer(dk, L["a"])
-        grads[nWv] = _sum_outer(dv, L["a"])
-        da = dq @ P[nWq] + dk @ P[nWk] + dv @ P[nWv]
+        if cfg.get("fp8_backward"):         # the fused QKV product: one tensor each side
+            d_model, dkv = dq.shape[-1], dk.shape[-1]
+            da, dWqkv = _fp8_backward_pair(np.concatenate([dq, dk, dv], axis=-1), L["a"],
+                                           np.concatenate([P[nWq], P[nWk], P[nWv]], axis=0))
+            grads[nWq] = dWqkv[:d_model]
+            grads[nWk] = dWqkv[d_model:d_model + dkv]
+            grads[nWv] = dWqkv[d_model + dkv:]
+        else:
+            grads[nWq] = _sum_outer(dq, L["a"])
+            grads[nWk] = _sum_outer(dk, L["a"])
+            grads[nWv] = _sum_outer(dv, L["a"])
+            da = dq @ P[nWq] + dk @ P[nWk] + dv @ P[nWv]
         if da_gate is not None:
             da[..., :Cg] += da_gate
         dx = dx + rmsnorm_backward(da, L["a"], L["r1"])

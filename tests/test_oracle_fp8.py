@@ -118,3 +118,114 @@ def test_bf16_round_known_values_and_ties():
     y = r(x)
     assert np.all(np.abs(y - x) <= 2.0 ** -8 * np.abs(x) * (1 + 1e-6))   # unit roundoff 2^-8
     assert np.all(np.ascontiguousarray(y.astype(np.float32)).view(np.uint32) & 0xFFFF == 0)
+
+
+# ------------------------------------------------------------------ e5m2
+def test_e5m2_known_codes():
+    t = fp8.e5m2_decode_table()
+    assert t[0x3C] == 1.0 and t[0x3E] == 1.5 and t[0x3A] == 0.75 and t[0xC0] == -2.0
+    assert t[0x7B] == 57344.0                       # largest finite: 1.75 * 2^15
+    assert t[0x01] == 2.0 ** -16 and t[0x04] == 2.0 ** -14   # smallest subnormal, normal
+    assert np.isinf(t[0x7C]) and np.isinf(t[0xFC]) and t[0xFC] < 0
+    assert all(np.isnan(t[c]) for c in (0x7D, 0x7E, 0x7F, 0xFD, 0xFE, 0xFF))
+    enc = fp8.e5m2_encode
+    assert enc(1.125) == 0x3C                       # halfway 1 / 1.25: the even code
+    assert enc(1.375) == 0x3E                       # halfway 1.25 / 1.5: the even code
+    assert enc(2.0 ** -17) == 0x00 and enc(1.5 * 2.0 ** -17) == 0x01
+    assert enc(6.0e4) == 0x7B and enc(-1.0e9) == 0xFB   # saturation, no infinity
+    assert enc(-0.0) == 0x80 and enc(np.nan) == 0x7F
+
+
+def test_e5m2_round_trip_of_every_finite_value():
+    codes = np.array([c for c in range(256) if np.isfinite(fp8.e5m2_decode_table()[c])],
+                     np.uint8)
+    np.testing.assert_array_equal(fp8.e5m2_encode(fp8.e5m2_decode(codes)), codes)
+
+
+def test_e5m2_is_fp16_rounded_to_its_top_byte():
+    # e5m2 has fp16's sign and exponent fields with its two top mantissa bits, so
+    # for fp16 inputs its code is the fp16 bit pattern rounded to nearest even on
+    # bit 8 (saturated at the largest finite code): an encoder built on bits,
+    # independent of the table search
+    rng = np.random.default_rng(7)
+    h = rng.integers(0, 0x7C00, 200000).astype(np.uint16)      # finite magnitudes
+    h |= (rng.integers(0, 2, h.size) << 15).astype(np.uint16)   # signs
+    x = h.view(np.float16).astype(np.float64)
+    mag = (h & 0x7FFF).astype(np.uint32)
+    r = (mag + 0x7F + ((mag >> 8) & 1)) >> 8
+    r = np.minimum(r, 0x7B)
+    ref = (r | ((h >> 15).astype(np.uint32) << 7)).astype(np.uint8)
+    np.testing.assert_array_equal(fp8.e5m2_encode(x), ref)
+
+
+def test_e5m2_tensorwise_scale_maps_amax_to_57344():
+    x = np.random.default_rng(2).standard_normal((40, 30)) * 1e-6
+    codes, amax, scale = fp8.quantize_tensorwise(x, fp8.E5M2)
+    assert scale == np.float32(57344.0) / np.float32(amax)
+    assert np.max(np.abs(fp8.e5m2_decode(codes))) == 57344.0
+    v = fp8.e5m2_decode(codes) / scale
+    assert np.all(np.abs(v - x) <= 2.0 ** -3 * np.abs(x) + 2.0 ** -16 / scale)  # 2 mantissa bits
+
+
+def test_fp8_backward_pair_is_exact_for_representable_operands():
+    # dY: max 1.75 * 2^3 = 14 -> e5m2 scale 57344 / 14 = 2^12 exactly; it also holds
+    # 2^-16, which e5m2 keeps (2^-4 after scaling) and e4m3 would flush (scale
+    # 448 / 14 = 32 takes it to 2^-11, under half its smallest code 2^-9): a
+    # swapped format fails.  X: max 3.5 -> e4m3 scale 128; W: max 1.75 -> 256.
+    from oracle.model import _fp8_backward_pair
+    rng = np.random.default_rng(5)
+    dY = rng.choice([-1.5, -1.0, -0.5, 0.0, 0.75, 1.25, 2.0], size=(2, 6, 8))
+    dY[0, 0, 0], dY[1, 2, 3] = 14.0, 2.0 ** -16
+    X = rng.choice([-3.5, -1.0, -0.25, 0.0, 0.5, 1.5], size=(2, 6, 5))
+    X[0, 1, 1] = 3.5
+    W = rng.choice([-1.75, -0.5, 0.125, 1.0], size=(8, 5))
+    W[0, 0] = 1.75
+    dX, dW = _fp8_backward_pair(dY, X, W)
+    np.testing.assert_array_equal(dX, dY @ W)
+    np.testing.assert_array_equal(dW, dY.reshape(-1, 8).T @ X.reshape(-1, 5))
+    # the same tensor read as e4m3 loses the 2^-16 entry
+    v4 = fp8.dequantized(dY.reshape(-1, 8), fp8.E4M3)
+    assert v4.reshape(dY.shape)[1, 2, 3] == 0.0
+
+
+def _small_model(seed=0):
+    from oracle.model import param_shapes
+    from gpt_pretraining_step_gemms_amd import synthetic
+    cfg = dict(n_layer=2, d_model=32, n_head=2, head_dim=16, d_ff=128, vocab=64, seq_len=8,
+               rope_base=10000.0, norm_eps=1e-6)
+    params = {k: v.astype(np.float64) for k, v in
+              synthetic.normal_params(seed, param_shapes(cfg), 0.3).items()}
+    tok, tgt = synthetic.token_rows(seed + 1, 2, 8, 64, "uniform")
+    return cfg, params, tok, tgt
+
+
+def test_fp8_backward_leaves_the_loss_and_head_and_stays_close():
+    # the backward products do not touch the forward or the lm_head: loss, dWh
+    # and (through the final norm) nothing else is shared exactly; every block
+    # gradient keeps its direction under e5m2 gradients (2 mantissa bits)
+    import oracle
+    cfg, params, tok, tgt = _small_model()
+    f8 = dict(cfg, fp8_forward=True)
+    l0, g0 = oracle.loss_and_grads(params, tok, tgt, f8)
+    l1, g1 = oracle.loss_and_grads(params, tok, tgt, dict(f8, fp8_backward=True))
+    assert l0 == l1
+    np.testing.assert_array_equal(g0["Wh"], g1["Wh"])
+    for n in g0:
+        a, b = g0[n].ravel(), g1[n].ravel()
+        c = a @ b / (np.linalg.norm(a) * np.linalg.norm(b))
+        if n == "Wh":
+            continue
+        assert 0.9 < c < 1.0, (n, c)       # changed, but in the same direction
+
+
+def test_fp8_backward_scales_exactly_with_a_power_of_two_loss_scale():
+    # tensorwise scales follow the tensor: multiplying the loss by 2^k multiplies
+    # every dY by 2^k, its amax too, so the codes are unchanged and every
+    # gradient scales by exactly 2^k
+    import oracle
+    cfg, params, tok, tgt = _small_model(3)
+    c8 = dict(cfg, fp8_forward=True, fp8_backward=True)
+    _, g1 = oracle.loss_and_grads(params, tok, tgt, c8)
+    _, g8 = oracle.loss_and_grads(params, tok, tgt, c8, grad_scale=8.0)
+    for n in g1:
+        np.testing.assert_array_equal(g8[n], 8.0 * g1[n], err_msg=n)
