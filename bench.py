@@ -42,6 +42,9 @@ def parse():
                     help="key/value heads for grouped-query attention (default: one per head)")
     ap.add_argument("--fp8-forward", action="store_true",
                     help="forward block products in fp8 e4m3 (tensorwise scales; backward bf16)")
+    ap.add_argument("--fp8-backward", action="store_true",
+                    help="with --fp8-forward: the backward block products in fp8 too "
+                         "(gradients e5m2)")
     ap.add_argument("--model-features", default="",
                     help='comma list of the further model mechanisms: ve (value embeddings), '
                          'resid (residual/x0 lambdas), smear, backout; or "all"')
@@ -255,7 +258,10 @@ def main():
     if args.kv_heads:
         cfg = dc_replace(cfg, n_kv_head=args.kv_heads)
     if args.fp8_forward:
-        cfg = dc_replace(cfg, fp8_forward=True)
+        cfg = dc_replace(cfg, fp8_forward=True, fp8_backward=args.fp8_backward)
+    elif args.fp8_backward:
+        print("bench.py: --fp8-backward needs --fp8-forward", file=sys.stderr)
+        sys.exit(2)
     feats = {f.strip() for f in args.model_features.split(",") if f.strip()}
     if "all" in feats:
         feats = {"ve", "resid", "smear", "backout"}
@@ -357,6 +363,7 @@ def main():
                                f"{cfg.n_head}x128 heads"
                                f"{f' over {cfg.kv_heads} key/value heads' if cfg.kv_heads != cfg.n_head else ''}"
                                f"{', forward block products in fp8 e4m3' if cfg.fp8_forward else ''}"
+                               f"{', backward block products in fp8 (gradients e5m2)' if cfg.fp8_backward else ''}"
                                f"{feature_text(cfg)}"
                                f", {attention}, MLP {cfg.d_ff} ReLU^2, "
                                f"vocab {cfg.vocab}, "

@@ -42,6 +42,7 @@ class ModelConfig:
     init_std: float = 0.02
     n_kv_head: int = 0    # key/value heads for grouped-query attention (0: n_head)
     fp8_forward: bool = False   # forward block products in fp8 e4m3, tensorwise scales
+    fp8_backward: bool = False  # and their backward products (gradients e5m2)
     # the pages' further model mechanisms (off in the benchmark configurations)
     value_embeds: bool = False  # gated value embeddings on every other layer
     resid_lambdas: bool = False # per-layer scaling of the stream and of the embedding output
@@ -58,6 +59,7 @@ class ModelConfig:
                     head_dim=self.head_dim, d_ff=self.d_ff, vocab=self.vocab,
                     seq_len=self.seq_len, rope_base=self.rope_base, norm_eps=self.norm_eps,
                     n_kv_head=self.kv_heads, fp8_forward=self.fp8_forward,
+                    fp8_backward=self.fp8_backward,
                     value_embeds=self.value_embeds, resid_lambdas=self.resid_lambdas,
                     smear=self.smear, backout=self.backout,
                     ve_gate_channels=self.ve_gate_channels)

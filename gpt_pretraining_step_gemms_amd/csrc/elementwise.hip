@@ -752,7 +752,7 @@ inline int grid1d(size_t n, int block = 256) {
 }
 
 
-// ------------------------------------------------ fp8 e4m3, tensorwise scale
+// ------------------------------------- fp8 (e4m3, e5m2), tensorwise scale
 // The maximum that keeps a NaN (fmaxf drops it): a NaN anywhere in a tensor
 // makes its amax and scale NaN, and with them every code (0x7F).
 NC_DEV float max_nan(float a, float b) { return (a > b || a != a) ? a : b; }
@@ -780,9 +780,10 @@ __global__ __launch_bounds__(256) void amax_partial_kernel(const T* __restrict__
   if (threadIdx.x == 0) partial[blockIdx.x] = m;
 }
 
-// amax_scale[0] = amax, amax_scale[1] = 448 / amax (1 when amax is 0)
+// amax_scale[0] = amax, amax_scale[1] = fmax / amax (1 when amax is 0); fmax is
+// the format's largest finite value (448 for e4m3, 57344 for e5m2)
 __global__ __launch_bounds__(256) void amax_final_kernel(const float* __restrict__ partial,
-                                                         int parts,
+                                                         int parts, float fmax,
                                                          float* __restrict__ amax_scale) {
   __shared__ float red[4];
   float m = 0.f;
@@ -790,26 +791,48 @@ __global__ __launch_bounds__(256) void amax_final_kernel(const float* __restrict
   m = block_max_nan(m, red);
   if (threadIdx.x == 0) {
     amax_scale[0] = m;
-    amax_scale[1] = m != m ? m : (m > 0.f ? 448.f / m : 1.f);
+    amax_scale[1] = m != m ? m : (m > 0.f ? fmax / m : 1.f);
   }
 }
 
-// OCP fp8 e4m3 (bias 7, 3 mantissa bits, largest finite 448, no infinities),
-// round to nearest even, saturating at 448; NaN is code 0x7F
-NC_DEV unsigned e4m3_rne(float x) {
+// OCP fp8, round to nearest even, saturating at the largest finite value;
+// NaN is code 0x7F.  FMT 0: e4m3 (bias 7, 3 mantissa bits, largest 448, no
+// infinities); FMT 1: e5m2 (bias 15, 2 mantissa bits, largest 57344; the
+// infinity codes are never produced).
+template <int FMT>
+struct Fp8Fmt;
+template <>
+struct Fp8Fmt<0> {
+  static constexpr int MB = 3, BIAS = 7;
+  static constexpr unsigned MAXC = 0x7Eu;
+  static constexpr float MAXV = 448.f, MINN = 0x1p-6f, SUB = 0x1p9f;
+};
+template <>
+struct Fp8Fmt<1> {
+  static constexpr int MB = 2, BIAS = 15;
+  static constexpr unsigned MAXC = 0x7Bu;
+  static constexpr float MAXV = 57344.f, MINN = 0x1p-14f, SUB = 0x1p16f;
+};
+
+template <int FMT>
+NC_DEV unsigned fp8_rne(float x) {
+  using F = Fp8Fmt<FMT>;
+  constexpr float M1 = (float)(1 << F::MB);
   if (x != x) return 0x7Fu;
   const unsigned sign = (__float_as_uint(x) >> 24) & 0x80u;
-  const float a = fminf(fabsf(x), 448.f);
-  if (!(a >= 0x1p-6f)) return sign | (unsigned)rintf(a * 512.f);   // multiples of 2^-9
+  const float a = fminf(fabsf(x), F::MAXV);
+  // subnormals: multiples of the smallest step (2^-9 or 2^-16); rounding up to
+  // the first normal gives its code
+  if (!(a >= F::MINN)) return sign | (unsigned)rintf(a * F::SUB);
   int e;
   const float f = frexpf(a, &e);                 // a = f 2^e, f in [0.5, 1)
-  float m = rintf((2.f * f - 1.f) * 8.f);        // a = (1 + m/8) 2^(e-1)
-  int E = e - 1 + 7;
-  if (m >= 8.f) {
+  float m = rintf((2.f * f - 1.f) * M1);         // a = (1 + m / 2^MB) 2^(e-1)
+  int E = e - 1 + F::BIAS;
+  if (m >= M1) {
     m = 0.f;
     E += 1;
   }
-  const unsigned code = min(((unsigned)E << 3) | (unsigned)m, 0x7Eu);
+  const unsigned code = min(((unsigned)E << F::MB) | (unsigned)m, F::MAXC);
   return sign | code;
 }
 
@@ -832,6 +855,7 @@ __global__ __launch_bounds__(256) void amax_partial_bf16x8_kernel(const bf16* __
   if (threadIdx.x == 0) partial[blockIdx.x] = m;
 }
 
+template <int FMT>
 __global__ __launch_bounds__(256) void fp8_quantize_bf16x8_kernel(
     const bf16* __restrict__ x, int64_t n, const float* __restrict__ amax_scale,
     uint8_t* __restrict__ q) {
@@ -842,22 +866,61 @@ __global__ __launch_bounds__(256) void fp8_quantize_bf16x8_kernel(
     unsigned lo = 0, hi = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      lo |= e4m3_rne(static_cast<float>(v[e]) * sc) << (8 * e);
-      hi |= e4m3_rne(static_cast<float>(v[e + 4]) * sc) << (8 * e);
+      lo |= fp8_rne<FMT>(static_cast<float>(v[e]) * sc) << (8 * e);
+      hi |= fp8_rne<FMT>(static_cast<float>(v[e + 4]) * sc) << (8 * e);
     }
     *reinterpret_cast<uint2*>(q + 8 * i) = make_uint2(lo, hi);
   }
   for (int64_t i = 8 * n8 + (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
-    q[i] = (uint8_t)e4m3_rne(static_cast<float>(x[i]) * sc);
+    q[i] = (uint8_t)fp8_rne<FMT>(static_cast<float>(x[i]) * sc);
 }
 
-template <typename T>
+template <typename T, int FMT>
 __global__ __launch_bounds__(256) void fp8_quantize_kernel(const T* __restrict__ x, int64_t n,
                                                            const float* __restrict__ amax_scale,
                                                            uint8_t* __restrict__ q) {
   const float sc = amax_scale[1];
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-    q[i] = (uint8_t)e4m3_rne(to_f(x[i]) * sc);
+    q[i] = (uint8_t)fp8_rne<FMT>(to_f(x[i]) * sc);
+}
+
+// bf16 x [R, C] (row stride C) in 64 x 64 tiles: the codes in x's layout
+// (q [R, C], if given) and transposed (qt [C, R], if given).  A thread codes 2
+// x 8 consecutive values of a row (8-byte stores to q) and drops each code into
+// an LDS tile kept column-major, so that the transposed rows leave as 16-byte
+// stores: thread t writes rows 16 (t % 4) .. +15 of column t / 4.  The four
+// 16-row chunks of column c sit in the order chunk ^ ((c >> 3) & 3), which
+// spreads one byte-store instruction's 64 lanes over 16 banks instead of 2.
+template <int FMT>
+__global__ __launch_bounds__(256) void fp8_quantize_2d_kernel(
+    const bf16* __restrict__ x, int R, int C, const float* __restrict__ amax_scale,
+    uint8_t* __restrict__ q, uint8_t* __restrict__ qt) {
+  constexpr int LDT = 80;                        // bytes per LDS column (64 + 16 padding)
+  __shared__ __attribute__((aligned(16))) uint8_t tile[64 * LDT];
+  const int tiles_c = C / 64;
+  const int r0 = (blockIdx.x / tiles_c) * 64, c0 = (blockIdx.x % tiles_c) * 64;
+  const float sc = amax_scale[1];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int id = threadIdx.x + 256 * i;         // 512 chunks of 8 values
+    const int r = id >> 3, cc = (id & 7) * 8;
+    const int64_t off = (int64_t)(r0 + r) * C + c0 + cc;
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(x + off);
+    unsigned lo = 0, hi = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const unsigned code = fp8_rne<FMT>(static_cast<float>(v[e]) * sc);
+      if (e < 4) lo |= code << (8 * e); else hi |= code << (8 * (e - 4));
+      const int c = cc + e;
+      tile[c * LDT + ((((r >> 4) ^ (c >> 3)) & 3) << 4) + (r & 15)] = (uint8_t)code;
+    }
+    if (q) *reinterpret_cast<uint2*>(q + off) = make_uint2(lo, hi);
+  }
+  if (!qt) return;
+  __syncthreads();
+  const int c = threadIdx.x >> 2, rr = (threadIdx.x & 3) * 16;
+  const uint4 t = *reinterpret_cast<const uint4*>(tile + c * LDT + ((((rr >> 4) ^ (c >> 3)) & 3) << 4));
+  *reinterpret_cast<uint4*>(qt + (int64_t)(c0 + c) * R + r0 + rr) = t;
 }
 }  // namespace
 
@@ -1110,10 +1173,17 @@ hipError_t nc_normuon_stats(const float* X, int64_t x_stride, int R, int C, int 
   return hipGetLastError();
 }
 
-hipError_t nc_fp8_quantize(int dtype, const void* x, int64_t n, float* partial,
-                           float* amax_scale, uint8_t* q, hipStream_t st) {
-  const bool vec = dtype && (reinterpret_cast<uintptr_t>(x) & 15) == 0 &&
-                   (reinterpret_cast<uintptr_t>(q) & 7) == 0;
+hipError_t nc_fp8_quantize(int dtype, int fmt, const void* x, int64_t rows, int64_t cols,
+                           float* partial, float* amax_scale, uint8_t* q, uint8_t* qt,
+                           hipStream_t st) {
+  const int64_t n = rows * cols;
+  if (n <= 0) return hipSuccess;
+  if (fmt != 0 && fmt != 1) return hipErrorInvalidValue;
+  auto al = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; };
+  if (qt && !(dtype && rows % 64 == 0 && cols % 64 == 0 && rows <= 0x7fffffff &&
+              cols <= 0x7fffffff && al(x, 16) && al(q, 8) && al(qt, 16)))
+    return hipErrorInvalidValue;
+  const bool vec = dtype && al(x, 16) && al(q, 8);
   const int64_t per = vec ? 8 * 256 : 256;          // values per block and pass
   const int parts = (int)std::min<int64_t>(std::max<int64_t>(ceil_div64(n, per), 1), 1024);
   if (vec)
@@ -1122,13 +1192,28 @@ hipError_t nc_fp8_quantize(int dtype, const void* x, int64_t n, float* partial,
     amax_partial_kernel<bf16><<<parts, 256, 0, st>>>((const bf16*)x, n, partial);
   else
     amax_partial_kernel<float><<<parts, 256, 0, st>>>((const float*)x, n, partial);
-  amax_final_kernel<<<1, 256, 0, st>>>(partial, parts, amax_scale);
+  amax_final_kernel<<<1, 256, 0, st>>>(partial, parts, fmt ? 57344.f : 448.f, amax_scale);
+  if (qt) {
+    const int64_t tiles = (rows / 64) * (cols / 64);
+    if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+    if (fmt)
+      fp8_quantize_2d_kernel<1><<<(int)tiles, 256, 0, st>>>((const bf16*)x, (int)rows,
+                                                            (int)cols, amax_scale, q, qt);
+    else
+      fp8_quantize_2d_kernel<0><<<(int)tiles, 256, 0, st>>>((const bf16*)x, (int)rows,
+                                                            (int)cols, amax_scale, q, qt);
+    return hipGetLastError();
+  }
+  if (!q) return hipErrorInvalidValue;
   const int blocks = (int)std::min<int64_t>(std::max<int64_t>(ceil_div64(n, per), 1), 8192);
-  if (vec)
-    fp8_quantize_bf16x8_kernel<<<blocks, 256, 0, st>>>((const bf16*)x, n, amax_scale, q);
-  else if (dtype)
-    fp8_quantize_kernel<bf16><<<blocks, 256, 0, st>>>((const bf16*)x, n, amax_scale, q);
-  else
-    fp8_quantize_kernel<float><<<blocks, 256, 0, st>>>((const float*)x, n, amax_scale, q);
+  auto launch = [&]<int FMT>() {
+    if (vec)
+      fp8_quantize_bf16x8_kernel<FMT><<<blocks, 256, 0, st>>>((const bf16*)x, n, amax_scale, q);
+    else if (dtype)
+      fp8_quantize_kernel<bf16, FMT><<<blocks, 256, 0, st>>>((const bf16*)x, n, amax_scale, q);
+    else
+      fp8_quantize_kernel<float, FMT><<<blocks, 256, 0, st>>>((const float*)x, n, amax_scale, q);
+  };
+  if (fmt) launch.template operator()<1>(); else launch.template operator()<0>();
   return hipGetLastError();
 }

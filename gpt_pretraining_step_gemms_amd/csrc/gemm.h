@@ -36,12 +36,14 @@ struct GemmParams {
   // fp8 only: per-tensor scales {amax, s} of A and B (device); acc is divided by
   // s_A * s_B before the epilogue.  Null: no device scales.
   const float* scale_a; const float* scale_b;
+  int fmt_a;                         // fp8 only: A's format, 0 = e4m3, 1 = e5m2 (B is e4m3)
 };
 
 // dtype: 0 = fp32 operands (VALU kernel), 1 = bf16 operands (MFMA kernel)
 hipError_t nc_launch_gemm(int dtype, const GemmParams& p, hipStream_t stream);
-// fp8 e4m3 operands (bytes), both K-contiguous: K % 128 == 0, lda, ldb (and batch
-// strides) % 16 == 0, 16-byte aligned; epilogues as for bf16, no split-K
+// fp8 operands (bytes; A e4m3 or e5m2 by fmt_a, B e4m3), both K-contiguous:
+// K % 128 == 0, lda, ldb (and batch strides) % 16 == 0, 16-byte aligned; epilogues
+// as for bf16; split-K (splits > 1) with an fp32 output and the workspace
 hipError_t nc_launch_gemm_f8(const GemmParams& p, hipStream_t stream);
 // splits a weight-gradient GEMM would use for M x N with reduction K (bf16 path)
 int nc_gemm_pick_splits(int M, int N, int K);

@@ -701,24 +701,26 @@ NC_DEV void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// One v_mfma_f32_16x16x128_f8f6f4 (fp8 e4m3 on both operands): a lane's 32
-// operand bytes are the two 16-byte fragments the bf16 path reads for the two
-// 32-deep substeps of a 64-element (128-byte) k-step.  Both operands take the
-// same byte positions, so each of the step's 128 k is summed exactly once.
+// One v_mfma_f32_16x16x128_f8f6f4: a lane's 32 operand bytes are the two
+// 16-byte fragments the bf16 path reads for the two 32-deep substeps of a
+// 64-element (128-byte) k-step.  Both operands take the same byte positions, so
+// each of the step's 128 k is summed exactly once.  FA is A's format (0: e4m3,
+// 1: e5m2, the instruction's format codes); B is e4m3.
+template <int FA>
 NC_DEV f32x4 mfma_f8(bf16x8 a0, bf16x8 a1, bf16x8 b0, bf16x8 b1, f32x4 c) {
   typedef int i32x8 __attribute__((ext_vector_type(8)));
   const i32x4 x0 = __builtin_bit_cast(i32x4, a0), x1 = __builtin_bit_cast(i32x4, a1);
   const i32x4 y0 = __builtin_bit_cast(i32x4, b0), y1 = __builtin_bit_cast(i32x4, b1);
   const i32x8 a = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
   const i32x8 b = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, 0, 0, 0, 0, 0);
 }
 
-// F8: operands are fp8 e4m3 bytes, handled by the loads as pairs (the
-// launcher halves K and the leading dimensions), K-contiguous, half-stage ring
-// with 16 x 16 MFMAs only.
+// F8: operands are fp8 bytes (A in format FA_, B e4m3), handled by the loads
+// as pairs (the launcher halves K and the leading dimensions), K-contiguous,
+// half-stage ring with 16 x 16 MFMAs only.
 template <int AL, int BL, int WM_, int WN_, int ST_, int PK_, int MI_, bool F8 = false,
-          int WTN_ = 64>
+          int WTN_ = 64, int FA_ = 0>
 __global__ __launch_bounds__(WM_ * WN_ * 64, (Pipe<WM_, WN_, ST_, PK_, MI_, WTN_>::kBlocksPerCU))
 void gemm_bf16_pipe_kernel(GemmParams p) {
   using C = Pipe<WM_, WN_, ST_, PK_, MI_, WTN_>;
@@ -874,7 +876,7 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
 #pragma unroll
       for (int t = 0; t < NM; ++t) {
         const int ii = t / TN, j = t % TN;
-        acc[ii][j] = mfma_f8(fr[0][ii], fr[1][ii], fr[0][TM + j], fr[1][TM + j], acc[ii][j]);
+        acc[ii][j] = mfma_f8<FA_>(fr[0][ii], fr[1][ii], fr[0][TM + j], fr[1][TM + j], acc[ii][j]);
         load_at(t);
       }
       __builtin_amdgcn_s_setprio(0);
@@ -1176,12 +1178,13 @@ bool pipe_ok(const GemmParams& p) {
   return true;
 }
 
-template <int AL, int BL, int WM, int WN, int ST, int PK, int MI, bool F8 = false, int WTN = 64>
+template <int AL, int BL, int WM, int WN, int ST, int PK, int MI, bool F8 = false, int WTN = 64,
+          int FA = 0>
 hipError_t launch_pipe_cfg(const GemmParams& p, hipStream_t st) {
   using C = Pipe<WM, WN, ST, PK, MI, WTN>;
   const int tiles = ceil_div(p.M, C::BM) * ceil_div(p.N, C::BN);
   dim3 grid(tiles, 1, p.batch * p.splits);
-  gemm_bf16_pipe_kernel<AL, BL, WM, WN, ST, PK, MI, F8, WTN><<<grid, C::NT, 0, st>>>(p);
+  gemm_bf16_pipe_kernel<AL, BL, WM, WN, ST, PK, MI, F8, WTN, FA><<<grid, C::NT, 0, st>>>(p);
   return hipGetLastError();
 }
 
@@ -1245,14 +1248,33 @@ size_t nc_gemm_workspace_bytes(int M, int N, int splits) {
   return splits > 1 ? (size_t)splits * M * N * sizeof(float) : 0;
 }
 
+// C (+)= the split-K slabs in fixed order
+static hipError_t splitk_reduce(const GemmParams& p, hipStream_t st) {
+  const int64_t total = (int64_t)p.M * p.N * p.batch;
+  const bool rows_ok = p.N % 4 == 0 && p.ldc % 4 == 0 && (p.batch == 1 || p.sC % 4 == 0) &&
+                       (reinterpret_cast<uintptr_t>(p.C) & 15) == 0 &&
+                       (int64_t)p.M * p.batch <= 0x7fffffff;
+  if (rows_ok) {
+    splitk_reduce_rows_kernel<<<p.M * p.batch, 256, 0, st>>>(p);
+  } else {
+    const int blocks = (int)std::min<int64_t>(ceil_div64(total, 256), 65536);
+    splitk_reduce_kernel<<<blocks, 256, 0, st>>>(p);
+  }
+  return hipGetLastError();
+}
+
 hipError_t nc_launch_gemm_f8(const GemmParams& p_in, hipStream_t st) {
   GemmParams p = p_in;
   if (p.M <= 0 || p.N <= 0 || p.batch <= 0) return hipSuccess;
   auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
   if (p.a_layout != kKCont || p.b_layout != kKCont || p.K <= 0 || p.K % 128 || p.lda % 16 ||
-      p.ldb % 16 || (p.batch > 1 && (p.sA % 16 || p.sB % 16)) || !al16(p.A) || !al16(p.B))
+      p.ldb % 16 || (p.batch > 1 && (p.sA % 16 || p.sB % 16)) || !al16(p.A) || !al16(p.B) ||
+      (p.fmt_a != 0 && p.fmt_a != 1))
     return hipErrorInvalidValue;
-  p.splits = 1;
+  if (p.splits < 1) p.splits = 1;
+  if (p.splits > 1 && ((p.epi != kEpiStoreF32 && p.epi != kEpiAccF32) || !p.workspace ||
+                       p.workspace_bytes < nc_gemm_workspace_bytes(p.M, p.N, p.splits) * p.batch))
+    return hipErrorInvalidValue;
   p.vec_epi = p.ldc % 8 == 0 && (p.batch == 1 || p.sC % 8 == 0) && al16(p.C) &&
               al16(p.aux_in) && al16(p.aux_out);
   // the loads move byte pairs: K, leading dimensions and batch strides in pairs
@@ -1262,7 +1284,10 @@ hipError_t nc_launch_gemm_f8(const GemmParams& p_in, hipStream_t st) {
   p.sA /= 2;
   p.sB /= 2;
   if (!pipe_ok(p)) return hipErrorInvalidValue;
-  return launch_pipe_cfg<kKCont, kKCont, 2, 4, 5, 64, 16, true>(p, st);
+  const hipError_t e = p.fmt_a ? launch_pipe_cfg<kKCont, kKCont, 2, 4, 5, 64, 16, true, 64, 1>(p, st)
+                               : launch_pipe_cfg<kKCont, kKCont, 2, 4, 5, 64, 16, true, 64, 0>(p, st);
+  if (e != hipSuccess || p.splits == 1) return e;
+  return splitk_reduce(p, st);
 }
 
 hipError_t nc_launch_gemm(int dtype, const GemmParams& p_in, hipStream_t st) {
@@ -1290,15 +1315,5 @@ hipError_t nc_launch_gemm(int dtype, const GemmParams& p_in, hipStream_t st) {
   const bool use_pipe = pipe_ok(p);
   hipError_t e = use_pipe ? launch_pipe(p, st) : launch_bf16_cfg<256, 256, 2, 4>(p, st);
   if (e != hipSuccess || p.splits == 1) return e;
-  const int64_t total = (int64_t)p.M * p.N * p.batch;
-  const bool rows_ok = p.N % 4 == 0 && p.ldc % 4 == 0 && (p.batch == 1 || p.sC % 4 == 0) &&
-                       (reinterpret_cast<uintptr_t>(p.C) & 15) == 0 &&
-                       (int64_t)p.M * p.batch <= 0x7fffffff;
-  if (rows_ok) {
-    splitk_reduce_rows_kernel<<<p.M * p.batch, 256, 0, st>>>(p);
-  } else {
-    const int blocks = (int)std::min<int64_t>(ceil_div64(total, 256), 65536);
-    splitk_reduce_kernel<<<blocks, 256, 0, st>>>(p);
-  }
-  return hipGetLastError();
+  return splitk_reduce(p, st);
 }

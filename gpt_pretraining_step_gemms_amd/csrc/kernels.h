@@ -108,11 +108,15 @@ hipError_t nc_attn_bwd(int dtype, const void* q, const void* k, const void* v, i
                        int Hkv, int window, const float* rqk, const float* cos_sin,
                        hipStream_t st);
 
-// ---- fp8 e4m3 with one scale per tensor: amax_scale[0] = max |x|, amax_scale[1] =
-// 448 / amax (1 if amax = 0), q[i] = e4m3(x[i] * scale) (round to nearest even,
-// saturating); partial: 1024 floats of scratch
-hipError_t nc_fp8_quantize(int dtype, const void* x, int64_t n, float* partial,
-                           float* amax_scale, uint8_t* q, hipStream_t st);
+// ---- fp8 with one scale per tensor, x [rows, cols] (row stride cols): fmt 0 = e4m3
+// (fmax 448), 1 = e5m2 (fmax 57344); amax_scale[0] = max |x|, amax_scale[1] = fmax /
+// amax (1 if amax = 0); codes fp8(x * scale) (round to nearest even, saturating) in
+// x's layout into q and/or transposed [cols, rows] into qt (qt needs bf16 x, rows and
+// cols multiples of 64, 16-byte aligned x and qt, 8-byte aligned q; q alone may be
+// any shape); partial: 1024 floats of scratch
+hipError_t nc_fp8_quantize(int dtype, int fmt, const void* x, int64_t rows, int64_t cols,
+                           float* partial, float* amax_scale, uint8_t* q, uint8_t* qt,
+                           hipStream_t st);
 
 // ---- softmax cross-entropy over rows of fp32 logits
 // dz = scale*(softmax(z) - onehot(y)) in the activation type; loss_rows[i] = lse - z[y].

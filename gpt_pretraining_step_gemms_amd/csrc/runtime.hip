@@ -62,6 +62,7 @@ struct nc_ctx {
   int L, d, H, F, V, T, maxB, Nmax, chunk;
   int Hkv, dk, W;   // key/value heads, their width Hkv*128, qkv row width d + 2 dk
   bool fp8 = false;  // forward block products in fp8 e4m3 (tensorwise scales)
+  bool fp8b = false; // and their backward products (gradients e5m2)
   // further mechanisms (nc_model_config.features)
   bool ve_on = false, resid_on = false, smear_on = false, backout_on = false;
   int Cg = 32;                 // value-embedding gate channels
@@ -75,6 +76,10 @@ struct nc_ctx {
   size_t x0b = 0, xprev = 0, dx0b = 0, gbb = 0, xbb = 0, part_a = 0, part_b = 0, sig_s = 0,
          gs_s = 0, dz_s = 0, sig_ve = 0, dz_ve = 0, ve_rows = 0, outer_part = 0;
   size_t q8a = 0, q8w = 0, q8s = 0, q8ws = 0;   // their codes, scales and amax scratch
+  // fp8 backward: per layer the transposed codes of the four forward activations
+  // (a1 [d, N] | o [d, N] | a2 [d, N] | g [F, N]) and their scales (8 floats);
+  // the gradient's codes in its layout and transposed, and its scale
+  size_t q8xt = 0, q8xt_layer = 0, q8xs = 0, q8dy = 0, q8dyt = 0, q8dys = 0;
   int64_t S, n_block, n_total;
   std::vector<ParamInfo> params;
   // parameter arena byte offsets
@@ -145,6 +150,18 @@ nc_status validate(const nc_model_config* m, const nc_optim_config* o, std::stri
   if (m->fp8_forward != 0 && m->fp8_forward != 1) { why = "fp8_forward is 0 or 1"; return NC_ERR_INVALID_ARG; }
   if (m->fp8_forward && m->dtype != NC_BF16) {
     why = "fp8_forward needs the bf16 configuration";
+    return NC_ERR_UNSUPPORTED;
+  }
+  if (m->fp8_backward != 0 && m->fp8_backward != 1) {
+    why = "fp8_backward is 0 or 1";
+    return NC_ERR_INVALID_ARG;
+  }
+  if (m->fp8_backward && !m->fp8_forward) {
+    why = "fp8_backward needs fp8_forward (it reuses the forward's activation codes)";
+    return NC_ERR_UNSUPPORTED;
+  }
+  if (m->fp8_backward && m->seq_len % 128) {
+    why = "fp8_backward needs seq_len % 128 == 0 (the weight gradients sum tokens in steps of 128)";
     return NC_ERR_UNSUPPORTED;
   }
   if (m->fp8_forward && m->d_ff % 128) {
@@ -398,6 +415,15 @@ void plan(nc_ctx* c) {
     c->q8s = a.take(4 * sizeof(float));
     c->q8ws = a.take(1024 * sizeof(float));
   }
+  if (c->fp8b) {
+    c->q8xt_layer = N * (size_t)(3 * d + F);
+    c->q8xt = a.take((size_t)L * c->q8xt_layer);
+    c->q8xs = a.take((size_t)L * 8 * sizeof(float));
+    const size_t wmax = (size_t)std::max(W, F);
+    c->q8dy = a.take(N * wmax);
+    c->q8dyt = a.take(N * wmax);
+    c->q8dys = a.take(2 * sizeof(float));
+  }
   c->act_bytes = a.cur;
 }
 
@@ -478,7 +504,8 @@ hipError_t gemm(nc_ctx* c, const void* A_, int64_t lda, int al, const void* B_, 
 // per tensor (codes in q8a / q8w, scales {amax, s} in q8s[0..1] / q8s[2..3]);
 // the kernel divides the sums by s_X s_W.
 hipError_t gemm_fp8_fwd(nc_ctx* c, const void* X, int K, const void* Wt, int Nout, void* C,
-                        int64_t ldc, int N, int epi) {
+                        int64_t ldc, int N, int epi, uint8_t* xt = nullptr,
+                        float* xscale = nullptr) {
   float* sc = reinterpret_cast<float*>(c->aa + c->q8s);
   float* ws = reinterpret_cast<float*>(c->aa + c->q8ws);
   uint8_t* xa = reinterpret_cast<uint8_t*>(c->aa + c->q8a);
@@ -491,22 +518,97 @@ hipError_t gemm_fp8_fwd(nc_ctx* c, const void* X, int K, const void* Wt, int Nou
   }
   // every extent inside its arena, also in a dry run
   if (!in_arena(c, X, nx * 2) || !in_arena(c, Wt, nw * 2) || !in_arena(c, xa, nx) ||
-      !in_arena(c, wq, nw) || !in_arena(c, C, ((size_t)(N - 1) * ldc + Nout) * (c_f32 ? 4 : 2))) {
+      !in_arena(c, wq, nw) || !in_arena(c, C, ((size_t)(N - 1) * ldc + Nout) * (c_f32 ? 4 : 2)) ||
+      (xt && !in_arena(c, xt, nx)) || (xscale && !in_arena(c, xscale, 2 * sizeof(float)))) {
     c->range_error = "fp8 GEMM operand outside its arena (N=" + std::to_string(N) +
                      " Nout=" + std::to_string(Nout) + " K=" + std::to_string(K) + ")";
     return hipErrorInvalidValue;
   }
   if (c->dry_run) return hipSuccess;
-  hipError_t e = nc_fp8_quantize(1, X, (int64_t)nx, ws, sc, xa, c->st);
+  float* xs = xscale ? xscale : sc;
+  hipError_t e = nc_fp8_quantize(1, 0, X, N, K, ws, xs, xa, xt, c->st);
   if (e != hipSuccess) return e;
-  e = nc_fp8_quantize(1, Wt, (int64_t)nw, ws, sc + 2, wq, c->st);
+  e = nc_fp8_quantize(1, 0, Wt, Nout, K, ws, sc + 2, wq, nullptr, c->st);
   if (e != hipSuccess) return e;
   GemmParams g{};
   g.A = xa; g.B = wq; g.C = C;
   g.lda = K; g.ldb = K; g.ldc = ldc;
   g.M = N; g.N = Nout; g.K = K; g.batch = 1; g.splits = 1;
   g.a_layout = kKCont; g.b_layout = kKCont; g.epi = epi; g.alpha = 1.f;
-  g.scale_a = sc; g.scale_b = sc + 2;
+  g.scale_a = xs; g.scale_b = sc + 2;
+  return nc_launch_gemm_f8(g, c->st);
+}
+
+// Backward of an fp8 block product y = x W^T.  fp8_grad_codes: the bf16
+// gradient dY [N, w] to e5m2 codes in its layout (q8dy) and transposed
+// (q8dyt), scale in q8dys.
+hipError_t fp8_grad_codes(nc_ctx* c, const void* dY, int N, int w) {
+  uint8_t* q = reinterpret_cast<uint8_t*>(c->aa + c->q8dy);
+  uint8_t* qt = reinterpret_cast<uint8_t*>(c->aa + c->q8dyt);
+  float* ds = reinterpret_cast<float*>(c->aa + c->q8dys);
+  const size_t n = (size_t)N * w;
+  if (!in_arena(c, dY, n * 2) || !in_arena(c, q, n) || !in_arena(c, qt, n)) {
+    c->range_error = "fp8 gradient codes outside the arena (N=" + std::to_string(N) +
+                     " w=" + std::to_string(w) + ")";
+    return hipErrorInvalidValue;
+  }
+  if (c->dry_run) return hipSuccess;
+  return nc_fp8_quantize(1, 1, dY, N, w, reinterpret_cast<float*>(c->aa + c->q8ws), ds, q, qt,
+                         c->st);
+}
+
+// dX (epilogue epi, aux g for the ReLU^2 backward) = dY W from the gradient's
+// codes [N, out] and the transposed e4m3 codes of the bf16 weight copy W
+// [out, in] (quantised here into q8w, scale in q8s[2..3]).
+hipError_t gemm_fp8_dx(nc_ctx* c, const void* Wt, int out, int in, void* C, int64_t ldc, int N,
+                       int epi, const void* aux = nullptr) {
+  float* sc = reinterpret_cast<float*>(c->aa + c->q8s);
+  uint8_t* wq = reinterpret_cast<uint8_t*>(c->aa + c->q8w);
+  const uint8_t* dyq = reinterpret_cast<const uint8_t*>(c->aa + c->q8dy);
+  const bool c_f32 = epi == kEpiStoreF32 || epi == kEpiAccF32;
+  const size_t nw = (size_t)out * in, cext = ((size_t)(N - 1) * ldc + in) * (c_f32 ? 4 : 2);
+  if (!in_arena(c, Wt, nw * 2) || !in_arena(c, wq, nw) || !in_arena(c, dyq, (size_t)N * out) ||
+      !in_arena(c, C, cext) || (aux && !in_arena(c, aux, cext))) {
+    c->range_error = "fp8 input-gradient operand outside its arena (N=" + std::to_string(N) +
+                     " out=" + std::to_string(out) + " in=" + std::to_string(in) + ")";
+    return hipErrorInvalidValue;
+  }
+  if (c->dry_run) return hipSuccess;
+  hipError_t e = nc_fp8_quantize(1, 0, Wt, out, in, reinterpret_cast<float*>(c->aa + c->q8ws),
+                                 sc + 2, nullptr, wq, c->st);
+  if (e != hipSuccess) return e;
+  GemmParams g{};
+  g.A = dyq; g.B = wq; g.C = C; g.aux_in = aux;
+  g.lda = out; g.ldb = out; g.ldc = ldc;
+  g.M = N; g.N = in; g.K = out; g.batch = 1; g.splits = 1;
+  g.a_layout = kKCont; g.b_layout = kKCont; g.epi = epi; g.alpha = 1.f;
+  g.scale_a = reinterpret_cast<const float*>(c->aa + c->q8dys); g.scale_b = sc + 2;
+  g.fmt_a = 1;
+  return nc_launch_gemm_f8(g, c->st);
+}
+
+// dW [out, in] += dY^T X from the transposed gradient codes [out, N] and the
+// forward's transposed activation codes xt [in, N] (scale xs), split over K = N.
+hipError_t gemm_fp8_dw(nc_ctx* c, const uint8_t* xt, const float* xs, int out, int in, float* G,
+                       int N, int splits) {
+  const uint8_t* dyt = reinterpret_cast<const uint8_t*>(c->aa + c->q8dyt);
+  if (splits > 1 && nc_gemm_workspace_bytes(out, in, splits) > c->ws_bytes) splits = 1;
+  if (!in_arena(c, xt, (size_t)in * N) || !in_arena(c, xs, 2 * sizeof(float)) ||
+      !in_arena(c, dyt, (size_t)out * N) || !in_arena(c, G, (size_t)out * in * 4)) {
+    c->range_error = "fp8 weight-gradient operand outside its arena (N=" + std::to_string(N) +
+                     " out=" + std::to_string(out) + " in=" + std::to_string(in) + ")";
+    return hipErrorInvalidValue;
+  }
+  if (c->dry_run) return hipSuccess;
+  GemmParams g{};
+  g.A = dyt; g.B = xt; g.C = G;
+  g.lda = N; g.ldb = N; g.ldc = in;
+  g.M = out; g.N = in; g.K = N; g.batch = 1; g.splits = splits;
+  g.a_layout = kKCont; g.b_layout = kKCont; g.epi = kEpiAccF32; g.alpha = 1.f;
+  g.scale_a = reinterpret_cast<const float*>(c->aa + c->q8dys); g.scale_b = xs;
+  g.fmt_a = 1;
+  g.workspace = reinterpret_cast<float*>(c->aa + c->ws);
+  g.workspace_bytes = c->ws_bytes;
   return nc_launch_gemm_f8(g, c->st);
 }
 
@@ -539,6 +641,7 @@ static nc_ctx* make_ctx(const nc_model_config* cfg, const nc_optim_config* ocfg)
   c->L = cfg->n_layer; c->d = cfg->d_model; c->H = cfg->n_head; c->F = cfg->d_ff;
   c->Hkv = cfg->n_kv_head > 0 ? cfg->n_kv_head : cfg->n_head;
   c->fp8 = cfg->fp8_forward != 0;
+  c->fp8b = c->fp8 && cfg->fp8_backward != 0;
   c->dk = c->Hkv * 128;
   c->W = c->d + 2 * c->dk;
   c->V = cfg->vocab; c->T = cfg->seq_len; c->maxB = cfg->max_micro_batch;
@@ -724,6 +827,16 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
     NC_TRY(nc_embed_fwd(tok, E, x, N, d, V, flags, st), "embed");
     if (x0b) NC_TRY(hipMemcpyAsync(x0b, x, Nd * 4, hipMemcpyDeviceToDevice, st), "x0");
   }
+  // fp8 backward: the forward quantiser also writes the transposed codes of
+  // each layer's four activations (a1, o, a2, g) and keeps their scales
+  auto xt_of = [&](int l, int which) -> uint8_t* {
+    if (!ctx->fp8b) return nullptr;
+    return A<uint8_t>(ctx, ctx->q8xt) + (size_t)l * ctx->q8xt_layer + (size_t)which * d * N;
+  };
+  auto xs_of = [&](int l, int which) -> float* {
+    if (!ctx->fp8b) return nullptr;
+    return A<float>(ctx, ctx->q8xs) + (size_t)l * 8 + 2 * which;
+  };
   for (int l = 0; l < L; ++l) {
     const LayerAct& la = ctx->la[l];
     const size_t wb = (size_t)l * ctx->S;
@@ -738,7 +851,8 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
     } else {
       NC_TRY(nc_rmsnorm_fwd(dt, x, aa + la.a1, A<float>(ctx, la.r1), N, d, eps, st), "norm1");
     }
-    NC_GEMM(ctx->fp8 ? gemm_fp8_fwd(ctx, aa + la.a1, d, wptr(ctx, wb), Wd, qkv, Wd, N, kEpiStore)
+    NC_GEMM(ctx->fp8 ? gemm_fp8_fwd(ctx, aa + la.a1, d, wptr(ctx, wb), Wd, qkv, Wd, N, kEpiStore,
+                                    xt_of(l, 0), xs_of(l, 0))
                      : gemm(ctx, aa + la.a1, d, kKCont, wptr(ctx, wb), d, kKCont, qkv, Wd, N, Wd,
                             d, kEpiStore), "qkv");
     if (ctx->ve_slot[l] >= 0) {
@@ -752,16 +866,17 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
            "qknorm");
     NC_TRY(nc_attn_fwd(dt, qkv, qkv + d * es, qkv + (d + dk) * es, Wd, aa + la.o, d,
                        A<float>(ctx, la.lse), B, T, H, Hkv, ctx->windows[l], st), "attn fwd");
-    NC_GEMM(ctx->fp8 ? gemm_fp8_fwd(ctx, aa + la.o, d, wptr(ctx, wb + oWo), d, x, d, N, kEpiAccF32)
+    NC_GEMM(ctx->fp8 ? gemm_fp8_fwd(ctx, aa + la.o, d, wptr(ctx, wb + oWo), d, x, d, N, kEpiAccF32,
+                                    xt_of(l, 1), xs_of(l, 1))
                      : gemm(ctx, aa + la.o, d, kKCont, wptr(ctx, wb + oWo), d, kKCont, x, d, N, d,
                             d, kEpiAccF32), "out proj");
     NC_TRY(nc_rmsnorm_fwd(dt, x, aa + la.a2, A<float>(ctx, la.r2), N, d, eps, st), "norm2");
     NC_GEMM(ctx->fp8 ? gemm_fp8_fwd(ctx, aa + la.a2, d, wptr(ctx, wb + oW1), F, aa + la.g, F, N,
-                                    kEpiRelu2)
+                                    kEpiRelu2, xt_of(l, 2), xs_of(l, 2))
                      : gemm(ctx, aa + la.a2, d, kKCont, wptr(ctx, wb + oW1), d, kKCont, aa + la.g,
                             F, N, F, d, kEpiRelu2), "mlp up");
     NC_GEMM(ctx->fp8 ? gemm_fp8_fwd(ctx, aa + la.g, F, wptr(ctx, wb + oW1 + (size_t)F * d), d, x,
-                                    d, N, kEpiAccF32)
+                                    d, N, kEpiAccF32, xt_of(l, 3), xs_of(l, 3))
                      : gemm(ctx, aa + la.g, F, kKCont, wptr(ctx, wb + oW1 + (size_t)F * d), F,
                             kKCont, x, d, N, d, F, kEpiAccF32), "mlp down");
   }
@@ -810,21 +925,38 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
     char* qkv = aa + la.qkv;
     char* dqkv = aa + ctx->dqkv;
     // MLP
-    NC_GEMM(gemm(ctx, dxT, d, kKCont, wptr(ctx, w2), F, kMNCont, aa + ctx->dh, F, N, F, d,
-                kEpiRelu2Bwd, aa + la.g), "dh");
-    NC_GEMM(gemm(ctx, dxT, d, kMNCont, aa + la.g, F, kMNCont, G + w2, F, d, F, N, kEpiAccF32,
-                nullptr, nullptr, ctx->splits_2), "dW2");
-    NC_GEMM(gemm(ctx, aa + ctx->dh, F, kMNCont, aa + la.a2, d, kMNCont, G + w1, d, F, d, N,
-                kEpiAccF32, nullptr, nullptr, ctx->splits_1), "dW1");
-    NC_GEMM(gemm(ctx, aa + ctx->dh, F, kKCont, wptr(ctx, w1), d, kMNCont, da, d, N, d, F,
-                kEpiStoreF32), "da2");
+    if (ctx->fp8b) {   // the eight products in fp8: dY e5m2, X and W e4m3
+      NC_GEMM(fp8_grad_codes(ctx, dxT, N, d), "dx codes");
+      NC_GEMM(gemm_fp8_dx(ctx, wptr(ctx, w2), d, F, aa + ctx->dh, F, N, kEpiRelu2Bwd, aa + la.g),
+              "dh");
+      NC_GEMM(gemm_fp8_dw(ctx, xt_of(l, 3), xs_of(l, 3), d, F, G + w2, N, ctx->splits_2), "dW2");
+      NC_GEMM(fp8_grad_codes(ctx, aa + ctx->dh, N, F), "dh codes");
+      NC_GEMM(gemm_fp8_dw(ctx, xt_of(l, 2), xs_of(l, 2), F, d, G + w1, N, ctx->splits_1), "dW1");
+      NC_GEMM(gemm_fp8_dx(ctx, wptr(ctx, w1), F, d, da, d, N, kEpiStoreF32), "da2");
+    } else {
+      NC_GEMM(gemm(ctx, dxT, d, kKCont, wptr(ctx, w2), F, kMNCont, aa + ctx->dh, F, N, F, d,
+                  kEpiRelu2Bwd, aa + la.g), "dh");
+      NC_GEMM(gemm(ctx, dxT, d, kMNCont, aa + la.g, F, kMNCont, G + w2, F, d, F, N, kEpiAccF32,
+                  nullptr, nullptr, ctx->splits_2), "dW2");
+      NC_GEMM(gemm(ctx, aa + ctx->dh, F, kMNCont, aa + la.a2, d, kMNCont, G + w1, d, F, d, N,
+                  kEpiAccF32, nullptr, nullptr, ctx->splits_1), "dW1");
+      NC_GEMM(gemm(ctx, aa + ctx->dh, F, kKCont, wptr(ctx, w1), d, kMNCont, da, d, N, d, F,
+                  kEpiStoreF32), "da2");
+    }
     NC_TRY(nc_rmsnorm_bwd(dt, da, aa + la.a2, A<float>(ctx, la.r2), dx, dxT, N, d, 1, st),
            "norm2 bwd");
     // attention
-    NC_GEMM(gemm(ctx, dxT, d, kKCont, wptr(ctx, wb + oWo), d, kMNCont, aa + ctx->dO, d,
-                N, d, d, kEpiStore), "dO");
-    NC_GEMM(gemm(ctx, dxT, d, kMNCont, aa + la.o, d, kMNCont, G + wb + oWo, d, d, d, N,
-                kEpiAccF32, nullptr, nullptr, ctx->splits_o), "dWo");
+    if (ctx->fp8b) {
+      NC_GEMM(fp8_grad_codes(ctx, dxT, N, d), "dx codes");
+      NC_GEMM(gemm_fp8_dx(ctx, wptr(ctx, wb + oWo), d, d, aa + ctx->dO, d, N, kEpiStore), "dO");
+      NC_GEMM(gemm_fp8_dw(ctx, xt_of(l, 1), xs_of(l, 1), d, d, G + wb + oWo, N, ctx->splits_o),
+              "dWo");
+    } else {
+      NC_GEMM(gemm(ctx, dxT, d, kKCont, wptr(ctx, wb + oWo), d, kMNCont, aa + ctx->dO, d,
+                  N, d, d, kEpiStore), "dO");
+      NC_GEMM(gemm(ctx, dxT, d, kMNCont, aa + la.o, d, kMNCont, G + wb + oWo, d, d, d, N,
+                  kEpiAccF32, nullptr, nullptr, ctx->splits_o), "dWo");
+    }
     // bf16: D and the QK-norm + rotary backward are formed inside the attention
     // backward kernels; fp32: separate kernels
     NC_TRY(nc_attn_bwd(dt, qkv, qkv + d * es, qkv + (d + dk) * es, Wd, aa + la.o, aa + ctx->dO, d,
@@ -848,10 +980,17 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
                                  A<float>(ctx, ctx->outer_part),
                                  G + ctx->e_wg + (size_t)vs * Hkv * ctx->Cg, st), "gate grad");
     }
-    NC_GEMM(gemm(ctx, dqkv, Wd, kMNCont, aa + la.a1, d, kMNCont, G + wb, d, Wd, d, N,
-                kEpiAccF32, nullptr, nullptr, ctx->splits_qkv), "dWqkv");
-    NC_GEMM(gemm(ctx, dqkv, Wd, kKCont, wptr(ctx, wb), d, kMNCont, da, d, N, d, Wd,
-                kEpiStoreF32), "da1");
+    if (ctx->fp8b) {
+      NC_GEMM(fp8_grad_codes(ctx, dqkv, N, Wd), "dqkv codes");
+      NC_GEMM(gemm_fp8_dw(ctx, xt_of(l, 0), xs_of(l, 0), Wd, d, G + wb, N, ctx->splits_qkv),
+              "dWqkv");
+      NC_GEMM(gemm_fp8_dx(ctx, wptr(ctx, wb), Wd, d, da, d, N, kEpiStoreF32), "da1");
+    } else {
+      NC_GEMM(gemm(ctx, dqkv, Wd, kMNCont, aa + la.a1, d, kMNCont, G + wb, d, Wd, d, N,
+                  kEpiAccF32, nullptr, nullptr, ctx->splits_qkv), "dWqkv");
+      NC_GEMM(gemm(ctx, dqkv, Wd, kKCont, wptr(ctx, wb), d, kMNCont, da, d, N, d, Wd,
+                  kEpiStoreF32), "da1");
+    }
     if (vs >= 0)
       NC_TRY(nc_ve_gate_da(A<float>(ctx, ctx->dz_ve), Pm + ctx->e_wg + (size_t)vs * Hkv * ctx->Cg,
                            da, d, N, Hkv, ctx->Cg, st), "gate input grad");
@@ -1331,43 +1470,66 @@ nc_status nc_op_gemm_noalloc(int32_t dtype, const void* A_, size_t A_bytes, int6
                     p0, p1, splits, ws, ws_bytes, stream);
 }
 
-nc_status nc_op_gemm_fp8(const void* A_, size_t A_bytes, int64_t lda, const void* B_,
-                         size_t B_bytes, int64_t ldb, void* C_, size_t C_bytes, int64_t ldc,
-                         int32_t M, int32_t N, int32_t K, int32_t epi, float alpha, void* stream) {
-  if (!A_ || !B_ || !C_ || M < 0 || N < 0 || K < 1) return NC_ERR_INVALID_ARG;
-  if (epi != kEpiStore && epi != kEpiStoreF32 && epi != kEpiAccF32 && epi != kEpiRelu2)
+nc_status nc_op_gemm_fp8(int32_t a_format, const void* A_, size_t A_bytes, int64_t lda,
+                         const void* B_, size_t B_bytes, int64_t ldb, void* C_, size_t C_bytes,
+                         int64_t ldc, int32_t M, int32_t N, int32_t K, int32_t epi,
+                         const void* aux_in, size_t aux_in_bytes, float alpha, int32_t splits,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (!A_ || !B_ || !C_ || M < 0 || N < 0 || K < 1 || splits < 1) return NC_ERR_INVALID_ARG;
+  if (a_format != NC_FP8_E4M3 && a_format != NC_FP8_E5M2) return NC_ERR_INVALID_ARG;
+  if (epi != kEpiStore && epi != kEpiStoreF32 && epi != kEpiAccF32 && epi != kEpiRelu2 &&
+      epi != kEpiRelu2Bwd)
     return NC_ERR_INVALID_ARG;
   if (lda < K || ldb < K || ldc < N) return NC_ERR_INVALID_ARG;
-  const size_t ce = epi == kEpiStoreF32 || epi == kEpiAccF32 ? 4 : 2;
+  const bool f32_out = epi == kEpiStoreF32 || epi == kEpiAccF32;
+  if (splits > 1 && !f32_out) return NC_ERR_INVALID_ARG;
+  const size_t ce = f32_out ? 4 : 2;
   if (!span_ok(A_bytes, M, K, lda, 0, 1, 1) || !span_ok(B_bytes, N, K, ldb, 0, 1, 1) ||
       !span_ok(C_bytes, M, N, ldc, 0, 1, ce))
     return NC_ERR_INVALID_ARG;
+  if (epi == kEpiRelu2Bwd && (!aux_in || !span_ok(aux_in_bytes, M, N, ldc, 0, 1, 2)))
+    return NC_ERR_INVALID_ARG;
+  if (splits > 1 && (!workspace || workspace_bytes < nc_gemm_workspace_bytes(M, N, splits)))
+    return NC_ERR_INVALID_ARG;
   if (K % 128 || lda % 16 || ldb % 16) return NC_ERR_UNSUPPORTED;
   GemmParams g{};
-  g.A = A_; g.B = B_; g.C = C_;
+  g.A = A_; g.B = B_; g.C = C_; g.aux_in = aux_in;
   g.lda = lda; g.ldb = ldb; g.ldc = ldc;
-  g.M = M; g.N = N; g.K = K; g.batch = 1; g.splits = 1;
+  g.M = M; g.N = N; g.K = K; g.batch = 1; g.splits = splits;
   g.a_layout = kKCont; g.b_layout = kKCont; g.epi = epi;
   g.alpha = alpha;
+  g.fmt_a = a_format;
+  g.workspace = static_cast<float*>(workspace);
+  g.workspace_bytes = workspace_bytes;
   const hipError_t e = nc_launch_gemm_f8(g, static_cast<hipStream_t>(stream));
   if (e == hipErrorInvalidValue) return NC_ERR_UNSUPPORTED;
   return e == hipSuccess ? NC_OK : NC_ERR_HIP;
 }
 
-nc_status nc_op_fp8_quantize(int32_t dtype, const void* x, size_t x_bytes, int64_t n,
-                             float* amax_scale, size_t amax_scale_bytes, void* q, size_t q_bytes,
-                             float* workspace, size_t workspace_bytes, void* stream) {
-  if (!x || !amax_scale || !q || !workspace || n < 1) return NC_ERR_INVALID_ARG;
-  if (dtype != NC_FP32 && dtype != NC_BF16) return NC_ERR_INVALID_ARG;
-  const size_t es = dtype == NC_BF16 ? 2 : 4;
-  if ((uint64_t)n > x_bytes / es || (uint64_t)n > q_bytes || amax_scale_bytes < 2 * sizeof(float) ||
-      workspace_bytes < 1024 * sizeof(float))
+nc_status nc_op_fp8_quantize(int32_t dtype, int32_t format, const void* x, size_t x_bytes,
+                             int64_t rows, int64_t cols, float* amax_scale,
+                             size_t amax_scale_bytes, void* q, size_t q_bytes, void* qt,
+                             size_t qt_bytes, float* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (!x || !amax_scale || (!q && !qt) || !workspace || rows < 1 || cols < 1)
     return NC_ERR_INVALID_ARG;
-  return nc_fp8_quantize(dtype == NC_BF16, x, n, workspace, amax_scale,
-                         static_cast<uint8_t*>(q), static_cast<hipStream_t>(stream)) ==
-                 hipSuccess
-             ? NC_OK
-             : NC_ERR_HIP;
+  if (dtype != NC_FP32 && dtype != NC_BF16) return NC_ERR_INVALID_ARG;
+  if (format != NC_FP8_E4M3 && format != NC_FP8_E5M2) return NC_ERR_INVALID_ARG;
+  if (rows > INT64_MAX / cols) return NC_ERR_INVALID_ARG;
+  const uint64_t n = (uint64_t)rows * (uint64_t)cols;
+  const size_t es = dtype == NC_BF16 ? 2 : 4;
+  if (n > x_bytes / es || (q && n > q_bytes) || (qt && n > qt_bytes) ||
+      amax_scale_bytes < 2 * sizeof(float) || workspace_bytes < 1024 * sizeof(float))
+    return NC_ERR_INVALID_ARG;
+  auto al = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; };
+  if (qt && !(dtype == NC_BF16 && rows % 64 == 0 && cols % 64 == 0 && al(x, 16) && al(qt, 16) &&
+              al(q, 8)))
+    return NC_ERR_UNSUPPORTED;
+  const hipError_t e = nc_fp8_quantize(dtype == NC_BF16, format, x, rows, cols, workspace,
+                                       amax_scale, static_cast<uint8_t*>(q),
+                                       static_cast<uint8_t*>(qt), static_cast<hipStream_t>(stream));
+  if (e == hipErrorInvalidValue) return NC_ERR_UNSUPPORTED;
+  return e == hipSuccess ? NC_OK : NC_ERR_HIP;
 }
 
 // Extents of the attention operands: q, o, dq have H heads, k, v, dk, dv

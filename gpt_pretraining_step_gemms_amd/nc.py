@@ -23,6 +23,7 @@ NC_FP32, NC_BF16 = 0, 1
 NC_PARAM, NC_GRAD, NC_MOMENTUM, NC_ADAM_M, NC_ADAM_V = 0, 1, 2, 3, 4
 NC_K_CONTIGUOUS, NC_MN_CONTIGUOUS = 0, 1
 NC_FEAT_VALUE_EMBEDS, NC_FEAT_RESID_LAMBDAS, NC_FEAT_SMEAR, NC_FEAT_BACKOUT = 1, 2, 4, 8
+FP8_E4M3, FP8_E5M2 = 0, 1
 EPI_STORE, EPI_STORE_F32, EPI_ACC_F32, EPI_RELU2, EPI_RELU2_BWD, EPI_POLY, EPI_DUAL = range(7)
 
 
@@ -40,7 +41,8 @@ class ModelCfgC(ctypes.Structure):
                                                  ("n_kv_head", ctypes.c_int32),
                                                  ("fp8_forward", ctypes.c_int32),
                                                  ("features", ctypes.c_int32),
-                                                 ("ve_gate_channels", ctypes.c_int32)]
+                                                 ("ve_gate_channels", ctypes.c_int32),
+                                                 ("fp8_backward", ctypes.c_int32)]
 
 
 class OptimCfgC(ctypes.Structure):
@@ -98,8 +100,9 @@ def load():
                        I64, I64, I64, I32, P, SZ, P, SZ, F32, F32, F32, I32, P, SZ, P],
         "nc_op_gemm_noalloc": [I32, P, SZ, I64, I32, P, SZ, I64, I32, P, SZ, I64, I32, I32, I32,
                                I32, I64, I64, I64, I32, P, SZ, P, SZ, F32, F32, F32, I32, P],
-        "nc_op_gemm_fp8": [P, SZ, I64, P, SZ, I64, P, SZ, I64, I32, I32, I32, I32, F32, P],
-        "nc_op_fp8_quantize": [I32, P, SZ, I64, P, SZ, P, SZ, P, SZ, P],
+        "nc_op_gemm_fp8": [I32, P, SZ, I64, P, SZ, I64, P, SZ, I64, I32, I32, I32, I32, P, SZ,
+                           F32, I32, P, SZ, P],
+        "nc_op_fp8_quantize": [I32, I32, P, SZ, I64, I64, P, SZ, P, SZ, P, SZ, P, SZ, P],
         "nc_op_attention_fwd": [I32, P, SZ, P, SZ, P, SZ, I64, P, SZ, I64, P, SZ, I32, I32, I32,
                                 I32, I32, P],
         "nc_op_attention_bwd": [I32, P, SZ, P, SZ, P, SZ, I64, P, SZ, P, SZ, I64, P, SZ, P, SZ,
@@ -124,7 +127,7 @@ def model_cfg_c(cfg: ModelConfig, max_micro_batch=None):
                      cfg.seq_len, max_micro_batch or cfg.micro_batch,
                      NC_BF16 if cfg.dtype == "bf16" else NC_FP32, cfg.rope_base, cfg.norm_eps,
                      cfg.n_kv_head, int(bool(cfg.fp8_forward)), features_of(cfg),
-                     cfg.ve_gate_channels)
+                     cfg.ve_gate_channels, int(bool(cfg.fp8_backward)))
 
 
 def features_of(cfg: ModelConfig):
@@ -167,7 +170,7 @@ def plan(cfg: ModelConfig, ocfg: OptimConfig = OptimConfig(), max_micro_batch=No
 
 
 def _ptr(t):
-    return ctypes.c_void_p(t.data_ptr())
+    return ctypes.c_void_p(None if t is None else t.data_ptr())
 
 
 class Model:
@@ -378,19 +381,26 @@ def attention_bwd(q, k, v, o, dO, lse, D, dq, dk, dv, B, T, H, ld_qkv, ld_o, ld_
     _check(s, what="nc_op_attention_bwd")
 
 
-def gemm_fp8(A8, B8, C, M, N, K, alpha, epilogue=EPI_STORE, lda=None, ldb=None, ldc=None):
-    """C = alpha * A8 B8^T for K-contiguous uint8 (fp8 e4m3) operands."""
+def gemm_fp8(A8, B8, C, M, N, K, alpha, epilogue=EPI_STORE, lda=None, ldb=None, ldc=None,
+             a_format=FP8_E4M3, aux_in=None, splits=1, workspace=None):
+    """C = alpha * A8 B8^T for K-contiguous uint8 fp8 operands (A e4m3 or e5m2,
+    B e4m3)."""
     lib = load()
-    s = lib.nc_op_gemm_fp8(_ptr(A8), extent(A8), lda or A8.shape[-1], _ptr(B8), extent(B8),
-                           ldb or B8.shape[-1], _ptr(C), extent(C), ldc or C.shape[-1], M, N, K,
-                           epilogue, alpha, _stream())
+    s = lib.nc_op_gemm_fp8(a_format, _ptr(A8), extent(A8), lda or A8.shape[-1], _ptr(B8),
+                           extent(B8), ldb or B8.shape[-1], _ptr(C), extent(C),
+                           ldc or C.shape[-1], M, N, K, epilogue, _ptr(aux_in), extent(aux_in),
+                           alpha, splits, _ptr(workspace), extent(workspace), _stream())
     _check(s, what="nc_op_gemm_fp8")
 
 
-def fp8_quantize(x, q, amax_scale, workspace):
-    """q (uint8, x.numel()) = e4m3(x * 448 / amax); amax_scale (2 floats) = amax, scale."""
+def fp8_quantize(x, q, amax_scale, workspace, fmt=FP8_E4M3, qt=None, rows=None, cols=None):
+    """Tensorwise fp8 codes of x [rows, cols] (default: one row of x.numel()):
+    q in x's layout and/or qt transposed; amax_scale (2 floats) = amax, scale."""
     lib = load()
-    s = lib.nc_op_fp8_quantize(_dtype_code(x), _ptr(x), extent(x), x.numel(), _ptr(amax_scale),
-                               extent(amax_scale), _ptr(q), extent(q), _ptr(workspace),
-                               extent(workspace), _stream())
+    if rows is None:
+        rows, cols = (1, x.numel()) if qt is None else (x.shape[0], x.numel() // x.shape[0])
+    s = lib.nc_op_fp8_quantize(_dtype_code(x), fmt, _ptr(x), extent(x), rows, cols,
+                               _ptr(amax_scale), extent(amax_scale), _ptr(q), extent(q),
+                               _ptr(qt), extent(qt), _ptr(workspace), extent(workspace),
+                               _stream())
     _check(s, what="nc_op_fp8_quantize")

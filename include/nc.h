@@ -81,6 +81,12 @@ typedef struct {
                               the three efficiency tricks); 0 = the plain model */
   int32_t ve_gate_channels;/* channels of the value-embedding gate input (0 = 32;
                               a multiple of 8, at most 64 and at most d_model) */
+  int32_t fp8_backward;    /* 1: also the eight backward products of those four (the
+                              input gradient dY W and the weight gradient dY^T X of each)
+                              in fp8, the gradient dY in e5m2 (scale 57344 / amax) and X,
+                              W in e4m3 with the forward's scales; the transposed codes
+                              of X are written by the forward quantiser and kept per
+                              layer.  Needs fp8_forward and seq_len % 128 == 0. */
 } nc_model_config;
 
 /* Feature bits of nc_model_config.features.

@@ -22,6 +22,9 @@ extern "C" {
 
 /* Operand layouts for nc_op_gemm */
 enum { NC_K_CONTIGUOUS = 0, NC_MN_CONTIGUOUS = 1 };
+/* fp8 formats (OCP 8-bit floating point): e4m3 for activations and weights,
+ * e5m2 for gradients */
+enum { NC_FP8_E4M3 = 0, NC_FP8_E5M2 = 1 };
 /* Epilogues for nc_op_gemm (acc = alpha * A B^T in fp32) */
 enum {
   NC_EPI_STORE = 0,       /* C = acc, activation dtype */
@@ -79,27 +82,40 @@ nc_status nc_op_gemm_noalloc(int32_t dtype, const void* A, size_t A_bytes, int64
                              float alpha, float p0, float p1, int32_t splits, void* stream);
 
 /* fp8 GEMM: acc[m, n] = alpha * sum_k A(m, k) B(n, k) with A [M, K] and B [N, K]
- * K-contiguous OCP fp8 e4m3 bytes (row strides lda, ldb in bytes), fp32
- * accumulation; the epilogue writes C (row stride ldc elements): NC_EPI_STORE
- * (bf16), NC_EPI_STORE_F32, NC_EPI_ACC_F32 (C += acc) or NC_EPI_RELU2 (bf16
- * max(acc, 0)^2), as for nc_op_gemm.  The pages' later runs train most linear layers in FP8
- * with one scale per tensor (apidog.com, "3. Manajemen Presisi
- * (nanochat/common.py)"); alpha carries the product of the two inverse scales.
+ * K-contiguous OCP fp8 bytes (row strides lda, ldb in bytes), A in e4m3
+ * (a_format NC_FP8_E4M3) or e5m2 (NC_FP8_E5M2), B in e4m3, fp32 accumulation;
+ * the epilogue writes C (row stride ldc elements): NC_EPI_STORE (bf16),
+ * NC_EPI_STORE_F32, NC_EPI_ACC_F32 (C += acc), NC_EPI_RELU2 (bf16
+ * max(acc, 0)^2) or NC_EPI_RELU2_BWD (bf16 2 sqrt(aux_in) acc, aux_in bf16
+ * [M, N] with stride ldc), as for nc_op_gemm.  The pages' later runs train most
+ * linear layers in FP8 with one scale per tensor (apidog.com, "3. Manajemen
+ * Presisi (nanochat/common.py)"); alpha carries the product of the two inverse
+ * scales.  splits > 1 splits K over that many workgroups per output tile (fp32
+ * epilogues only), the partials going to workspace (splits * M * N * 4 bytes)
+ * and summed in a fixed order; splits 1 needs no workspace.
  * Requirements: K % 128 == 0, lda and ldb multiples of 16, 16-byte aligned
  * operands (NC_ERR_UNSUPPORTED otherwise). */
-nc_status nc_op_gemm_fp8(const void* A, size_t A_bytes, int64_t lda, const void* B,
-                         size_t B_bytes, int64_t ldb, void* C, size_t C_bytes, int64_t ldc,
-                         int32_t M, int32_t N, int32_t K, int32_t epilogue, float alpha,
-                         void* stream);
+nc_status nc_op_gemm_fp8(int32_t a_format, const void* A, size_t A_bytes, int64_t lda,
+                         const void* B, size_t B_bytes, int64_t ldb, void* C, size_t C_bytes,
+                         int64_t ldc, int32_t M, int32_t N, int32_t K, int32_t epilogue,
+                         const void* aux_in, size_t aux_in_bytes, float alpha, int32_t splits,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
-/* Tensorwise fp8 quantisation of n values x (dtype NC_FP32 or NC_BF16):
- * amax_scale[0] = max |x|, amax_scale[1] = s = 448 / amax (1 if amax = 0), and
- * q[i] = e4m3(x[i] * s) rounded to nearest even and saturated at 448, so that
- * x ~ q / s.  A NaN in x makes amax and s NaN and every code 0x7F (e4m3 NaN).
- * amax_scale: 2 device floats; workspace: 1024 device floats of scratch. */
-nc_status nc_op_fp8_quantize(int32_t dtype, const void* x, size_t x_bytes, int64_t n,
-                             float* amax_scale, size_t amax_scale_bytes, void* q, size_t q_bytes,
-                             float* workspace, size_t workspace_bytes, void* stream);
+/* Tensorwise fp8 quantisation of x [rows, cols] (row stride cols; dtype
+ * NC_FP32 or NC_BF16) to format NC_FP8_E4M3 (largest finite 448) or
+ * NC_FP8_E5M2 (57344): amax_scale[0] = max |x|, amax_scale[1] = s = largest /
+ * amax (1 if amax = 0), and each code = fp8(x * s) rounded to nearest even and
+ * saturated at the largest finite value, so that x ~ code / s.  Codes go to q
+ * in x's layout [rows, cols] and/or to qt transposed [cols, rows] (either may
+ * be null, not both; qt needs NC_BF16, rows and cols multiples of 64, 16-byte
+ * aligned x and qt; q then 8-byte aligned).  A NaN in x makes amax and s NaN
+ * and every code 0x7F (NaN in both formats).  amax_scale: 2 device floats;
+ * workspace: 1024 device floats of scratch. */
+nc_status nc_op_fp8_quantize(int32_t dtype, int32_t format, const void* x, size_t x_bytes,
+                             int64_t rows, int64_t cols, float* amax_scale,
+                             size_t amax_scale_bytes, void* q, size_t q_bytes, void* qt,
+                             size_t qt_bytes, float* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /* Causal attention forward, head dim 128, scale 1/sqrt(128).  q, k, v:
  * token-major rows (row b*T + t, head h at columns h*128 .. h*128+127, row

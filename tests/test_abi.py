@@ -66,6 +66,15 @@ def test_invalid_configurations_are_rejected():
     assert _status_of_plan(replace(small, fp8_forward=True)) == nc.NC_OK
     assert _status_of_plan(replace(small, d_ff=1600, fp8_forward=True)) == nc.NC_ERR_UNSUPPORTED
     assert _status_of_plan(replace(small, d_ff=1600)) == nc.NC_OK
+    # fp8 backward products reuse the forward's codes and sum tokens in steps of 128
+    assert _status_of_plan(replace(small, fp8_forward=True, fp8_backward=True)) == nc.NC_OK
+    assert _status_of_plan(replace(small, fp8_backward=True)) == nc.NC_ERR_UNSUPPORTED
+    assert _status_of_plan(replace(small, seq_len=192, fp8_forward=True,
+                                   fp8_backward=True)) == nc.NC_ERR_UNSUPPORTED
+    _, a8b = nc.plan(replace(small, fp8_forward=True, fp8_backward=True))
+    _, a8 = nc.plan(replace(small, fp8_forward=True))
+    N, d, F = 4 * 128, 128, 1536            # the kept transposed codes: L [3d + F, N] bytes
+    assert a8b - a8 >= 2 * N * (3 * d + F)
     o = OptimConfig(ns_coeffs=((1.0, 0.0, 0.0),) * 8)
     assert _status_of_plan(TINY, o) == nc.NC_OK
     c = nc.optim_cfg_c(o)
@@ -102,18 +111,19 @@ SMALL_BF16 = dict(name="small", n_layer=2, d_model=384, n_head=3, head_dim=128, 
 @pytest.mark.parametrize("name", ["tiny", "small", "d12", "d20", "d24", "d26", "small_gqa",
                                   "d20_gqa", "d26_gqa", "small_fp8", "d20_fp8", "d26_gqa_fp8",
                                   "tiny_feat", "small_feat", "d20_feat", "d20_gqa_feat",
-                                  "small_fp8_feat"])
+                                  "small_fp8_feat", "small_fp8b", "d20_fp8b", "d26_gqa_fp8b",
+                                  "small_fp8b_feat"])
 def test_every_launch_of_a_step_stays_inside_the_arenas(name):
     """Dry run of nc_fwd_bwd + nc_optimizer_step: every GEMM operand extent is
     checked against the planned arenas (no device access)."""
     from dataclasses import replace as dc_replace
     from gpt_pretraining_step_gemms_amd.configs import ModelConfig
-    base = name.replace("_gqa", "").replace("_fp8", "").replace("_feat", "")
+    base = name.replace("_gqa", "").replace("_fp8b", "").replace("_fp8", "").replace("_feat", "")
     cfg = ModelConfig(**SMALL_BF16) if base == "small" else CONFIGS[base]
     if "_gqa" in name:
         cfg = dc_replace(cfg, n_kv_head=1)
     if "_fp8" in name:
-        cfg = dc_replace(cfg, fp8_forward=True)
+        cfg = dc_replace(cfg, fp8_forward=True, fp8_backward="_fp8b" in name)
     if "_feat" in name:
         cfg = dc_replace(cfg, value_embeds=True, resid_lambdas=True, smear=True, backout=True)
     lib = nc.load()
@@ -321,20 +331,36 @@ def test_op_argument_errors_return_before_any_launch():
     fake = ctypes.c_void_p(0x100000)
     fp = ctypes.c_void_p(0x200000)
     BIG = 1 << 40
-    # fp8 GEMM: epilogue, leading dimensions, K
-    args = lambda K, lda, ldb, ldc, epi: (fake, BIG, lda, fake, BIG, ldb, fake, BIG, ldc, 64, 64,
-                                          K, epi, 1.0, None)
-    assert lib.nc_op_gemm_fp8(*args(256, 256, 256, 64, nc.EPI_RELU2_BWD)) == nc.NC_ERR_INVALID_ARG
-    assert lib.nc_op_gemm_fp8(*args(256, 128, 256, 64, nc.EPI_STORE)) == nc.NC_ERR_INVALID_ARG
-    assert lib.nc_op_gemm_fp8(*args(192, 192, 192, 64, nc.EPI_STORE)) == nc.NC_ERR_UNSUPPORTED
-    assert lib.nc_op_gemm_fp8(*args(256, 264, 256, 64, nc.EPI_STORE)) == nc.NC_ERR_UNSUPPORTED
-    assert lib.nc_op_gemm_fp8(None, BIG, 256, fake, BIG, 256, fake, BIG, 64, 64, 64, 256, 0, 1.0,
-                              None) == nc.NC_ERR_INVALID_ARG
-    # fp8 quantiser
-    q = lambda dt, n, ws: lib.nc_op_fp8_quantize(dt, fake, BIG, n, fp, 8, fake, BIG, ws, 4096, None)
-    assert q(nc.NC_FP32, 0, fp) == nc.NC_ERR_INVALID_ARG
-    assert q(7, 16, fp) == nc.NC_ERR_INVALID_ARG
-    assert q(nc.NC_FP32, 16, None) == nc.NC_ERR_INVALID_ARG
+    # fp8 GEMM: format, epilogue, leading dimensions, K, split-K
+    def g8(K, lda, ldb, ldc, epi, fmt=nc.FP8_E4M3, aux=None, splits=1, ws=None, ws_bytes=0):
+        return lib.nc_op_gemm_fp8(fmt, fake, BIG, lda, fake, BIG, ldb, fake, BIG, ldc, 64, 64, K,
+                                  epi, aux, BIG if aux else 0, 1.0, splits, ws, ws_bytes, None)
+    assert g8(256, 256, 256, 64, nc.EPI_POLY) == nc.NC_ERR_INVALID_ARG
+    assert g8(256, 256, 256, 64, nc.EPI_RELU2_BWD) == nc.NC_ERR_INVALID_ARG      # no aux_in
+    assert g8(256, 256, 256, 64, nc.EPI_STORE, fmt=2) == nc.NC_ERR_INVALID_ARG
+    assert g8(256, 128, 256, 64, nc.EPI_STORE) == nc.NC_ERR_INVALID_ARG
+    assert g8(192, 192, 192, 64, nc.EPI_STORE) == nc.NC_ERR_UNSUPPORTED
+    assert g8(256, 264, 256, 64, nc.EPI_STORE) == nc.NC_ERR_UNSUPPORTED
+    assert g8(256, 256, 256, 64, nc.EPI_STORE, splits=2, ws=fp, ws_bytes=BIG) == nc.NC_ERR_INVALID_ARG
+    assert g8(256, 256, 256, 64, nc.EPI_ACC_F32, splits=2) == nc.NC_ERR_INVALID_ARG   # no workspace
+    assert g8(256, 256, 256, 64, nc.EPI_ACC_F32, splits=2, ws=fp,
+              ws_bytes=2 * 64 * 64 * 4 - 4) == nc.NC_ERR_INVALID_ARG
+    assert g8(256, 256, 256, 64, nc.EPI_STORE, splits=0) == nc.NC_ERR_INVALID_ARG
+    assert lib.nc_op_gemm_fp8(0, None, BIG, 256, fake, BIG, 256, fake, BIG, 64, 64, 64, 256, 0,
+                              None, 0, 1.0, 1, None, 0, None) == nc.NC_ERR_INVALID_ARG
+    # fp8 quantiser: dtype, format, sizes, a destination, the transposed layout's limits
+    def q(dt, rows, cols, ws, fmt=nc.FP8_E4M3, qd=fake, qt=None):
+        return lib.nc_op_fp8_quantize(dt, fmt, fake, BIG, rows, cols, fp, 8, qd, BIG, qt,
+                                      BIG if qt else 0, ws, 4096, None)
+    assert q(nc.NC_FP32, 0, 16, fp) == nc.NC_ERR_INVALID_ARG
+    assert q(nc.NC_FP32, 1, 0, fp) == nc.NC_ERR_INVALID_ARG
+    assert q(7, 1, 16, fp) == nc.NC_ERR_INVALID_ARG
+    assert q(nc.NC_FP32, 1, 16, None) == nc.NC_ERR_INVALID_ARG
+    assert q(nc.NC_BF16, 1, 16, fp, fmt=3) == nc.NC_ERR_INVALID_ARG
+    assert q(nc.NC_BF16, 64, 64, fp, qd=None) == nc.NC_ERR_INVALID_ARG            # no output
+    assert q(nc.NC_FP32, 64, 64, fp, qt=fake) == nc.NC_ERR_UNSUPPORTED           # fp32, transposed
+    assert q(nc.NC_BF16, 64, 96, fp, qt=fake) == nc.NC_ERR_UNSUPPORTED           # cols % 64
+    assert q(nc.NC_BF16, 1 << 40, 1 << 40, fp) == nc.NC_ERR_INVALID_ARG          # size overflow
     # attention: key/value heads must divide the query heads; window >= -1; bf16 T % 128
     def fwd(H, hkv, win, T=256, dt=nc.NC_BF16):
         return lib.nc_op_attention_fwd(dt, fake, BIG, fake, BIG, fake, BIG, 3 * 128 * H, fake, BIG,
@@ -400,13 +426,17 @@ def test_op_operand_extents_are_checked_before_any_launch():
     assert gemm(epi=nc.EPI_RELU2_BWD, aux=M * N * 2 - 2) == nc.NC_ERR_INVALID_ARG
     assert gemm(splits=4, ws_bytes=4 * M * N * 4 - 4) == nc.NC_ERR_INVALID_ARG
     # fp8 GEMM and quantiser
-    assert lib.nc_op_gemm_fp8(fake, 64 * 256 - 1, 256, fake, BIG, 256, fake, BIG, 64, 64, 64, 256,
-                              nc.EPI_STORE, 1.0, None) == nc.NC_ERR_INVALID_ARG
-    assert lib.nc_op_gemm_fp8(fake, BIG, 256, fake, BIG, 256, fake, 64 * 64 * 4 - 4, 64, 64, 64,
-                              256, nc.EPI_STORE_F32, 1.0, None) == nc.NC_ERR_INVALID_ARG
-    qz = lambda xb, qb, ab=8, wb=4096: lib.nc_op_fp8_quantize(nc.NC_BF16, fake, xb, 1000, fake, ab,
-                                                              fake, qb, fake, wb, None)
+    g8 = lambda a_bytes=BIG, c_bytes=BIG, epi=nc.EPI_STORE, aux=None, aux_bytes=0: \
+        lib.nc_op_gemm_fp8(0, fake, a_bytes, 256, fake, BIG, 256, fake, c_bytes, 64, 64, 64, 256,
+                           epi, aux, aux_bytes, 1.0, 1, None, 0, None)
+    assert g8(a_bytes=64 * 256 - 1) == nc.NC_ERR_INVALID_ARG
+    assert g8(c_bytes=64 * 64 * 4 - 4, epi=nc.EPI_STORE_F32) == nc.NC_ERR_INVALID_ARG
+    assert g8(epi=nc.EPI_RELU2_BWD, aux=fake, aux_bytes=64 * 64 * 2 - 2) == nc.NC_ERR_INVALID_ARG
+    qz = lambda xb, qb, ab=8, wb=4096, qtb=0: lib.nc_op_fp8_quantize(
+        nc.NC_BF16, 0, fake, xb, 1000, 1, fake, ab, fake, qb, fake if qtb else None, qtb, fake, wb,
+        None)
     assert qz(1999, BIG) == nc.NC_ERR_INVALID_ARG
     assert qz(BIG, 999) == nc.NC_ERR_INVALID_ARG
     assert qz(BIG, BIG, ab=4) == nc.NC_ERR_INVALID_ARG
     assert qz(BIG, BIG, wb=4092) == nc.NC_ERR_INVALID_ARG
+    assert qz(BIG, BIG, qtb=999) == nc.NC_ERR_INVALID_ARG

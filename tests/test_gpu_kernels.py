@@ -580,3 +580,125 @@ def test_fp8_gemm_mlp_up_shape_sampled():
     a = A8[torch.from_numpy(rows).cuda()].cpu().numpy()
     ref = ofp8.fp8_matmul(a, B8.cpu().numpy(), 0.25)
     assert max_rel(host(C[torch.from_numpy(rows).cuda()]), ref) < 2e-4
+
+
+@pytest.mark.parametrize("dtype,n", [(F32, 1000), (F32, 300001), (BF, 65536 + 7)])
+def test_fp8_quantize_e5m2_bit_exact(dtype, n):
+    """Tensorwise e5m2 (gradients): amax, scale 57344 / amax and every byte
+    equal to the oracle's table-search codec."""
+    rng = np.random.default_rng(n + 1)
+    x = rng.standard_normal(n).astype(np.float32) * rng.uniform(1e-7, 1e-3)
+    x[:6] = [0.0, -0.0, 1e-30, -2e-12, 3e-5, -3e-5]
+    xd = dev(x, dtype)
+    xs = host(xd).astype(np.float32)
+    q = torch.empty(n, dtype=torch.uint8, device="cuda")
+    amax_scale = torch.empty(2, dtype=F32, device="cuda")
+    ws = torch.empty(1024, dtype=F32, device="cuda")
+    nc.fp8_quantize(xd, q, amax_scale, ws, fmt=nc.FP8_E5M2)
+    torch.cuda.synchronize()
+    codes, amax, scale = ofp8.quantize_tensorwise(xs, ofp8.E5M2)
+    assert tuple(host(amax_scale)) == (amax, scale)
+    got = q.cpu().numpy()
+    assert np.array_equal(got, codes), np.flatnonzero(got != codes)[:10]
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("R,C,both", [(64, 64, True), (192, 320, True), (2048, 1280, True),
+                                      (512, 5120, False)])
+def test_fp8_quantize_transposed_codes(fmt, R, C, both):
+    """The 2-D quantiser: codes in x's layout and transposed, byte for byte the
+    oracle's codes and their transpose (and the transposed ones alone)."""
+    rng = np.random.default_rng(R + C + fmt)
+    x = (rng.standard_normal((R, C)) * (1e-4 if fmt else 1.0)).astype(np.float32)
+    xd = dev(x, BF)
+    xs = host(xd).astype(np.float32)
+    q = torch.zeros(R, C, dtype=torch.uint8, device="cuda") if both else None
+    qt = torch.zeros(C, R, dtype=torch.uint8, device="cuda")
+    amax_scale = torch.empty(2, dtype=F32, device="cuda")
+    ws = torch.empty(1024, dtype=F32, device="cuda")
+    print(f"[fp8 quantize 2d] fmt={fmt} R={R} C={C}", flush=True)
+    nc.fp8_quantize(xd, q, amax_scale, ws, fmt=fmt, qt=qt, rows=R, cols=C)
+    torch.cuda.synchronize()
+    codes, amax, scale = ofp8.quantize_tensorwise(xs, ofp8.E5M2 if fmt else ofp8.E4M3)
+    assert tuple(host(amax_scale)) == (amax, scale)
+    if both:
+        assert np.array_equal(q.cpu().numpy(), codes)
+    assert np.array_equal(qt.cpu().numpy(), codes.T)
+
+
+def _e5m2_e4m3_operands(rng, M, N, K, a_std=1e-4):
+    a, _, sa = ofp8.quantize_tensorwise(a_std * rng.standard_normal((M, K)), ofp8.E5M2)
+    b, _, sb = ofp8.quantize_tensorwise(0.02 * rng.standard_normal((N, K)), ofp8.E4M3)
+    return a, b, 1.0 / (sa * sb)
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 128), (300, 520, 256), (70, 40, 384),
+                                   (513, 1000, 2048)])
+def test_fp8_gemm_e5m2_a_vs_oracle(M, N, K):
+    """A in e5m2 (a gradient), B in e4m3: C = alpha A B^T against the fp64
+    product of the decoded values (same bound as the e4m3 x e4m3 product; a
+    wrong format code would misread every A byte)."""
+    rng = np.random.default_rng(M * 7 + N + K)
+    a, b, alpha = _e5m2_e4m3_operands(rng, M, N, K)
+    ref = ofp8.fp8_matmul(a, b, alpha, ofp8.E5M2, ofp8.E4M3)
+    A8, B8 = torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()
+    print(f"[fp8 gemm e5m2] M={M} N={N} K={K}", flush=True)
+    Cf = torch.empty(M, N, dtype=F32, device="cuda")
+    nc.gemm_fp8(A8, B8, Cf, M, N, K, alpha, epilogue=nc.EPI_STORE_F32, a_format=nc.FP8_E5M2)
+    torch.cuda.synchronize()
+    err = max_rel(host(Cf), ref)
+    print(f"[fp8 gemm e5m2] max-rel {err:.2e}", flush=True)
+    assert err < 2e-4
+
+
+@pytest.mark.parametrize("splits", [2, 5])
+def test_fp8_gemm_split_k_and_relu2_backward(splits):
+    """Split-K on fp8 operands (fp32 partials summed in a fixed order, added to
+    C) equals the unsplit product to the kernel's rounding, and the ReLU^2
+    backward epilogue 2 sqrt(g) acc reads its bf16 aux rows."""
+    M, N, K = 320, 384, 2048
+    rng = np.random.default_rng(splits)
+    a, b, alpha = _e5m2_e4m3_operands(rng, M, N, K)
+    ref = ofp8.fp8_matmul(a, b, alpha, ofp8.E5M2, ofp8.E4M3)
+    A8, B8 = torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()
+    c0 = rng.standard_normal((M, N)).astype(np.float32)
+    C = torch.from_numpy(c0).cuda()
+    ws = torch.empty(splits * M * N, dtype=F32, device="cuda")
+    nc.gemm_fp8(A8, B8, C, M, N, K, alpha, epilogue=nc.EPI_ACC_F32, a_format=nc.FP8_E5M2,
+                splits=splits, workspace=ws)
+    C1 = torch.from_numpy(c0).cuda()
+    nc.gemm_fp8(A8, B8, C1, M, N, K, alpha, epilogue=nc.EPI_ACC_F32, a_format=nc.FP8_E5M2)
+    g = np.abs(rng.standard_normal((M, N))).astype(np.float32)
+    gd = dev(g, BF)
+    D = torch.empty(M, N, dtype=BF, device="cuda")
+    nc.gemm_fp8(A8, B8, D, M, N, K, alpha, epilogue=nc.EPI_RELU2_BWD, a_format=nc.FP8_E5M2,
+                aux_in=gd)
+    torch.cuda.synchronize()
+    scale = np.max(np.abs(ref))
+    assert np.max(np.abs(host(C) - (c0 + ref))) < 2e-4 * scale + 1e-6
+    assert np.max(np.abs(host(C) - host(C1))) < 2e-4 * scale + 1e-6
+    d_ref = 2.0 * np.sqrt(host(gd).astype(np.float64)) * ref
+    assert max_rel(host(D), d_ref) < 2 ** -7
+
+
+def test_fp8_gemm_weight_gradient_shape_sampled():
+    """The weight-gradient shape of a d20 micro-batch (dW2: [1280, 5120],
+    K = 65536 tokens) in fp8 with the split count the step uses: sampled
+    rows against the decoded product."""
+    M, N, K = 1280, 5120, 65536
+    splits = 5                                       # what the split cost model picks here
+    g = torch.Generator(device="cuda").manual_seed(9)
+    A8 = torch.randint(0, 256, (M, K), dtype=torch.uint8, device="cuda", generator=g)
+    B8 = torch.randint(0, 256, (N, K), dtype=torch.uint8, device="cuda", generator=g)
+    A8 &= 0xB3                                       # e5m2: no inf/NaN codes, modest magnitudes
+    B8 &= 0xB7                                       # e4m3: no NaN codes
+    C = torch.zeros(M, N, dtype=F32, device="cuda")
+    ws = torch.empty(splits * M * N, dtype=F32, device="cuda")
+    print(f"[fp8 dW shape] splits={splits}", flush=True)
+    nc.gemm_fp8(A8, B8, C, M, N, K, 1.0, epilogue=nc.EPI_ACC_F32, a_format=nc.FP8_E5M2,
+                splits=splits, workspace=ws)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 640, M - 1])
+    a = A8[torch.from_numpy(rows).cuda()].cpu().numpy()
+    ref = ofp8.fp8_matmul(a, B8.cpu().numpy(), 1.0, ofp8.E5M2, ofp8.E4M3)
+    assert max_rel(host(C[torch.from_numpy(rows).cuda()]), ref) < 2e-4
