@@ -63,6 +63,25 @@ NC_DEV float block_max(float v, float* red) {
   return s;
 }
 
+// The maximum that keeps a NaN (fmaxf drops it): a NaN anywhere in a tensor
+// makes its fp8 amax and scale NaN, and with them every code (0x7F).
+NC_DEV float max_nan(float a, float b) { return (a > b || a != a) ? a : b; }
+NC_DEV float block_max_nan(float v, float* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max_nan(v, __shfl_xor(v, o, kWave));
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.f;
+  for (int i = 0; i < nw; ++i) s = max_nan(s, red[i]);
+  return s;
+}
+// |x| rounded to bf16 as a float: round-to-nearest is monotonic, so the largest
+// |bf16(x_i)| of a set equals bf16(max |x_i|), and a producer can keep the max
+// of its fp32 values and round once
+NC_DEV float bf16_abs(float x) { return fabsf(static_cast<float>(static_cast<bf16>(x))); }
+
 // ------------------------------------------------------ 8x8 16-bit transpose
 // in[j] holds 8 consecutive 16-bit values of row j (4 dwords); out[i] receives
 // column i, i.e. element i of every row, as 8 consecutive 16-bit values.

@@ -192,70 +192,92 @@ __global__ __launch_bounds__(256) void embed_fixup_kernel(const int32_t* __restr
 // ------------------------------------------------------------------ RMSNorm
 constexpr int kMaxVec = 8;  // float4 per lane: d <= 2048
 
+// amax_part (optional, bf16 outputs): per block the largest |y| (|dxT| in the
+// backward) as stored, for the output's fp8 scale without another pass over it.
 template <typename T>
 __global__ void rmsnorm_fwd_kernel(const float* __restrict__ x, T* __restrict__ y,
-                                   float* __restrict__ r, int rows, int d, float eps) {
+                                   float* __restrict__ r, int rows, int d, float eps,
+                                   float* __restrict__ amax_part) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
   const int lane = threadIdx.x & 63;
-  const float* xr = x + (int64_t)row * d;
-  float v[kMaxVec][4];
-  float ss = 0.f;
+  float amx = 0.f;
+  if (row < rows) {
+    const float* xr = x + (int64_t)row * d;
+    float v[kMaxVec][4];
+    float ss = 0.f;
 #pragma unroll
-  for (int k = 0; k < kMaxVec; ++k) {
-    const int i = (lane + k * 64) * 4;
-    if (i < d) {
-      Vec4<float>::load(xr + i, v[k]);
-      ss += v[k][0] * v[k][0] + v[k][1] * v[k][1] + v[k][2] * v[k][2] + v[k][3] * v[k][3];
+    for (int k = 0; k < kMaxVec; ++k) {
+      const int i = (lane + k * 64) * 4;
+      if (i < d) {
+        Vec4<float>::load(xr + i, v[k]);
+        ss += v[k][0] * v[k][0] + v[k][1] * v[k][1] + v[k][2] * v[k][2] + v[k][3] * v[k][3];
+      }
+    }
+    ss = wave_sum(ss);
+    const float rs = 1.0f / sqrtf(ss / d + eps);
+    if (lane == 0) r[row] = rs;
+    T* yr = y + (int64_t)row * d;
+#pragma unroll
+    for (int k = 0; k < kMaxVec; ++k) {
+      const int i = (lane + k * 64) * 4;
+      if (i < d) {
+        float o[4] = {v[k][0] * rs, v[k][1] * rs, v[k][2] * rs, v[k][3] * rs};
+        Vec4<T>::store(yr + i, o);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) amx = max_nan(amx, fabsf(o[e]));
+      }
     }
   }
-  ss = wave_sum(ss);
-  const float rs = 1.0f / sqrtf(ss / d + eps);
-  if (lane == 0) r[row] = rs;
-  T* yr = y + (int64_t)row * d;
-#pragma unroll
-  for (int k = 0; k < kMaxVec; ++k) {
-    const int i = (lane + k * 64) * 4;
-    if (i < d) {
-      float o[4] = {v[k][0] * rs, v[k][1] * rs, v[k][2] * rs, v[k][3] * rs};
-      Vec4<T>::store(yr + i, o);
-    }
+  if (amax_part) {                                 // the same for every thread of the block
+    __shared__ float red[4];
+    amx = block_max_nan(amx, red);
+    if (threadIdx.x == 0) amax_part[blockIdx.x] = bf16_abs(amx);
   }
 }
 
 template <typename T>
 __global__ void rmsnorm_bwd_kernel(const float* __restrict__ dy, const T* __restrict__ y,
                                    const float* __restrict__ r, float* __restrict__ dx,
-                                   T* __restrict__ dxT, int rows, int d, int accumulate) {
+                                   T* __restrict__ dxT, int rows, int d, int accumulate,
+                                   float* __restrict__ amax_part) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
   const int lane = threadIdx.x & 63;
-  const int64_t off = (int64_t)row * d;
-  float g[kMaxVec][4], yy[kMaxVec][4];
-  float dot = 0.f;
+  float amx = 0.f;
+  if (row < rows) {
+    const int64_t off = (int64_t)row * d;
+    float g[kMaxVec][4], yy[kMaxVec][4];
+    float dot = 0.f;
 #pragma unroll
-  for (int k = 0; k < kMaxVec; ++k) {
-    const int i = (lane + k * 64) * 4;
-    if (i < d) {
-      Vec4<float>::load(dy + off + i, g[k]);
-      Vec4<T>::load(y + off + i, yy[k]);
-      dot += g[k][0] * yy[k][0] + g[k][1] * yy[k][1] + g[k][2] * yy[k][2] + g[k][3] * yy[k][3];
+    for (int k = 0; k < kMaxVec; ++k) {
+      const int i = (lane + k * 64) * 4;
+      if (i < d) {
+        Vec4<float>::load(dy + off + i, g[k]);
+        Vec4<T>::load(y + off + i, yy[k]);
+        dot += g[k][0] * yy[k][0] + g[k][1] * yy[k][1] + g[k][2] * yy[k][2] + g[k][3] * yy[k][3];
+      }
+    }
+    const float mean = wave_sum(dot) / d;
+    const float rs = r[row];
+#pragma unroll
+    for (int k = 0; k < kMaxVec; ++k) {
+      const int i = (lane + k * 64) * 4;
+      if (i < d) {
+        float o[4];
+        if (accumulate) Vec4<float>::load(dx + off + i, o);
+        else o[0] = o[1] = o[2] = o[3] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] += rs * (g[k][e] - yy[k][e] * mean);
+        Vec4<float>::store(dx + off + i, o);
+        Vec4<T>::store(dxT + off + i, o);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) amx = max_nan(amx, fabsf(o[e]));
+      }
     }
   }
-  const float mean = wave_sum(dot) / d;
-  const float rs = r[row];
-#pragma unroll
-  for (int k = 0; k < kMaxVec; ++k) {
-    const int i = (lane + k * 64) * 4;
-    if (i < d) {
-      float o[4];
-      if (accumulate) Vec4<float>::load(dx + off + i, o);
-      else o[0] = o[1] = o[2] = o[3] = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] += rs * (g[k][e] - yy[k][e] * mean);
-      Vec4<float>::store(dx + off + i, o);
-      Vec4<T>::store(dxT + off + i, o);
-    }
+  if (amax_part) {
+    __shared__ float red[4];
+    amx = block_max_nan(amx, red);
+    if (threadIdx.x == 0) amax_part[blockIdx.x] = bf16_abs(amx);
   }
 }
 
@@ -753,21 +775,6 @@ inline int grid1d(size_t n, int block = 256) {
 
 
 // ------------------------------------- fp8 (e4m3, e5m2), tensorwise scale
-// The maximum that keeps a NaN (fmaxf drops it): a NaN anywhere in a tensor
-// makes its amax and scale NaN, and with them every code (0x7F).
-NC_DEV float max_nan(float a, float b) { return (a > b || a != a) ? a : b; }
-NC_DEV float block_max_nan(float v, float* red) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max_nan(v, __shfl_xor(v, o, kWave));
-  __syncthreads();
-  if (lane == 0) red[w] = v;
-  __syncthreads();
-  float s = 0.f;
-  for (int i = 0; i < nw; ++i) s = max_nan(s, red[i]);
-  return s;
-}
-
 // amax: per-block partial maxima of |x| (fixed order), then one block folds them
 template <typename T>
 __global__ __launch_bounds__(256) void amax_partial_kernel(const T* __restrict__ x, int64_t n,
@@ -997,20 +1004,23 @@ hipError_t nc_embed_bwd(const int32_t* tok, const float* dx, float* dE, int n_to
 }
 
 hipError_t nc_rmsnorm_fwd(int dtype, const float* x, void* y, float* r, int rows, int d,
-                          float eps, hipStream_t st) {
+                          float eps, hipStream_t st, float* amax_part) {
   const int g = ceil_div(rows, 4);
-  if (dtype) rmsnorm_fwd_kernel<bf16><<<g, 256, 0, st>>>(x, (bf16*)y, r, rows, d, eps);
-  else rmsnorm_fwd_kernel<float><<<g, 256, 0, st>>>(x, (float*)y, r, rows, d, eps);
+  if (dtype) rmsnorm_fwd_kernel<bf16><<<g, 256, 0, st>>>(x, (bf16*)y, r, rows, d, eps, amax_part);
+  else rmsnorm_fwd_kernel<float><<<g, 256, 0, st>>>(x, (float*)y, r, rows, d, eps, amax_part);
   return hipGetLastError();
 }
 
 hipError_t nc_rmsnorm_bwd(int dtype, const float* dy, const void* y, const float* r, float* dx,
-                          void* dxT, int rows, int d, int accumulate, hipStream_t st) {
+                          void* dxT, int rows, int d, int accumulate, hipStream_t st,
+                          float* amax_part) {
   const int g = ceil_div(rows, 4);
   if (dtype)
-    rmsnorm_bwd_kernel<bf16><<<g, 256, 0, st>>>(dy, (const bf16*)y, r, dx, (bf16*)dxT, rows, d, accumulate);
+    rmsnorm_bwd_kernel<bf16><<<g, 256, 0, st>>>(dy, (const bf16*)y, r, dx, (bf16*)dxT, rows, d,
+                                                accumulate, amax_part);
   else
-    rmsnorm_bwd_kernel<float><<<g, 256, 0, st>>>(dy, (const float*)y, r, dx, (float*)dxT, rows, d, accumulate);
+    rmsnorm_bwd_kernel<float><<<g, 256, 0, st>>>(dy, (const float*)y, r, dx, (float*)dxT, rows, d,
+                                                 accumulate, amax_part);
   return hipGetLastError();
 }
 
@@ -1173,26 +1183,13 @@ hipError_t nc_normuon_stats(const float* X, int64_t x_stride, int R, int C, int 
   return hipGetLastError();
 }
 
-hipError_t nc_fp8_quantize(int dtype, int fmt, const void* x, int64_t rows, int64_t cols,
-                           float* partial, float* amax_scale, uint8_t* q, uint8_t* qt,
-                           hipStream_t st) {
+// The codes of x with the scale already in amax_scale[1].
+static hipError_t fp8_codes(int dtype, int fmt, const void* x, int64_t rows, int64_t cols,
+                     const float* amax_scale, uint8_t* q, uint8_t* qt, hipStream_t st) {
   const int64_t n = rows * cols;
-  if (n <= 0) return hipSuccess;
-  if (fmt != 0 && fmt != 1) return hipErrorInvalidValue;
   auto al = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; };
-  if (qt && !(dtype && rows % 64 == 0 && cols % 64 == 0 && rows <= 0x7fffffff &&
-              cols <= 0x7fffffff && al(x, 16) && al(q, 8) && al(qt, 16)))
-    return hipErrorInvalidValue;
   const bool vec = dtype && al(x, 16) && al(q, 8);
-  const int64_t per = vec ? 8 * 256 : 256;          // values per block and pass
-  const int parts = (int)std::min<int64_t>(std::max<int64_t>(ceil_div64(n, per), 1), 1024);
-  if (vec)
-    amax_partial_bf16x8_kernel<<<parts, 256, 0, st>>>((const bf16*)x, n, partial);
-  else if (dtype)
-    amax_partial_kernel<bf16><<<parts, 256, 0, st>>>((const bf16*)x, n, partial);
-  else
-    amax_partial_kernel<float><<<parts, 256, 0, st>>>((const float*)x, n, partial);
-  amax_final_kernel<<<1, 256, 0, st>>>(partial, parts, fmt ? 57344.f : 448.f, amax_scale);
+  const int64_t per = vec ? 8 * 256 : 256;
   if (qt) {
     const int64_t tiles = (rows / 64) * (cols / 64);
     if (tiles > 0x7fffffff) return hipErrorInvalidValue;
@@ -1217,3 +1214,40 @@ hipError_t nc_fp8_quantize(int dtype, int fmt, const void* x, int64_t rows, int6
   if (fmt) launch.template operator()<1>(); else launch.template operator()<0>();
   return hipGetLastError();
 }
+
+hipError_t nc_fp8_quantize(int dtype, int fmt, const void* x, int64_t rows, int64_t cols,
+                           float* partial, float* amax_scale, uint8_t* q, uint8_t* qt,
+                           hipStream_t st) {
+  const int64_t n = rows * cols;
+  if (n <= 0) return hipSuccess;
+  if (fmt != 0 && fmt != 1) return hipErrorInvalidValue;
+  auto al = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; };
+  if (qt && !(dtype && rows % 64 == 0 && cols % 64 == 0 && rows <= 0x7fffffff &&
+              cols <= 0x7fffffff && al(x, 16) && al(q, 8) && al(qt, 16)))
+    return hipErrorInvalidValue;
+  const bool vec = dtype && al(x, 16) && al(q, 8);
+  const int64_t per = vec ? 8 * 256 : 256;          // values per block and pass
+  const int parts = (int)std::min<int64_t>(std::max<int64_t>(ceil_div64(n, per), 1), 1024);
+  if (vec)
+    amax_partial_bf16x8_kernel<<<parts, 256, 0, st>>>((const bf16*)x, n, partial);
+  else if (dtype)
+    amax_partial_kernel<bf16><<<parts, 256, 0, st>>>((const bf16*)x, n, partial);
+  else
+    amax_partial_kernel<float><<<parts, 256, 0, st>>>((const float*)x, n, partial);
+  amax_final_kernel<<<1, 256, 0, st>>>(partial, parts, fmt ? 57344.f : 448.f, amax_scale);
+  return fp8_codes(dtype, fmt, x, rows, cols, amax_scale, q, qt, st);
+}
+
+hipError_t nc_fp8_quantize_parts(int fmt, const void* x, int64_t rows, int64_t cols,
+                                 const float* amax_parts, int n_parts, float* amax_scale,
+                                 uint8_t* q, uint8_t* qt, hipStream_t st) {
+  if (rows * cols <= 0) return hipSuccess;
+  if ((fmt != 0 && fmt != 1) || n_parts < 1) return hipErrorInvalidValue;
+  auto al = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; };
+  if (qt && !(rows % 64 == 0 && cols % 64 == 0 && rows <= 0x7fffffff && cols <= 0x7fffffff &&
+              al(x, 16) && al(q, 8) && al(qt, 16)))
+    return hipErrorInvalidValue;
+  amax_final_kernel<<<1, 256, 0, st>>>(amax_parts, n_parts, fmt ? 57344.f : 448.f, amax_scale);
+  return fp8_codes(1, fmt, x, rows, cols, amax_scale, q, qt, st);
+}
+

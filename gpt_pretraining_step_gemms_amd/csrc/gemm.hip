@@ -27,9 +27,10 @@ NC_DEV int swz(int row, int chunk) { return chunk ^ ((row ^ (row >> 3)) & 7); }
 
 // ------------------------------------------------------------------ epilogue
 // One output element at offset `off` of C (and of aux_in / aux_out); every
-// epilogue takes acc = alpha * v.
+// epilogue takes acc = alpha * v.  The ReLU^2 epilogues return |the value
+// before rounding| (for the output's amax), the others 0.
 template <typename T, int EPI>
-NC_DEV void epi_one(const GemmParams& p, int64_t off, float v) {
+NC_DEV float epi_one(const GemmParams& p, int64_t off, float v) {
   if constexpr (EPI == kEpiStore) {
     static_cast<T*>(p.C)[off] = to_t<T>(p.alpha * v);
   } else if constexpr (EPI == kEpiStoreF32) {
@@ -39,10 +40,13 @@ NC_DEV void epi_one(const GemmParams& p, int64_t off, float v) {
   } else if constexpr (EPI == kEpiRelu2) {
     const float r = fmaxf(p.alpha * v, 0.f);
     static_cast<T*>(p.C)[off] = to_t<T>(r * r);
+    return r * r;
   } else if constexpr (EPI == kEpiRelu2Bwd) {
     // v_sqrt_f32 (1 ulp) rather than the correctly rounded library sequence
     const float g = to_f(static_cast<const T*>(p.aux_in)[off]);
-    static_cast<T*>(p.C)[off] = to_t<T>(2.f * __builtin_amdgcn_sqrtf(fmaxf(g, 0.f)) * (p.alpha * v));
+    const float r = 2.f * __builtin_amdgcn_sqrtf(fmaxf(g, 0.f)) * (p.alpha * v);
+    static_cast<T*>(p.C)[off] = to_t<T>(r);
+    return fabsf(r);
   } else if constexpr (EPI == kEpiPoly) {
     const float a = to_f(static_cast<const T*>(p.aux_in)[off]);
     static_cast<T*>(p.C)[off] = to_t<T>(p.p0 * a + p.p1 * (p.alpha * v));
@@ -52,6 +56,15 @@ NC_DEV void epi_one(const GemmParams& p, int64_t off, float v) {
     static_cast<float*>(p.C)[off] = r;
     static_cast<T*>(p.aux_out)[off] = to_t<T>(r);
   }
+  return 0.f;
+}
+
+// largest |r[e]| of 8 values, NaN kept
+NC_DEV float amax8(const float (&r)[8]) {
+  float m = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m = max_nan(m, fabsf(r[e]));
+  return m;
 }
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -86,7 +99,7 @@ NC_DEV void st8(float* q, const float (&x)[8]) {
 // Eight consecutive outputs of one row at offset `off` of C (and aux), with
 // 16-byte accesses: the same arithmetic as epi_one (bf16 activations).
 template <int EPI>
-NC_DEV void epi_vec8(const GemmParams& p, int64_t off, const float (&v)[8]) {
+NC_DEV float epi_vec8(const GemmParams& p, int64_t off, const float (&v)[8]) {
   float r[8], a[8];
   if constexpr (EPI == kEpiStore) {
 #pragma unroll
@@ -108,11 +121,13 @@ NC_DEV void epi_vec8(const GemmParams& p, int64_t off, const float (&v)[8]) {
       r[e] = t * t;
     }
     st8(static_cast<bf16*>(p.C) + off, r);
+    return amax8(r);
   } else if constexpr (EPI == kEpiRelu2Bwd) {
     ld8(static_cast<const bf16*>(p.aux_in) + off, a);
 #pragma unroll
     for (int e = 0; e < 8; ++e) r[e] = 2.f * __builtin_amdgcn_sqrtf(fmaxf(a[e], 0.f)) * (p.alpha * v[e]);
     st8(static_cast<bf16*>(p.C) + off, r);
+    return amax8(r);
   } else if constexpr (EPI == kEpiPoly) {
     ld8(static_cast<const bf16*>(p.aux_in) + off, a);
 #pragma unroll
@@ -130,6 +145,7 @@ NC_DEV void epi_vec8(const GemmParams& p, int64_t off, const float (&v)[8]) {
     st8(static_cast<float*>(p.C) + off, r);
     st8(static_cast<bf16*>(p.aux_out) + off, r);
   }
+  return 0.f;
 }
 
 // The epilogue in two phases, so that a wave can issue the loads of several
@@ -169,8 +185,8 @@ NC_DEV void epi_load8(const GemmParams& p, int64_t off, EpiIn<EPI>& in) {
 }
 // Same arithmetic as epi_one / epi_vec8, on values read by epi_load8.
 template <int EPI>
-NC_DEV void epi_apply8(const GemmParams& p, int64_t off, const float (&v)[8],
-                       const EpiIn<EPI>& in) {
+NC_DEV float epi_apply8(const GemmParams& p, int64_t off, const float (&v)[8],
+                        const EpiIn<EPI>& in) {
   float a[8], r[8];
   if constexpr (epi_reads<EPI>() == 2) {
 #pragma unroll
@@ -187,6 +203,7 @@ NC_DEV void epi_apply8(const GemmParams& p, int64_t off, const float (&v)[8],
 #pragma unroll
     for (int e = 0; e < 8; ++e) r[e] = 2.f * __builtin_amdgcn_sqrtf(fmaxf(a[e], 0.f)) * (p.alpha * v[e]);
     st8(static_cast<bf16*>(p.C) + off, r);
+    return amax8(r);
   } else if constexpr (EPI == kEpiPoly) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) r[e] = p.p0 * a[e] + p.p1 * (p.alpha * v[e]);
@@ -197,8 +214,9 @@ NC_DEV void epi_apply8(const GemmParams& p, int64_t off, const float (&v)[8],
     st8(static_cast<float*>(p.C) + off, r);
     st8(static_cast<bf16*>(p.aux_out) + off, r);
   } else {
-    epi_vec8<EPI>(p, off, v);                      // stores only
+    return epi_vec8<EPI>(p, off, v);               // stores only
   }
+  return 0.f;
 }
 
 // Calls f.template operator()<EPI>() with the epilogue chosen at run time, so
@@ -1077,6 +1095,7 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
   else sbase = sidx == 0 ? st0 : st1;
   float* stg = reinterpret_cast<float*>(sbase) + (wave % EP_PER) * EP_FLOATS;
   const bool split_out = p.splits > 1;
+  float amx = 0.f;                                 // largest |output| of this lane (amax_part)
   float* W = split_out ? p.workspace + ((int64_t)split * p.batch + b) * (int64_t)p.M * p.N
                        : nullptr;
   const int64_t cb = (int64_t)b * p.sC;
@@ -1147,9 +1166,10 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
           } else {
             const int64_t off = cb + (int64_t)m * ld_out + n;
             if (vec && n + 8 <= p.N) {
-              epi_apply8<EPI>(p, off, v, in[ii][t]);
+              amx = max_nan(amx, epi_apply8<EPI>(p, off, v, in[ii][t]));
             } else {
-              for (int e = 0; e < 8 && n + e < p.N; ++e) epi_one<bf16, EPI>(p, off + e, v[e]);
+              for (int e = 0; e < 8 && n + e < p.N; ++e)
+                amx = max_nan(amx, epi_one<bf16, EPI>(p, off + e, v[e]));
             }
           }
         }
@@ -1158,6 +1178,12 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
   };
   if (split_out) run.template operator()<kEpiStoreF32>();
   else with_epilogue(p.epi, run);
+  if (p.amax_part) {
+    // the staging buffers are free once every wave has passed the first
+    // barrier inside block_max_nan
+    amx = block_max_nan(amx, reinterpret_cast<float*>(st0));
+    if (threadIdx.x == 0) p.amax_part[blockIdx.x] = bf16_abs(amx);
+  }
 }
 
 // The pipelined kernel applies when K is a multiple of 32, every operand start
@@ -1272,6 +1298,7 @@ hipError_t nc_launch_gemm_f8(const GemmParams& p_in, hipStream_t st) {
       (p.fmt_a != 0 && p.fmt_a != 1))
     return hipErrorInvalidValue;
   if (p.splits < 1) p.splits = 1;
+  if (p.amax_part && (p.batch != 1 || p.splits != 1)) return hipErrorInvalidValue;
   if (p.splits > 1 && ((p.epi != kEpiStoreF32 && p.epi != kEpiAccF32) || !p.workspace ||
                        p.workspace_bytes < nc_gemm_workspace_bytes(p.M, p.N, p.splits) * p.batch))
     return hipErrorInvalidValue;
@@ -1295,6 +1322,7 @@ hipError_t nc_launch_gemm(int dtype, const GemmParams& p_in, hipStream_t st) {
   if (p.M <= 0 || p.N <= 0 || p.batch <= 0) return hipSuccess;
   if (p.splits < 1) p.splits = 1;
   if (dtype == 0) {
+    if (p.amax_part) return hipErrorInvalidValue;
     p.splits = 1;
     dim3 grid(ceil_div(p.M, 64) * ceil_div(p.N, 64), 1, p.batch);
     const int code = p.a_layout * 2 + p.b_layout;
@@ -1313,6 +1341,7 @@ hipError_t nc_launch_gemm(int dtype, const GemmParams& p_in, hipStream_t st) {
                 al16(p.aux_in) && al16(p.aux_out);
   }
   const bool use_pipe = pipe_ok(p);
+  if (p.amax_part && (!use_pipe || p.batch != 1 || p.splits != 1)) return hipErrorInvalidValue;
   hipError_t e = use_pipe ? launch_pipe(p, st) : launch_bf16_cfg<256, 256, 2, 4>(p, st);
   if (e != hipSuccess || p.splits == 1) return e;
   return splitk_reduce(p, st);

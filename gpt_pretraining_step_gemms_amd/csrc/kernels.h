@@ -74,11 +74,14 @@ hipError_t nc_outer_accumulate(int dtype, const float* A, int H, const void* B, 
 hipError_t nc_sum_into(const float* vals, int n, float* out, hipStream_t st);
 
 // ---- RMSNorm (rows of length d; eps)
+// amax_part (optional): per block of 4 rows, the largest |y| as stored (|dxT| in
+// the backward), ceil(rows / 4) floats, for an fp8 scale of the output.
 hipError_t nc_rmsnorm_fwd(int dtype, const float* x, void* y, float* r, int rows, int d,
-                          float eps, hipStream_t st);
+                          float eps, hipStream_t st, float* amax_part = nullptr);
 // dx (+)= r*(dy - y*mean(dy*y)); also writes dxT = dx in the activation type.
 hipError_t nc_rmsnorm_bwd(int dtype, const float* dy, const void* y, const float* r, float* dx,
-                          void* dxT, int rows, int d, int accumulate, hipStream_t st);
+                          void* dxT, int rows, int d, int accumulate, hipStream_t st,
+                          float* amax_part = nullptr);
 
 // ---- QK RMSNorm + rotary (qkv token-major [n_tok, (H + 2 Hkv)*128]: H q heads, Hkv k
 // heads, Hkv v heads; in place on the q and k heads; rqk [n_tok, H + Hkv])
@@ -117,6 +120,11 @@ hipError_t nc_attn_bwd(int dtype, const void* q, const void* k, const void* v, i
 hipError_t nc_fp8_quantize(int dtype, int fmt, const void* x, int64_t rows, int64_t cols,
                            float* partial, float* amax_scale, uint8_t* q, uint8_t* qt,
                            hipStream_t st);
+// The same with the amax already reduced to n_parts per-block maxima of |x| by
+// x's producer (amax_parts): no pass over x for the scale.
+hipError_t nc_fp8_quantize_parts(int fmt, const void* x, int64_t rows, int64_t cols,
+                                 const float* amax_parts, int n_parts, float* amax_scale,
+                                 uint8_t* q, uint8_t* qt, hipStream_t st);
 
 // ---- softmax cross-entropy over rows of fp32 logits
 // dz = scale*(softmax(z) - onehot(y)) in the activation type; loss_rows[i] = lse - z[y].

@@ -75,11 +75,19 @@ struct nc_ctx {
   // activation arena: feature buffers
   size_t x0b = 0, xprev = 0, dx0b = 0, gbb = 0, xbb = 0, part_a = 0, part_b = 0, sig_s = 0,
          gs_s = 0, dz_s = 0, sig_ve = 0, dz_ve = 0, ve_rows = 0, outer_part = 0;
-  size_t q8a = 0, q8w = 0, q8s = 0, q8ws = 0;   // their codes, scales and amax scratch
+  size_t q8a = 0, q8s = 0, q8ws = 0;   // activation codes, a scale pair, amax scratch
   // fp8 backward: per layer the transposed codes of the four forward activations
   // (a1 [d, N] | o [d, N] | a2 [d, N] | g [F, N]) and their scales (8 floats);
   // the gradient's codes in its layout and transposed, and its scale
   size_t q8xt = 0, q8xt_layer = 0, q8xs = 0, q8dy = 0, q8dyt = 0, q8dys = 0;
+  // the weights' e4m3 codes per layer (Wqkv | Wo | W1 | W2 in their layout,
+  // then, with fp8 backward, transposed) and scales (8 floats per layer), made
+  // once after each change of the weights and reused by every micro-batch
+  size_t q8wc = 0, q8wc_layer = 0, q8wcs = 0;
+  bool w8_ok = false;
+  // per-block maxima of |a tensor|, written by its producer (RMSNorm, the
+  // ReLU^2 epilogues) for the tensor's fp8 scale; q8part_n floats
+  size_t q8part = 0, q8part_n = 0;
   int64_t S, n_block, n_total;
   std::vector<ParamInfo> params;
   // parameter arena byte offsets
@@ -409,11 +417,19 @@ void plan(nc_ctx* c) {
     c->nm_scale = a.take((size_t)6 * L * 4);
   }
   if (c->fp8) {
-    // codes of the largest activation operand [N, max(d, F)] and weight operand
+    // codes of the largest activation operand [N, max(d, F)]
     c->q8a = a.take(N * (size_t)std::max(d, F));
-    c->q8w = a.take((size_t)std::max(W, F) * std::max(d, F));
     c->q8s = a.take(4 * sizeof(float));
     c->q8ws = a.take(1024 * sizeof(float));
+  }
+  if (c->fp8) {
+    c->q8part_n = std::max<size_t>(ceil_div64(N, 4),
+                                   (size_t)ceil_div64(N, 256) * ceil_div(std::max(F, W), 256));
+    c->q8part = a.take(c->q8part_n * sizeof(float));
+    const size_t wn = (size_t)W * d + (size_t)d * d + 2 * (size_t)F * d;
+    c->q8wc_layer = (c->fp8b ? 2 : 1) * wn;
+    c->q8wc = a.take((size_t)L * c->q8wc_layer);
+    c->q8wcs = a.take((size_t)L * 8 * sizeof(float));
   }
   if (c->fp8b) {
     c->q8xt_layer = N * (size_t)(3 * d + F);
@@ -499,17 +515,62 @@ hipError_t gemm(nc_ctx* c, const void* A_, int64_t lda, int al, const void* B_, 
   return nc_launch_gemm(dt, g, c->st);
 }
 
+// fp8 block products: one e4m3 scale per tensor (the pair {amax, s}); the
+// kernel divides the sums by the two operands' s.
+// The weight codes of layer l, product j (0 Wqkv [W, d], 1 Wo [d, d], 2 W1 [F, d],
+// 3 W2 [d, F]): in the weight's layout (transposed = false) or transposed, and
+// the scale pair.
+struct WCodes { uint8_t* q; float* s; };
+WCodes wcodes(nc_ctx* c, int l, int j, bool transposed) {
+  const size_t d = c->d, F = c->F, W = c->W;
+  const size_t off[4] = {0, W * d, W * d + d * d, W * d + d * d + F * d};
+  const size_t half = W * d + d * d + 2 * F * d;
+  uint8_t* base = reinterpret_cast<uint8_t*>(c->aa + c->q8wc) + (size_t)l * c->q8wc_layer;
+  return {base + (transposed ? half : 0) + off[j],
+          reinterpret_cast<float*>(c->aa + c->q8wcs) + (size_t)l * 8 + 2 * j};
+}
+
+// element offsets of Wo and W1 inside a layer's block (Wq | Wk | Wv | Wo | W1 | W2)
+size_t oWo_of(const nc_ctx* c) { return (size_t)c->d * c->d + 2ULL * c->dk * c->d; }
+size_t oW1_of(const nc_ctx* c) { return oWo_of(c) + (size_t)c->d * c->d; }
+
+// The e4m3 codes of every layer's four weights (bf16 copies), in their layout
+// and, with fp8 backward, transposed: once after each change of the weights.
+hipError_t quantize_weights(nc_ctx* c) {
+  const int d = c->d, F = c->F, W = c->W;
+  const int rows[4] = {W, d, F, d}, cols[4] = {d, d, d, F};
+  const size_t off[4] = {0, oWo_of(c), oW1_of(c), oW1_of(c) + (size_t)F * d};
+  for (int l = 0; l < c->L; ++l)
+    for (int j = 0; j < 4; ++j) {
+      const WCodes q = wcodes(c, l, j, false), qt = wcodes(c, l, j, true);
+      const void* w = wptr(c, (size_t)l * c->S + off[j]);
+      const size_t n = (size_t)rows[j] * cols[j];
+      if (!in_arena(c, w, n * 2) || !in_arena(c, q.q, n) || !in_arena(c, q.s, 8) ||
+          (c->fp8b && !in_arena(c, qt.q, n))) {
+        c->range_error = "fp8 weight codes outside the arena (layer " + std::to_string(l) + ")";
+        return hipErrorInvalidValue;
+      }
+      if (c->dry_run) continue;
+      const hipError_t e = nc_fp8_quantize(1, 0, w, rows[j], cols[j],
+                                           reinterpret_cast<float*>(c->aa + c->q8ws), q.s, q.q,
+                                           c->fp8b ? qt.q : nullptr, c->st);
+      if (e != hipSuccess) return e;
+    }
+  return hipSuccess;
+}
+
 // Forward block product in fp8: C (epilogue epi) = X W^T with X bf16 [N, K]
-// and W the bf16 weight copy [Nout, K], both quantised to e4m3 with one scale
-// per tensor (codes in q8a / q8w, scales {amax, s} in q8s[0..1] / q8s[2..3]);
-// the kernel divides the sums by s_X s_W.
-hipError_t gemm_fp8_fwd(nc_ctx* c, const void* X, int K, const void* Wt, int Nout, void* C,
+// quantised here (codes in q8a, and transposed into xt when given; scale pair
+// in xscale or q8s[0..1]) and the weight's codes wq [Nout, K] with scale ws.
+// x_parts (n_parts floats): per-block maxima of |X| from X's producer, used
+// instead of a pass over X; c_parts: C's own per-tile maxima (ReLU^2 epilogue).
+hipError_t gemm_fp8_fwd(nc_ctx* c, const void* X, int K, WCodes w, int Nout, void* C,
                         int64_t ldc, int N, int epi, uint8_t* xt = nullptr,
-                        float* xscale = nullptr) {
+                        float* xscale = nullptr, const float* x_parts = nullptr,
+                        int n_parts = 0, float* c_parts = nullptr) {
   float* sc = reinterpret_cast<float*>(c->aa + c->q8s);
   float* ws = reinterpret_cast<float*>(c->aa + c->q8ws);
   uint8_t* xa = reinterpret_cast<uint8_t*>(c->aa + c->q8a);
-  uint8_t* wq = reinterpret_cast<uint8_t*>(c->aa + c->q8w);
   const bool c_f32 = epi == kEpiStoreF32 || epi == kEpiAccF32;
   const size_t nx = (size_t)N * K, nw = (size_t)Nout * K;
   if (K % 128) {
@@ -517,72 +578,75 @@ hipError_t gemm_fp8_fwd(nc_ctx* c, const void* X, int K, const void* Wt, int Nou
     return hipErrorInvalidValue;
   }
   // every extent inside its arena, also in a dry run
-  if (!in_arena(c, X, nx * 2) || !in_arena(c, Wt, nw * 2) || !in_arena(c, xa, nx) ||
-      !in_arena(c, wq, nw) || !in_arena(c, C, ((size_t)(N - 1) * ldc + Nout) * (c_f32 ? 4 : 2)) ||
-      (xt && !in_arena(c, xt, nx)) || (xscale && !in_arena(c, xscale, 2 * sizeof(float)))) {
+  if (!in_arena(c, X, nx * 2) || !in_arena(c, w.q, nw) || !in_arena(c, xa, nx) ||
+      !in_arena(c, C, ((size_t)(N - 1) * ldc + Nout) * (c_f32 ? 4 : 2)) ||
+      (xt && !in_arena(c, xt, nx)) || (xscale && !in_arena(c, xscale, 2 * sizeof(float))) ||
+      (x_parts && !in_arena(c, x_parts, (size_t)n_parts * 4)) ||
+      (c_parts && !in_arena(c, c_parts, (size_t)ceil_div(N, 256) * ceil_div(Nout, 256) * 4))) {
     c->range_error = "fp8 GEMM operand outside its arena (N=" + std::to_string(N) +
                      " Nout=" + std::to_string(Nout) + " K=" + std::to_string(K) + ")";
     return hipErrorInvalidValue;
   }
   if (c->dry_run) return hipSuccess;
   float* xs = xscale ? xscale : sc;
-  hipError_t e = nc_fp8_quantize(1, 0, X, N, K, ws, xs, xa, xt, c->st);
-  if (e != hipSuccess) return e;
-  e = nc_fp8_quantize(1, 0, Wt, Nout, K, ws, sc + 2, wq, nullptr, c->st);
+  const hipError_t e = x_parts ? nc_fp8_quantize_parts(0, X, N, K, x_parts, n_parts, xs, xa, xt,
+                                                       c->st)
+                               : nc_fp8_quantize(1, 0, X, N, K, ws, xs, xa, xt, c->st);
   if (e != hipSuccess) return e;
   GemmParams g{};
-  g.A = xa; g.B = wq; g.C = C;
+  g.A = xa; g.B = w.q; g.C = C;
+  g.amax_part = c_parts;
   g.lda = K; g.ldb = K; g.ldc = ldc;
   g.M = N; g.N = Nout; g.K = K; g.batch = 1; g.splits = 1;
   g.a_layout = kKCont; g.b_layout = kKCont; g.epi = epi; g.alpha = 1.f;
-  g.scale_a = xs; g.scale_b = sc + 2;
+  g.scale_a = xs; g.scale_b = w.s;
   return nc_launch_gemm_f8(g, c->st);
 }
 
 // Backward of an fp8 block product y = x W^T.  fp8_grad_codes: the bf16
 // gradient dY [N, w] to e5m2 codes in its layout (q8dy) and transposed
 // (q8dyt), scale in q8dys.
-hipError_t fp8_grad_codes(nc_ctx* c, const void* dY, int N, int w) {
+// parts (n_parts floats): per-block maxima of |dY| from dY's producer.
+hipError_t fp8_grad_codes(nc_ctx* c, const void* dY, int N, int w, const float* parts = nullptr,
+                          int n_parts = 0) {
   uint8_t* q = reinterpret_cast<uint8_t*>(c->aa + c->q8dy);
   uint8_t* qt = reinterpret_cast<uint8_t*>(c->aa + c->q8dyt);
   float* ds = reinterpret_cast<float*>(c->aa + c->q8dys);
   const size_t n = (size_t)N * w;
-  if (!in_arena(c, dY, n * 2) || !in_arena(c, q, n) || !in_arena(c, qt, n)) {
+  if (!in_arena(c, dY, n * 2) || !in_arena(c, q, n) || !in_arena(c, qt, n) ||
+      (parts && !in_arena(c, parts, (size_t)n_parts * 4))) {
     c->range_error = "fp8 gradient codes outside the arena (N=" + std::to_string(N) +
                      " w=" + std::to_string(w) + ")";
     return hipErrorInvalidValue;
   }
   if (c->dry_run) return hipSuccess;
+  if (parts) return nc_fp8_quantize_parts(1, dY, N, w, parts, n_parts, ds, q, qt, c->st);
   return nc_fp8_quantize(1, 1, dY, N, w, reinterpret_cast<float*>(c->aa + c->q8ws), ds, q, qt,
                          c->st);
 }
 
 // dX (epilogue epi, aux g for the ReLU^2 backward) = dY W from the gradient's
-// codes [N, out] and the transposed e4m3 codes of the bf16 weight copy W
-// [out, in] (quantised here into q8w, scale in q8s[2..3]).
-hipError_t gemm_fp8_dx(nc_ctx* c, const void* Wt, int out, int in, void* C, int64_t ldc, int N,
-                       int epi, const void* aux = nullptr) {
-  float* sc = reinterpret_cast<float*>(c->aa + c->q8s);
-  uint8_t* wq = reinterpret_cast<uint8_t*>(c->aa + c->q8w);
+// codes [N, out] and the transposed codes wt [in, out] of the weight W [out, in].
+hipError_t gemm_fp8_dx(nc_ctx* c, WCodes wt, int out, int in, void* C, int64_t ldc, int N,
+                       int epi, const void* aux = nullptr, float* c_parts = nullptr) {
   const uint8_t* dyq = reinterpret_cast<const uint8_t*>(c->aa + c->q8dy);
   const bool c_f32 = epi == kEpiStoreF32 || epi == kEpiAccF32;
   const size_t nw = (size_t)out * in, cext = ((size_t)(N - 1) * ldc + in) * (c_f32 ? 4 : 2);
-  if (!in_arena(c, Wt, nw * 2) || !in_arena(c, wq, nw) || !in_arena(c, dyq, (size_t)N * out) ||
-      !in_arena(c, C, cext) || (aux && !in_arena(c, aux, cext))) {
+  if (!in_arena(c, wt.q, nw) || !in_arena(c, dyq, (size_t)N * out) || !in_arena(c, C, cext) ||
+      (aux && !in_arena(c, aux, cext)) ||
+      (c_parts && !in_arena(c, c_parts, (size_t)ceil_div(N, 256) * ceil_div(in, 256) * 4))) {
     c->range_error = "fp8 input-gradient operand outside its arena (N=" + std::to_string(N) +
                      " out=" + std::to_string(out) + " in=" + std::to_string(in) + ")";
     return hipErrorInvalidValue;
   }
   if (c->dry_run) return hipSuccess;
-  hipError_t e = nc_fp8_quantize(1, 0, Wt, out, in, reinterpret_cast<float*>(c->aa + c->q8ws),
-                                 sc + 2, nullptr, wq, c->st);
-  if (e != hipSuccess) return e;
   GemmParams g{};
-  g.A = dyq; g.B = wq; g.C = C; g.aux_in = aux;
+  g.A = dyq; g.B = wt.q; g.C = C; g.aux_in = aux;
+  g.amax_part = c_parts;
   g.lda = out; g.ldb = out; g.ldc = ldc;
   g.M = N; g.N = in; g.K = out; g.batch = 1; g.splits = 1;
   g.a_layout = kKCont; g.b_layout = kKCont; g.epi = epi; g.alpha = 1.f;
-  g.scale_a = reinterpret_cast<const float*>(c->aa + c->q8dys); g.scale_b = sc + 2;
+  g.scale_a = reinterpret_cast<const float*>(c->aa + c->q8dys); g.scale_b = wt.s;
   g.fmt_a = 1;
   return nc_launch_gemm_f8(g, c->st);
 }
@@ -730,6 +794,7 @@ nc_status nc_bind(nc_ctx* ctx, void* d_param_arena, size_t param_bytes, void* d_
   NC_TRY(nc_fill_f32(A<float>(ctx, ctx->flags), 0.f, 1, ctx->st), "clear input flags");
   ctx->step = 0;
   NC_TRY(hipStreamSynchronize(ctx->st), "bind sync");
+  ctx->w8_ok = false;
   ctx->bound = true;
   return NC_OK;
 }
@@ -762,6 +827,7 @@ nc_status nc_init_params(nc_ctx* ctx, uint64_t seed, float std) {
       NC_TRY(nc_fill_f32(P<float>(ctx, ctx->oP) + ctx->e_rl, 1.f, ctx->L, ctx->st), "resid");
   }
   ctx->step = 0;
+  ctx->w8_ok = false;
   return refresh_shadows(ctx);
 }
 
@@ -797,7 +863,7 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
   const int N = B * T;
   const int Hkv = ctx->Hkv, dk = ctx->dk, Wd = ctx->W;
   // offsets of Wo and W1 inside a layer's block (Wq | Wk | Wv | Wo | W1 | W2)
-  const size_t oWo = (size_t)d * d + 2ULL * dk * d, oW1 = oWo + (size_t)d * d;
+  const size_t oWo = oWo_of(ctx), oW1 = oW1_of(ctx);
   const float eps = ctx->cfg.norm_eps;
   hipStream_t st = ctx->st;
   const size_t es = ctx->es;
@@ -811,6 +877,10 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
 
   // ---------------------------------------------------------------- forward
   int32_t* flags = A<int32_t>(ctx, ctx->flags);
+  if (ctx->fp8 && !ctx->w8_ok) {   // weight codes for this and the following micro-batches
+    NC_GEMM(quantize_weights(ctx), "weight codes");
+    if (!ctx->dry_run) ctx->w8_ok = true;
+  }
   const float* Pm = P<float>(ctx, ctx->oP);
   const float* E = Pm + ctx->n_block;
   float* x0b = ctx->resid_on ? A<float>(ctx, ctx->x0b) : nullptr;
@@ -827,6 +897,9 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
     NC_TRY(nc_embed_fwd(tok, E, x, N, d, V, flags, st), "embed");
     if (x0b) NC_TRY(hipMemcpyAsync(x0b, x, Nd * 4, hipMemcpyDeviceToDevice, st), "x0");
   }
+  // fp8: the producers of a1, a2 (RMSNorm) and g (the ReLU^2 epilogue) leave
+  // per-block maxima of their output for its scale
+  float* parts = ctx->fp8 ? A<float>(ctx, ctx->q8part) : nullptr;
   // fp8 backward: the forward quantiser also writes the transposed codes of
   // each layer's four activations (a1, o, a2, g) and keeps their scales
   auto xt_of = [&](int l, int which) -> uint8_t* {
@@ -841,7 +914,8 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
     const LayerAct& la = ctx->la[l];
     const size_t wb = (size_t)l * ctx->S;
     char* qkv = aa + la.qkv;
-    if (ctx->resid_on || (ctx->backout_on && l == ctx->Lb)) {
+    const bool mixed = ctx->resid_on || (ctx->backout_on && l == ctx->Lb);
+    if (mixed) {
       // x <- resid_l x + x0_l x0 (saving the stream before the mix), then norm1
       NC_TRY(nc_rmsnorm_mix_fwd(dt, x, x0b, ctx->resid_on ? xprev_of(l) : xb,
                                 ctx->resid_on ? Pm + ctx->e_rl + l : nullptr,
@@ -849,10 +923,12 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
                                 ctx->resid_on, aa + la.a1, A<float>(ctx, la.r1), N, d, eps, st),
              "mix norm1");
     } else {
-      NC_TRY(nc_rmsnorm_fwd(dt, x, aa + la.a1, A<float>(ctx, la.r1), N, d, eps, st), "norm1");
+      NC_TRY(nc_rmsnorm_fwd(dt, x, aa + la.a1, A<float>(ctx, la.r1), N, d, eps, st, parts),
+             "norm1");
     }
-    NC_GEMM(ctx->fp8 ? gemm_fp8_fwd(ctx, aa + la.a1, d, wptr(ctx, wb), Wd, qkv, Wd, N, kEpiStore,
-                                    xt_of(l, 0), xs_of(l, 0))
+    NC_GEMM(ctx->fp8 ? gemm_fp8_fwd(ctx, aa + la.a1, d, wcodes(ctx, l, 0, false), Wd, qkv, Wd, N,
+                                    kEpiStore, xt_of(l, 0), xs_of(l, 0),
+                                    mixed ? nullptr : parts, ceil_div(N, 4))
                      : gemm(ctx, aa + la.a1, d, kKCont, wptr(ctx, wb), d, kKCont, qkv, Wd, N, Wd,
                             d, kEpiStore), "qkv");
     if (ctx->ve_slot[l] >= 0) {
@@ -866,17 +942,19 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
            "qknorm");
     NC_TRY(nc_attn_fwd(dt, qkv, qkv + d * es, qkv + (d + dk) * es, Wd, aa + la.o, d,
                        A<float>(ctx, la.lse), B, T, H, Hkv, ctx->windows[l], st), "attn fwd");
-    NC_GEMM(ctx->fp8 ? gemm_fp8_fwd(ctx, aa + la.o, d, wptr(ctx, wb + oWo), d, x, d, N, kEpiAccF32,
+    NC_GEMM(ctx->fp8 ? gemm_fp8_fwd(ctx, aa + la.o, d, wcodes(ctx, l, 1, false), d, x, d, N, kEpiAccF32,
                                     xt_of(l, 1), xs_of(l, 1))
                      : gemm(ctx, aa + la.o, d, kKCont, wptr(ctx, wb + oWo), d, kKCont, x, d, N, d,
                             d, kEpiAccF32), "out proj");
-    NC_TRY(nc_rmsnorm_fwd(dt, x, aa + la.a2, A<float>(ctx, la.r2), N, d, eps, st), "norm2");
-    NC_GEMM(ctx->fp8 ? gemm_fp8_fwd(ctx, aa + la.a2, d, wptr(ctx, wb + oW1), F, aa + la.g, F, N,
-                                    kEpiRelu2, xt_of(l, 2), xs_of(l, 2))
+    NC_TRY(nc_rmsnorm_fwd(dt, x, aa + la.a2, A<float>(ctx, la.r2), N, d, eps, st, parts), "norm2");
+    NC_GEMM(ctx->fp8 ? gemm_fp8_fwd(ctx, aa + la.a2, d, wcodes(ctx, l, 2, false), F, aa + la.g, F, N,
+                                    kEpiRelu2, xt_of(l, 2), xs_of(l, 2), parts, ceil_div(N, 4),
+                                    parts)
                      : gemm(ctx, aa + la.a2, d, kKCont, wptr(ctx, wb + oW1), d, kKCont, aa + la.g,
                             F, N, F, d, kEpiRelu2), "mlp up");
-    NC_GEMM(ctx->fp8 ? gemm_fp8_fwd(ctx, aa + la.g, F, wptr(ctx, wb + oW1 + (size_t)F * d), d, x,
-                                    d, N, kEpiAccF32, xt_of(l, 3), xs_of(l, 3))
+    NC_GEMM(ctx->fp8 ? gemm_fp8_fwd(ctx, aa + la.g, F, wcodes(ctx, l, 3, false), d, x,
+                                    d, N, kEpiAccF32, xt_of(l, 3), xs_of(l, 3), parts,
+                                    ceil_div(N, 256) * ceil_div(F, 256))
                      : gemm(ctx, aa + la.g, F, kKCont, wptr(ctx, wb + oW1 + (size_t)F * d), F,
                             kKCont, x, d, N, d, F, kEpiAccF32), "mlp down");
   }
@@ -903,8 +981,13 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
                 nullptr, nullptr, ctx->splits_head), "dWh");
   }
   NC_TRY(nc_sum_scaled(A<float>(ctx, ctx->loss_rows), N, 1.f / (float)N, d_loss, st), "loss");
-  NC_TRY(nc_rmsnorm_bwd(dt, da, aa + ctx->xf, A<float>(ctx, ctx->rf), dx, dxT, N, d, 0, st),
-         "normf bwd");
+  // fp8 backward: dxT's per-block maxima come from the RMSNorm backward that
+  // wrote it (the mixed-stream backward leaves none: dxT_parts false)
+  float* bparts = ctx->fp8b ? parts : nullptr;
+  const int nb_rows = ceil_div(N, 4), nb_ff = ceil_div(N, 256) * ceil_div(F, 256);
+  NC_TRY(nc_rmsnorm_bwd(dt, da, aa + ctx->xf, A<float>(ctx, ctx->rf), dx, dxT, N, d, 0, st,
+                        bparts), "normf bwd");
+  bool dxT_parts = bparts != nullptr;
   float* part_a = (ctx->resid_on || ctx->backout_on) ? A<float>(ctx, ctx->part_a) : nullptr;
   float* part_b = (ctx->resid_on || ctx->backout_on) ? A<float>(ctx, ctx->part_b) : nullptr;
   float* gb = ctx->backout_on ? A<float>(ctx, ctx->gbb) : nullptr;
@@ -926,13 +1009,14 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
     char* dqkv = aa + ctx->dqkv;
     // MLP
     if (ctx->fp8b) {   // the eight products in fp8: dY e5m2, X and W e4m3
-      NC_GEMM(fp8_grad_codes(ctx, dxT, N, d), "dx codes");
-      NC_GEMM(gemm_fp8_dx(ctx, wptr(ctx, w2), d, F, aa + ctx->dh, F, N, kEpiRelu2Bwd, aa + la.g),
+      NC_GEMM(fp8_grad_codes(ctx, dxT, N, d, dxT_parts ? bparts : nullptr, nb_rows), "dx codes");
+      NC_GEMM(gemm_fp8_dx(ctx, wcodes(ctx, l, 3, true), d, F, aa + ctx->dh, F, N, kEpiRelu2Bwd,
+                          aa + la.g, bparts),
               "dh");
       NC_GEMM(gemm_fp8_dw(ctx, xt_of(l, 3), xs_of(l, 3), d, F, G + w2, N, ctx->splits_2), "dW2");
-      NC_GEMM(fp8_grad_codes(ctx, aa + ctx->dh, N, F), "dh codes");
+      NC_GEMM(fp8_grad_codes(ctx, aa + ctx->dh, N, F, bparts, nb_ff), "dh codes");
       NC_GEMM(gemm_fp8_dw(ctx, xt_of(l, 2), xs_of(l, 2), F, d, G + w1, N, ctx->splits_1), "dW1");
-      NC_GEMM(gemm_fp8_dx(ctx, wptr(ctx, w1), F, d, da, d, N, kEpiStoreF32), "da2");
+      NC_GEMM(gemm_fp8_dx(ctx, wcodes(ctx, l, 2, true), F, d, da, d, N, kEpiStoreF32), "da2");
     } else {
       NC_GEMM(gemm(ctx, dxT, d, kKCont, wptr(ctx, w2), F, kMNCont, aa + ctx->dh, F, N, F, d,
                   kEpiRelu2Bwd, aa + la.g), "dh");
@@ -943,12 +1027,12 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
       NC_GEMM(gemm(ctx, aa + ctx->dh, F, kKCont, wptr(ctx, w1), d, kMNCont, da, d, N, d, F,
                   kEpiStoreF32), "da2");
     }
-    NC_TRY(nc_rmsnorm_bwd(dt, da, aa + la.a2, A<float>(ctx, la.r2), dx, dxT, N, d, 1, st),
+    NC_TRY(nc_rmsnorm_bwd(dt, da, aa + la.a2, A<float>(ctx, la.r2), dx, dxT, N, d, 1, st, bparts),
            "norm2 bwd");
     // attention
     if (ctx->fp8b) {
-      NC_GEMM(fp8_grad_codes(ctx, dxT, N, d), "dx codes");
-      NC_GEMM(gemm_fp8_dx(ctx, wptr(ctx, wb + oWo), d, d, aa + ctx->dO, d, N, kEpiStore), "dO");
+      NC_GEMM(fp8_grad_codes(ctx, dxT, N, d, bparts, nb_rows), "dx codes");
+      NC_GEMM(gemm_fp8_dx(ctx, wcodes(ctx, l, 1, true), d, d, aa + ctx->dO, d, N, kEpiStore), "dO");
       NC_GEMM(gemm_fp8_dw(ctx, xt_of(l, 1), xs_of(l, 1), d, d, G + wb + oWo, N, ctx->splits_o),
               "dWo");
     } else {
@@ -984,7 +1068,7 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
       NC_GEMM(fp8_grad_codes(ctx, dqkv, N, Wd), "dqkv codes");
       NC_GEMM(gemm_fp8_dw(ctx, xt_of(l, 0), xs_of(l, 0), Wd, d, G + wb, N, ctx->splits_qkv),
               "dWqkv");
-      NC_GEMM(gemm_fp8_dx(ctx, wptr(ctx, wb), Wd, d, da, d, N, kEpiStoreF32), "da1");
+      NC_GEMM(gemm_fp8_dx(ctx, wcodes(ctx, l, 0, true), Wd, d, da, d, N, kEpiStoreF32), "da1");
     } else {
       NC_GEMM(gemm(ctx, dqkv, Wd, kMNCont, aa + la.a1, d, kMNCont, G + wb, d, Wd, d, N,
                   kEpiAccF32, nullptr, nullptr, ctx->splits_qkv), "dWqkv");
@@ -1006,9 +1090,11 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
         NC_TRY(nc_sum_into(part_a, N, G + ctx->e_rl + l, st), "resid grad");
         NC_TRY(nc_sum_into(part_b, N, G + ctx->e_x0l + l, st), "x0 grad");
       }
+      dxT_parts = false;
     } else {
-      NC_TRY(nc_rmsnorm_bwd(dt, da, aa + la.a1, A<float>(ctx, la.r1), dx, dxT, N, d, 1, st),
-             "norm1 bwd");
+      NC_TRY(nc_rmsnorm_bwd(dt, da, aa + la.a1, A<float>(ctx, la.r1), dx, dxT, N, d, 1, st,
+                            bparts), "norm1 bwd");
+      dxT_parts = bparts != nullptr;
     }
   }
   // the gradient at the embedding output: dx (+ dx0b, the x0 paths)
@@ -1068,6 +1154,7 @@ nc_status nc_optimizer_step(nc_ctx* ctx, float lr_mult) {
   const int dt = ctx->dt, L = ctx->L, d = ctx->d, F = ctx->F, V = ctx->V;
   hipStream_t st = ctx->st;
   ctx->step += 1;
+  ctx->w8_ok = false;        // the weights change: their fp8 codes are made again
   const double t = (double)ctx->step;
   const float bc1 = (float)(1.0 - std::pow((double)o.adam_beta1, t));
   const float bc2 = (float)(1.0 - std::pow((double)o.adam_beta2, t));
@@ -1255,6 +1342,7 @@ nc_status nc_set_param(nc_ctx* ctx, int32_t i, const float* src, int32_t src_on_
   const ParamInfo& p = ctx->params[i];
   const size_t n = (size_t)p.rows * p.cols;
   float* dst = P<float>(ctx, ctx->oP) + p.elem;
+  ctx->w8_ok = false;
   NC_TRY(hipMemcpyAsync(dst, src, n * 4,
                         src_on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice, ctx->st),
          "set param");

@@ -209,6 +209,32 @@ def test_fp8_backward_full_step(name):
                prep=feature_params if "features" in name else None)
 
 
+def test_fp8_weight_codes_follow_the_weights():
+    """The weights' fp8 codes are made once and reused by later micro-batches;
+    after an optimizer step or nc_set_param they are made again: the loss of
+    the next micro-batch equals, bit for bit, that of a fresh model holding
+    the same weights."""
+    cfg = replace(SMALL_BF16, fp8_forward=True, fp8_backward=True)
+    m, params, tok, tgt = setup(cfg, B=2, seed=57)
+    l1, _ = run_gpu(m, tok, tgt)
+    l1b, _ = run_gpu(m, tok, tgt)                     # reused codes
+    assert l1 == l1b
+    m.optimizer_step()
+    l2, g2 = run_gpu(m, tok, tgt)
+    after = {n: m.get(n) for n in m.names()}
+    fresh = nc.Model(cfg, OptimConfig(), max_micro_batch=2)
+    fresh.set_params(after)
+    l2f, g2f = run_gpu(fresh, tok, tgt)
+    assert l2 == l2f and l2 != l1
+    for n in g2:
+        assert np.array_equal(g2[n], g2f[n]), n
+    m.set_params(params)                              # back to the first weights
+    l3, _ = run_gpu(m, tok, tgt)
+    assert l3 == l1
+    fresh.close()
+    m.close()
+
+
 def test_d12_shape_one_row():
     check_step(with_batch(D12, micro_batch=1), B=1, seed=7)
 
