@@ -53,7 +53,7 @@ Readings where the pages are silent:
   backward treats the rounding as the identity (gradients with the
   unrounded operands).  The lm_head is exact.
 * FP8 backward products (cfg["fp8_backward"], the same passage: the
-  reading takes "most linear layers" to cover their backward products
+  reading takes the linear layers meant there to cover their backward products
   too): the input gradient dX = dY W and the weight gradient dW = dY^T X of
   each of the four block products use the e5m2 values of the bf16 gradient
   dY (one scale per tensor; the fused QKV gradient [dq | dk | dv] is one
