@@ -407,7 +407,7 @@ NC_DEV void attn_store_grad(const f32x16 (&acc)[4], float scale, bf16* __restric
 // stay in registers as the B operands) and walks the 64-query tiles from the
 // diagonal down.  Q, dO and the tile's log-sum-exp and D reach LDS by direct
 // loads, double-buffered; Q^T and dO^T fragments come from transpose reads.
-constexpr int kDkvStage = 2 * 64 * 128 + 256;     // Q | dO | lse[64] D[64] (fp32)
+constexpr int kDkvStage = 2 * 64 * 128 + 256;     // Q | dO | -lse log2(e) [64], D [64] (fp32)
 
 // one 128-key block kblk of key/value head bhk; st0 / st1: stages of kDkvStage
 // elements.  kGrouped: G > 1 query heads per key/value head, walked in turn (a
@@ -415,7 +415,7 @@ constexpr int kDkvStage = 2 * 64 * 128 + 256;     // Q | dO | lse[64] D[64] (fp3
 template <bool kGrouped>
 NC_DEV void attn_bwd_dkv_block(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    int64_t ld, const bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ lse,
+    int64_t ld, const bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ nl2,
     const float* __restrict__ Dv, bf16* __restrict__ dk, bf16* __restrict__ dv, int64_t ldd,
     int T, int H, int G, int win, float scale_log2, float scale, int kblk, int bhk, bf16* st0,
     bf16* st1, const QkNorm& nq) {
@@ -427,7 +427,7 @@ NC_DEV void attn_bwd_dkv_block(
   const int h0 = kGrouped ? hk * G : hk;
   int64_t base = (int64_t)b * T * ld + h0 * 128;
   int64_t obase = (int64_t)b * T * ldo + h0 * 128;
-  const float* lse_bh = lse + ((int64_t)b * H + h0) * T;
+  const float* lse_bh = nl2 + ((int64_t)b * H + h0) * T;
   const float* D_bh = Dv + ((int64_t)b * H + h0) * T;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -508,7 +508,7 @@ NC_DEV void attn_bwd_dkv_block(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int e = g * 4 + i;
-          const float pv = fast_exp2(fmaf(sacc[qb][e], scale_log2, -la[i] * kLog2e));
+          const float pv = fast_exp2(fmaf(sacc[qb][e], scale_log2, la[i]));
           p[qb][e] = pv;
           ds[qb][e] = pv * (pacc[qb][e] - da[i]);
         }
@@ -540,7 +540,7 @@ NC_DEV void attn_bwd_dkv_block(
         const int h = h0 + g;
         base = (int64_t)b * T * ld + h * 128;
         obase = (int64_t)b * T * ldo + h * 128;
-        lse_bh = lse + ((int64_t)b * H + h) * T;
+        lse_bh = nl2 + ((int64_t)b * H + h) * T;
         D_bh = Dv + ((int64_t)b * H + h) * T;
         __syncthreads();                           // the previous head's last tile is read
       }
@@ -568,9 +568,9 @@ NC_DEV void attn_bwd_dkv_block(
 NC_DEV void attn_bwd_dq_block(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, const bf16* __restrict__ o, const bf16* __restrict__ dO, int64_t ldo,
-    const float* __restrict__ lse, float* __restrict__ Dv, bf16* __restrict__ dq, int64_t ldd,
-    int T, int H, int G, int win, float scale_log2, float scale, int qb, int bh, bf16* st0,
-    bf16* st1, const QkNorm& nq) {
+    const float* __restrict__ lse, float* __restrict__ Dv, float* __restrict__ NL,
+    bf16* __restrict__ dq, int64_t ldd, int T, int H, int G, int win, float scale_log2,
+    float scale, int qb, int bh, bf16* st0, bf16* st1, const QkNorm& nq) {
   constexpr int KT = 64 * 128;
   const int b = bh / H, h = bh % H;
   const int64_t base = (int64_t)b * T * ld + h * 128;
@@ -603,7 +603,10 @@ NC_DEV void attn_bwd_dq_block(
       for (int j = 0; j < 8; ++j) part += (float)df[s][j] * (float)of[j];
     }
     Dq = part + __shfl_xor(part, 32, 64);
-    if (half == 0) Dv[((int64_t)b * H + h) * T + myq] = Dq;
+    if (half == 0) {
+      Dv[((int64_t)b * H + h) * T + myq] = Dq;
+      NL[((int64_t)b * H + h) * T + myq] = -lse2;   // -lse log2(e) for the dK/dV kernel
+    }
   }
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
@@ -740,7 +743,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 template <bool kGrouped>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    int64_t ld, const bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ lse,
+    int64_t ld, const bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ nl2,
     const float* __restrict__ Dv, bf16* __restrict__ dk, bf16* __restrict__ dv, int64_t ldd,
     int T, int H, int G, int win, float scale_log2, float scale, QkNorm nq) {
   __shared__ __attribute__((aligned(1024))) bf16 st0[kDkvStage];
@@ -748,27 +751,28 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
   // key block kblk walks up to T/64 - 2 kblk query tiles: the low blocks are the long ones
   const BlockJob jb = block_job(T / 128, win >= T, false);
   if (jb.second >= 0) {
-    attn_bwd_dkv_block<kGrouped>(q, k, v, ld, dO, ldo, lse, Dv, dk, dv, ldd, T, H, G, win,
+    attn_bwd_dkv_block<kGrouped>(q, k, v, ld, dO, ldo, nl2, Dv, dk, dv, ldd, T, H, G, win,
                                  scale_log2, scale, jb.second, jb.bh, st0, st1, nq);
     __syncthreads();
   }
-  attn_bwd_dkv_block<kGrouped>(q, k, v, ld, dO, ldo, lse, Dv, dk, dv, ldd, T, H, G, win,
+  attn_bwd_dkv_block<kGrouped>(q, k, v, ld, dO, ldo, nl2, Dv, dk, dv, ldd, T, H, G, win,
                                scale_log2, scale, jb.first, jb.bh, st0, st1, nq);
 }
 
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, const bf16* __restrict__ o, const bf16* __restrict__ dO, int64_t ldo,
-    const float* __restrict__ lse, float* __restrict__ Dv, bf16* __restrict__ dq, int64_t ldd,
+    const float* __restrict__ lse, float* __restrict__ Dv, float* __restrict__ NL,
+    bf16* __restrict__ dq, int64_t ldd,
     int T, int H, int G, int win, float scale_log2, float scale, QkNorm nq) {
   __shared__ __attribute__((aligned(1024))) bf16 st0[2 * 64 * 128];   // K | V
   __shared__ __attribute__((aligned(1024))) bf16 st1[2 * 64 * 128];
   const BlockJob jb = block_job(T / 128, win >= T, true);
-  attn_bwd_dq_block(q, k, v, ld, o, dO, ldo, lse, Dv, dq, ldd, T, H, G, win, scale_log2, scale,
+  attn_bwd_dq_block(q, k, v, ld, o, dO, ldo, lse, Dv, NL, dq, ldd, T, H, G, win, scale_log2, scale,
                     jb.first, jb.bh, st0, st1, nq);
   if (jb.second < 0) return;
   __syncthreads();
-  attn_bwd_dq_block(q, k, v, ld, o, dO, ldo, lse, Dv, dq, ldd, T, H, G, win, scale_log2, scale,
+  attn_bwd_dq_block(q, k, v, ld, o, dO, ldo, lse, Dv, NL, dq, ldd, T, H, G, win, scale_log2, scale,
                     jb.second, jb.bh, st0, st1, nq);
 }
 
@@ -911,13 +915,16 @@ hipError_t nc_attn_bwd(int dtype, const void* q, const void* k, const void* v, i
     if (T % 128) return hipErrorInvalidValue;
     const int jobs = attn_jobs_per_head(T, win);
     const QkNorm nq{rqk, cos_sin, H + Hkv};
-    // dQ first: it also forms D = rowsum(dO * O), which the dK/dV kernel reads
+    // dQ first: it also forms D = rowsum(dO * O) and -lse log2(e) (in the second
+    // half of D), which the dK/dV kernel reads, so that a score's weight there is
+    // one fma and one exp2
+    float* NL = D + (int64_t)B * H * T;
     attn_bwd_dq_kernel<<<B * H * jobs, 256, 0, st>>>(
         (const bf16*)q, (const bf16*)k, (const bf16*)v, ld, (const bf16*)o, (const bf16*)dO,
-        ldo, lse, D, (bf16*)dq, ldd, T, H, G, win, scale * kLog2e, scale, nq);
+        ldo, lse, D, NL, (bf16*)dq, ldd, T, H, G, win, scale * kLog2e, scale, nq);
     auto dkv_kernel = G > 1 ? attn_bwd_dkv_kernel<true> : attn_bwd_dkv_kernel<false>;
     dkv_kernel<<<B * Hkv * jobs, 256, 0, st>>>(
-        (const bf16*)q, (const bf16*)k, (const bf16*)v, ld, (const bf16*)dO, ldo, lse, D,
+        (const bf16*)q, (const bf16*)k, (const bf16*)v, ld, (const bf16*)dO, ldo, NL, D,
         (bf16*)dk, (bf16*)dv, ldd, T, H, G, win, scale * kLog2e, scale, nq);
   } else {
     if (rqk) return hipErrorInvalidValue;     // fp32: separate D and QK-norm kernels

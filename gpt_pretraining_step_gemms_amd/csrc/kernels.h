@@ -100,7 +100,8 @@ hipError_t nc_attn_fwd(int dtype, const void* q, const void* k, const void* v, i
 // D[b,h,t] = sum_d dO*O
 hipError_t nc_attn_bwd_pre(int dtype, const void* o, const void* dO, int64_t ld_o, float* D,
                            int B, int T, int H, hipStream_t st);
-// Writes D = rowsum(dO*O) ([B, H, T]) and dq, dk, dv.  With rqk and cos_sin
+// Writes D = rowsum(dO*O) ([B, H, T]; bf16: followed by -lse log2(e), [B, H, T]) and
+// dq, dk, dv.  With rqk and cos_sin
 // (bf16 only) the QK-norm + rotary backward is applied to dq and dk on their
 // way out (rqk [B*T, H + Hkv] reciprocal RMS of the forward's q/k heads,
 // cos_sin the rotary table [2][T][64]): the gradients are then those at the

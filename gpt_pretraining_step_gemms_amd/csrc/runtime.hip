@@ -321,7 +321,7 @@ void plan(nc_ctx* c) {
   c->da = a.take(N * d * 4);
   c->dqkv = a.take(N * W * es);
   c->dO = a.take(N * d * es);
-  c->Dbuf = a.take(N * H * 4);
+  c->Dbuf = a.take(2 * N * H * 4);     // D, and -lse log2(e) for the bf16 dK/dV kernel
   c->dh = a.take(N * F * es);
   c->z = a.take((size_t)c->chunk * V * 4);
   c->dz = a.take((size_t)c->chunk * V * es);
@@ -1664,7 +1664,7 @@ nc_status nc_op_attention_bwd(int32_t dtype, const void* q, size_t q_bytes, cons
       !attn_rows_ok(dO_bytes, rows, H, ld_o, es) || !attn_rows_ok(dq_bytes, rows, H, ld_d, es) ||
       !attn_rows_ok(dk_bytes, rows, hk, ld_d, es) || !attn_rows_ok(dv_bytes, rows, hk, ld_d, es) ||
       !span_ok(lse_bytes, (int64_t)B * H, T, T, 0, 1, 4) ||
-      !span_ok(D_bytes, (int64_t)B * H, T, T, 0, 1, 4))
+      !span_ok(D_bytes, (int64_t)(dtype == NC_BF16 ? 2 : 1) * B * H, T, T, 0, 1, 4))
     return NC_ERR_INVALID_ARG;
   if (dtype == NC_BF16 && (T % 128 || ld_qkv % 8 || ld_o % 8 || ld_d % 8)) return NC_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);

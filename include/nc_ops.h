@@ -134,7 +134,8 @@ nc_status nc_op_attention_fwd(int32_t dtype, const void* q, size_t q_bytes, cons
                               int32_t n_kv_head, int32_t window, void* stream);
 
 /* Causal attention backward from o, lse of the forward and dO (layout of o).
- * D (fp32 [B, H, T]) is caller-provided scratch receiving rowsum(dO * o).
+ * D is caller-provided fp32 scratch receiving rowsum(dO * o) in its first
+ * [B, H, T] (NC_BF16: [2, B, H, T], the second half receiving -lse log2(e)).
  * Writes dq, dk, dv (layout of q/k/v with row stride ld_d; dk and dv of a
  * key/value head sum over its query heads).  n_kv_head and window as for the
  * forward pass (the same values the forward pass used). */

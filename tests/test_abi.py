@@ -401,7 +401,7 @@ def test_op_operand_extents_are_checked_before_any_launch():
     # exactly the bytes each one needs: ((rows - 1) ld + heads 128) elements
     need_q, need_kv = ((rows - 1) * good_ld + d) * 2, ((rows - 1) * good_ld + dk) * 2
     ext = dict(q=need_q, k=need_kv, v=need_kv, o=rows * d * 2, dO=rows * d * 2,
-               lse=B * H * T * 4, D=B * H * T * 4, dq=need_q, dk=need_kv, dv=need_kv)
+               lse=B * H * T * 4, D=2 * B * H * T * 4, dq=need_q, dk=need_kv, dv=need_kv)
     def bwd(**short):
         e = {k: v - short.get(k, 0) for k, v in ext.items()}
         return lib.nc_op_attention_bwd(nc.NC_BF16, fake, e["q"], fake, e["k"], fake, e["v"], good_ld,

@@ -234,7 +234,7 @@ def test_attention_forward_backward_vs_oracle(dtype, B, T, H):
     q, k, v = qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:]
     nc.attention_fwd(q, k, v, o, lse, B, T, H, ld_qkv=3 * d, ld_o=d)
     dqkv = torch.zeros_like(qkv)
-    D = torch.empty(B, H, T, dtype=F32, device="cuda")
+    D = torch.empty(2, B, H, T, dtype=F32, device="cuda")
     nc.attention_bwd(q, k, v, o, dO, lse, D, dqkv[:, :d], dqkv[:, d:2 * d], dqkv[:, 2 * d:],
                      B, T, H, ld_qkv=3 * d, ld_o=d, ld_d=3 * d)
     torch.cuda.synchronize()
@@ -280,7 +280,7 @@ def test_attention_sliding_window_vs_oracle(dtype, B, T, H, w):
     print(f"[attn window] {dtype} B={B} T={T} H={H} w={w}", flush=True)
     nc.attention_fwd(q, k, v, o, lse, B, T, H, ld_qkv=3 * d, ld_o=d, window=w)
     dqkv = torch.zeros_like(qkv)
-    D = torch.empty(B, H, T, dtype=F32, device="cuda")
+    D = torch.empty(2, B, H, T, dtype=F32, device="cuda")
     nc.attention_bwd(q, k, v, o, dO, lse, D, dqkv[:, :d], dqkv[:, d:2 * d], dqkv[:, 2 * d:],
                      B, T, H, ld_qkv=3 * d, ld_o=d, ld_d=3 * d, window=w)
     torch.cuda.synchronize()
@@ -316,7 +316,7 @@ def test_attention_many_heads_sampled(w):
     print(f"[attn heads] B={B} T={T} H={H} w={w}", flush=True)
     nc.attention_fwd(q, k, v, o, lse, B, T, H, 3 * d, d, window=w)
     dqkv = torch.zeros_like(qkv)
-    D = torch.empty(B, H, T, dtype=F32, device="cuda")
+    D = torch.empty(2, B, H, T, dtype=F32, device="cuda")
     nc.attention_bwd(q, k, v, o, dO, lse, D, dqkv[:, :d], dqkv[:, d:2 * d], dqkv[:, 2 * d:],
                      B, T, H, 3 * d, d, 3 * d, window=w)
     torch.cuda.synchronize()
@@ -355,7 +355,7 @@ def test_attention_grouped_query_vs_oracle(dtype, B, T, H, Hkv, w):
     ld = d + 2 * dk
     nc.attention_fwd(q, k, v, o, lse, B, T, H, ld, d, window=w, n_kv_head=Hkv)
     dqkv = torch.zeros_like(qkv)
-    D = torch.empty(B, H, T, dtype=F32, device="cuda")
+    D = torch.empty(2, B, H, T, dtype=F32, device="cuda")
     nc.attention_bwd(q, k, v, o, dO, lse, D, dqkv[:, :d], dqkv[:, d:d + dk], dqkv[:, d + dk:],
                      B, T, H, ld, d, ld, window=w, n_kv_head=Hkv)
     torch.cuda.synchronize()
@@ -395,7 +395,7 @@ def test_attention_d20_launch_sampled(w):
     print(f"[attn d20] w={w}", flush=True)
     nc.attention_fwd(q, k, v, o, lse, B, T, H, 3 * d, d, window=w)
     dqkv = torch.empty_like(qkv)
-    D = torch.empty(B, H, T, dtype=F32, device="cuda")
+    D = torch.empty(2, B, H, T, dtype=F32, device="cuda")
     nc.attention_bwd(q, k, v, o, dO, lse, D, dqkv[:, :d], dqkv[:, d:2 * d], dqkv[:, 2 * d:],
                      B, T, H, 3 * d, d, 3 * d, window=w)
     torch.cuda.synchronize()
@@ -425,7 +425,7 @@ def test_attention_window_covering_the_row_is_bitwise_causal():
         lse = torch.empty(B, H, T, dtype=F32, device="cuda")
         nc.attention_fwd(q, k, v, o, lse, B, T, H, 3 * d, d, window=w)
         dqkv = torch.zeros_like(qkv)
-        D = torch.empty(B, H, T, dtype=F32, device="cuda")
+        D = torch.empty(2, B, H, T, dtype=F32, device="cuda")
         nc.attention_bwd(q, k, v, o, dO, lse, D, dqkv[:, :d], dqkv[:, d:2 * d], dqkv[:, 2 * d:],
                          B, T, H, 3 * d, d, 3 * d, window=w)
         res.append((o, lse, dqkv))
