@@ -898,6 +898,46 @@ __global__ __launch_bounds__(256) void fp8_quantize_kernel(const T* __restrict__
 // stores: thread t writes rows 16 (t % 4) .. +15 of column t / 4.  The four
 // 16-row chunks of column c sit in the order chunk ^ ((c >> 3) & 3), which
 // spreads one byte-store instruction's 64 lanes over 16 banks instead of 2.
+// The same with 128 x 128 tiles (both dimensions multiples of 128): every row of
+// either output leaves as whole 128-byte lines (a 64-wide tile writes half
+// lines).  A thread codes 8 x 8 values; the column-major LDS tile holds 8
+// 16-row chunks per column, in the order chunk ^ ((c >> 3) & 7).
+template <int FMT>
+__global__ __launch_bounds__(256) void fp8_quantize_2d128_kernel(
+    const bf16* __restrict__ x, int R, int C, const float* __restrict__ amax_scale,
+    uint8_t* __restrict__ q, uint8_t* __restrict__ qt) {
+  constexpr int LDT = 144;                       // bytes per LDS column (128 + 16 padding)
+  __shared__ __attribute__((aligned(16))) uint8_t tile[128 * LDT];
+  const int tiles_c = C / 128;
+  const int r0 = (blockIdx.x / tiles_c) * 128, c0 = (blockIdx.x % tiles_c) * 128;
+  const float sc = amax_scale[1];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int id = threadIdx.x + 256 * i;         // 2048 chunks of 8 values
+    const int r = id >> 4, cc = (id & 15) * 8;
+    const int64_t off = (int64_t)(r0 + r) * C + c0 + cc;
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(x + off);
+    unsigned lo = 0, hi = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const unsigned code = fp8_rne<FMT>(static_cast<float>(v[e]) * sc);
+      if (e < 4) lo |= code << (8 * e); else hi |= code << (8 * (e - 4));
+      const int c = cc + e;
+      tile[c * LDT + ((((r >> 4) ^ (c >> 3)) & 7) << 4) + (r & 15)] = (uint8_t)code;
+    }
+    if (q) *reinterpret_cast<uint2*>(q + off) = make_uint2(lo, hi);
+  }
+  if (!qt) return;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int id = threadIdx.x + 256 * j;         // 1024 chunks of 16 codes
+    const int c = id >> 3, ch = id & 7;
+    const uint4 t = *reinterpret_cast<const uint4*>(tile + c * LDT + (((ch ^ (c >> 3)) & 7) << 4));
+    *reinterpret_cast<uint4*>(qt + (int64_t)(c0 + c) * R + r0 + ch * 16) = t;
+  }
+}
+
 template <int FMT>
 __global__ __launch_bounds__(256) void fp8_quantize_2d_kernel(
     const bf16* __restrict__ x, int R, int C, const float* __restrict__ amax_scale,
@@ -1190,6 +1230,17 @@ static hipError_t fp8_codes(int dtype, int fmt, const void* x, int64_t rows, int
   auto al = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; };
   const bool vec = dtype && al(x, 16) && al(q, 8);
   const int64_t per = vec ? 8 * 256 : 256;
+  if (qt && rows % 128 == 0 && cols % 128 == 0) {
+    const int64_t tiles = (rows / 128) * (cols / 128);
+    if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+    if (fmt)
+      fp8_quantize_2d128_kernel<1><<<(int)tiles, 256, 0, st>>>((const bf16*)x, (int)rows,
+                                                               (int)cols, amax_scale, q, qt);
+    else
+      fp8_quantize_2d128_kernel<0><<<(int)tiles, 256, 0, st>>>((const bf16*)x, (int)rows,
+                                                               (int)cols, amax_scale, q, qt);
+    return hipGetLastError();
+  }
   if (qt) {
     const int64_t tiles = (rows / 64) * (cols / 64);
     if (tiles > 0x7fffffff) return hipErrorInvalidValue;
