@@ -142,7 +142,8 @@ NC_DEV bf16x8 fa_frag_vt(const bf16* tile, int row_base, int col_base, int lane)
 }
 
 // one 128-query block qb of head bh; st0 / st1: K | V stages of 2 x 64 x 128
-NC_DEV void attn_fwd_block(
+// Returns the largest |o| this lane stored (before rounding to bf16).
+NC_DEV float attn_fwd_block(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, bf16* __restrict__ o, int64_t ldo, float* __restrict__ lse, int T, int H,
     int G, int win, float scale_log2, int qb, int bh, bf16* st0, bf16* st1) {
@@ -267,13 +268,18 @@ NC_DEV void attn_fwd_block(
   constexpr int OSTR = 136;
   __syncthreads();
   bf16* os = (wave < 2 ? st0 : st1) + (wave & 1) * 32 * OSTR;
+  float amx = 0.f;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       bf16x4 w;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = (bf16)(oacc[db][g * 4 + i] * inv);
+      for (int i = 0; i < 4; ++i) {
+        const float ov = oacc[db][g * 4 + i] * inv;
+        amx = max_nan(amx, fabsf(ov));
+        w[i] = (bf16)ov;
+      }
       *reinterpret_cast<bf16x4*>(os + l32 * OSTR + db * 32 + g * 8 + half * 4) = w;
     }
   __syncthreads();
@@ -285,6 +291,7 @@ NC_DEV void attn_fwd_block(
     u32x4 val = {lo[0], lo[1], hi[0], hi[1]};
     *reinterpret_cast<u32x4*>(o + ((int64_t)b * T + q0w + r) * ldo + h * 128 + c * 8) = val;
   }
+  return amx;
 }
 
 
@@ -311,13 +318,15 @@ struct QkNorm {
 // further) per lane, 8 lanes per row, so that xr, the rotary table and the
 // output move in 16-byte accesses, all issued before any of them is used.
 // The caller has made the region free (no wave still reads it).
-NC_DEV void attn_store_grad(const f32x16 (&acc)[4], float scale, bf16* __restrict__ out,
+// Returns the largest |value| this lane stored (before rounding to bf16).
+NC_DEV float attn_store_grad(const f32x16 (&acc)[4], float scale, bf16* __restrict__ out,
                             int64_t ldd, int64_t out_row, const bf16* __restrict__ xr,
                             int64_t ld, int64_t xr_row, int row0, int64_t n0, int T, int hn,
                             const QkNorm& nq, float* stg, int lane) {
   constexpr int SL = 132;
   const int half = lane >> 5, l32 = lane & 31;
   const int u = lane & 7, rl = lane >> 3;
+  float amx = 0.f;
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
 #pragma unroll
@@ -348,6 +357,7 @@ NC_DEV void attn_store_grad(const f32x16 (&acc)[4], float scale, bf16* __restric
         for (int j = 0; j < 8; ++j) {
           h1[j] = (bf16)g1[it][j];
           h2[j] = (bf16)g2[it][j];
+          amx = max_nan(amx, max_nan(fabsf(g1[it][j]), fabsf(g2[it][j])));
         }
         bf16* o = out + out_row + row * ldd + 8 * u;
         *reinterpret_cast<bf16x8*>(o) = h1;
@@ -391,8 +401,10 @@ NC_DEV void attn_store_grad(const f32x16 (&acc)[4], float scale, bf16* __restric
       bf16x8 h1, h2;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        h1[j] = (bf16)(rs[it] * (dy1[j] - y1[j] * mean));
-        h2[j] = (bf16)(rs[it] * (dy2[j] - y2[j] * mean));
+        const float v1 = rs[it] * (dy1[j] - y1[j] * mean), v2 = rs[it] * (dy2[j] - y2[j] * mean);
+        h1[j] = (bf16)v1;
+        h2[j] = (bf16)v2;
+        amx = max_nan(amx, max_nan(fabsf(v1), fabsf(v2)));
       }
       const int row = 16 * p + it * 8 + rl;
       bf16* o = out + out_row + row * ldd + 8 * u;
@@ -400,6 +412,7 @@ NC_DEV void attn_store_grad(const f32x16 (&acc)[4], float scale, bf16* __restric
       *reinterpret_cast<bf16x8*>(o + 64) = h2;
     }
   }
+  return amx;
 }
 
 // ============================================================ dK / dV
@@ -413,7 +426,7 @@ constexpr int kDkvStage = 2 * 64 * 128 + 256;     // Q | dO | -lse log2(e) [64],
 // elements.  kGrouped: G > 1 query heads per key/value head, walked in turn (a
 // separate instantiation keeps the plain path's registers as they were).
 template <bool kGrouped>
-NC_DEV void attn_bwd_dkv_block(
+NC_DEV float attn_bwd_dkv_block(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, const bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ nl2,
     const float* __restrict__ Dv, bf16* __restrict__ dk, bf16* __restrict__ dv, int64_t ldd,
@@ -554,10 +567,11 @@ NC_DEV void attn_bwd_dkv_block(
   const int64_t row_out = ((int64_t)b * T + k0w) * ldd + hk * 128;
   __syncthreads();                                 // every wave is done with the stages
   float* stg = reinterpret_cast<float*>(wave < 2 ? st0 : st1) + (wave & 1) * 16 * 132;
-  attn_store_grad(dvacc, 1.f, dv, ldd, row_out, nullptr, 0, 0, k0w, 0, T, 0,
-                  QkNorm{nullptr, nullptr, 0}, stg, lane);
-  attn_store_grad(dkacc, scale, dk, ldd, row_out, k, ld, kvbase + (int64_t)k0w * ld, k0w,
-                  (int64_t)b * T + k0w, T, H + hk, nq, stg, lane);
+  const float amx = attn_store_grad(dvacc, 1.f, dv, ldd, row_out, nullptr, 0, 0, k0w, 0, T, 0,
+                                    QkNorm{nullptr, nullptr, 0}, stg, lane);
+  return max_nan(amx, attn_store_grad(dkacc, scale, dk, ldd, row_out, k, ld,
+                                      kvbase + (int64_t)k0w * ld, k0w, (int64_t)b * T + k0w, T,
+                                      H + hk, nq, stg, lane));
 }
 
 // ================================================================== dQ
@@ -565,7 +579,7 @@ NC_DEV void attn_bwd_dkv_block(
 // to the diagonal, like the forward pass: S^T = K Q^T and dP^T = V dO^T with
 // one query per lane, then dQ += dS K with K^T fragments from transpose reads.
 // one 128-query block qb of head bh; st0 / st1: K | V stages of 2 x 64 x 128
-NC_DEV void attn_bwd_dq_block(
+NC_DEV float attn_bwd_dq_block(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, const bf16* __restrict__ o, const bf16* __restrict__ dO, int64_t ldo,
     const float* __restrict__ lse, float* __restrict__ Dv, float* __restrict__ NL,
@@ -684,8 +698,8 @@ NC_DEV void attn_bwd_dq_block(
 
   __syncthreads();                                 // every wave is done with the stages
   float* stg = reinterpret_cast<float*>(wave < 2 ? st0 : st1) + (wave & 1) * 16 * 132;
-  attn_store_grad(dqacc, scale, dq, ldd, ((int64_t)b * T + q0w) * ldd + h * 128, q, ld,
-                  base + (int64_t)q0w * ld, q0w, (int64_t)b * T + q0w, T, h, nq, stg, lane);
+  return attn_store_grad(dqacc, scale, dq, ldd, ((int64_t)b * T + q0w) * ldd + h * 128, q, ld,
+                         base + (int64_t)q0w * ld, q0w, (int64_t)b * T + q0w, T, h, nq, stg, lane);
 }
 
 // Workgroup -> (b*H + h, 128-row blocks).
@@ -726,18 +740,29 @@ NC_DEV BlockJob block_job(int nb, bool paired, bool high_first) {
 // workgroups per (b, h) for the bf16 kernels
 inline int attn_jobs_per_head(int T, int win) { return win >= T ? (T / 128 + 1) / 2 : T / 128; }
 
+// amax_part (optional): per workgroup the largest |o| stored, for o's fp8 scale.
+// Its block reduction reuses st0, once every wave is past the first barrier in it.
+NC_DEV void attn_amax_out(float amx, float* amax_part, bf16* st0) {
+  if (!amax_part) return;
+  amx = block_max_nan(amx, reinterpret_cast<float*>(st0));
+  if (threadIdx.x == 0) amax_part[blockIdx.x] = bf16_abs(amx);
+}
+
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, bf16* __restrict__ o, int64_t ldo, float* __restrict__ lse, int T, int H,
-    int G, int win, float scale_log2) {
+    int G, int win, float scale_log2, float* __restrict__ amax_part) {
   __shared__ __attribute__((aligned(1024))) bf16 st0[2 * 64 * 128];   // K | V of even tiles
   __shared__ __attribute__((aligned(1024))) bf16 st1[2 * 64 * 128];   // K | V of odd tiles
   const BlockJob jb = block_job(T / 128, win >= T, true);
-  attn_fwd_block(q, k, v, ld, o, ldo, lse, T, H, G, win, scale_log2, jb.first, jb.bh, st0, st1);
-  if (jb.second < 0) return;
-  __syncthreads();                                 // the first block's O staging is read
-  attn_fwd_block(q, k, v, ld, o, ldo, lse, T, H, G, win, scale_log2, jb.second, jb.bh, st0,
-                 st1);
+  float amx = attn_fwd_block(q, k, v, ld, o, ldo, lse, T, H, G, win, scale_log2, jb.first,
+                             jb.bh, st0, st1);
+  if (jb.second >= 0) {
+    __syncthreads();                               // the first block's O staging is read
+    amx = max_nan(amx, attn_fwd_block(q, k, v, ld, o, ldo, lse, T, H, G, win, scale_log2,
+                                      jb.second, jb.bh, st0, st1));
+  }
+  attn_amax_out(amx, amax_part, st0);
 }
 
 template <bool kGrouped>
@@ -745,18 +770,22 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, const bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ nl2,
     const float* __restrict__ Dv, bf16* __restrict__ dk, bf16* __restrict__ dv, int64_t ldd,
-    int T, int H, int G, int win, float scale_log2, float scale, QkNorm nq) {
+    int T, int H, int G, int win, float scale_log2, float scale, QkNorm nq,
+    float* __restrict__ amax_part) {
   __shared__ __attribute__((aligned(1024))) bf16 st0[kDkvStage];
   __shared__ __attribute__((aligned(1024))) bf16 st1[kDkvStage];
   // key block kblk walks up to T/64 - 2 kblk query tiles: the low blocks are the long ones
   const BlockJob jb = block_job(T / 128, win >= T, false);
+  float amx = 0.f;
   if (jb.second >= 0) {
-    attn_bwd_dkv_block<kGrouped>(q, k, v, ld, dO, ldo, nl2, Dv, dk, dv, ldd, T, H, G, win,
-                                 scale_log2, scale, jb.second, jb.bh, st0, st1, nq);
+    amx = attn_bwd_dkv_block<kGrouped>(q, k, v, ld, dO, ldo, nl2, Dv, dk, dv, ldd, T, H, G, win,
+                                       scale_log2, scale, jb.second, jb.bh, st0, st1, nq);
     __syncthreads();
   }
-  attn_bwd_dkv_block<kGrouped>(q, k, v, ld, dO, ldo, nl2, Dv, dk, dv, ldd, T, H, G, win,
-                               scale_log2, scale, jb.first, jb.bh, st0, st1, nq);
+  amx = max_nan(amx, attn_bwd_dkv_block<kGrouped>(q, k, v, ld, dO, ldo, nl2, Dv, dk, dv, ldd, T,
+                                                  H, G, win, scale_log2, scale, jb.first, jb.bh,
+                                                  st0, st1, nq));
+  attn_amax_out(amx, amax_part, st0);
 }
 
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
@@ -764,16 +793,19 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     int64_t ld, const bf16* __restrict__ o, const bf16* __restrict__ dO, int64_t ldo,
     const float* __restrict__ lse, float* __restrict__ Dv, float* __restrict__ NL,
     bf16* __restrict__ dq, int64_t ldd,
-    int T, int H, int G, int win, float scale_log2, float scale, QkNorm nq) {
+    int T, int H, int G, int win, float scale_log2, float scale, QkNorm nq,
+    float* __restrict__ amax_part) {
   __shared__ __attribute__((aligned(1024))) bf16 st0[2 * 64 * 128];   // K | V
   __shared__ __attribute__((aligned(1024))) bf16 st1[2 * 64 * 128];
   const BlockJob jb = block_job(T / 128, win >= T, true);
-  attn_bwd_dq_block(q, k, v, ld, o, dO, ldo, lse, Dv, NL, dq, ldd, T, H, G, win, scale_log2, scale,
-                    jb.first, jb.bh, st0, st1, nq);
-  if (jb.second < 0) return;
-  __syncthreads();
-  attn_bwd_dq_block(q, k, v, ld, o, dO, ldo, lse, Dv, NL, dq, ldd, T, H, G, win, scale_log2, scale,
-                    jb.second, jb.bh, st0, st1, nq);
+  float amx = attn_bwd_dq_block(q, k, v, ld, o, dO, ldo, lse, Dv, NL, dq, ldd, T, H, G, win,
+                                scale_log2, scale, jb.first, jb.bh, st0, st1, nq);
+  if (jb.second >= 0) {
+    __syncthreads();
+    amx = max_nan(amx, attn_bwd_dq_block(q, k, v, ld, o, dO, ldo, lse, Dv, NL, dq, ldd, T, H, G,
+                                         win, scale_log2, scale, jb.second, jb.bh, st0, st1, nq));
+  }
+  attn_amax_out(amx, amax_part, st0);
 }
 
 // ========================================================== fp32 path
@@ -883,9 +915,15 @@ __global__ void attn_bwd_dkv_f32_kernel(const float* __restrict__ q, const float
 
 }  // namespace
 
+int nc_attn_amax_parts(int B, int T, int H, int Hkv, int window, int backward) {
+  const int win = window < 0 || window > T ? T : window;
+  const int jobs = attn_jobs_per_head(T, win);
+  return B * (backward ? H + Hkv : H) * jobs;
+}
+
 hipError_t nc_attn_fwd(int dtype, const void* q, const void* k, const void* v, int64_t ld,
                        void* o, int64_t ldo, float* lse, int B, int T, int H, int Hkv, int window,
-                       hipStream_t st) {
+                       hipStream_t st, float* amax_part) {
   const float scale = 1.0f / sqrtf(128.f);
   const int win = window < 0 || window > T ? T : window;
   if (Hkv < 1 || H % Hkv) return hipErrorInvalidValue;
@@ -894,7 +932,7 @@ hipError_t nc_attn_fwd(int dtype, const void* q, const void* k, const void* v, i
     if (T % 128) return hipErrorInvalidValue;
     attn_fwd_kernel<<<B * H * attn_jobs_per_head(T, win), 256, 0, st>>>(
         (const bf16*)q, (const bf16*)k, (const bf16*)v, ld, (bf16*)o, ldo, lse, T, H, G, win,
-        scale * kLog2e);
+        scale * kLog2e, amax_part);
   } else {
     attn_fwd_f32_kernel<<<ceil_div(B * H * T, 4), 256, 0, st>>>(
         (const float*)q, (const float*)k, (const float*)v, ld, (float*)o, ldo, lse, B, T, H, G,
@@ -906,7 +944,8 @@ hipError_t nc_attn_fwd(int dtype, const void* q, const void* k, const void* v, i
 hipError_t nc_attn_bwd(int dtype, const void* q, const void* k, const void* v, int64_t ld,
                        const void* o, const void* dO, int64_t ldo, const float* lse, float* D,
                        void* dq, void* dk, void* dv, int64_t ldd, int B, int T, int H, int Hkv,
-                       int window, const float* rqk, const float* cos_sin, hipStream_t st) {
+                       int window, const float* rqk, const float* cos_sin, hipStream_t st,
+                       float* amax_part) {
   const float scale = 1.0f / sqrtf(128.f);
   const int win = window < 0 || window > T ? T : window;
   if (Hkv < 1 || H % Hkv) return hipErrorInvalidValue;
@@ -921,11 +960,12 @@ hipError_t nc_attn_bwd(int dtype, const void* q, const void* k, const void* v, i
     float* NL = D + (int64_t)B * H * T;
     attn_bwd_dq_kernel<<<B * H * jobs, 256, 0, st>>>(
         (const bf16*)q, (const bf16*)k, (const bf16*)v, ld, (const bf16*)o, (const bf16*)dO,
-        ldo, lse, D, NL, (bf16*)dq, ldd, T, H, G, win, scale * kLog2e, scale, nq);
+        ldo, lse, D, NL, (bf16*)dq, ldd, T, H, G, win, scale * kLog2e, scale, nq, amax_part);
     auto dkv_kernel = G > 1 ? attn_bwd_dkv_kernel<true> : attn_bwd_dkv_kernel<false>;
     dkv_kernel<<<B * Hkv * jobs, 256, 0, st>>>(
         (const bf16*)q, (const bf16*)k, (const bf16*)v, ld, (const bf16*)dO, ldo, NL, D,
-        (bf16*)dk, (bf16*)dv, ldd, T, H, G, win, scale * kLog2e, scale, nq);
+        (bf16*)dk, (bf16*)dv, ldd, T, H, G, win, scale * kLog2e, scale, nq,
+        amax_part ? amax_part + (int64_t)B * H * jobs : nullptr);
   } else {
     if (rqk) return hipErrorInvalidValue;     // fp32: separate D and QK-norm kernels
     hipError_t e = nc_attn_bwd_pre(0, o, dO, ldo, D, B, T, H, st);

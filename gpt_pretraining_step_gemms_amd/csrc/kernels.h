@@ -96,7 +96,7 @@ hipError_t nc_qk_norm_rope_bwd(int dtype, void* dqkv, const void* qkv, const flo
 // Hkv key/value heads (H % Hkv == 0), query head h reads key/value head h / (H / Hkv)
 hipError_t nc_attn_fwd(int dtype, const void* q, const void* k, const void* v, int64_t ld_qkv,
                        void* o, int64_t ld_o, float* lse, int B, int T, int H, int Hkv,
-                       int window, hipStream_t st);
+                       int window, hipStream_t st, float* amax_part = nullptr);
 // D[b,h,t] = sum_d dO*O
 hipError_t nc_attn_bwd_pre(int dtype, const void* o, const void* dO, int64_t ld_o, float* D,
                            int B, int T, int H, hipStream_t st);
@@ -110,7 +110,11 @@ hipError_t nc_attn_bwd(int dtype, const void* q, const void* k, const void* v, i
                        const void* o, const void* dO, int64_t ld_o, const float* lse, float* D,
                        void* dq, void* dk, void* dv, int64_t ld_dqkv, int B, int T, int H,
                        int Hkv, int window, const float* rqk, const float* cos_sin,
-                       hipStream_t st);
+                       hipStream_t st, float* amax_part = nullptr);
+// bf16 path, amax_part (optional): per workgroup the largest |stored output| (o in
+// the forward; dq then dk/dv in the backward), nc_attn_amax_parts(...) floats, for
+// the output's fp8 scale without another pass over it.
+int nc_attn_amax_parts(int B, int T, int H, int Hkv, int window, int backward);
 
 // ---- fp8 with one scale per tensor, x [rows, cols] (row stride cols): fmt 0 = e4m3
 // (fmax 448), 1 = e5m2 (fmax 57344); amax_scale[0] = max |x|, amax_scale[1] = fmax /

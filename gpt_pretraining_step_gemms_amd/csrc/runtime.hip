@@ -423,8 +423,11 @@ void plan(nc_ctx* c) {
     c->q8ws = a.take(1024 * sizeof(float));
   }
   if (c->fp8) {
-    c->q8part_n = std::max<size_t>(ceil_div64(N, 4),
-                                   (size_t)ceil_div64(N, 256) * ceil_div(std::max(F, W), 256));
+    // (RMSNorm: a block per 4 rows; GEMM: a tile per 256 x 256; attention: at most
+    // a workgroup per 128 rows of each query and key/value head)
+    c->q8part_n = std::max<size_t>({(size_t)ceil_div64(N, 4),
+                                    (size_t)ceil_div64(N, 256) * ceil_div(std::max(F, W), 256),
+                                    (size_t)ceil_div64(N, 128) * (H + Hkv)});
     c->q8part = a.take(c->q8part_n * sizeof(float));
     const size_t wn = (size_t)W * d + (size_t)d * d + 2 * (size_t)F * d;
     c->q8wc_layer = (c->fp8b ? 2 : 1) * wn;
@@ -941,9 +944,11 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
     NC_TRY(nc_qk_norm_rope_fwd(dt, qkv, A<float>(ctx, la.rqk), tab, N, T, H, Hkv, eps, st),
            "qknorm");
     NC_TRY(nc_attn_fwd(dt, qkv, qkv + d * es, qkv + (d + dk) * es, Wd, aa + la.o, d,
-                       A<float>(ctx, la.lse), B, T, H, Hkv, ctx->windows[l], st), "attn fwd");
+                       A<float>(ctx, la.lse), B, T, H, Hkv, ctx->windows[l], st, parts),
+           "attn fwd");
     NC_GEMM(ctx->fp8 ? gemm_fp8_fwd(ctx, aa + la.o, d, wcodes(ctx, l, 1, false), d, x, d, N, kEpiAccF32,
-                                    xt_of(l, 1), xs_of(l, 1))
+                                    xt_of(l, 1), xs_of(l, 1), parts,
+                                    nc_attn_amax_parts(B, T, H, Hkv, ctx->windows[l], 0))
                      : gemm(ctx, aa + la.o, d, kKCont, wptr(ctx, wb + oWo), d, kKCont, x, d, N, d,
                             d, kEpiAccF32), "out proj");
     NC_TRY(nc_rmsnorm_fwd(dt, x, aa + la.a2, A<float>(ctx, la.r2), N, d, eps, st, parts), "norm2");
@@ -1046,7 +1051,8 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
     NC_TRY(nc_attn_bwd(dt, qkv, qkv + d * es, qkv + (d + dk) * es, Wd, aa + la.o, aa + ctx->dO, d,
                        A<float>(ctx, la.lse), A<float>(ctx, ctx->Dbuf), dqkv, dqkv + d * es,
                        dqkv + (d + dk) * es, Wd, B, T, H, Hkv, ctx->windows[l],
-                       dt ? A<float>(ctx, la.rqk) : nullptr, dt ? tab : nullptr, st), "attn bwd");
+                       dt ? A<float>(ctx, la.rqk) : nullptr, dt ? tab : nullptr, st, bparts),
+           "attn bwd");
     if (!dt)
       NC_TRY(nc_qk_norm_rope_bwd(dt, dqkv, qkv, A<float>(ctx, la.rqk), tab, N, T, H, Hkv, st),
              "qknorm bwd");
@@ -1065,7 +1071,9 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
                                  G + ctx->e_wg + (size_t)vs * Hkv * ctx->Cg, st), "gate grad");
     }
     if (ctx->fp8b) {
-      NC_GEMM(fp8_grad_codes(ctx, dqkv, N, Wd), "dqkv codes");
+      NC_GEMM(fp8_grad_codes(ctx, dqkv, N, Wd, bparts,
+                             nc_attn_amax_parts(B, T, H, Hkv, ctx->windows[l], 1)),
+              "dqkv codes");
       NC_GEMM(gemm_fp8_dw(ctx, xt_of(l, 0), xs_of(l, 0), Wd, d, G + wb, N, ctx->splits_qkv),
               "dWqkv");
       NC_GEMM(gemm_fp8_dx(ctx, wcodes(ctx, l, 0, true), Wd, d, da, d, N, kEpiStoreF32), "da1");
