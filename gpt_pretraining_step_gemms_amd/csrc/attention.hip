@@ -142,7 +142,9 @@ NC_DEV bf16x8 fa_frag_vt(const bf16* tile, int row_base, int col_base, int lane)
 }
 
 // one 128-query block qb of head bh; st0 / st1: K | V stages of 2 x 64 x 128
-// Returns the largest |o| this lane stored (before rounding to bf16).
+// kAmax: also return the largest |o| this lane stored (before rounding to
+// bf16); a separate instantiation keeps the plain kernel as it was.
+template <bool kAmax>
 NC_DEV float attn_fwd_block(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, bf16* __restrict__ o, int64_t ldo, float* __restrict__ lse, int T, int H,
@@ -277,7 +279,7 @@ NC_DEV float attn_fwd_block(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float ov = oacc[db][g * 4 + i] * inv;
-        amx = max_nan(amx, fabsf(ov));
+        if constexpr (kAmax) amx = max_nan(amx, fabsf(ov));
         w[i] = (bf16)ov;
       }
       *reinterpret_cast<bf16x4*>(os + l32 * OSTR + db * 32 + g * 8 + half * 4) = w;
@@ -318,7 +320,8 @@ struct QkNorm {
 // further) per lane, 8 lanes per row, so that xr, the rotary table and the
 // output move in 16-byte accesses, all issued before any of them is used.
 // The caller has made the region free (no wave still reads it).
-// Returns the largest |value| this lane stored (before rounding to bf16).
+// kAmax: also return the largest |value| this lane stored (before rounding to bf16).
+template <bool kAmax>
 NC_DEV float attn_store_grad(const f32x16 (&acc)[4], float scale, bf16* __restrict__ out,
                             int64_t ldd, int64_t out_row, const bf16* __restrict__ xr,
                             int64_t ld, int64_t xr_row, int row0, int64_t n0, int T, int hn,
@@ -357,7 +360,7 @@ NC_DEV float attn_store_grad(const f32x16 (&acc)[4], float scale, bf16* __restri
         for (int j = 0; j < 8; ++j) {
           h1[j] = (bf16)g1[it][j];
           h2[j] = (bf16)g2[it][j];
-          amx = max_nan(amx, max_nan(fabsf(g1[it][j]), fabsf(g2[it][j])));
+          if constexpr (kAmax) amx = max_nan(amx, max_nan(fabsf(g1[it][j]), fabsf(g2[it][j])));
         }
         bf16* o = out + out_row + row * ldd + 8 * u;
         *reinterpret_cast<bf16x8*>(o) = h1;
@@ -404,7 +407,7 @@ NC_DEV float attn_store_grad(const f32x16 (&acc)[4], float scale, bf16* __restri
         const float v1 = rs[it] * (dy1[j] - y1[j] * mean), v2 = rs[it] * (dy2[j] - y2[j] * mean);
         h1[j] = (bf16)v1;
         h2[j] = (bf16)v2;
-        amx = max_nan(amx, max_nan(fabsf(v1), fabsf(v2)));
+        if constexpr (kAmax) amx = max_nan(amx, max_nan(fabsf(v1), fabsf(v2)));
       }
       const int row = 16 * p + it * 8 + rl;
       bf16* o = out + out_row + row * ldd + 8 * u;
@@ -425,7 +428,7 @@ constexpr int kDkvStage = 2 * 64 * 128 + 256;     // Q | dO | -lse log2(e) [64],
 // one 128-key block kblk of key/value head bhk; st0 / st1: stages of kDkvStage
 // elements.  kGrouped: G > 1 query heads per key/value head, walked in turn (a
 // separate instantiation keeps the plain path's registers as they were).
-template <bool kGrouped>
+template <bool kGrouped, bool kAmax>
 NC_DEV float attn_bwd_dkv_block(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, const bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ nl2,
@@ -567,9 +570,9 @@ NC_DEV float attn_bwd_dkv_block(
   const int64_t row_out = ((int64_t)b * T + k0w) * ldd + hk * 128;
   __syncthreads();                                 // every wave is done with the stages
   float* stg = reinterpret_cast<float*>(wave < 2 ? st0 : st1) + (wave & 1) * 16 * 132;
-  const float amx = attn_store_grad(dvacc, 1.f, dv, ldd, row_out, nullptr, 0, 0, k0w, 0, T, 0,
+  const float amx = attn_store_grad<kAmax>(dvacc, 1.f, dv, ldd, row_out, nullptr, 0, 0, k0w, 0, T, 0,
                                     QkNorm{nullptr, nullptr, 0}, stg, lane);
-  return max_nan(amx, attn_store_grad(dkacc, scale, dk, ldd, row_out, k, ld,
+  return max_nan(amx, attn_store_grad<kAmax>(dkacc, scale, dk, ldd, row_out, k, ld,
                                       kvbase + (int64_t)k0w * ld, k0w, (int64_t)b * T + k0w, T,
                                       H + hk, nq, stg, lane));
 }
@@ -579,6 +582,7 @@ NC_DEV float attn_bwd_dkv_block(
 // to the diagonal, like the forward pass: S^T = K Q^T and dP^T = V dO^T with
 // one query per lane, then dQ += dS K with K^T fragments from transpose reads.
 // one 128-query block qb of head bh; st0 / st1: K | V stages of 2 x 64 x 128
+template <bool kAmax>
 NC_DEV float attn_bwd_dq_block(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, const bf16* __restrict__ o, const bf16* __restrict__ dO, int64_t ldo,
@@ -698,7 +702,7 @@ NC_DEV float attn_bwd_dq_block(
 
   __syncthreads();                                 // every wave is done with the stages
   float* stg = reinterpret_cast<float*>(wave < 2 ? st0 : st1) + (wave & 1) * 16 * 132;
-  return attn_store_grad(dqacc, scale, dq, ldd, ((int64_t)b * T + q0w) * ldd + h * 128, q, ld,
+  return attn_store_grad<kAmax>(dqacc, scale, dq, ldd, ((int64_t)b * T + q0w) * ldd + h * 128, q, ld,
                          base + (int64_t)q0w * ld, q0w, (int64_t)b * T + q0w, T, h, nq, stg, lane);
 }
 
@@ -748,6 +752,7 @@ NC_DEV void attn_amax_out(float amx, float* amax_part, bf16* st0) {
   if (threadIdx.x == 0) amax_part[blockIdx.x] = bf16_abs(amx);
 }
 
+template <bool kAmax>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, bf16* __restrict__ o, int64_t ldo, float* __restrict__ lse, int T, int H,
@@ -755,17 +760,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   __shared__ __attribute__((aligned(1024))) bf16 st0[2 * 64 * 128];   // K | V of even tiles
   __shared__ __attribute__((aligned(1024))) bf16 st1[2 * 64 * 128];   // K | V of odd tiles
   const BlockJob jb = block_job(T / 128, win >= T, true);
-  float amx = attn_fwd_block(q, k, v, ld, o, ldo, lse, T, H, G, win, scale_log2, jb.first,
+  float amx = attn_fwd_block<kAmax>(q, k, v, ld, o, ldo, lse, T, H, G, win, scale_log2, jb.first,
                              jb.bh, st0, st1);
   if (jb.second >= 0) {
     __syncthreads();                               // the first block's O staging is read
-    amx = max_nan(amx, attn_fwd_block(q, k, v, ld, o, ldo, lse, T, H, G, win, scale_log2,
+    amx = max_nan(amx, attn_fwd_block<kAmax>(q, k, v, ld, o, ldo, lse, T, H, G, win, scale_log2,
                                       jb.second, jb.bh, st0, st1));
   }
   attn_amax_out(amx, amax_part, st0);
 }
 
-template <bool kGrouped>
+template <bool kGrouped, bool kAmax>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, const bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ nl2,
@@ -778,16 +783,17 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
   const BlockJob jb = block_job(T / 128, win >= T, false);
   float amx = 0.f;
   if (jb.second >= 0) {
-    amx = attn_bwd_dkv_block<kGrouped>(q, k, v, ld, dO, ldo, nl2, Dv, dk, dv, ldd, T, H, G, win,
+    amx = attn_bwd_dkv_block<kGrouped, kAmax>(q, k, v, ld, dO, ldo, nl2, Dv, dk, dv, ldd, T, H, G, win,
                                        scale_log2, scale, jb.second, jb.bh, st0, st1, nq);
     __syncthreads();
   }
-  amx = max_nan(amx, attn_bwd_dkv_block<kGrouped>(q, k, v, ld, dO, ldo, nl2, Dv, dk, dv, ldd, T,
+  amx = max_nan(amx, attn_bwd_dkv_block<kGrouped, kAmax>(q, k, v, ld, dO, ldo, nl2, Dv, dk, dv, ldd, T,
                                                   H, G, win, scale_log2, scale, jb.first, jb.bh,
                                                   st0, st1, nq));
   attn_amax_out(amx, amax_part, st0);
 }
 
+template <bool kAmax>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, const bf16* __restrict__ o, const bf16* __restrict__ dO, int64_t ldo,
@@ -798,11 +804,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
   __shared__ __attribute__((aligned(1024))) bf16 st0[2 * 64 * 128];   // K | V
   __shared__ __attribute__((aligned(1024))) bf16 st1[2 * 64 * 128];
   const BlockJob jb = block_job(T / 128, win >= T, true);
-  float amx = attn_bwd_dq_block(q, k, v, ld, o, dO, ldo, lse, Dv, NL, dq, ldd, T, H, G, win,
+  float amx = attn_bwd_dq_block<kAmax>(q, k, v, ld, o, dO, ldo, lse, Dv, NL, dq, ldd, T, H, G, win,
                                 scale_log2, scale, jb.first, jb.bh, st0, st1, nq);
   if (jb.second >= 0) {
     __syncthreads();
-    amx = max_nan(amx, attn_bwd_dq_block(q, k, v, ld, o, dO, ldo, lse, Dv, NL, dq, ldd, T, H, G,
+    amx = max_nan(amx, attn_bwd_dq_block<kAmax>(q, k, v, ld, o, dO, ldo, lse, Dv, NL, dq, ldd, T, H, G,
                                          win, scale_log2, scale, jb.second, jb.bh, st0, st1, nq));
   }
   attn_amax_out(amx, amax_part, st0);
@@ -930,7 +936,8 @@ hipError_t nc_attn_fwd(int dtype, const void* q, const void* k, const void* v, i
   const int G = H / Hkv;
   if (dtype) {
     if (T % 128) return hipErrorInvalidValue;
-    attn_fwd_kernel<<<B * H * attn_jobs_per_head(T, win), 256, 0, st>>>(
+    auto fwd_kernel = amax_part ? attn_fwd_kernel<true> : attn_fwd_kernel<false>;
+    fwd_kernel<<<B * H * attn_jobs_per_head(T, win), 256, 0, st>>>(
         (const bf16*)q, (const bf16*)k, (const bf16*)v, ld, (bf16*)o, ldo, lse, T, H, G, win,
         scale * kLog2e, amax_part);
   } else {
@@ -958,10 +965,14 @@ hipError_t nc_attn_bwd(int dtype, const void* q, const void* k, const void* v, i
     // half of D), which the dK/dV kernel reads, so that a score's weight there is
     // one fma and one exp2
     float* NL = D + (int64_t)B * H * T;
-    attn_bwd_dq_kernel<<<B * H * jobs, 256, 0, st>>>(
+    auto dq_kernel = amax_part ? attn_bwd_dq_kernel<true> : attn_bwd_dq_kernel<false>;
+    dq_kernel<<<B * H * jobs, 256, 0, st>>>(
         (const bf16*)q, (const bf16*)k, (const bf16*)v, ld, (const bf16*)o, (const bf16*)dO,
         ldo, lse, D, NL, (bf16*)dq, ldd, T, H, G, win, scale * kLog2e, scale, nq, amax_part);
-    auto dkv_kernel = G > 1 ? attn_bwd_dkv_kernel<true> : attn_bwd_dkv_kernel<false>;
+    auto dkv_kernel = G > 1 ? (amax_part ? attn_bwd_dkv_kernel<true, true>
+                                         : attn_bwd_dkv_kernel<true, false>)
+                            : (amax_part ? attn_bwd_dkv_kernel<false, true>
+                                         : attn_bwd_dkv_kernel<false, false>);
     dkv_kernel<<<B * Hkv * jobs, 256, 0, st>>>(
         (const bf16*)q, (const bf16*)k, (const bf16*)v, ld, (const bf16*)dO, ldo, NL, D,
         (bf16*)dk, (bf16*)dv, ldd, T, H, G, win, scale * kLog2e, scale, nq,

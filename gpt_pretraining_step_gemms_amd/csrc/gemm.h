@@ -37,7 +37,7 @@ struct GemmParams {
   // s_A * s_B before the epilogue.  Null: no device scales.
   const float* scale_a; const float* scale_b;
   int fmt_a;                         // fp8 only: A's format, 0 = e4m3, 1 = e5m2 (B is e4m3)
-  // optional, ReLU^2 and ReLU^2-backward epilogues of the pipelined kernel (one
+  // optional, ReLU^2 and ReLU^2-backward epilogues of the fp8 kernel (one
   // batch, no split): per workgroup the largest |C| as stored (bf16), one float
   // per output tile, for C's fp8 scale without another pass over C
   float* amax_part;

@@ -1165,11 +1165,16 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
             }
           } else {
             const int64_t off = cb + (int64_t)m * ld_out + n;
+            // (the output amax is kept by the fp8 instantiations only, so that
+            // the bf16 kernels stay as they were)
             if (vec && n + 8 <= p.N) {
-              amx = max_nan(amx, epi_apply8<EPI>(p, off, v, in[ii][t]));
+              const float m8 = epi_apply8<EPI>(p, off, v, in[ii][t]);
+              if constexpr (F8) amx = max_nan(amx, m8);
             } else {
-              for (int e = 0; e < 8 && n + e < p.N; ++e)
-                amx = max_nan(amx, epi_one<bf16, EPI>(p, off + e, v[e]));
+              for (int e = 0; e < 8 && n + e < p.N; ++e) {
+                const float m1 = epi_one<bf16, EPI>(p, off + e, v[e]);
+                if constexpr (F8) amx = max_nan(amx, m1);
+              }
             }
           }
         }
@@ -1178,7 +1183,7 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
   };
   if (split_out) run.template operator()<kEpiStoreF32>();
   else with_epilogue(p.epi, run);
-  if (p.amax_part) {
+  if (F8 && p.amax_part) {
     // the staging buffers are free once every wave has passed the first
     // barrier inside block_max_nan
     amx = block_max_nan(amx, reinterpret_cast<float*>(st0));
@@ -1341,7 +1346,7 @@ hipError_t nc_launch_gemm(int dtype, const GemmParams& p_in, hipStream_t st) {
                 al16(p.aux_in) && al16(p.aux_out);
   }
   const bool use_pipe = pipe_ok(p);
-  if (p.amax_part && (!use_pipe || p.batch != 1 || p.splits != 1)) return hipErrorInvalidValue;
+  if (p.amax_part) return hipErrorInvalidValue;    // kept by the fp8 kernels only
   hipError_t e = use_pipe ? launch_pipe(p, st) : launch_bf16_cfg<256, 256, 2, 4>(p, st);
   if (e != hipSuccess || p.splits == 1) return e;
   return splitk_reduce(p, st);
