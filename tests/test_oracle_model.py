@@ -300,3 +300,39 @@ def test_accumulation_of_half_batches_equals_full_batch():
     for n in g_full:
         np.testing.assert_allclose(g_a[n] + g_b[n], g_full[n], rtol=0,
                                    atol=1e-12 * max(1e-30, np.max(np.abs(g_full[n]))))
+
+
+@pytest.mark.filterwarnings("ignore:The number of unique classes")
+def test_zero_layer_model_is_softmax_regression_on_normalised_embeddings():
+    """With no blocks the model is multinomial logistic regression of the
+    next token on the normalised embedding row: its loss is the library's
+    log-loss of softmax(N(E[tok]) Wh^T), and the lm_head gradient is the
+    regression's (softmax - onehot)^T features / n (checked against finite
+    differences of that library loss)."""
+    from sklearn.metrics import log_loss
+    V, d = 50, 32
+    cfg = dict(n_layer=0, d_model=d, n_head=1, head_dim=d, d_ff=64, vocab=V, seq_len=8,
+               rope_base=10000.0, norm_eps=1e-6)
+    params = {k: v.astype(np.float64) for k, v in
+              synthetic.normal_params(4, param_shapes(cfg), 0.5).items()}
+    tok, tgt = synthetic.token_rows(5, 3, 8, V, "uniform")
+    loss, grads = oracle.loss_and_grads(params, tok, tgt, cfg)
+    x = params["E"][tok.reshape(-1)]
+    feats = x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + 1e-6)
+
+    def lib_loss(Wh):
+        z = feats @ Wh.T
+        prob = np.exp(z - z.max(1, keepdims=True))
+        prob /= prob.sum(1, keepdims=True)
+        return log_loss(tgt.reshape(-1), prob, labels=np.arange(V))
+
+    assert loss == pytest.approx(lib_loss(params["Wh"]), rel=1e-12)
+    rng = np.random.default_rng(6)
+    h = 1e-6
+    for _ in range(20):
+        i, j = rng.integers(V), rng.integers(d)
+        Wp, Wm = params["Wh"].copy(), params["Wh"].copy()
+        Wp[i, j] += h
+        Wm[i, j] -= h
+        fd = (lib_loss(Wp) - lib_loss(Wm)) / (2 * h)
+        assert grads["Wh"][i, j] == pytest.approx(fd, rel=1e-5, abs=1e-9)
