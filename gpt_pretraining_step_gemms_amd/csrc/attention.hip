@@ -89,19 +89,42 @@ NC_DEV void fa_wait_vmcnt() {
 }
 NC_DEV void fa_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// Swizzle of 16-byte chunks in a [rows][128] bf16 tile: chunk c of row r is
-// stored at c ^ fa_swz(r).  Eight consecutive rows read at one chunk
-// (ds_read_b128) and four consecutive rows read at two neighbouring chunks
-// (ds_read_b64_tr_b16) both hit 8 distinct bank groups.
-NC_DEV int fa_swz(int r) { return (2 * (r & 3)) | ((r >> 2) & 1); }
+// Swizzles of 16-byte chunks in a [rows][128] bf16 tile: chunk c of row r is
+// stored at c ^ fa_swz<SW>(r).  A 256-byte row spans all 64 LDS banks; a
+// ds_read_b128 serves 16 lanes per pass and a ds_read_b64_tr_b16 32 lanes,
+// so a fragment read takes one pass only when the rows it touches land on
+// distinct chunk positions.  The two fragment reads are
+//   * rows: 32 consecutive rows at one chunk (ds_read_b128, lanes 0-15 and
+//     16-31 each take 16 rows), and
+//   * transposed: 4 consecutive rows (from a multiple of 4) x 4 chunks of an
+//     aligned quad, twice (rows + 8), per 32 lanes (ds_read_b64_tr_b16).
+// Kinds:
+//   0: 2 (r & 3) + ((r >> 2) & 1), period 8: two passes for either read, but
+//      one swizzle serves tiles read both ways, and rows r + 8 share it;
+//   1: r & 15: one pass for row reads (tiles only read that way);
+//   2: 4 (r & 3) + ((r >> 2) & 1), period 8: one pass for transposed reads
+//      (tiles only read that way), rows r + 8 sharing the swizzle.
+// A 16-row swizzle that serves both reads in one pass (4 (r & 3) +
+// ((r >> 2) & 3)) gives rows r + 8 another swizzle, so the transposed read's
+// second half needs its own address, and the row reads need twice the
+// address variants: in dK/dV it measured level (the saved LDS cycles paid for
+// by the extra registers and address arithmetic), and dQ spilled.
+template <int SW>
+NC_DEV int fa_swz(int r) {
+  static_assert(SW >= 0 && SW <= 2, "swizzle kinds 0, 1, 2");
+  if constexpr (SW == 0) return (2 * (r & 3)) | ((r >> 2) & 1);
+  else if constexpr (SW == 1) return r & 15;
+  else return 4 * (r & 3) + ((r >> 2) & 1);
+}
 
 // this wave's share (4 x 1 KB) of a 64-row x 128 token-major tile into LDS
+template <int SW>
 NC_DEV void fa_issue_rows(const bf16* src, int64_t ld, int row0, bf16* tile, int wave, int lane) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int blk = wave * 4 + i;                 // 16 blocks of 4 rows
     const int r = blk * 4 + (lane >> 4);
-    const int c = (lane & 15) ^ fa_swz(r);
+    const int c = (lane & 15) ^ fa_swz<SW>(r);
     fa_dma16(src + (int64_t)(row0 + r) * ld + c * 8, tile + blk * 512);
   }
 }
@@ -121,18 +144,21 @@ NC_DEV void fa_dma4(const float* g, const float* lds) {
 }
 
 typedef __bf16 fa_bf16x4 __attribute__((ext_vector_type(4)));
+template <int SW>
 NC_DEV bf16x8 fa_frag_k(const bf16* tile, int r, int c) {
-  return *reinterpret_cast<const bf16x8*>(tile + r * 128 + ((c ^ fa_swz(r)) << 3));
+  return *reinterpret_cast<const bf16x8*>(tile + r * 128 + ((c ^ fa_swz<SW>(r)) << 3));
 }
 // 8 values of head dim `col_base + lane%16` (within a 16-wide column block) at
-// key rows row_base + {0..3} and row_base + 8 + {0..3}, from a [key][128] tile
-// stored with the fa_swz swizzle (rows r and r + 8 share it)
+// key rows row_base + {0..3} and row_base + 8 + {0..3} (row_base % 16 < 8),
+// from a [key][128] tile stored with the fa_swz<SW> swizzle
+template <int SW>
 NC_DEV bf16x8 fa_frag_vt(const bf16* tile, int row_base, int col_base, int lane) {
+  static_assert(SW != 1, "kind 1 tiles are only read by rows");
   const int t = lane & 15;
   const int r = row_base + (t >> 2);
   const int col = col_base + 4 * (t & 3);
-  const bf16* p0 = tile + r * 128 + (((col >> 3) ^ fa_swz(r)) << 3) + (col & 7);
-  const bf16* p1 = p0 + 8 * 128;                 // row + 8: same swizzle
+  const bf16* p0 = tile + r * 128 + (((col >> 3) ^ fa_swz<SW>(r)) << 3) + (col & 7);
+  const bf16* p1 = p0 + 8 * 128;                 // rows + 8: same swizzle
   const fa_bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) fa_bf16x4*)p0);
   const fa_bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) fa_bf16x4*)p1);
   bf16x8 v;
@@ -140,6 +166,12 @@ NC_DEV bf16x8 fa_frag_vt(const bf16* tile, int row_base, int col_base, int lane)
   v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
   return v;
 }
+
+// Swizzle per tile (each kernel stages its own): the forward's K tile is only
+// read by rows and its V tile only transposed, so both take one pass (the
+// forward measured 1.5-2 % faster than with kind 0, outputs bitwise equal);
+// dQ reads K both ways, and dK/dV reads Q and dO both ways (kind 0).
+constexpr int kSwFwdK = 1, kSwFwdV = 2, kSwDqK = 0, kSwDqV = 0, kSwDkv = 0;
 
 // one 128-query block qb of head bh; st0 / st1: K | V stages of 2 x 64 x 128
 // kAmax: also return the largest |o| this lane stored (before rounding to
@@ -180,8 +212,8 @@ NC_DEV float attn_fwd_block(
   const int n_kv = 2 * qb + 2;
   const int kv_lo = max(0, qb * 128 - win) / 64;
   auto issue = [&](int kv, bf16* st) {
-    fa_issue_rows(kg, ld, kv * 64, st, wave, lane);
-    fa_issue_rows(vg, ld, kv * 64, st + KT, wave, lane);
+    fa_issue_rows<kSwFwdK>(kg, ld, kv * 64, st, wave, lane);
+    fa_issue_rows<kSwFwdV>(vg, ld, kv * 64, st + KT, wave, lane);
   };
   auto step = [&](int kv, const bf16* ks, bf16* next) {
     fa_wait_vmcnt<0>();         // this wave's loads of tile kv have landed
@@ -197,7 +229,7 @@ NC_DEV float attn_fwd_block(
       for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
 #pragma unroll
       for (int s = 0; s < 8; ++s)
-        sacc[kb] = mfma(fa_frag_k(ks, kb * 32 + l32, s * 2 + half), qf[s], sacc[kb]);
+        sacc[kb] = mfma(fa_frag_k<kSwFwdK>(ks, kb * 32 + l32, s * 2 + half), qf[s], sacc[kb]);
     }
     // Online softmax in the log2 domain.  The running max m of a query only
     // moves when the tile's max exceeds it by more than 8: the weights
@@ -251,7 +283,7 @@ NC_DEV float attn_fwd_block(
       const int row_base = (j >> 1) * 32 + (j & 1) * 16 + half * 4;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
-        oacc[db] = mfma(fa_frag_vt(vs, row_base, db * 32 + 16 * ((lane >> 4) & 1), lane), pf,
+        oacc[db] = mfma(fa_frag_vt<kSwFwdV>(vs, row_base, db * 32 + 16 * ((lane >> 4) & 1), lane), pf,
                         oacc[db]);
     }
   };
@@ -471,8 +503,8 @@ NC_DEV float attn_bwd_dkv_block(
   // query tiles from the diagonal to the last query whose window holds a key of the block
   const int qt0 = kblk * 2, nqt = min(T / 64, (kblk * 128 + 127 + win) / 64 + 1);
   auto issue = [&](int qt, bf16* st) {
-    fa_issue_rows(q + base, ld, qt * 64, st, wave, lane);
-    fa_issue_rows(dO + obase, ldo, qt * 64, st + KT, wave, lane);
+    fa_issue_rows<kSwDkv>(q + base, ld, qt * 64, st, wave, lane);
+    fa_issue_rows<kSwDkv>(dO + obase, ldo, qt * 64, st + KT, wave, lane);
     if (wave == 0) {
       float* stats = reinterpret_cast<float*>(st + 2 * KT);
       fa_dma4(lse_bh + qt * 64 + lane, stats);
@@ -496,8 +528,8 @@ NC_DEV float attn_bwd_dkv_block(
       for (int e = 0; e < 16; ++e) { sacc[qb][e] = 0.f; pacc[qb][e] = 0.f; }
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        sacc[qb] = mfma(fa_frag_k(Qs, qb * 32 + l32, s * 2 + half), kf[s], sacc[qb]);
-        pacc[qb] = mfma(fa_frag_k(dOs, qb * 32 + l32, s * 2 + half), vf[s], pacc[qb]);
+        sacc[qb] = mfma(fa_frag_k<kSwDkv>(Qs, qb * 32 + l32, s * 2 + half), kf[s], sacc[qb]);
+        pacc[qb] = mfma(fa_frag_k<kSwDkv>(dOs, qb * 32 + l32, s * 2 + half), vf[s], pacc[qb]);
       }
     }
     // masks (only tiles crossing an edge of the band): queries before the
@@ -537,8 +569,8 @@ NC_DEV float attn_bwd_dkv_block(
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const int cb = db * 32 + 16 * ((lane >> 4) & 1);
-        dvacc[db] = mfma(pa, fa_frag_vt(dOs, row_base, cb, lane), dvacc[db]);
-        dkacc[db] = mfma(dsa, fa_frag_vt(Qs, row_base, cb, lane), dkacc[db]);
+        dvacc[db] = mfma(pa, fa_frag_vt<kSwDkv>(dOs, row_base, cb, lane), dvacc[db]);
+        dkacc[db] = mfma(dsa, fa_frag_vt<kSwDkv>(Qs, row_base, cb, lane), dkacc[db]);
       }
     }
   };
@@ -642,8 +674,8 @@ NC_DEV float attn_bwd_dq_block(
   const int n_kv = 2 * qb + 2;
   const int kv_lo = max(0, qb * 128 - win) / 64;
   auto issue = [&](int kv, bf16* st) {
-    fa_issue_rows(kg, ld, kv * 64, st, wave, lane);
-    fa_issue_rows(vg, ld, kv * 64, st + KT, wave, lane);
+    fa_issue_rows<kSwDqK>(kg, ld, kv * 64, st, wave, lane);
+    fa_issue_rows<kSwDqV>(vg, ld, kv * 64, st + KT, wave, lane);
   };
   auto step = [&](int kv, const bf16* cur, bf16* next) {
     fa_wait_vmcnt<0>();
@@ -660,8 +692,8 @@ NC_DEV float attn_bwd_dq_block(
       for (int e = 0; e < 16; ++e) { sacc[kb][e] = 0.f; pacc[kb][e] = 0.f; }
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        sacc[kb] = mfma(fa_frag_k(Ks, kb * 32 + l32, s * 2 + half), qf[s], sacc[kb]);
-        pacc[kb] = mfma(fa_frag_k(Vs, kb * 32 + l32, s * 2 + half), df[s], pacc[kb]);
+        sacc[kb] = mfma(fa_frag_k<kSwDqK>(Ks, kb * 32 + l32, s * 2 + half), qf[s], sacc[kb]);
+        pacc[kb] = mfma(fa_frag_k<kSwDqV>(Vs, kb * 32 + l32, s * 2 + half), df[s], pacc[kb]);
       }
     }
     // masks (only tiles crossing an edge of the band): keys after the query
@@ -689,7 +721,7 @@ NC_DEV float attn_bwd_dq_block(
       const int row_base = (j >> 1) * 32 + (j & 1) * 16 + half * 4;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
-        dqacc[db] = mfma(a, fa_frag_vt(Ks, row_base, db * 32 + 16 * ((lane >> 4) & 1), lane),
+        dqacc[db] = mfma(a, fa_frag_vt<kSwDqK>(Ks, row_base, db * 32 + 16 * ((lane >> 4) & 1), lane),
                          dqacc[db]);
     }
   };
