@@ -235,8 +235,8 @@ __global__ void rmsnorm_fwd_kernel(const float* __restrict__ x, T* __restrict__ 
   }
 }
 
-template <typename T>
-__global__ void rmsnorm_bwd_kernel(const float* __restrict__ dy, const T* __restrict__ y,
+template <typename T, typename TD>
+__global__ void rmsnorm_bwd_kernel(const TD* __restrict__ dy, const T* __restrict__ y,
                                    const float* __restrict__ r, float* __restrict__ dx,
                                    T* __restrict__ dxT, int rows, int d, int accumulate,
                                    float* __restrict__ amax_part) {
@@ -251,7 +251,7 @@ __global__ void rmsnorm_bwd_kernel(const float* __restrict__ dy, const T* __rest
     for (int k = 0; k < kMaxVec; ++k) {
       const int i = (lane + k * 64) * 4;
       if (i < d) {
-        Vec4<float>::load(dy + off + i, g[k]);
+        Vec4<TD>::load(dy + off + i, g[k]);
         Vec4<T>::load(y + off + i, yy[k]);
         dot += g[k][0] * yy[k][0] + g[k][1] * yy[k][1] + g[k][2] * yy[k][2] + g[k][3] * yy[k][3];
       }
@@ -1051,16 +1051,19 @@ hipError_t nc_rmsnorm_fwd(int dtype, const float* x, void* y, float* r, int rows
   return hipGetLastError();
 }
 
-hipError_t nc_rmsnorm_bwd(int dtype, const float* dy, const void* y, const float* r, float* dx,
-                          void* dxT, int rows, int d, int accumulate, hipStream_t st,
+hipError_t nc_rmsnorm_bwd(int dtype, const void* dy, int dy_bf16, const void* y, const float* r,
+                          float* dx, void* dxT, int rows, int d, int accumulate, hipStream_t st,
                           float* amax_part) {
   const int g = ceil_div(rows, 4);
-  if (dtype)
-    rmsnorm_bwd_kernel<bf16><<<g, 256, 0, st>>>(dy, (const bf16*)y, r, dx, (bf16*)dxT, rows, d,
-                                                accumulate, amax_part);
+  if (dtype && dy_bf16)
+    rmsnorm_bwd_kernel<bf16, bf16><<<g, 256, 0, st>>>((const bf16*)dy, (const bf16*)y, r, dx,
+                                                      (bf16*)dxT, rows, d, accumulate, amax_part);
+  else if (dtype)
+    rmsnorm_bwd_kernel<bf16, float><<<g, 256, 0, st>>>((const float*)dy, (const bf16*)y, r, dx,
+                                                       (bf16*)dxT, rows, d, accumulate, amax_part);
   else
-    rmsnorm_bwd_kernel<float><<<g, 256, 0, st>>>(dy, (const float*)y, r, dx, (float*)dxT, rows, d,
-                                                 accumulate, amax_part);
+    rmsnorm_bwd_kernel<float, float><<<g, 256, 0, st>>>((const float*)dy, (const float*)y, r, dx,
+                                                        (float*)dxT, rows, d, accumulate, amax_part);
   return hipGetLastError();
 }
 

@@ -723,9 +723,7 @@ NC_DEV void wait_vmcnt() {
 // 16-byte fragments the bf16 path reads for the two 32-deep substeps of a
 // 64-element (128-byte) k-step.  Both operands take the same byte positions, so
 // each of the step's 128 k is summed exactly once.  FA is A's format (0: e4m3,
-// 1: e5m2, the instruction's format codes); B is e4m3.  Like the bf16 16 x 16
-// tiles, the product is computed transposed (B's fragment as the instruction's
-// first operand), so that a lane holds 4 consecutive columns of one row.
+// 1: e5m2, the instruction's format codes); B is e4m3.
 template <int FA>
 NC_DEV f32x4 mfma_f8(bf16x8 a0, bf16x8 a1, bf16x8 b0, bf16x8 b1, f32x4 c) {
   typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -733,7 +731,7 @@ NC_DEV f32x4 mfma_f8(bf16x8 a0, bf16x8 a1, bf16x8 b0, bf16x8 b1, f32x4 c) {
   const i32x4 y0 = __builtin_bit_cast(i32x4, b0), y1 = __builtin_bit_cast(i32x4, b1);
   const i32x8 a = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
   const i32x8 b = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, c, 0, FA, 0, 0, 0, 0);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, 0, 0, 0, 0, 0);
 }
 
 // F8: operands are fp8 bytes (A in format FA_, B e4m3), handled by the loads
@@ -924,7 +922,7 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
         if constexpr (MI == 32)
           acc[ii][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[ii], cur[TM + j], acc[ii][j], 0, 0, 0);
         else
-          acc[ii][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur[TM + j], cur[ii], acc[ii][j], 0, 0, 0);
+          acc[ii][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur[ii], cur[TM + j], acc[ii][j], 0, 0, 0);
         if constexpr (PREF) __builtin_amdgcn_sched_barrier(0);
         if (PREF && s + 1 < NSUB && t < NR) {
           read_one(s + 1, t, nxf[t]);
@@ -973,7 +971,7 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
 #pragma unroll
         for (int t = 0; t < NM; ++t) {
           const int ii = t / TN, j = t % TN;
-          acc[ii][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(frB[cur][j], frA[ii], acc[ii][j],
+          acc[ii][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(frA[ii], frB[cur][j], acc[ii][j],
                                                                 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
           if (t < TN) {
@@ -1129,8 +1127,7 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
       for (int ii = 0; ii < GI; ++ii) {
         const int i = i0 + ii;                           // 32-row block of the wave tile
         // 32 x 32 tile: lane c + 32 h holds column c, rows 8 (e / 4) + 4 h + e % 4;
-        // 16 x 16 tile (computed transposed): lane r + 16 g holds row r,
-        // columns 4 g + e, written as one 16-byte store
+        // 16 x 16 tile: lane c + 16 g holds column c, rows 4 g + e
         if constexpr (MI == 32) {
 #pragma unroll
           for (int j = 0; j < TNH; ++j)
@@ -1143,8 +1140,10 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
           for (int i2 = 0; i2 < 2; ++i2)
 #pragma unroll
             for (int j = 0; j < TNH; ++j)
-              *reinterpret_cast<f32x4*>(stg + (i2 * 16 + (lane & 15)) * EP_LD + j * 16 +
-                                        4 * (lane >> 4)) = acc[2 * i + i2][hc * TNH + j];
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                stg[(i2 * 16 + 4 * (lane >> 4) + e) * EP_LD + j * 16 + (lane & 15)] =
+                    acc[2 * i + i2][hc * TNH + j][e];
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -1182,70 +1181,8 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
       }
     }
   };
-  // bf16 outputs that read nothing back (plain store, ReLU^2) from the bf16
-  // kernels with 16 x 16 tiles (the fp8 ones, which keep the output's amax,
-  // have no registers to spare for it): the epilogue is applied in the
-  // accumulator layout, and each wave stages its whole 128 x 64 bf16 tile in
-  // its own 16 KB of the ring at once (8-byte writes of a lane's 4 columns,
-  // 16-byte reads of 8), then stores whole rows.  The 8-byte chunk c of a
-  // 128-byte row r sits at c ^ 2 ((r / 2) % 8): both the writes and the reads
-  // are conflict free.  The fp32 path stages 32 rows at a time and waits for
-  // each round.  (Same-box A/B, outputs bitwise equal: MLP up-projection with
-  // ReLU^2 1.7 % faster, the input-gradient stores 0.9 %.)
-  constexpr int RB = WTN * 2, RS = WTM * RB;           // row and region bytes
-  constexpr bool BF16_EPI = !F8 && MI == 16 && HALF && WTM == 128 && WTN == 64 &&
-                            (C::NT / 64) * RS <= 4 * BUF * 2;
-  auto run_bf16 = [&]<int EPI>() {
-    constexpr int PER = BUF * 2 / RS;                  // regions per ring buffer
-    const int bi = wave / PER;
-    unsigned char* reg = reinterpret_cast<unsigned char*>(
-        bi == 0 ? st0 : (bi == 1 ? st1 : (bi == 2 ? st2 : st3))) + (wave % PER) * RS;
-    auto chunk = [](int row, int c8) { return c8 ^ (2 * ((row >> 1) & 7)); };
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int row = 16 * i + (lane & 15), c8 = 4 * j + (lane >> 4);
-        bf16x4_t w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float r = p.alpha * acc[i][j][e];
-          if constexpr (EPI == kEpiRelu2) {
-            r = fmaxf(r, 0.f);
-            r *= r;
-          }
-          w[e] = static_cast<bf16>(r);
-        }
-        *reinterpret_cast<bf16x4_t*>(reg + row * RB + 8 * chunk(row, c8)) = w;
-      }
-    // (read back by the same wave: a wave's LDS operations complete in order)
-    constexpr int LPR = WTN / 8, RPI = 64 / LPR;       // lanes per row, rows per read
-#pragma unroll
-    for (int t = 0; t < WTM / RPI; ++t) {
-      const int row = RPI * t + lane / LPR, q = lane % LPR;
-      const bf16x8 h = *reinterpret_cast<const bf16x8*>(reg + row * RB + 8 * chunk(row, 2 * q));
-      const int m = m0 + wm * WTM + row, n = n0 + wn * WTN + 8 * q;
-      if (m >= p.M || n >= p.N) continue;
-      bf16* c = static_cast<bf16*>(p.C) + cb + (int64_t)m * p.ldc + n;
-      if (n + 8 <= p.N) {
-        __builtin_nontemporal_store(h, reinterpret_cast<bf16x8*>(c));
-      } else {
-        for (int e = 0; e < 8 && n + e < p.N; ++e) c[e] = h[e];
-      }
-    }
-  };
-  bool done = false;
-  if constexpr (BF16_EPI) {
-    if (!split_out && p.vec_epi && (p.epi == kEpiStore || p.epi == kEpiRelu2)) {
-      if (p.epi == kEpiStore) run_bf16.template operator()<kEpiStore>();
-      else run_bf16.template operator()<kEpiRelu2>();
-      done = true;
-    }
-  }
-  if (!done) {
-    if (split_out) run.template operator()<kEpiStoreF32>();
-    else with_epilogue(p.epi, run);
-  }
+  if (split_out) run.template operator()<kEpiStoreF32>();
+  else with_epilogue(p.epi, run);
   if (F8 && p.amax_part) {
     // the staging buffers are free once every wave has passed the first
     // barrier inside block_max_nan

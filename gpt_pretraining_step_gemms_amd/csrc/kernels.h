@@ -79,8 +79,9 @@ hipError_t nc_sum_into(const float* vals, int n, float* out, hipStream_t st);
 hipError_t nc_rmsnorm_fwd(int dtype, const float* x, void* y, float* r, int rows, int d,
                           float eps, hipStream_t st, float* amax_part = nullptr);
 // dx (+)= r*(dy - y*mean(dy*y)); also writes dxT = dx in the activation type.
-hipError_t nc_rmsnorm_bwd(int dtype, const float* dy, const void* y, const float* r, float* dx,
-                          void* dxT, int rows, int d, int accumulate, hipStream_t st,
+// dy: the gradient at the norm's output, fp32, or bf16 with dy_bf16 (bf16 only)
+hipError_t nc_rmsnorm_bwd(int dtype, const void* dy, int dy_bf16, const void* y, const float* r,
+                          float* dx, void* dxT, int rows, int d, int accumulate, hipStream_t st,
                           float* amax_part = nullptr);
 
 // ---- QK RMSNorm + rotary (qkv token-major [n_tok, (H + 2 Hkv)*128]: H q heads, Hkv k

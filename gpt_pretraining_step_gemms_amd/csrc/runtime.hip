@@ -990,7 +990,7 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
   // wrote it (the mixed-stream backward leaves none: dxT_parts false)
   float* bparts = ctx->fp8b ? parts : nullptr;
   const int nb_rows = ceil_div(N, 4), nb_ff = ceil_div(N, 256) * ceil_div(F, 256);
-  NC_TRY(nc_rmsnorm_bwd(dt, da, aa + ctx->xf, A<float>(ctx, ctx->rf), dx, dxT, N, d, 0, st,
+  NC_TRY(nc_rmsnorm_bwd(dt, da, 0, aa + ctx->xf, A<float>(ctx, ctx->rf), dx, dxT, N, d, 0, st,
                         bparts), "normf bwd");
   bool dxT_parts = bparts != nullptr;
   float* part_a = (ctx->resid_on || ctx->backout_on) ? A<float>(ctx, ctx->part_a) : nullptr;
@@ -1004,6 +1004,14 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
   }
   if (dx0b) NC_TRY(nc_fill_f32(dx0b, 0.f, Nd, st), "zero dx0");
   if (ctx->ve_on) NC_TRY(nc_embed_sort(tok, N, V, emb_scratch, st), "token sort");
+
+  // The gradient at a block norm's output (da, from the da1 / da2 products)
+  // is stored in bf16 when nothing else adds into it (no value-embedding gate,
+  // no mixed-stream norm): half the bytes for the product's epilogue and the
+  // norm backward.  The final norm's comes from the split-K lm_head product
+  // and stays fp32.
+  const bool da16 = dt && !ctx->ve_on && !ctx->resid_on && !ctx->backout_on;
+  const int epi_da = da16 ? kEpiStore : kEpiStoreF32;
 
   // --------------------------------------------------------------- backward
   for (int l = L - 1; l >= 0; --l) {
@@ -1021,7 +1029,7 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
       NC_GEMM(gemm_fp8_dw(ctx, xt_of(l, 3), xs_of(l, 3), d, F, G + w2, N, ctx->splits_2), "dW2");
       NC_GEMM(fp8_grad_codes(ctx, aa + ctx->dh, N, F, bparts, nb_ff), "dh codes");
       NC_GEMM(gemm_fp8_dw(ctx, xt_of(l, 2), xs_of(l, 2), F, d, G + w1, N, ctx->splits_1), "dW1");
-      NC_GEMM(gemm_fp8_dx(ctx, wcodes(ctx, l, 2, true), F, d, da, d, N, kEpiStoreF32), "da2");
+      NC_GEMM(gemm_fp8_dx(ctx, wcodes(ctx, l, 2, true), F, d, da, d, N, epi_da), "da2");
     } else {
       NC_GEMM(gemm(ctx, dxT, d, kKCont, wptr(ctx, w2), F, kMNCont, aa + ctx->dh, F, N, F, d,
                   kEpiRelu2Bwd, aa + la.g), "dh");
@@ -1030,9 +1038,10 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
       NC_GEMM(gemm(ctx, aa + ctx->dh, F, kMNCont, aa + la.a2, d, kMNCont, G + w1, d, F, d, N,
                   kEpiAccF32, nullptr, nullptr, ctx->splits_1), "dW1");
       NC_GEMM(gemm(ctx, aa + ctx->dh, F, kKCont, wptr(ctx, w1), d, kMNCont, da, d, N, d, F,
-                  kEpiStoreF32), "da2");
+                  epi_da), "da2");
     }
-    NC_TRY(nc_rmsnorm_bwd(dt, da, aa + la.a2, A<float>(ctx, la.r2), dx, dxT, N, d, 1, st, bparts),
+    NC_TRY(nc_rmsnorm_bwd(dt, da, da16, aa + la.a2, A<float>(ctx, la.r2), dx, dxT, N, d, 1, st,
+                          bparts),
            "norm2 bwd");
     // attention
     if (ctx->fp8b) {
@@ -1076,12 +1085,12 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
               "dqkv codes");
       NC_GEMM(gemm_fp8_dw(ctx, xt_of(l, 0), xs_of(l, 0), Wd, d, G + wb, N, ctx->splits_qkv),
               "dWqkv");
-      NC_GEMM(gemm_fp8_dx(ctx, wcodes(ctx, l, 0, true), Wd, d, da, d, N, kEpiStoreF32), "da1");
+      NC_GEMM(gemm_fp8_dx(ctx, wcodes(ctx, l, 0, true), Wd, d, da, d, N, epi_da), "da1");
     } else {
       NC_GEMM(gemm(ctx, dqkv, Wd, kMNCont, aa + la.a1, d, kMNCont, G + wb, d, Wd, d, N,
                   kEpiAccF32, nullptr, nullptr, ctx->splits_qkv), "dWqkv");
       NC_GEMM(gemm(ctx, dqkv, Wd, kKCont, wptr(ctx, wb), d, kMNCont, da, d, N, d, Wd,
-                  kEpiStoreF32), "da1");
+                  epi_da), "da1");
     }
     if (vs >= 0)
       NC_TRY(nc_ve_gate_da(A<float>(ctx, ctx->dz_ve), Pm + ctx->e_wg + (size_t)vs * Hkv * ctx->Cg,
@@ -1100,7 +1109,7 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
       }
       dxT_parts = false;
     } else {
-      NC_TRY(nc_rmsnorm_bwd(dt, da, aa + la.a1, A<float>(ctx, la.r1), dx, dxT, N, d, 1, st,
+      NC_TRY(nc_rmsnorm_bwd(dt, da, da16, aa + la.a1, A<float>(ctx, la.r1), dx, dxT, N, d, 1, st,
                             bparts), "norm1 bwd");
       dxT_parts = bparts != nullptr;
     }
