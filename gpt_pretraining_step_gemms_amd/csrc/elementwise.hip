@@ -245,7 +245,9 @@ __global__ void rmsnorm_bwd_kernel(const TD* __restrict__ dy, const T* __restric
   float amx = 0.f;
   if (row < rows) {
     const int64_t off = (int64_t)row * d;
-    float g[kMaxVec][4], yy[kMaxVec][4];
+    // the accumulated gradient is loaded with dy and y, so that one memory
+    // round trip per row sits in front of the reduction instead of two
+    float g[kMaxVec][4], yy[kMaxVec][4], o0[kMaxVec][4];
     float dot = 0.f;
 #pragma unroll
     for (int k = 0; k < kMaxVec; ++k) {
@@ -253,18 +255,18 @@ __global__ void rmsnorm_bwd_kernel(const TD* __restrict__ dy, const T* __restric
       if (i < d) {
         Vec4<TD>::load(dy + off + i, g[k]);
         Vec4<T>::load(y + off + i, yy[k]);
+        if (accumulate) Vec4<float>::load(dx + off + i, o0[k]);
+        else o0[k][0] = o0[k][1] = o0[k][2] = o0[k][3] = 0.f;
         dot += g[k][0] * yy[k][0] + g[k][1] * yy[k][1] + g[k][2] * yy[k][2] + g[k][3] * yy[k][3];
       }
     }
-    const float mean = wave_sum(dot) / d;
     const float rs = r[row];
+    const float mean = wave_sum(dot) / d;
 #pragma unroll
     for (int k = 0; k < kMaxVec; ++k) {
       const int i = (lane + k * 64) * 4;
       if (i < d) {
-        float o[4];
-        if (accumulate) Vec4<float>::load(dx + off + i, o);
-        else o[0] = o[1] = o[2] = o[3] = 0.f;
+        float o[4] = {o0[k][0], o0[k][1], o0[k][2], o0[k][3]};
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] += rs * (g[k][e] - yy[k][e] * mean);
         Vec4<float>::store(dx + off + i, o);
