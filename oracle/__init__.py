@@ -24,9 +24,18 @@ Sources (web pages on nanochat; cited by title and section):
 Where the pages are silent, the reading taken is stated in the function that
 applies it.  Pins: every function here is checked by ``tests/test_oracle_*.py``
 against closed forms, invariants, textbook routines (SVD, polar
-decomposition) and central finite differences.  Parity unpinned: the absolute
-loss and gradient values of the d12..d26 shapes (the pages print none); they
-are covered only by the structural pins above.
+decomposition) and central finite differences.  Parity unpinned (no value
+printed by the pages and no closed form; covered only by the structural pins
+above and by the GPU-against-oracle tests):
+* the absolute loss and gradient values of the d12..d26 shapes;
+* Newton-Schulz coefficient rows three to five of the Polar Express schedule
+  (an input here, like a learning rate; rows one and two are pinned to the
+  printed ones, the later rows follow the same construction);
+* ``optim.normuon_update``: the reading of the NorMuon fragment (per-output-row
+  second moment, norm-preserving rescale) is checked against its own
+  invariants, not against values from the pages;
+* ``fp8``: the e5m2 format for gradients and which products run in fp8 are
+  readings; the codecs themselves are pinned against the format definitions.
 """
 
 from .model import (  # noqa: F401
