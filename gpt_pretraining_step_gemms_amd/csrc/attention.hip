@@ -176,11 +176,17 @@ constexpr int kSwFwdK = 1, kSwFwdV = 2, kSwDqK = 0, kSwDqV = 0, kSwDkv = 0;
 // one 128-query block qb of head bh; st0 / st1: K | V stages of 2 x 64 x 128
 // kAmax: also return the largest |o| this lane stored (before rounding to
 // bf16); a separate instantiation keeps the plain kernel as it was.
-template <bool kAmax>
+// kFixed: q and k rows are RMS-normalised (the model's QK-norm; rotary
+// rotations keep the norm), so every score satisfies |q.k| <= 128 (1 + 2^-9)^2
+// and its log2-domain value s * scale_log2 stays below mfix = 129 scale_log2.
+// The softmax then uses the fixed offset mfix for every query: no running
+// max, no rescale, and weights 2^(x - mfix) <= 1 (fp32 and bf16 keep their
+// relative precision at any such magnitude).
+template <bool kAmax, bool kFixed>
 NC_DEV float attn_fwd_block(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, bf16* __restrict__ o, int64_t ldo, float* __restrict__ lse, int T, int H,
-    int G, int win, float scale_log2, int qb, int bh, bf16* st0, bf16* st1) {
+    int G, int win, float scale_log2, float mfix, int qb, int bh, bf16* st0, bf16* st1) {
   constexpr int KT = 64 * 128;                    // one 64 x 128 tile
   const int b = bh / H, h = bh % H;
   const int64_t base = (int64_t)b * T * ld + h * 128;
@@ -206,7 +212,7 @@ NC_DEV float attn_fwd_block(
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
-  float m = -INFINITY, l = 0.f;
+  float m = kFixed ? mfix : -INFINITY, l = 0.f;
 
   // key tiles from the block's first window start to the diagonal
   const int n_kv = 2 * qb + 2;
@@ -240,7 +246,6 @@ NC_DEV float attn_fwd_block(
     // then see no key at all in a tile; its running max stays -inf and the
     // weights below use a finite stand-in so that they come out 0, not NaN.
     const bool need_mask = kv * 64 + 63 > q0w || kv * 64 < q0w + 31 - win;
-    float mt = -INFINITY;
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -250,24 +255,27 @@ NC_DEV float attn_fwd_block(
           if (key > myq || key < myq - win) sacc[kb][e] = -INFINITY;
         }
     }
+    if constexpr (!kFixed) {
+      float mt = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[kb][e]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * scale_log2;
-    const bool move = mt > m + 8.f;
-    if (__builtin_amdgcn_ballot_w64(move)) {
-      const float alpha = move ? fast_exp2(m - mt) : 1.f;
-      if (move) m = mt;
-      l *= alpha;
+        for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[kb][e]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * scale_log2;
+      const bool move = mt > m + 8.f;
+      if (__builtin_amdgcn_ballot_w64(move)) {
+        const float alpha = move ? fast_exp2(m - mt) : 1.f;
+        if (move) m = mt;
+        l *= alpha;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+          for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+      }
     }
     float sv[2][16];
     float ls = 0.f;
-    const float mf = fmaxf(m, -3.0e38f);
+    const float mf = kFixed ? mfix : fmaxf(m, -3.0e38f);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -784,20 +792,20 @@ NC_DEV void attn_amax_out(float amx, float* amax_part, bf16* st0) {
   if (threadIdx.x == 0) amax_part[blockIdx.x] = bf16_abs(amx);
 }
 
-template <bool kAmax>
+template <bool kAmax, bool kFixed>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, bf16* __restrict__ o, int64_t ldo, float* __restrict__ lse, int T, int H,
-    int G, int win, float scale_log2, float* __restrict__ amax_part) {
+    int G, int win, float scale_log2, float mfix, float* __restrict__ amax_part) {
   __shared__ __attribute__((aligned(1024))) bf16 st0[2 * 64 * 128];   // K | V of even tiles
   __shared__ __attribute__((aligned(1024))) bf16 st1[2 * 64 * 128];   // K | V of odd tiles
   const BlockJob jb = block_job(T / 128, win >= T, true);
-  float amx = attn_fwd_block<kAmax>(q, k, v, ld, o, ldo, lse, T, H, G, win, scale_log2, jb.first,
-                             jb.bh, st0, st1);
+  float amx = attn_fwd_block<kAmax, kFixed>(q, k, v, ld, o, ldo, lse, T, H, G, win, scale_log2,
+                                            mfix, jb.first, jb.bh, st0, st1);
   if (jb.second >= 0) {
     __syncthreads();                               // the first block's O staging is read
-    amx = max_nan(amx, attn_fwd_block<kAmax>(q, k, v, ld, o, ldo, lse, T, H, G, win, scale_log2,
-                                      jb.second, jb.bh, st0, st1));
+    amx = max_nan(amx, attn_fwd_block<kAmax, kFixed>(q, k, v, ld, o, ldo, lse, T, H, G, win,
+                                                     scale_log2, mfix, jb.second, jb.bh, st0, st1));
   }
   attn_amax_out(amx, amax_part, st0);
 }
@@ -961,17 +969,18 @@ int nc_attn_amax_parts(int B, int T, int H, int Hkv, int window, int backward) {
 
 hipError_t nc_attn_fwd(int dtype, const void* q, const void* k, const void* v, int64_t ld,
                        void* o, int64_t ldo, float* lse, int B, int T, int H, int Hkv, int window,
-                       hipStream_t st, float* amax_part) {
+                       hipStream_t st, float* amax_part, int qk_normed) {
   const float scale = 1.0f / sqrtf(128.f);
   const int win = window < 0 || window > T ? T : window;
   if (Hkv < 1 || H % Hkv) return hipErrorInvalidValue;
   const int G = H / Hkv;
   if (dtype) {
     if (T % 128) return hipErrorInvalidValue;
-    auto fwd_kernel = amax_part ? attn_fwd_kernel<true> : attn_fwd_kernel<false>;
+    auto fwd_kernel = qk_normed ? (amax_part ? attn_fwd_kernel<true, true> : attn_fwd_kernel<false, true>)
+                                : (amax_part ? attn_fwd_kernel<true, false> : attn_fwd_kernel<false, false>);
     fwd_kernel<<<B * H * attn_jobs_per_head(T, win), 256, 0, st>>>(
         (const bf16*)q, (const bf16*)k, (const bf16*)v, ld, (bf16*)o, ldo, lse, T, H, G, win,
-        scale * kLog2e, amax_part);
+        scale * kLog2e, 129.f * scale * kLog2e, amax_part);
   } else {
     attn_fwd_f32_kernel<<<ceil_div(B * H * T, 4), 256, 0, st>>>(
         (const float*)q, (const float*)k, (const float*)v, ld, (float*)o, ldo, lse, B, T, H, G,

@@ -95,9 +95,11 @@ hipError_t nc_qk_norm_rope_bwd(int dtype, void* dqkv, const void* qkv, const flo
 // ---- attention on token-major q/k/v (row stride ld_qkv), head dim 128; query t
 // sees keys max(0, t - window) .. t (window < 0: keys 0 .. t); H query heads,
 // Hkv key/value heads (H % Hkv == 0), query head h reads key/value head h / (H / Hkv)
+// qk_normed: q and k rows are RMS-normalised (|q.k| <= 128), so the bf16
+// kernel may use a fixed softmax offset instead of a running max
 hipError_t nc_attn_fwd(int dtype, const void* q, const void* k, const void* v, int64_t ld_qkv,
                        void* o, int64_t ld_o, float* lse, int B, int T, int H, int Hkv,
-                       int window, hipStream_t st, float* amax_part = nullptr);
+                       int window, hipStream_t st, float* amax_part = nullptr, int qk_normed = 0);
 // D[b,h,t] = sum_d dO*O
 hipError_t nc_attn_bwd_pre(int dtype, const void* o, const void* dO, int64_t ld_o, float* D,
                            int B, int T, int H, hipStream_t st);

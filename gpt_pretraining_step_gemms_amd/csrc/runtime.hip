@@ -944,7 +944,7 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
     NC_TRY(nc_qk_norm_rope_fwd(dt, qkv, A<float>(ctx, la.rqk), tab, N, T, H, Hkv, eps, st),
            "qknorm");
     NC_TRY(nc_attn_fwd(dt, qkv, qkv + d * es, qkv + (d + dk) * es, Wd, aa + la.o, d,
-                       A<float>(ctx, la.lse), B, T, H, Hkv, ctx->windows[l], st, parts),
+                       A<float>(ctx, la.lse), B, T, H, Hkv, ctx->windows[l], st, parts, 1),
            "attn fwd");
     NC_GEMM(ctx->fp8 ? gemm_fp8_fwd(ctx, aa + la.o, d, wcodes(ctx, l, 1, false), d, x, d, N, kEpiAccF32,
                                     xt_of(l, 1), xs_of(l, 1), parts,
