@@ -18,6 +18,17 @@ template <> struct Vec4<float> {
   NC_DEV static void store(float* p, const float o[4]) {
     *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
   }
+  // single-use streams (non-temporal)
+  NC_DEV static void load_nt(const float* p, float o[4]) {
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    const f4 v = __builtin_nontemporal_load(reinterpret_cast<const f4*>(p));
+    o[0] = v[0]; o[1] = v[1]; o[2] = v[2]; o[3] = v[3];
+  }
+  NC_DEV static void store_nt(float* p, const float o[4]) {
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    const f4 v = {o[0], o[1], o[2], o[3]};
+    __builtin_nontemporal_store(v, reinterpret_cast<f4*>(p));
+  }
 };
 template <> struct Vec4<bf16> {
   NC_DEV static void load(const bf16* p, float o[4]) {
@@ -28,6 +39,11 @@ template <> struct Vec4<bf16> {
     bf16x4 v;
     v[0] = (bf16)o[0]; v[1] = (bf16)o[1]; v[2] = (bf16)o[2]; v[3] = (bf16)o[3];
     *reinterpret_cast<bf16x4*>(p) = v;
+  }
+  NC_DEV static void store_nt(bf16* p, const float o[4]) {
+    bf16x4 v;
+    v[0] = (bf16)o[0]; v[1] = (bf16)o[1]; v[2] = (bf16)o[2]; v[3] = (bf16)o[3];
+    __builtin_nontemporal_store(v, reinterpret_cast<bf16x4*>(p));
   }
 };
 
@@ -474,13 +490,20 @@ __global__ __launch_bounds__(NTH) void cross_entropy_kernel(
   __shared__ float red[NTH / 64];
   const int row = blockIdx.x;
   const float* zr = z + (int64_t)row * V;
+  // the target and its logit are loaded first, so that their round trips
+  // overlap the row's loads instead of following the two reductions
+  // (a target outside [0, V): NaN loss and dz for the row, bit 1 of *flag)
+  const int yraw = tgt[row];
+  const bool ok = yraw >= 0 && yraw < V;
+  const int y = ok ? yraw : -1;
+  const float zy = threadIdx.x == 0 && ok ? zr[y] : 0.f;
   float v[KV][4];
   float m = -INFINITY;
 #pragma unroll
   for (int k = 0; k < KV; ++k) {
     const int i = threadIdx.x * 4 + k * 4 * NTH;
     if (i < V) {
-      Vec4<float>::load(zr + i, v[k]);
+      Vec4<float>::load_nt(zr + i, v[k]);
       m = fmaxf(m, fmaxf(fmaxf(v[k][0], v[k][1]), fmaxf(v[k][2], v[k][3])));
     }
   }
@@ -499,12 +522,8 @@ __global__ __launch_bounds__(NTH) void cross_entropy_kernel(
     }
   }
   const float S = block_sum(s, red);
-  // a target outside [0, V): NaN loss and dz for the row, bit 1 of *flag
-  const int yraw = tgt[row];
-  const bool ok = yraw >= 0 && yraw < V;
-  const int y = ok ? yraw : -1;
   if (threadIdx.x == 0) {
-    loss_rows[row] = ok ? M + logf(S) - zr[y] : NAN;
+    loss_rows[row] = ok ? M + logf(S) - zy : NAN;
     if (!ok) atomicOr(flag, 2);
   }
   const float inv = ok ? 1.f / S : NAN;
@@ -516,7 +535,7 @@ __global__ __launch_bounds__(NTH) void cross_entropy_kernel(
       float o[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = scale * (v[k][e] * inv - (i + e == y ? 1.f : 0.f));
-      Vec4<T>::store(dr + i, o);
+      Vec4<T>::store_nt(dr + i, o);
     }
   }
 }
@@ -791,13 +810,24 @@ __global__ __launch_bounds__(256) void amax_partial_kernel(const T* __restrict__
 
 // amax_scale[0] = amax, amax_scale[1] = fmax / amax (1 when amax is 0); fmax is
 // the format's largest finite value (448 for e4m3, 57344 for e5m2)
-__global__ __launch_bounds__(256) void amax_final_kernel(const float* __restrict__ partial,
-                                                         int parts, float fmax,
-                                                         float* __restrict__ amax_scale) {
-  __shared__ float red[4];
-  float m = 0.f;
-  for (int i = threadIdx.x; i < parts; i += 256) m = max_nan(m, partial[i]);
-  m = block_max_nan(m, red);
+// One block of 1,024 threads; each thread keeps four independent maxima so
+// that its loads are issued back to back (a single running max over a
+// strided loop issued one load per iteration: 14.6 us per call for 16,384
+// partials).  NaN-propagating max is order independent.
+__global__ __launch_bounds__(1024) void amax_final_kernel(const float* __restrict__ partial,
+                                                          int parts, float fmax,
+                                                          float* __restrict__ amax_scale) {
+  __shared__ float red[16];
+  float m0 = 0.f, m1 = 0.f, m2 = 0.f, m3 = 0.f;
+  int i = threadIdx.x;
+  for (; i + 3 * 1024 < parts; i += 4 * 1024) {
+    m0 = max_nan(m0, partial[i]);
+    m1 = max_nan(m1, partial[i + 1024]);
+    m2 = max_nan(m2, partial[i + 2048]);
+    m3 = max_nan(m3, partial[i + 3072]);
+  }
+  for (; i < parts; i += 1024) m0 = max_nan(m0, partial[i]);
+  float m = block_max_nan(max_nan(max_nan(m0, m1), max_nan(m2, m3)), red);
   if (threadIdx.x == 0) {
     amax_scale[0] = m;
     amax_scale[1] = m != m ? m : (m > 0.f ? fmax / m : 1.f);
@@ -1290,7 +1320,7 @@ hipError_t nc_fp8_quantize(int dtype, int fmt, const void* x, int64_t rows, int6
     amax_partial_kernel<bf16><<<parts, 256, 0, st>>>((const bf16*)x, n, partial);
   else
     amax_partial_kernel<float><<<parts, 256, 0, st>>>((const float*)x, n, partial);
-  amax_final_kernel<<<1, 256, 0, st>>>(partial, parts, fmt ? 57344.f : 448.f, amax_scale);
+  amax_final_kernel<<<1, 1024, 0, st>>>(partial, parts, fmt ? 57344.f : 448.f, amax_scale);
   return fp8_codes(dtype, fmt, x, rows, cols, amax_scale, q, qt, st);
 }
 
@@ -1303,7 +1333,7 @@ hipError_t nc_fp8_quantize_parts(int fmt, const void* x, int64_t rows, int64_t c
   if (qt && !(rows % 64 == 0 && cols % 64 == 0 && rows <= 0x7fffffff && cols <= 0x7fffffff &&
               al(x, 16) && al(q, 8) && al(qt, 16)))
     return hipErrorInvalidValue;
-  amax_final_kernel<<<1, 256, 0, st>>>(amax_parts, n_parts, fmt ? 57344.f : 448.f, amax_scale);
+  amax_final_kernel<<<1, 1024, 0, st>>>(amax_parts, n_parts, fmt ? 57344.f : 448.f, amax_scale);
   return fp8_codes(1, fmt, x, rows, cols, amax_scale, q, qt, st);
 }
 
