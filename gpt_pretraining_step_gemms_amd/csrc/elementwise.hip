@@ -35,6 +35,10 @@ template <> struct Vec4<bf16> {
     const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
     o[0] = (float)v[0]; o[1] = (float)v[1]; o[2] = (float)v[2]; o[3] = (float)v[3];
   }
+  NC_DEV static void load_nt(const bf16* p, float o[4]) {
+    const bf16x4 v = __builtin_nontemporal_load(reinterpret_cast<const bf16x4*>(p));
+    o[0] = (float)v[0]; o[1] = (float)v[1]; o[2] = (float)v[2]; o[3] = (float)v[3];
+  }
   NC_DEV static void store(bf16* p, const float o[4]) {
     bf16x4 v;
     v[0] = (bf16)o[0]; v[1] = (bf16)o[1]; v[2] = (bf16)o[2]; v[3] = (bf16)o[3];
@@ -225,7 +229,7 @@ __global__ void rmsnorm_fwd_kernel(const float* __restrict__ x, T* __restrict__ 
     for (int k = 0; k < kMaxVec; ++k) {
       const int i = (lane + k * 64) * 4;
       if (i < d) {
-        Vec4<float>::load(xr + i, v[k]);
+        Vec4<float>::load_nt(xr + i, v[k]);
         ss += v[k][0] * v[k][0] + v[k][1] * v[k][1] + v[k][2] * v[k][2] + v[k][3] * v[k][3];
       }
     }
@@ -269,7 +273,7 @@ __global__ void rmsnorm_bwd_kernel(const TD* __restrict__ dy, const T* __restric
     for (int k = 0; k < kMaxVec; ++k) {
       const int i = (lane + k * 64) * 4;
       if (i < d) {
-        Vec4<TD>::load(dy + off + i, g[k]);
+        Vec4<TD>::load_nt(dy + off + i, g[k]);
         Vec4<T>::load(y + off + i, yy[k]);
         if (accumulate) Vec4<float>::load(dx + off + i, o0[k]);
         else o0[k][0] = o0[k][1] = o0[k][2] = o0[k][3] = 0.f;

@@ -445,9 +445,13 @@ __global__ __launch_bounds__(256) void splitk_reduce_rows_kernel(GemmParams p) {
   const int64_t total = (int64_t)p.M * p.N * p.batch;
   const float* w = p.workspace + (int64_t)row * p.N;
   float* c = static_cast<float*>(p.C) + b * p.sC + (int64_t)m * p.ldc;
+  // (the slabs are read once: non-temporal loads, unrolled so that several
+  // are in flight; the sum keeps the fixed split order)
   for (int n = threadIdx.x * 4; n < p.N; n += blockDim.x * 4) {
-    f32x4 acc = *reinterpret_cast<const f32x4*>(w + n);
-    for (int k = 1; k < p.splits; ++k) acc += *reinterpret_cast<const f32x4*>(w + k * total + n);
+    f32x4 acc = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(w + n));
+#pragma unroll 4
+    for (int k = 1; k < p.splits; ++k)
+      acc += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(w + k * total + n));
     f32x4* out = reinterpret_cast<f32x4*>(c + n);
     if (p.epi == kEpiAccF32) *out = *out + acc; else *out = acc;
   }
