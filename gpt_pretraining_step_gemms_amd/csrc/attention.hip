@@ -14,8 +14,9 @@
 //    index is permuted identically on both operands).
 //  * backward: two deterministic kernels, no atomics.  dK/dV: a workgroup owns
 //    128 keys and walks the query tiles from the diagonal down, recomputing
-//    P = exp(S - lse) and dS = P (dP - D).  dQ: a workgroup owns 128 queries
-//    and walks the key tiles up to the diagonal.
+//    P = exp(S - lse) and dS = P (dP - D), with two waves per 32-key slice
+//    (one forms S, P and dV, the other dP, dS and dK one tile later).  dQ: a
+//    workgroup owns 128 queries and walks the key tiles up to the diagonal.
 //  * Tiles reach LDS in their token-major layout by direct loads; the operands
 //    needed transposed (V^T, Q^T, dO^T, K^T) are read with ds_read_b64_tr_b16,
 //    which transposes 16-bit values in the LDS read.
@@ -40,6 +41,12 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 // accumulator registers hf*8 .. hf*8+7 of a 32x32 tile, as an MFMA operand
 NC_DEV bf16x8 pack_half(const float* v, int hf) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (bf16)v[hf * 8 + e];
+  return r;
+}
+NC_DEV bf16x8 pack_half(const f32x16& v, int hf) {
   bf16x8 r;
 #pragma unroll
   for (int e = 0; e < 8; ++e) r[e] = (bf16)v[hf * 8 + e];
@@ -109,12 +116,16 @@ NC_DEV void fa_barrier() { asm volatile("s_barrier" ::: "memory"); }
 // second half needs its own address, and the row reads need twice the
 // address variants: in dK/dV it measured level (the saved LDS cycles paid for
 // by the extra registers and address arithmetic), and dQ spilled.
+//   3: 4 (r & 3) + ((r >> 2) & 3), period 16: one pass for either read, but
+//      rows r + 8 take another swizzle, so the transposed read's second half
+//      needs its own addresses (used where the registers allow it).
 template <int SW>
 NC_DEV int fa_swz(int r) {
-  static_assert(SW >= 0 && SW <= 2, "swizzle kinds 0, 1, 2");
+  static_assert(SW >= 0 && SW <= 3, "swizzle kinds 0, 1, 2, 3");
   if constexpr (SW == 0) return (2 * (r & 3)) | ((r >> 2) & 1);
   else if constexpr (SW == 1) return r & 15;
-  else return 4 * (r & 3) + ((r >> 2) & 1);
+  else if constexpr (SW == 2) return 4 * (r & 3) + ((r >> 2) & 1);
+  else return 4 * (r & 3) + ((r >> 2) & 3);
 }
 
 // this wave's share (4 x 1 KB) of a 64-row x 128 token-major tile into LDS
@@ -158,7 +169,8 @@ NC_DEV bf16x8 fa_frag_vt(const bf16* tile, int row_base, int col_base, int lane)
   const int r = row_base + (t >> 2);
   const int col = col_base + 4 * (t & 3);
   const bf16* p0 = tile + r * 128 + (((col >> 3) ^ fa_swz<SW>(r)) << 3) + (col & 7);
-  const bf16* p1 = p0 + 8 * 128;                 // rows + 8: same swizzle
+  const bf16* p1 = SW == 3 ? tile + (r + 8) * 128 + (((col >> 3) ^ fa_swz<SW>(r + 8)) << 3) + (col & 7)
+                           : p0 + 8 * 128;       // rows + 8: the same swizzle below kind 3
   const fa_bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) fa_bf16x4*)p0);
   const fa_bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) fa_bf16x4*)p1);
   bf16x8 v;
@@ -170,8 +182,9 @@ NC_DEV bf16x8 fa_frag_vt(const bf16* tile, int row_base, int col_base, int lane)
 // Swizzle per tile (each kernel stages its own): the forward's K tile is only
 // read by rows and its V tile only transposed, so both take one pass (the
 // forward measured 1.5-2 % faster than with kind 0, outputs bitwise equal);
-// dQ reads K both ways, and dK/dV reads Q and dO both ways (kind 0).
-constexpr int kSwFwdK = 1, kSwFwdV = 2, kSwDqK = 0, kSwDqV = 0, kSwDkv = 0;
+// dQ reads K both ways (kind 0), and dK/dV reads Q and dO both ways (kind 3:
+// its two-role layout leaves the registers for the second half's addresses).
+constexpr int kSwFwdK = 1, kSwFwdV = 2, kSwDqK = 0, kSwDqV = 0, kSwDkv = 3;
 
 // one 128-query block qb of head bh; st0 / st1: K | V stages of 2 x 64 x 128
 // kAmax: also return the largest |o| this lane stored (before rounding to
@@ -459,162 +472,237 @@ NC_DEV float attn_store_grad(const f32x16 (&acc)[4], float scale, bf16* __restri
 }
 
 // ============================================================ dK / dV
-// A workgroup owns 128 keys (4 waves x 32; K and V rows of each wave's keys
-// stay in registers as the B operands) and walks the 64-query tiles from the
-// diagonal down.  Q, dO and the tile's log-sum-exp and D reach LDS by direct
-// loads, double-buffered; Q^T and dO^T fragments come from transpose reads.
-constexpr int kDkvStage = 2 * 64 * 128 + 256;     // Q | dO | -lse log2(e) [64], D [64] (fp32)
+// A workgroup owns 128 keys of one key/value head (four 32-key slices) and
+// walks the 64-query tiles from the diagonal down, with eight waves, two per
+// slice.  Wave pr (0..3) holds the slice's K rows and dV accumulators: for
+// query tile i it forms S = Q K^T, the weights P = exp(S - lse) (left in LDS
+// for its partner) and dV += P^T dO.  Wave pr + 4 holds the V rows and dK
+// accumulators and runs one tile behind: in the same round it forms
+// dS = P (dP - D) and dK += dS^T Q for tile i - 1 (its dP kept in registers
+// from the round before, P read from LDS), then dP = dO V^T for tile i.
+//  * Holding one 32-key operand and one accumulator set each, a wave needs at
+//    most 256 registers, so two waves share a SIMD, and with one barrier per
+//    round one wave's exponentials or dS arithmetic run under the other's
+//    MFMAs.  (One wave per slice holding both, at one wave per SIMD, took
+//    25 % longer; the two roles with a barrier between P and its use, 13 %.)
+//  * Q tiles stay for three rounds (the lagging wave reads tile i - 1 while
+//    tile i + 1 arrives), dO tiles and P (fp32, as the first wave computed
+//    it) for two.  Q, dO, -lse log2(e) and D arrive by direct loads.
+//  * Grouped heads: the walk runs over the query tiles of each of the G query
+//    heads of the key/value head in turn, into the same accumulators.
+constexpr int kDkvTile = 64 * 128 * 2;                    // bytes of one Q or dO tile
+constexpr int kDkvQ = 0, kDkvDO = 3 * kDkvTile;         // Q tiles x 3, dO tiles x 2
+constexpr int kDkvStats = kDkvDO + 2 * kDkvTile;        // x 3: -lse log2(e) [64], D [64] (fp32)
+constexpr int kDkvPex = kDkvStats + 3 * 512;             // x 2: P of 4 slices x 32 keys x 64 queries
+constexpr int kDkvPexBytes = 4 * 64 * 32 * 4;
+constexpr int kDkvSmem = kDkvPex + 2 * kDkvPexBytes;    // 148,992 bytes
+static_assert(kDkvSmem <= 160 * 1024, "LDS");
+static_assert(8 * 16 * 132 * 4 <= kDkvSmem, "epilogue staging");
 
-// one 128-key block kblk of key/value head bhk; st0 / st1: stages of kDkvStage
-// elements.  kGrouped: G > 1 query heads per key/value head, walked in turn (a
-// separate instantiation keeps the plain path's registers as they were).
+// s_barrier once this wave's tile loads and LDS writes have landed
+NC_DEV void fa_wait_all_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <bool kGrouped, bool kAmax>
 NC_DEV float attn_bwd_dkv_block(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, const bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ nl2,
     const float* __restrict__ Dv, bf16* __restrict__ dk, bf16* __restrict__ dv, int64_t ldd,
-    int T, int H, int G, int win, float scale_log2, float scale, int kblk, int bhk, bf16* st0,
-    bf16* st1, const QkNorm& nq) {
-  constexpr int KT = 64 * 128;
+    int T, int H, int G, int win, float scale_log2, float scale, int kblk, int bhk,
+    char* smem, const QkNorm& nq) {
   const int Hkv = kGrouped ? H / G : H;
   const int b = bhk / Hkv, hk = bhk % Hkv;
   const int64_t kvbase = (int64_t)b * T * ld + hk * 128;
-  // the query head being walked: hk itself, or each head of the group in turn
-  const int h0 = kGrouped ? hk * G : hk;
-  int64_t base = (int64_t)b * T * ld + h0 * 128;
-  int64_t obase = (int64_t)b * T * ldo + h0 * 128;
-  const float* lse_bh = nl2 + ((int64_t)b * H + h0) * T;
-  const float* D_bh = Dv + ((int64_t)b * H + h0) * T;
+  const int h0 = kGrouped ? hk * G : hk;        // the group's first query head
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool wP = wave < 4;                       // S, P, dV (else dP, dS, dK one tile behind)
+  const int pr = wave & 3;
   const int half = lane >> 5, l32 = lane & 31;
-  const int k0w = kblk * 128 + wave * 32;
+  const int k0w = kblk * 128 + pr * 32;
   const int mykey = k0w + l32;
+  auto qtile = [&](int i) { return reinterpret_cast<bf16*>(smem + kDkvQ + (i % 3) * kDkvTile); };
+  auto dotile = [&](int i) { return reinterpret_cast<bf16*>(smem + kDkvDO + (i & 1) * kDkvTile); };
+  auto stats = [&](int i) { return reinterpret_cast<float*>(smem + kDkvStats + (i % 3) * 512); };
+  auto pex = [&](int i) {
+    return reinterpret_cast<float*>(smem + kDkvPex + (i & 1) * kDkvPexBytes) + pr * (64 * 32);
+  };
 
-  bf16x8 kf[8], vf[8];
+  bf16x8 kv[8];                                   // K rows (wP) or V rows
+  const bf16* kvsrc = (wP ? k : v) + kvbase + (int64_t)mykey * ld + half * 8;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    kf[s] = *reinterpret_cast<const bf16x8*>(k + kvbase + (int64_t)mykey * ld + s * 16 + half * 8);
-    vf[s] = *reinterpret_cast<const bf16x8*>(v + kvbase + (int64_t)mykey * ld + s * 16 + half * 8);
-  }
+  for (int s = 0; s < 8; ++s) kv[s] = *reinterpret_cast<const bf16x8*>(kvsrc + s * 16);
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    settle(kf[s]);
-    settle(vf[s]);
-  }
-  f32x16 dkacc[4], dvacc[4];
+  for (int s = 0; s < 8; ++s) settle(kv[s]);
+  f32x16 acc[4];                                  // dV (wP) or dK
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) { dkacc[i][e] = 0.f; dvacc[i][e] = 0.f; }
+    for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+  f32x16 sacc[2];                                 // S (wP), or dP of the previous tile
 
   // query tiles from the diagonal to the last query whose window holds a key of the block
   const int qt0 = kblk * 2, nqt = min(T / 64, (kblk * 128 + 127 + win) / 64 + 1);
-  auto issue = [&](int qt, bf16* st) {
-    fa_issue_rows<kSwDkv>(q + base, ld, qt * 64, st, wave, lane);
-    fa_issue_rows<kSwDkv>(dO + obase, ldo, qt * 64, st + KT, wave, lane);
-    if (wave == 0) {
-      float* stats = reinterpret_cast<float*>(st + 2 * KT);
-      fa_dma4(lse_bh + qt * 64 + lane, stats);
-      fa_dma4(D_bh + qt * 64 + lane, stats + 64);
-    }
+  // The walk: tile i is query tile qt0 + i % n of query head h0 + i / n (one
+  // head unless grouped), so the lagging wave's round runs across heads too.
+  const int n = nqt - qt0, ntiles = kGrouped ? G * n : n;
+  auto tile_qt = [&](int i) { return kGrouped ? qt0 + i % n : qt0 + i; };
+  // queries all before this slice's keys, or all past these keys' windows
+  auto active = [&](int qt) { return qt * 64 + 63 >= k0w && qt * 64 <= k0w + 31 + win; };
+  auto issue = [&](int i) {
+    const int h = kGrouped ? h0 + i / n : h0, qt = tile_qt(i);
+    if (wP) fa_issue_rows<kSwDkv>(q + (int64_t)b * T * ld + h * 128, ld, qt * 64, qtile(i), pr, lane);
+    else fa_issue_rows<kSwDkv>(dO + (int64_t)b * T * ldo + h * 128, ldo, qt * 64, dotile(i), pr, lane);
+    const int64_t st = ((int64_t)b * H + h) * T + qt * 64 + lane;
+    if (wave == 0) fa_dma4(nl2 + st, stats(i));
+    if (wave == 4) fa_dma4(Dv + st, stats(i) + 64);
   };
-  auto step = [&](int qt, const bf16* cur, bf16* next) {
-    fa_wait_vmcnt<0>();
-    fa_barrier();
-    if (qt + 1 < nqt) issue(qt + 1, next);
-    if (qt * 64 + 63 < k0w) return;               // queries all before this wave's keys
-    if (qt * 64 > k0w + 31 + win) return;         // queries all past these keys' windows
-    const bf16* Qs = cur;
-    const bf16* dOs = cur + KT;
-    const float* lse_s = reinterpret_cast<const float*>(cur + 2 * KT);
-    const float* D_s = lse_s + 64;
-    f32x16 sacc[2], pacc[2];
+  // Per-lane byte offsets of the fragment reads inside a tile (swizzle kind
+  // 3), made once and kept in registers: a tile's reads then cost one add per
+  // offset for the tile's position in the ring, the rest are immediates.
+  //  * rows (ds_read_b128): row l32 (+ 32 qb), 16-byte chunk 2 s + half;
+  //  * transposed (ds_read_b64_tr_b16): rows 4 half + (t >> 2) (+ 8 for the
+  //    second half; + 16 (j & 1) + 32 (j >> 1)), columns 32 db + 16 ((lane >> 4) & 1) + 4 (t & 3).
+  unsigned roff[8], toff[4][2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+  for (int s = 0; s < 8; ++s) {
+    roff[s] = l32 * 256 + (((s * 2 + half) ^ fa_swz<kSwDkv>(l32)) << 4);
+    asm volatile("" : "+v"(roff[s]));
+  }
+  {
+    const int t = lane & 15;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) { sacc[qb][e] = 0.f; pacc[qb][e] = 0.f; }
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        sacc[qb] = mfma(fa_frag_k<kSwDkv>(Qs, qb * 32 + l32, s * 2 + half), kf[s], sacc[qb]);
-        pacc[qb] = mfma(fa_frag_k<kSwDkv>(dOs, qb * 32 + l32, s * 2 + half), vf[s], pacc[qb]);
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int r = half * 4 + (t >> 2) + 8 * h2;
+        const int col = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (t & 3);
+        toff[db][h2] = r * 256 + (((col >> 3) ^ fa_swz<kSwDkv>(r)) << 4) + (col & 7) * 2;
+        asm volatile("" : "+v"(toff[db][h2]));
       }
-    }
-    // masks (only tiles crossing an edge of the band): queries before the
-    // key, and queries whose window ends before it
-    if (qt * 64 < k0w + 31 || qt * 64 + 63 > k0w + win) {
+  }
+  // rows x kv[] products of a tile: S from Q rows (wP) or dP from dO rows
+  auto scores = [&](const bf16* X) {
+    const char* xb = reinterpret_cast<const char*>(X);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[qb][e] = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const char* rp = xb + roff[s];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int qq = qt * 64 + qb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
-          if (qq < mykey || qq > mykey + win) sacc[qb][e] = -INFINITY;
-        }
+        sacc[qb] = mfma(*reinterpret_cast<const bf16x8*>(rp + qb * 8192), kv[s], sacc[qb]);
     }
-    float p[2][16], ds[2][16];
+  };
+  // acc += w^T Y with w the 32 keys x 64 queries in sacc, Y read transposed
+  auto accumulate = [&](const bf16* Y) {
+    const char* yb = reinterpret_cast<const char*>(Y);
+    const char* tp[4][2];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) tp[db][h2] = yb + toff[db][h2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 op = pack_half(sacc[j >> 1], j & 1);
+      const int jo = (j >> 1) * 8192 + (j & 1) * 4096;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        typedef __attribute__((address_space(3))) fa_bf16x4 lds4;
+        const fa_bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4*)(tp[db][0] + jo));
+        const fa_bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4*)(tp[db][1] + jo));
+        bf16x8 f;
+        f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
+        f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
+        acc[db] = mfma(op, f, acc[db]);
+      }
+    }
+  };
+  // lagging wave, tile i: dS = P (dP - D) in sacc, then dK += dS^T Q
+  auto dk_round = [&](int i) {
+    const float* P = pex(i);
+    const float* D_s = stats(i) + 64;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int ql = qb * 32 + g * 8 + half * 4;
-        const float4 l4 = *reinterpret_cast<const float4*>(lse_s + ql);
-        const float4 d4 = *reinterpret_cast<const float4*>(D_s + ql);
-        const float la[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float4 p4 = *reinterpret_cast<const float4*>(P + ((qb * 4 + g) * 64 + lane) * 4);
+        const float4 d4 = *reinterpret_cast<const float4*>(D_s + qb * 32 + g * 8 + half * 4);
+        const float pa[4] = {p4.x, p4.y, p4.z, p4.w};
         const float da[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int e = g * 4 + i;
-          const float pv = fast_exp2(fmaf(sacc[qb][e], scale_log2, la[i]));
-          p[qb][e] = pv;
-          ds[qb][e] = pv * (pacc[qb][e] - da[i]);
-        }
+        for (int e = 0; e < 4; ++e) sacc[qb][g * 4 + e] = pa[e] * (sacc[qb][g * 4 + e] - da[e]);
       }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bf16x8 pa = pack_half(p[j >> 1], j & 1);
-      const bf16x8 dsa = pack_half(ds[j >> 1], j & 1);
-      const int row_base = (j >> 1) * 32 + (j & 1) * 16 + half * 4;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int cb = db * 32 + 16 * ((lane >> 4) & 1);
-        dvacc[db] = mfma(pa, fa_frag_vt<kSwDkv>(dOs, row_base, cb, lane), dvacc[db]);
-        dkacc[db] = mfma(dsa, fa_frag_vt<kSwDkv>(Qs, row_base, cb, lane), dkacc[db]);
-      }
-    }
+    accumulate(qtile(i));
   };
 
+  // The two roles walk the tiles in separate loops (each keeps its own
+  // registers) with the same barriers: one per tile and one after the last.
   auto walk = [&]() {
-    issue(qt0, st0);
-    for (int qt = qt0; qt < nqt; qt += 2) {
-      step(qt, st0, st1);
-      if (qt + 1 < nqt) step(qt + 1, st1, st0);
+    issue(0);
+    if (wP) {
+      for (int i = 0; i < ntiles; ++i) {
+        const int qt = tile_qt(i);
+        fa_wait_all_barrier();                     // tile i landed; P of tile i - 1 read
+        if (i + 1 < ntiles) issue(i + 1);
+        if (!active(qt)) continue;
+        scores(qtile(i));
+        // masks (only tiles crossing an edge of the band): queries before the
+        // key, and queries whose window ends before it
+        if (qt * 64 < k0w + 31 || qt * 64 + 63 > k0w + win) {
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int qq = qt * 64 + qb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+              if (qq < mykey || qq > mykey + win) sacc[qb][e] = -INFINITY;
+            }
+        }
+        const float* lse_s = stats(i);
+        float* P = pex(i);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float4 l4 = *reinterpret_cast<const float4*>(lse_s + qb * 32 + g * 8 + half * 4);
+            const float la[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              sacc[qb][g * 4 + e] = fast_exp2(fmaf(sacc[qb][g * 4 + e], scale_log2, la[e]));
+            const float4 p4 = make_float4(sacc[qb][g * 4], sacc[qb][g * 4 + 1],
+                                          sacc[qb][g * 4 + 2], sacc[qb][g * 4 + 3]);
+            *reinterpret_cast<float4*>(P + ((qb * 4 + g) * 64 + lane) * 4) = p4;
+          }
+        accumulate(dotile(i));
+      }
+      fa_wait_all_barrier();                       // P of the last tile written
+    } else {
+      bool prev = false;                           // sacc holds dP of tile i - 1
+      for (int i = 0; i < ntiles; ++i) {
+        fa_wait_all_barrier();
+        if (i + 1 < ntiles) issue(i + 1);
+        if (prev) dk_round(i - 1);
+        prev = active(tile_qt(i));
+        if (prev) scores(dotile(i));
+      }
+      fa_wait_all_barrier();
+      if (prev) dk_round(ntiles - 1);
     }
   };
-  if constexpr (kGrouped) {
-    for (int g = 0; g < G; ++g) {
-      if (g) {
-        const int h = h0 + g;
-        base = (int64_t)b * T * ld + h * 128;
-        obase = (int64_t)b * T * ldo + h * 128;
-        lse_bh = nl2 + ((int64_t)b * H + h) * T;
-        D_bh = Dv + ((int64_t)b * H + h) * T;
-        __syncthreads();                           // the previous head's last tile is read
-      }
-      walk();
-    }
-  } else {
-    walk();
-  }
+  walk();
 
   // C[key][d]: lane holds column d = db*32 + l32, rows key = 8*(e/4) + 4*half + e%4
   const int64_t row_out = ((int64_t)b * T + k0w) * ldd + hk * 128;
-  __syncthreads();                                 // every wave is done with the stages
-  float* stg = reinterpret_cast<float*>(wave < 2 ? st0 : st1) + (wave & 1) * 16 * 132;
-  const float amx = attn_store_grad<kAmax>(dvacc, 1.f, dv, ldd, row_out, nullptr, 0, 0, k0w, 0, T, 0,
-                                    QkNorm{nullptr, nullptr, 0}, stg, lane);
-  return max_nan(amx, attn_store_grad<kAmax>(dkacc, scale, dk, ldd, row_out, k, ld,
-                                      kvbase + (int64_t)k0w * ld, k0w, (int64_t)b * T + k0w, T,
-                                      H + hk, nq, stg, lane));
+  __syncthreads();                                 // every wave is done with the tiles
+  float* stg = reinterpret_cast<float*>(smem) + wave * 16 * 132;
+  if (wP)
+    return attn_store_grad<kAmax>(acc, 1.f, dv, ldd, row_out, nullptr, 0, 0, k0w, 0, T, 0,
+                                  QkNorm{nullptr, nullptr, 0}, stg, lane);
+  return attn_store_grad<kAmax>(acc, scale, dk, ldd, row_out, k, ld, kvbase + (int64_t)k0w * ld,
+                                k0w, (int64_t)b * T + k0w, T, H + hk, nq, stg, lane);
 }
 
 // ================================================================== dQ
@@ -810,27 +898,27 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   attn_amax_out(amx, amax_part, st0);
 }
 
+// kAmax: also leave per workgroup the largest |dk|, |dv| stored (amax_part)
 template <bool kGrouped, bool kAmax>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
+__global__ __launch_bounds__(512, 1) void attn_bwd_dkv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     int64_t ld, const bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ nl2,
     const float* __restrict__ Dv, bf16* __restrict__ dk, bf16* __restrict__ dv, int64_t ldd,
     int T, int H, int G, int win, float scale_log2, float scale, QkNorm nq,
     float* __restrict__ amax_part) {
-  __shared__ __attribute__((aligned(1024))) bf16 st0[kDkvStage];
-  __shared__ __attribute__((aligned(1024))) bf16 st1[kDkvStage];
+  __shared__ __attribute__((aligned(1024))) char smem[kDkvSmem];
   // key block kblk walks up to T/64 - 2 kblk query tiles: the low blocks are the long ones
   const BlockJob jb = block_job(T / 128, win >= T, false);
   float amx = 0.f;
   if (jb.second >= 0) {
-    amx = attn_bwd_dkv_block<kGrouped, kAmax>(q, k, v, ld, dO, ldo, nl2, Dv, dk, dv, ldd, T, H, G, win,
-                                       scale_log2, scale, jb.second, jb.bh, st0, st1, nq);
+    amx = attn_bwd_dkv_block<kGrouped, kAmax>(q, k, v, ld, dO, ldo, nl2, Dv, dk, dv, ldd, T, H,
+                                               G, win, scale_log2, scale, jb.second, jb.bh, smem, nq);
     __syncthreads();
   }
-  amx = max_nan(amx, attn_bwd_dkv_block<kGrouped, kAmax>(q, k, v, ld, dO, ldo, nl2, Dv, dk, dv, ldd, T,
-                                                  H, G, win, scale_log2, scale, jb.first, jb.bh,
-                                                  st0, st1, nq));
-  attn_amax_out(amx, amax_part, st0);
+  amx = max_nan(amx, attn_bwd_dkv_block<kGrouped, kAmax>(q, k, v, ld, dO, ldo, nl2, Dv, dk, dv,
+                                                          ldd, T, H, G, win, scale_log2, scale,
+                                                          jb.first, jb.bh, smem, nq));
+  attn_amax_out(amx, amax_part, reinterpret_cast<bf16*>(smem));
 }
 
 template <bool kAmax>
@@ -1014,7 +1102,7 @@ hipError_t nc_attn_bwd(int dtype, const void* q, const void* k, const void* v, i
                                          : attn_bwd_dkv_kernel<true, false>)
                             : (amax_part ? attn_bwd_dkv_kernel<false, true>
                                          : attn_bwd_dkv_kernel<false, false>);
-    dkv_kernel<<<B * Hkv * jobs, 256, 0, st>>>(
+    dkv_kernel<<<B * Hkv * jobs, 512, 0, st>>>(
         (const bf16*)q, (const bf16*)k, (const bf16*)v, ld, (const bf16*)dO, ldo, NL, D,
         (bf16*)dk, (bf16*)dv, ldd, T, H, G, win, scale * kLog2e, scale, nq,
         amax_part ? amax_part + (int64_t)B * H * jobs : nullptr);
