@@ -20,6 +20,9 @@ enum NcEpi {
   kEpiPoly = 5,       // C = p0*aux_in + p1*acc    (Newton-Schulz: b*A + c*A*A, a*X + B*X)
   kEpiDual = 6,       // C(f32) = p0*aux_in(f32, optional) + p1*acc; aux_out = C in the
                       // activation type (fp32 iterate + its matrix-core copy)
+  kEpiQkNorm = 7,     // the QKV product (bf16, one batch, no split, K % 64 == 0, N % 128 ==
+                      // 0): C = alpha*acc, and each of the first qk_heads 128-column heads
+                      // of a row is RMS-normalised and rotated (rope, rqk below)
 };
 
 struct GemmParams {
@@ -41,6 +44,13 @@ struct GemmParams {
   // batch, no split): per workgroup the largest |C| as stored (bf16), one float
   // per output tile, for C's fp8 scale without another pass over C
   float* amax_part;
+  // kEpiQkNorm only: row m is position m % rope_T of its sequence; head j < qk_heads
+  // of the row (columns 128 j .. 128 j + 127) becomes R_t (x r) with
+  // r = (mean(x^2) + qk_eps)^-1/2, and rqk[m * qk_heads + j] = r.  rope: cos | sin
+  // tables [rope_T][64]; R_t pairs dims i and i + 64.
+  const float* rope; float* rqk;
+  int rope_T, qk_heads;
+  float qk_eps;
 };
 
 // dtype: 0 = fp32 operands (VALU kernel), 1 = bf16 operands (MFMA kernel)

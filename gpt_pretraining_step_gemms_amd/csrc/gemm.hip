@@ -1185,8 +1185,81 @@ void gemm_bf16_pipe_kernel(GemmParams p) {
       }
     }
   };
+  // QK-norm + rotary epilogue of the QKV product.  A head's 128 columns are
+  // the tiles of waves wn and wn ^ 1 (wn even: dims 0-63); the two read each
+  // other's staged block, so each lane holds 8 dims of its row and their
+  // rotary partners 64 apart: 8 lanes per row sum the squares, then the lane
+  // normalises, rotates and stores its 8 outputs.  Two barriers per 32-row
+  // block (the partner's block is staged; it has been read before the next
+  // block overwrites it).
+  auto run_qk = [&]() {
+    constexpr int NIB = WTM / 32;
+    const int pw = wave ^ 1;
+    const int psidx = pw / EP_PER;
+    bf16* pbase;
+    if constexpr (EP_BUFS >= 3) pbase = psidx == 0 ? st0 : (psidx == 1 ? st1 : st2);
+    else pbase = psidx == 0 ? st0 : st1;
+    const float* pstg = reinterpret_cast<const float*>(pbase) + (pw % EP_PER) * EP_FLOATS;
+    const int ncol = n0 + wn * WTN;
+    const int head = ncol >> 7;
+    const bool normed = head < p.qk_heads, lo = (wn & 1) == 0;
+    bf16* Cb = static_cast<bf16*>(p.C) + cb;
+#pragma unroll
+    for (int i = 0; i < NIB; ++i) {
+#pragma unroll
+      for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            stg[(i2 * 16 + 4 * (lane >> 4) + e) * EP_LD + j * 16 + (lane & 15)] = acc[2 * i + i2][j][e];
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int row = rsub + 8 * t;
+        float v[8], w[8], o[8];
+        ld8(stg + row * EP_LD + 8 * q, v);
+        ld8(pstg + row * EP_LD + 8 * q, w);
+        const int m = m0 + wm * WTM + i * 32 + row;
+        const int n = ncol + 8 * q;
+        if (normed) {
+          float ss = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            v[e] *= p.alpha;
+            w[e] *= p.alpha;
+            ss += v[e] * v[e] + w[e] * w[e];
+          }
+          ss += __shfl_xor(ss, 1, kWave);
+          ss += __shfl_xor(ss, 2, kWave);
+          ss += __shfl_xor(ss, 4, kWave);
+          const float rs = 1.0f / sqrtf(ss / 128.f + p.qk_eps);
+          const int tp = m % p.rope_T;
+          float c[8], sn[8];
+          ld8(p.rope + tp * 64 + 8 * q, c);
+          ld8(p.rope + p.rope_T * 64 + tp * 64 + 8 * q, sn);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float y1 = (lo ? v[e] : w[e]) * rs, y2 = (lo ? w[e] : v[e]) * rs;
+            o[e] = lo ? y1 * c[e] - y2 * sn[e] : y1 * sn[e] + y2 * c[e];
+          }
+          if (lo && q == 0 && m < p.M) p.rqk[(int64_t)m * p.qk_heads + head] = rs;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = p.alpha * v[e];
+        }
+        if (m < p.M && n < p.N) st8(Cb + (int64_t)m * p.ldc + n, o);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+  };
   if (split_out) run.template operator()<kEpiStoreF32>();
-  else with_epilogue(p.epi, run);
+  else if constexpr (AL == kKCont && BL == kKCont && !F8 && MI == 16 && WTN == 64 && WN % 2 == 0) {
+    if (p.epi == kEpiQkNorm) run_qk();
+    else with_epilogue(p.epi, run);
+  } else {
+    with_epilogue(p.epi, run);
+  }
   if (F8 && p.amax_part) {
     // the staging buffers are free once every wave has passed the first
     // barrier inside block_max_nan
@@ -1304,7 +1377,7 @@ hipError_t nc_launch_gemm_f8(const GemmParams& p_in, hipStream_t st) {
   auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
   if (p.a_layout != kKCont || p.b_layout != kKCont || p.K <= 0 || p.K % 128 || p.lda % 16 ||
       p.ldb % 16 || (p.batch > 1 && (p.sA % 16 || p.sB % 16)) || !al16(p.A) || !al16(p.B) ||
-      (p.fmt_a != 0 && p.fmt_a != 1))
+      (p.fmt_a != 0 && p.fmt_a != 1) || p.epi == kEpiQkNorm)
     return hipErrorInvalidValue;
   if (p.splits < 1) p.splits = 1;
   if (p.amax_part && (p.batch != 1 || p.splits != 1)) return hipErrorInvalidValue;
@@ -1331,7 +1404,7 @@ hipError_t nc_launch_gemm(int dtype, const GemmParams& p_in, hipStream_t st) {
   if (p.M <= 0 || p.N <= 0 || p.batch <= 0) return hipSuccess;
   if (p.splits < 1) p.splits = 1;
   if (dtype == 0) {
-    if (p.amax_part) return hipErrorInvalidValue;
+    if (p.amax_part || p.epi == kEpiQkNorm) return hipErrorInvalidValue;
     p.splits = 1;
     dim3 grid(ceil_div(p.M, 64) * ceil_div(p.N, 64), 1, p.batch);
     const int code = p.a_layout * 2 + p.b_layout;
@@ -1351,6 +1424,12 @@ hipError_t nc_launch_gemm(int dtype, const GemmParams& p_in, hipStream_t st) {
   }
   const bool use_pipe = pipe_ok(p);
   if (p.amax_part) return hipErrorInvalidValue;    // kept by the fp8 kernels only
+  // the QK-norm epilogue: in the 64-deep K-contiguous configuration only
+  if (p.epi == kEpiQkNorm &&
+      (!use_pipe || p.a_layout != kKCont || p.b_layout != kKCont || p.K % 64 || p.N % 128 ||
+       p.splits != 1 || p.batch != 1 || !p.vec_epi || !p.rope || !p.rqk || p.rope_T < 1 ||
+       p.qk_heads < 0 || p.qk_heads * 128 > p.N))
+    return hipErrorInvalidValue;
   hipError_t e = use_pipe ? launch_pipe(p, st) : launch_bf16_cfg<256, 256, 2, 4>(p, st);
   if (e != hipSuccess || p.splits == 1) return e;
   return splitk_reduce(p, st);

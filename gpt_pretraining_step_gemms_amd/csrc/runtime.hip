@@ -518,6 +518,27 @@ hipError_t gemm(nc_ctx* c, const void* A_, int64_t lda, int al, const void* B_, 
   return nc_launch_gemm(dt, g, c->st);
 }
 
+// The QKV product (bf16) with the QK-norm + rotary forward in its epilogue:
+// the first nh heads of each row (the query and key heads) come out
+// RMS-normalised and rotated, and rqk gets their 1 / rms.
+hipError_t gemm_qk_norm(nc_ctx* c, const void* A_, const void* W, void* C_, int M, int Wd, int K,
+                        float* rqk, const float* tab, int T, int nh, float eps) {
+  GemmParams g{};
+  g.A = A_; g.B = W; g.C = C_;
+  g.lda = K; g.ldb = K; g.ldc = Wd;
+  g.M = M; g.N = Wd; g.K = K; g.batch = 1;
+  g.a_layout = kKCont; g.b_layout = kKCont; g.epi = kEpiQkNorm;
+  g.alpha = 1.f; g.splits = 1;
+  g.rope = tab; g.rqk = rqk; g.rope_T = T; g.qk_heads = nh; g.qk_eps = eps;
+  if (!operands_in_arenas(c, g, 2)) return hipErrorInvalidValue;
+  if (!in_arena(c, tab, (size_t)2 * T * 64 * 4) || !in_arena(c, rqk, (size_t)M * nh * 4)) {
+    c->range_error = "QK-norm table or rms output outside its arena";
+    return hipErrorInvalidValue;
+  }
+  if (c->dry_run) return hipSuccess;
+  return nc_launch_gemm(1, g, c->st);
+}
+
 // fp8 block products: one e4m3 scale per tensor (the pair {amax, s}); the
 // kernel divides the sums by the two operands' s.
 // The weight codes of layer l, product j (0 Wqkv [W, d], 1 Wo [d, d], 2 W1 [F, d],
@@ -932,6 +953,8 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
     NC_GEMM(ctx->fp8 ? gemm_fp8_fwd(ctx, aa + la.a1, d, wcodes(ctx, l, 0, false), Wd, qkv, Wd, N,
                                     kEpiStore, xt_of(l, 0), xs_of(l, 0),
                                     mixed ? nullptr : parts, ceil_div(N, 4))
+                     : dt ? gemm_qk_norm(ctx, aa + la.a1, wptr(ctx, wb), qkv, N, Wd, d,
+                                         A<float>(ctx, la.rqk), tab, T, H + Hkv, eps)
                      : gemm(ctx, aa + la.a1, d, kKCont, wptr(ctx, wb), d, kKCont, qkv, Wd, N, Wd,
                             d, kEpiStore), "qkv");
     if (ctx->ve_slot[l] >= 0) {
@@ -941,8 +964,9 @@ nc_status nc_fwd_bwd(nc_ctx* ctx, const int32_t* tok, const int32_t* tgt, int32_
                            qkv + (d + dk) * es, Wd, A<float>(ctx, ctx->sig_ve) + (size_t)i * N * Hkv,
                            N, Hkv, ctx->Cg, V, st), "value embedding");
     }
-    NC_TRY(nc_qk_norm_rope_fwd(dt, qkv, A<float>(ctx, la.rqk), tab, N, T, H, Hkv, eps, st),
-           "qknorm");
+    if (ctx->fp8 || !dt)   // bf16: formed in the QKV product's epilogue
+      NC_TRY(nc_qk_norm_rope_fwd(dt, qkv, A<float>(ctx, la.rqk), tab, N, T, H, Hkv, eps, st),
+             "qknorm");
     NC_TRY(nc_attn_fwd(dt, qkv, qkv + d * es, qkv + (d + dk) * es, Wd, aa + la.o, d,
                        A<float>(ctx, la.lse), B, T, H, Hkv, ctx->windows[l], st, parts, 1),
            "attn fwd");
