@@ -425,6 +425,11 @@ def test_op_operand_extents_are_checked_before_any_launch():
     assert gemm(lda=K - 8) == nc.NC_ERR_INVALID_ARG
     assert gemm(epi=nc.EPI_RELU2_BWD, aux=M * N * 2 - 2) == nc.NC_ERR_INVALID_ARG
     assert gemm(splits=4, ws_bytes=4 * M * N * 4 - 4) == nc.NC_ERR_INVALID_ARG
+    # epilogue 7 (the QKV product's QK-norm + rotary) is the step's own, not an op's
+    assert gemm(epi=7) == nc.NC_ERR_INVALID_ARG
+    assert lib.nc_op_gemm_noalloc(nc.NC_BF16, fake, BIG, K, 0, fake, BIG, K, 0, fake, BIG, N, M, N,
+                                  K, 1, 0, 0, 0, 7, None, 0, None, 0, 1.0, 0.0, 0.0, 1,
+                                  None) == nc.NC_ERR_INVALID_ARG
     # fp8 GEMM and quantiser
     g8 = lambda a_bytes=BIG, c_bytes=BIG, epi=nc.EPI_STORE, aux=None, aux_bytes=0: \
         lib.nc_op_gemm_fp8(0, fake, a_bytes, 256, fake, BIG, 256, fake, c_bytes, 64, 64, 64, 256,
@@ -432,6 +437,7 @@ def test_op_operand_extents_are_checked_before_any_launch():
     assert g8(a_bytes=64 * 256 - 1) == nc.NC_ERR_INVALID_ARG
     assert g8(c_bytes=64 * 64 * 4 - 4, epi=nc.EPI_STORE_F32) == nc.NC_ERR_INVALID_ARG
     assert g8(epi=nc.EPI_RELU2_BWD, aux=fake, aux_bytes=64 * 64 * 2 - 2) == nc.NC_ERR_INVALID_ARG
+    assert g8(epi=7) == nc.NC_ERR_INVALID_ARG
     qz = lambda xb, qb, ab=8, wb=4096, qtb=0: lib.nc_op_fp8_quantize(
         nc.NC_BF16, 0, fake, xb, 1000, 1, fake, ab, fake, qb, fake if qtb else None, qtb, fake, wb,
         None)
