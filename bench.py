@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--roofline-iters", type=int, default=20)
     ap.add_argument("--roofline-fp8", action="store_true",
                     help="only the fp8 GEMM at the MLP up-projection shape (tensorwise e4m3)")
+    ap.add_argument("--attention-only", action="store_true",
+                    help="only the bf16 attention forward and backward of one layer and "
+                         "micro-batch (the op entry points, 3 warm-up + --roofline-iters calls)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="with --roofline-only: also run a 1 GiB copy kernel (counter scale)")
     return ap.parse_args()
@@ -89,6 +92,47 @@ def roofline_gemm(cfg, iters):
             "bound": "mfma", "achieved": flops / sec / 1e12, "peak": PEAK_BF16 / 1e12,
             "unit": "TFLOP/s", "frac": flops / sec / PEAK_BF16,
             "traffic": measured_traffic(2 * (M * K + N * K + M * N))}
+
+
+def attention_only(cfg, iters):
+    """bf16 causal attention of one layer and micro-batch ([B*T, 3d] token-major
+    q | k | v, head dim 128) through the op entry points: the forward, then the
+    backward (dQ kernel, then dK/dV kernel), each timed with HIP events on the
+    launch stream.  FLOPs are the algorithmic causal counts, 2 N T d (forward)
+    and 5 N T d (backward)."""
+    import torch
+    from gpt_pretraining_step_gemms_amd import nc
+    B, T, H = cfg.micro_batch, cfg.seq_len, cfg.n_head
+    d = H * 128
+    g = torch.Generator(device="cuda").manual_seed(5)
+    qkv = torch.randn(B * T, 3 * d, device="cuda", generator=g).to(torch.bfloat16)
+    dO = (1e-3 * torch.randn(B * T, d, device="cuda", generator=g)).to(torch.bfloat16)
+    q, k, v = qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:]
+    o = torch.empty(B * T, d, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(B, H, T, dtype=torch.float32, device="cuda")
+    dqkv = torch.empty_like(qkv)
+    D = torch.empty(2, B, H, T, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    fwd = lambda: nc.attention_fwd(q, k, v, o, lse, B, T, H, 3 * d, d)
+    bwd = lambda: nc.attention_bwd(q, k, v, o, dO, lse, D, dqkv[:, :d], dqkv[:, d:2 * d],
+                                   dqkv[:, 2 * d:], B, T, H, 3 * d, d, 3 * d)
+    out = {"shape": {"B": B, "T": T, "H": H, "head_dim": 128}}
+    N = B * T
+    for name, f, flops in (("forward", fwd, 2.0 * N * T * d), ("backward", bwd, 5.0 * N * T * d)):
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(iters):
+            f()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        sec = t0.elapsed_time(t1) / 1e3 / iters
+        out[name] = {"avg_call_us": sec * 1e6, "achieved_tflops": flops / sec / 1e12,
+                     "frac": flops / sec / PEAK_BF16}
+    return out
 
 
 PEAK_FP8 = 5.0e15           # MI355X dense fp8 MFMA, FLOP/s
@@ -273,6 +317,9 @@ def main():
                      smear="smear" in feats, backout="backout" in feats)
     if args.roofline_fp8:
         print(json.dumps({"roofline_fp8": roofline_gemm_fp8(cfg, args.roofline_iters)}))
+        return
+    if args.attention_only:
+        print(json.dumps({"attention": attention_only(cfg, args.roofline_iters)}))
         return
     if args.roofline_only:
         r = roofline_gemm(cfg, args.roofline_iters)
