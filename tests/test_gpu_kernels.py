@@ -224,7 +224,7 @@ def _heads(x, B, T, H, col0):
     return a.reshape(B, T, H, 128).transpose(0, 2, 1, 3)
 
 
-@pytest.mark.parametrize("dtype,B,T,H", [(BF, 2, 256, 2), (BF, 1, 2048, 2), (BF, 2, 384, 1),
+@pytest.mark.parametrize("dtype,B,T,H", [(BF, 2, 256, 2), (BF, 1, 2048, 2), (BF, 2, 384, 1), (BF, 3, 128, 2),
                                          (BF, 4, 640, 2), (F32, 2, 64, 1), (F32, 1, 100, 2)])
 def test_attention_forward_backward_vs_oracle(dtype, B, T, H):
     d = H * 128
